@@ -1,0 +1,160 @@
+"""The draft-then-verify loop on a tiny random decoder (CPU oracle, float64).
+
+Used only to pin the accept rule and the round semantics against the pages' central claim: the
+loop emits exactly what greedy decoding over the full cache emits, whatever the drafter proposes
+("VeriCache: making lossy KV compression exact", The Core Idea and Verifying Without Giving Back
+the Speedup; "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference", Abstract and
+Results). The drafter and the verifier share the model weights and differ only in the cache they
+read (Methodology).
+
+The model: one attention layer with grouped-query heads over token + position embeddings, a
+residual connection and an untied output head. Keys/values of a position depend only on its token
+and position, so both caches are functions of the committed tokens; the compressed cache is rebuilt
+from the committed prefix each round (reading: the compressed copy tracks the committed prefix and
+draft-time entries are discarded after the round).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .accept import accept
+from .attention import decode
+from .quant import quantize_groups
+
+
+class TinyModel:
+    def __init__(self, seed=0, vocab=11, dm=16, d=8, Hq=4, Hkv=2, max_pos=128):
+        g = np.random.default_rng(seed)
+        self.V, self.dm, self.d, self.Hq, self.Hkv = vocab, dm, d, Hq, Hkv
+        self.E = g.standard_normal((vocab, dm))
+        self.P = 0.5 * g.standard_normal((max_pos, dm))
+        self.Wq = g.standard_normal((Hq * d, dm)) / np.sqrt(dm)
+        self.Wk = g.standard_normal((Hkv * d, dm)) / np.sqrt(dm)
+        self.Wv = g.standard_normal((Hkv * d, dm)) / np.sqrt(dm)
+        self.Wo = g.standard_normal((dm, Hq * d)) / np.sqrt(Hq * d)
+        self.Wlm = 3.0 * g.standard_normal((vocab, dm)) / np.sqrt(dm)
+        self.scale = 1.0 / np.sqrt(d)
+
+    def _x(self, tok, pos):
+        return self.E[tok] + self.P[pos]
+
+    def kv(self, tok, pos):
+        x = self._x(tok, pos)
+        return (self.Wk @ x).reshape(self.Hkv, self.d), (self.Wv @ x).reshape(self.Hkv, self.d)
+
+    def next_logits(self, tok, pos, K, V):
+        """Logits after token `tok` at `pos`, attending over K/V [Hkv][S, d] (S includes pos)."""
+        x = self._x(tok, pos)
+        q = (self.Wq @ x).reshape(self.Hq, self.d)
+        G = self.Hq // self.Hkv
+        o = np.concatenate([decode(q[h], K[h // G], V[h // G], self.scale)[0]
+                            for h in range(self.Hq)])
+        return self.Wlm @ (x + self.Wo @ o)
+
+
+def full_cache(model, tokens):
+    """Per kv head: keys/values of every position of `tokens`, float64 [Hkv][len, d]."""
+    kvs = [model.kv(t, p) for p, t in enumerate(tokens)]
+    K = [np.stack([k[h] for k, _ in kvs]) for h in range(model.Hkv)]
+    V = [np.stack([v[h] for _, v in kvs]) for h in range(model.Hkv)]
+    return K, V
+
+
+def greedy(model, prompt, steps):
+    """Plain greedy decoding over the full cache."""
+    toks = list(prompt)
+    out = []
+    while len(out) < steps:
+        K, V = full_cache(model, toks)
+        z = model.next_logits(toks[-1], len(toks) - 1, K, V)
+        t = int(np.argmax(z))
+        out.append(t)
+        toks.append(t)
+    return out
+
+
+# ---- drafters: each maps (model, committed tokens, x) -> x proposed tokens -----------------
+
+def _draft_with_cache(model, toks, x, compress):
+    """Autoregressive drafting: the committed positions come from compress(full cache); the
+    draft's own positions are appended exactly."""
+    K, V = full_cache(model, toks)
+    K, V = compress(K, V)
+    K = [k.copy() for k in K]
+    V = [v.copy() for v in V]
+    seq = list(toks)
+    draft = []
+    for _ in range(x):
+        z = model.next_logits(seq[-1], len(seq) - 1, K, V)
+        t = int(np.argmax(z))
+        draft.append(t)
+        seq.append(t)
+        k, v = model.kv(t, len(seq) - 1)
+        K = [np.vstack([K[h], k[h]]) for h in range(model.Hkv)]
+        V = [np.vstack([V[h], v[h]]) for h in range(model.Hkv)]
+    return draft
+
+
+def drafter_exact(model, toks, x):
+    return _draft_with_cache(model, toks, x, lambda K, V: (K, V))
+
+
+def drafter_quant(model, toks, x, bits=2):
+    """Per-token min/max quantisation of every committed key and value row (lossy)."""
+    def comp(K, V):
+        def q(A):
+            c, s, m = quantize_groups(A.astype(np.float32), bits, "f32")
+            return c.astype(np.float64) * s[:, None] + m[:, None]
+        return [q(k) for k in K], [q(v) for v in V]
+    return _draft_with_cache(model, toks, x, comp)
+
+
+def drafter_drop(model, toks, x, sinks=2, recent=3):
+    """Keep the first `sinks` and last `recent` committed positions (lossy)."""
+    def comp(K, V):
+        n = K[0].shape[0]
+        keep = sorted(set(range(min(sinks, n))) | set(range(max(0, n - recent), n)))
+        return [k[keep] for k in K], [v[keep] for v in V]
+    return _draft_with_cache(model, toks, x, comp)
+
+
+def drafter_wrong(model, toks, x):
+    """Always proposes tokens the full-cache model would not pick first."""
+    K, V = full_cache(model, toks)
+    z = model.next_logits(toks[-1], len(toks) - 1, K, V)
+    return [(int(np.argmax(z)) + 1) % model.V] * x
+
+
+def drafter_random(model, toks, x, seed=0):
+    g = np.random.default_rng(seed + len(toks))
+    return [int(t) for t in g.integers(0, model.V, size=x)]
+
+
+def verify(model, toks, draft):
+    """One pass over the full cache: predictions after the last committed token and after each
+    draft token, x + 1 in all (each position attends causally over everything before it)."""
+    seq = list(toks) + list(draft)
+    K, V = full_cache(model, seq)
+    n = len(toks)
+    preds = []
+    for i in range(len(draft) + 1):
+        p = n - 1 + i
+        Kp = [k[: p + 1] for k in K]
+        Vp = [v[: p + 1] for v in V]
+        preds.append(int(np.argmax(model.next_logits(seq[p], p, Kp, Vp))))
+    return preds
+
+
+def vericache(model, prompt, steps, x, drafter):
+    """Repeat draft / verify / accept until `steps` tokens are emitted; returns (tokens, rounds)
+    with rounds = [(a, emitted count)]."""
+    toks = list(prompt)
+    out, rounds = [], []
+    while len(out) < steps:
+        draft = drafter(model, toks, x)
+        a, _, emitted = accept(draft, verify(model, toks, draft))
+        emitted = emitted[: steps - len(out)]
+        rounds.append((a, len(emitted)))
+        out += emitted
+        toks += emitted
+    return out, rounds

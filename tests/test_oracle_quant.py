@@ -1,0 +1,175 @@
+"""Pins of the oracle's KIVI quantiser and packed layout (CPU only).
+
+Each check is something the definition fixes independently of the oracle's code: the half-step
+error bound, exact reconstruction of on-grid and constant groups, the extreme codes, monotonicity,
+locality of per-channel / per-token statistics, the float16 directed roundings, and the packed
+layout's bijectivity plus hand-derived spot bytes.
+"""
+import numpy as np
+import pytest
+
+from kv_cache_compressed_amd import synth
+from oracle import quant as Q
+
+
+def _groups(seed, shape, scale=1.0, bf16=False):
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32) * np.float32(scale)
+    return synth.round_bf16(x) if bf16 else x
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("meta", ["f32", "f16"])
+@pytest.mark.parametrize("bf16,scale", [(False, 1.0), (True, 1.0), (True, 8.0), (False, 1e-3)])
+def test_half_step_bound(bits, meta, bf16, scale):
+    X = _groups(1, (500, 32), scale, bf16)
+    c, s, m = Q.quantize_groups(X, bits, meta)
+    xh = c.astype(np.float64) * s[:, None] + m[:, None]
+    err = np.abs(X.astype(np.float64) - xh)
+    mag = np.maximum(np.abs(X), np.maximum(np.abs(m), s)[:, None]).astype(np.float64)
+    assert np.all(err <= s[:, None] / 2 + 2.0 ** -20 * mag)
+    assert c.max() <= 2 ** bits - 1
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("meta", ["f32", "f16"])
+def test_on_grid_exact(bits, meta):
+    g = np.random.default_rng(2)
+    lv = 2 ** bits - 1
+    for _ in range(200):
+        step = np.float32(2.0 ** g.integers(-6, 3))
+        base = np.float32(g.integers(-64, 64)) * step
+        k = g.integers(0, lv + 1, size=32)
+        k[0], k[1] = 0, lv                      # min and max present
+        X = (base + k.astype(np.float32) * step).astype(np.float32)
+        c, s, m = Q.quantize_groups(X[None], bits, meta)
+        assert s[0] == step and m[0] == base
+        assert np.array_equal(c[0], k)
+        assert np.array_equal(c[0].astype(np.float64) * s[0] + m[0], X.astype(np.float64))
+
+
+@pytest.mark.parametrize("meta", ["f32", "f16"])
+def test_constant_group(meta):
+    X = np.full((3, 32), np.float32(0.375))
+    X[1] = -2.5
+    X[2] = 0.0
+    c, s, m = Q.quantize_groups(X, 2, meta)
+    assert np.all(c == 0) and np.all(s == 0)
+    assert np.array_equal(m, X[:, 0])
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("meta", ["f32", "f16"])
+def test_extremes_and_monotone(bits, meta):
+    X = _groups(3, (300, 32), 1.0, True)
+    c, s, m = Q.quantize_groups(X, bits, meta)
+    lo = np.argmin(X, axis=1)
+    hi = np.argmax(X, axis=1)
+    r = np.arange(X.shape[0])
+    assert np.all(c[r, lo] == 0)
+    assert np.all(c[r, hi] == 2 ** bits - 1)
+    order = np.argsort(X, axis=1, kind="stable")
+    cs = np.take_along_axis(c, order, axis=1).astype(int)
+    assert np.all(np.diff(cs, axis=1) >= 0)
+
+
+def test_f16_directed_rounding():
+    x = np.random.default_rng(4).standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    x = np.concatenate([x, np.float32([0.0, 1.0, -1.0, 6e-8, -6e-8, 1e-9, 65504.0])])
+    dn = Q.f16_round_down(x)
+    up = Q.f16_round_up(x)
+    assert np.all(dn.astype(np.float32) <= x)
+    assert np.all(up.astype(np.float32) >= x)
+    with np.errstate(over="ignore"):
+        assert np.all(np.nextafter(dn, np.float16(np.inf)).astype(np.float32) > x)
+        assert np.all(np.nextafter(up, np.float16(-np.inf)).astype(np.float32) < x)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_key_stats_are_per_channel_per_group(bits):
+    K = _groups(5, (96, 128), 1.0, True)
+    c0, s0, m0 = Q.quantize_k(K, bits, "f16")
+    assert s0.shape == (3, 128) and m0.shape == (3, 128)
+    K2 = K.copy()
+    K2[40, 7] = np.float32(50.0)                # token 40 lies in group 1
+    c1, s1, m1 = Q.quantize_k(K2, bits, "f16")
+    changed = np.argwhere(s0 != s1)
+    assert changed.tolist() == [[1, 7]]
+    diff = np.argwhere(c0 != c1)
+    assert np.all(diff[:, 1] == 7) and np.all((diff[:, 0] >= 32) & (diff[:, 0] < 64))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_value_stats_are_per_token_per_channel_group(bits):
+    V = _groups(6, (40, 128), 1.0, True)
+    c0, s0, m0 = Q.quantize_v(V, bits, "f16")
+    assert s0.shape == (40, 4)
+    V2 = V.copy()
+    V2[9, 70] = np.float32(-40.0)              # channel 70 lies in channel group 2
+    c1, s1, m1 = Q.quantize_v(V2, bits, "f16")
+    assert np.argwhere(m0 != m1).tolist() == [[9, 2]]
+    diff = np.argwhere(c0 != c1)
+    assert np.all(diff[:, 0] == 9) and np.all((diff[:, 1] >= 64) & (diff[:, 1] < 96))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("kind", ["k", "v"])
+def test_layout_is_a_bijection(bits, kind):
+    tok, ch = Q._slot_map(bits, kind)
+    pairs = set(zip(tok.reshape(-1).tolist(), ch.reshape(-1).tolist()))
+    assert len(pairs) == 32 * 128 and tok.size == 32 * 128
+    assert tok.min() == 0 and tok.max() == 31 and ch.min() == 0 and ch.max() == 127
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("kind", ["k", "v"])
+def test_pack_roundtrip(bits, kind):
+    codes = np.random.default_rng(7).integers(0, 2 ** bits, size=(96, 128)).astype(np.uint8)
+    packed = Q.pack_codes(codes, bits, kind)
+    assert packed.shape == (96, 128 * bits // 8)
+    assert np.array_equal(Q.unpack_codes(packed, bits, kind), codes)
+
+
+def _single(bits, kind, t, c, val):
+    codes = np.zeros((32, 128), np.uint8)
+    codes[t, c] = val
+    return Q.pack_codes(codes, bits, kind).reshape(-1)
+
+
+def test_layout_spot_bytes():
+    """Spot bytes derived by hand from the layout formulas in include/vc.h."""
+    # keys, 2-bit: (token 0, channel 0) -> lane 0, word 0, half 0, slot 0 -> byte 0 bits 0-1
+    b = _single(2, "k", 0, 0, 3)
+    assert b[0] == 0x03 and b.sum() == 3
+    # keys, 2-bit: (token 17, channel 33) -> i=1, u//2=1; c=33: kb=1, gq=0, 2p+hf=1 -> p=0, hf=1
+    #   kb=1 -> u%2=0, s//4=1 -> u=2, s=4; lane 1 -> word 1*4+2=6; bit 16+2*4=24 -> byte 6*4+3
+    b = _single(2, "k", 17, 33, 2)
+    assert b[6 * 4 + 3] == 0x02 and b.sum() == 2
+    # values, 4-bit: (token 5, channel 18) -> tile 1, i=2; token 5: p//2=0, gq=1, 2(p%2)+hf=1 ->
+    #   p=0, hf=1; lane 2+16=18, word u=1 -> word 18*8+1=145; bit 16 -> byte 145*4+2
+    b = _single(4, "v", 5, 18, 9)
+    assert b[145 * 4 + 2] == 0x09 and b.sum() == 9
+    # values, 2-bit: (token 22, channel 127) -> tile 7: u=3, s//4=1; i=15; token 22: p//2=1,
+    #   4gq+2(p%2)+hf=6 -> gq=1, p%2=1, hf=0 -> p=3, s=7; lane 31 -> word 31*4+3=127; bit 14
+    b = _single(2, "v", 22, 127, 1)
+    assert b[127 * 4 + 1] == 0x40 and b.sum() == 0x40
+
+
+def test_kivi_layer_dequant_error_budget_4bit():
+    """Dequantised keys/values of a 4-bit fp32-metadata cache stay within half a step."""
+    g = np.random.default_rng(8)
+    K = g.standard_normal((256, 128)).astype(np.float32)
+    V = g.standard_normal((256, 128)).astype(np.float32)
+    lay = Q.KiviLayer(K, V, n_q=224, bits=4, meta_dtype="f32", res_dtype="f32")
+    Kh = lay.keys(32)
+    Vh = lay.values(32)
+    ks = np.repeat(lay.ks, 32, axis=0)
+    vs = np.repeat(lay.vs, 32, axis=1)
+    assert np.all(np.abs(Kh[:224] - K[:224]) <= ks / 2 + 1e-6)
+    assert np.all(np.abs(Vh[:224] - V[:224]) <= vs / 2 + 1e-6)
+    assert np.array_equal(Kh[224:], K[224:].astype(np.float64))  # residual exact (fp32)
+
+
+def test_residual_f16_rounding_of_bf16_is_exact_in_normal_range():
+    x = synth.round_bf16(np.random.default_rng(9).standard_normal(10000).astype(np.float32))
+    x = x[np.abs(x) >= 2.0 ** -14]
+    assert np.array_equal(Q.to_res(x, "f16"), x.astype(np.float64))
