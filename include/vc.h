@@ -1,0 +1,213 @@
+/*
+ * vc.h -- C ABI of libvc, the MI355X (gfx950) draft/verify attention path of VeriCache.
+ *
+ * The method (pages: "VeriCache: making lossy KV compression exact", a blog walk-through;
+ * "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference", a knowledge-base summary of
+ * the paper): a compressed KV cache in GPU memory drafts x tokens one at a time; one pass of the
+ * same model over the full KV cache then predicts every drafted position plus one more; the
+ * drafts are accepted up to the first disagreement, where the full-cache token is emitted
+ * instead. This library holds the attention and accept steps of that round:
+ *
+ *   vc_quantize_kv       KIVI-style b-bit quantisation of cached keys/values   (compressor)
+ *   vc_kivi_append       append full-precision tokens to the KIVI residual     (compressor)
+ *   vc_draft_attn_quant  one-query decode attention over the quantised cache  (draft)
+ *   vc_draft_attn_drop   one-query decode attention over kept positions       (draft)
+ *   vc_verify_attn       L-query causal block attention over the full cache   (verify)
+ *   vc_lse_merge         log-sum-exp merge of split partials                  (verify / draft)
+ *   vc_accept            per-row argmax, first disagreement, correction token (accept)
+ *
+ * Conventions (all calls):
+ *   - Every buffer is owned by the caller. Device pointers are HIP device memory; the library
+ *     allocates nothing and keeps no pointer after the stream work ends.
+ *   - Calls are asynchronous on the given stream (a hipStream_t passed as void*, NULL = the
+ *     default stream) and re-entrant; there is no mutable global state.
+ *   - Every argument is checked on the host before anything is enqueued; on any error nothing is
+ *     enqueued and a status != VC_OK is returned, with a detail string in vc_last_error()
+ *     (thread-local). HIP runtime failures return VC_ERR_HIP. No C++ exception crosses the ABI.
+ *   - Device pointers must be 16-byte aligned. Head dimension d is 128 everywhere.
+ *   - Query head h reads kv head h / (Hq / Hkv) (grouped-query attention, contiguous groups).
+ *   - sm_scale multiplies q.k before the softmax (1/sqrt(128) for the pages' models).
+ */
+#ifndef VC_H
+#define VC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t vc_status;
+enum {
+  VC_OK = 0,
+  VC_ERR_INVALID = 1,     /* bad argument (null pointer, shape, alignment, range)          */
+  VC_ERR_UNSUPPORTED = 2, /* valid combination that this build does not implement           */
+  VC_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the matching *_workspace()   */
+  VC_ERR_HIP = 4          /* a HIP runtime call failed; vc_last_error() names it            */
+};
+
+enum { VC_F32 = 0, VC_F16 = 1, VC_BF16 = 2 };
+
+/*
+ * One attention layer's KIVI cache ("VeriCache: Turning Lossy KV Cache into Lossless LLM
+ * Inference", Key Contributions: KIVI is one of the quantising drafters; the compressor interface
+ * exposes bits per element; Limitations: one uniform bit width). Keys are quantised per channel
+ * over groups of 32 consecutive tokens, values per token over groups of 32 consecutive channels;
+ * the most recent tokens stay in a full-precision residual ring.
+ *
+ * Per group of 32 values: min m and max M; stored min m^ = m (fp32 metadata) or the largest fp16
+ * <= m (fp16 metadata); stored scale s^ = fl32(fl32(M - m^) / (2^b - 1)), rounded up to fp16 for
+ * fp16 metadata; code = 0 if s^ == 0, else clamp(rint_even(fl32(fl32(x - m^) / s^)), 0, 2^b-1);
+ * x_hat = code * s^ + m^. Every step is one correctly rounded IEEE operation, so codes and
+ * metadata are reproducible bit for bit.
+ *
+ * Code layout. Codes of each (b, h) form blocks of 32 tokens x 128 channels; block g holds
+ * tokens 32g..32g+31 and occupies bytes [32g, 32g+32) x row_bytes of the [tok_cap][row_bytes]
+ * buffer (row_bytes = 128*bits/8), i.e. 32*row_bytes contiguous bytes. A block is 64 "lanes" of
+ * 2*bits little-endian 32-bit words; word u of lane l is word l*(2*bits)+u of the block. A word
+ * has two 16-bit halves hf in {0,1}; half hf holds 16/bits slots s, slot s at bits
+ * [16*hf + bits*s, 16*hf + bits*s + bits). With i = l % 16 and gq = l / 16:
+ *   keys,   2-bit: token = 16*(u/2) + i,  kb = 2*(u%2) + s/4,  p = s%4
+ *   keys,   4-bit: token = 16*(u/4) + i,  kb = u%4,            p = s
+ *           both:  channel = 32*kb + 8*gq + 2*p + hf
+ *   values, 2-bit: tile = 2*u + s/4,  p = s%4
+ *   values, 4-bit: tile = u,          p = s
+ *           both:  channel = 16*tile + i,  token = 16*(p/2) + 4*gq + 2*(p%2) + hf
+ * (The layout puts the codes one 64-lane matrix-core operand needs into one lane's words.)
+ */
+typedef struct vc_kivi {
+  int32_t bits;       /* 2 or 4                                                         */
+  int32_t group;      /* 32                                                             */
+  int32_t meta_dtype; /* VC_F32 or VC_F16: storage of (scale, min) pairs                */
+  int32_t res_dtype;  /* VC_F32 or VC_F16: storage of residual keys/values              */
+  int32_t B, Hkv, d;  /* batch, kv heads, head dim (128)                                 */
+  int32_t res_cap;    /* residual ring slots per (b, h); multiple of 32, >= 32          */
+  int64_t tok_cap;    /* quantised-token capacity per (b, h); multiple of 32            */
+  void *k_codes;      /* [B][Hkv][tok_cap][128*bits/8] uint8, layout above              */
+  void *v_codes;      /* [B][Hkv][tok_cap][128*bits/8] uint8, layout above              */
+  void *k_meta;       /* [B][Hkv][tok_cap/32][128][2] (scale, min) in meta_dtype         */
+  void *v_meta;       /* [B][Hkv][tok_cap][4][2]      (scale, min) in meta_dtype         */
+  void *k_res;        /* [B][Hkv][res_cap][128] in res_dtype; token t in slot t % res_cap */
+  void *v_res;        /* [B][Hkv][res_cap][128] in res_dtype                             */
+} vc_kivi;
+
+/*
+ * Quantise tokens t0 .. t0+ntok-1 of every (b, h) into the cache's codes and metadata.
+ * Source element (b, h, i, c) (token t0+i) is read at k[((b*Hkv + h)*src_bh_stride) + i*128 + c]
+ * (likewise v), src_dtype VC_F32 | VC_F16 | VC_BF16, device memory. t0 and ntok are multiples of
+ * 32, t0 + ntok <= tok_cap, src_bh_stride >= ntok*128. Used at prefill (source: the full cache)
+ * and to flush 32 residual tokens (source: the ring slots of those tokens).
+ * Pages: compressors keep every position at fewer bits ("VeriCache: making lossy KV compression
+ * exact", The Tradeoff VeriCache Is Trying to Escape).
+ */
+vc_status vc_quantize_kv(const vc_kivi *c, const void *k, const void *v, int32_t src_dtype,
+                         int64_t src_bh_stride, int64_t t0, int64_t ntok, void *stream);
+
+/*
+ * Write tokens t0 .. t0+ntok-1 (same source addressing as vc_quantize_kv) into the residual ring
+ * slots (t0+i) % res_cap, converted to res_dtype with round-half-even. 1 <= ntok <= res_cap.
+ */
+vc_status vc_kivi_append(const vc_kivi *c, const void *k, const void *v, int32_t src_dtype,
+                         int64_t src_bh_stride, int64_t t0, int64_t ntok, void *stream);
+
+/*
+ * Draft attention over the KIVI cache ("VeriCache: making lossy KV compression exact", The Core
+ * Idea: the model drafts each token over the compressed cache; Verifying Without Giving Back the
+ * Speedup: drafting is bound by GPU memory bandwidth).
+ * For every (b, query head h): keys/values = dequantised tokens 0..n_q-1 followed by residual
+ * tokens n_q..n_q+r-1 (ring slots); s_t = sm_scale * q.k_t; out = softmax(s) . V;
+ * lse = log-sum-exp of s (natural log).
+ *   q    [B][Hq][128] in q_dtype (VC_F32 | VC_BF16 | VC_F16), device
+ *   out  [B][Hq][128] fp32, device;  lse [B][Hq] fp32 or NULL
+ *   n_q  multiple of 32, <= tok_cap;  0 <= r <= res_cap;  n_q + r >= 1;  Hq % Hkv == 0,
+ *        Hq/Hkv <= 8
+ *   ws   device workspace of vc_draft_quant_workspace() bytes. Its first 4096 bytes are ticket
+ *        counters that must be zero before first use; every completed call leaves them zero.
+ *        Calls that overlap in time must not share a workspace.
+ */
+vc_status vc_draft_attn_quant(const vc_kivi *c, int64_t n_q, int32_t r, const void *q,
+                              int32_t q_dtype, int32_t Hq, float sm_scale, float *out, float *lse,
+                              void *ws, size_t ws_bytes, void *stream);
+vc_status vc_draft_quant_workspace(const vc_kivi *c, int64_t n_q, int32_t r, int32_t Hq,
+                                   size_t *bytes);
+
+/*
+ * Draft attention over kept positions of a token-dropping compressor ("VeriCache: Turning Lossy KV
+ * Cache into Lossless LLM Inference", Key Contributions: the interface exposes dropped positions;
+ * Limitations: identical drop counts for every head).
+ * For every (b, query head h, kv head g = h/(Hq/Hkv)): keys/values = rows idx[b][g][0..n_keep-1]
+ * of k/v[b][g]; same attention as above.
+ *   k, v  [B][Hkv][tok_cap][128] in kv_dtype (VC_BF16 | VC_F16), device
+ *   idx   [B][Hkv][idx_cap] int32 positions; entries outside [0, tok_cap) contribute nothing
+ *   q     [B][Hq][128] in kv_dtype; out [B][Hq][128] fp32; lse [B][Hq] or NULL
+ *   1 <= n_keep <= idx_cap;  ws as for vc_draft_attn_quant (vc_draft_drop_workspace() bytes).
+ */
+vc_status vc_draft_attn_drop(const void *k, const void *v, int32_t kv_dtype, int32_t B,
+                             int32_t Hkv, int64_t tok_cap, const int32_t *idx, int64_t n_keep,
+                             int64_t idx_cap, const void *q, int32_t Hq, float sm_scale,
+                             float *out, float *lse, void *ws, size_t ws_bytes, void *stream);
+vc_status vc_draft_drop_workspace(int32_t B, int32_t Hkv, int32_t Hq, int64_t n_keep,
+                                  size_t *bytes);
+
+/*
+ * Verify attention ("VeriCache: making lossy KV compression exact", The Core Idea: one pass over
+ * the full cache yields a prediction for every drafted position plus one; Verifying Without Giving
+ * Back the Speedup: the full cache may live in CPU memory and be brought in only to verify).
+ * Row i (0 <= i < L) of query head h is at position n+i and attends over past tokens 0..n-1 and
+ * block tokens 0..i (causal). Split-K partials over the past (and over the block) are merged with
+ * log-sum-exp.
+ *   q            [B][Hq][L][128] in dtype, device
+ *   k_blk, v_blk [B][Hkv][L][128] in dtype, device (keys/values of positions n..n+L-1)
+ *   k_past, v_past  element (b, h, t, c) at [((b*Hkv + h)*past_stride + t)*128 + c], dtype;
+ *                device memory, or pinned host memory when past_on_host != 0 (then streamed in
+ *                chunks of chunk_tokens tokens through the workspace, copies on `copy`, compute
+ *                on `compute`; pageable host memory is rejected). past_stride >= n.
+ *   out          [B][Hq][L][128] fp32; lse [B][Hq][L] fp32 or NULL
+ *   dtype        VC_BF16 (matrix-core path) or VC_F32 (vector path; device-resident past only)
+ *   1 <= L <= 32, n >= 0, Hq % Hkv == 0, Hq/Hkv <= 8.
+ *   ws           vc_verify_workspace() bytes (partials, plus two chunk stages when streaming).
+ * The host past must stay valid until `compute` has passed this call: `compute` waits for every
+ * copy, so synchronising `compute` suffices.
+ */
+vc_status vc_verify_attn(const void *q, const void *k_blk, const void *v_blk, int32_t L,
+                         const void *k_past, const void *v_past, int64_t past_stride, int64_t n,
+                         int32_t past_on_host, int64_t chunk_tokens, int32_t dtype, int32_t B,
+                         int32_t Hq, int32_t Hkv, float sm_scale, float *out, float *lse, void *ws,
+                         size_t ws_bytes, void *compute_stream, void *copy_stream);
+vc_status vc_verify_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int64_t n,
+                              int32_t past_on_host, int64_t chunk_tokens, int32_t dtype,
+                              size_t *bytes);
+
+/*
+ * Log-sum-exp merge of S split partials per row (the pages are silent on how split work is
+ * combined; this is the exact recombination of softmax partials):
+ *   part_o  [rows][S][d] fp32: o_s = sum_t e^{s_t - m_s} v_t over split s
+ *   part_ml [rows][S][2] fp32: (m_s, l_s = sum_t e^{s_t - m_s}); l_s == 0 marks an empty split
+ *   m = max m_s;  out = sum_s o_s e^{m_s - m} / sum_s l_s e^{m_s - m};  lse = m + ln(sum ...)
+ *   out [rows][d] fp32, lse [rows] or NULL. A row with no live split gets out = 0, lse = -inf.
+ *   1 <= S <= 4096, d == 128.
+ */
+vc_status vc_lse_merge(const float *part_o, const float *part_ml, int64_t rows, int32_t S,
+                       int32_t d, float *out, float *lse, void *stream);
+
+/*
+ * Greedy accept ("VeriCache: making lossy KV compression exact", The Core Idea, Figure 1 and the
+ * worked example): v_i = argmax logits[b][i] (lowest index on ties) for i < L; a = first i < L-1
+ * with drafts[b][i] != v_i, or L-1 if none; next = v_a (the correction, or the bonus token).
+ * With L == 1 this is plain greedy argmax (drafts may be NULL).
+ *   logits     [B][L][V] fp32, finite; drafts [B][L-1] int32
+ *   accept_len [B] int32 (a);  next_token [B] int32;  argmax [B][L] int32 or NULL
+ *   1 <= L <= 64, 1 <= V <= 2^30.
+ */
+vc_status vc_accept(const float *logits, const int32_t *drafts, int32_t B, int32_t L, int32_t V,
+                    int32_t *accept_len, int32_t *next_token, int32_t *argmax, void *stream);
+
+const char *vc_status_string(vc_status s);
+const char *vc_last_error(void);
+int32_t vc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VC_H */

@@ -1,0 +1,287 @@
+// C ABI of libvc: host-side argument validation and launch orchestration.
+//
+// Every argument is checked before anything is enqueued; on error nothing is enqueued and the
+// reason is kept in a thread-local string for vc_last_error(). No exception crosses the ABI.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+vc_status fail(vc_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+vc_status hip_fail(hipError_t e, const char* where) {
+  (void)hipGetLastError();  // clear the sticky launch error of this thread
+  return fail(VC_ERR_HIP, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+vc_status ok() {
+  g_err.clear();
+  return VC_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, ...)                                  \
+  do {                                                      \
+    if (!(cond)) return fail(VC_ERR_INVALID, __VA_ARGS__);  \
+  } while (0)
+#define REQUIRE_PTR(p)                                                                \
+  do {                                                                                \
+    if ((p) == nullptr) return fail(VC_ERR_INVALID, "%s is null", #p);              \
+    if (!aligned16(p)) return fail(VC_ERR_INVALID, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+bool valid_dtype(int32_t t) { return t == VC_F32 || t == VC_F16 || t == VC_BF16; }
+
+vc_status check_kivi(const vc_kivi* c) {
+  REQUIRE(c != nullptr, "kivi descriptor is null");
+  REQUIRE(c->bits == 2 || c->bits == 4, "bits must be 2 or 4 (got %d)", c->bits);
+  REQUIRE(c->group == 32, "group must be 32 (got %d)", c->group);
+  REQUIRE(c->meta_dtype == VC_F32 || c->meta_dtype == VC_F16, "meta_dtype must be VC_F32 or VC_F16");
+  REQUIRE(c->res_dtype == VC_F32 || c->res_dtype == VC_F16, "res_dtype must be VC_F32 or VC_F16");
+  REQUIRE(c->B >= 1 && c->Hkv >= 1, "B and Hkv must be >= 1");
+  REQUIRE(c->d == 128, "head dim must be 128 (got %d)", c->d);
+  REQUIRE(c->res_cap >= 32 && c->res_cap % 32 == 0, "res_cap must be a positive multiple of 32");
+  REQUIRE(c->tok_cap >= 0 && c->tok_cap % 32 == 0, "tok_cap must be a non-negative multiple of 32");
+  REQUIRE((int64_t)c->B * c->Hkv <= 65535, "B*Hkv must be <= 65535");
+  REQUIRE_PTR(c->k_res);
+  REQUIRE_PTR(c->v_res);
+  if (c->tok_cap > 0) {
+    REQUIRE_PTR(c->k_codes);
+    REQUIRE_PTR(c->v_codes);
+    REQUIRE_PTR(c->k_meta);
+    REQUIRE_PTR(c->v_meta);
+  }
+  return VC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t vc_abi_version(void) { return 1; }
+
+const char* vc_last_error(void) { return g_err.c_str(); }
+
+const char* vc_status_string(vc_status s) {
+  switch (s) {
+    case VC_OK: return "VC_OK";
+    case VC_ERR_INVALID: return "VC_ERR_INVALID";
+    case VC_ERR_UNSUPPORTED: return "VC_ERR_UNSUPPORTED";
+    case VC_ERR_WORKSPACE: return "VC_ERR_WORKSPACE";
+    case VC_ERR_HIP: return "VC_ERR_HIP";
+    default: return "VC_ERR_UNKNOWN";
+  }
+}
+
+vc_status vc_quantize_kv(const vc_kivi* c, const void* k, const void* v, int32_t src_dtype,
+                         int64_t src_bh_stride, int64_t t0, int64_t ntok, void* stream) {
+  if (vc_status st = check_kivi(c)) return st;
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE(valid_dtype(src_dtype), "src_dtype must be VC_F32, VC_F16 or VC_BF16");
+  REQUIRE(t0 >= 0 && t0 % 32 == 0, "t0 must be a non-negative multiple of 32");
+  REQUIRE(ntok >= 0 && ntok % 32 == 0, "ntok must be a non-negative multiple of 32");
+  REQUIRE(t0 + ntok <= c->tok_cap, "t0 + ntok (%lld) exceeds tok_cap (%lld)", (long long)(t0 + ntok),
+          (long long)c->tok_cap);
+  REQUIRE(src_bh_stride >= ntok * 128, "src_bh_stride must be >= ntok*128");
+  if (ntok == 0) return ok();
+  hipError_t e = vc::launch_quantize(*c, k, v, src_dtype, src_bh_stride, t0, ntok,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_quantize_kv launch");
+  return ok();
+}
+
+vc_status vc_kivi_append(const vc_kivi* c, const void* k, const void* v, int32_t src_dtype,
+                         int64_t src_bh_stride, int64_t t0, int64_t ntok, void* stream) {
+  if (vc_status st = check_kivi(c)) return st;
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE(valid_dtype(src_dtype), "src_dtype must be VC_F32, VC_F16 or VC_BF16");
+  REQUIRE(t0 >= 0, "t0 must be >= 0");
+  REQUIRE(ntok >= 1 && ntok <= c->res_cap, "ntok must be in [1, res_cap]");
+  REQUIRE(src_bh_stride >= ntok * 128, "src_bh_stride must be >= ntok*128");
+  hipError_t e = vc::launch_append(*c, k, v, src_dtype, src_bh_stride, t0, ntok,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_kivi_append launch");
+  return ok();
+}
+
+vc_status vc_draft_quant_workspace(const vc_kivi* c, int64_t n_q, int32_t r, int32_t Hq,
+                                   size_t* bytes) {
+  if (vc_status st = check_kivi(c)) return st;
+  REQUIRE(bytes != nullptr, "bytes is null");
+  REQUIRE(n_q >= 0 && n_q % 32 == 0 && n_q <= c->tok_cap, "n_q must be a multiple of 32 in [0, tok_cap]");
+  REQUIRE(Hq >= 1 && Hq % c->Hkv == 0, "Hq must be a positive multiple of Hkv");
+  (void)r;
+  *bytes = vc::plan_draft_quant(*c, n_q, Hq).ws_bytes;
+  return ok();
+}
+
+vc_status vc_draft_attn_quant(const vc_kivi* c, int64_t n_q, int32_t r, const void* q,
+                              int32_t q_dtype, int32_t Hq, float sm_scale, float* out, float* lse,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (vc_status st = check_kivi(c)) return st;
+  REQUIRE(n_q >= 0 && n_q % 32 == 0 && n_q <= c->tok_cap, "n_q must be a multiple of 32 in [0, tok_cap]");
+  REQUIRE(r >= 0 && r <= c->res_cap, "r must be in [0, res_cap]");
+  REQUIRE(n_q + r >= 1, "no keys: n_q + r must be >= 1");
+  REQUIRE(Hq >= 1 && Hq % c->Hkv == 0, "Hq must be a positive multiple of Hkv");
+  REQUIRE(valid_dtype(q_dtype), "q_dtype must be VC_F32, VC_F16 or VC_BF16");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(out);
+  if (Hq / c->Hkv > 8) return fail(VC_ERR_UNSUPPORTED, "Hq/Hkv > 8 is not supported");
+  if (c->res_cap > 512) return fail(VC_ERR_UNSUPPORTED, "res_cap > 512 is not supported");
+  if ((int64_t)c->B * c->Hkv > vc::COUNTER_BYTES / 4)
+    return fail(VC_ERR_UNSUPPORTED, "B*Hkv > %d is not supported", vc::COUNTER_BYTES / 4);
+  const vc::DraftQuantPlan plan = vc::plan_draft_quant(*c, n_q, Hq);
+  if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
+    return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,
+                ws ? ws_bytes : (size_t)0);
+  hipError_t e = vc::launch_draft_quant(*c, n_q, r, q, q_dtype, Hq, sm_scale, out, lse, ws, plan,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_draft_attn_quant launch");
+  return ok();
+}
+
+vc_status vc_draft_drop_workspace(int32_t B, int32_t Hkv, int32_t Hq, int64_t n_keep, size_t* bytes) {
+  REQUIRE(bytes != nullptr, "bytes is null");
+  REQUIRE(B >= 1 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, "bad head/batch sizes");
+  REQUIRE(n_keep >= 1, "n_keep must be >= 1");
+  *bytes = vc::plan_draft_drop(B, Hkv, Hq, n_keep).ws_bytes;
+  return ok();
+}
+
+vc_status vc_draft_attn_drop(const void* k, const void* v, int32_t kv_dtype, int32_t B,
+                             int32_t Hkv, int64_t tok_cap, const int32_t* idx, int64_t n_keep,
+                             int64_t idx_cap, const void* q, int32_t Hq, float sm_scale,
+                             float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(out);
+  REQUIRE(valid_dtype(kv_dtype), "kv_dtype must be VC_F32, VC_F16 or VC_BF16");
+  REQUIRE(B >= 1 && Hkv >= 1, "B and Hkv must be >= 1");
+  REQUIRE(Hq >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv");
+  REQUIRE(tok_cap >= 1, "tok_cap must be >= 1");
+  REQUIRE(n_keep >= 1 && n_keep <= idx_cap, "n_keep must be in [1, idx_cap]");
+  REQUIRE((int64_t)B * Hkv <= 65535, "B*Hkv must be <= 65535");
+  if (kv_dtype != VC_BF16) return fail(VC_ERR_UNSUPPORTED, "only VC_BF16 keys/values are supported");
+  if (Hq / Hkv > 8) return fail(VC_ERR_UNSUPPORTED, "Hq/Hkv > 8 is not supported");
+  if ((int64_t)B * Hkv > vc::COUNTER_BYTES / 4)
+    return fail(VC_ERR_UNSUPPORTED, "B*Hkv > %d is not supported", vc::COUNTER_BYTES / 4);
+  const vc::DraftDropPlan plan = vc::plan_draft_drop(B, Hkv, Hq, n_keep);
+  if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
+    return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,
+                ws ? ws_bytes : (size_t)0);
+  hipError_t e = vc::launch_draft_drop(k, v, kv_dtype, B, Hkv, tok_cap, idx, n_keep, idx_cap, q, Hq,
+                                       sm_scale, out, lse, ws, plan, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_draft_attn_drop launch");
+  return ok();
+}
+
+vc_status vc_verify_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int64_t n,
+                              int32_t past_on_host, int64_t chunk_tokens, int32_t dtype,
+                              size_t* bytes) {
+  REQUIRE(bytes != nullptr, "bytes is null");
+  REQUIRE(B >= 1 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, "bad head/batch sizes");
+  REQUIRE(L >= 1 && L <= 32, "L must be in [1, 32]");
+  REQUIRE(n >= 0, "n must be >= 0");
+  REQUIRE(dtype == VC_BF16 || dtype == VC_F32, "dtype must be VC_BF16 or VC_F32");
+  if (past_on_host) REQUIRE(chunk_tokens >= 32, "chunk_tokens must be >= 32 when streaming");
+  *bytes = vc::plan_verify(B, Hq, Hkv, L, n, past_on_host, chunk_tokens, dtype).ws_bytes;
+  return ok();
+}
+
+vc_status vc_verify_attn(const void* q, const void* k_blk, const void* v_blk, int32_t L,
+                         const void* k_past, const void* v_past, int64_t past_stride, int64_t n,
+                         int32_t past_on_host, int64_t chunk_tokens, int32_t dtype, int32_t B,
+                         int32_t Hq, int32_t Hkv, float sm_scale, float* out, float* lse, void* ws,
+                         size_t ws_bytes, void* compute_stream, void* copy_stream) {
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_blk);
+  REQUIRE_PTR(v_blk);
+  REQUIRE_PTR(out);
+  REQUIRE(L >= 1 && L <= 32, "L must be in [1, 32] (got %d)", L);
+  REQUIRE(n >= 0, "n must be >= 0");
+  REQUIRE(past_stride >= n, "past_stride must be >= n");
+  REQUIRE(B >= 1 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv");
+  REQUIRE(dtype == VC_BF16 || dtype == VC_F32, "dtype must be VC_BF16 or VC_F32");
+  REQUIRE((int64_t)B * Hkv <= 65535, "B*Hkv must be <= 65535");
+  if (n > 0) {
+    REQUIRE_PTR(k_past);
+    REQUIRE_PTR(v_past);
+  }
+  if (Hq / Hkv > 8) return fail(VC_ERR_UNSUPPORTED, "Hq/Hkv > 8 is not supported");
+  if (dtype == VC_F32) {
+    if (past_on_host) return fail(VC_ERR_UNSUPPORTED, "host-streamed past needs VC_BF16");
+    if ((int64_t)B * Hq * L > 65535) return fail(VC_ERR_UNSUPPORTED, "VC_F32 verify needs B*Hq*L <= 65535");
+  }
+  if (past_on_host) {
+    REQUIRE(chunk_tokens >= 32, "chunk_tokens must be >= 32 when streaming");
+    REQUIRE(n >= 1, "a host-streamed past needs n >= 1");
+    for (const void* p : {k_past, v_past}) {
+      hipPointerAttribute_t attr;
+      hipError_t e = hipPointerGetAttributes(&attr, p);
+      if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(VC_ERR_INVALID, "past_on_host needs pinned host memory (hipHostMalloc); got pageable or device memory");
+      }
+    }
+  }
+  const vc::VerifyPlan plan = vc::plan_verify(B, Hq, Hkv, L, n, past_on_host, chunk_tokens, dtype);
+  if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
+    return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,
+                ws ? ws_bytes : (size_t)0);
+  hipError_t e = vc::launch_verify(q, k_blk, v_blk, L, k_past, v_past, past_stride, n, past_on_host,
+                                   dtype, B, Hq, Hkv, sm_scale, out, lse, ws, plan,
+                                   static_cast<hipStream_t>(compute_stream),
+                                   static_cast<hipStream_t>(copy_stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_verify_attn");
+  return ok();
+}
+
+vc_status vc_lse_merge(const float* part_o, const float* part_ml, int64_t rows, int32_t S, int32_t d,
+                       float* out, float* lse, void* stream) {
+  REQUIRE_PTR(part_o);
+  REQUIRE_PTR(part_ml);
+  REQUIRE_PTR(out);
+  REQUIRE(rows >= 1, "rows must be >= 1");
+  REQUIRE(S >= 1 && S <= 4096, "S must be in [1, 4096]");
+  REQUIRE(d == 128, "d must be 128");
+  REQUIRE((rows + 3) / 4 <= 2147483647LL, "too many rows");
+  hipError_t e = vc::launch_merge(part_o, part_ml, rows, S, out, lse, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_lse_merge launch");
+  return ok();
+}
+
+vc_status vc_accept(const float* logits, const int32_t* drafts, int32_t B, int32_t L, int32_t V,
+                    int32_t* accept_len, int32_t* next_token, int32_t* argmax, void* stream) {
+  REQUIRE_PTR(logits);
+  REQUIRE(accept_len != nullptr, "accept_len is null");
+  REQUIRE(next_token != nullptr, "next_token is null");
+  REQUIRE(B >= 1, "B must be >= 1");
+  REQUIRE(L >= 1 && L <= 64, "L must be in [1, 64] (got %d)", L);
+  REQUIRE(V >= 1 && V <= (1 << 30), "V must be in [1, 2^30]");
+  if (L > 1) REQUIRE(drafts != nullptr, "drafts is null (needed when L > 1)");
+  hipError_t e = vc::launch_accept(logits, drafts, B, L, V, accept_len, next_token, argmax,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_accept launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Host-side launchers of the libvc kernels (validated arguments only; see api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vc.h"
+
+namespace vc {
+
+hipError_t launch_quantize(const vc_kivi& c, const void* k, const void* v, int src_dtype,
+                           int64_t src_bh_stride, int64_t t0, int64_t ntok, hipStream_t s);
+hipError_t launch_append(const vc_kivi& c, const void* k, const void* v, int src_dtype,
+                         int64_t src_bh_stride, int64_t t0, int64_t ntok, hipStream_t s);
+
+hipError_t launch_accept(const float* logits, const int32_t* drafts, int B, int L, int V,
+                         int32_t* accept_len, int32_t* next_token, int32_t* argmax, hipStream_t s);
+
+hipError_t launch_merge(const float* part_o, const float* part_ml, int64_t rows, int S,
+                        float* out, float* lse, hipStream_t s);
+
+// Draft over the quantised cache.
+struct DraftQuantPlan {
+  int splits;        // quantised-token splits per (b, kv head)
+  int total_splits;  // splits + 1 (the residual split)
+  size_t ws_bytes;
+};
+DraftQuantPlan plan_draft_quant(const vc_kivi& c, int64_t n_q, int Hq);
+hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* q, int q_dtype,
+                              int Hq, float sm_scale, float* out, float* lse, void* ws,
+                              const DraftQuantPlan& plan, hipStream_t s);
+
+// Draft over kept positions.
+struct DraftDropPlan {
+  int splits;
+  size_t ws_bytes;
+};
+DraftDropPlan plan_draft_drop(int B, int Hkv, int Hq, int64_t n_keep);
+hipError_t launch_draft_drop(const void* k, const void* v, int kv_dtype, int B, int Hkv,
+                             int64_t tok_cap, const int32_t* idx, int64_t n_keep, int64_t idx_cap,
+                             const void* q, int Hq, float sm_scale, float* out, float* lse,
+                             void* ws, const DraftDropPlan& plan, hipStream_t s);
+
+// Verify.
+struct VerifyPlan {
+  int past_splits;      // splits over the device-resident past (or per streamed chunk)
+  int chunks;           // streamed chunks (0 when the past is device resident)
+  int64_t chunk_tokens;
+  int total_splits;     // partials per row
+  size_t part_bytes;    // partial buffers
+  size_t stage_bytes;   // one chunk stage (K and V), 0 when resident
+  size_t ws_bytes;
+};
+VerifyPlan plan_verify(int B, int Hq, int Hkv, int L, int64_t n, int past_on_host,
+                       int64_t chunk_tokens, int dtype);
+hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, int L,
+                         const void* k_past, const void* v_past, int64_t past_stride, int64_t n,
+                         int past_on_host, int dtype, int B, int Hq, int Hkv, float sm_scale,
+                         float* out, float* lse, void* ws, const VerifyPlan& plan,
+                         hipStream_t compute, hipStream_t copy);
+
+}  // namespace vc

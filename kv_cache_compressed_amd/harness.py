@@ -1,0 +1,183 @@
+"""One synthetic single-layer draft/verify round on the GPU, driven through libvc.
+
+Device memory, streams and the stand-in logits projection (z = W o, a plain fp32 GEMM in place of
+the model's LM head) come from PyTorch; every attention, quantisation, cache-append and accept
+step is a libvc call. Inputs come from the seeded generator (kv_cache_compressed_amd.synth).
+
+Round ("VeriCache: making lossy KV compression exact", The Core Idea): x draft steps over the
+compressed cache (each: append the step's key/value, draft attention, logits, greedy argmax), one
+verify pass of x+1 rows over the full cache, logits, accept.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import synth, vc
+
+SM_SCALE = float(np.float32(1.0 / np.sqrt(128.0)))
+
+
+def _dev(x: np.ndarray, dtype, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=dtype)
+
+
+class RoundState:
+    """Device state of one workload: caches, inputs, outputs and workspaces."""
+
+    def __init__(self, w: synth.Workload, seed: int = 0, device: str = "cuda", inputs=None,
+                 idx_lists=None, replicas: int = 1):
+        self.w, self.seed, self.device = w, seed, device
+        if inputs is None:
+            K, V = synth.kv_past(w, seed)
+            Kn, Vn = synth.kv_new(w, seed)
+            inputs = (K, V, Kn, Vn, synth.q_new(w, seed), synth.projection(w, seed))
+        K, V, Kn, Vn, Q, W = inputs
+        tdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+        self.tdt = tdt
+        B, Hkv, Hq, L, n, x = w.B, w.Hkv, w.Hq, w.L, w.n, w.x
+        # round block (positions n .. n+x): keys/values and queries
+        self.k_blk = _dev(Kn, tdt, device)
+        self.v_blk = _dev(Vn, tdt, device)
+        self.q_verify = _dev(Q, tdt, device)                                   # [B, Hq, L, 128]
+        self.q_draft = self.q_verify.permute(2, 0, 1, 3).contiguous()          # [L, B, Hq, 128]
+        self.W = _dev(W, torch.float32, device)                                # [V, Hq*128]
+        # full cache: device store [B, Hkv, tok_cap, 128] (past + block), or pinned host past
+        cap = w.tok_cap
+        if w.past_on_host:
+            self.k_host = torch.empty((B, Hkv, n, 128), dtype=tdt, pin_memory=True)
+            self.v_host = torch.empty_like(self.k_host, pin_memory=True)
+            self.k_host.copy_(torch.from_numpy(K).to(tdt))
+            self.v_host.copy_(torch.from_numpy(V).to(tdt))
+            self.k_store = self.v_store = None
+        else:
+            self.k_store = torch.zeros((B, Hkv, cap, 128), dtype=tdt, device=device)
+            self.v_store = torch.zeros_like(self.k_store)
+            self.k_store[:, :, :n] = _dev(K, tdt, device)
+            self.v_store[:, :, :n] = _dev(V, tdt, device)
+            self.k_store[:, :, n:n + L] = self.k_blk
+            self.v_store[:, :, n:n + L] = self.v_blk
+        # drafter caches
+        self.ws_draft = vc.Workspace(device)
+        self.ws_verify = vc.Workspace(device)
+        self.replicas = []
+        if w.drafter == "kivi":
+            if w.past_on_host:  # prefill: quantise from a temporary device copy of the past
+                kt = _dev(K, tdt, device)
+                vt = _dev(V, tdt, device)
+                src = (kt, vt, n * 128)
+            else:
+                src = (self.k_store, self.v_store, cap * 128)
+            for _ in range(max(1, replicas)):
+                c = vc.KiviCache(B, Hkv, max(w.n_q, 32), w.bits,
+                                 vc.VC_F16 if w.meta_dtype == "f16" else vc.VC_F32,
+                                 vc.VC_F16 if w.res_dtype == "f16" else vc.VC_F32, w.res_cap, device)
+                vc.vc_quantize_kv(c, src[0], src[1], 0, w.n_q, src_bh_stride=src[2])
+                if n > w.n_q:
+                    vc.vc_kivi_append(c, src[0][:, :, w.n_q:], src[1][:, :, w.n_q:], w.n_q, n - w.n_q,
+                                      src_bh_stride=src[2])
+                self.replicas.append(c)
+            if w.past_on_host:
+                torch.cuda.synchronize()
+                del kt, vt
+        else:
+            if idx_lists is None:
+                idx_lists = [[synth.keep_list(w, seed, b, h) for h in range(Hkv)] for b in range(B)]
+            self.idx_lists = idx_lists
+            kept = len(idx_lists[0][0])
+            idx = np.zeros((B, Hkv, kept + x), np.int32)
+            for b in range(B):
+                for h in range(Hkv):
+                    idx[b, h, :kept] = idx_lists[b][h]
+                    idx[b, h, kept:] = np.arange(n, n + x)
+            self.idx = torch.from_numpy(idx).to(device)
+            self.kept = kept
+        # outputs
+        f32 = dict(dtype=torch.float32, device=device)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.out_d = torch.zeros((x, B, Hq, 128), **f32)
+        self.lse_d = torch.zeros((x, B, Hq), **f32)
+        self.logits_d = torch.zeros((x, B, w.vocab), **f32)
+        self.tok_d = torch.zeros((x, B), **i32)
+        self.scratch_a = torch.zeros((B,), **i32)
+        self.drafts = torch.zeros((B, x), **i32)
+        self.out_v = torch.zeros((B, Hq, L, 128), **f32)
+        self.lse_v = torch.zeros((B, Hq, L), **f32)
+        self.logits_v = torch.zeros((B, L, w.vocab), **f32)
+        self.accept_len = torch.zeros((B,), **i32)
+        self.next_tok = torch.zeros((B,), **i32)
+        self.argmax_v = torch.zeros((B, L), **i32)
+        self.copy_stream = torch.cuda.Stream(device=device) if w.past_on_host else None
+        self._rep = 0
+        self.verify_ws_bytes = vc.vc_verify_workspace(B, Hq, Hkv, L, n, w.past_on_host,
+                                                      w.chunk_tokens, self._vdt())
+
+    def _vdt(self):
+        return vc.VC_BF16 if self.w.kv_dtype == "bf16" else vc.VC_F32
+
+    # ---- steps ---------------------------------------------------------------------------
+    def draft_attention(self, j: int, cache=None):
+        """Draft attention of step j (position n+j) into out_d[j], lse_d[j]."""
+        w = self.w
+        if w.drafter == "kivi":
+            c = cache or self.replicas[0]
+            r = (w.n - w.n_q) + j + 1
+            nb = vc.vc_draft_quant_workspace(c, w.n_q, r, w.Hq)
+            vc.vc_draft_attn_quant(c, w.n_q, r, self.q_draft[j], self.out_d[j], self.lse_d[j],
+                                   self.ws_draft.get(nb), SM_SCALE)
+        else:
+            n_keep = self.kept + j + 1
+            nb = vc.vc_draft_drop_workspace(w.B, w.Hkv, w.Hq, n_keep)
+            vc.vc_draft_attn_drop(self.k_store, self.v_store, self.idx, n_keep, self.q_draft[j],
+                                  self.out_d[j], self.lse_d[j], self.ws_draft.get(nb), SM_SCALE)
+
+    def append_draft_entry(self, j: int, cache=None):
+        w = self.w
+        if w.drafter == "kivi":
+            c = cache or self.replicas[0]
+            vc.vc_kivi_append(c, self.k_blk[:, :, j], self.v_blk[:, :, j], w.n + j, 1,
+                              src_bh_stride=w.L * 128)
+
+    def draft_step(self, j: int):
+        c = None
+        if self.replicas:
+            c = self.replicas[self._rep % len(self.replicas)]
+            self._rep += 1
+        self.append_draft_entry(j, c)
+        self.draft_attention(j, c)
+        w = self.w
+        torch.matmul(self.out_d[j].view(w.B, -1), self.W.t(), out=self.logits_d[j])
+        vc.vc_accept(self.logits_d[j].view(w.B, 1, w.vocab), None, self.scratch_a, self.tok_d[j])
+
+    def verify_attention(self):
+        w = self.w
+        ws = self.ws_verify.get(self.verify_ws_bytes)
+        if w.past_on_host:
+            vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.k_host, self.v_host, w.n,
+                              self.out_v, self.lse_v, ws, SM_SCALE, past_stride=w.n,
+                              past_on_host=True, chunk_tokens=w.chunk_tokens,
+                              copy_stream=self.copy_stream)
+        else:
+            vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.k_store, self.v_store, w.n,
+                              self.out_v, self.lse_v, ws, SM_SCALE, past_stride=w.tok_cap)
+
+    def verify_step(self):
+        w = self.w
+        self.verify_attention()
+        flat = self.out_v.permute(0, 2, 1, 3).reshape(w.B * w.L, w.Hq * 128)
+        torch.matmul(flat, self.W.t(), out=self.logits_v.view(w.B * w.L, w.vocab))
+        self.drafts.copy_(self.tok_d.t())
+        vc.vc_accept(self.logits_v, self.drafts, self.accept_len, self.next_tok, self.argmax_v)
+
+    def run_round(self):
+        for j in range(self.w.x):
+            self.draft_step(j)
+        self.verify_step()
+
+    def results(self) -> dict:
+        torch.cuda.synchronize()
+        return dict(drafts=self.drafts.cpu().numpy(), draft_logits=self.logits_d.cpu().numpy(),
+                    verified=self.argmax_v.cpu().numpy(), verify_logits=self.logits_v.cpu().numpy(),
+                    a=self.accept_len.cpu().numpy(), next=self.next_tok.cpu().numpy(),
+                    out_d=self.out_d.cpu().numpy(), lse_d=self.lse_d.cpu().numpy(),
+                    out_v=self.out_v.cpu().numpy(), lse_v=self.lse_v.cpu().numpy())

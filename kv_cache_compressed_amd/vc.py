@@ -1,0 +1,236 @@
+"""Thin ctypes binding of libvc (include/vc.h): the same entry points, argument marshalling only.
+
+Every step of the draft/verify path runs in libvc's HIP kernels. This module only turns torch
+tensors into pointers, sizes and dtype codes, passes the current HIP stream, and raises on a
+non-OK status. It never computes anything itself and has no fallback: if libvc.so is missing it
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvc.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "vc.h")
+
+VC_OK, VC_ERR_INVALID, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_HIP = 0, 1, 2, 3, 4
+VC_F32, VC_F16, VC_BF16 = 0, 1, 2
+_TORCH_DT = {torch.float32: VC_F32, torch.float16: VC_F16, torch.bfloat16: VC_BF16}
+
+_lib = None
+
+
+class VcError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class vc_kivi(ctypes.Structure):
+    _fields_ = [
+        ("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("meta_dtype", ctypes.c_int32),
+        ("res_dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("res_cap", ctypes.c_int32), ("tok_cap", ctypes.c_int64),
+        ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p), ("k_meta", ctypes.c_void_p),
+        ("v_meta", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+    ]
+
+
+_P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_KP = ctypes.POINTER(vc_kivi)
+_SIGS = {
+    "vc_quantize_kv": [_KP, _P, _P, _I32, _I64, _I64, _I64, _P],
+    "vc_kivi_append": [_KP, _P, _P, _I32, _I64, _I64, _I64, _P],
+    "vc_draft_attn_quant": [_KP, _I64, _I32, _P, _I32, _I32, _F, _P, _P, _P, _SZ, _P],
+    "vc_draft_quant_workspace": [_KP, _I64, _I32, _I32, ctypes.POINTER(_SZ)],
+    "vc_draft_attn_drop": [_P, _P, _I32, _I32, _I32, _I64, _P, _I64, _I64, _P, _I32, _F, _P, _P, _P,
+                           _SZ, _P],
+    "vc_draft_drop_workspace": [_I32, _I32, _I32, _I64, ctypes.POINTER(_SZ)],
+    "vc_verify_attn": [_P, _P, _P, _I32, _P, _P, _I64, _I64, _I32, _I64, _I32, _I32, _I32, _I32, _F,
+                       _P, _P, _P, _SZ, _P, _P],
+    "vc_verify_workspace": [_I32, _I32, _I32, _I32, _I64, _I32, _I64, _I32, ctypes.POINTER(_SZ)],
+    "vc_lse_merge": [_P, _P, _I64, _I32, _I32, _P, _P, _P],
+    "vc_accept": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
+    "vc_status_string": [_I32],
+    "vc_last_error": [],
+    "vc_abi_version": [],
+}
+
+
+def lib():
+    """Load libvc.so (built in-tree by kv_cache_compressed_amd.build); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_compressed_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(l, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int32
+        l.vc_status_string.restype = ctypes.c_char_p
+        l.vc_last_error.restype = ctypes.c_char_p
+        _lib = l
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Names of every function include/vc.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:vc_status|const char \*|int32_t)\s*(vc_\w+)\s*\(", text, re.M)))
+
+
+def _check(st: int):
+    if st != VC_OK:
+        l = lib()
+        raise VcError(st, f"{l.vc_status_string(st).decode()}: {l.vc_last_error().decode()}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(stream)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    return _TORCH_DT[t.dtype]
+
+
+# ------------------------------------------------------------------------------------------
+# KIVI cache storage (device tensors) and its C descriptor
+# ------------------------------------------------------------------------------------------
+class KiviCache:
+    """Device buffers of one layer's KIVI cache, laid out as include/vc.h describes."""
+
+    def __init__(self, B, Hkv, tok_cap, bits, meta_dtype, res_dtype, res_cap, device="cuda", d=128):
+        assert tok_cap % 32 == 0 and res_cap % 32 == 0 and d == 128
+        self.B, self.Hkv, self.tok_cap, self.bits, self.res_cap, self.d = B, Hkv, tok_cap, bits, res_cap, d
+        self.meta_dtype, self.res_dtype = meta_dtype, res_dtype
+        row = d * bits // 8
+        mdt = torch.float16 if meta_dtype == VC_F16 else torch.float32
+        rdt = torch.float16 if res_dtype == VC_F16 else torch.float32
+        cap = max(tok_cap, 32)
+        self.k_codes = torch.zeros(B, Hkv, cap, row, dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros_like(self.k_codes)
+        self.k_meta = torch.zeros(B, Hkv, cap // 32, d, 2, dtype=mdt, device=device)
+        self.v_meta = torch.zeros(B, Hkv, cap, d // 32, 2, dtype=mdt, device=device)
+        self.k_res = torch.zeros(B, Hkv, res_cap, d, dtype=rdt, device=device)
+        self.v_res = torch.zeros_like(self.k_res)
+
+    def desc(self) -> vc_kivi:
+        return vc_kivi(self.bits, 32, self.meta_dtype, self.res_dtype, self.B, self.Hkv, self.d,
+                       self.res_cap, self.tok_cap, _ptr(self.k_codes), _ptr(self.v_codes),
+                       _ptr(self.k_meta), _ptr(self.v_meta), _ptr(self.k_res), _ptr(self.v_res))
+
+
+class Workspace:
+    """A zero-initialised device workspace (the draft calls need their counters zeroed once)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+# ------------------------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ------------------------------------------------------------------------------------------
+def vc_quantize_kv(cache: KiviCache, k, v, t0: int, ntok: int, src_bh_stride: int | None = None,
+                   stream=None):
+    """k, v: device tensors whose (b, h) slices start src_bh_stride elements apart (default: a
+    contiguous [B, Hkv, ntok, 128] tensor)."""
+    stride = k.stride(1) if src_bh_stride is None else src_bh_stride
+    d = cache.desc()
+    _check(lib().vc_quantize_kv(ctypes.byref(d), _ptr(k), _ptr(v), dtype_code(k), stride, t0, ntok,
+                                _stream(stream)))
+
+
+def vc_kivi_append(cache: KiviCache, k, v, t0: int, ntok: int, src_bh_stride: int | None = None,
+                   stream=None):
+    stride = k.stride(1) if src_bh_stride is None else src_bh_stride
+    d = cache.desc()
+    _check(lib().vc_kivi_append(ctypes.byref(d), _ptr(k), _ptr(v), dtype_code(k), stride, t0, ntok,
+                                _stream(stream)))
+
+
+def vc_draft_quant_workspace(cache: KiviCache, n_q: int, r: int, Hq: int) -> int:
+    n = _SZ(0)
+    d = cache.desc()
+    _check(lib().vc_draft_quant_workspace(ctypes.byref(d), n_q, r, Hq, ctypes.byref(n)))
+    return n.value
+
+
+def vc_draft_attn_quant(cache: KiviCache, n_q: int, r: int, q, out, lse, ws: torch.Tensor,
+                        sm_scale: float, stream=None):
+    d = cache.desc()
+    _check(lib().vc_draft_attn_quant(ctypes.byref(d), n_q, r, _ptr(q), dtype_code(q), q.shape[1],
+                                     sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                     _stream(stream)))
+
+
+def vc_draft_drop_workspace(B: int, Hkv: int, Hq: int, n_keep: int) -> int:
+    n = _SZ(0)
+    _check(lib().vc_draft_drop_workspace(B, Hkv, Hq, n_keep, ctypes.byref(n)))
+    return n.value
+
+
+def vc_draft_attn_drop(k, v, idx, n_keep: int, q, out, lse, ws: torch.Tensor, sm_scale: float,
+                       stream=None):
+    """k, v: [B, Hkv, tok_cap, 128]; idx: int32 [B, Hkv, idx_cap]; q: [B, Hq, 128]."""
+    B, Hkv, tok_cap, _ = k.shape
+    _check(lib().vc_draft_attn_drop(_ptr(k), _ptr(v), dtype_code(k), B, Hkv, tok_cap, _ptr(idx),
+                                    n_keep, idx.shape[2], _ptr(q), q.shape[1], sm_scale, _ptr(out),
+                                    _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def vc_verify_workspace(B, Hq, Hkv, L, n, past_on_host, chunk_tokens, dtype) -> int:
+    nb = _SZ(0)
+    _check(lib().vc_verify_workspace(B, Hq, Hkv, L, n, int(past_on_host), chunk_tokens, dtype,
+                                     ctypes.byref(nb)))
+    return nb.value
+
+
+def vc_verify_attn(q, k_blk, v_blk, k_past, v_past, n: int, out, lse, ws: torch.Tensor,
+                   sm_scale: float, past_stride: int | None = None, past_on_host: bool = False,
+                   chunk_tokens: int = 0, stream=None, copy_stream=None):
+    """q [B, Hq, L, 128]; k_blk/v_blk [B, Hkv, L, 128]; k_past/v_past [B, Hkv, >=n, 128]."""
+    B, Hq, L, _ = q.shape
+    Hkv = k_blk.shape[1]
+    stride = k_past.shape[2] if past_stride is None else past_stride
+    comp = _stream(stream)
+    cp = _stream(copy_stream) if copy_stream is not None else comp
+    _check(lib().vc_verify_attn(_ptr(q), _ptr(k_blk), _ptr(v_blk), L, _ptr(k_past), _ptr(v_past),
+                                stride, n, int(past_on_host), chunk_tokens, dtype_code(q), B, Hq, Hkv,
+                                sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), comp, cp))
+
+
+def vc_lse_merge(part_o, part_ml, out, lse, stream=None):
+    """part_o [rows, S, 128], part_ml [rows, S, 2] -> out [rows, 128], lse [rows]."""
+    rows, S, d = part_o.shape
+    _check(lib().vc_lse_merge(_ptr(part_o), _ptr(part_ml), rows, S, d, _ptr(out), _ptr(lse),
+                              _stream(stream)))
+
+
+def vc_accept(logits, drafts, accept_len, next_token, argmax=None, stream=None):
+    """logits [B, L, V] fp32; drafts [B, L-1] int32 (or None when L == 1)."""
+    B, L, V = logits.shape
+    _check(lib().vc_accept(_ptr(logits), _ptr(drafts), B, L, V, _ptr(accept_len), _ptr(next_token),
+                           _ptr(argmax), _stream(stream)))

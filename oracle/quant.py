@@ -208,6 +208,7 @@ class KiviLayer:
     def __init__(self, K: np.ndarray, V: np.ndarray, n_q: int, bits: int, meta_dtype: str,
                  res_dtype: str):
         self.bits, self.meta_dtype, self.res_dtype, self.n_q = bits, meta_dtype, res_dtype, n_q
+        self.d = K.shape[1]
         K32 = np.asarray(K, np.float32)
         V32 = np.asarray(V, np.float32)
         self.kc, self.ks, self.km = quantize_k(K32[:n_q], bits, meta_dtype)
@@ -223,12 +224,12 @@ class KiviLayer:
     def keys(self, r: int) -> np.ndarray:
         """Dequantised keys 0..n_q-1 followed by the first r residual keys, float64."""
         parts = [dequantize_k(self.kc, self.ks, self.km)] if self.n_q else []
-        parts.append(np.array(self.res_k[:r], np.float64).reshape(r, -1))
+        parts.append(np.array(self.res_k[:r], np.float64).reshape(r, self.d))
         return np.concatenate(parts, axis=0)
 
     def values(self, r: int) -> np.ndarray:
         parts = [dequantize_v(self.vc, self.vs, self.vm)] if self.n_q else []
-        parts.append(np.array(self.res_v[:r], np.float64).reshape(r, -1))
+        parts.append(np.array(self.res_v[:r], np.float64).reshape(r, self.d))
         return np.concatenate(parts, axis=0)
 
 

@@ -1,0 +1,145 @@
+"""C-ABI checks that need no GPU: libvc.so loads, exports every function include/vc.h declares,
+and rejects invalid arguments on the host with the documented status (nothing is enqueued: these
+calls never reach a HIP launch). Pointers are fake but 16-byte aligned; validation never
+dereferences them.
+"""
+import ctypes
+
+import pytest
+
+from kv_cache_compressed_amd import vc
+
+P = 0x10000  # a fake, aligned "device" pointer
+BAD = 0x10004  # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    return vc.lib()
+
+
+def test_every_header_symbol_is_exported(L):
+    names = vc.header_symbols()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(vc._SIGS) == set(names)
+
+
+def test_version_and_strings(L):
+    assert L.vc_abi_version() == 1
+    assert L.vc_status_string(0) == b"VC_OK"
+    assert L.vc_status_string(4) == b"VC_ERR_HIP"
+    assert L.vc_status_string(99) == b"VC_ERR_UNKNOWN"
+
+
+def _kivi(**kw):
+    d = dict(bits=2, group=32, meta_dtype=vc.VC_F16, res_dtype=vc.VC_F16, B=2, Hkv=2, d=128,
+             res_cap=256, tok_cap=1024, k_codes=P, v_codes=P, k_meta=P, v_meta=P, k_res=P, v_res=P)
+    d.update(kw)
+    return vc.vc_kivi(*[d[f] for f, _ in vc.vc_kivi._fields_])
+
+
+def _err(L):
+    return L.vc_last_error().decode()
+
+
+@pytest.mark.parametrize("field,val,msg", [
+    ("bits", 3, "bits"), ("bits", 8, "bits"), ("group", 64, "group"), ("d", 64, "head dim"),
+    ("meta_dtype", vc.VC_BF16, "meta_dtype"), ("res_dtype", 7, "res_dtype"), ("res_cap", 40, "res_cap"),
+    ("tok_cap", 33, "tok_cap"), ("k_codes", 0, "k_codes"), ("v_meta", BAD, "aligned"), ("B", 0, "B"),
+])
+def test_quantize_rejects_bad_descriptor(L, field, val, msg):
+    k = _kivi(**{field: val})
+    st = L.vc_quantize_kv(ctypes.byref(k), P, P, vc.VC_BF16, 1024 * 128, 0, 64, None)
+    assert st == vc.VC_ERR_INVALID and msg in _err(L)
+
+
+def test_quantize_rejects_bad_ranges(L):
+    k = _kivi()
+    assert L.vc_quantize_kv(ctypes.byref(k), P, P, vc.VC_BF16, 1 << 20, 16, 32, None) == vc.VC_ERR_INVALID
+    assert L.vc_quantize_kv(ctypes.byref(k), P, P, vc.VC_BF16, 1 << 20, 0, 48, None) == vc.VC_ERR_INVALID
+    assert L.vc_quantize_kv(ctypes.byref(k), P, P, vc.VC_BF16, 1 << 20, 992, 64, None) == vc.VC_ERR_INVALID
+    assert "tok_cap" in _err(L)
+    assert L.vc_quantize_kv(ctypes.byref(k), P, P, vc.VC_BF16, 100, 0, 64, None) == vc.VC_ERR_INVALID
+    assert L.vc_quantize_kv(ctypes.byref(k), P, P, 9, 1 << 20, 0, 64, None) == vc.VC_ERR_INVALID
+    assert L.vc_quantize_kv(None, P, P, vc.VC_BF16, 1 << 20, 0, 64, None) == vc.VC_ERR_INVALID
+    # ntok == 0 is a valid no-op that enqueues nothing
+    assert L.vc_quantize_kv(ctypes.byref(k), P, P, vc.VC_BF16, 1 << 20, 0, 0, None) == vc.VC_OK
+
+
+def test_append_rejects(L):
+    k = _kivi()
+    assert L.vc_kivi_append(ctypes.byref(k), P, P, vc.VC_BF16, 128, 0, 0, None) == vc.VC_ERR_INVALID
+    assert L.vc_kivi_append(ctypes.byref(k), P, P, vc.VC_BF16, 1 << 20, 0, 257, None) == vc.VC_ERR_INVALID
+    assert L.vc_kivi_append(ctypes.byref(k), P, BAD, vc.VC_BF16, 1 << 20, 0, 1, None) == vc.VC_ERR_INVALID
+
+
+def test_draft_quant_rejects(L):
+    k = _kivi()
+    call = lambda **a: L.vc_draft_attn_quant(
+        ctypes.byref(a.get("kivi", k)), a.get("n_q", 512), a.get("r", 100), a.get("q", P), vc.VC_BF16,
+        a.get("Hq", 8), 0.088, a.get("out", P), None, a.get("ws", P), a.get("ws_bytes", 1 << 30), None)
+    assert call(n_q=500) == vc.VC_ERR_INVALID
+    assert call(n_q=2048) == vc.VC_ERR_INVALID
+    assert call(r=300) == vc.VC_ERR_INVALID
+    assert call(n_q=0, r=0) == vc.VC_ERR_INVALID and "no keys" in _err(L)
+    assert call(Hq=7) == vc.VC_ERR_INVALID
+    assert call(q=0) == vc.VC_ERR_INVALID
+    assert call(out=BAD) == vc.VC_ERR_INVALID
+    assert call(Hq=2 * 9) == vc.VC_ERR_UNSUPPORTED
+    assert call(kivi=_kivi(res_cap=1024)) == vc.VC_ERR_UNSUPPORTED
+    assert call(ws=0) == vc.VC_ERR_WORKSPACE
+    assert call(ws_bytes=100) == vc.VC_ERR_WORKSPACE
+    n = ctypes.c_size_t(0)
+    assert L.vc_draft_quant_workspace(ctypes.byref(k), 512, 100, 8, ctypes.byref(n)) == vc.VC_OK
+    assert n.value > 4096
+    assert call(ws_bytes=n.value - 1) == vc.VC_ERR_WORKSPACE
+
+
+def test_draft_drop_rejects(L):
+    call = lambda **a: L.vc_draft_attn_drop(
+        P, P, a.get("dt", vc.VC_BF16), 2, 2, 5000, a.get("idx", P), a.get("n_keep", 100),
+        a.get("idx_cap", 200), P, a.get("Hq", 8), 0.088, P, None, a.get("ws", P), a.get("ws_bytes", 1 << 30), None)
+    assert call(idx=0) == vc.VC_ERR_INVALID
+    assert call(n_keep=0) == vc.VC_ERR_INVALID
+    assert call(n_keep=300) == vc.VC_ERR_INVALID
+    assert call(Hq=5) == vc.VC_ERR_INVALID
+    assert call(dt=vc.VC_F32) == vc.VC_ERR_UNSUPPORTED
+    assert call(ws_bytes=10) == vc.VC_ERR_WORKSPACE
+
+
+def test_verify_rejects(L):
+    call = lambda **a: L.vc_verify_attn(
+        P, P, P, a.get("L", 31), a.get("kp", P), P, a.get("stride", 4096), a.get("n", 4000),
+        a.get("host", 0), a.get("chunk", 0), a.get("dt", vc.VC_BF16), 2, a.get("Hq", 8), 2, 0.088, P,
+        None, P, a.get("ws_bytes", 1 << 34), None, None)
+    assert call(L=0) == vc.VC_ERR_INVALID
+    assert call(L=33) == vc.VC_ERR_INVALID and "L must be" in _err(L)
+    assert call(stride=100) == vc.VC_ERR_INVALID
+    assert call(kp=0) == vc.VC_ERR_INVALID
+    assert call(dt=vc.VC_F16) == vc.VC_ERR_INVALID
+    assert call(Hq=5) == vc.VC_ERR_INVALID
+    assert call(Hq=18) == vc.VC_ERR_UNSUPPORTED
+    assert call(dt=vc.VC_F32, host=1, chunk=1024) == vc.VC_ERR_UNSUPPORTED
+    assert call(host=1, chunk=16) == vc.VC_ERR_INVALID
+    assert call(ws_bytes=64) == vc.VC_ERR_WORKSPACE
+
+
+def test_merge_and_accept_reject(L):
+    assert L.vc_lse_merge(P, P, 10, 0, 128, P, None, None) == vc.VC_ERR_INVALID
+    assert L.vc_lse_merge(P, P, 10, 5000, 128, P, None, None) == vc.VC_ERR_INVALID
+    assert L.vc_lse_merge(P, P, 10, 4, 64, P, None, None) == vc.VC_ERR_INVALID
+    assert L.vc_lse_merge(P, BAD, 10, 4, 128, P, None, None) == vc.VC_ERR_INVALID
+    assert L.vc_accept(P, P, 1, 65, 10, P, P, None, None) == vc.VC_ERR_INVALID
+    assert L.vc_accept(P, None, 1, 9, 10, P, P, None, None) == vc.VC_ERR_INVALID
+    assert L.vc_accept(P, P, 0, 9, 10, P, P, None, None) == vc.VC_ERR_INVALID
+    assert L.vc_accept(P, P, 1, 9, 0, P, P, None, None) == vc.VC_ERR_INVALID
+
+
+def test_workspace_queries_grow_with_work(L):
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.vc_verify_workspace(8, 32, 8, 31, 32768, 0, 0, vc.VC_BF16, ctypes.byref(a)) == vc.VC_OK
+    assert L.vc_verify_workspace(1, 32, 8, 31, 500000, 1, 65536, vc.VC_BF16, ctypes.byref(b)) == vc.VC_OK
+    assert b.value > 2 * 8 * 65536 * 128 * 2 * 2  # two chunk stages of keys + values
+    assert L.vc_draft_drop_workspace(4, 8, 64, 25000, ctypes.byref(a)) == vc.VC_OK and a.value > 4096

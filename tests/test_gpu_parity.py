@@ -1,0 +1,429 @@
+"""GPU parity of every libvc entry point against the CPU oracle, element by element.
+
+Bars (the path's stated tolerances): bf16 attention outputs within 2e-2 absolute; fp32 outputs
+within 1e-3 of the largest reference magnitude (norm-wise relative); codes, metadata bits, argmax,
+accept lengths and emitted tokens bit-exact, except token rows whose oracle top-2 logit gap is below
+1e-3. A tighter per-kernel bound derived from each kernel's arithmetic is asserted too (see TIGHT),
+so that a small bug cannot hide under the loose bar.
+
+Sizes span several tiles, splits and ragged tails while the float64 oracle finishes in seconds.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compressed_amd import harness, synth, vc
+from oracle import accept as oacc
+from oracle import attention as oatt
+from oracle import quant as oq
+from oracle.round import Round
+
+pytestmark = pytest.mark.gpu
+
+GAP = 1e-3
+# Tight bounds from the arithmetic: fp32 accumulation, fp16 operands with hi/lo splits on the score
+# side and an 11-bit (draft) or ~16-bit (verify/drop) softmax weight on the value side. Outputs
+# are weighted means of O(1) values, so the weight rounding bounds the error at ~2^-11 of max|v|.
+TIGHT = {"draft_quant": 2e-3, "draft_drop": 5e-4, "verify": 5e-4}
+
+W_SMALL = {
+    "c1": synth.WORKLOADS["c1"],
+    "c2s": synth.WORKLOADS["c2"].with_(B=2, n=1500),
+    "c2g8": synth.WORKLOADS["c2"].with_(B=1, Hq=64, n=1200, x=5),
+    "c4s": synth.WORKLOADS["c4"].with_(n=5000, chunk_tokens=1024),
+    "c3s": synth.WORKLOADS["c3"].with_(B=2, n=4000),
+}
+
+
+def _inputs(w, seed=0):
+    K, V = synth.kv_past(w, seed)
+    Kn, Vn = synth.kv_new(w, seed)
+    return K, V, Kn, Vn, synth.q_new(w, seed), synth.projection(w, seed)
+
+
+def _close(got, ref, bf16, tight, what):
+    err = float(np.abs(np.asarray(got, np.float64) - ref).max())
+    scale = float(np.abs(ref).max())
+    print(f"[{what}] max|err| = {err:.3e} (max|ref| = {scale:.3e})", flush=True)
+    if bf16:
+        assert err <= 2e-2, what
+    else:
+        assert err <= 1e-3 * scale, what
+    assert err <= tight * max(1.0, scale), f"{what}: above the arithmetic bound"
+    return err
+
+
+# ------------------------------------------------------------------------------------------
+# accept
+# ------------------------------------------------------------------------------------------
+def test_accept_worked_example(gpu_lib):
+    drafts = np.arange(8, dtype=np.int32)[None]                  # A..H
+    verified = [0, 1, 2, 3, 4, 23, 6, 7, 5]                      # A B C D E X ...
+    Z = np.random.default_rng(0).standard_normal((1, 9, 32)).astype(np.float32)
+    for i, t in enumerate(verified):
+        Z[0, i, t] = 10.0
+    z = torch.from_numpy(Z).cuda()
+    a = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nx = torch.zeros_like(a)
+    am = torch.zeros((1, 9), dtype=torch.int32, device="cuda")
+    vc.vc_accept(z, torch.from_numpy(drafts).cuda(), a, nx, am)
+    assert a.item() == 5 and nx.item() == 23
+    assert am.cpu().numpy()[0].tolist() == verified
+
+
+@pytest.mark.parametrize("B,L,V", [(1, 9, 2048), (8, 31, 2048), (16, 31, 32000), (3, 5, 2047), (8, 1, 2048)])
+def test_accept_random(gpu_lib, B, L, V):
+    g = np.random.default_rng(B * 100 + L)
+    Z = g.standard_normal((B, L, V)).astype(np.float32)
+    # plant exact ties and coarse logits so that ties are common
+    Z[:, :, V // 3] = Z.max(axis=2) + 1.0
+    Z[:, :, V // 2] = Z[:, :, V // 3]
+    Z[1::2] = np.round(Z[1::2])
+    ref_arg = oacc.argmax_rows(Z)
+    drafts = ref_arg[:, :-1].copy()
+    for b in range(B):                       # a random first disagreement (or none)
+        k = int(g.integers(0, L))
+        if k < L - 1:
+            drafts[b, k] = (drafts[b, k] + 1) % V
+    drafts = drafts.astype(np.int32)
+    a = torch.zeros(B, dtype=torch.int32, device="cuda")
+    nx = torch.zeros_like(a)
+    am = torch.zeros((B, L), dtype=torch.int32, device="cuda")
+    vc.vc_accept(torch.from_numpy(Z).cuda(), torch.from_numpy(drafts).cuda() if L > 1 else None, a, nx, am)
+    assert np.array_equal(am.cpu().numpy(), ref_arg)
+    for b in range(B):
+        ra, rn, _ = oacc.accept(drafts[b], ref_arg[b])
+        assert a[b].item() == ra and nx[b].item() == rn
+
+
+# ------------------------------------------------------------------------------------------
+# merge
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("S", [1, 7, 300])
+def test_lse_merge(gpu_lib, S):
+    g = np.random.default_rng(S)
+    rows = 37
+    po = g.standard_normal((rows, S, 128)).astype(np.float32)
+    m = (g.standard_normal((rows, S)) * 5).astype(np.float32)
+    l = g.uniform(0.5, 50, (rows, S)).astype(np.float32)
+    empty = g.random((rows, S)) < 0.3
+    m[empty], l[empty], po[empty] = -np.inf, 0.0, 0.0
+    m[3], l[3], po[3] = -np.inf, 0.0, 0.0                       # a row with no live split
+    ml = np.stack([m, l], axis=2).astype(np.float32)
+    out = torch.zeros((rows, 128), device="cuda")
+    lse = torch.zeros(rows, device="cuda")
+    vc.vc_lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(ml).cuda(), out, lse)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for r in range(rows):
+        ro, rl = oatt.lse_merge([(po[r, s].astype(np.float64), float(m[r, s]), float(l[r, s])) for s in range(S)])
+        if rl == -np.inf:
+            assert lse[r] == -np.inf and np.all(out[r] == 0)
+        else:
+            assert np.allclose(out[r], ro, rtol=1e-5, atol=1e-6) and abs(lse[r] - rl) < 1e-5
+
+
+# ------------------------------------------------------------------------------------------
+# quantisation and residual
+# ------------------------------------------------------------------------------------------
+def _cache_for(w):
+    return vc.KiviCache(w.B, w.Hkv, max(w.n_q, 32), w.bits, vc.VC_F16 if w.meta_dtype == "f16" else vc.VC_F32,
+                        vc.VC_F16 if w.res_dtype == "f16" else vc.VC_F32, w.res_cap, "cuda")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2s", "c4s"])
+def test_quantize_bit_exact(gpu_lib, name):
+    w = W_SMALL[name]
+    K, V = synth.kv_past(w)
+    tdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    c = _cache_for(w)
+    Kd, Vd = torch.from_numpy(K).to("cuda", tdt), torch.from_numpy(V).to("cuda", tdt)
+    vc.vc_quantize_kv(c, Kd, Vd, 0, w.n_q)
+    torch.cuda.synchronize()
+    mdt = np.float16 if w.meta_dtype == "f16" else np.float32
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kc, ks, km = oq.quantize_k(K[b, h, :w.n_q], w.bits, w.meta_dtype)
+            vcod, vs, vm = oq.quantize_v(V[b, h, :w.n_q], w.bits, w.meta_dtype)
+            assert np.array_equal(c.k_codes[b, h, :w.n_q].cpu().numpy(), oq.pack_codes(kc, w.bits, "k"))
+            assert np.array_equal(c.v_codes[b, h, :w.n_q].cpu().numpy(), oq.pack_codes(vcod, w.bits, "v"))
+            gk = c.k_meta[b, h, :w.n_q // 32].cpu().numpy()
+            gv = c.v_meta[b, h, :w.n_q].cpu().numpy()
+            assert np.array_equal(gk[..., 0], ks.astype(mdt)) and np.array_equal(gk[..., 1], km.astype(mdt))
+            assert np.array_equal(gv[..., 0], vs.astype(mdt)) and np.array_equal(gv[..., 1], vm.astype(mdt))
+
+
+def test_quantize_extreme_groups(gpu_lib):
+    """Constant groups, on-grid groups, huge and tiny magnitudes, negative zeros: codes and
+    metadata bit-exact (fp16 directed rounding and scale 0 paths)."""
+    g = np.random.default_rng(5)
+    T = 128
+    K = g.standard_normal((1, 1, T, 128)).astype(np.float32)
+    K[0, 0, :32, :8] = 0.375                       # constant per-channel groups
+    K[0, 0, 32:64] *= 1e-6                          # tiny
+    K[0, 0, 64:96] *= 3000.0                        # large
+    K[0, 0, 96:, 5] = -0.0
+    V = K.copy()
+    V[0, 0, :, :32] = 2.5                           # constant per-token groups
+    for meta in ("f16", "f32"):
+        for bits in (2, 4):
+            c = vc.KiviCache(1, 1, T, bits, vc.VC_F16 if meta == "f16" else vc.VC_F32, vc.VC_F32, 32, "cuda")
+            vc.vc_quantize_kv(c, torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), 0, T)
+            torch.cuda.synchronize()
+            kc, ks, km = oq.quantize_k(K[0, 0], bits, meta)
+            vcod, vs, vm = oq.quantize_v(V[0, 0], bits, meta)
+            mdt = np.float16 if meta == "f16" else np.float32
+            assert np.array_equal(c.k_codes[0, 0].cpu().numpy(), oq.pack_codes(kc, bits, "k"))
+            assert np.array_equal(c.v_codes[0, 0].cpu().numpy(), oq.pack_codes(vcod, bits, "v"))
+            assert np.array_equal(c.k_meta[0, 0, ..., 0].cpu().numpy(), ks.astype(mdt))
+            assert np.array_equal(c.k_meta[0, 0, ..., 1].cpu().numpy(), km.astype(mdt))
+            assert np.array_equal(c.v_meta[0, 0, ..., 0].cpu().numpy(), vs.astype(mdt))
+            assert np.array_equal(c.v_meta[0, 0, ..., 1].cpu().numpy(), vm.astype(mdt))
+
+
+def test_append_ring_and_flush(gpu_lib):
+    """Residual appends wrap around the ring with round-half-even storage; a flush quantises 32
+    ring tokens exactly as the oracle quantises the same stored values."""
+    w = W_SMALL["c2s"]
+    g = np.random.default_rng(6)
+    X = synth.round_bf16(g.standard_normal((w.B, w.Hkv, 300, 128)).astype(np.float32))
+    Y = synth.round_bf16(g.standard_normal((w.B, w.Hkv, 300, 128)).astype(np.float32))
+    c = vc.KiviCache(w.B, w.Hkv, 512, 2, vc.VC_F16, vc.VC_F16, 256, "cuda")
+    Xd, Yd = torch.from_numpy(X).to("cuda", torch.bfloat16), torch.from_numpy(Y).to("cuda", torch.bfloat16)
+    t0 = 200                                          # tokens 200..499 -> slots wrap at 256
+    vc.vc_kivi_append(c, Xd[:, :, :100], Yd[:, :, :100], t0, 100, src_bh_stride=300 * 128)
+    vc.vc_kivi_append(c, Xd[:, :, 100:], Yd[:, :, 100:], t0 + 100, 200, src_bh_stride=300 * 128)
+    torch.cuda.synchronize()
+    ring = c.k_res.cpu().numpy()
+    for t in range(300):
+        slot = (t0 + t) % 256
+        if t >= 300 - 256:                             # still present (not overwritten)
+            assert np.array_equal(ring[:, :, slot].astype(np.float64), oq.to_res(X[:, :, t], "f16"))
+    # flush tokens 480..511 (ring slots 224..255) into quantised group 15
+    src = c.k_res[:, :, 224:256]
+    srcv = c.v_res[:, :, 224:256]
+    vc.vc_quantize_kv(c, src, srcv, 480, 32, src_bh_stride=256 * 128)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            vals = c.k_res[b, h, 224:256].float().cpu().numpy()
+            kc, ks, km = oq.quantize_k(vals, 2, "f16")
+            assert np.array_equal(c.k_codes[b, h, 480:512].cpu().numpy(), oq.pack_codes(kc, 2, "k"))
+            assert np.array_equal(c.k_meta[b, h, 15, :, 0].cpu().numpy(), ks.astype(np.float16))
+
+
+# ------------------------------------------------------------------------------------------
+# draft attention
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["c1", "c2s", "c2g8", "c4s"])
+def test_draft_quant_parity(gpu_lib, name):
+    w = W_SMALL[name]
+    inp = _inputs(w)
+    st = harness.RoundState(w, inputs=inp)
+    rnd = Round(w, *inp)
+    bf16 = w.kv_dtype == "bf16"
+    for j in range(w.x):
+        st.append_draft_entry(j)
+        st.draft_attention(j)
+    res = st.results()
+    for j in sorted({0, w.x // 2, w.x - 1}):
+        for b in range(w.B):
+            O, lse = rnd.draft_step(b, j)
+            _close(res["out_d"][j, b], O, bf16, TIGHT["draft_quant"], f"{name} draft j={j} b={b}")
+            _close(res["lse_d"][j, b], lse, bf16, TIGHT["draft_quant"], f"{name} draft lse j={j} b={b}")
+
+
+@pytest.mark.parametrize("n_q_zero", [True, False])
+def test_draft_quant_edges(gpu_lib, n_q_zero):
+    """Residual only (nothing quantised) and quantised only (empty residual)."""
+    base = synth.WORKLOADS["c2"].with_(B=1, x=2)
+    w = base.with_(n=100, R=128) if n_q_zero else base.with_(n=1024, R=0)
+    inp = _inputs(w)
+    K, V, Kn, Vn, Q, W = inp
+    c = _cache_for(w)
+    Kd, Vd = torch.from_numpy(K).to("cuda", torch.bfloat16), torch.from_numpy(V).to("cuda", torch.bfloat16)
+    vc.vc_quantize_kv(c, Kd, Vd, 0, w.n_q)
+    if w.n > w.n_q:
+        vc.vc_kivi_append(c, Kd[:, :, w.n_q:], Vd[:, :, w.n_q:], w.n_q, w.n - w.n_q, src_bh_stride=w.n * 128)
+    q = torch.from_numpy(Q[:, :, 0]).to("cuda", torch.bfloat16).contiguous()
+    out = torch.zeros((w.B, w.Hq, 128), device="cuda")
+    lse = torch.zeros((w.B, w.Hq), device="cuda")
+    r = w.n - w.n_q
+    ws = torch.zeros(vc.vc_draft_quant_workspace(c, w.n_q, r, w.Hq), dtype=torch.uint8, device="cuda")
+    vc.vc_draft_attn_quant(c, w.n_q, r, q, out, lse, ws, harness.SM_SCALE)
+    torch.cuda.synchronize()
+    for h in range(w.Hq):
+        lay = oq.KiviLayer(K[0, h // w.G], V[0, h // w.G], w.n_q, w.bits, w.meta_dtype, w.res_dtype)
+        o, l = oatt.decode(Q[0, h, 0], lay.keys(r), lay.values(r))
+        _close(out[0, h].cpu().numpy(), o, True, TIGHT["draft_quant"], f"edge n_q={w.n_q} h={h}")
+        assert abs(lse[0, h].item() - l) < 2e-3
+
+
+@pytest.mark.parametrize("name", ["c3s"])
+def test_draft_drop_parity(gpu_lib, name):
+    w = W_SMALL[name]
+    inp = _inputs(w)
+    idx = [[synth.keep_list(w, 0, b, h) for h in range(w.Hkv)] for b in range(w.B)]
+    st = harness.RoundState(w, inputs=inp, idx_lists=idx)
+    rnd = Round(w, *inp, idx=idx)
+    for j in range(w.x):
+        st.draft_attention(j)
+    res = st.results()
+    for j in sorted({0, 13, w.x - 1}):
+        for b in range(w.B):
+            O, lse = rnd.draft_step(b, j)
+            _close(res["out_d"][j, b], O, True, TIGHT["draft_drop"], f"{name} drop j={j} b={b}")
+            _close(res["lse_d"][j, b], lse, True, TIGHT["draft_drop"], f"{name} drop lse j={j} b={b}")
+
+
+def test_draft_drop_keep_all_and_invalid_entries(gpu_lib):
+    """Keep-all equals full attention; entries outside [0, tok_cap) contribute nothing; a ragged
+    n_keep (not a multiple of 32) is honoured."""
+    w = synth.WORKLOADS["c3"].with_(B=1, Hkv=2, Hq=16, n=777, x=1)
+    K, V, Kn, Vn, Q, W = _inputs(w)
+    cap = 800
+    Kd = torch.zeros((1, 2, cap, 128), dtype=torch.bfloat16, device="cuda")
+    Vd = torch.zeros_like(Kd)
+    Kd[:, :, :777] = torch.from_numpy(K).to("cuda", torch.bfloat16)
+    Vd[:, :, :777] = torch.from_numpy(V).to("cuda", torch.bfloat16)
+    idx = np.tile(np.arange(777, dtype=np.int32), (1, 2, 1))
+    bad = idx.copy()
+    bad = np.concatenate([bad, np.full((1, 2, 5), -3, np.int32), np.full((1, 2, 5), 10 ** 6, np.int32)], axis=2)
+    q = torch.from_numpy(Q[:, :, 0]).to("cuda", torch.bfloat16).contiguous()
+    for ilist in (idx, bad):
+        out = torch.zeros((1, 16, 128), device="cuda")
+        n_keep = ilist.shape[2]
+        ws = torch.zeros(vc.vc_draft_drop_workspace(1, 2, 16, n_keep), dtype=torch.uint8, device="cuda")
+        vc.vc_draft_attn_drop(Kd, Vd, torch.from_numpy(ilist).cuda(), n_keep, q, out, None, ws, harness.SM_SCALE)
+        torch.cuda.synchronize()
+        for h in range(16):
+            o, _ = oatt.decode(Q[0, h, 0], K[0, h // 8], V[0, h // 8])
+            _close(out[0, h].cpu().numpy(), o, True, TIGHT["draft_drop"], f"keep-all h={h}")
+
+
+# ------------------------------------------------------------------------------------------
+# verify
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s"])
+def test_verify_parity(gpu_lib, name):
+    w = W_SMALL[name]
+    inp = _inputs(w)
+    idx = [[synth.keep_list(w, 0, b, h) for h in range(w.Hkv)] for b in range(w.B)] if w.drafter == "drop" else None
+    st = harness.RoundState(w, inputs=inp, idx_lists=idx)
+    rnd = Round(w, *inp, idx=idx)
+    st.verify_attention()
+    res = st.results()
+    bf16 = w.kv_dtype == "bf16"
+    for b in range(w.B):
+        for hq in sorted({0, w.Hq // 2 + 1, w.Hq - 1}):
+            O, lse = rnd.verify_head(b, hq)
+            _close(res["out_v"][b, hq], O, bf16, TIGHT["verify"], f"{name} verify b={b} h={hq}")
+            _close(res["lse_v"][b, hq], lse, bf16, TIGHT["verify"], f"{name} verify lse b={b} h={hq}")
+
+
+@pytest.mark.parametrize("n,L", [(0, 31), (1, 1), (33, 32), (1000, 9), (4096, 31)])
+def test_verify_shapes(gpu_lib, n, L):
+    w = synth.WORKLOADS["c2"].with_(B=2, Hq=8, Hkv=2, n=n, x=L - 1)
+    K, V, Kn, Vn, Q, W = _inputs(w)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", torch.bfloat16)
+    out = torch.zeros((2, 8, L, 128), device="cuda")
+    lse = torch.zeros((2, 8, L), device="cuda")
+    nb = vc.vc_verify_workspace(2, 8, 2, L, n, False, 0, vc.VC_BF16)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    kp = dev(K) if n else dev(np.zeros((2, 2, 1, 128), np.float32))
+    vp = dev(V) if n else kp
+    vc.vc_verify_attn(dev(Q), dev(Kn), dev(Vn), kp, vp, n, out, lse, ws, harness.SM_SCALE,
+                      past_stride=max(n, 1))
+    torch.cuda.synchronize()
+    for b in range(2):
+        for hq in range(8):
+            O, l = oatt.verify_block(Q[b, hq], K[b, hq // 4], V[b, hq // 4], Kn[b, hq // 4], Vn[b, hq // 4])
+            _close(out[b, hq].cpu().numpy(), O, True, TIGHT["verify"], f"verify n={n} L={L} b={b} h={hq}")
+
+
+def test_verify_streamed_equals_resident(gpu_lib):
+    """Host-streamed past (pinned, small chunks: many stage flips and a partial last chunk) gives the
+    oracle's result, and the resident path gives the same numbers within fp32 reassociation."""
+    w = W_SMALL["c4s"].with_(chunk_tokens=320)
+    inp = _inputs(w)
+    st = harness.RoundState(w, inputs=inp)
+    st.verify_attention()
+    streamed = st.results()
+    K, V, Kn, Vn, Q, W = inp
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", torch.bfloat16)
+    out = torch.zeros_like(st.out_v)
+    lse = torch.zeros_like(st.lse_v)
+    ws = torch.zeros(vc.vc_verify_workspace(1, 32, 8, 31, w.n, False, 0, vc.VC_BF16), dtype=torch.uint8, device="cuda")
+    vc.vc_verify_attn(st.q_verify, st.k_blk, st.v_blk, dev(K), dev(V), w.n, out, lse, ws, harness.SM_SCALE)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().numpy() - streamed["out_v"]).max() < 1e-5
+    rnd = Round(w, *inp)
+    for hq in (0, 17, 31):
+        O, l = rnd.verify_head(0, hq)
+        _close(streamed["out_v"][0, hq], O, True, TIGHT["verify"], f"streamed h={hq}")
+
+
+def test_pageable_host_past_is_rejected(gpu_lib):
+    w = W_SMALL["c4s"]
+    q = torch.zeros((1, 32, 31, 128), dtype=torch.bfloat16, device="cuda")
+    kb = torch.zeros((1, 8, 31, 128), dtype=torch.bfloat16, device="cuda")
+    host = torch.zeros((1, 8, 64, 128), dtype=torch.bfloat16)       # pageable
+    out = torch.zeros((1, 32, 31, 128), device="cuda")
+    ws = torch.zeros(vc.vc_verify_workspace(1, 32, 8, 31, 64, True, 32, vc.VC_BF16), dtype=torch.uint8, device="cuda")
+    with pytest.raises(vc.VcError) as e:
+        vc.vc_verify_attn(q, kb, kb, host, host, 64, out, None, ws, harness.SM_SCALE, past_on_host=True,
+                          chunk_tokens=32)
+    assert e.value.status == vc.VC_ERR_INVALID
+
+
+# ------------------------------------------------------------------------------------------
+# whole rounds: emitted tokens
+# ------------------------------------------------------------------------------------------
+def _check_tokens(gpu, ref_rounds, w):
+    exempt = 0
+    for b, ref in enumerate(ref_rounds):
+        dmask = ref["draft_gap"] >= GAP
+        vmask = ref["verify_gap"] >= GAP
+        exempt += int((~dmask).sum() + (~vmask).sum())
+        assert np.array_equal(gpu["drafts"][b][dmask], ref["drafts"][dmask]), f"draft tokens b={b}"
+        assert np.array_equal(gpu["verified"][b][vmask], ref["verified"][vmask]), f"verify argmax b={b}"
+        a, nxt, _ = oacc.accept(gpu["drafts"][b], gpu["verified"][b])
+        assert gpu["a"][b] == a and gpu["next"][b] == nxt
+        if dmask[: ref["a"] + 1].all() and vmask[: ref["a"] + 1].all():
+            assert gpu["a"][b] == ref["a"] and gpu["next"][b] == ref["next"]
+    return exempt
+
+
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s"])
+def test_round_tokens(gpu_lib, name):
+    w = W_SMALL[name]
+    inp = _inputs(w)
+    idx = [[synth.keep_list(w, 0, b, h) for h in range(w.Hkv)] for b in range(w.B)] if w.drafter == "drop" else None
+    st = harness.RoundState(w, inputs=inp, idx_lists=idx)
+    st.run_round()
+    gpu = st.results()
+    rnd = Round(w, *inp, idx=idx)
+    refs = [rnd.run(b) for b in range(w.B)]
+    exempt = _check_tokens(gpu, refs, w)
+    acc = [int(a) for a in gpu["a"]]
+    print(f"[{name}] accepted {acc} of x={w.x}; exempt rows {exempt}", flush=True)
+
+
+def test_uncompressed_drafter_round_accepts_everything(gpu_lib):
+    """KIVI drafter with nothing quantised (R >= n): the GPU drafter reads exactly what the verifier
+    reads, so every draft must be accepted (the pages' same-weights argument)."""
+    w = synth.WORKLOADS["c1"].with_(n=200, R=256, res_cap=256)
+    st = harness.RoundState(w)
+    st.run_round()
+    gpu = st.results()
+    assert np.all(gpu["a"] == w.x)
+
+
+def test_deterministic(gpu_lib):
+    w = W_SMALL["c2s"]
+    st = harness.RoundState(w)
+    st.run_round()
+    r1 = st.results()
+    st.run_round()
+    r2 = st.results()
+    for k in ("out_d", "lse_d", "out_v", "lse_v", "drafts", "verified", "a", "next"):
+        assert np.array_equal(r1[k], r2[k]), k
