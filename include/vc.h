@@ -86,7 +86,7 @@ typedef struct vc_kivi {
   int64_t tok_cap;    /* quantised-token capacity per (b, h); multiple of 32            */
   void *k_codes;      /* [B][Hkv][tok_cap][128*bits/8] uint8, layout above              */
   void *v_codes;      /* [B][Hkv][tok_cap][128*bits/8] uint8, layout above              */
-  void *k_meta;       /* [B][Hkv][tok_cap/32][128][2] (scale, min) in meta_dtype         */
+  void *k_meta;       /* [B][Hkv][tok_cap/32][2][128]: per group 128 scales then 128 mins */
   void *v_meta;       /* [B][Hkv][tok_cap][4][2]      (scale, min) in meta_dtype         */
   void *k_res;        /* [B][Hkv][res_cap][128] in res_dtype; token t in slot t % res_cap */
   void *v_res;        /* [B][Hkv][res_cap][128] in res_dtype                             */
@@ -122,9 +122,8 @@ vc_status vc_kivi_append(const vc_kivi *c, const void *k, const void *v, int32_t
  *   out  [B][Hq][128] fp32, device;  lse [B][Hq] fp32 or NULL
  *   n_q  multiple of 32, <= tok_cap;  0 <= r <= res_cap;  n_q + r >= 1;  Hq % Hkv == 0,
  *        Hq/Hkv <= 8
- *   ws   device workspace of vc_draft_quant_workspace() bytes. Its first 4096 bytes are ticket
- *        counters that must be zero before first use; every completed call leaves them zero.
- *        Calls that overlap in time must not share a workspace.
+ *   ws   device workspace of vc_draft_quant_workspace() bytes (split partials; contents need no
+ *        initialisation). Calls that overlap in time must not share a workspace.
  */
 vc_status vc_draft_attn_quant(const vc_kivi *c, int64_t n_q, int32_t r, const void *q,
                               int32_t q_dtype, int32_t Hq, float sm_scale, float *out, float *lse,

@@ -145,8 +145,6 @@ vc_status vc_draft_attn_quant(const vc_kivi* c, int64_t n_q, int32_t r, const vo
   REQUIRE_PTR(out);
   if (Hq / c->Hkv > 8) return fail(VC_ERR_UNSUPPORTED, "Hq/Hkv > 8 is not supported");
   if (c->res_cap > 512) return fail(VC_ERR_UNSUPPORTED, "res_cap > 512 is not supported");
-  if ((int64_t)c->B * c->Hkv > vc::COUNTER_BYTES / 4)
-    return fail(VC_ERR_UNSUPPORTED, "B*Hkv > %d is not supported", vc::COUNTER_BYTES / 4);
   const vc::DraftQuantPlan plan = vc::plan_draft_quant(*c, n_q, Hq);
   if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
     return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,
@@ -182,8 +180,6 @@ vc_status vc_draft_attn_drop(const void* k, const void* v, int32_t kv_dtype, int
   REQUIRE((int64_t)B * Hkv <= 65535, "B*Hkv must be <= 65535");
   if (kv_dtype != VC_BF16) return fail(VC_ERR_UNSUPPORTED, "only VC_BF16 keys/values are supported");
   if (Hq / Hkv > 8) return fail(VC_ERR_UNSUPPORTED, "Hq/Hkv > 8 is not supported");
-  if ((int64_t)B * Hkv > vc::COUNTER_BYTES / 4)
-    return fail(VC_ERR_UNSUPPORTED, "B*Hkv > %d is not supported", vc::COUNTER_BYTES / 4);
   const vc::DraftDropPlan plan = vc::plan_draft_drop(B, Hkv, Hq, n_keep);
   if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
     return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,

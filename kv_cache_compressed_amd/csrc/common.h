@@ -19,7 +19,6 @@ constexpr int D = 128;          // head dimension
 constexpr int GROUP = 32;       // KIVI group size
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr int COUNTER_BYTES = 4096;  // ticket counters at the head of a draft workspace
 
 // ---------------------------------------------------------------------------------------------
 // scalar conversions
@@ -59,9 +58,53 @@ __device__ __forceinline__ float f16_round_up(float x) {
   return (float)h;
 }
 
-// Pack two floats into an f16x2 word (round to nearest even).
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Pack two floats into an f16x2 word, round to nearest even (one v_cvt_pk_f16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  return (uint32_t)f16_bits((f16)lo) | ((uint32_t)f16_bits((f16)hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t{lo, hi}), half2_t));
+}
+
+// ---------------------------------------------------------------------------------------------
+// mixed-precision FMAs (v_fma_mix*): f32 operands combined with fp16 halves of packed words,
+// results written straight into fp16 halves. Word b holds an fp16 pair (lo, hi).
+// ---------------------------------------------------------------------------------------------
+// (fp16(a0 * b0.lo), fp16(a1 * b1.lo)) as one packed word
+__device__ __forceinline__ uint32_t mix_mul_pair(float a0, uint32_t b0, float a1, uint32_t b1) {
+  uint32_t d;  // the low half is written first, the high half second
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=&v"(d) : "v"(a0), "v"(b0));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(d) : "v"(a1), "v"(b1));
+  return d;
+}
+// (fp16(a0 * b0.lo - h.lo), fp16(a1 * b1.lo - h.hi)): the rounding remainders of mix_mul_pair
+__device__ __forceinline__ uint32_t mix_rem_pair(float a0, uint32_t b0, float a1, uint32_t b1,
+                                                 uint32_t h) {
+  uint32_t d;
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,1,1]" : "=&v"(d) : "v"(a0), "v"(b0), "v"(h));
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]"
+      : "+v"(d) : "v"(a1), "v"(b1), "v"(h));
+  return d;
+}
+// (fp16(a0 * w.lo), fp16(a1 * w.hi)) for a packed fp16 pair w
+__device__ __forceinline__ uint32_t mix_mul2(float a0, float a1, uint32_t w) {
+  uint32_t d;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=&v"(d) : "v"(a0), "v"(w));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(d) : "v"(a1), "v"(w));
+  return d;
+}
+// (fp16(a0 * w.lo - h.lo), fp16(a1 * w.hi - h.hi)): the rounding remainders of mix_mul2
+__device__ __forceinline__ uint32_t mix_rem2(float a0, float a1, uint32_t w, uint32_t h) {
+  uint32_t d;
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,1,1]" : "=&v"(d) : "v"(a0), "v"(w), "v"(h));
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
+      : "+v"(d) : "v"(a1), "v"(w), "v"(h));
+  return d;
+}
+// acc + a * b.hi
+__device__ __forceinline__ float mix_fma_hi(float a, uint32_t b, float acc) {
+  asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(acc) : "v"(a), "v"(b));
+  return acc;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -73,14 +116,20 @@ __device__ __forceinline__ float dpp_xor1(float x) {
 }
 __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
-// Reductions over the four 16-lane rows that hold the same column (lanes l, l^16, l^32, l^48).
+// Reductions over the four 16-lane rows that hold the same column (lanes l, l^16, l^32, l^48),
+// with gfx950's row-swap permutes (no LDS round trip): permlane16_swap(x, x) returns x with odd and
+// even rows exchanged between its two results, permlane32_swap likewise for the two wave halves.
 __device__ __forceinline__ float max_over_rows(float x) {
-  x = fmaxf(x, shfl_xor(x, 16));
-  return fmaxf(x, shfl_xor(x, 32));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_over_rows(float x) {
-  x += shfl_xor(x, 16);
-  return x + shfl_xor(x, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 __device__ __forceinline__ float wave_max(float x) {
   for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, shfl_xor(x, m));

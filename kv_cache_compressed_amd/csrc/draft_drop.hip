@@ -12,7 +12,7 @@
 // per-wave LDS tile transposed to channel-major token pairs. QK^T and PV run on
 // v_mfma_f32_16x16x32_bf16; columns j = 2h + hl carry query head h twice so that the PV product
 // can take the softmax weight as a bf16 hi (hl = 0) + lo (hl = 1) pair without moving data across
-// lanes. Split partials are merged by the last workgroup of each (b, kv head) (ticket counter).
+// lanes. Split partials are merged by a small second kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,7 +34,6 @@ struct DDArgs {
   float* lse;
   float* part_o;
   float* part_ml;
-  unsigned* counters;
   int64_t tok_cap, n_keep, idx_cap;
   int Hkv, Hq, G, splits;
   float qscale;
@@ -44,7 +43,6 @@ __global__ void __launch_bounds__(THREADS) draft_drop_kernel(DDArgs a) {
   // per-wave transposed value tiles; reused for the cross-wave merge after the main loop
   __shared__ uint32_t s_raw[WAVES * D * VT_STRIDE];
   __shared__ float s_m[WAVES][8], s_l[WAVES][8];
-  __shared__ int s_last;
   float(*s_o)[8][D] = reinterpret_cast<float(*)[8][D]>(s_raw);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -138,14 +136,14 @@ __global__ void __launch_bounds__(THREADS) draft_drop_kernel(DDArgs a) {
     }
     mx = max_over_rows(mx);
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
     uint32_t pw[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      float p0 = (m_new == -INFINITY) ? 0.f : exp2f(sc[e] - m_new);
-      float p1 = (m_new == -INFINITY) ? 0.f : exp2f(sc[e + 1] - m_new);
+      float p0 = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[e] - m_new);
+      float p1 = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[e + 1] - m_new);
       psum += p0 + p1;
       const float h0 = __uint_as_float(__float_as_uint(p0) & 0xffff0000u);
       const float h1 = __uint_as_float(__float_as_uint(p1) & 0xffff0000u);
@@ -214,19 +212,6 @@ __global__ void __launch_bounds__(THREADS) draft_drop_kernel(DDArgs a) {
     }
   }
 
-  // ---- ticket: the last split of this (b, kv head) merges -----------------------------------
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(a.counters + bh, 1u) == (unsigned)(a.splits - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int hh = wave; hh < a.G; hh += WAVES) {
-    const int64_t row = (int64_t)b * a.Hq + kvh * a.G + hh;
-    merge_row_wave(a.part_o + row * a.splits * D, a.part_ml + row * a.splits * 2, a.splits,
-                   a.out + row * D, a.lse ? a.lse + row : nullptr);
-  }
-  if (tid == 0) a.counters[bh] = 0u;
 }
 
 }  // namespace
@@ -235,10 +220,10 @@ DraftDropPlan plan_draft_drop(int B, int Hkv, int Hq, int64_t n_keep) {
   DraftDropPlan p;
   const int64_t units = (int64_t)B * Hkv;
   const int64_t nblk = (n_keep + BLK - 1) / BLK;
-  int64_t s = (1024 + units - 1) / units;
+  int64_t s = std::max<int64_t>(1, 512 / units);  // one resident round at 2 workgroups per CU
   s = std::min<int64_t>(s, std::max<int64_t>(1, nblk / 8));
   p.splits = (int)std::max<int64_t>(1, s);
-  p.ws_bytes = COUNTER_BYTES + (size_t)B * Hq * p.splits * (D + 2) * sizeof(float);
+  p.ws_bytes = (size_t)B * Hq * p.splits * (D + 2) * sizeof(float);
   return p;
 }
 
@@ -254,9 +239,8 @@ hipError_t launch_draft_drop(const void* k, const void* v, int kv_dtype, int B, 
   a.q = static_cast<const uint16_t*>(q);
   a.out = out;
   a.lse = lse;
-  a.counters = static_cast<unsigned*>(ws);
   const size_t rows = (size_t)B * Hq;
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + COUNTER_BYTES);
+  a.part_o = static_cast<float*>(ws);
   a.part_ml = a.part_o + rows * plan.splits * D;
   a.tok_cap = tok_cap;
   a.n_keep = n_keep;
@@ -268,7 +252,9 @@ hipError_t launch_draft_drop(const void* k, const void* v, int kv_dtype, int B, 
   a.qscale = sm_scale * LOG2E;
   hipLaunchKernelGGL(draft_drop_kernel, dim3(plan.splits, (unsigned)(B * Hkv)), dim3(THREADS), 0,
                      s, a);
-  return hipGetLastError();
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_merge(a.part_o, a.part_ml, (int64_t)rows, plan.splits, out, lse, s);
 }
 
 }  // namespace vc

@@ -14,9 +14,9 @@
 // an exact fp16 operand by masking it into the mantissa of a half (a subnormal equal to
 // code * 4^p * 2^-24 for the slot position p), which costs one AND per two codes; the power of
 // four of the slot position is divided out of the other operand. The other operand (q_c s_gc in
-// the QK product, p_t s_tcg in the PV product) is prepared once per 32-token group. q s is carried
-// as an fp16 hi + lo pair in two matrix columns so that the scores keep ~22 significant bits; p s
-// is carried as one fp16 (11 bits) since the softmax weights enter the output linearly.
+// the QK product, p_t s_tcg in the PV product) is prepared once per 32-token group: q s as an fp16
+// hi + lo pair in two matrix columns (scores keep ~22 significant bits), p s as one fp16 (the
+// weights enter the output linearly).
 //
 // Work split. Workgroup = 4 waves on one (b, kv head) and one contiguous range of groups (a
 // split); wave w takes every 4th group of the range. Lane l of a wave is (column j = l % 16,
@@ -24,8 +24,12 @@
 // so up to 8 query heads share each code load. The scores of a 16-token tile come back in the
 // layout the PV product needs as its B operand, so softmax weights never cross lanes. The
 // residual tokens (n_q .. n_q+r-1, fp16/fp32 ring) form one extra split computed on the vector
-// ALUs. Each split writes an unnormalised partial (o, m, l); the last split of a (b, kv head) to
-// finish (ticket counter) merges them with log-sum-exp and writes the output.
+// ALUs. Each split writes an unnormalised partial (o, m, l); a small second kernel merges them with
+// log-sum-exp. (A fused last-workgroup merge would need device-scope fences, which on this
+// multi-XCD part write back and invalidate the L2 of every workgroup's XCD: far dearer than a
+// launch.)
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -39,6 +43,10 @@ constexpr int RES_MAX = 512;           // residual ring slots handled by the res
 constexpr float SCALE_QK = 256.0f;     // 2^8: magnitude headroom of the fp16 QK operand
 constexpr float SCALE_PV = 256.0f;     // 2^8: same for the PV operand
 constexpr float SUBNORMAL = 16777216.0f;  // 2^24: one fp16 subnormal step is 2^-24
+constexpr float LAZY = 2.0f;           // log2 slack before the running max is moved
+// LDS: residual split [q 8xD | p 8xRES_MAX | ml 16 | reduction WAVESx8xD] floats; the quantised
+// split uses it for 4 waves x 2 metadata buffers x 2 KB and, after its loop, the wave merge.
+constexpr int SMEM_FLOATS = 8 * D + 8 * RES_MAX + 16 + WAVES * 8 * D;
 
 struct DQArgs {
   const uint8_t* k_codes;
@@ -52,7 +60,6 @@ struct DQArgs {
   float* lse;
   float* part_o;
   float* part_ml;
-  unsigned* counters;
   int64_t tok_cap, n_q;
   int r, res_cap, res_dtype, q_dtype;
   int Hkv, Hq, G;
@@ -77,41 +84,55 @@ __device__ __forceinline__ u32x4 unpack4(uint32_t w) {
   return u32x4{w & 0x000F000Fu, w & 0x00F000F0u, x & 0x000F000Fu, x & 0x00F000F0u};
 }
 
-// (scale, min) of key channel c of group g.
-template <bool META_F16>
-__device__ __forceinline__ float2 kmeta(const void* base, int64_t idx) {
-  if (META_F16) {
-    const uint32_t w = static_cast<const uint32_t*>(base)[idx];
-    return make_float2(f16_bits_to_f32(w & 0xffffu), f16_bits_to_f32(w >> 16));
-  }
-  return static_cast<const float2*>(base)[idx];
-}
 
-template <int BITS, bool META_F16>
+// One split of quantised groups. Every column of a query head h carries the same scores (the
+// head's CPH columns j = CPH*h .. CPH*h + CPH-1 get identical QK operands), so no lane ever needs
+// another lane's score. q*s enters the QK product as an fp16 hi part and an fp16 lo part, in two
+// matrix products accumulated into the same registers (scores keep ~22 significant bits; a single
+// fp16 would move them by up to ~1e-3 in log2 units at outlier channels).
+//   CPH == 4 (G <= 4): PV column CPH*h + cg carries p * s_cg for value channel group cg, so one PV
+//                      operand serves all eight channel tiles (each lane prepares 8 products).
+//   CPH == 2 (G <= 8): PV uses one operand per channel group (both columns of the head alike).
+// With fp16 metadata the key bias sum_c q_c m_gc is a matrix product too: q (bf16/fp16 values are
+// exact in fp16) against the group's fp16 mins, exact products accumulated in fp32.
+template <int BITS, bool META_F16, int CPH>
 __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
-  constexpr int WPL = 2 * BITS;        // packed words per lane per block
+  constexpr int WPL = 2 * BITS;              // packed code words per lane per block
   constexpr int ROW_BYTES = D * BITS / 8;
+  constexpr int MB = META_F16 ? 512 : 1024;  // bytes of one group's key (or value) metadata
+  constexpr int MCH = META_F16 ? 1 : 2;      // 16-byte metadata chunks loaded per lane
+  constexpr int NBP = CPH == 4 ? 1 : 4;      // PV B operands per group
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, gq = lane >> 4;
-  const int h = j >> 1, hl = j & 1;
+  const int h = j / CPH, k = j % CPH;        // query head of this column, slot within the head
   const bool active = h < a.G;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int hq = kvh * a.G + h;
 
-  // Query values of this lane's 32 channels (c = 32 kb + 8 gq + e), pre-scaled to log2 units.
-  float qb[32];
+  // Query of this lane's 32 channels (c = 32 kb + 8 gq + e) in log2 units, pre-multiplied by the
+  // fp16 headroom scale and divided by the slot-position power of element e; and, for the bias
+  // product, the raw query as fp16 pairs.
+  float qs[32];
+  u32x4 qh[4];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < 4; ++kb) {
+    float qv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = 32 * kb + 8 * gq + e;
-      qb[kb * 8 + e] = active ? load_as_f32(a.q, ((int64_t)b * a.Hq + hq) * D + c, a.q_dtype) * a.qscale : 0.f;
+      qv[e] = active ? load_as_f32(a.q, ((int64_t)b * a.Hq + hq) * D + c, a.q_dtype) : 0.f;
+      qs[kb * 8 + e] = qv[e] * a.qscale * (SCALE_QK * cls_inv<BITS>(e));
     }
-  const float mk = hl ? 1.f : 0.f;  // lo lanes subtract the hi part
+    qh[kb] = u32x4{pack_f16x2(qv[0], qv[1]), pack_f16x2(qv[2], qv[3]), pack_f16x2(qv[4], qv[5]),
+                   pack_f16x2(qv[6], qv[7])};
+  }
 
   const int g_begin = (int)((int64_t)a.ngroups * split / a.splits);
   const int g_end = (int)((int64_t)a.ngroups * (split + 1) / a.splits);
   const int64_t ngcap = a.tok_cap / GROUP;
+
+  // per-wave double-buffered LDS copy of one group's key + value metadata
+  uint8_t* mbuf = reinterpret_cast<uint8_t*>(smem) + wave * (4 * MB);
 
   float m_run = -INFINITY, l_lane = 0.f;
   float bv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -119,121 +140,215 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int g = g_begin + wave; g < g_end; g += WAVES) {
+  // raw loads of one group: code words and this lane's share of the metadata
+  u32x4 kw[WPL / 4], vw[WPL / 4], mw[MCH];
+  auto load_group = [&](int g) {
     const int64_t blk = (int64_t)bh * a.tok_cap + (int64_t)g * GROUP;
-    // ---- loads --------------------------------------------------------------------------
     const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_codes + blk * ROW_BYTES) + lane * (WPL / 4);
     const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_codes + blk * ROW_BYTES) + lane * (WPL / 4);
-    uint32_t kw[WPL], vw[WPL];
 #pragma unroll
     for (int u = 0; u < WPL / 4; ++u) {
-      const u32x4 tk = __builtin_nontemporal_load(kp + u);
-      const u32x4 tv = __builtin_nontemporal_load(vp + u);
+      kw[u] = __builtin_nontemporal_load(kp + u);
+      vw[u] = __builtin_nontemporal_load(vp + u);
+    }
+    // metadata: key stats of group g (MB bytes) then value stats of its 32 tokens (MB bytes)
+    const uint8_t* kmeta = static_cast<const uint8_t*>(a.k_meta) + ((int64_t)bh * ngcap + g) * MB;
+    const uint8_t* vmeta = static_cast<const uint8_t*>(a.v_meta) + blk * (MB / GROUP);
+#pragma unroll
+    for (int z = 0; z < MCH; ++z) {
+      const int off = z * 1024 + lane * 16;  // byte offset in [key meta | value meta]
+      const uint8_t* src = off < MB ? kmeta + off : vmeta + (off - MB);
+      mw[z] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+    }
+  };
+
+  int buf = 0;
+  if (g_begin + wave < g_end) load_group(g_begin + wave);
+  for (int g = g_begin + wave; g < g_end; g += WAVES, buf ^= 1) {
+    // ---- this group's data to LDS / registers; prefetch the next group ----------------------
+    uint8_t* mb = mbuf + buf * (2 * MB);
+#pragma unroll
+    for (int z = 0; z < MCH; ++z) *reinterpret_cast<u32x4*>(mb + z * 1024 + lane * 16) = mw[z];
+    uint32_t kwd[WPL], vwd[WPL];
+#pragma unroll
+    for (int u = 0; u < WPL / 4; ++u)
 #pragma unroll
       for (int z = 0; z < 4; ++z) {
-        kw[4 * u + z] = tk[z];
-        vw[4 * u + z] = tv[z];
+        kwd[4 * u + z] = kw[u][z];
+        vwd[4 * u + z] = vw[u][z];
       }
-    }
-    // ---- QK operand: q_c * s_gc as hi/lo fp16, and the bias sum_c q_c m_gc ----------------
-    u32x4 bq[4];
-    float bias = 0.f;
-    const int64_t kmb = ((int64_t)bh * ngcap + g) * D;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float vals[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 sm = kmeta<META_F16>(a.k_meta, kmb + 32 * kb + 8 * gq + e);
-        const float qt = qb[kb * 8 + e] * sm.x * (SCALE_QK * cls_inv<BITS>(e));
-        const float hi = (float)(f16)qt;
-        vals[e] = qt - mk * hi;
-        bias += qb[kb * 8 + e] * sm.y;
-      }
-      bq[kb] = u32x4{pack_f16x2(vals[0], vals[1]), pack_f16x2(vals[2], vals[3]),
-                     pack_f16x2(vals[4], vals[5]), pack_f16x2(vals[6], vals[7])};
-    }
-    bias = sum_over_rows(bias);
-    // ---- QK on the matrix cores: two 16-token tiles x four 32-channel blocks -----------
+    if (g + WAVES < g_end) load_group(g + WAVES);
+    wave_lds_sync();
+    // ---- key bias and QK -------------------------------------------------------------------
+    // key metadata in LDS: scales at [c * ESZ], mins at [(D + c) * ESZ]
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    float bias;
+    if (META_F16) {
+      f32x4 sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const u32x4 av = BITS == 2 ? unpack2(kw[2 * tb + kb / 2], kb & 1) : unpack4(kw[4 * tb + kb]);
-        s[tb] = mfma_f16(av, bq[kb], s[tb]);
+        const u32x4 mn = *reinterpret_cast<const u32x4*>(mb + (D + 32 * kb + 8 * gq) * 2);
+        sb = mfma_f16(mn, qh[kb], sb);  // every row: sum_c m_c q_c (exact products)
       }
-    // ---- scores (log2 units) and online softmax ------------------------------------------
+      bias = sb[0] * a.qscale;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const u32x4 sc = *reinterpret_cast<const u32x4*>(mb + (32 * kb + 8 * gq) * 2);
+        u32x4 bhi, blo;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float q0 = qs[kb * 8 + 2 * e2], q1 = qs[kb * 8 + 2 * e2 + 1];
+          bhi[e2] = mix_mul2(q0, q1, sc[e2]);
+          blo[e2] = mix_rem2(q0, q1, sc[e2], bhi[e2]);
+        }
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const u32x4 av = BITS == 2 ? unpack2(kwd[2 * tb + kb / 2], kb & 1) : unpack4(kwd[4 * tb + kb]);
+          s[tb] = mfma_f16(av, bhi, s[tb]);
+          s[tb] = mfma_f16(av, blo, s[tb]);
+        }
+      }
+    } else {
+      float bias_e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float4* sp = reinterpret_cast<const float4*>(mb + (32 * kb + 8 * gq) * 4);
+        const float4* mp = reinterpret_cast<const float4*>(mb + (D + 32 * kb + 8 * gq) * 4);
+        const float4 s0 = sp[0], s1 = sp[1], m0 = mp[0], m1 = mp[1];
+        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const float mn[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        float hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float qt = qs[kb * 8 + e] * sc[e];
+          hi[e] = (float)(f16)qt;
+          lo[e] = qt - hi[e];
+          bias_e[e] += qs[kb * 8 + e] * mn[e];
+        }
+        const u32x4 bhi = u32x4{pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3]),
+                                pack_f16x2(hi[4], hi[5]), pack_f16x2(hi[6], hi[7])};
+        const u32x4 blo = u32x4{pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
+                                pack_f16x2(lo[4], lo[5]), pack_f16x2(lo[6], lo[7])};
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const u32x4 av = BITS == 2 ? unpack2(kwd[2 * tb + kb / 2], kb & 1) : unpack4(kwd[4 * tb + kb]);
+          s[tb] = mfma_f16(av, bhi, s[tb]);
+          s[tb] = mfma_f16(av, blo, s[tb]);
+        }
+      }
+      bias = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bias += bias_e[e] * (1.0f / (SCALE_QK * cls_inv<BITS>(e)));
+      bias = sum_over_rows(bias);
+    }
+    // ---- scores (log2 units) and online softmax with a lazily moved reference max -----------
     float sc[8];
     float mx = -INFINITY;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float raw = s[tb][r] + dpp_xor1(s[tb][r]);  // hi column + lo column
-        const float v = raw * (SUBNORMAL / SCALE_QK) + bias;
+        const float v = s[tb][r] * (SUBNORMAL / SCALE_QK) + bias;
         sc[tb * 4 + r] = v;
         mx = fmaxf(mx, v);
       }
     mx = max_over_rows(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
+    // The reference max moves only when a score exceeds it by more than LAZY (log2 units), so
+    // weights stay <= 2^LAZY and most groups skip the rescale of the accumulators.
+    const bool move = mx > m_run + LAZY;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      const float m_new = move ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_lane *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) bv[cg] *= alpha;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sc[e] = exp2f(sc[e] - m_new);
+      sc[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
       psum += sc[e];
     }
-    l_lane = l_lane * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] *= alpha;
-#pragma unroll
-    for (int cg = 0; cg < 4; ++cg) bv[cg] *= alpha;
-    // ---- PV operand: p_t * s_tcg (fp16, hi columns only) and the bias sum_t p_t m_tcg ----
+    l_lane += psum;
+    // ---- PV operand(s) and value bias --------------------------------------------------------
     // Element e of this lane's B operand is token 16*(e/4) + 4*gq + e%4 = sc[e]'s token.
-    u32x4 bp[4];
-    {
+    u32x4 bp[NBP];
+    if (CPH == 4) {
+      const int cg = k;  // this column's value channel group
+      if (META_F16) {
+        uint32_t wv[8];
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tok = 16 * (e >> 2) + 4 * gq + (e & 3);
+          wv[e] = *reinterpret_cast<const uint32_t*>(mb + MB + tok * 16 + cg * 4);
+          pe[e] = active ? sc[e] : 0.f;
+          bv[0] = mix_fma_hi(pe[e], wv[e], bv[0]);
+        }
+        uint32_t pw[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)
+          pw[e2] = mix_mul_pair(pe[2 * e2] * (SCALE_PV * cls_inv<BITS>(2 * e2)), wv[2 * e2],
+                                pe[2 * e2 + 1] * (SCALE_PV * cls_inv<BITS>(2 * e2 + 1)), wv[2 * e2 + 1]);
+        bp[0] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+      } else {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tok = 16 * (e >> 2) + 4 * gq + (e & 3);
+          const float2 w = *reinterpret_cast<const float2*>(mb + MB + tok * 32 + cg * 8);
+          const float pe = active ? sc[e] : 0.f;
+          pv[e] = pe * w.x * (SCALE_PV * cls_inv<BITS>(e));
+          bv[0] += pe * w.y;
+        }
+        bp[0] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
+                      pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7])};
+      }
+    } else {
       float pv[4][8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tok = 16 * (e >> 2) + 4 * gq + (e & 3);
-        const int64_t vmi = (blk + tok) * 4;
         float svals[4], mvals[4];
         if (META_F16) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint32_t*>(a.v_meta) + vmi);
+          const u32x4 w = *reinterpret_cast<const u32x4*>(mb + MB + tok * 16);
 #pragma unroll
           for (int cg = 0; cg < 4; ++cg) {
             svals[cg] = f16_bits_to_f32(w[cg] & 0xffffu);
             mvals[cg] = f16_bits_to_f32(w[cg] >> 16);
           }
         } else {
-          const float4* p4 = reinterpret_cast<const float4*>(static_cast<const float2*>(a.v_meta) + vmi);
+          const float4* p4 = reinterpret_cast<const float4*>(mb + MB + tok * 32);
           const float4 w0 = p4[0], w1 = p4[1];
           svals[0] = w0.x; mvals[0] = w0.y; svals[1] = w0.z; mvals[1] = w0.w;
           svals[2] = w1.x; mvals[2] = w1.y; svals[3] = w1.z; mvals[3] = w1.w;
         }
-        const float pe = (hl == 0 && active) ? sc[e] : 0.f;
+        const float pe = active ? sc[e] : 0.f;
+        const float pes = pe * (SCALE_PV * cls_inv<BITS>(e));
 #pragma unroll
         for (int cg = 0; cg < 4; ++cg) {
-          pv[cg][e] = pe * svals[cg] * (SCALE_PV * cls_inv<BITS>(e));
+          pv[cg][e] = pes * svals[cg];
           bv[cg] += pe * mvals[cg];
         }
       }
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg)
+      for (int cg = 0; cg < NBP; ++cg)
         bp[cg] = u32x4{pack_f16x2(pv[cg][0], pv[cg][1]), pack_f16x2(pv[cg][2], pv[cg][3]),
                        pack_f16x2(pv[cg][4], pv[cg][5]), pack_f16x2(pv[cg][6], pv[cg][7])};
     }
     // ---- PV on the matrix cores: eight 16-channel tiles, K = the group's 32 tokens ------
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const u32x4 av = BITS == 2 ? unpack2(vw[t / 2], t & 1) : unpack4(vw[t]);
-      acc[t] = mfma_f16(av, bp[t / 2], acc[t]);
+      const u32x4 av = BITS == 2 ? unpack2(vwd[t / 2], t & 1) : unpack4(vwd[t]);
+      acc[t] = mfma_f16(av, bp[CPH == 4 ? 0 : t / 2], acc[t]);
     }
   }
 
   // ---- wave result -> LDS: m [WAVES][8], l [WAVES][8], o [WAVES][8][D] --------------------
+  __syncthreads();  // every wave is done with its metadata buffers
   float* s_m = smem;
   float* s_l = smem + WAVES * 8;
   float* s_o = smem + 2 * WAVES * 8;
@@ -241,11 +356,24 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
   float bvt[4];
 #pragma unroll
   for (int cg = 0; cg < 4; ++cg) bvt[cg] = sum_over_rows(bv[cg]);
-  if (active && hl == 0) {
-    if (gq == 0) {
-      s_m[wave * 8 + h] = m_run * LN2;  // natural-log units from here on
-      s_l[wave * 8 + h] = l_tot;
+  if (active && k == 0 && gq == 0) {
+    s_m[wave * 8 + h] = m_run * LN2;  // natural-log units from here on
+    s_l[wave * 8 + h] = l_tot;
+  }
+  if (CPH == 4) {
+    // lane (head h, column group cg = k) owns channel tiles 2cg and 2cg + 1
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t / 2 != k) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * t + 4 * gq + r;
+          s_o[(wave * 8 + h) * D + c] = acc[t][r] * (SUBNORMAL / SCALE_PV) + bvt[0];
+        }
+      }
     }
+  } else if (active && k == 0) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -283,29 +411,224 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
   }
 }
 
-// Residual tokens n_q .. n_q+r-1 from the fp16/fp32 ring, on the vector ALUs.
+// Residual tokens n_q .. n_q+r-1 from an fp16 ring, on the matrix cores: wave w takes every 4th
+// block of 32 ring tokens. Keys go straight from their ring rows into the row operand of QK^T
+// (fp16 keys times fp16-exact queries: exact products, fp32 sums); values are staged in LDS as
+// channel-major token pairs for the PV product; softmax weights enter as fp16 hi + lo.
+constexpr int RVT = 17;  // dwords per staged value row (16 token pairs + 1 pad)
+
+__device__ void residual_split_mfma(const DQArgs& a, int bh, int split, float* smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, gq = lane >> 4;
+  const int cph = a.G <= 4 ? 4 : 2;
+  const int h = j / cph, k = j % cph;
+  const bool active = h < a.G;
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  const int hq = kvh * a.G + h;
+  u32x4 qh[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    float qv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      qv[e] = active ? load_as_f32(a.q, ((int64_t)b * a.Hq + hq) * D + 32 * kb + 8 * gq + e, a.q_dtype) : 0.f;
+    qh[kb] = u32x4{pack_f16x2(qv[0], qv[1]), pack_f16x2(qv[2], qv[3]), pack_f16x2(qv[4], qv[5]),
+                   pack_f16x2(qv[6], qv[7])};
+  }
+  const f16* kres = static_cast<const f16*>(a.k_res) + (int64_t)bh * a.res_cap * D;
+  const f16* vres = static_cast<const f16*>(a.v_res) + (int64_t)bh * a.res_cap * D;
+  const int base = (int)(a.n_q % a.res_cap);
+  uint32_t* vt = reinterpret_cast<uint32_t*>(smem) + wave * D * RVT;
+  float m_run = -INFINITY, l_lane = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nblk = (a.r + 31) / 32;
+  for (int blk = wave; blk < nblk; blk += WAVES) {
+    const int t0 = blk * 32;
+    // keys of tokens t0 + 16 tb + j into the row operand
+    u32x4 kop[2][4];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int tt = t0 + 16 * tb + j;
+      int slot = base + tt;
+      if (slot >= a.res_cap) slot -= a.res_cap;
+      const bool ok = tt < a.r;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        kop[tb][kb] = ok ? *reinterpret_cast<const u32x4*>(kres + (int64_t)slot * D + 32 * kb + 8 * gq)
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+    // values, transposed to token pairs: lane (pair tp = lane % 16, channel quarter cq)
+    {
+      const int tp = lane & 15, cq = lane >> 4;
+      u32x4 v0[4], v1[4];
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        const int tt = t0 + 2 * tp + z;
+        int slot = base + tt;
+        if (slot >= a.res_cap) slot -= a.res_cap;
+        const bool ok = tt < a.r;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const u32x4 t = ok ? *reinterpret_cast<const u32x4*>(vres + (int64_t)slot * D + 32 * cq + 8 * w4)
+                             : u32x4{0u, 0u, 0u, 0u};
+          if (z == 0) v0[w4] = t; else v1[w4] = t;
+        }
+      }
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4)
+#pragma unroll
+        for (int zz = 0; zz < 4; ++zz) {
+          const int c = 32 * cq + 8 * w4 + 2 * zz;
+          vt[c * RVT + tp] = __builtin_amdgcn_perm(v1[w4][zz], v0[w4][zz], 0x05040100u);
+          vt[(c + 1) * RVT + tp] = __builtin_amdgcn_perm(v1[w4][zz], v0[w4][zz], 0x07060302u);
+        }
+    }
+    f32x4 s[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) c = mfma_f16(kop[tb][kb], qh[kb], c);
+      s[tb] = c;
+    }
+    float sc[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tt = t0 + 16 * (e >> 2) + 4 * gq + (e & 3);
+      const float v = tt < a.r ? s[e >> 2][e & 3] * a.qscale : -INFINITY;
+      sc[e] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = max_over_rows(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_lane *= alpha;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+    float hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = (m_new == -INFINITY || !active) ? 0.f : __builtin_amdgcn_exp2f(sc[e] - m_new);
+      l_lane += p;
+      hi[e] = (float)(f16)p;
+      lo[e] = p - hi[e];
+    }
+    const u32x4 phi = u32x4{pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3]), pack_f16x2(hi[4], hi[5]),
+                            pack_f16x2(hi[6], hi[7])};
+    const u32x4 plo = u32x4{pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]), pack_f16x2(lo[4], lo[5]),
+                            pack_f16x2(lo[6], lo[7])};
+    wave_lds_sync();  // every lane's transposed value writes land before the operand reads
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t* vr = vt + (16 * t + j) * RVT;
+      const u32x4 vop = u32x4{vr[2 * gq], vr[2 * gq + 1], vr[8 + 2 * gq], vr[8 + 2 * gq + 1]};
+      acc[t] = mfma_f16(vop, phi, acc[t]);
+      acc[t] = mfma_f16(vop, plo, acc[t]);
+    }
+    wave_lds_sync();  // operand reads finish before the next block overwrites the tile
+  }
+  // ---- waves -> LDS -> this split's partial ----------------------------------------------
+  __syncthreads();
+  float* s_m = smem;
+  float* s_l = smem + WAVES * 8;
+  float* s_o = smem + 2 * WAVES * 8;
+  const float l_tot = sum_over_rows(l_lane);
+  if (active && k == 0) {
+    if (gq == 0) {
+      s_m[wave * 8 + h] = m_run * LN2;
+      s_l[wave * 8 + h] = l_tot;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) s_o[(wave * 8 + h) * D + 16 * t + 4 * gq + rr] = acc[t][rr];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < a.G * D; idx += THREADS) {
+    const int hh = idx / D, c = idx % D;
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w)
+      if (s_l[w * 8 + hh] > 0.f) m = fmaxf(m, s_m[w * 8 + hh]);
+    float o = 0.f, l = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float lw = s_l[w * 8 + hh];
+        if (lw > 0.f) {
+          const float f = __expf(s_m[w * 8 + hh] - m);
+          o += f * s_o[(w * 8 + hh) * D + c];
+          l += f * lw;
+        }
+      }
+    }
+    const int64_t row = (int64_t)b * a.Hq + kvh * a.G + hh;
+    a.part_o[(row * a.total_splits + split) * D + c] = o;
+    if (c == 0) {
+      a.part_ml[(row * a.total_splits + split) * 2 + 0] = m;
+      a.part_ml[(row * a.total_splits + split) * 2 + 1] = l;
+    }
+  }
+}
+
+// Residual tokens n_q .. n_q+r-1 from the fp16/fp32 ring, on the vector ALUs: one thread per
+// token for the scores (whole 16-byte row loads), then each wave takes every 4th token for the
+// weighted value sum (two channels per lane, coalesced rows), reduced across waves in LDS.
+template <bool RES_F16>
 __device__ void residual_split(const DQArgs& a, int bh, int split, float* smem) {
+  using RT = typename std::conditional<RES_F16, f16, float>::type;
+  constexpr int PER16 = 16 / sizeof(RT);  // ring elements per 16-byte load
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int G = a.G, r = a.r;
-  float* s_q = smem;                  // [8][D]
-  float* s_p = smem + 8 * D;          // [8][RES_MAX]
-  float* s_ml = s_p + 8 * RES_MAX;    // [8][2]
+  float* s_q = smem;                        // [8][D]
+  float* s_p = smem + 8 * D;                // [8][RES_MAX]
+  float* s_ml = s_p + 8 * RES_MAX;          // [8][2]
+  float* s_red = s_ml + 16;                 // [WAVES][8][D]
   for (int idx = tid; idx < G * D; idx += THREADS) {
     const int hh = idx / D, c = idx % D;
     s_q[idx] = load_as_f32(a.q, ((int64_t)b * a.Hq + kvh * G + hh) * D + c, a.q_dtype) * a.qscale;
   }
   __syncthreads();
-  const int64_t res_base = (int64_t)bh * a.res_cap;
+  const RT* kres = static_cast<const RT*>(a.k_res) + (int64_t)bh * a.res_cap * D;
+  const RT* vres = static_cast<const RT*>(a.v_res) + (int64_t)bh * a.res_cap * D;
+  const int base = (int)(a.n_q % a.res_cap);
   for (int t = tid; t < r; t += THREADS) {
-    const int64_t slot = (a.n_q + t) % a.res_cap;
-    const int64_t rowi = (res_base + slot) * D;
+    int slot = base + t;
+    if (slot >= a.res_cap) slot -= a.res_cap;
+    const u32x4* row = reinterpret_cast<const u32x4*>(kres + (int64_t)slot * D);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < D; ++c) {
-      const float kx = load_as_f32(a.k_res, rowi + c, a.res_dtype);
+#pragma unroll 1
+    for (int z0 = 0; z0 < D / PER16; z0 += 4) {  // 4 x 16 bytes of the key row at a time
+      u32x4 kv[4];
 #pragma unroll
-      for (int hh = 0; hh < 8; ++hh)
-        if (hh < G) acc[hh] += s_q[hh * D + c] * kx;
+      for (int z = 0; z < 4; ++z) kv[z] = row[z0 + z];
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        float kx[PER16];
+        if (RES_F16) {
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            kx[2 * y] = f16_bits_to_f32(kv[z][y] & 0xffffu);
+            kx[2 * y + 1] = f16_bits_to_f32(kv[z][y] >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int y = 0; y < 4; ++y) kx[y] = __uint_as_float(kv[z][y]);
+        }
+        const int c0 = (z0 + z) * PER16;
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+          if (hh < G) {
+#pragma unroll
+            for (int y = 0; y < PER16; ++y) acc[hh] += s_q[hh * D + c0 + y] * kx[y];
+          }
+        }
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh)
@@ -318,7 +641,7 @@ __device__ void residual_split(const DQArgs& a, int bh, int split, float* smem) 
     m = wave_max(m);
     float l = 0.f;
     for (int t = lane; t < r; t += 64) {
-      const float p = exp2f(s_p[hh * RES_MAX + t] - m);
+      const float p = __builtin_amdgcn_exp2f(s_p[hh * RES_MAX + t] - m);
       s_p[hh * RES_MAX + t] = p;
       l += p;
     }
@@ -329,13 +652,47 @@ __device__ void residual_split(const DQArgs& a, int bh, int split, float* smem) 
     }
   }
   __syncthreads();
+  {
+    float o[8][2];
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) o[hh][0] = o[hh][1] = 0.f;
+#pragma unroll 4
+    for (int t = wave; t < r; t += WAVES) {
+      int slot = base + t;
+      if (slot >= a.res_cap) slot -= a.res_cap;
+      float v0, v1;
+      if (RES_F16) {
+        const uint32_t w = reinterpret_cast<const uint32_t*>(vres + (int64_t)slot * D)[lane];
+        v0 = f16_bits_to_f32(w & 0xffffu);
+        v1 = f16_bits_to_f32(w >> 16);
+      } else {
+        const float2 w = reinterpret_cast<const float2*>(vres + (int64_t)slot * D)[lane];
+        v0 = w.x;
+        v1 = w.y;
+      }
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) {
+        if (hh < G) {
+          const float p = s_p[hh * RES_MAX + t];
+          o[hh][0] += p * v0;
+          o[hh][1] += p * v1;
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+      if (hh < G) {
+        s_red[(wave * 8 + hh) * D + 2 * lane] = o[hh][0];
+        s_red[(wave * 8 + hh) * D + 2 * lane + 1] = o[hh][1];
+      }
+    }
+  }
+  __syncthreads();
   for (int idx = tid; idx < G * D; idx += THREADS) {
     const int hh = idx / D, c = idx % D;
     float o = 0.f;
-    for (int t = 0; t < r; ++t) {
-      const int64_t slot = (a.n_q + t) % a.res_cap;
-      o += s_p[hh * RES_MAX + t] * load_as_f32(a.v_res, (res_base + slot) * D + c, a.res_dtype);
-    }
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) o += s_red[(w * 8 + hh) * D + c];
     const int64_t row = (int64_t)b * a.Hq + kvh * G + hh;
     a.part_o[(row * a.total_splits + split) * D + c] = o;
     if (c == 0) {
@@ -345,31 +702,18 @@ __device__ void residual_split(const DQArgs& a, int bh, int split, float* smem) 
   }
 }
 
-template <int BITS, bool META_F16>
-__global__ void __launch_bounds__(THREADS) draft_quant_kernel(DQArgs a) {
-  __shared__ float smem[8 * D + 8 * RES_MAX + 16];
-  __shared__ int s_last;
+template <int BITS, bool META_F16, bool RES_F16, int CPH>
+__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 4))) draft_quant_kernel(DQArgs a) {
+  __shared__ float smem[SMEM_FLOATS];
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
   if (split < a.splits)
-    quant_split<BITS, META_F16>(a, bh, split, smem);
+    quant_split<BITS, META_F16, CPH>(a, bh, split, smem);
+  else if (RES_F16 && a.q_dtype != VC_F32)
+    residual_split_mfma(a, bh, split, smem);
   else
-    residual_split(a, bh, split, smem);
+    residual_split<RES_F16>(a, bh, split, smem);
 
-  // ---- ticket: the last split of this (b, kv head) merges every partial -----------------
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(a.counters + bh, 1u) == (unsigned)(a.total_splits - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
-  for (int hh = threadIdx.x >> 6; hh < a.G; hh += WAVES) {
-    const int64_t row = (int64_t)b * a.Hq + kvh * a.G + hh;
-    merge_row_wave(a.part_o + row * a.total_splits * D, a.part_ml + row * a.total_splits * 2,
-                   a.total_splits, a.out + row * D, a.lse ? a.lse + row : nullptr);
-  }
-  if (threadIdx.x == 0) a.counters[bh] = 0u;
 }
 
 }  // namespace
@@ -378,13 +722,15 @@ DraftQuantPlan plan_draft_quant(const vc_kivi& c, int64_t n_q, int Hq) {
   DraftQuantPlan p;
   const int64_t ngroups = n_q / GROUP;
   const int64_t units = (int64_t)c.B * c.Hkv;
-  int64_t s = (1024 + units - 1) / units;       // aim at ~1024 workgroups
-  s = std::min<int64_t>(s, std::max<int64_t>(1, ngroups / 8));  // >= 2 groups per wave
+  // One resident round of workgroups: 256 CUs x 3 workgroups (the kernel is built for 3 waves
+  // per SIMD), counting the residual split of every (b, kv head); at least 2 groups per wave.
+  int64_t s = std::max<int64_t>(1, 768 / units - 1);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, ngroups / 8));
   if (ngroups == 0) s = 0;
   p.splits = (int)s;
   p.total_splits = p.splits + 1;
   const size_t rows = (size_t)c.B * Hq;
-  p.ws_bytes = COUNTER_BYTES + rows * p.total_splits * (D + 2) * sizeof(float);
+  p.ws_bytes = rows * p.total_splits * (D + 2) * sizeof(float);
   return p;
 }
 
@@ -401,9 +747,8 @@ hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* 
   a.q = q;
   a.out = out;
   a.lse = lse;
-  a.counters = static_cast<unsigned*>(ws);
   const size_t rows = (size_t)c.B * Hq;
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + COUNTER_BYTES);
+  a.part_o = static_cast<float*>(ws);
   a.part_ml = a.part_o + rows * plan.total_splits * D;
   a.tok_cap = c.tok_cap;
   a.n_q = n_q;
@@ -419,15 +764,24 @@ hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* 
   a.total_splits = plan.total_splits;
   a.qscale = sm_scale * LOG2E;
   dim3 grid((unsigned)plan.total_splits, (unsigned)(c.B * c.Hkv));
-  const bool f16m = c.meta_dtype == VC_F16;
+  const bool f16m = c.meta_dtype == VC_F16, f16r = c.res_dtype == VC_F16;
+  const bool wide = a.G <= 4;
+#define VC_DQ_LAUNCH(BITS, MF, RF)                                                              \
+  do {                                                                                          \
+    if (wide) hipLaunchKernelGGL((draft_quant_kernel<BITS, MF, RF, 4>), grid, dim3(THREADS), 0, s, a); \
+    else hipLaunchKernelGGL((draft_quant_kernel<BITS, MF, RF, 2>), grid, dim3(THREADS), 0, s, a);      \
+  } while (0)
   if (c.bits == 2) {
-    if (f16m) hipLaunchKernelGGL((draft_quant_kernel<2, true>), grid, dim3(THREADS), 0, s, a);
-    else hipLaunchKernelGGL((draft_quant_kernel<2, false>), grid, dim3(THREADS), 0, s, a);
+    if (f16m) { if (f16r) VC_DQ_LAUNCH(2, true, true); else VC_DQ_LAUNCH(2, true, false); }
+    else { if (f16r) VC_DQ_LAUNCH(2, false, true); else VC_DQ_LAUNCH(2, false, false); }
   } else {
-    if (f16m) hipLaunchKernelGGL((draft_quant_kernel<4, true>), grid, dim3(THREADS), 0, s, a);
-    else hipLaunchKernelGGL((draft_quant_kernel<4, false>), grid, dim3(THREADS), 0, s, a);
+    if (f16m) { if (f16r) VC_DQ_LAUNCH(4, true, true); else VC_DQ_LAUNCH(4, true, false); }
+    else { if (f16r) VC_DQ_LAUNCH(4, false, true); else VC_DQ_LAUNCH(4, false, false); }
   }
-  return hipGetLastError();
+#undef VC_DQ_LAUNCH
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_merge(a.part_o, a.part_ml, (int64_t)rows, plan.total_splits, out, lse, s);
 }
 
 }  // namespace vc

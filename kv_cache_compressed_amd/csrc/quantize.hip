@@ -92,7 +92,15 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a) {
     }
     const Stats st = group_stats(lo, hi, LEVELS, meta_f16);
     kst[tid] = st;
-    store_meta(a.k_meta, ((int64_t)bh * (a.tok_cap / GROUP) + g) * D + tid, st, meta_f16);
+    // key metadata is planar per group: 128 scales, then 128 mins
+    const int64_t base = ((int64_t)bh * (a.tok_cap / GROUP) + g) * 2 * D;
+    if (meta_f16) {
+      static_cast<f16*>(a.k_meta)[base + tid] = (f16)st.scale;  // exact: fp16 values
+      static_cast<f16*>(a.k_meta)[base + D + tid] = (f16)st.mn;
+    } else {
+      static_cast<float*>(a.k_meta)[base + tid] = st.scale;
+      static_cast<float*>(a.k_meta)[base + D + tid] = st.mn;
+    }
   } else {  // value statistics: one token over one 32-channel group
     const int t = (tid - D) / 4, cg = (tid - D) % 4;
     float lo = sv[t][cg * GROUP], hi = lo;

@@ -157,12 +157,12 @@ __global__ void __launch_bounds__(512) verify_bf16_kernel(VArgs a) {
       }
       mx = max_over_rows(mx);
       const float m_new = fmaxf(m_run[ct], mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[ct] - m_new);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[ct] - m_new);
       m_run[ct] = m_new;
       float psum = 0.f, hi[8], lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = (m_new == -INFINITY) ? 0.f : exp2f(sc[e] - m_new);
+        const float p = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[e] - m_new);
         psum += p;
         hi[e] = __uint_as_float(__float_as_uint(p) & 0xffff0000u);  // truncated: exact split
         lo[e] = p - hi[e];
@@ -261,8 +261,8 @@ __global__ void __launch_bounds__(256) verify_f32_kernel(VF32Args a) {
     __syncthreads();
     const float mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    const float p = (key < k_end) ? exp2f(s - m_new) : 0.f;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float p = (key < k_end) ? __builtin_amdgcn_exp2f(s - m_new) : 0.f;
     s_p[tid] = p;
     const float ps = wave_sum(p);
     __syncthreads();

@@ -68,14 +68,20 @@ class RoundState:
                 src = (kt, vt, n * 128)
             else:
                 src = (self.k_store, self.v_store, cap * 128)
-            for _ in range(max(1, replicas)):
+            # Replicas hold identical copies of the quantised codes/metadata (so consecutive draft
+            # steps can read different copies, as the layers of a real model would); they share one
+            # residual ring, to which each draft-round entry is appended once.
+            for k in range(max(1, replicas)):
                 c = vc.KiviCache(B, Hkv, max(w.n_q, 32), w.bits,
                                  vc.VC_F16 if w.meta_dtype == "f16" else vc.VC_F32,
                                  vc.VC_F16 if w.res_dtype == "f16" else vc.VC_F32, w.res_cap, device)
                 vc.vc_quantize_kv(c, src[0], src[1], 0, w.n_q, src_bh_stride=src[2])
-                if n > w.n_q:
-                    vc.vc_kivi_append(c, src[0][:, :, w.n_q:], src[1][:, :, w.n_q:], w.n_q, n - w.n_q,
-                                      src_bh_stride=src[2])
+                if k == 0:
+                    if n > w.n_q:
+                        vc.vc_kivi_append(c, src[0][:, :, w.n_q:], src[1][:, :, w.n_q:], w.n_q,
+                                          n - w.n_q, src_bh_stride=src[2])
+                else:
+                    c.k_res, c.v_res = self.replicas[0].k_res, self.replicas[0].v_res
                 self.replicas.append(c)
             if w.past_on_host:
                 torch.cuda.synchronize()
@@ -131,11 +137,11 @@ class RoundState:
             vc.vc_draft_attn_drop(self.k_store, self.v_store, self.idx, n_keep, self.q_draft[j],
                                   self.out_d[j], self.lse_d[j], self.ws_draft.get(nb), SM_SCALE)
 
-    def append_draft_entry(self, j: int, cache=None):
+    def append_draft_entry(self, j: int):
+        """Append the key/value of position n+j to the (shared) residual ring."""
         w = self.w
         if w.drafter == "kivi":
-            c = cache or self.replicas[0]
-            vc.vc_kivi_append(c, self.k_blk[:, :, j], self.v_blk[:, :, j], w.n + j, 1,
+            vc.vc_kivi_append(self.replicas[0], self.k_blk[:, :, j], self.v_blk[:, :, j], w.n + j, 1,
                               src_bh_stride=w.L * 128)
 
     def draft_step(self, j: int):
@@ -143,7 +149,7 @@ class RoundState:
         if self.replicas:
             c = self.replicas[self._rep % len(self.replicas)]
             self._rep += 1
-        self.append_draft_entry(j, c)
+        self.append_draft_entry(j)
         self.draft_attention(j, c)
         w = self.w
         torch.matmul(self.out_d[j].view(w.B, -1), self.W.t(), out=self.logits_d[j])
@@ -169,10 +175,66 @@ class RoundState:
         self.drafts.copy_(self.tok_d.t())
         vc.vc_accept(self.logits_v, self.drafts, self.accept_len, self.next_tok, self.argmax_v)
 
-    def run_round(self):
-        for j in range(self.w.x):
-            self.draft_step(j)
-        self.verify_step()
+    def run_round(self, timer=None):
+        """One round. `timer`, if given, is called as timer(kind, start) with kind in
+        {"draft", "verify"} right before (start=True) and after (start=False) each attention
+        launch, on the host thread that enqueues them (for event timing on the current stream)."""
+        w = self.w
+        for j in range(w.x):
+            c = None
+            if self.replicas:
+                c = self.replicas[self._rep % len(self.replicas)]
+                self._rep += 1
+            self.append_draft_entry(j)
+            if timer:
+                timer("draft", True)
+            self.draft_attention(j, c)
+            if timer:
+                timer("draft", False)
+            torch.matmul(self.out_d[j].view(w.B, -1), self.W.t(), out=self.logits_d[j])
+            vc.vc_accept(self.logits_d[j].view(w.B, 1, w.vocab), None, self.scratch_a, self.tok_d[j])
+        if timer:
+            timer("verify", True)
+        self.verify_attention()
+        if timer:
+            timer("verify", False)
+        flat = self.out_v.permute(0, 2, 1, 3).reshape(w.B * w.L, w.Hq * 128)
+        torch.matmul(flat, self.W.t(), out=self.logits_v.view(w.B * w.L, w.vocab))
+        self.drafts.copy_(self.tok_d.t())
+        vc.vc_accept(self.logits_v, self.drafts, self.accept_len, self.next_tok, self.argmax_v)
+
+    # ---- algorithmic work (what the method must move / compute) -------------------------
+    def draft_bytes(self, j: int) -> int:
+        """Bytes one draft-attention launch of step j must move: codes + metadata of n_q quantised
+        tokens, the r full-precision residual tokens, the queries in and the outputs out."""
+        w = self.w
+        if w.drafter == "kivi":
+            meta_b = 2 if w.meta_dtype == "f16" else 4
+            res_b = 2 if w.res_dtype == "f16" else 4
+            per_tok = 2 * 128 * w.bits // 8 + (128 * 2 * meta_b) // 32 + 4 * 2 * meta_b
+            r = (w.n - w.n_q) + j + 1
+            kv = w.B * w.Hkv * (w.n_q * per_tok + r * 2 * 128 * res_b)
+        else:
+            kv_b = 2 if w.kv_dtype == "bf16" else 4
+            kv = w.B * w.Hkv * (self.kept + j + 1) * (2 * 128 * kv_b + 4)
+        q_b = 2 if w.kv_dtype == "bf16" else 4
+        return kv + w.B * w.Hq * (128 * q_b + 129 * 4)
+
+    def draft_flops(self, j: int) -> int:
+        w = self.w
+        keys = (w.n + j + 1) if w.drafter == "kivi" else (self.kept + j + 1)
+        return 4 * 128 * w.B * w.Hq * keys
+
+    def verify_bytes(self) -> int:
+        w = self.w
+        kv_b = 2 if w.kv_dtype == "bf16" else 4
+        return (w.B * w.Hkv * (w.n + w.L) * 2 * 128 * kv_b + w.B * w.Hq * w.L * 128 * kv_b
+                + w.B * w.Hq * w.L * 129 * 4)
+
+    def verify_flops(self) -> int:
+        w = self.w
+        keys = sum(w.n + i + 1 for i in range(w.L))
+        return 4 * 128 * w.B * w.Hq * keys
 
     def results(self) -> dict:
         torch.cuda.synchronize()

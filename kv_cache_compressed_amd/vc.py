@@ -126,7 +126,7 @@ class KiviCache:
         cap = max(tok_cap, 32)
         self.k_codes = torch.zeros(B, Hkv, cap, row, dtype=torch.uint8, device=device)
         self.v_codes = torch.zeros_like(self.k_codes)
-        self.k_meta = torch.zeros(B, Hkv, cap // 32, d, 2, dtype=mdt, device=device)
+        self.k_meta = torch.zeros(B, Hkv, cap // 32, 2, d, dtype=mdt, device=device)  # scales, mins
         self.v_meta = torch.zeros(B, Hkv, cap, d // 32, 2, dtype=mdt, device=device)
         self.k_res = torch.zeros(B, Hkv, res_cap, d, dtype=rdt, device=device)
         self.v_res = torch.zeros_like(self.k_res)
@@ -138,7 +138,7 @@ class KiviCache:
 
 
 class Workspace:
-    """A zero-initialised device workspace (the draft calls need their counters zeroed once)."""
+    """A reusable device workspace, grown on demand."""
 
     def __init__(self, device="cuda"):
         self.device = device

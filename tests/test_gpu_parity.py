@@ -21,10 +21,12 @@ from oracle.round import Round
 pytestmark = pytest.mark.gpu
 
 GAP = 1e-3
-# Tight bounds from the arithmetic: fp32 accumulation, fp16 operands with hi/lo splits on the score
-# side and an 11-bit (draft) or ~16-bit (verify/drop) softmax weight on the value side. Outputs
-# are weighted means of O(1) values, so the weight rounding bounds the error at ~2^-11 of max|v|.
-TIGHT = {"draft_quant": 2e-3, "draft_drop": 5e-4, "verify": 5e-4}
+# Tight bounds from the arithmetic (relative to max(1, max|ref|)): fp32 accumulation everywhere;
+# the quantised draft carries q*s as an fp16 hi+lo pair (~2^-22) but the softmax weight times the
+# value scale as one fp16 (2^-11 relative per weight), so its error is ~2^-11 of the output scale;
+# the verify and dropped-token paths carry the weight as a bf16 hi+lo pair (~2^-16) with exact
+# bf16 keys/values. Observed maxima on the parity cases: 1.6e-4 / 1.6e-6 / 8.6e-6.
+TIGHT = {"draft_quant": 1e-3, "draft_drop": 5e-5, "verify": 1e-4}
 
 W_SMALL = {
     "c1": synth.WORKLOADS["c1"],
@@ -148,7 +150,7 @@ def test_quantize_bit_exact(gpu_lib, name):
             assert np.array_equal(c.v_codes[b, h, :w.n_q].cpu().numpy(), oq.pack_codes(vcod, w.bits, "v"))
             gk = c.k_meta[b, h, :w.n_q // 32].cpu().numpy()
             gv = c.v_meta[b, h, :w.n_q].cpu().numpy()
-            assert np.array_equal(gk[..., 0], ks.astype(mdt)) and np.array_equal(gk[..., 1], km.astype(mdt))
+            assert np.array_equal(gk[:, 0], ks.astype(mdt)) and np.array_equal(gk[:, 1], km.astype(mdt))
             assert np.array_equal(gv[..., 0], vs.astype(mdt)) and np.array_equal(gv[..., 1], vm.astype(mdt))
 
 
@@ -174,8 +176,8 @@ def test_quantize_extreme_groups(gpu_lib):
             mdt = np.float16 if meta == "f16" else np.float32
             assert np.array_equal(c.k_codes[0, 0].cpu().numpy(), oq.pack_codes(kc, bits, "k"))
             assert np.array_equal(c.v_codes[0, 0].cpu().numpy(), oq.pack_codes(vcod, bits, "v"))
-            assert np.array_equal(c.k_meta[0, 0, ..., 0].cpu().numpy(), ks.astype(mdt))
-            assert np.array_equal(c.k_meta[0, 0, ..., 1].cpu().numpy(), km.astype(mdt))
+            assert np.array_equal(c.k_meta[0, 0, :, 0].cpu().numpy(), ks.astype(mdt))
+            assert np.array_equal(c.k_meta[0, 0, :, 1].cpu().numpy(), km.astype(mdt))
             assert np.array_equal(c.v_meta[0, 0, ..., 0].cpu().numpy(), vs.astype(mdt))
             assert np.array_equal(c.v_meta[0, 0, ..., 1].cpu().numpy(), vm.astype(mdt))
 
@@ -208,7 +210,8 @@ def test_append_ring_and_flush(gpu_lib):
             vals = c.k_res[b, h, 224:256].float().cpu().numpy()
             kc, ks, km = oq.quantize_k(vals, 2, "f16")
             assert np.array_equal(c.k_codes[b, h, 480:512].cpu().numpy(), oq.pack_codes(kc, 2, "k"))
-            assert np.array_equal(c.k_meta[b, h, 15, :, 0].cpu().numpy(), ks.astype(np.float16))
+            assert np.array_equal(c.k_meta[b, h, 15, 0].cpu().numpy(), ks[0].astype(np.float16))
+            assert np.array_equal(c.k_meta[b, h, 15, 1].cpu().numpy(), km[0].astype(np.float16))
 
 
 # ------------------------------------------------------------------------------------------
