@@ -121,9 +121,12 @@ vc_status vc_kivi_append(const vc_kivi *c, const void *k, const void *v, int32_t
  *   q    [B][Hq][128] in q_dtype (VC_F32 | VC_BF16 | VC_F16), device
  *   out  [B][Hq][128] fp32, device;  lse [B][Hq] fp32 or NULL
  *   n_q  multiple of 32, <= tok_cap;  0 <= r <= res_cap;  n_q + r >= 1;  Hq % Hkv == 0,
- *        Hq/Hkv <= 8
- *   ws   device workspace of vc_draft_quant_workspace() bytes (split partials; contents need no
- *        initialisation). Calls that overlap in time must not share a workspace.
+ *        Hq/Hkv <= 8;  B*Hkv <= 16384
+ *   ws   device workspace of at least vc_draft_quant_workspace() bytes: its first 64 KB hold one
+ *        ticket counter per (b, kv head), the rest the split partials. Zero-fill the workspace
+ *        once after allocating it; every call leaves the counters at zero again, so a workspace
+ *        can then be reused for any later call (any shape). Calls that overlap in time must not
+ *        share a workspace. The splits and their log-sum-exp merge run in one kernel.
  */
 vc_status vc_draft_attn_quant(const vc_kivi *c, int64_t n_q, int32_t r, const void *q,
                               int32_t q_dtype, int32_t Hq, float sm_scale, float *out, float *lse,

@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ pa
                                                     float* __restrict__ lse) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  merge_row_wave(part_o + row * S * D, part_ml + row * S * 2, S, out + row * D,
+  merge_row_wave<false>(part_o + row * S * D, part_ml + row * S * 2, S, out + row * D,
                  lse ? lse + row : nullptr);
 }
 

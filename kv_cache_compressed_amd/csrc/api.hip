@@ -145,6 +145,8 @@ vc_status vc_draft_attn_quant(const vc_kivi* c, int64_t n_q, int32_t r, const vo
   REQUIRE_PTR(out);
   if (Hq / c->Hkv > 8) return fail(VC_ERR_UNSUPPORTED, "Hq/Hkv > 8 is not supported");
   if (c->res_cap > 512) return fail(VC_ERR_UNSUPPORTED, "res_cap > 512 is not supported");
+  if ((int64_t)c->B * c->Hkv > (int64_t)(vc::DRAFT_COUNTER_BYTES / 4))
+    return fail(VC_ERR_UNSUPPORTED, "B*Hkv > %d is not supported", (int)(vc::DRAFT_COUNTER_BYTES / 4));
   const vc::DraftQuantPlan plan = vc::plan_draft_quant(*c, n_q, Hq);
   if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
     return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,

@@ -36,6 +36,40 @@ __device__ __forceinline__ float load_as_f32(const void* p, int64_t i, int dtype
   return dtype == VC_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
 }
 
+// Elements i .. i+7 of a VC_F32 / VC_F16 / VC_BF16 array (i a multiple of 8, array 16-byte
+// aligned), fetched with 16-byte loads as raw words (load8_raw) and converted to float later
+// (cvt8), so the loads can be issued well ahead of their use.
+struct Raw8 {
+  u32x4 a, b;  // VC_F32: 8 floats; 16-bit types: a holds all 8
+};
+__device__ __forceinline__ Raw8 load8_raw(const void* p, int64_t i, int dtype) {
+  // branch-free: a 16-bit type loads its 16 bytes twice
+  const int esz = dtype == VC_F32 ? 4 : 2;
+  const uint8_t* b = static_cast<const uint8_t*>(p) + i * esz;
+  Raw8 r;
+  r.a = *reinterpret_cast<const u32x4*>(b);
+  r.b = *reinterpret_cast<const u32x4*>(b + (esz == 4 ? 16 : 0));
+  return r;
+}
+__device__ __forceinline__ void cvt8(const Raw8& r, int dtype, float* out) {
+#pragma unroll
+  for (int z = 0; z < 4; ++z) {
+    if (dtype == VC_F32) {
+      out[z] = __uint_as_float(r.a[z]);
+      out[4 + z] = __uint_as_float(r.b[z]);
+    } else if (dtype == VC_BF16) {
+      out[2 * z] = bf16_bits_to_f32(r.a[z] & 0xffffu);
+      out[2 * z + 1] = bf16_bits_to_f32(r.a[z] >> 16);
+    } else {
+      out[2 * z] = f16_bits_to_f32(r.a[z] & 0xffffu);
+      out[2 * z + 1] = f16_bits_to_f32(r.a[z] >> 16);
+    }
+  }
+}
+__device__ __forceinline__ void load8_as_f32(const void* p, int64_t i, int dtype, float* out) {
+  cvt8(load8_raw(p, i, dtype), dtype, out);
+}
+
 // Largest fp16 value <= x, as float.
 __device__ __forceinline__ float f16_round_down(float x) {
   f16 h = (f16)x;  // round to nearest even
@@ -140,8 +174,24 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Order this wave's LDS writes before its following LDS reads of other lanes' data (a wave's LDS
-// instructions execute in order; the fences keep the compiler from moving memory operations).
+// Direct global -> LDS copy (global_load_lds_dwordx4): lane l's 16 bytes from g land at
+// lds + 16 l, where lds is the wave's common base. Completion is counted by vmcnt; the compiler
+// does not order LDS reads after it, so callers wait explicitly. (The host pass of this file has
+// no such instruction; the body exists for the device pass only.)
+template <int AUX>
+__device__ __forceinline__ void copy16_to_lds(const void* g, void* lds) {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, AUX);
+#endif
+}
+
+// Compiler-only ordering of this wave's LDS accesses: the hardware already runs one wave's LDS
+// instructions in order, so a later read sees an earlier write of another lane of the same wave.
+// (No fence: a fence would also wait for outstanding global loads and direct-to-LDS copies.)
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
+// Order this wave's LDS writes before its following LDS reads of other lanes' data, with fences
+// that also keep the compiler from moving memory operations (and wait for outstanding loads).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
@@ -166,30 +216,86 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 // split partials and their log-sum-exp merge (natural-log units)
 // part_o [rows][S][D], part_ml [rows][S][2] = (m, l)
 // ---------------------------------------------------------------------------------------------
-// Merge the S partials of one row; called by 64 lanes of one wave, lane handles channels
-// 2*lane, 2*lane+1. Writes out[row][D] (normalised) and lse[row] (if non-null).
+// Merge the S partials of one row; called by the 64 lanes of one wave, lane handles channels
+// 2*lane, 2*lane+1. Writes out[row][D] (normalised) and lse[row] (if non-null). Lane s reads split
+// s's (m, l), so every partial load of the row is in flight at once. COHERENT reads bypass the
+// non-coherent caches (device-scope relaxed atomic loads), for partials written by other
+// workgroups of the same kernel.
+// ---------------------------------------------------------------------------------------------
+// Device-scope store that writes through the non-coherent caches (read back by load_f32<true>).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <bool COHERENT>
+__device__ __forceinline__ float load_f32(const float* p) {
+  if constexpr (COHERENT)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+template <bool COHERENT>
+__device__ __forceinline__ float2 load_f32x2(const float* p) {
+  if constexpr (COHERENT) {
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+  } else {
+    return *reinterpret_cast<const float2*>(p);
+  }
+}
+
+template <bool COHERENT>
 __device__ __forceinline__ void merge_row_wave(const float* __restrict__ part_o,
                                               const float* __restrict__ part_ml, int S,
                                               float* __restrict__ out, float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   float m = -INFINITY;
+  float o0 = 0.f, o1 = 0.f, l = 0.f;
+  if (S <= 16) {
+    // every load of the row in one round trip (splits past S re-read split S-1 and weigh 0)
+    const float2 ml = load_f32x2<COHERENT>(part_ml + 2 * min(lane, S - 1));
+    float2 po[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) po[s] = load_f32x2<COHERENT>(part_o + (int64_t)min(s, S - 1) * D + 2 * lane);
+    const bool live = lane < S && ml.y > 0.f;
+    m = wave_max(live ? ml.x : -INFINITY);
+    const float w = (live && m != -INFINITY) ? __expf(ml.x - m) : 0.f;
+    l = w * ml.y;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
+      o0 += ws * po[s].x;
+      o1 += ws * po[s].y;
+    }
+  } else {
   for (int s = lane; s < S; s += 64) {
-    const float ms = part_ml[2 * s], ls = part_ml[2 * s + 1];
-    if (ls > 0.f) m = fmaxf(m, ms);
+    const float2 ml = load_f32x2<COHERENT>(part_ml + 2 * s);
+    if (ml.y > 0.f) m = fmaxf(m, ml.x);
   }
   m = wave_max(m);
-  float o0 = 0.f, o1 = 0.f, l = 0.f;
   if (m != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float ls = part_ml[2 * s + 1];
-      if (!(ls > 0.f)) continue;
-      const float w = __expf(part_ml[2 * s] - m);
-      const float2 po = reinterpret_cast<const float2*>(part_o + (int64_t)s * D)[lane];
-      o0 += w * po.x;
-      o1 += w * po.y;
-      l += w * ls;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      // lane s0 + i holds split (s0 + i)'s weight; empty splits weigh 0 (their o is 0)
+      float w = 0.f;
+      if (s0 + lane < S) {
+        const float2 ml = load_f32x2<COHERENT>(part_ml + 2 * (s0 + lane));
+        if (ml.y > 0.f) {
+          w = __expf(ml.x - m);
+          l += w * ml.y;
+        }
+      }
+      const int n = min(64, S - s0);
+#pragma unroll 4
+      for (int i = 0; i < n; ++i) {
+        const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i));
+        const float2 po = load_f32x2<COHERENT>(part_o + (int64_t)(s0 + i) * D + 2 * lane);
+        o0 += wi * po.x;
+        o1 += wi * po.y;
+      }
     }
   }
+  }
+  l = wave_sum(l);
   float2 res;
   if (l > 0.f) {
     const float inv = 1.0f / l;

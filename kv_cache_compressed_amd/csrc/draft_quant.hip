@@ -28,6 +28,7 @@
 // log-sum-exp. (A fused last-workgroup merge would need device-scope fences, which on this
 // multi-XCD part write back and invalidate the L2 of every workgroup's XCD: far dearer than a
 // launch.)
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -44,9 +45,13 @@ constexpr float SCALE_QK = 256.0f;     // 2^8: magnitude headroom of the fp16 QK
 constexpr float SCALE_PV = 256.0f;     // 2^8: same for the PV operand
 constexpr float SUBNORMAL = 16777216.0f;  // 2^24: one fp16 subnormal step is 2^-24
 constexpr float LAZY = 2.0f;           // log2 slack before the running max is moved
+// Workgroups resident per CU (= waves per SIMD); the LDS of a CU (160 KB) is shared among them.
+constexpr int WG_PER_CU = 3;
+constexpr int NUM_CUS = 256;
+constexpr int RING_WAVE_BYTES = (160 * 1024 / WG_PER_CU / WAVES) / 1024 * 1024;
 // LDS: residual split [q 8xD | p 8xRES_MAX | ml 16 | reduction WAVESx8xD] floats; the quantised
-// split uses it for 4 waves x 2 metadata buffers x 2 KB and, after its loop, the wave merge.
-constexpr int SMEM_FLOATS = 8 * D + 8 * RES_MAX + 16 + WAVES * 8 * D;
+// split uses it for one 12 KB ring per wave and, after its loop, the wave merge.
+constexpr int RES_SMEM_FLOATS = 8 * D + 8 * RES_MAX + 16 + WAVES * 8 * D;
 
 struct DQArgs {
   const uint8_t* k_codes;
@@ -60,6 +65,7 @@ struct DQArgs {
   float* lse;
   float* part_o;
   float* part_ml;
+  unsigned* counters;  // one ticket per (b, kv head); zero between calls
   int64_t tok_cap, n_q;
   int r, res_cap, res_dtype, q_dtype;
   int Hkv, Hq, G;
@@ -85,11 +91,152 @@ __device__ __forceinline__ u32x4 unpack4(uint32_t w) {
 }
 
 
-// One split of quantised groups. Every column of a query head h carries the same scores (the
-// head's CPH columns j = CPH*h .. CPH*h + CPH-1 get identical QK operands), so no lane ever needs
-// another lane's score. q*s enters the QK product as an fp16 hi part and an fp16 lo part, in two
-// matrix products accumulated into the same registers (scores keep ~22 significant bits; a single
-// fp16 would move them by up to ~1e-3 in log2 units at outlier channels).
+// Per-wave LDS ring for the quantised split: slot size, 16-byte-per-lane copies per slot, depth,
+// and a small per-wave scratch area after the slots.
+constexpr int DMA_NT = 2;  // cache policy of the ring copies: non-temporal (streamed once)
+constexpr int WAVE_SCRATCH = 1024;
+template <int BITS, bool META_F16>
+struct RingPlan {
+  static constexpr int CB = GROUP * D * BITS / 8;      // one group's key (or value) codes
+  static constexpr int MB = META_F16 ? 512 : 1024;     // one group's key (or value) metadata
+  static constexpr int SLOT = 2 * CB + 2 * MB;
+  static constexpr int LOADS = SLOT / 1024;
+  static constexpr int DEPTH = std::max(2, (RING_WAVE_BYTES - WAVE_SCRATCH) / SLOT);
+  static constexpr int BYTES = DEPTH * SLOT + WAVE_SCRATCH;  // per wave
+  static_assert(SLOT % 1024 == 0, "ring plan");
+};
+
+// Wait until at most `ahead` groups' copies (LOADS each) are still in flight: the copies of the
+// group issued before them have then landed in LDS. The memory clobbers keep the compiler from
+// moving LDS reads across the wait (it does not track direct-to-LDS copies itself).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+template <int LOADS, int DEPTH>
+__device__ __forceinline__ void wait_dma(int ahead) {
+  if (DEPTH > 3 && ahead >= 3) wait_vm<3 * LOADS>();
+  else if (DEPTH > 2 && ahead >= 2) wait_vm<2 * LOADS>();
+  else if (ahead >= 1) wait_vm<LOADS>();
+  else wait_vm<0>();
+}
+
+// The groups of one wave (g_begin + wave, + WAVES, ...) streamed through its LDS ring. A slot holds
+// one group: key codes (CB bytes), value codes (CB), key metadata (MB), value metadata (MB), filled
+// by LOADS 16-byte-per-lane copies; copy z lands at slot + 1024 z + 16 lane. Lane l's operand word
+// u comes from source bytes 16 (l WPL/4 + u), so each lane reads its own words back from
+// consecutive 16-byte LDS cells (no bank conflicts).
+template <int BITS, bool META_F16>
+struct GroupRing {
+  using RP = RingPlan<BITS, META_F16>;
+  static constexpr int WPL = 2 * BITS;  // packed code words per lane per group
+  uint8_t* ring;
+  const uint8_t* src[RP::LOADS];
+  int64_t step[RP::LOADS];
+  int g0, n;  // first group of this wave, number of groups
+
+  __device__ GroupRing(const DQArgs& a, int bh, int g_begin, int g_end, float* smem, int wave, int lane) {
+    ring = reinterpret_cast<uint8_t*>(smem) + wave * RP::BYTES;
+    g0 = g_begin + wave;
+    n = g0 < g_end ? (g_end - g0 + WAVES - 1) / WAVES : 0;
+    const int64_t blk0 = (int64_t)bh * a.tok_cap;  // token 0 of this (b, kv head)
+    constexpr int ROW_BYTES = D * BITS / 8;
+    const uint8_t* kc = a.k_codes + blk0 * ROW_BYTES + lane * 16 * (WPL / 4);
+    const uint8_t* vc = a.v_codes + blk0 * ROW_BYTES + lane * 16 * (WPL / 4);
+    const uint8_t* km = static_cast<const uint8_t*>(a.k_meta) + (int64_t)bh * (a.tok_cap / GROUP) * RP::MB;
+    const uint8_t* vm = static_cast<const uint8_t*>(a.v_meta) + blk0 * (RP::MB / GROUP);
+#pragma unroll
+    for (int u = 0; u < WPL / 4; ++u) {
+      src[u] = kc + 16 * u;
+      src[WPL / 4 + u] = vc + 16 * u;
+      step[u] = step[WPL / 4 + u] = RP::CB;
+    }
+    if (META_F16) {  // one copy: lanes 0-31 key metadata, lanes 32-63 value metadata
+      src[WPL / 2] = lane < 32 ? km + lane * 16 : vm + (lane - 32) * 16;
+      step[WPL / 2] = RP::MB;
+    } else {
+      src[WPL / 2] = km + lane * 16;
+      src[WPL / 2 + 1] = vm + lane * 16;
+      step[WPL / 2] = step[WPL / 2 + 1] = RP::MB;
+    }
+  }
+  __device__ uint8_t* slot(int i) const { return ring + (i % RP::DEPTH) * RP::SLOT; }
+  __device__ uint8_t* scratch() const { return ring + RP::DEPTH * RP::SLOT; }
+  __device__ void issue(int i) {
+    const int g = g0 + WAVES * i;
+    uint8_t* dst = slot(i);
+#pragma unroll
+    for (int z = 0; z < RP::LOADS; ++z) copy16_to_lds<DMA_NT>(src[z] + g * step[z], dst + 1024 * z);
+  }
+  __device__ void start() {
+#pragma unroll
+    for (int i = 0; i < RP::DEPTH - 1; ++i)
+      if (i < n) issue(i);
+  }
+  // Refill the slot freed by group i-1, wait for group i's copies, return its slot.
+  __device__ uint8_t* acquire(int i) {
+    if (i + RP::DEPTH - 1 < n) issue(i + RP::DEPTH - 1);
+    wait_dma<RP::LOADS, RP::DEPTH>(min(RP::DEPTH - 1, n - 1 - i));
+    return slot(i);
+  }
+  // This lane's packed key and value code words of the group in slot sl.
+  __device__ void codes(const uint8_t* sl, int lane, uint32_t* kwd, uint32_t* vwd) const {
+#pragma unroll
+    for (int u = 0; u < WPL / 4; ++u) {
+      const u32x4 kv4 = *reinterpret_cast<const u32x4*>(sl + 1024 * u + 16 * lane);
+      const u32x4 vv4 = *reinterpret_cast<const u32x4*>(sl + 1024 * (WPL / 4 + u) + 16 * lane);
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        kwd[4 * u + z] = kv4[z];
+        vwd[4 * u + z] = vv4[z];
+      }
+    }
+  }
+};
+
+// The four waves' results, staged in LDS as m [WAVES][8] (natural log), l [WAVES][8] and
+// o [WAVES][8][D], merged into this split's partial (device-scope stores, read back by the merge).
+__device__ void write_split_partial(const DQArgs& a, int bh, int split, const float* smem) {
+  const float* s_m = smem;
+  const float* s_l = smem + WAVES * 8;
+  const float* s_o = smem + 2 * WAVES * 8;
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  for (int idx = threadIdx.x; idx < a.G * D; idx += THREADS) {
+    const int hh = idx / D, c = idx % D;
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w)
+      if (s_l[w * 8 + hh] > 0.f) m = fmaxf(m, s_m[w * 8 + hh]);
+    float o = 0.f, l = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float lw = s_l[w * 8 + hh];
+        if (lw > 0.f) {
+          const float f = __expf(s_m[w * 8 + hh] - m);
+          o += f * s_o[(w * 8 + hh) * D + c];
+          l += f * lw;
+        }
+      }
+    }
+    const int64_t row = (int64_t)b * a.Hq + kvh * a.G + hh;
+    store_coherent(a.part_o + (row * a.total_splits + split) * D + c, o);
+    if (c == 0) {
+      store_coherent(a.part_ml + (row * a.total_splits + split) * 2 + 0, m);
+      store_coherent(a.part_ml + (row * a.total_splits + split) * 2 + 1, l);
+    }
+  }
+}
+
+// One split of quantised groups, general form (fp32 metadata, or up to 8 query heads per kv head).
+// Every column of a query head h carries the same scores (the head's CPH columns j = CPH*h ..
+// CPH*h + CPH-1 get identical QK operands), so no lane ever needs another lane's score. q*s enters
+// the QK product as an fp16 hi part and an fp16 lo part, in two matrix products accumulated into
+// the same registers (scores keep ~22 significant bits; a single fp16 would move them by up to
+// ~1e-3 in log2 units at outlier channels).
 //   CPH == 4 (G <= 4): PV column CPH*h + cg carries p * s_cg for value channel group cg, so one PV
 //                      operand serves all eight channel tiles (each lane prepares 8 products).
 //   CPH == 2 (G <= 8): PV uses one operand per channel group (both columns of the head alike).
@@ -97,14 +244,12 @@ __device__ __forceinline__ u32x4 unpack4(uint32_t w) {
 // exact in fp16) against the group's fp16 mins, exact products accumulated in fp32.
 template <int BITS, bool META_F16, int CPH>
 __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
-  constexpr int WPL = 2 * BITS;              // packed code words per lane per block
-  constexpr int ROW_BYTES = D * BITS / 8;
-  constexpr int MB = META_F16 ? 512 : 1024;  // bytes of one group's key (or value) metadata
-  constexpr int MCH = META_F16 ? 1 : 2;      // 16-byte metadata chunks loaded per lane
-  constexpr int NBP = CPH == 4 ? 1 : 4;      // PV B operands per group
+  constexpr int WPL = 2 * BITS;
+  constexpr int MB = RingPlan<BITS, META_F16>::MB;
+  constexpr int NBP = CPH == 4 ? 1 : 4;  // PV B operands per group
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, gq = lane >> 4;
-  const int h = j / CPH, k = j % CPH;        // query head of this column, slot within the head
+  const int h = j / CPH, k = j % CPH;  // query head of this column, slot within the head
   const bool active = h < a.G;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int hq = kvh * a.G + h;
@@ -127,63 +272,25 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
                    pack_f16x2(qv[6], qv[7])};
   }
 
-  const int g_begin = (int)((int64_t)a.ngroups * split / a.splits);
-  const int g_end = (int)((int64_t)a.ngroups * (split + 1) / a.splits);
-  const int64_t ngcap = a.tok_cap / GROUP;
-
-  // per-wave double-buffered LDS copy of one group's key + value metadata
-  uint8_t* mbuf = reinterpret_cast<uint8_t*>(smem) + wave * (4 * MB);
-
   float m_run = -INFINITY, l_lane = 0.f;
   float bv[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // raw loads of one group: code words and this lane's share of the metadata
-  u32x4 kw[WPL / 4], vw[WPL / 4], mw[MCH];
-  auto load_group = [&](int g) {
-    const int64_t blk = (int64_t)bh * a.tok_cap + (int64_t)g * GROUP;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_codes + blk * ROW_BYTES) + lane * (WPL / 4);
-    const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_codes + blk * ROW_BYTES) + lane * (WPL / 4);
-#pragma unroll
-    for (int u = 0; u < WPL / 4; ++u) {
-      kw[u] = __builtin_nontemporal_load(kp + u);
-      vw[u] = __builtin_nontemporal_load(vp + u);
-    }
-    // metadata: key stats of group g (MB bytes) then value stats of its 32 tokens (MB bytes)
-    const uint8_t* kmeta = static_cast<const uint8_t*>(a.k_meta) + ((int64_t)bh * ngcap + g) * MB;
-    const uint8_t* vmeta = static_cast<const uint8_t*>(a.v_meta) + blk * (MB / GROUP);
-#pragma unroll
-    for (int z = 0; z < MCH; ++z) {
-      const int off = z * 1024 + lane * 16;  // byte offset in [key meta | value meta]
-      const uint8_t* src = off < MB ? kmeta + off : vmeta + (off - MB);
-      mw[z] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-    }
-  };
-
-  int buf = 0;
-  if (g_begin + wave < g_end) load_group(g_begin + wave);
-  for (int g = g_begin + wave; g < g_end; g += WAVES, buf ^= 1) {
-    // ---- this group's data to LDS / registers; prefetch the next group ----------------------
-    uint8_t* mb = mbuf + buf * (2 * MB);
-#pragma unroll
-    for (int z = 0; z < MCH; ++z) *reinterpret_cast<u32x4*>(mb + z * 1024 + lane * 16) = mw[z];
+  GroupRing<BITS, META_F16> gr(a, bh, (int)((int64_t)a.ngroups * split / a.splits),
+                               (int)((int64_t)a.ngroups * (split + 1) / a.splits), smem, wave, lane);
+  gr.start();
+  for (int i = 0; i < gr.n; ++i) {
+    const uint8_t* sl = gr.acquire(i);
+    const uint8_t* mb = sl + 2 * RingPlan<BITS, META_F16>::CB;
     uint32_t kwd[WPL], vwd[WPL];
-#pragma unroll
-    for (int u = 0; u < WPL / 4; ++u)
-#pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        kwd[4 * u + z] = kw[u][z];
-        vwd[4 * u + z] = vw[u][z];
-      }
-    if (g + WAVES < g_end) load_group(g + WAVES);
-    wave_lds_sync();
+    gr.codes(sl, lane, kwd, vwd);
     // ---- key bias and QK -------------------------------------------------------------------
     // key metadata in LDS: scales at [c * ESZ], mins at [(D + c) * ESZ]
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     float bias;
-    if (META_F16) {
+    if constexpr (META_F16) {
       f32x4 sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -193,8 +300,8 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
       bias = sb[0] * a.qscale;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const u32x4 sc = *reinterpret_cast<const u32x4*>(mb + (32 * kb + 8 * gq) * 2);
         u32x4 bhi, blo;
+        const u32x4 sc = *reinterpret_cast<const u32x4*>(mb + (32 * kb + 8 * gq) * 2);
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const float q0 = qs[kb * 8 + 2 * e2], q1 = qs[kb * 8 + 2 * e2 + 1];
@@ -242,17 +349,11 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
       bias = sum_over_rows(bias);
     }
     // ---- scores (log2 units) and online softmax with a lazily moved reference max -----------
-    float sc[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = s[tb][r] * (SUBNORMAL / SCALE_QK) + bias;
-        sc[tb * 4 + r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = max_over_rows(mx);
+    // score = s * 2^16 + bias is monotonic in s, so the column max is taken on the raw sums
+    constexpr float KS = SUBNORMAL / SCALE_QK;
+    const float sraw = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    const float mx = fmaf(max_over_rows(sraw), KS, bias);
     // The reference max moves only when a score exceeds it by more than LAZY (log2 units), so
     // weights stay <= 2^LAZY and most groups skip the rescale of the accumulators.
     const bool move = mx > m_run + LAZY;
@@ -266,10 +367,13 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
 #pragma unroll
       for (int cg = 0; cg < 4; ++cg) bv[cg] *= alpha;
     }
+    // weights (columns of absent heads carry finite junk that is never written out)
+    float sc[8];
+    const float off = bias - m_run;
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sc[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
+      sc[e] = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][e & 3], KS, off));
       psum += sc[e];
     }
     l_lane += psum;
@@ -280,19 +384,17 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
       const int cg = k;  // this column's value channel group
       if (META_F16) {
         uint32_t wv[8];
-        float pe[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tok = 16 * (e >> 2) + 4 * gq + (e & 3);
           wv[e] = *reinterpret_cast<const uint32_t*>(mb + MB + tok * 16 + cg * 4);
-          pe[e] = active ? sc[e] : 0.f;
-          bv[0] = mix_fma_hi(pe[e], wv[e], bv[0]);
+          bv[0] = mix_fma_hi(sc[e], wv[e], bv[0]);
         }
         uint32_t pw[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2)
-          pw[e2] = mix_mul_pair(pe[2 * e2] * (SCALE_PV * cls_inv<BITS>(2 * e2)), wv[2 * e2],
-                                pe[2 * e2 + 1] * (SCALE_PV * cls_inv<BITS>(2 * e2 + 1)), wv[2 * e2 + 1]);
+          pw[e2] = mix_mul_pair(sc[2 * e2] * (SCALE_PV * cls_inv<BITS>(2 * e2)), wv[2 * e2],
+                                sc[2 * e2 + 1] * (SCALE_PV * cls_inv<BITS>(2 * e2 + 1)), wv[2 * e2 + 1]);
         bp[0] = u32x4{pw[0], pw[1], pw[2], pw[3]};
       } else {
         float pv[8];
@@ -300,9 +402,8 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
         for (int e = 0; e < 8; ++e) {
           const int tok = 16 * (e >> 2) + 4 * gq + (e & 3);
           const float2 w = *reinterpret_cast<const float2*>(mb + MB + tok * 32 + cg * 8);
-          const float pe = active ? sc[e] : 0.f;
-          pv[e] = pe * w.x * (SCALE_PV * cls_inv<BITS>(e));
-          bv[0] += pe * w.y;
+          pv[e] = sc[e] * w.x * (SCALE_PV * cls_inv<BITS>(e));
+          bv[0] += sc[e] * w.y;
         }
         bp[0] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
                       pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7])};
@@ -326,12 +427,11 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
           svals[0] = w0.x; mvals[0] = w0.y; svals[1] = w0.z; mvals[1] = w0.w;
           svals[2] = w1.x; mvals[2] = w1.y; svals[3] = w1.z; mvals[3] = w1.w;
         }
-        const float pe = active ? sc[e] : 0.f;
-        const float pes = pe * (SCALE_PV * cls_inv<BITS>(e));
+        const float pes = sc[e] * (SCALE_PV * cls_inv<BITS>(e));
 #pragma unroll
         for (int cg = 0; cg < 4; ++cg) {
           pv[cg][e] = pes * svals[cg];
-          bv[cg] += pe * mvals[cg];
+          bv[cg] += sc[e] * mvals[cg];
         }
       }
 #pragma unroll
@@ -348,7 +448,7 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
   }
 
   // ---- wave result -> LDS: m [WAVES][8], l [WAVES][8], o [WAVES][8][D] --------------------
-  __syncthreads();  // every wave is done with its metadata buffers
+  __syncthreads();  // every wave is done with its ring
   float* s_m = smem;
   float* s_l = smem + WAVES * 8;
   float* s_o = smem + 2 * WAVES * 8;
@@ -383,32 +483,200 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
       }
   }
   __syncthreads();
-  // ---- merge the four waves into this split's partial -----------------------------------
-  for (int idx = tid; idx < a.G * D; idx += THREADS) {
-    const int hh = idx / D, c = idx % D;
-    float m = -INFINITY;
+  write_split_partial(a, bh, split, smem);
+}
+
+// Row reductions over the 16 lanes of a DPP row (lanes 16 gq .. 16 gq + 15).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_mov<0x124>(x));  // row_ror:4
+  return fmaxf(x, dpp_mov<0x128>(x));  // row_ror:8
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x124>(x);
+  return x + dpp_mov<0x128>(x);
+}
+
+// One split of quantised groups, fast form for fp16 metadata and up to 4 query heads per kv head.
+// QK^T is computed transposed: the q*s operand is the row operand, with row 4h + r carrying head
+// h's fp16 hi part (r even) or lo part (r odd), built once per (head, channel) per group by the
+// wave into an LDS table; the key codes are the column operand (column = token). Lane (j, gq) then
+// holds head gq's hi and lo sums for token j of each 16-token tile, so a score costs one add and no
+// lane computes another lane's softmax work. The weights go through a 512-byte LDS exchange into
+// the PV operand layout (column 4h + cg carries p * s_cg of value channel group cg), the same PV
+// product as the general form.
+template <int BITS>
+__device__ void quant_split_t(const DQArgs& a, int bh, int split, float* smem) {
+  constexpr int WPL = 2 * BITS;
+  constexpr int MB = RingPlan<BITS, true>::MB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, gq = lane >> 4;
+  const int hp = j >> 2, cg = j & 3;  // PV layout: column j = 4 hp + cg
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  const int64_t qrow0 = (int64_t)b * a.Hq + kvh * a.G;  // query row of head 0 of this kv head
+
+  // The query loads go out first, then the first groups' copies; both are in flight together.
+  const int th = lane >> 4, tc = lane & 15;  // table lane: head th, 8-channel chunk tc
+  // (lanes of absent heads read head G-1 and zero it afterwards)
+  Raw8 qraw[4];
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w)
-      if (s_l[w * 8 + hh] > 0.f) m = fmaxf(m, s_m[w * 8 + hh]);
-    float o = 0.f, l = 0.f;
-    if (m != -INFINITY) {
+  for (int kb = 0; kb < 4; ++kb)
+    qraw[kb] = load8_raw(a.q, (qrow0 + min(hp, a.G - 1)) * D + 32 * kb + 8 * gq, a.q_dtype);
+  const Raw8 traw = load8_raw(a.q, (qrow0 + min(th, a.G - 1)) * D + 8 * tc, a.q_dtype);
+  asm volatile("" ::: "memory");
+  GroupRing<BITS, true> gr(a, bh, (int)((int64_t)a.ngroups * split / a.splits),
+                           (int)((int64_t)a.ngroups * (split + 1) / a.splits), smem, wave, lane);
+  gr.start();
+  float qv[4][8], qt[8];
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) {
-        const float lw = s_l[w * 8 + hh];
-        if (lw > 0.f) {
-          const float f = __expf(s_m[w * 8 + hh] - m);
-          o += f * s_o[(w * 8 + hh) * D + c];
-          l += f * lw;
-        }
+  for (int kb = 0; kb < 4; ++kb) {
+    cvt8(qraw[kb], a.q_dtype, qv[kb]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[kb][e] = hp < a.G ? qv[kb][e] : 0.f;
+  }
+  cvt8(traw, a.q_dtype, qt);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qt[e] = th < a.G ? qt[e] : 0.f;
+
+  // Bias operand: row j carries head j/4's query (channels 32 kb + 8 gq + e) as fp16.
+  u32x4 qh[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    qh[kb] = u32x4{pack_f16x2(qv[kb][0], qv[kb][1]), pack_f16x2(qv[kb][2], qv[kb][3]),
+                   pack_f16x2(qv[kb][4], qv[kb][5]), pack_f16x2(qv[kb][6], qv[kb][7])};
+  // Table operand source: query in log2 units times the fp16 headroom scale over the
+  // slot-position power of element e.
+  float qs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qs[e] = qt[e] * a.qscale * (SCALE_QK * cls_inv<BITS>(e));
+
+  float m_run = -INFINITY;  // head gq
+  float l_lane = 0.f;       // head gq, this lane's tokens
+  float bv = 0.f;           // PV layout: value bias of column j
+  f32x4 acc[8];             // PV layout
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  float* s_p = reinterpret_cast<float*>(gr.scratch());  // [4 heads][32 tokens] weights
+  float* s_alpha = s_p + 128;                            // [4] rescale factors
+  for (int i = 0; i < gr.n; ++i) {
+    uint8_t* sl = gr.acquire(i);
+    const uint8_t* mb = sl + 2 * RingPlan<BITS, true>::CB;
+    uint32_t kwd[WPL], vwd[WPL];
+    gr.codes(sl, lane, kwd, vwd);
+    // ---- key bias: rows 4h.. carry head h's sum_c q_c m_c (exact products) -------------------
+    f32x4 sb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const u32x4 mn = *reinterpret_cast<const u32x4*>(mb + (D + 32 * kb + 8 * gq) * 2);
+      sb = mfma_f16(qh[kb], mn, sb);
+    }
+    const float bias = sb[0] * a.qscale;  // head gq
+    // ---- q*s table over this slot's code words (already in registers; the slot is refilled
+    // only after this group): hi parts at [h][chunk], lo parts at [4 + h][chunk], 16 bytes each
+    u32x4* tbl = reinterpret_cast<u32x4*>(sl);
+    {
+      const u32x4 sc = *reinterpret_cast<const u32x4*>(mb + (lane & 15) * 16);
+      u32x4 thi, tlo;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        thi[e2] = mix_mul2(qs[2 * e2], qs[2 * e2 + 1], sc[e2]);
+        tlo[e2] = mix_rem2(qs[2 * e2], qs[2 * e2 + 1], sc[e2], thi[e2]);
+      }
+      tbl[lane] = thi;
+      tbl[64 + lane] = tlo;
+      wave_lds_order();
+    }
+    // ---- QK^T transposed: s[tb][r] = head gq, part r, token 16 tb + j -------------------------
+    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const u32x4* trow = tbl + (j & 1) * 64 + 16 * (j >> 2) + gq;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const u32x4 aq = trow[4 * kb];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const u32x4 bk = BITS == 2 ? unpack2(kwd[2 * tb + kb / 2], kb & 1) : unpack4(kwd[4 * tb + kb]);
+        s[tb] = mfma_f16(aq, bk, s[tb]);
       }
     }
-    const int64_t row = (int64_t)b * a.Hq + kvh * a.G + hh;
-    a.part_o[(row * a.total_splits + split) * D + c] = o;
-    if (c == 0) {
-      a.part_ml[(row * a.total_splits + split) * 2 + 0] = m;
-      a.part_ml[(row * a.total_splits + split) * 2 + 1] = l;
+    // ---- scores (log2 units), lazily moved reference max, weights ----------------------------
+    constexpr float KS = SUBNORMAL / SCALE_QK;
+    const float z0 = s[0][0] + s[0][1], z1 = s[1][0] + s[1][1];
+    const float mx = fmaf(row16_max(fmaxf(z0, z1)), KS, bias);  // score is monotonic in z
+    const bool move = mx > m_run + LAZY;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      const float m_new = move ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_lane *= alpha;
+      if (j == 0) s_alpha[gq] = alpha;
+      wave_lds_order();
+      const float ap = s_alpha[hp];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= ap;
+      bv *= ap;
+    }
+    const float off = bias - m_run;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(z0, KS, off));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(z1, KS, off));
+    l_lane += p0 + p1;
+    s_p[gq * 32 + j] = p0;
+    s_p[gq * 32 + 16 + j] = p1;
+    wave_lds_order();
+    // ---- PV operand: element e = token 16 (e/4) + 4 gq + e%4 of head hp ----------------------
+    const float4 pa = *reinterpret_cast<const float4*>(s_p + hp * 32 + 4 * gq);
+    const float4 pb = *reinterpret_cast<const float4*>(s_p + hp * 32 + 16 + 4 * gq);
+    const float pe[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    uint32_t wv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tok = 16 * (e >> 2) + 4 * gq + (e & 3);
+      wv[e] = *reinterpret_cast<const uint32_t*>(mb + MB + tok * 16 + cg * 4);
+      bv = mix_fma_hi(pe[e], wv[e], bv);
+    }
+    uint32_t pw[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      pw[e2] = mix_mul_pair(pe[2 * e2] * (SCALE_PV * cls_inv<BITS>(2 * e2)), wv[2 * e2],
+                            pe[2 * e2 + 1] * (SCALE_PV * cls_inv<BITS>(2 * e2 + 1)), wv[2 * e2 + 1]);
+    const u32x4 bp = u32x4{pw[0], pw[1], pw[2], pw[3]};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u32x4 av = BITS == 2 ? unpack2(vwd[t / 2], t & 1) : unpack4(vwd[t]);
+      acc[t] = mfma_f16(av, bp, acc[t]);
     }
   }
+
+  // ---- wave result -> LDS: m [WAVES][8], l [WAVES][8], o [WAVES][8][D] --------------------
+  __syncthreads();  // every wave is done with its ring
+  float* s_m = smem;
+  float* s_l = smem + WAVES * 8;
+  float* s_o = smem + 2 * WAVES * 8;
+  const float l_tot = row16_sum(l_lane);
+  const float bvt = sum_over_rows(bv);
+  if (j == 0 && gq < a.G) {
+    s_m[wave * 8 + gq] = m_run * LN2;  // natural-log units from here on
+    s_l[wave * 8 + gq] = l_tot;
+  }
+  // lane (head hp, column group cg) owns channel tiles 2cg and 2cg + 1
+  if (hp < a.G) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t / 2 != cg) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s_o[(wave * 8 + hp) * D + 16 * t + 4 * gq + r] = acc[t][r] * (SUBNORMAL / SCALE_PV) + bvt;
+    }
+  }
+  __syncthreads();
+  write_split_partial(a, bh, split, smem);
 }
 
 // Residual tokens n_q .. n_q+r-1 from an fp16 ring, on the matrix cores: wave w takes every 4th
@@ -416,6 +684,8 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
 // (fp16 keys times fp16-exact queries: exact products, fp32 sums); values are staged in LDS as
 // channel-major token pairs for the PV product; softmax weights enter as fp16 hi + lo.
 constexpr int RVT = 17;  // dwords per staged value row (16 token pairs + 1 pad)
+static_assert(WAVES * D * RVT <= RES_SMEM_FLOATS && 2 * WAVES * 8 + WAVES * 8 * D <= RES_SMEM_FLOATS,
+              "residual LDS");
 
 __device__ void residual_split_mfma(const DQArgs& a, int bh, int split, float* smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -424,14 +694,17 @@ __device__ void residual_split_mfma(const DQArgs& a, int bh, int split, float* s
   const int h = j / cph, k = j % cph;
   const bool active = h < a.G;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
-  const int hq = kvh * a.G + h;
+  const int hq = kvh * a.G + min(h, a.G - 1);  // absent heads read head G-1, zeroed below
   u32x4 qh[4];
+  Raw8 qraw[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) qraw[kb] = load8_raw(a.q, ((int64_t)b * a.Hq + hq) * D + 32 * kb + 8 * gq, a.q_dtype);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     float qv[8];
+    cvt8(qraw[kb], a.q_dtype, qv);
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      qv[e] = active ? load_as_f32(a.q, ((int64_t)b * a.Hq + hq) * D + 32 * kb + 8 * gq + e, a.q_dtype) : 0.f;
+    for (int e = 0; e < 8; ++e) qv[e] = active ? qv[e] : 0.f;
     qh[kb] = u32x4{pack_f16x2(qv[0], qv[1]), pack_f16x2(qv[2], qv[3]), pack_f16x2(qv[4], qv[5]),
                    pack_f16x2(qv[6], qv[7])};
   }
@@ -567,10 +840,10 @@ __device__ void residual_split_mfma(const DQArgs& a, int bh, int split, float* s
       }
     }
     const int64_t row = (int64_t)b * a.Hq + kvh * a.G + hh;
-    a.part_o[(row * a.total_splits + split) * D + c] = o;
+    store_coherent(a.part_o + (row * a.total_splits + split) * D + c, o);
     if (c == 0) {
-      a.part_ml[(row * a.total_splits + split) * 2 + 0] = m;
-      a.part_ml[(row * a.total_splits + split) * 2 + 1] = l;
+      store_coherent(a.part_ml + (row * a.total_splits + split) * 2 + 0, m);
+      store_coherent(a.part_ml + (row * a.total_splits + split) * 2 + 1, l);
     }
   }
 }
@@ -694,26 +967,54 @@ __device__ void residual_split(const DQArgs& a, int bh, int split, float* smem) 
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) o += s_red[(w * 8 + hh) * D + c];
     const int64_t row = (int64_t)b * a.Hq + kvh * G + hh;
-    a.part_o[(row * a.total_splits + split) * D + c] = o;
+    store_coherent(a.part_o + (row * a.total_splits + split) * D + c, o);
     if (c == 0) {
-      a.part_ml[(row * a.total_splits + split) * 2 + 0] = s_ml[2 * hh];
-      a.part_ml[(row * a.total_splits + split) * 2 + 1] = s_ml[2 * hh + 1];
+      store_coherent(a.part_ml + (row * a.total_splits + split) * 2 + 0, s_ml[2 * hh]);
+      store_coherent(a.part_ml + (row * a.total_splits + split) * 2 + 1, s_ml[2 * hh + 1]);
     }
   }
 }
 
+// Ticket: the last workgroup of a (b, kv head) to finish merges every split's partial (read back
+// past the non-coherent caches) and returns the ticket to zero. Partials are written with
+// device-scope stores and waited for before the ticket is taken, so no cache-wide fence is needed.
+__device__ void merge_if_last(const DQArgs& a, int bh, float* smem) {
+  wait_vm<0>();
+  __syncthreads();
+  int* s_last = reinterpret_cast<int*>(smem);
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == (unsigned)(a.total_splits - 1);
+    if (last) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = last;
+  }
+  __syncthreads();
+  if (!*s_last) return;
+  const int wave = threadIdx.x >> 6;
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  for (int hh = wave; hh < a.G; hh += WAVES) {
+    const int64_t row = (int64_t)b * a.Hq + kvh * a.G + hh;
+    merge_row_wave<true>(a.part_o + row * a.total_splits * D, a.part_ml + row * a.total_splits * 2,
+                         a.total_splits, a.out + row * D, a.lse ? a.lse + row : nullptr);
+  }
+}
+
 template <int BITS, bool META_F16, bool RES_F16, int CPH>
-__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 4))) draft_quant_kernel(DQArgs a) {
-  __shared__ float smem[SMEM_FLOATS];
+__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WG_PER_CU, WG_PER_CU))) draft_quant_kernel(DQArgs a) {
+  __shared__ float smem[std::max(WAVES * RingPlan<BITS, META_F16>::BYTES / 4, RES_SMEM_FLOATS)];
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
-  if (split < a.splits)
-    quant_split<BITS, META_F16, CPH>(a, bh, split, smem);
+  if (split < a.splits) {
+    if constexpr (META_F16 && CPH == 4)
+      quant_split_t<BITS>(a, bh, split, smem);
+    else
+      quant_split<BITS, META_F16, CPH>(a, bh, split, smem);
+  }
   else if (RES_F16 && a.q_dtype != VC_F32)
     residual_split_mfma(a, bh, split, smem);
   else
     residual_split<RES_F16>(a, bh, split, smem);
-
+  merge_if_last(a, bh, smem);
 }
 
 }  // namespace
@@ -724,13 +1025,13 @@ DraftQuantPlan plan_draft_quant(const vc_kivi& c, int64_t n_q, int Hq) {
   const int64_t units = (int64_t)c.B * c.Hkv;
   // One resident round of workgroups: 256 CUs x 3 workgroups (the kernel is built for 3 waves
   // per SIMD), counting the residual split of every (b, kv head); at least 2 groups per wave.
-  int64_t s = std::max<int64_t>(1, 768 / units - 1);
+  int64_t s = std::max<int64_t>(1, NUM_CUS * WG_PER_CU / units - 1);
   s = std::min<int64_t>(s, std::max<int64_t>(1, ngroups / 8));
   if (ngroups == 0) s = 0;
   p.splits = (int)s;
   p.total_splits = p.splits + 1;
   const size_t rows = (size_t)c.B * Hq;
-  p.ws_bytes = rows * p.total_splits * (D + 2) * sizeof(float);
+  p.ws_bytes = DRAFT_COUNTER_BYTES + rows * p.total_splits * (D + 2) * sizeof(float);
   return p;
 }
 
@@ -748,7 +1049,8 @@ hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* 
   a.out = out;
   a.lse = lse;
   const size_t rows = (size_t)c.B * Hq;
-  a.part_o = static_cast<float*>(ws);
+  a.counters = static_cast<unsigned*>(ws);
+  a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + DRAFT_COUNTER_BYTES);
   a.part_ml = a.part_o + rows * plan.total_splits * D;
   a.tok_cap = c.tok_cap;
   a.n_q = n_q;
@@ -779,9 +1081,7 @@ hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* 
     else { if (f16r) VC_DQ_LAUNCH(4, false, true); else VC_DQ_LAUNCH(4, false, false); }
   }
 #undef VC_DQ_LAUNCH
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  return launch_merge(a.part_o, a.part_ml, (int64_t)rows, plan.total_splits, out, lse, s);
+  return hipGetLastError();
 }
 
 }  // namespace vc

@@ -20,6 +20,8 @@ hipError_t launch_merge(const float* part_o, const float* part_ml, int64_t rows,
                         float* out, float* lse, hipStream_t s);
 
 // Draft over the quantised cache.
+// Ticket counters at the start of a draft workspace: one per (b, kv head), at most 16384.
+constexpr size_t DRAFT_COUNTER_BYTES = 65536;
 struct DraftQuantPlan {
   int splits;        // quantised-token splits per (b, kv head)
   int total_splits;  // splits + 1 (the residual split)

@@ -261,6 +261,44 @@ def test_draft_quant_edges(gpu_lib, n_q_zero):
         assert abs(lse[0, h].item() - l) < 2e-3
 
 
+def test_draft_quant_ticket_merge_repeatable(gpu_lib):
+    """The in-kernel merge (last workgroup of each (b, kv head) merges the splits) gives bitwise
+    identical outputs on every call, leaves the ticket counters at zero, and one workspace serves
+    calls of different shapes in turn."""
+    w = W_SMALL["c2s"]
+    K, V, Kn, Vn, Q, W = _inputs(w)
+    c = _cache_for(w)
+    Kd, Vd = torch.from_numpy(K).to("cuda", torch.bfloat16), torch.from_numpy(V).to("cuda", torch.bfloat16)
+    vc.vc_quantize_kv(c, Kd, Vd, 0, w.n_q)
+    r = w.n - w.n_q
+    vc.vc_kivi_append(c, Kd[:, :, w.n_q:], Vd[:, :, w.n_q:], w.n_q, r, src_bh_stride=w.n * 128)
+    q = torch.from_numpy(Q[:, :, 0]).to("cuda", torch.bfloat16).contiguous()
+    big = max(vc.vc_draft_quant_workspace(c, w.n_q, r, w.Hq), vc.vc_draft_quant_workspace(c, 64, r, w.Hq))
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    outs = {}
+    for rep in range(12):
+        for n_q in (w.n_q, 64):  # alternate shapes (different split counts) on one workspace
+            out = torch.zeros((w.B, w.Hq, 128), device="cuda")
+            lse = torch.zeros((w.B, w.Hq), device="cuda")
+            vc.vc_draft_attn_quant(c, n_q, r, q, out, lse, ws, harness.SM_SCALE)
+            torch.cuda.synchronize()
+            if n_q not in outs:
+                outs[n_q] = (out.clone(), lse.clone())
+            else:
+                assert torch.equal(out, outs[n_q][0]) and torch.equal(lse, outs[n_q][1]), f"rep {rep} n_q {n_q}"
+            assert int(ws[:65536].view(torch.int32).abs().sum().item()) == 0, "tickets not returned to zero"
+    # the short call is right too: first 64 quantised tokens + the same ring slots, which hold
+    # tokens n_q.. because n_q = 64 (mod res_cap) for this workload
+    assert w.n_q % w.res_cap == 64
+    for h in range(0, w.Hq, 5):
+        lay = oq.KiviLayer(K[0, h // w.G], V[0, h // w.G], 64, w.bits, w.meta_dtype, w.res_dtype)
+        ring = oq.KiviLayer(K[0, h // w.G], V[0, h // w.G], w.n_q, w.bits, w.meta_dtype, w.res_dtype)
+        keys = np.concatenate([lay.keys(0), ring.keys(r)[w.n_q:]])
+        vals = np.concatenate([lay.values(0), ring.values(r)[w.n_q:]])
+        o, l = oatt.decode(Q[0, h, 0], keys, vals)
+        _close(outs[64][0][0, h].cpu().numpy(), o, True, TIGHT["draft_quant"], f"short call h={h}")
+
+
 @pytest.mark.parametrize("name", ["c3s"])
 def test_draft_drop_parity(gpu_lib, name):
     w = W_SMALL[name]
