@@ -59,6 +59,7 @@ class RoundState:
             self.v_store[:, :, n:n + L] = self.v_blk
         # drafter caches
         self.ws_draft = vc.Workspace(device)
+        self._ws_sizes = {}
         self.ws_verify = vc.Workspace(device)
         self.replicas = []
         if w.drafter == "kivi":
@@ -128,7 +129,10 @@ class RoundState:
         if w.drafter == "kivi":
             c = cache or self.replicas[0]
             r = (w.n - w.n_q) + j + 1
-            nb = vc.vc_draft_quant_workspace(c, w.n_q, r, w.Hq)
+            key = (id(c), w.n_q, r)
+            nb = self._ws_sizes.get(key)
+            if nb is None:
+                nb = self._ws_sizes[key] = vc.vc_draft_quant_workspace(c, w.n_q, r, w.Hq)
             vc.vc_draft_attn_quant(c, w.n_q, r, self.q_draft[j], self.out_d[j], self.lse_d[j],
                                    self.ws_draft.get(nb), SM_SCALE)
         else:
@@ -235,6 +239,30 @@ class RoundState:
         w = self.w
         keys = sum(w.n + i + 1 for i in range(w.L))
         return 4 * 128 * w.B * w.Hq * keys
+
+    def capture_round(self):
+        """Capture one whole round (every launch of run_round, in order) into a HIP graph, after an
+        eager round that sizes every workspace. Each replay redoes the round on the same inputs:
+        the residual appends rewrite the same ring slots, so replays are idempotent. Not for the
+        host-streamed verify (its copy-stream events are not captured)."""
+        assert not self.w.past_on_host, "graph capture covers HBM-resident rounds only"
+        self.run_round()
+        torch.cuda.synchronize()
+        rep0 = self._rep
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                self.run_round()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self._rep = rep0
+        self.graph = g
+        return g
+
+    def replay_round(self):
+        self.graph.replay()
 
     def results(self) -> dict:
         torch.cuda.synchronize()

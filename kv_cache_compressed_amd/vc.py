@@ -132,9 +132,13 @@ class KiviCache:
         self.v_res = torch.zeros_like(self.k_res)
 
     def desc(self) -> vc_kivi:
-        return vc_kivi(self.bits, 32, self.meta_dtype, self.res_dtype, self.B, self.Hkv, self.d,
-                       self.res_cap, self.tok_cap, _ptr(self.k_codes), _ptr(self.v_codes),
-                       _ptr(self.k_meta), _ptr(self.v_meta), _ptr(self.k_res), _ptr(self.v_res))
+        """The C descriptor (built once: the buffers never move)."""
+        if getattr(self, "_desc", None) is None:
+            self._desc = vc_kivi(self.bits, 32, self.meta_dtype, self.res_dtype, self.B, self.Hkv,
+                                 self.d, self.res_cap, self.tok_cap, _ptr(self.k_codes),
+                                 _ptr(self.v_codes), _ptr(self.k_meta), _ptr(self.v_meta),
+                                 _ptr(self.k_res), _ptr(self.v_res))
+        return self._desc
 
 
 class Workspace:

@@ -299,6 +299,28 @@ def test_draft_quant_ticket_merge_repeatable(gpu_lib):
         _close(outs[64][0][0, h].cpu().numpy(), o, True, TIGHT["draft_quant"], f"short call h={h}")
 
 
+def test_round_graph_replays_match_eager(gpu_lib):
+    """A round captured as a HIP graph gives, on every replay, exactly the eager round's outputs
+    (outputs are cleared before each replay; eager work and syncs run between replays)."""
+    w = W_SMALL["c2s"]
+    st = harness.RoundState(w, inputs=_inputs(w), replicas=2)
+    st.run_round()
+    ref = st.results()
+    st.capture_round()
+    bufs = [st.out_d, st.lse_d, st.out_v, st.lse_v, st.logits_d, st.logits_v, st.accept_len, st.next_tok]
+    for rep in range(3):
+        for t in bufs:
+            t.zero_()
+        torch.cuda.synchronize()
+        st.replay_round()
+        torch.cuda.synchronize()
+        got = st.results()
+        for k in ("out_d", "lse_d", "out_v", "lse_v", "drafts", "verified", "a", "next"):
+            assert np.array_equal(got[k], ref[k]), f"replay {rep}: {k} differs"
+        st.run_round()  # eager round between replays
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("name", ["c3s"])
 def test_draft_drop_parity(gpu_lib, name):
     w = W_SMALL[name]
