@@ -15,19 +15,19 @@
 // code * 4^p * 2^-24 for the slot position p), which costs one AND per two codes; the power of
 // four of the slot position is divided out of the other operand. The other operand (q_c s_gc in
 // the QK product, p_t s_tcg in the PV product) is prepared once per 32-token group: q s as an fp16
-// hi + lo pair in two matrix columns (scores keep ~22 significant bits), p s as one fp16 (the
-// weights enter the output linearly).
+// hi + lo pair (scores keep ~22 significant bits), p s as one fp16 (the weights enter the output
+// linearly).
 //
-// Work split. Workgroup = 4 waves on one (b, kv head) and one contiguous range of groups (a
-// split); wave w takes every 4th group of the range. Lane l of a wave is (column j = l % 16,
-// row block gq = l / 16); column j = 2h + hl carries query head h (hl = 0: hi part, 1: lo part),
-// so up to 8 query heads share each code load. The scores of a 16-token tile come back in the
-// layout the PV product needs as its B operand, so softmax weights never cross lanes. The
-// residual tokens (n_q .. n_q+r-1, fp16/fp32 ring) form one extra split computed on the vector
-// ALUs. Each split writes an unnormalised partial (o, m, l); a small second kernel merges them with
-// log-sum-exp. (A fused last-workgroup merge would need device-scope fences, which on this
-// multi-XCD part write back and invalidate the L2 of every workgroup's XCD: far dearer than a
-// launch.)
+// Work split. Workgroup = 4 waves on one (b, kv head) and one contiguous range of 32-token groups
+// (a split); wave w takes every 4th group of the range and streams them through its own LDS ring
+// with direct global -> LDS copies (several groups in flight, no registers held). With fp16
+// metadata and up to 4 query heads per kv head, QK^T runs transposed against an LDS table of the
+// group's q*s operands so each lane owns one head's scores (quant_split_t); the general form keeps
+// a head's scores in CPH identical columns (quant_split). The residual tokens (n_q .. n_q+r-1, an
+// fp16 or fp32 ring) form one extra split. Each split writes an unnormalised partial (o, m, l)
+// with device-scope stores; the last workgroup of the (b, kv head) to finish (a ticket counter in
+// the workspace) merges them with log-sum-exp, so one kernel does the whole call and no
+// cache-wide fence is needed.
 #include <algorithm>
 #include <type_traits>
 
