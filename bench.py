@@ -34,6 +34,27 @@ DRAFT_SRC = os.path.join(ROOT, "kv_cache_compressed_amd", "csrc", "draft_quant.h
 
 METRIC = "draft/verify attention GB/s (% of 8 TB/s HBM) + verified tokens/s at 32K ctx"
 
+DRAFT_NAME = {("kivi", 2): "draft attention over the 2-bit KIVI cache",
+              ("kivi", 4): "draft attention over the 4-bit KIVI cache",
+              ("drop", 0): "draft attention over the kept positions (token dropping)"}
+WORKLOAD_TEXT = {
+    "c1": "one attention layer, batch 1, 32/8 heads, d 128, context 2048, fp32 Q/K/V, KIVI 4-bit "
+          "(group 32, fp32 residual 32, fp32 metadata), draft length 8, 9-row causal verify",
+    "c2": "Llama-3.1-8B-shaped layer, batch 8, context 32768, 32/8 heads, d 128, KIVI 2-bit (group 32, "
+          "fp16 residual 128, fp16 metadata), draft length 30, 31-row causal verify over HBM-resident "
+          "bf16 KV",
+    "c3": "Llama-70B-shaped layer, batch 4, context 100000, 64/8 heads, d 128, token-dropping drafter "
+          "(25% kept: 64 sinks + 256 recent + top-scoring), draft length 30, 31-row causal verify over "
+          "HBM-resident bf16 KV",
+    "c4": "Llama-3.1-8B-shaped layer, batch 1, context 500000, 32/8 heads, d 128, full bf16 KV in pinned "
+          "host memory streamed in 65536-token chunks, KIVI 4-bit drafter (fp16 residual 128, fp16 "
+          "metadata) in HBM, draft length 30, 31-row causal verify"}
+DATA_TEXT = {
+    "c1": "synthetic (seeded N(0,1) fp32 Q/K/V, random fp32 logits projection)",
+    "c2": "synthetic (seeded N(0,1) bf16 KV with 1% x8 outlier channels, random fp32 logits projection)",
+    "c3": "synthetic (seeded N(0,1) bf16 KV, seeded keep-list scores, random fp32 logits projection)",
+    "c4": "synthetic (seeded N(0,1) bf16 KV, random fp32 logits projection)"}
+
 
 def _src_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
@@ -80,6 +101,30 @@ def cpu_baseline(w, inputs, a_plus_1: int, draft_steps: int, verify_heads: int):
             "sample": sample, "seconds_per_round_est": t_round}
 
 
+def _h2d_rate(torch, st) -> dict:
+    """Achieved pinned host -> HBM rate of a plain copy of the streamed verify's bytes, in the same
+    chunks (median of 5 passes)."""
+    w = st.w
+    ct = w.chunk_tokens
+    dk = torch.empty((w.B, w.Hkv, ct, 128), dtype=st.k_host.dtype, device="cuda")
+    dv = torch.empty_like(dk)
+    nbytes = 2 * st.k_host.numel() * st.k_host.element_size()
+    times = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for c0 in range(0, w.n, ct):
+            ln = min(ct, w.n - c0)
+            for b in range(w.B):  # one contiguous pinned -> device copy per (b, kv head) slice
+                for h in range(w.Hkv):
+                    dk[b, h, :ln].copy_(st.k_host[b, h, c0:c0 + ln], non_blocking=True)
+                    dv[b, h, :ln].copy_(st.v_host[b, h, c0:c0 + ln], non_blocking=True)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"bytes": nbytes, "seconds": t, "GB_s": nbytes / t / 1e9}
+
+
 def _back_to_back_us(torch, launch, n: int) -> float:
     """Mean duration of n launches enqueued back to back between two events (microseconds)."""
     for i in range(3):
@@ -109,6 +154,11 @@ def main():
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the rounds, run a plain device-to-device copy of this many MB three "
                          "times (reference kernel of known traffic for HBM counter runs)")
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4"],
+                    help="c2 (default, the headline line): 8 x 32K, KIVI 2-bit. c1: 1 x 2048 fp32, "
+                         "KIVI 4-bit. c3: 4 x 100K, Llama-70B-shaped, token-dropping drafter (25%% "
+                         "kept). c4: 1 x 500K, full KV in pinned host memory streamed in 64K-token "
+                         "chunks, KIVI 4-bit drafter")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every launch of a round from Python instead of replaying the "
                          "round captured as a HIP graph")
@@ -127,12 +177,18 @@ def main():
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
         sys.exit(1)
 
-    w = synth.WORKLOADS["c2"]
+    w = synth.WORKLOADS[args.workload]
     t_setup = time.perf_counter()
     K, V = synth.kv_past(w, args.seed)
     Kn, Vn = synth.kv_new(w, args.seed)
     inputs = (K, V, Kn, Vn, synth.q_new(w, args.seed), synth.projection(w, args.seed))
-    st = harness.RoundState(w, seed=args.seed, inputs=inputs, replicas=args.replicas)
+    idx = None
+    if w.drafter == "drop":
+        idx = [[synth.keep_list(w, args.seed, b, h) for h in range(w.Hkv)] for b in range(w.B)]
+    st = harness.RoundState(w, seed=args.seed, inputs=inputs, idx_lists=idx,
+                            replicas=args.replicas if w.drafter == "kivi" else 1)
+    if w.past_on_host:
+        args.eager = True  # the host-streamed verify's copy-stream events are not captured
     torch.cuda.synchronize()
     print(f"# setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
 
@@ -164,9 +220,11 @@ def main():
     # Kernel durations for the roofline: the same launches (draft steps 0..29 over the rotating
     # replicas, the round's verify) enqueued back to back between two events on the launch stream,
     # so host enqueue time cannot show up as kernel time.
-    d_kernel_us = _back_to_back_us(torch, lambda i: st.draft_attention(i % w.x, st.replicas[i % len(st.replicas)]),
+    reps = st.replicas or [None]
+    d_kernel_us = _back_to_back_us(torch, lambda i: st.draft_attention(i % w.x, reps[i % len(reps)]),
                                    3 * w.x)
-    v_kernel_us = _back_to_back_us(torch, lambda i: st.verify_attention(), 10)
+    v_kernel_us = _back_to_back_us(torch, lambda i: st.verify_attention(), 3 if w.past_on_host else 10)
+    h2d = _h2d_rate(torch, st) if w.past_on_host else None
     a_plus_1 = int((res["a"] + 1).sum())
     tok_s = a_plus_1 / (elapsed / args.steps)
 
@@ -190,18 +248,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 KV with 1% x8 outlier channels, random fp32 logits projection)",
-        "config": {"workload": "Llama-3.1-8B-shaped layer, batch 8, context 32768, 32/8 heads, d 128, "
-                               "KIVI 2-bit (group 32, fp16 residual 128, fp16 metadata), draft length 30, "
-                               "31-row causal verify over HBM-resident bf16 KV",
+        "dtype": "f32" if w.kv_dtype == "f32" else "bf16",
+        "data": DATA_TEXT[args.workload],
+        "config": {"workload": WORKLOAD_TEXT[args.workload],
                    "global_batch": w.B, "seq_len": w.n, "parallelism": "single GPU",
                    "compressed_cache_replicas": args.replicas,
                    "round_launch": "eager" if args.eager else "hip graph replay"},
-        "roofline": {"bound": "hbm", "kernel": "draft attention over the 2-bit KIVI cache",
+        "roofline": {"bound": "hbm", "kernel": DRAFT_NAME[w.drafter, w.bits],
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
+                     "traffic": traffic if args.workload == "c2" else None,
                      "bytes_per_launch": int(d_bytes), "launch_us": round(d_kernel_us, 2)},
         "draft_attention": {"launch_us": round(d_kernel_us, 2), "GB_s": round(achieved, 1),
                             "TFLOP_s": round(d_flops / d_mean_s / 1e12, 2)},
@@ -212,7 +268,15 @@ def main():
         "round": {"accepted": [int(a) for a in res["a"]], "emitted_per_round": a_plus_1,
                   "positions_verified_per_s": round(w.B * w.L / (elapsed / args.steps), 1)},
     }
-    if not args.no_cpu_baseline:
+    if h2d is not None:
+        v_gbs_pcie = st.verify_bytes() / v_mean_s / 1e9
+        line["verify_attention"]["pcie"] = {
+            "bound": "pcie", "achieved": round(v_gbs_pcie, 2), "peak": round(h2d["GB_s"], 2),
+            "unit": "GB/s", "frac": round(v_gbs_pcie / h2d["GB_s"], 4),
+            "peak_is": "achieved pinned host->device rate of a plain copy of the same bytes in the "
+                       "same 64K-token chunks (median of 5)",
+            "frac_of_64GBs": round(v_gbs_pcie / 64.0, 4)}
+    if not args.no_cpu_baseline and args.workload == "c2":
         line["cpu_baseline"] = cpu_baseline(w, inputs, a_plus_1, args.cpu_draft_steps,
                                             args.cpu_verify_heads)
     print(json.dumps(line), flush=True)

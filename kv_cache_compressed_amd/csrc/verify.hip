@@ -48,28 +48,99 @@ struct VArgs {
   float* part_ml;
 };
 
-__device__ __forceinline__ uint32_t bf16_pack_rne(float lo, float hi) {
-  const uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-  const uint32_t ra = (a + 0x7fffu + ((a >> 16) & 1u)) >> 16;
-  const uint32_t rb = (b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u;
-  return ra | rb;
+constexpr float LAZY = 2.0f;  // log2 slack before a row's reference max is moved
+
+// One key/value tile (32 tokens x 128 channels) in flight in registers: KI 16-byte key chunks and
+// VI token pairs of 16-byte value chunks per thread.
+template <int NT>
+struct TileRegs {
+  static constexpr int KI = (TK * (D / 8) + NT - 1) / NT;
+  static constexpr int VI = ((TK / 2) * (D / 8) + NT - 1) / NT;
+  u32x4 k[KI];
+  u32x4 v0[VI], v1[VI];
+};
+
+// Issue the loads of tile `tile` through buffer resources whose size is the source's ntok rows,
+// so rows past the end read as zero with no per-row checks; each thread's byte offsets are fixed
+// and the tile offset is a uniform scalar.
+constexpr int RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit data format
+template <int NT>
+__device__ __forceinline__ void tile_load(TileRegs<NT>& r, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          int64_t tile, bool live) {
+  const int tid = threadIdx.x;
+  const int sbase = live ? (int)(tile * TK * D * 2) : 0x7fffff00;  // dead tiles: out of range -> 0
+  // Every load is unconditional (threads past an item range re-read a valid item and do not store
+  // it), so the loads form straight-line code the compiler can count precisely.
+#pragma unroll
+  for (int z = 0; z < TileRegs<NT>::KI; ++z) {
+    const int idx = (tid + z * NT) % (TK * (D / 8));
+    const int t = idx / (D / 8), c8 = idx % (D / 8);
+    r.k[z] = __builtin_amdgcn_raw_buffer_load_b128(rk, t * D * 2 + c8 * 16, sbase, 0);
+  }
+#pragma unroll
+  for (int z = 0; z < TileRegs<NT>::VI; ++z) {
+    const int idx = (tid + z * NT) % ((TK / 2) * (D / 8));
+    const int tp = idx % (TK / 2), c8 = idx / (TK / 2);
+    r.v0[z] = __builtin_amdgcn_raw_buffer_load_b128(rv, 2 * tp * D * 2 + c8 * 16, sbase, 0);
+    r.v1[z] = __builtin_amdgcn_raw_buffer_load_b128(rv, (2 * tp + 1) * D * 2 + c8 * 16, sbase, 0);
+  }
 }
 
-__global__ void __launch_bounds__(512) verify_bf16_kernel(VArgs a) {
-  __shared__ uint16_t s_k[TK * K_STRIDE];
-  __shared__ uint32_t s_vt[D * VT_STRIDE];
+// Write a loaded tile to LDS: keys row-major (padded rows), values transposed to channel-major
+// token pairs: s_vt[c][tp] = (v[2tp][c], v[2tp+1][c]).
+template <int NT>
+__device__ __forceinline__ void tile_store(const TileRegs<NT>& r, uint16_t* s_k, uint32_t* s_vt) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int z = 0; z < TileRegs<NT>::KI; ++z) {
+    const int idx = tid + z * NT;
+    const int t = idx / (D / 8), c8 = idx % (D / 8);
+    if (idx < TK * (D / 8)) *reinterpret_cast<u32x4*>(s_k + t * K_STRIDE + c8 * 8) = r.k[z];
+  }
+#pragma unroll
+  for (int z = 0; z < TileRegs<NT>::VI; ++z) {
+    const int idx = tid + z * NT;
+    const int tp = idx % (TK / 2), c8 = idx / (TK / 2);
+    if (idx < (TK / 2) * (D / 8)) {
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        s_vt[(c8 * 8 + 2 * y) * VT_STRIDE + tp] = __builtin_amdgcn_perm(r.v1[z][y], r.v0[z][y], 0x05040100u);
+        s_vt[(c8 * 8 + 2 * y + 1) * VT_STRIDE + tp] = __builtin_amdgcn_perm(r.v1[z][y], r.v0[z][y], 0x07060302u);
+      }
+    }
+  }
+}
+
+// Workgroup = NW waves (NW >= G) on one (b, kv head) and one range of 32-token tiles; wave w < G
+// owns query head kvh*G + w and its L rows (two 16-row column tiles); all NW waves stage tiles.
+// Tiles are double-buffered in LDS and loaded two tiles ahead into registers, so each tile costs
+// one barrier and its loads overlap the two tiles before it.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) verify_bf16_kernel(VArgs a) {
+  constexpr int NT = 64 * NW;
+  __shared__ uint16_t s_k[2][TK * K_STRIDE];
+  __shared__ uint32_t s_vt[2][D * VT_STRIDE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nthreads = blockDim.x;
   const int j = lane & 15, gq = lane >> 4;
   const int bh = blockIdx.y, split = blockIdx.x;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
-  const int hq = kvh * a.G + wave;
+  const bool computes = wave < a.G;
+  const int hq = kvh * a.G + min(wave, a.G - 1);
 
   // tile range of this split
   const int64_t ntiles = (a.ntok + TK - 1) / TK;
   const int64_t t_begin = ntiles * split / a.splits;
   const int64_t t_end = ntiles * (split + 1) / a.splits;
+  const int nbytes = (int)(a.ntok * D * 2);  // this (b, kv head)'s source rows
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.k + (int64_t)bh * a.bh_stride * D), (short)0, nbytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.v + (int64_t)bh * a.bh_stride * D), (short)0, nbytes, RSRC_WORD3);
+
+  TileRegs<NT> ra, rb;
+  tile_load<NT>(ra, rk, rv, t_begin, t_begin < t_end);
+  tile_load<NT>(rb, rk, rv, t_begin + 1, t_begin + 1 < t_end);
 
   // Q^T operand: column tile ct holds rows 16ct + j; lane holds channels 32kb + 8gq + 0..7.
   u32x4 qop[2][4];
@@ -95,104 +166,107 @@ __global__ void __launch_bounds__(512) verify_bf16_kernel(VArgs a) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* kbase = a.k + (int64_t)bh * a.bh_stride * D;
-  const uint16_t* vbase = a.v + (int64_t)bh * a.bh_stride * D;
+  tile_store<NT>(ra, s_k[0], s_vt[0]);
+  __syncthreads();
 
-  for (int64_t tile = t_begin; tile < t_end; ++tile) {
-    const int64_t tok0 = tile * TK;
-    const int tlen = (int)min<int64_t>(TK, a.ntok - tok0);
-    __syncthreads();  // previous tile fully consumed
-    // ---- stage keys (row-major) ---------------------------------------------------------
-    for (int idx = tid; idx < TK * (D / 8); idx += nthreads) {
-      const int t = idx / (D / 8), c8 = idx % (D / 8);
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if (t < tlen) val = *reinterpret_cast<const u32x4*>(kbase + (tok0 + t) * D + c8 * 8);
-      *reinterpret_cast<u32x4*>(s_k + t * K_STRIDE + c8 * 8) = val;
-    }
-    // ---- stage values transposed: s_vt[c][tp] = (v[2tp][c], v[2tp+1][c]) -------------------
-    for (int idx = tid; idx < (TK / 2) * (D / 8); idx += nthreads) {
-      const int tp = idx % (TK / 2), c8 = idx / (TK / 2);
-      u32x4 v0 = u32x4{0u, 0u, 0u, 0u}, v1 = u32x4{0u, 0u, 0u, 0u};
-      if (2 * tp < tlen) v0 = *reinterpret_cast<const u32x4*>(vbase + (tok0 + 2 * tp) * D + c8 * 8);
-      if (2 * tp + 1 < tlen) v1 = *reinterpret_cast<const u32x4*>(vbase + (tok0 + 2 * tp + 1) * D + c8 * 8);
+  // One tile: compute `tile` from LDS buffer `cur`; `ahead` holds tile+1 (loaded), `free` is
+  // reloaded with tile+2, then `ahead` goes to the other buffer.
+  auto step = [&](int64_t tile, int cur, TileRegs<NT>& free, TileRegs<NT>& ahead) {
+    tile_load<NT>(free, rk, rv, tile + 2, tile + 2 < t_end);
+    if (computes && tile < t_end) {
+      const int64_t tok0 = tile * TK;
+      const int tlen = (int)min<int64_t>(TK, a.ntok - tok0);
+      const uint16_t* sk = s_k[cur];
+      const uint32_t* svt = s_vt[cur];
+      // ---- QK^T: S^T[token][row] ----------------------------------------------------------
+      f32x4 s[2][2];
 #pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        // channels 8c8 + 2z (low halves) and 8c8 + 2z + 1 (high halves)
-        s_vt[(c8 * 8 + 2 * z) * VT_STRIDE + tp] = __builtin_amdgcn_perm(v1[z], v0[z], 0x05040100u);
-        s_vt[(c8 * 8 + 2 * z + 1) * VT_STRIDE + tp] = __builtin_amdgcn_perm(v1[z], v0[z], 0x07060302u);
+      for (int tb = 0; tb < 2; ++tb) {
+        u32x4 kop[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          kop[kb] = *reinterpret_cast<const u32x4*>(sk + (16 * tb + j) * K_STRIDE + 32 * kb + 8 * gq);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) c = mfma_bf16(kop[kb], qop[ct][kb], c);
+          s[tb][ct] = c;
+        }
+      }
+      // ---- masked online softmax per query row, lazily moved reference max ------------------
+      // (scores are scaled inside the exponent: the max is taken on the raw products)
+      const bool masked = a.causal || tlen < TK;
+      u32x4 phi[2], plo[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int row = 16 * ct + j;
+        float raw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) raw[e] = s[e >> 2][ct][e & 3];
+        if (masked) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int tok = 16 * (e >> 2) + 4 * gq + (e & 3);
+            bool ok = tok < tlen;
+            if (a.causal) ok = ok && (tok0 + tok <= row);
+            raw[e] = ok ? raw[e] : -INFINITY;
+          }
+        }
+        const float mraw = fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])),
+                                 fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])));
+        const float mx = max_over_rows(mraw) * a.qscale;
+        const bool move = mx > m_run[ct] + LAZY;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+          const float m_new = move ? mx : m_run[ct];
+          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[ct] - m_new);
+          m_run[ct] = m_new;
+          l_lane[ct] *= alpha;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[ct][t] *= alpha;
+        }
+        const float nref = m_run[ct] == -INFINITY ? 0.f : -m_run[ct];
+        float p[8], lo[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(fmaf(raw[e], a.qscale, nref));  // masked: exp2(-inf) = 0
+          psum += p[e];
+          lo[e] = p[e] - __uint_as_float(__float_as_uint(p[e]) & 0xffff0000u);  // exact remainder
+        }
+        l_lane[ct] += psum;
+        // bf16 hi = truncated p; bf16 lo = truncated remainder (the pair keeps ~16 bits)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          phi[ct][e2] = __builtin_amdgcn_perm(__float_as_uint(p[2 * e2 + 1]), __float_as_uint(p[2 * e2]), 0x07060302u);
+          plo[ct][e2] = __builtin_amdgcn_perm(__float_as_uint(lo[2 * e2 + 1]), __float_as_uint(lo[2 * e2]), 0x07060302u);
+        }
+      }
+      // ---- PV: O^T[c][row] += V^T[c][tok] P^T[tok][row] ---------------------------------------
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t* vr = svt + (16 * t + j) * VT_STRIDE;
+        const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vr + 2 * gq);
+        const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + 8 + 2 * gq);
+        const u32x4 vop = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          acc[ct][t] = mfma_bf16(vop, phi[ct], acc[ct][t]);
+          acc[ct][t] = mfma_bf16(vop, plo[ct], acc[ct][t]);
+        }
       }
     }
+    tile_store<NT>(ahead, s_k[cur ^ 1], s_vt[cur ^ 1]);  // a tile past the range stores zeros
     __syncthreads();
-    // ---- QK^T: S^T[token][row] ------------------------------------------------------------
-    f32x4 s[2][2];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      u32x4 kop[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        kop[kb] = *reinterpret_cast<const u32x4*>(s_k + (16 * tb + j) * K_STRIDE + 32 * kb + 8 * gq);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) c = mfma_bf16(kop[kb], qop[ct][kb], c);
-        s[tb][ct] = c;
-      }
-    }
-    // ---- masked online softmax per query row --------------------------------------------
-    u32x4 phi[2], plo[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int row = 16 * ct + j;
-      float sc[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tok = 16 * (e >> 2) + 4 * gq + (e & 3);
-        bool ok = tok < tlen;
-        if (a.causal) ok = ok && (tok0 + tok <= row);
-        const float v = ok ? s[e >> 2][ct][e & 3] * a.qscale : -INFINITY;
-        sc[e] = v;
-        mx = fmaxf(mx, v);
-      }
-      mx = max_over_rows(mx);
-      const float m_new = fmaxf(m_run[ct], mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[ct] - m_new);
-      m_run[ct] = m_new;
-      float psum = 0.f, hi[8], lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[e] - m_new);
-        psum += p;
-        hi[e] = __uint_as_float(__float_as_uint(p) & 0xffff0000u);  // truncated: exact split
-        lo[e] = p - hi[e];
-      }
-      l_lane[ct] = l_lane[ct] * alpha + psum;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc[ct][t] *= alpha;
-      phi[ct] = u32x4{(__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u),
-                      (__float_as_uint(hi[2]) >> 16) | (__float_as_uint(hi[3]) & 0xffff0000u),
-                      (__float_as_uint(hi[4]) >> 16) | (__float_as_uint(hi[5]) & 0xffff0000u),
-                      (__float_as_uint(hi[6]) >> 16) | (__float_as_uint(hi[7]) & 0xffff0000u)};
-      plo[ct] = u32x4{bf16_pack_rne(lo[0], lo[1]), bf16_pack_rne(lo[2], lo[3]),
-                      bf16_pack_rne(lo[4], lo[5]), bf16_pack_rne(lo[6], lo[7])};
-    }
-    // ---- PV: O^T[c][row] += V^T[c][tok] P^T[tok][row] ----------------------------------------
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t* vr = s_vt + (16 * t + j) * VT_STRIDE;
-      const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vr + 2 * gq);
-      const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + 8 + 2 * gq);
-      const u32x4 vop = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        acc[ct][t] = mfma_bf16(vop, phi[ct], acc[ct][t]);
-        acc[ct][t] = mfma_bf16(vop, plo[ct], acc[ct][t]);
-      }
-    }
+  };
+  // tiles in pairs; a pair's second tile past the range loads zeros and computes nothing
+  for (int64_t tile = t_begin; tile < t_end; tile += 2) {
+    step(tile, 0, ra, rb);
+    step(tile + 1, 1, rb, ra);
   }
 
   // ---- write this wave's partial rows ------------------------------------------------------
+  if (!computes) return;
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int row = 16 * ct + j;
@@ -376,8 +450,15 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
   a.qscale = qscale;
   a.part_o = part_o;
   a.part_ml = part_ml;
-  const dim3 block(64 * G);
+  const int NW = G <= 4 ? 4 : 8;
+  const dim3 block(64 * NW);
   const unsigned units = (unsigned)(B * Hkv);
+  auto launch_bf16 = [&](dim3 grid) {
+    if (NW == 4)
+      hipLaunchKernelGGL(verify_bf16_kernel<4>, grid, block, 0, compute, a);
+    else
+      hipLaunchKernelGGL(verify_bf16_kernel<8>, grid, block, 0, compute, a);
+  };
 
   if (!past_on_host) {
     if (plan.past_splits > 0) {
@@ -388,7 +469,7 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
       a.splits = plan.past_splits;
       a.split_offset = 0;
       a.causal = 0;
-      hipLaunchKernelGGL(verify_bf16_kernel, dim3(plan.past_splits, units), block, 0, compute, a);
+      launch_bf16(dim3(plan.past_splits, units));
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   } else {
@@ -435,7 +516,7 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
       a.splits = plan.past_splits;
       a.split_offset = c * plan.past_splits;
       a.causal = 0;
-      hipLaunchKernelGGL(verify_bf16_kernel, dim3(plan.past_splits, units), block, 0, compute, a);
+      launch_bf16(dim3(plan.past_splits, units));
       if ((err = hipGetLastError()) != hipSuccess) break;
       err = hipEventRecord(done[z], compute);
     }
@@ -457,7 +538,7 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
   a.splits = 1;
   a.split_offset = plan.total_splits - 1;
   a.causal = 1;
-  hipLaunchKernelGGL(verify_bf16_kernel, dim3(1, units), block, 0, compute, a);
+  launch_bf16(dim3(1, units));
   if ((err = hipGetLastError()) != hipSuccess) return err;
   return launch_merge(part_o, part_ml, (int64_t)rows, plan.total_splits, out, lse, compute);
 }
