@@ -131,8 +131,15 @@ class KiviCache:
         self.k_res = torch.zeros(B, Hkv, res_cap, d, dtype=rdt, device=device)
         self.v_res = torch.zeros_like(self.k_res)
 
+    _BUFFERS = ("k_codes", "v_codes", "k_meta", "v_meta", "k_res", "v_res")
+
+    def __setattr__(self, name, value):
+        if name in self._BUFFERS:  # a replaced buffer invalidates the cached descriptor
+            object.__setattr__(self, "_desc", None)
+        object.__setattr__(self, name, value)
+
     def desc(self) -> vc_kivi:
-        """The C descriptor (built once: the buffers never move)."""
+        """The C descriptor, built on first use and rebuilt after a buffer is replaced."""
         if getattr(self, "_desc", None) is None:
             self._desc = vc_kivi(self.bits, 32, self.meta_dtype, self.res_dtype, self.B, self.Hkv,
                                  self.d, self.res_cap, self.tok_cap, _ptr(self.k_codes),

@@ -143,3 +143,18 @@ def test_workspace_queries_grow_with_work(L):
     assert L.vc_verify_workspace(1, 32, 8, 31, 500000, 1, 65536, vc.VC_BF16, ctypes.byref(b)) == vc.VC_OK
     assert b.value > 2 * 8 * 65536 * 128 * 2 * 2  # two chunk stages of keys + values
     assert L.vc_draft_drop_workspace(4, 8, 64, 25000, ctypes.byref(a)) == vc.VC_OK and a.value > 4096
+
+
+def test_kivi_descriptor_follows_replaced_buffers():
+    """Replicas share one residual ring by replacing their ring tensors: the cached C descriptor
+    must then point at the new buffers."""
+    import torch
+
+    c = vc.KiviCache(1, 2, 64, 2, vc.VC_F16, vc.VC_F16, 64, device="cpu")
+    before = c.desc().k_res
+    ring = torch.zeros(1, 2, 64, 128, dtype=torch.float16)
+    c.k_res, c.v_res = ring, ring.clone()
+    d = c.desc()
+    assert d.k_res == ring.data_ptr() != before
+    assert d.v_res == c.v_res.data_ptr()
+    assert d.k_codes == c.k_codes.data_ptr()
