@@ -24,7 +24,9 @@
 // metadata and up to 4 query heads per kv head, QK^T runs transposed against an LDS table of the
 // group's q*s operands so each lane owns one head's scores (quant_split_t); the general form keeps
 // a head's scores in CPH identical columns (quant_split). The residual tokens (n_q .. n_q+r-1, an
-// fp16 or fp32 ring) form one extra split. Each split writes an unnormalised partial (o, m, l)
+// fp16 or fp32 ring) form one extra split, run by the last workgroup of each (b, kv head) before a
+// correspondingly smaller share of the groups, so every workgroup carries about the same work.
+// Each split writes an unnormalised partial (o, m, l)
 // with device-scope stores; the last workgroup of the (b, kv head) to finish (a ticket counter in
 // the workspace) merges them with log-sum-exp, so one kernel does the whole call and no
 // cache-wide fence is needed.
@@ -41,6 +43,7 @@ namespace {
 constexpr int WAVES = 4;
 constexpr int THREADS = 64 * WAVES;
 constexpr int RES_MAX = 512;           // residual ring slots handled by the residual split
+constexpr int RES_UNITS = 3;           // work of one 32-token residual block, in quantised groups
 constexpr float SCALE_QK = 256.0f;     // 2^8: magnitude headroom of the fp16 QK operand
 constexpr float SCALE_PV = 256.0f;     // 2^8: same for the PV operand
 constexpr float SUBNORMAL = 16777216.0f;  // 2^24: one fp16 subnormal step is 2^-24
@@ -69,7 +72,9 @@ struct DQArgs {
   int64_t tok_cap, n_q;
   int r, res_cap, res_dtype, q_dtype;
   int Hkv, Hq, G;
-  int ngroups, splits, total_splits;
+  int ngroups, splits, total_splits;  // splits = quantised-only workgroups; partials = splits + 2
+  int nwg;                             // workgroups per (b, kv head) = splits + 1
+  int64_t units;                       // work units: quantised groups + RES_UNITS per residual block
   float qscale;  // sm_scale * log2(e): scores are kept in log2 units inside the kernel
 };
 
@@ -243,7 +248,7 @@ __device__ void write_split_partial(const DQArgs& a, int bh, int split, const fl
 // With fp16 metadata the key bias sum_c q_c m_gc is a matrix product too: q (bf16/fp16 values are
 // exact in fp16) against the group's fp16 mins, exact products accumulated in fp32.
 template <int BITS, bool META_F16, int CPH>
-__device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
+__device__ void quant_split(const DQArgs& a, int bh, int g_begin, int g_end, int split, float* smem) {
   constexpr int WPL = 2 * BITS;
   constexpr int MB = RingPlan<BITS, META_F16>::MB;
   constexpr int NBP = CPH == 4 ? 1 : 4;  // PV B operands per group
@@ -278,8 +283,7 @@ __device__ void quant_split(const DQArgs& a, int bh, int split, float* smem) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  GroupRing<BITS, META_F16> gr(a, bh, (int)((int64_t)a.ngroups * split / a.splits),
-                               (int)((int64_t)a.ngroups * (split + 1) / a.splits), smem, wave, lane);
+  GroupRing<BITS, META_F16> gr(a, bh, g_begin, g_end, smem, wave, lane);
   gr.start();
   for (int i = 0; i < gr.n; ++i) {
     const uint8_t* sl = gr.acquire(i);
@@ -513,7 +517,7 @@ __device__ __forceinline__ float row16_sum(float x) {
 // the PV operand layout (column 4h + cg carries p * s_cg of value channel group cg), the same PV
 // product as the general form.
 template <int BITS>
-__device__ void quant_split_t(const DQArgs& a, int bh, int split, float* smem) {
+__device__ void quant_split_t(const DQArgs& a, int bh, int g_begin, int g_end, int split, float* smem) {
   constexpr int WPL = 2 * BITS;
   constexpr int MB = RingPlan<BITS, true>::MB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -531,8 +535,7 @@ __device__ void quant_split_t(const DQArgs& a, int bh, int split, float* smem) {
     qraw[kb] = load8_raw(a.q, (qrow0 + min(hp, a.G - 1)) * D + 32 * kb + 8 * gq, a.q_dtype);
   const Raw8 traw = load8_raw(a.q, (qrow0 + min(th, a.G - 1)) * D + 8 * tc, a.q_dtype);
   asm volatile("" ::: "memory");
-  GroupRing<BITS, true> gr(a, bh, (int)((int64_t)a.ngroups * split / a.splits),
-                           (int)((int64_t)a.ngroups * (split + 1) / a.splits), smem, wave, lane);
+  GroupRing<BITS, true> gr(a, bh, g_begin, g_end, smem, wave, lane);
   gr.start();
   float qv[4][8], qt[8];
 #pragma unroll
@@ -984,7 +987,7 @@ __device__ void merge_if_last(const DQArgs& a, int bh, float* smem) {
   int* s_last = reinterpret_cast<int*>(smem);
   if (threadIdx.x == 0) {
     const unsigned old = __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old == (unsigned)(a.total_splits - 1);
+    const int last = old == (unsigned)(a.nwg - 1);
     if (last) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *s_last = last;
   }
@@ -1004,16 +1007,22 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WG
   __shared__ float smem[std::max(WAVES * RingPlan<BITS, META_F16>::BYTES / 4, RES_SMEM_FLOATS)];
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
-  if (split < a.splits) {
-    if constexpr (META_F16 && CPH == 4)
-      quant_split_t<BITS>(a, bh, split, smem);
+  // Work units: the quantised groups, then RES_UNITS per 32-token residual block; workgroup w
+  // takes units [U w / nwg, U (w+1) / nwg). The last workgroup also runs the residual split
+  // (partial index splits + 1) before its share of quantised groups (partial index w).
+  const int g_begin = (int)std::min<int64_t>(a.ngroups, a.units * split / a.nwg);
+  const int g_end = (int)std::min<int64_t>(a.ngroups, a.units * (split + 1) / a.nwg);
+  if (split == a.nwg - 1) {
+    if (RES_F16 && a.q_dtype != VC_F32)
+      residual_split_mfma(a, bh, a.splits + 1, smem);
     else
-      quant_split<BITS, META_F16, CPH>(a, bh, split, smem);
+      residual_split<RES_F16>(a, bh, a.splits + 1, smem);
+    __syncthreads();  // the residual split's LDS is free again
   }
-  else if (RES_F16 && a.q_dtype != VC_F32)
-    residual_split_mfma(a, bh, split, smem);
+  if constexpr (META_F16 && CPH == 4)
+    quant_split_t<BITS>(a, bh, g_begin, g_end, split, smem);
   else
-    residual_split<RES_F16>(a, bh, split, smem);
+    quant_split<BITS, META_F16, CPH>(a, bh, g_begin, g_end, split, smem);
   merge_if_last(a, bh, smem);
 }
 
@@ -1024,12 +1033,12 @@ DraftQuantPlan plan_draft_quant(const vc_kivi& c, int64_t n_q, int Hq) {
   const int64_t ngroups = n_q / GROUP;
   const int64_t units = (int64_t)c.B * c.Hkv;
   // One resident round of workgroups: 256 CUs x 3 workgroups (the kernel is built for 3 waves
-  // per SIMD), counting the residual split of every (b, kv head); at least 2 groups per wave.
+  // per SIMD), splits + 1 per (b, kv head); at least 2 groups per wave.
   int64_t s = std::max<int64_t>(1, NUM_CUS * WG_PER_CU / units - 1);
   s = std::min<int64_t>(s, std::max<int64_t>(1, ngroups / 8));
   if (ngroups == 0) s = 0;
   p.splits = (int)s;
-  p.total_splits = p.splits + 1;
+  p.total_splits = p.splits + 2;  // partials: one per workgroup + the residual split's
   const size_t rows = (size_t)c.B * Hq;
   p.ws_bytes = DRAFT_COUNTER_BYTES + rows * p.total_splits * (D + 2) * sizeof(float);
   return p;
@@ -1064,8 +1073,10 @@ hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* 
   a.ngroups = (int)(n_q / GROUP);
   a.splits = plan.splits;
   a.total_splits = plan.total_splits;
+  a.nwg = plan.splits + 1;
+  a.units = a.ngroups + (int64_t)RES_UNITS * ((r + GROUP - 1) / GROUP);
   a.qscale = sm_scale * LOG2E;
-  dim3 grid((unsigned)plan.total_splits, (unsigned)(c.B * c.Hkv));
+  dim3 grid((unsigned)(plan.splits + 1), (unsigned)(c.B * c.Hkv));
   const bool f16m = c.meta_dtype == VC_F16, f16r = c.res_dtype == VC_F16;
   const bool wide = a.G <= 4;
 #define VC_DQ_LAUNCH(BITS, MF, RF)                                                              \

@@ -24,7 +24,7 @@ hipError_t launch_merge(const float* part_o, const float* part_ml, int64_t rows,
 constexpr size_t DRAFT_COUNTER_BYTES = 65536;
 struct DraftQuantPlan {
   int splits;        // quantised-token splits per (b, kv head)
-  int total_splits;  // splits + 1 (the residual split)
+  int total_splits;  // partials per row: splits + 1 workgroups' groups + the residual split
   size_t ws_bytes;
 };
 DraftQuantPlan plan_draft_quant(const vc_kivi& c, int64_t n_q, int Hq);
