@@ -51,6 +51,19 @@ __device__ __forceinline__ Raw8 load8_raw(const void* p, int64_t i, int dtype) {
   r.b = *reinterpret_cast<const u32x4*>(b + (esz == 4 ? 16 : 0));
   return r;
 }
+// As load8_raw, but issued as inline assembly the compiler does not track: the caller must wait
+// for it explicitly (s_waitcnt vmcnt) through raw8_wait_* before reading the registers. Lets a
+// kernel keep these loads in flight across direct-to-LDS copies it waits for itself.
+__device__ __forceinline__ Raw8 load8_raw_untracked(const void* p, int64_t i, int dtype) {
+  const int esz = dtype == VC_F32 ? 4 : 2;
+  const uint8_t* b = static_cast<const uint8_t*>(p) + i * esz;
+  const uint8_t* b2 = b + (esz == 4 ? 16 : 0);
+  Raw8 r;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r.a) : "v"(b) : "memory");
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r.b) : "v"(b2) : "memory");
+  return r;
+}
+
 __device__ __forceinline__ void cvt8(const Raw8& r, int dtype, float* out) {
 #pragma unroll
   for (int z = 0; z < 4; ++z) {

@@ -43,7 +43,7 @@ namespace {
 constexpr int WAVES = 4;
 constexpr int THREADS = 64 * WAVES;
 constexpr int RES_MAX = 512;           // residual ring slots handled by the residual split
-constexpr int RES_UNITS = 3;           // work of one 32-token residual block, in quantised groups
+constexpr int RES_UNITS = 5;           // work of one 32-token residual block, in quantised groups
 constexpr float SCALE_QK = 256.0f;     // 2^8: magnitude headroom of the fp16 QK operand
 constexpr float SCALE_PV = 256.0f;     // 2^8: same for the PV operand
 constexpr float SUBNORMAL = 16777216.0f;  // 2^24: one fp16 subnormal step is 2^-24
@@ -146,7 +146,7 @@ struct GroupRing {
   __device__ GroupRing(const DQArgs& a, int bh, int g_begin, int g_end, float* smem, int wave, int lane) {
     ring = reinterpret_cast<uint8_t*>(smem) + wave * RP::BYTES;
     g0 = g_begin + wave;
-    n = g0 < g_end ? (g_end - g0 + WAVES - 1) / WAVES : 0;
+    n = __builtin_amdgcn_readfirstlane(g0 < g_end ? (g_end - g0 + WAVES - 1) / WAVES : 0);  // wave-uniform
     const int64_t blk0 = (int64_t)bh * a.tok_cap;  // token 0 of this (b, kv head)
     constexpr int ROW_BYTES = D * BITS / 8;
     const uint8_t* kc = a.k_codes + blk0 * ROW_BYTES + lane * 16 * (WPL / 4);
@@ -170,16 +170,25 @@ struct GroupRing {
   }
   __device__ uint8_t* slot(int i) const { return ring + (i % RP::DEPTH) * RP::SLOT; }
   __device__ uint8_t* scratch() const { return ring + RP::DEPTH * RP::SLOT; }
-  __device__ void issue(int i) {
-    const int g = g0 + WAVES * i;
+  // Copy local group gi into the slot of local group i.
+  __device__ void issue(int i, int gi) {
+    const int g = g0 + WAVES * gi;
     uint8_t* dst = slot(i);
 #pragma unroll
     for (int z = 0; z < RP::LOADS; ++z) copy16_to_lds<DMA_NT>(src[z] + g * step[z], dst + 1024 * z);
   }
+  __device__ void issue(int i) { issue(i, i); }
+  // The first DEPTH-1 groups, as straight-line code (a wave with fewer groups re-copies its last
+  // one into the spare slots), so that the compiler can count the copies in flight; then wait
+  // until only those copies are outstanding: everything loaded before start() has arrived.
   __device__ void start() {
+    if (n == 0) {  // nothing to copy: only the loads issued before start() are outstanding
+      wait_vm<0>();
+      return;
+    }
 #pragma unroll
-    for (int i = 0; i < RP::DEPTH - 1; ++i)
-      if (i < n) issue(i);
+    for (int i = 0; i < RP::DEPTH - 1; ++i) issue(i, min(i, n - 1));
+    wait_vm<(RP::DEPTH - 1) * RP::LOADS>();
   }
   // Refill the slot freed by group i-1, wait for group i's copies, return its slot.
   __device__ uint8_t* acquire(int i) {
@@ -529,14 +538,18 @@ __device__ void quant_split_t(const DQArgs& a, int bh, int g_begin, int g_end, i
   // The query loads go out first, then the first groups' copies; both are in flight together.
   const int th = lane >> 4, tc = lane & 15;  // table lane: head th, 8-channel chunk tc
   // (lanes of absent heads read head G-1 and zero it afterwards)
+  // The query loads are untracked by the compiler; start() waits for them explicitly while the
+  // ring copies stay in flight (the register dependence below keeps every read after that wait).
   Raw8 qraw[4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
-    qraw[kb] = load8_raw(a.q, (qrow0 + min(hp, a.G - 1)) * D + 32 * kb + 8 * gq, a.q_dtype);
-  const Raw8 traw = load8_raw(a.q, (qrow0 + min(th, a.G - 1)) * D + 8 * tc, a.q_dtype);
-  asm volatile("" ::: "memory");
+    qraw[kb] = load8_raw_untracked(a.q, (qrow0 + min(hp, a.G - 1)) * D + 32 * kb + 8 * gq, a.q_dtype);
+  Raw8 traw = load8_raw_untracked(a.q, (qrow0 + min(th, a.G - 1)) * D + 8 * tc, a.q_dtype);
   GroupRing<BITS, true> gr(a, bh, g_begin, g_end, smem, wave, lane);
   gr.start();
+  // tie the query registers to the wait that retired their loads
+  asm volatile("" : "+v"(qraw[0].a), "+v"(qraw[0].b), "+v"(qraw[1].a), "+v"(qraw[1].b), "+v"(qraw[2].a),
+               "+v"(qraw[2].b), "+v"(qraw[3].a), "+v"(qraw[3].b), "+v"(traw.a), "+v"(traw.b));
   float qv[4][8], qt[8];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
