@@ -187,6 +187,18 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding (s_waitcnt vmcnt).
+// Direct-to-LDS copies count like loads and complete in order, so this is how a kernel knows
+// which of its copies have landed; the memory clobbers keep the compiler from moving LDS reads
+// across the wait (it does not track direct-to-LDS copies itself).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
 // Direct global -> LDS copy (global_load_lds_dwordx4): lane l's 16 bytes from g land at
 // lds + 16 l, where lds is the wave's common base. Completion is counted by vmcnt; the compiler
 // does not order LDS reads after it, so callers wait explicitly. (The host pass of this file has

@@ -112,15 +112,7 @@ struct RingPlan {
 };
 
 // Wait until at most `ahead` groups' copies (LOADS each) are still in flight: the copies of the
-// group issued before them have then landed in LDS. The memory clobbers keep the compiler from
-// moving LDS reads across the wait (it does not track direct-to-LDS copies itself).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N < 64, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
+// group issued before them have then landed in LDS (see wait_vm).
 template <int LOADS, int DEPTH>
 __device__ __forceinline__ void wait_dma(int ahead) {
   if (DEPTH > 3 && ahead >= 3) wait_vm<3 * LOADS>();

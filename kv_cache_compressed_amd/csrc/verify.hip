@@ -7,15 +7,16 @@
 // from one-token decoding); "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference", Key
 // Contributions (verification is bound by the interconnect and FLOPs).
 //
-// bf16 path (matrix cores). Workgroup = G waves on one (b, kv head) and one range of 32-token
-// key tiles; wave w owns query head kvh*G + w and its L rows (two 16-row column tiles). Each key
-// tile is staged once in LDS for all G waves: keys row-major (bf16), values transposed to
-// channel-major token pairs (bf16x2) so that the PV product reads its operand with 8-byte LDS
-// loads. QK^T uses v_mfma_f32_16x16x32_bf16 with the keys as the row operand, so each lane gets the
-// scores of 8 tokens for one query row in exactly the layout the PV product wants for its B
-// operand. The softmax weights are carried as a bf16 hi + lo pair (two accumulations), which keeps
-// ~16 significant bits in the weights at the cost of a second PV product; the fp32 accumulators
-// are exact enough that the logits keep their argmax.
+// bf16 path (matrix cores). Workgroup = 4 waves (8 when G > 4) on one (b, kv head) and one range
+// of 32-token key tiles; wave w < G owns query head kvh*G + w and its L rows (two 16-row column
+// tiles). Tiles reach LDS through direct buffer -> LDS copies into a 3-stage ring (two tiles in
+// flight), row-major with swizzled 16-byte chunks, one workgroup barrier per tile. QK^T uses
+// v_mfma_f32_16x16x32_bf16 with the keys as the row operand (S^T), so each lane holds 8 token
+// scores of one query row, which is the layout of the PV product's column operand; the values
+// reach the PV row operand through the LDS transpose read. The softmax weights are carried as a
+// bf16 hi + lo pair (two accumulations), which keeps ~16 significant bits in the weights at the
+// cost of a second PV product (bf16 weights alone move the logits by ~1e-2, enough to flip
+// near-tied tokens); the fp32 accumulators keep the logits' argmax.
 //
 // fp32 path (vector ALUs): one workgroup per (row, split) with a thread per key.
 //
@@ -29,9 +30,12 @@ namespace vc {
 
 namespace {
 
-constexpr int TK = 32;             // keys per tile
-constexpr int K_STRIDE = D + 8;    // bf16 elements per staged key row (16-byte pad)
-constexpr int VT_STRIDE = TK / 2 + 4;  // dwords per staged transposed value row
+constexpr int TK = 32;             // keys per tile (one ring stage)
+constexpr int NTB = TK / 16;       // 16-token row tiles of QK^T per tile
+constexpr int NHF = TK / 32;       // 32-token PV contraction blocks per tile
+constexpr int WG_PER_CU = 3;       // resident workgroups per CU (waves per SIMD for G <= 4)
+constexpr int RING = 3;            // tile stages per workgroup (RING - 1 in flight)
+constexpr int TILE_BYTES = TK * D * 2;  // one tile of keys (or values), bf16
 
 struct VArgs {
   const uint16_t* q;       // [B][Hq][L][D] bf16
@@ -49,77 +53,68 @@ struct VArgs {
 };
 
 constexpr float LAZY = 2.0f;  // log2 slack before a row's reference max is moved
-
-// One key/value tile (32 tokens x 128 channels) in flight in registers: KI 16-byte key chunks and
-// VI token pairs of 16-byte value chunks per thread.
-template <int NT>
-struct TileRegs {
-  static constexpr int KI = (TK * (D / 8) + NT - 1) / NT;
-  static constexpr int VI = ((TK / 2) * (D / 8) + NT - 1) / NT;
-  u32x4 k[KI];
-  u32x4 v0[VI], v1[VI];
-};
-
-// Issue the loads of tile `tile` through buffer resources whose size is the source's ntok rows,
-// so rows past the end read as zero with no per-row checks; each thread's byte offsets are fixed
-// and the tile offset is a uniform scalar.
 constexpr int RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit data format
-template <int NT>
-__device__ __forceinline__ void tile_load(TileRegs<NT>& r, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                          int64_t tile, bool live) {
-  const int tid = threadIdx.x;
-  const int sbase = live ? (int)(tile * TK * D * 2) : 0x7fffff00;  // dead tiles: out of range -> 0
-  // Every load is unconditional (threads past an item range re-read a valid item and do not store
-  // it), so the loads form straight-line code the compiler can count precisely.
-#pragma unroll
-  for (int z = 0; z < TileRegs<NT>::KI; ++z) {
-    const int idx = (tid + z * NT) % (TK * (D / 8));
-    const int t = idx / (D / 8), c8 = idx % (D / 8);
-    r.k[z] = __builtin_amdgcn_raw_buffer_load_b128(rk, t * D * 2 + c8 * 16, sbase, 0);
-  }
-#pragma unroll
-  for (int z = 0; z < TileRegs<NT>::VI; ++z) {
-    const int idx = (tid + z * NT) % ((TK / 2) * (D / 8));
-    const int tp = idx % (TK / 2), c8 = idx / (TK / 2);
-    r.v0[z] = __builtin_amdgcn_raw_buffer_load_b128(rv, 2 * tp * D * 2 + c8 * 16, sbase, 0);
-    r.v1[z] = __builtin_amdgcn_raw_buffer_load_b128(rv, (2 * tp + 1) * D * 2 + c8 * 16, sbase, 0);
-  }
-}
 
-// Write a loaded tile to LDS: keys row-major (padded rows), values transposed to channel-major
-// token pairs: s_vt[c][tp] = (v[2tp][c], v[2tp+1][c]).
-template <int NT>
-__device__ __forceinline__ void tile_store(const TileRegs<NT>& r, uint16_t* s_k, uint32_t* s_vt) {
-  const int tid = threadIdx.x;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Tiles live in LDS row-major (256 bytes per token row) with their 16-byte chunks swizzled,
+// chunk c of row r at position r*16 + (c ^ (r & 15)), so that the 16 rows a matrix-core operand
+// read touches fall in different banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
+
+// Values row operand: two LDS transpose reads (ds_read_b64_tr_b16), rows `addr` and 16 rows
+// further (4096 bytes), issued as inline asm. The builtin form is compiled with a wait for every
+// buffer -> LDS copy in flight (the compiler cannot tell which LDS bytes those copies target),
+// which would stall every tile on the copies of the tiles behind it. The compiler does not track
+// these reads either: tr16_wait() must run before the registers are used.
+__device__ __forceinline__ u32x4 tr16_issue(unsigned addr) {
+  u32x2 r0, r1;
+  // early clobber: the second read must not find its address register overwritten by the first
+  asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:4096"
+               : "=&v"(r0), "=&v"(r1)
+               : "v"(addr));
+  return u32x4{r0[0], r0[1], r1[0], r1[1]};
+}
+__device__ __forceinline__ void tr16_wait(u32x4& r) { asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r)); }
+
+// Copy tile `tile` of one (b, kv head) source into ring slot `slot` (keys, then values): each of
+// the NW waves copies TK*16/(64*NW) 16-byte chunks per operand with buffer -> LDS loads; the
+// buffer resources span the source's ntok rows, so rows past the end (and whole tiles past the
+// range) arrive as zeros.
+template <int NW>
+__device__ __forceinline__ void tile_copy(uint8_t* ring, int slot, __amdgpu_buffer_rsrc_t rk,
+                                          __amdgpu_buffer_rsrc_t rv, int64_t tile, bool live) {
+  constexpr int PER_WAVE = TK * 16 / (64 * NW);  // 16-byte chunks per lane per operand
+  static_assert(PER_WAVE >= 1 && TK * 16 % (64 * NW) == 0, "tile copy split");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned sbase = live ? (unsigned)(tile * TILE_BYTES) : 0x7ffff000u;  // dead: out of range
+  uint8_t* kdst = ring + slot * 2 * TILE_BYTES;
+  uint8_t* vdst = kdst + TILE_BYTES;
 #pragma unroll
-  for (int z = 0; z < TileRegs<NT>::KI; ++z) {
-    const int idx = tid + z * NT;
-    const int t = idx / (D / 8), c8 = idx % (D / 8);
-    if (idx < TK * (D / 8)) *reinterpret_cast<u32x4*>(s_k + t * K_STRIDE + c8 * 8) = r.k[z];
-  }
-#pragma unroll
-  for (int z = 0; z < TileRegs<NT>::VI; ++z) {
-    const int idx = tid + z * NT;
-    const int tp = idx % (TK / 2), c8 = idx / (TK / 2);
-    if (idx < (TK / 2) * (D / 8)) {
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        s_vt[(c8 * 8 + 2 * y) * VT_STRIDE + tp] = __builtin_amdgcn_perm(r.v1[z][y], r.v0[z][y], 0x05040100u);
-        s_vt[(c8 * 8 + 2 * y + 1) * VT_STRIDE + tp] = __builtin_amdgcn_perm(r.v1[z][y], r.v0[z][y], 0x07060302u);
-      }
-    }
+  for (int z = 0; z < PER_WAVE; ++z) {
+    const int base = (wave * PER_WAVE + z) * 64;  // first LDS position of this copy
+    const int p = base + lane;
+    const int row = p >> 4, chunk = (p & 15) ^ (row & 15);
+    const unsigned voff = (unsigned)(row * 256 + chunk * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + base * 16), 16,
+                                             voff, sbase, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + base * 16), 16,
+                                             voff, sbase, 0, 0);
   }
 }
 
 // Workgroup = NW waves (NW >= G) on one (b, kv head) and one range of 32-token tiles; wave w < G
-// owns query head kvh*G + w and its L rows (two 16-row column tiles); all NW waves stage tiles.
-// Tiles are double-buffered in LDS and loaded two tiles ahead into registers, so each tile costs
-// one barrier and its loads overlap the two tiles before it.
+// owns query head kvh*G + w and its L rows (two 16-row column tiles); all NW waves copy tiles.
+// Tiles stream through a RING-stage LDS ring (RING - 1 in flight) with direct buffer -> LDS
+// copies, one barrier per tile. Keys feed QK^T as the row operand; values are read straight into
+// the PV row operand with the LDS transpose read (ds_read_b64_tr_b16): source lane s of a
+// 16-lane block supplies 4 consecutive channels of one token row and result lane i receives
+// element e from source lane 4e + i/4, so no transposed copy of the values is ever written.
 template <int NW>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) verify_bf16_kernel(VArgs a) {
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4 ? WG_PER_CU : 2))) verify_bf16_kernel(VArgs a) {
   constexpr int NT = 64 * NW;
-  __shared__ uint16_t s_k[2][TK * K_STRIDE];
-  __shared__ uint32_t s_vt[2][D * VT_STRIDE];
+  constexpr int COPIES = 2 * TK * 16 / NT;  // buffer -> LDS copies per lane per tile
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RING * 2 * TILE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, gq = lane >> 4;
@@ -138,23 +133,19 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.v + (int64_t)bh * a.bh_stride * D), (short)0, nbytes, RSRC_WORD3);
 
-  TileRegs<NT> ra, rb;
-  tile_load<NT>(ra, rk, rv, t_begin, t_begin < t_end);
-  tile_load<NT>(rb, rk, rv, t_begin + 1, t_begin + 1 < t_end);
+  // the first RING - 1 tiles go out before anything else
+#pragma unroll
+  for (int z = 0; z < RING - 1; ++z) tile_copy<NW>(ring, z, rk, rv, t_begin + z, t_begin + z < t_end);
 
   // Q^T operand: column tile ct holds rows 16ct + j; lane holds channels 32kb + 8gq + 0..7.
   u32x4 qop[2][4];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
-    const int row = 16 * ct + j;
+    const int row = min(16 * ct + j, a.L - 1);  // rows past L read row L-1 and are never written
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      if (row < a.L) {
-        const int64_t off = (((int64_t)b * a.Hq + hq) * a.L + row) * D + 32 * kb + 8 * gq;
-        qop[ct][kb] = *reinterpret_cast<const u32x4*>(a.q + off);
-      } else {
-        qop[ct][kb] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int64_t off = (((int64_t)b * a.Hq + hq) * a.L + row) * D + 32 * kb + 8 * gq;
+      qop[ct][kb] = *reinterpret_cast<const u32x4*>(a.q + off);
     }
   }
 
@@ -166,26 +157,26 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  tile_store<NT>(ra, s_k[0], s_vt[0]);
-  __syncthreads();
-
-  // One tile: compute `tile` from LDS buffer `cur`; `ahead` holds tile+1 (loaded), `free` is
-  // reloaded with tile+2, then `ahead` goes to the other buffer.
-  auto step = [&](int64_t tile, int cur, TileRegs<NT>& free, TileRegs<NT>& ahead) {
-    tile_load<NT>(free, rk, rv, tile + 2, tile + 2 < t_end);
-    if (computes && tile < t_end) {
+  int slot = 0;
+  for (int64_t tile = t_begin; tile < t_end; ++tile) {
+    // this tile's copies have landed (only the RING - 2 later tiles' may be in flight), every
+    // wave's share of them is visible, and every wave is done with the slot refilled below
+    wait_vm<(RING - 2) * COPIES>();
+    __syncthreads();
+    tile_copy<NW>(ring, (slot + RING - 1) % RING, rk, rv, tile + RING - 1, tile + RING - 1 < t_end);
+    if (computes) {
       const int64_t tok0 = tile * TK;
       const int tlen = (int)min<int64_t>(TK, a.ntok - tok0);
-      const uint16_t* sk = s_k[cur];
-      const uint32_t* svt = s_vt[cur];
-      // ---- QK^T: S^T[token][row] ----------------------------------------------------------
-      f32x4 s[2][2];
+      const uint8_t* sk = ring + slot * 2 * TILE_BYTES;
+      const uint8_t* sv = sk + TILE_BYTES;
+      // ---- QK^T: S^T[token][row]: s[tb][ct][r] = token 16 tb + 4 gq + r, row 16 ct + j -------
+      f32x4 s[NTB][2];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
+      for (int tb = 0; tb < NTB; ++tb) {
         u32x4 kop[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          kop[kb] = *reinterpret_cast<const u32x4*>(sk + (16 * tb + j) * K_STRIDE + 32 * kb + 8 * gq);
+          kop[kb] = *reinterpret_cast<const u32x4*>(sk + swz(16 * tb + j, 4 * kb + gq) * 16);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -197,27 +188,30 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
       // ---- masked online softmax per query row, lazily moved reference max ------------------
       // (scores are scaled inside the exponent: the max is taken on the raw products)
       const bool masked = a.causal || tlen < TK;
-      u32x4 phi[2], plo[2];
+      u32x4 phi[2][NHF], plo[2][NHF];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const int row = 16 * ct + j;
-        float raw[8];
+        float raw[4 * NTB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) raw[e] = s[e >> 2][ct][e & 3];
+        for (int e = 0; e < 4 * NTB; ++e) raw[e] = s[e >> 2][ct][e & 3];
         if (masked) {
+          asm volatile("");  // keep this rarely taken path a branch (no if-conversion)
+          // tokens of this tile that row sees: tok < lim
+          const int lim = a.causal ? (int)min<int64_t>(tlen, row + 1 - tok0) : tlen;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int e = 0; e < 4 * NTB; ++e) {
             const int tok = 16 * (e >> 2) + 4 * gq + (e & 3);
-            bool ok = tok < tlen;
-            if (a.causal) ok = ok && (tok0 + tok <= row);
-            raw[e] = ok ? raw[e] : -INFINITY;
+            raw[e] = tok < lim ? raw[e] : -INFINITY;
           }
         }
-        const float mraw = fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])),
-                                 fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])));
+        float mraw = raw[0];
+#pragma unroll
+        for (int e = 1; e < 4 * NTB; ++e) mraw = fmaxf(mraw, raw[e]);
         const float mx = max_over_rows(mraw) * a.qscale;
         const bool move = mx > m_run[ct] + LAZY;
         if (__builtin_amdgcn_ballot_w64(move)) {
+          asm volatile("");  // keep this rarely taken path a branch (no if-conversion)
           const float m_new = move ? mx : m_run[ct];
           const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[ct] - m_new);
           m_run[ct] = m_new;
@@ -226,44 +220,54 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
           for (int t = 0; t < 8; ++t) acc[ct][t] *= alpha;
         }
         const float nref = m_run[ct] == -INFINITY ? 0.f : -m_run[ct];
-        float p[8], lo[8];
         float psum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(raw[e], a.qscale, nref));  // masked: exp2(-inf) = 0
-          psum += p[e];
-          lo[e] = p[e] - __uint_as_float(__float_as_uint(p[e]) & 0xffff0000u);  // exact remainder
+        for (int hf = 0; hf < NHF; ++hf) {
+          float p[8], lo[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(fmaf(raw[8 * hf + e], a.qscale, nref));  // masked: 0
+            psum += p[e];
+            lo[e] = p[e] - __uint_as_float(__float_as_uint(p[e]) & 0xffff0000u);  // exact remainder
+          }
+          // bf16 hi = truncated p; bf16 lo = truncated remainder (the pair keeps ~16 bits)
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            phi[ct][hf][e2] = __builtin_amdgcn_perm(__float_as_uint(p[2 * e2 + 1]), __float_as_uint(p[2 * e2]), 0x07060302u);
+            plo[ct][hf][e2] = __builtin_amdgcn_perm(__float_as_uint(lo[2 * e2 + 1]), __float_as_uint(lo[2 * e2]), 0x07060302u);
+          }
         }
         l_lane[ct] += psum;
-        // bf16 hi = truncated p; bf16 lo = truncated remainder (the pair keeps ~16 bits)
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          phi[ct][e2] = __builtin_amdgcn_perm(__float_as_uint(p[2 * e2 + 1]), __float_as_uint(p[2 * e2]), 0x07060302u);
-          plo[ct][e2] = __builtin_amdgcn_perm(__float_as_uint(lo[2 * e2 + 1]), __float_as_uint(lo[2 * e2]), 0x07060302u);
-        }
       }
       // ---- PV: O^T[c][row] += V^T[c][tok] P^T[tok][row] ---------------------------------------
+      // Row operand of channel tile t: lane (channel 16t + j, gq) needs tokens 4gq + e (e < 4) and
+      // 16 + 4gq + e; source lane s = j of block gq supplies channels 16t + 4(s&3) .. +3 of token
+      // 16h + 4gq + (s>>2) for the transpose read h.
+      // The reads of step k + 1 are in flight while step k's products run.
+      const unsigned sv_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)sv;
+      auto vaddr = [&](int k) {  // step k = (channel tile t, contraction block hf)
+        const int t = k / NHF, hf = k % NHF;
+        const int row = 32 * hf + 4 * gq + (j >> 2);
+        const int byte = (16 * t + 4 * (j & 3)) * 2;  // within the row
+        return sv_lds + (unsigned)(swz(row, byte >> 4) * 16 + (byte & 15));
+      };
+      u32x4 vop = tr16_issue(vaddr(0));
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t* vr = svt + (16 * t + j) * VT_STRIDE;
-        const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vr + 2 * gq);
-        const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + 8 + 2 * gq);
-        const u32x4 vop = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      for (int k = 0; k < 8 * NHF; ++k) {
+        const int t = k / NHF, hf = k % NHF;
+        tr16_wait(vop);
+        const u32x4 cur = vop;
+        if (k + 1 < 8 * NHF) vop = tr16_issue(vaddr(k + 1));
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          acc[ct][t] = mfma_bf16(vop, phi[ct], acc[ct][t]);
-          acc[ct][t] = mfma_bf16(vop, plo[ct], acc[ct][t]);
+          acc[ct][t] = mfma_bf16(cur, phi[ct][hf], acc[ct][t]);
+          acc[ct][t] = mfma_bf16(cur, plo[ct][hf], acc[ct][t]);
         }
       }
     }
-    tile_store<NT>(ahead, s_k[cur ^ 1], s_vt[cur ^ 1]);  // a tile past the range stores zeros
-    __syncthreads();
-  };
-  // tiles in pairs; a pair's second tile past the range loads zeros and computes nothing
-  for (int64_t tile = t_begin; tile < t_end; tile += 2) {
-    step(tile, 0, ra, rb);
-    step(tile + 1, 1, rb, ra);
+    slot = slot + 1 == RING ? 0 : slot + 1;
   }
+  wait_vm<0>();  // no copy may still target LDS when the workgroup ends
 
   // ---- write this wave's partial rows ------------------------------------------------------
   if (!computes) return;
@@ -379,7 +383,7 @@ VerifyPlan plan_verify(int B, int Hq, int Hkv, int L, int64_t n, int past_on_hos
     p.stage_bytes = 0;
   } else if (!past_on_host) {
     const int64_t tiles = (n + TK - 1) / TK;
-    int64_t s = (512 + units - 1) / units;
+    int64_t s = (256 * WG_PER_CU + units - 1) / units;
     s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 4));
     if (n == 0) s = 0;
     p.past_splits = (int)s;
@@ -392,7 +396,7 @@ VerifyPlan plan_verify(int B, int Hq, int Hkv, int L, int64_t n, int past_on_hos
     p.chunk_tokens = ct;
     p.chunks = (int)((n + ct - 1) / ct);
     const int64_t tiles = (ct + TK - 1) / TK;
-    int64_t s = (512 + units - 1) / units;
+    int64_t s = (256 * WG_PER_CU + units - 1) / units;
     s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 4));
     p.past_splits = (int)s;
     p.total_splits = p.chunks * p.past_splits + 1;
