@@ -205,6 +205,26 @@ vc_status vc_lse_merge(const float *part_o, const float *part_ml, int64_t rows, 
 vc_status vc_accept(const float *logits, const int32_t *drafts, int32_t B, int32_t L, int32_t V,
                     int32_t *accept_len, int32_t *next_token, int32_t *argmax, void *stream);
 
+/*
+ * Logits projection, the round's stand-in for a model's output head (a single attention layer has
+ * none): z[b][i][v] = sum_{h < Hq, c < 128} W[v][128 h + c] * o[b][h][i][c], fp32 with fp32
+ * accumulation, optionally fused with the greedy argmax of every row ("VeriCache: making lossy KV
+ * compression exact", The Core Idea and Figure 1: the draft's greedy token at every drafted
+ * position). Not one of the five calls of the path; it turns their outputs into tokens.
+ *   W      [V][Hq*128] fp32, device;  o [B][Hq][L][128] fp32, device (the attention outputs:
+ *          draft steps have L == 1, the verify block L rows)
+ *   logits [B][L][V] fp32 or NULL
+ *   argmax row (b, i) written to argmax[b * argmax_b_stride + i] (lowest index on ties), or NULL
+ *   ws     device, >= vc_project_workspace bytes, 16-byte aligned; zero-filled once before first
+ *          use (ticket counters; every call leaves them zero); may be NULL when argmax is NULL.
+ *          Calls that share a workspace must not overlap.
+ *   1 <= B*L <= 2^20, 1 <= V <= 2^24, 1 <= Hq <= 1024, Hq*128*V < 2^31.
+ */
+vc_status vc_project_workspace(int32_t B, int32_t L, int32_t V, size_t *bytes);
+vc_status vc_project_logits(const float *W, int32_t V, const float *o, int32_t B, int32_t Hq,
+                            int32_t L, float *logits, int32_t *argmax, int64_t argmax_b_stride,
+                            void *ws, size_t ws_bytes, void *stream);
+
 const char *vc_status_string(vc_status s);
 const char *vc_last_error(void);
 int32_t vc_abi_version(void);

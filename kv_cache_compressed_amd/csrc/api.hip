@@ -282,4 +282,36 @@ vc_status vc_accept(const float* logits, const int32_t* drafts, int32_t B, int32
   return ok();
 }
 
+vc_status vc_project_workspace(int32_t B, int32_t L, int32_t V, size_t* bytes) {
+  REQUIRE(bytes != nullptr, "bytes is null");
+  REQUIRE(B >= 1 && L >= 1 && (int64_t)B * L <= (1 << 20), "B*L must be in [1, 2^20]");
+  REQUIRE(V >= 1 && V <= (1 << 24), "V must be in [1, 2^24]");
+  *bytes = vc::plan_project(B * L, V).ws_bytes;
+  return ok();
+}
+
+vc_status vc_project_logits(const float* W, int32_t V, const float* o, int32_t B, int32_t Hq,
+                            int32_t L, float* logits, int32_t* argmax, int64_t argmax_b_stride,
+                            void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE_PTR(W);
+  REQUIRE_PTR(o);
+  REQUIRE(B >= 1 && L >= 1 && (int64_t)B * L <= (1 << 20), "B*L must be in [1, 2^20]");
+  REQUIRE(V >= 1 && V <= (1 << 24), "V must be in [1, 2^24]");
+  REQUIRE(Hq >= 1 && Hq <= 1024, "Hq must be in [1, 1024]");
+  REQUIRE((int64_t)Hq * 128 * V < ((int64_t)1 << 31), "Hq*128*V must be < 2^31");
+  REQUIRE(logits != nullptr || argmax != nullptr, "nothing to write: logits and argmax are null");
+  if (argmax != nullptr) {
+    REQUIRE(argmax_b_stride >= L, "argmax_b_stride must be >= L");
+    const vc::ProjectPlan plan = vc::plan_project(B * L, V);
+    if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
+      return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu",
+                  plan.ws_bytes, ws ? ws_bytes : (size_t)0);
+  }
+  const vc::ProjectPlan plan = vc::plan_project(B * L, V);
+  hipError_t e = vc::launch_project(W, V, o, B, Hq, L, logits, argmax, argmax_b_stride, ws, plan,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_project_logits launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -61,4 +61,15 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
                          float* out, float* lse, void* ws, const VerifyPlan& plan,
                          hipStream_t compute, hipStream_t copy);
 
+// Logits projection (+ argmax).
+struct ProjectPlan {
+  int nvt, nmt;          // vocabulary tiles, row tiles
+  size_t counter_bytes;  // ticket counters at the start of the workspace (one per row tile)
+  size_t ws_bytes;
+};
+ProjectPlan plan_project(int M, int V);
+hipError_t launch_project(const float* W, int V, const float* o, int B, int Hq, int L, float* z,
+                          int32_t* idx, int64_t idx_b_stride, void* ws, const ProjectPlan& plan,
+                          hipStream_t s);
+
 }  // namespace vc

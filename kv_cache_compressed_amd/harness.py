@@ -105,8 +105,6 @@ class RoundState:
         self.out_d = torch.zeros((x, B, Hq, 128), **f32)
         self.lse_d = torch.zeros((x, B, Hq), **f32)
         self.logits_d = torch.zeros((x, B, w.vocab), **f32)
-        self.tok_d = torch.zeros((x, B), **i32)
-        self.scratch_a = torch.zeros((B,), **i32)
         self.drafts = torch.zeros((B, x), **i32)
         self.out_v = torch.zeros((B, Hq, L, 128), **f32)
         self.lse_v = torch.zeros((B, Hq, L), **f32)
@@ -115,6 +113,8 @@ class RoundState:
         self.next_tok = torch.zeros((B,), **i32)
         self.argmax_v = torch.zeros((B, L), **i32)
         self.copy_stream = torch.cuda.Stream(device=device) if w.past_on_host else None
+        # projection workspace (draft argmax tickets); zero-filled once, calls leave it zero
+        self.ws_proj = torch.zeros((vc.vc_project_workspace(B, 1, w.vocab) + 3) // 4, **i32)
         self._rep = 0
         self.verify_ws_bytes = vc.vc_verify_workspace(B, Hq, Hkv, L, n, w.past_on_host,
                                                       w.chunk_tokens, self._vdt())
@@ -155,9 +155,7 @@ class RoundState:
             self._rep += 1
         self.append_draft_entry(j)
         self.draft_attention(j, c)
-        w = self.w
-        torch.matmul(self.out_d[j].view(w.B, -1), self.W.t(), out=self.logits_d[j])
-        vc.vc_accept(self.logits_d[j].view(w.B, 1, w.vocab), None, self.scratch_a, self.tok_d[j])
+        self.draft_tokens(j)
 
     def verify_attention(self):
         w = self.w
@@ -171,13 +169,24 @@ class RoundState:
             vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.k_store, self.v_store, w.n,
                               self.out_v, self.lse_v, ws, SM_SCALE, past_stride=w.tok_cap)
 
+    def draft_tokens(self, j: int):
+        """Logits of draft step j and its greedy token, written straight into drafts[:, j]."""
+        vc.vc_project_logits(self.W, self.out_d[j], logits=self.logits_d[j], argmax=self.drafts[:, j],
+                             argmax_b_stride=self.w.x, ws=self.ws_proj)
+
+    def verify_tokens(self):
+        """Logits of the verify rows, then greedy accept against the drafts. With B*L rows the
+        stand-in projection is a real GEMM (4 GFLOP fp32 at the 32K workload), so it runs on
+        the vendor fp32 matrix-core GEMM; the fused kernel serves the few-row draft steps."""
+        w = self.w
+        flat = self.out_v.permute(0, 2, 1, 3).reshape(w.B * w.L, w.Hq * 128)
+        torch.matmul(flat, self.W.t(), out=self.logits_v.view(w.B * w.L, w.vocab))
+        vc.vc_accept(self.logits_v, self.drafts, self.accept_len, self.next_tok, self.argmax_v)
+
     def verify_step(self):
         w = self.w
         self.verify_attention()
-        flat = self.out_v.permute(0, 2, 1, 3).reshape(w.B * w.L, w.Hq * 128)
-        torch.matmul(flat, self.W.t(), out=self.logits_v.view(w.B * w.L, w.vocab))
-        self.drafts.copy_(self.tok_d.t())
-        vc.vc_accept(self.logits_v, self.drafts, self.accept_len, self.next_tok, self.argmax_v)
+        self.verify_tokens()
 
     def run_round(self, timer=None):
         """One round. `timer`, if given, is called as timer(kind, start) with kind in
@@ -195,17 +204,13 @@ class RoundState:
             self.draft_attention(j, c)
             if timer:
                 timer("draft", False)
-            torch.matmul(self.out_d[j].view(w.B, -1), self.W.t(), out=self.logits_d[j])
-            vc.vc_accept(self.logits_d[j].view(w.B, 1, w.vocab), None, self.scratch_a, self.tok_d[j])
+            self.draft_tokens(j)
         if timer:
             timer("verify", True)
         self.verify_attention()
         if timer:
             timer("verify", False)
-        flat = self.out_v.permute(0, 2, 1, 3).reshape(w.B * w.L, w.Hq * 128)
-        torch.matmul(flat, self.W.t(), out=self.logits_v.view(w.B * w.L, w.vocab))
-        self.drafts.copy_(self.tok_d.t())
-        vc.vc_accept(self.logits_v, self.drafts, self.accept_len, self.next_tok, self.argmax_v)
+        self.verify_tokens()
 
     # ---- algorithmic work (what the method must move / compute) -------------------------
     def draft_bytes(self, j: int) -> int:

@@ -55,6 +55,8 @@ _SIGS = {
     "vc_verify_workspace": [_I32, _I32, _I32, _I32, _I64, _I32, _I64, _I32, ctypes.POINTER(_SZ)],
     "vc_lse_merge": [_P, _P, _I64, _I32, _I32, _P, _P, _P],
     "vc_accept": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
+    "vc_project_workspace": [_I32, _I32, _I32, ctypes.POINTER(_SZ)],
+    "vc_project_logits": [_P, _I32, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _SZ, _P],
     "vc_status_string": [_I32],
     "vc_last_error": [],
     "vc_abi_version": [],
@@ -245,3 +247,24 @@ def vc_accept(logits, drafts, accept_len, next_token, argmax=None, stream=None):
     B, L, V = logits.shape
     _check(lib().vc_accept(_ptr(logits), _ptr(drafts), B, L, V, _ptr(accept_len), _ptr(next_token),
                            _ptr(argmax), _stream(stream)))
+
+
+def vc_project_workspace(B: int, L: int, V: int) -> int:
+    n = _SZ()
+    _check(lib().vc_project_workspace(B, L, V, ctypes.byref(n)))
+    return n.value
+
+
+def vc_project_logits(W, o, logits=None, argmax=None, argmax_b_stride: int | None = None,
+                      ws: torch.Tensor | None = None, stream=None):
+    """W [V, Hq*128] fp32; o [B, Hq, L, 128] (or [B, Hq, 128] for L == 1) fp32 -> logits [B, L, V]
+    and/or argmax (row (b, i) at argmax.flat[b * argmax_b_stride + i]; default stride L)."""
+    V = W.shape[0]
+    B, Hq = o.shape[0], o.shape[1]
+    L = o.shape[2] if o.dim() == 4 else 1
+    if argmax_b_stride is None:
+        argmax_b_stride = L
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().vc_project_logits(_ptr(W), V, _ptr(o), B, Hq, L, _ptr(logits), _ptr(argmax),
+                                   argmax_b_stride, _ptr(ws), nb, _stream(stream)))
+

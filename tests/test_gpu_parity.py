@@ -16,7 +16,7 @@ from kv_cache_compressed_amd import harness, synth, vc
 from oracle import accept as oacc
 from oracle import attention as oatt
 from oracle import quant as oq
-from oracle.round import Round
+from oracle.round import Round, logits
 
 pytestmark = pytest.mark.gpu
 
@@ -96,6 +96,71 @@ def test_accept_random(gpu_lib, B, L, V):
     for b in range(B):
         ra, rn, _ = oacc.accept(drafts[b], ref_arg[b])
         assert a[b].item() == ra and nx[b].item() == rn
+
+
+# ------------------------------------------------------------------------------------------
+# logits projection (+ fused argmax)
+# ------------------------------------------------------------------------------------------
+def _project_ref(W, O):
+    """z [B, L, V] in float64 from the oracle's projection, and the fp32 error bound per element
+    (32 roundings of the absolute product sum: the kernel's chains are far shorter)."""
+    B, Hq, L, _ = O.shape
+    z = np.stack([np.stack([logits(W, O[b, :, i]) for i in range(L)]) for b in range(B)])
+    absum = np.stack([np.stack([logits(np.abs(W), np.abs(O[b, :, i])) for i in range(L)])
+                      for b in range(B)])
+    return z, 32 * 2.0 ** -24 * absum
+
+
+@pytest.mark.parametrize("B,L,Hq,V", [(8, 1, 32, 2048), (3, 5, 12, 1003), (2, 31, 32, 2048), (1, 1, 1, 77)])
+def test_project_logits(gpu_lib, B, L, Hq, V):
+    g = np.random.default_rng(B * 1000 + L * 10 + Hq)
+    W = g.standard_normal((V, Hq * 128)).astype(np.float32)
+    O = (g.standard_normal((B, Hq, L, 128)) * 0.1).astype(np.float32)
+    ref, bound = _project_ref(W, O)
+    Wt, Ot = torch.from_numpy(W).cuda(), torch.from_numpy(O).cuda()
+    z = torch.full((B, L, V), float("nan"), device="cuda")
+    am = torch.full((B, L + 3), -1, dtype=torch.int32, device="cuda")   # row stride L + 3
+    ws = torch.zeros((vc.vc_project_workspace(B, L, V) + 3) // 4, dtype=torch.int32, device="cuda")
+    for rep in range(2):                       # the ticket counters must come back to zero
+        vc.vc_project_logits(Wt, Ot, logits=z, argmax=am, argmax_b_stride=L + 3, ws=ws)
+        zc, ac = z.cpu().numpy(), am.cpu().numpy()
+        err = np.abs(zc - ref)
+        print(f"[project B={B} L={L} Hq={Hq} V={V}] max|err| {err.max():.3e}, max err/bound "
+              f"{(err / bound).max():.3f}", flush=True)
+        assert np.all(err <= bound)
+        # the fused argmax is the argmax of the logits it wrote (lowest index on ties) ...
+        assert np.array_equal(ac[:, :L], oacc.argmax_rows(zc))
+        assert np.all(ac[:, L:] == -1)
+        # ... and the oracle's, except near-tied rows
+        keep = oacc.top2_gap(ref.reshape(B * L, V)).reshape(B, L) >= GAP
+        assert np.array_equal(ac[:, :L][keep], oacc.argmax_rows(ref)[keep])
+        assert not ws[: ((B * L + 7) // 8)].any().item()
+    # logits only, no workspace; argmax only
+    z2 = torch.zeros_like(z)
+    vc.vc_project_logits(Wt, Ot, logits=z2)
+    assert torch.equal(z2, z)
+    am2 = torch.full((B, L), -1, dtype=torch.int32, device="cuda")
+    vc.vc_project_logits(Wt, Ot, argmax=am2, ws=ws)
+    assert np.array_equal(am2.cpu().numpy(), am.cpu().numpy()[:, :L])
+
+
+def test_project_argmax_ties_lowest_index(gpu_lib):
+    g = np.random.default_rng(7)
+    V, Hq = 300, 4
+    W = g.standard_normal((V, Hq * 128)).astype(np.float32)
+    O = g.standard_normal((1, Hq, 1, 128)).astype(np.float32)
+    r = int(np.argmax(logits(W, O[0, :, 0])))
+    for k in (3, 150, 299):                    # bitwise copies: exactly tied logits
+        W[k] = W[r]
+    expect = min(3, r)
+    Wt, Ot = torch.from_numpy(W).cuda(), torch.from_numpy(O).cuda()
+    ws = torch.zeros((vc.vc_project_workspace(1, 1, V) + 3) // 4, dtype=torch.int32, device="cuda")
+    z = torch.zeros((1, 1, V), device="cuda")
+    am = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+    vc.vc_project_logits(Wt, Ot, logits=z, argmax=am, ws=ws)
+    zc = z.cpu().numpy()[0, 0]
+    assert zc[3] == zc[r] == zc[150] == zc[299]
+    assert am.item() == expect
 
 
 # ------------------------------------------------------------------------------------------
