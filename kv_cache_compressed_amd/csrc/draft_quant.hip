@@ -205,6 +205,21 @@ struct GroupRing {
 
 // The four waves' results, staged in LDS as m [WAVES][8] (natural log), l [WAVES][8] and
 // o [WAVES][8][D], merged into this split's partial (device-scope stores, read back by the merge).
+// Progress-based wave priority. Waves issue oldest first, so with equal shares the waves that
+// started early race ahead and the CU's last waves run alone at the end, with too few loads in
+// flight to keep HBM busy. Every wave starts at the top level and steps down as it works through
+// its share (at 1/3, 2/3 and 5/6), so early starters yield to late ones and the waves of a CU
+// finish close together.
+struct ProgressPriority {
+  int q1, q2, q3;
+  __device__ explicit ProgressPriority(int n) : q1(n / 3), q2(2 * n / 3), q3(5 * n / 6) {}
+  __device__ void step(int i) const {
+    if (i == q1) __builtin_amdgcn_s_setprio(2);
+    if (i == q2) __builtin_amdgcn_s_setprio(1);
+    if (i == q3) __builtin_amdgcn_s_setprio(0);
+  }
+};
+
 __device__ void write_split_partial(const DQArgs& a, int bh, int split, const float* smem) {
   const float* s_m = smem;
   const float* s_l = smem + WAVES * 8;
@@ -286,7 +301,9 @@ __device__ void quant_split(const DQArgs& a, int bh, int g_begin, int g_end, int
 
   GroupRing<BITS, META_F16> gr(a, bh, g_begin, g_end, smem, wave, lane);
   gr.start();
+  const ProgressPriority prio(gr.n);
   for (int i = 0; i < gr.n; ++i) {
+    prio.step(i);
     const uint8_t* sl = gr.acquire(i);
     const uint8_t* mb = sl + 2 * RingPlan<BITS, META_F16>::CB;
     uint32_t kwd[WPL], vwd[WPL];
@@ -574,7 +591,9 @@ __device__ void quant_split_t(const DQArgs& a, int bh, int g_begin, int g_end, i
 
   float* s_p = reinterpret_cast<float*>(gr.scratch());  // [4 heads][32 tokens] weights
   float* s_alpha = s_p + 128;                            // [4] rescale factors
+  const ProgressPriority prio(gr.n);
   for (int i = 0; i < gr.n; ++i) {
+    prio.step(i);
     uint8_t* sl = gr.acquire(i);
     const uint8_t* mb = sl + 2 * RingPlan<BITS, true>::CB;
     uint32_t kwd[WPL], vwd[WPL];
@@ -1012,6 +1031,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WG
   __shared__ float smem[std::max(WAVES * RingPlan<BITS, META_F16>::BYTES / 4, RES_SMEM_FLOATS)];
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
+  __builtin_amdgcn_s_setprio(3);  // lowered step by step as the wave's share is worked off
   // Work units: the quantised groups, then RES_UNITS per 32-token residual block; workgroup w
   // takes units [U w / nwg, U (w+1) / nwg). The last workgroup also runs the residual split
   // (partial index splits + 1) before its share of quantised groups (partial index w).
@@ -1028,6 +1048,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WG
     quant_split_t<BITS>(a, bh, g_begin, g_end, split, smem);
   else
     quant_split<BITS, META_F16, CPH>(a, bh, g_begin, g_end, split, smem);
+  __builtin_amdgcn_s_setprio(3);  // the merge is on the launch's critical path
   merge_if_last(a, bh, smem);
 }
 

@@ -157,8 +157,17 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Progress-based wave priority (waves issue oldest first; with equal shares the workgroups that
+  // started early would finish early and leave the CU to the late ones at the end): start at the
+  // top level and step down at 1/3, 2/3 and 5/6 of this workgroup's tiles.
+  __builtin_amdgcn_s_setprio(3);
+  const int64_t q1 = t_begin + (t_end - t_begin) / 3, q2 = t_begin + 2 * (t_end - t_begin) / 3,
+                q3 = t_begin + 5 * (t_end - t_begin) / 6;
   int slot = 0;
   for (int64_t tile = t_begin; tile < t_end; ++tile) {
+    if (tile == q1) __builtin_amdgcn_s_setprio(2);
+    if (tile == q2) __builtin_amdgcn_s_setprio(1);
+    if (tile == q3) __builtin_amdgcn_s_setprio(0);
     // this tile's copies have landed (only the RING - 2 later tiles' may be in flight), every
     // wave's share of them is visible, and every wave is done with the slot refilled below
     wait_vm<(RING - 2) * COPIES>();
