@@ -4,8 +4,8 @@
 One step = one whole draft/verify round of the 32K-context Llama-3.1-8B-shaped attention layer
 (batch 8, 32 query / 8 kv heads, d 128, bf16 KV with 1% outlier channels, KIVI 2-bit drafter
 with an fp16 residual of 128 tokens, draft length 30, a 31-row causal verify over the full KV held
-in HBM): 30 x (residual append + draft attention + stand-in logits projection with its greedy
-argmax fused in), then verify attention + logits projection + accept. Inputs are seeded and synthetic and resident in
+in HBM): 30 x (draft attention with the step's residual append fused in + stand-in logits
+projection with its greedy argmax fused in), then verify attention + logits projection + accept. Inputs are seeded and synthetic and resident in
 HBM before the timed region starts.
 
 Reported (one JSON line):
@@ -200,8 +200,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # One round = 30 x (append, draft attention, logits projection + argmax) + verify attention,
-    # projection and accept: ~95 launches, replayed from a HIP graph so the host enqueue cost
+    # One round = 30 x (append + draft attention, logits projection + argmax) + verify attention,
+    # projection and accept: ~65 launches, replayed from a HIP graph so the host enqueue cost
     # (~10 us per launch from Python) does not pace the GPU.
     if not args.eager:
         st.capture_round()

@@ -118,6 +118,10 @@ vc_status vc_kivi_append(const vc_kivi *c, const void *k, const void *v, int32_t
  * For every (b, query head h): keys/values = dequantised tokens 0..n_q-1 followed by residual
  * tokens n_q..n_q+r-1 (ring slots); s_t = sm_scale * q.k_t; out = softmax(s) . V;
  * lse = log-sum-exp of s (natural log).
+ *   k_new, v_new  NULL, or the drafting step's own key/value: residual token n_q + r - 1 (r >= 1),
+ *        rows of 128 for each (b, kv head), new_bh_stride elements apart, in new_dtype, device.
+ *        It is stored into ring slot (n_q + r - 1) % res_cap (as vc_kivi_append would store it)
+ *        before the attention reads the residual, which saves a separate append launch per step.
  *   q    [B][Hq][128] in q_dtype (VC_F32 | VC_BF16 | VC_F16), device
  *   out  [B][Hq][128] fp32, device;  lse [B][Hq] fp32 or NULL
  *   n_q  multiple of 32, <= tok_cap;  0 <= r <= res_cap;  n_q + r >= 1;  Hq % Hkv == 0,
@@ -128,9 +132,10 @@ vc_status vc_kivi_append(const vc_kivi *c, const void *k, const void *v, int32_t
  *        can then be reused for any later call (any shape). Calls that overlap in time must not
  *        share a workspace. The splits and their log-sum-exp merge run in one kernel.
  */
-vc_status vc_draft_attn_quant(const vc_kivi *c, int64_t n_q, int32_t r, const void *q,
-                              int32_t q_dtype, int32_t Hq, float sm_scale, float *out, float *lse,
-                              void *ws, size_t ws_bytes, void *stream);
+vc_status vc_draft_attn_quant(const vc_kivi *c, int64_t n_q, int32_t r, const void *k_new,
+                              const void *v_new, int32_t new_dtype, int64_t new_bh_stride,
+                              const void *q, int32_t q_dtype, int32_t Hq, float sm_scale, float *out,
+                              float *lse, void *ws, size_t ws_bytes, void *stream);
 vc_status vc_draft_quant_workspace(const vc_kivi *c, int64_t n_q, int32_t r, int32_t Hq,
                                    size_t *bytes);
 

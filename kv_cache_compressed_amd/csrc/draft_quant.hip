@@ -76,6 +76,10 @@ struct DQArgs {
   int nwg;                             // workgroups per (b, kv head) = splits + 1
   int64_t units;                       // work units: quantised groups + RES_UNITS per residual block
   float qscale;  // sm_scale * log2(e): scores are kept in log2 units inside the kernel
+  const void* k_new;  // null, or residual token n_q + r - 1 to store before attending
+  const void* v_new;
+  int new_dtype;
+  int64_t new_bh_stride;  // elements between consecutive (b, kv head) rows of k_new / v_new
 };
 
 // Reciprocal of the slot-position power carried by unpacked element e of an operand.
@@ -1026,6 +1030,24 @@ __device__ void merge_if_last(const DQArgs& a, int bh, float* smem) {
   }
 }
 
+// The step's own key/value (residual token n_q + r - 1) into its ring slot, converted to the
+// residual dtype with round-half-even (as an append would store it): threads 0..127 take the
+// key's channels, 128..255 the value's. Only the workgroup that runs the residual split reads the
+// ring in this launch, and it does so after a barrier.
+__device__ void append_new_token(const DQArgs& a, int bh) {
+  static_assert(THREADS == 2 * D, "one thread per key or value channel");
+  const int c = threadIdx.x & (D - 1);
+  const bool val = threadIdx.x >= D;
+  const float x = load_as_f32(val ? a.v_new : a.k_new, (int64_t)bh * a.new_bh_stride + c, a.new_dtype);
+  const int64_t slot = (a.n_q + a.r - 1) % a.res_cap;
+  const int64_t off = ((int64_t)bh * a.res_cap + slot) * D + c;
+  void* dst = const_cast<void*>(val ? a.v_res : a.k_res);
+  if (a.res_dtype == VC_F32)
+    static_cast<float*>(dst)[off] = x;
+  else
+    static_cast<f16*>(dst)[off] = (f16)x;
+}
+
 template <int BITS, bool META_F16, bool RES_F16, int CPH>
 __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WG_PER_CU, WG_PER_CU))) draft_quant_kernel(DQArgs a) {
   __shared__ float smem[std::max(WAVES * RingPlan<BITS, META_F16>::BYTES / 4, RES_SMEM_FLOATS)];
@@ -1038,6 +1060,10 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WG
   const int g_begin = (int)std::min<int64_t>(a.ngroups, a.units * split / a.nwg);
   const int g_end = (int)std::min<int64_t>(a.ngroups, a.units * (split + 1) / a.nwg);
   if (split == a.nwg - 1) {
+    if (a.k_new) {
+      append_new_token(a, bh);
+      __syncthreads();  // the residual split below reads the slot back
+    }
     if (RES_F16 && a.q_dtype != VC_F32)
       residual_split_mfma(a, bh, a.splits + 1, smem);
     else
@@ -1070,10 +1096,15 @@ DraftQuantPlan plan_draft_quant(const vc_kivi& c, int64_t n_q, int Hq) {
   return p;
 }
 
-hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* q, int q_dtype,
-                              int Hq, float sm_scale, float* out, float* lse, void* ws,
+hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* k_new,
+                              const void* v_new, int new_dtype, int64_t new_bh_stride, const void* q,
+                              int q_dtype, int Hq, float sm_scale, float* out, float* lse, void* ws,
                               const DraftQuantPlan& plan, hipStream_t s) {
   DQArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_dtype = new_dtype;
+  a.new_bh_stride = new_bh_stride;
   a.k_codes = static_cast<const uint8_t*>(c.k_codes);
   a.v_codes = static_cast<const uint8_t*>(c.v_codes);
   a.k_meta = c.k_meta;

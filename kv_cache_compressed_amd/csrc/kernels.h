@@ -28,8 +28,9 @@ struct DraftQuantPlan {
   size_t ws_bytes;
 };
 DraftQuantPlan plan_draft_quant(const vc_kivi& c, int64_t n_q, int Hq);
-hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* q, int q_dtype,
-                              int Hq, float sm_scale, float* out, float* lse, void* ws,
+hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* k_new,
+                              const void* v_new, int new_dtype, int64_t new_bh_stride, const void* q,
+                              int q_dtype, int Hq, float sm_scale, float* out, float* lse, void* ws,
                               const DraftQuantPlan& plan, hipStream_t s);
 
 // Draft over kept positions.

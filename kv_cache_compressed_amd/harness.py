@@ -123,8 +123,10 @@ class RoundState:
         return vc.VC_BF16 if self.w.kv_dtype == "bf16" else vc.VC_F32
 
     # ---- steps ---------------------------------------------------------------------------
-    def draft_attention(self, j: int, cache=None):
-        """Draft attention of step j (position n+j) into out_d[j], lse_d[j]."""
+    def draft_attention(self, j: int, cache=None, append: bool = True):
+        """Draft attention of step j (position n+j) into out_d[j], lse_d[j]. With the KIVI drafter
+        the step's own key/value is first stored into the residual ring by the same launch
+        (append=False leaves the ring as it is, e.g. after append_draft_entry)."""
         w = self.w
         if w.drafter == "kivi":
             c = cache or self.replicas[0]
@@ -133,8 +135,11 @@ class RoundState:
             nb = self._ws_sizes.get(key)
             if nb is None:
                 nb = self._ws_sizes[key] = vc.vc_draft_quant_workspace(c, w.n_q, r, w.Hq)
+            kn = vn = None
+            if append:  # the step's own key/value goes into the (shared) residual ring in-kernel
+                kn, vn = self.k_blk[:, :, j], self.v_blk[:, :, j]
             vc.vc_draft_attn_quant(c, w.n_q, r, self.q_draft[j], self.out_d[j], self.lse_d[j],
-                                   self.ws_draft.get(nb), SM_SCALE)
+                                   self.ws_draft.get(nb), SM_SCALE, k_new=kn, v_new=vn)
         else:
             n_keep = self.kept + j + 1
             nb = vc.vc_draft_drop_workspace(w.B, w.Hkv, w.Hq, n_keep)
@@ -153,7 +158,6 @@ class RoundState:
         if self.replicas:
             c = self.replicas[self._rep % len(self.replicas)]
             self._rep += 1
-        self.append_draft_entry(j)
         self.draft_attention(j, c)
         self.draft_tokens(j)
 
@@ -198,7 +202,6 @@ class RoundState:
             if self.replicas:
                 c = self.replicas[self._rep % len(self.replicas)]
                 self._rep += 1
-            self.append_draft_entry(j)
             if timer:
                 timer("draft", True)
             self.draft_attention(j, c)

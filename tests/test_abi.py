@@ -78,8 +78,10 @@ def test_append_rejects(L):
 def test_draft_quant_rejects(L):
     k = _kivi()
     call = lambda **a: L.vc_draft_attn_quant(
-        ctypes.byref(a.get("kivi", k)), a.get("n_q", 512), a.get("r", 100), a.get("q", P), vc.VC_BF16,
-        a.get("Hq", 8), 0.088, a.get("out", P), None, a.get("ws", P), a.get("ws_bytes", 1 << 30), None)
+        ctypes.byref(a.get("kivi", k)), a.get("n_q", 512), a.get("r", 100), a.get("k_new", None),
+        a.get("v_new", None), a.get("new_dtype", vc.VC_BF16), a.get("new_stride", 128), a.get("q", P),
+        vc.VC_BF16, a.get("Hq", 8), 0.088, a.get("out", P), None, a.get("ws", P), a.get("ws_bytes", 1 << 30),
+        None)
     assert call(n_q=500) == vc.VC_ERR_INVALID
     assert call(n_q=2048) == vc.VC_ERR_INVALID
     assert call(r=300) == vc.VC_ERR_INVALID
@@ -89,6 +91,10 @@ def test_draft_quant_rejects(L):
     assert call(out=BAD) == vc.VC_ERR_INVALID
     assert call(Hq=2 * 9) == vc.VC_ERR_UNSUPPORTED
     assert call(kivi=_kivi(res_cap=1024)) == vc.VC_ERR_UNSUPPORTED
+    assert call(k_new=P) == vc.VC_ERR_INVALID                      # v_new missing
+    assert call(k_new=P, v_new=P, r=0) == vc.VC_ERR_INVALID         # the step's token is n_q + r - 1
+    assert call(k_new=P, v_new=P, new_dtype=7) == vc.VC_ERR_INVALID
+    assert call(k_new=P, v_new=P, new_stride=64) == vc.VC_ERR_INVALID
     assert call(ws=0) == vc.VC_ERR_WORKSPACE
     assert call(ws_bytes=100) == vc.VC_ERR_WORKSPACE
     n = ctypes.c_size_t(0)

@@ -284,15 +284,24 @@ def test_append_ring_and_flush(gpu_lib):
 # ------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["c1", "c2s", "c2g8", "c4s"])
 def test_draft_quant_parity(gpu_lib, name):
+    """Each step's key/value stored into the residual ring by the draft launch itself (as the
+    round runs it); a second state appends with vc_kivi_append first and must match bit for bit."""
     w = W_SMALL[name]
     inp = _inputs(w)
     st = harness.RoundState(w, inputs=inp)
+    ref_st = harness.RoundState(w, inputs=inp)
     rnd = Round(w, *inp)
     bf16 = w.kv_dtype == "bf16"
     for j in range(w.x):
-        st.append_draft_entry(j)
         st.draft_attention(j)
+        ref_st.append_draft_entry(j)
+        ref_st.draft_attention(j, append=False)
     res = st.results()
+    res_sep = ref_st.results()
+    for k in ("out_d", "lse_d"):
+        assert np.array_equal(res[k], res_sep[k]), f"fused append differs from a separate append ({k})"
+    c, c_sep = st.replicas[0], ref_st.replicas[0]
+    assert torch.equal(c.k_res, c_sep.k_res) and torch.equal(c.v_res, c_sep.v_res)
     for j in sorted({0, w.x // 2, w.x - 1}):
         for b in range(w.B):
             O, lse = rnd.draft_step(b, j)
