@@ -26,6 +26,8 @@ constexpr int PW = PT / 64;     // waves
 constexpr int VT = 8;           // vocabulary rows per workgroup
 constexpr int MT = 8;           // output rows per workgroup
 constexpr int CHUNK = 4 * PT;   // channels per chunk
+constexpr int TG = 8;           // ticket groups per row tile
+static_assert(PW == MT, "one wave per row in the final reduction");
 
 struct PArgs {
   const float* W;       // [V][Dm]
@@ -35,7 +37,7 @@ struct PArgs {
   float* z;             // [M][V] or null
   int32_t* idx;         // row (b, i) at idx[b * idx_b_stride + i], or null
   int64_t idx_b_stride;
-  unsigned* counters;   // one per row tile (grid.y); zero between calls
+  unsigned* counters;   // TG + 1 per row tile (grid.y); zero between calls
   float* part;          // [M][nvt][2]: (value, index bits) per vocabulary tile
 };
 
@@ -120,83 +122,82 @@ __global__ void __launch_bounds__(PT) project_kernel(PArgs a) {
   halve<32>(acc, lane);
   s_red[wave][lane] = acc[0];
   __syncthreads();
-  if (wave != 0) return;
-  float zv = 0.f;
+  __shared__ int s_last;
+  if (wave == 0) {
+    float zv = 0.f;
 #pragma unroll
-  for (int w2 = 0; w2 < PW; ++w2) zv += s_red[w2][lane];
-  const int v = v0 + lane / MT, m = m0 + lane % MT;  // lane = v_local * MT + m_local
-  const bool ok = v < a.V && m < a.M;
-  if (a.z && ok) a.z[(int64_t)m * a.V + v] = zv;
+    for (int w2 = 0; w2 < PW; ++w2) zv += s_red[w2][lane];
+    const int v = v0 + lane / MT, m = m0 + lane % MT;  // lane = v_local * MT + m_local
+    const bool ok = v < a.V && m < a.M;
+    if (a.z && ok) a.z[(int64_t)m * a.V + v] = zv;
+    if (a.idx) {
+      // best (value, index) of this tile per row: lanes m_local + MT k
+      float bv = ok ? zv : -INFINITY;
+      int bi = ok ? v : 0x7fffffff;
+#pragma unroll
+      for (int off = MT; off < 64; off <<= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      // Candidates go out as device-coherent stores and have completed before the ticket is
+      // taken; the last ticket holder reads them back with device-coherent loads. (Release /
+      // acquire fences would write back and invalidate the whole L2 instead, costing
+      // microseconds per call.) Two-level ticket: the tiles of a row tile count in TG group
+      // counters (tile t in group t % TG), the last of each group in a top counter, so no
+      // counter sees more than ~nvt/TG contending atomics.
+      if (lane < MT && m < a.M) {
+        float* p = a.part + ((int64_t)m * a.nvt + blockIdx.x) * 2;
+        store_coherent(p, bv);
+        store_coherent(p + 1, __int_as_float(bi));
+      }
+      wait_vm<0>();
+      if (lane == 0) {
+        unsigned* cnt = a.counters + blockIdx.y * (TG + 1);
+        const int grp = blockIdx.x % TG, ngrp = min(TG, a.nvt);
+        const unsigned in_grp = (unsigned)((a.nvt - grp + TG - 1) / TG);
+        int last = 0;
+        if (__hip_atomic_fetch_add(cnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_grp - 1) {
+          __hip_atomic_store(cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (__hip_atomic_fetch_add(cnt + TG, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(ngrp - 1)) {
+            __hip_atomic_store(cnt + TG, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = 1;
+          }
+        }
+        s_last = last;
+      }
+    }
+  }
   if (!a.idx) return;
+  __syncthreads();
+  if (!s_last) return;
 
-  // best (value, index) of this tile per row: lanes m_local + MT k
-  float bv = ok ? zv : -INFINITY;
-  int bi = ok ? v : 0x7fffffff;
-#pragma unroll
-  for (int off = MT; off < 64; off <<= 1) {
-    const float ov = __shfl_xor(bv, off, 64);
-    const int oi = __shfl_xor(bi, off, 64);
-    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-  }
-  // Candidates go out as device-coherent stores and have completed before the ticket is taken;
-  // the last ticket holder reads them back with device-coherent loads. (Release/acquire fences
-  // would write back and invalidate the whole L2 instead, costing microseconds per call.)
-  if (lane < MT && m < a.M) {
-    float* p = a.part + ((int64_t)m * a.nvt + blockIdx.x) * 2;
-    store_coherent(p, bv);
-    store_coherent(p + 1, __int_as_float(bi));
-  }
-  wait_vm<0>();
-  unsigned old = 0;
-  if (lane == 0)
-    old = __hip_atomic_fetch_add(a.counters + blockIdx.y, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __builtin_amdgcn_readfirstlane(old);
-  if (old != (unsigned)(a.nvt - 1)) return;
-  if (lane == 0) __hip_atomic_store(a.counters + blockIdx.y, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-  // last workgroup of this row tile: reduce the tiles' candidates. Candidates are loaded in
-  // batches of 4 per lane and row, all rows' loads in flight together.
-  float cv[MT];
-  int ci[MT];
-#pragma unroll
-  for (int mm = 0; mm < MT; ++mm) {
-    cv[mm] = -INFINITY;
-    ci[mm] = 0x7fffffff;
-  }
+  // Last workgroup of this row tile: wave w reduces the candidates of row m0 + w (4 loads per
+  // lane in flight per batch of 256 tiles).
+  const int row = m0 + wave;
+  if (row >= a.M) return;
+  float cv = -INFINITY;
+  int ci = 0x7fffffff;
   for (int t0 = 0; t0 < a.nvt; t0 += 256) {
-    float2 pv[MT][4];
+    float2 pv[4];
 #pragma unroll
-    for (int mm = 0; mm < MT; ++mm) {
-      const int row = min(m0 + mm, a.M - 1);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int t = min(t0 + lane + 64 * k, a.nvt - 1);  // past the end: re-read, no effect
-        pv[mm][k] = load_f32x2<true>(a.part + ((int64_t)row * a.nvt + t) * 2);
-      }
+    for (int k = 0; k < 4; ++k) {
+      const int t = min(t0 + lane + 64 * k, a.nvt - 1);  // past the end: re-read, no effect
+      pv[k] = load_f32x2<true>(a.part + ((int64_t)row * a.nvt + t) * 2);
     }
 #pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int pi = __float_as_int(pv[mm][k].y);
-        if (better(pv[mm][k].x, pi, cv[mm], ci[mm])) { cv[mm] = pv[mm][k].x; ci[mm] = pi; }
-      }
-  }
-#pragma unroll
-  for (int mm = 0; mm < MT; ++mm) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(cv[mm], off, 64);
-      const int oi = __shfl_xor(ci[mm], off, 64);
-      if (better(ov, oi, cv[mm], ci[mm])) { cv[mm] = ov; ci[mm] = oi; }
+    for (int k = 0; k < 4; ++k) {
+      const int pi = __float_as_int(pv[k].y);
+      if (better(pv[k].x, pi, cv, ci)) { cv = pv[k].x; ci = pi; }
     }
   }
-  // lane mm writes row m0 + mm
 #pragma unroll
-  for (int mm = 0; mm < MT; ++mm) {
-    const int row = m0 + mm;
-    if (lane == mm && row < a.M) a.idx[(int64_t)(row / a.L) * a.idx_b_stride + row % a.L] = ci[mm];
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(cv, off, 64);
+    const int oi = __shfl_xor(ci, off, 64);
+    if (better(ov, oi, cv, ci)) { cv = ov; ci = oi; }
   }
+  if (lane == 0) a.idx[(int64_t)(row / a.L) * a.idx_b_stride + row % a.L] = ci;
 }
 
 }  // namespace
@@ -205,7 +206,7 @@ ProjectPlan plan_project(int M, int V) {
   ProjectPlan p;
   p.nvt = (V + VT - 1) / VT;
   p.nmt = (M + MT - 1) / MT;
-  const size_t counters = ((size_t)p.nmt * sizeof(unsigned) + 255) & ~(size_t)255;
+  const size_t counters = ((size_t)p.nmt * (TG + 1) * sizeof(unsigned) + 255) & ~(size_t)255;
   p.counter_bytes = counters;
   p.ws_bytes = counters + (size_t)M * p.nvt * 2 * sizeof(float);
   return p;

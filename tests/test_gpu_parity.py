@@ -134,7 +134,7 @@ def test_project_logits(gpu_lib, B, L, Hq, V):
         # ... and the oracle's, except near-tied rows
         keep = oacc.top2_gap(ref.reshape(B * L, V)).reshape(B, L) >= GAP
         assert np.array_equal(ac[:, :L][keep], oacc.argmax_rows(ref)[keep])
-        assert not ws[: ((B * L + 7) // 8)].any().item()
+        assert not ws[: ((B * L + 7) // 8) * 9].any().item()   # ticket counters back at zero
     # logits only, no workspace; argmax only
     z2 = torch.zeros_like(z)
     vc.vc_project_logits(Wt, Ot, logits=z2)
