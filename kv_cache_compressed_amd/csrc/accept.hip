@@ -37,14 +37,23 @@ __global__ void __launch_bounds__(1024) accept_kernel(const float* __restrict__ 
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     if (vec) {
+      // UNROLL 16-byte loads per lane in flight at a time (lanes past the row re-read its last
+      // float4 and lose every comparison: an equal value at a higher index never wins)
+      constexpr int UNROLL = 8;
       const float4* z4 = reinterpret_cast<const float4*>(z);
-      for (int i = lane; i < V / 4; i += 64) {
-        const float4 t = z4[i];
-        const int base = 4 * i;
-        if (better(t.x, base + 0, bv, bi)) { bv = t.x; bi = base + 0; }
-        if (better(t.y, base + 1, bv, bi)) { bv = t.y; bi = base + 1; }
-        if (better(t.z, base + 2, bv, bi)) { bv = t.z; bi = base + 2; }
-        if (better(t.w, base + 3, bv, bi)) { bv = t.w; bi = base + 3; }
+      const int n4 = V / 4;
+      for (int i0 = 0; i0 < n4; i0 += 64 * UNROLL) {
+        float4 t[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) t[u] = z4[min(i0 + 64 * u + lane, n4 - 1)];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int base = 4 * min(i0 + 64 * u + lane, n4 - 1);
+          if (better(t[u].x, base + 0, bv, bi)) { bv = t[u].x; bi = base + 0; }
+          if (better(t[u].y, base + 1, bv, bi)) { bv = t[u].y; bi = base + 1; }
+          if (better(t[u].z, base + 2, bv, bi)) { bv = t[u].z; bi = base + 2; }
+          if (better(t[u].w, base + 3, bv, bi)) { bv = t[u].w; bi = base + 3; }
+        }
       }
     } else {
       for (int i = lane; i < V; i += 64) {

@@ -207,8 +207,6 @@ struct GroupRing {
   }
 };
 
-// The four waves' results, staged in LDS as m [WAVES][8] (natural log), l [WAVES][8] and
-// o [WAVES][8][D], merged into this split's partial (device-scope stores, read back by the merge).
 // Progress-based wave priority. Waves issue oldest first, so with equal shares the waves that
 // started early race ahead and the CU's last waves run alone at the end, with too few loads in
 // flight to keep HBM busy. Every wave starts at the top level and steps down as it works through
@@ -224,6 +222,8 @@ struct ProgressPriority {
   }
 };
 
+// The four waves' results, staged in LDS as m [WAVES][8] (natural log), l [WAVES][8] and
+// o [WAVES][8][D], merged into this split's partial (device-scope stores, read back by the merge).
 __device__ void write_split_partial(const DQArgs& a, int bh, int split, const float* smem) {
   const float* s_m = smem;
   const float* s_l = smem + WAVES * 8;

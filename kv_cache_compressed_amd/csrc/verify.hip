@@ -46,6 +46,9 @@ struct VArgs {
   int splits;              // workgroups per (b, kv head) for this source
   int split_offset;        // partial index of this launch's split 0
   int causal;              // source is the round's block: row i sees tokens 0..i
+  const uint16_t* k_blk;   // null, or the round's block [B][Hkv][L][D] as one more split
+  const uint16_t* v_blk;   //   (blockIdx.x == splits), causal, written to partial blk_index
+  int blk_index;
   int L, Hq, Hkv, G, total_splits;
   float qscale;            // sm_scale * log2(e)
   float* part_o;
@@ -118,20 +121,32 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, gq = lane >> 4;
-  const int bh = blockIdx.y, split = blockIdx.x;
+  const int bh = blockIdx.y;
+  // Jobs of this workgroup: split blockIdx.x of the launch's source (if blockIdx.x < splits),
+  // then, for the last workgroup of the row and when the round's block is given, the block as one
+  // more causal split (it is one tile: a workgroup of its own would not fit the resident round).
+  const bool do_past = (int)blockIdx.x < a.splits;
+  const bool do_blk = a.k_blk != nullptr && (int)blockIdx.x == max(a.splits, 1) - 1;
+  auto run_job = [&](const bool blk) {
+  const uint16_t* const src_k = blk ? a.k_blk : a.k;
+  const uint16_t* const src_v = blk ? a.v_blk : a.v;
+  const int64_t src_stride = blk ? a.L : a.bh_stride, src_ntok = blk ? a.L : a.ntok;
+  const int src_splits = blk ? 1 : a.splits, split = blk ? 0 : blockIdx.x;
+  const bool causal = blk || a.causal;
+  const int sidx = blk ? a.blk_index : a.split_offset + split;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const bool computes = wave < a.G;
   const int hq = kvh * a.G + min(wave, a.G - 1);
 
   // tile range of this split
-  const int64_t ntiles = (a.ntok + TK - 1) / TK;
-  const int64_t t_begin = ntiles * split / a.splits;
-  const int64_t t_end = ntiles * (split + 1) / a.splits;
-  const int nbytes = (int)(a.ntok * D * 2);  // this (b, kv head)'s source rows
+  const int64_t ntiles = (src_ntok + TK - 1) / TK;
+  const int64_t t_begin = ntiles * split / src_splits;
+  const int64_t t_end = ntiles * (split + 1) / src_splits;
+  const int nbytes = (int)(src_ntok * D * 2);  // this (b, kv head)'s source rows
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.k + (int64_t)bh * a.bh_stride * D), (short)0, nbytes, RSRC_WORD3);
+      const_cast<uint16_t*>(src_k + (int64_t)bh * src_stride * D), (short)0, nbytes, RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.v + (int64_t)bh * a.bh_stride * D), (short)0, nbytes, RSRC_WORD3);
+      const_cast<uint16_t*>(src_v + (int64_t)bh * src_stride * D), (short)0, nbytes, RSRC_WORD3);
 
   // the first RING - 1 tiles go out before anything else
 #pragma unroll
@@ -175,7 +190,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
     tile_copy<NW>(ring, (slot + RING - 1) % RING, rk, rv, tile + RING - 1, tile + RING - 1 < t_end);
     if (computes) {
       const int64_t tok0 = tile * TK;
-      const int tlen = (int)min<int64_t>(TK, a.ntok - tok0);
+      const int tlen = (int)min<int64_t>(TK, src_ntok - tok0);
       const uint8_t* sk = ring + slot * 2 * TILE_BYTES;
       const uint8_t* sv = sk + TILE_BYTES;
       // ---- QK^T: S^T[token][row]: s[tb][ct][r] = token 16 tb + 4 gq + r, row 16 ct + j -------
@@ -196,7 +211,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
       }
       // ---- masked online softmax per query row, lazily moved reference max ------------------
       // (scores are scaled inside the exponent: the max is taken on the raw products)
-      const bool masked = a.causal || tlen < TK;
+      const bool masked = causal || tlen < TK;
       u32x4 phi[2][NHF], plo[2][NHF];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -207,7 +222,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
         if (masked) {
           asm volatile("");  // keep this rarely taken path a branch (no if-conversion)
           // tokens of this tile that row sees: tok < lim
-          const int lim = a.causal ? (int)min<int64_t>(tlen, row + 1 - tok0) : tlen;
+          const int lim = causal ? (int)min<int64_t>(tlen, row + 1 - tok0) : tlen;
 #pragma unroll
           for (int e = 0; e < 4 * NTB; ++e) {
             const int tok = 16 * (e >> 2) + 4 * gq + (e & 3);
@@ -276,26 +291,32 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
     }
     slot = slot + 1 == RING ? 0 : slot + 1;
   }
-  wait_vm<0>();  // no copy may still target LDS when the workgroup ends
+  wait_vm<0>();  // no copy may still target LDS when the job (and the workgroup) ends
 
   // ---- write this wave's partial rows ------------------------------------------------------
-  if (!computes) return;
+  if (computes) {
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int row = 16 * ct + j;
-    const float l = sum_over_rows(l_lane[ct]);
-    if (row < a.L) {
-      const int64_t prow = ((int64_t)b * a.Hq + hq) * a.L + row;
-      const int sidx = a.split_offset + split;
-      float* po = a.part_o + (prow * a.total_splits + sidx) * D;
+    for (int ct = 0; ct < 2; ++ct) {
+      const int row = 16 * ct + j;
+      const float l = sum_over_rows(l_lane[ct]);
+      if (row < a.L) {
+        const int64_t prow = ((int64_t)b * a.Hq + hq) * a.L + row;
+        float* po = a.part_o + (prow * a.total_splits + sidx) * D;
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        *reinterpret_cast<f32x4*>(po + 16 * t + 4 * gq) = acc[ct][t];
-      if (gq == 0) {
-        a.part_ml[(prow * a.total_splits + sidx) * 2 + 0] = (l > 0.f) ? m_run[ct] * LN2 : -INFINITY;
-        a.part_ml[(prow * a.total_splits + sidx) * 2 + 1] = l;
+        for (int t = 0; t < 8; ++t)
+          *reinterpret_cast<f32x4*>(po + 16 * t + 4 * gq) = acc[ct][t];
+        if (gq == 0) {
+          a.part_ml[(prow * a.total_splits + sidx) * 2 + 0] = (l > 0.f) ? m_run[ct] * LN2 : -INFINITY;
+          a.part_ml[(prow * a.total_splits + sidx) * 2 + 1] = l;
+        }
       }
     }
+  }
+  };
+  if (do_past) run_job(false);
+  if (do_blk) {
+    if (do_past) __syncthreads();  // the block's copies refill the ring
+    run_job(true);
   }
 }
 
@@ -473,18 +494,23 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
       hipLaunchKernelGGL(verify_bf16_kernel<8>, grid, block, 0, compute, a);
   };
 
+  a.k_blk = nullptr;
+  a.v_blk = nullptr;
+  a.blk_index = plan.total_splits - 1;
   if (!past_on_host) {
-    if (plan.past_splits > 0) {
-      a.k = static_cast<const uint16_t*>(k_past);
-      a.v = static_cast<const uint16_t*>(v_past);
-      a.bh_stride = past_stride;
-      a.ntok = n;
-      a.splits = plan.past_splits;
-      a.split_offset = 0;
-      a.causal = 0;
-      launch_bf16(dim3(plan.past_splits, units));
-      if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
+    // the past's splits and the causal block (one more split) in one launch
+    a.k = static_cast<const uint16_t*>(k_past);
+    a.v = static_cast<const uint16_t*>(v_past);
+    a.bh_stride = past_stride;
+    a.ntok = n;
+    a.splits = plan.past_splits;
+    a.split_offset = 0;
+    a.causal = 0;
+    a.k_blk = static_cast<const uint16_t*>(k_blk);
+    a.v_blk = static_cast<const uint16_t*>(v_blk);
+    launch_bf16(dim3(std::max(plan.past_splits, 1), units));
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    return launch_merge(part_o, part_ml, (int64_t)rows, plan.total_splits, out, lse, compute);
   } else {
     // Stream the past chunk by chunk: copies on `copy` into stage c % 2, compute on `compute`.
     char* stage_base = static_cast<char*>(ws) + plan.part_bytes;
