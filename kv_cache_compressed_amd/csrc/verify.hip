@@ -89,7 +89,8 @@ __device__ __forceinline__ void tile_copy(uint8_t* ring, int slot, __amdgpu_buff
                                           __amdgpu_buffer_rsrc_t rv, int64_t tile, bool live) {
   constexpr int PER_WAVE = TK * 16 / (64 * NW);  // 16-byte chunks per lane per operand
   static_assert(PER_WAVE >= 1 && TK * 16 % (64 * NW) == 0, "tile copy split");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // LDS bases in scalar registers
   const unsigned sbase = live ? (unsigned)(tile * TILE_BYTES) : 0x7ffff000u;  // dead: out of range
   uint8_t* kdst = ring + slot * 2 * TILE_BYTES;
   uint8_t* vdst = kdst + TILE_BYTES;
@@ -165,6 +166,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
   }
 
   float m_run[2] = {-INFINITY, -INFINITY};
+  float nref[2] = {0.f, 0.f};  // -m_run, 0 while no key has been seen
   float l_lane[2] = {0.f, 0.f};
   f32x4 acc[2][8];
 #pragma unroll
@@ -229,28 +231,31 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
             raw[e] = tok < lim ? raw[e] : -INFINITY;
           }
         }
+        // The reference max moves only when the row's max exceeds it by LAZY: a lane compares its
+        // own 8 scores first, and only when some lane is over (rare after the first tile) is the
+        // row max formed across the row's 4 lanes and the row rescaled.
         float mraw = raw[0];
 #pragma unroll
         for (int e = 1; e < 4 * NTB; ++e) mraw = fmaxf(mraw, raw[e]);
-        const float mx = max_over_rows(mraw) * a.qscale;
-        const bool move = mx > m_run[ct] + LAZY;
-        if (__builtin_amdgcn_ballot_w64(move)) {
+        if (__builtin_amdgcn_ballot_w64(mraw * a.qscale > m_run[ct] + LAZY)) {
           asm volatile("");  // keep this rarely taken path a branch (no if-conversion)
+          const float mx = max_over_rows(mraw) * a.qscale;
+          const bool move = mx > m_run[ct] + LAZY;
           const float m_new = move ? mx : m_run[ct];
           const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[ct] - m_new);
           m_run[ct] = m_new;
+          nref[ct] = m_new == -INFINITY ? 0.f : -m_new;
           l_lane[ct] *= alpha;
 #pragma unroll
           for (int t = 0; t < 8; ++t) acc[ct][t] *= alpha;
         }
-        const float nref = m_run[ct] == -INFINITY ? 0.f : -m_run[ct];
         float psum = 0.f;
 #pragma unroll
         for (int hf = 0; hf < NHF; ++hf) {
           float p[8], lo[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(fmaf(raw[8 * hf + e], a.qscale, nref));  // masked: 0
+            p[e] = __builtin_amdgcn_exp2f(fmaf(raw[8 * hf + e], a.qscale, nref[ct]));  // masked: 0
             psum += p[e];
             lo[e] = p[e] - __uint_as_float(__float_as_uint(p[e]) & 0xffff0000u);  // exact remainder
           }
