@@ -15,6 +15,8 @@
  *   vc_verify_attn       L-query causal block attention over the full cache   (verify)
  *   vc_lse_merge         log-sum-exp merge of split partials                  (verify / draft)
  *   vc_accept            per-row argmax, first disagreement, correction token (accept)
+ *   vc_project_logits    logits of the attention outputs (+ greedy argmax): the
+ *                        single layer's stand-in for a model head              (harness)
  *
  * Conventions (all calls):
  *   - Every buffer is owned by the caller. Device pointers are HIP device memory; the library

@@ -1,12 +1,14 @@
 """One synthetic single-layer draft/verify round on the GPU, driven through libvc.
 
-Device memory, streams and the stand-in logits projection (z = W o, a plain fp32 GEMM in place of
-the model's LM head) come from PyTorch; every attention, quantisation, cache-append and accept
-step is a libvc call. Inputs come from the seeded generator (kv_cache_compressed_amd.synth).
+Device memory and streams come from PyTorch; every attention, quantisation, cache-append, accept
+and draft-step logits/argmax step is a libvc call. The stand-in logits projection (z = W o, an fp32
+product in place of the model's LM head) is libvc's fused projection + argmax kernel for the draft
+steps; for the B*L verify rows, where it is a real GEMM, it is the vendor fp32 GEMM through
+torch.matmul. Inputs come from the seeded generator (kv_cache_compressed_amd.synth).
 
 Round ("VeriCache: making lossy KV compression exact", The Core Idea): x draft steps over the
-compressed cache (each: append the step's key/value, draft attention, logits, greedy argmax), one
-verify pass of x+1 rows over the full cache, logits, accept.
+compressed cache (each: draft attention with the step's key/value appended by the same launch,
+logits with the greedy argmax), one verify pass of x+1 rows over the full cache, logits, accept.
 """
 from __future__ import annotations
 
