@@ -143,6 +143,28 @@ def test_merge_and_accept_reject(L):
     assert L.vc_accept(P, P, 1, 9, 0, P, P, None, None) == vc.VC_ERR_INVALID
 
 
+def test_project_rejects_and_sizes(L):
+    """Projection: argument checks (nothing enqueued) and the workspace size (ticket counters,
+    9 per 8-row tile, rounded to 256 B, then an 8-byte candidate per row and 8-row vocabulary tile)."""
+    n = ctypes.c_size_t()
+    assert L.vc_project_workspace(8, 1, 2048, ctypes.byref(n)) == vc.VC_OK
+    assert n.value == 256 + 8 * (2048 // 8) * 8
+    assert L.vc_project_workspace(8, 31, 2048, ctypes.byref(n)) == vc.VC_OK
+    assert n.value == (31 * 9 * 4 + 255) // 256 * 256 + 8 * 31 * 256 * 8
+    assert L.vc_project_workspace(0, 1, 2048, ctypes.byref(n)) == vc.VC_ERR_INVALID
+    call = lambda **a: L.vc_project_logits(a.get("W", P), a.get("V", 2048), a.get("o", P), a.get("B", 8),
+                                           a.get("Hq", 32), a.get("L", 1), a.get("z", P), a.get("idx", P),
+                                           a.get("stride", 1), a.get("ws", P), a.get("ws_bytes", 1 << 20), None)
+    assert call(W=0) == vc.VC_ERR_INVALID
+    assert call(o=BAD) == vc.VC_ERR_INVALID
+    assert call(V=0) == vc.VC_ERR_INVALID
+    assert call(Hq=0) == vc.VC_ERR_INVALID
+    assert call(z=None, idx=None) == vc.VC_ERR_INVALID and "nothing to write" in _err(L)
+    assert call(L=4, stride=3) == vc.VC_ERR_INVALID                # argmax row stride < L
+    assert call(ws=None) == vc.VC_ERR_WORKSPACE
+    assert call(ws_bytes=100) == vc.VC_ERR_WORKSPACE
+
+
 def test_workspace_queries_grow_with_work(L):
     a, b = ctypes.c_size_t(), ctypes.c_size_t()
     assert L.vc_verify_workspace(8, 32, 8, 31, 32768, 0, 0, vc.VC_BF16, ctypes.byref(a)) == vc.VC_OK
