@@ -174,7 +174,8 @@ vc_status vc_draft_drop_workspace(int32_t B, int32_t Hkv, int32_t Hq, int64_t n_
  *                on `compute`; pageable host memory is rejected). past_stride >= n.
  *   out          [B][Hq][L][128] fp32; lse [B][Hq][L] fp32 or NULL
  *   dtype        VC_BF16 (matrix-core path) or VC_F32 (vector path; device-resident past only)
- *   1 <= L <= 32, n >= 0, Hq % Hkv == 0, Hq/Hkv <= 8.
+ *   1 <= L <= 32, n >= 0, Hq % Hkv == 0, Hq/Hkv <= 8; VC_BF16: at most 8388607 tokens per
+ *   (b, kv head) in a resident past or in one streamed chunk (else VC_ERR_UNSUPPORTED).
  *   ws           vc_verify_workspace() bytes (partials, plus two chunk stages when streaming).
  * The host past must stay valid until `compute` has passed this call: `compute` waits for every
  * copy, so synchronising `compute` suffices.

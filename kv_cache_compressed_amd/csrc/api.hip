@@ -236,6 +236,14 @@ vc_status vc_verify_attn(const void* q, const void* k_blk, const void* v_blk, in
     if (past_on_host) return fail(VC_ERR_UNSUPPORTED, "host-streamed past needs VC_BF16");
     if ((int64_t)B * Hq * L > 65535) return fail(VC_ERR_UNSUPPORTED, "VC_F32 verify needs B*Hq*L <= 65535");
   }
+  if (dtype == VC_BF16) {
+    // one source of the matrix-core kernel (the resident past, or one streamed chunk) is addressed
+    // through a buffer resource of at most 2^31 - 1 bytes per (b, kv head): 256 bytes per token
+    const int64_t span = past_on_host ? std::min<int64_t>(chunk_tokens, n) : n;
+    if (span > (int64_t)8388607)
+      return fail(VC_ERR_UNSUPPORTED, "more than 8388607 past tokens per (b, kv head) in one %s",
+                  past_on_host ? "chunk (use a smaller chunk_tokens)" : "device-resident past (stream it)");
+  }
   if (past_on_host) {
     REQUIRE(chunk_tokens >= 32, "chunk_tokens must be >= 32 when streaming");
     REQUIRE(n >= 1, "a host-streamed past needs n >= 1");

@@ -85,25 +85,39 @@ __device__ __forceinline__ void tr16_wait(u32x4& r) { asm volatile("s_waitcnt lg
 // buffer resources span the source's ntok rows, so rows past the end (and whole tiles past the
 // range) arrive as zeros.
 template <int NW>
-__device__ __forceinline__ void tile_copy(uint8_t* ring, int slot, __amdgpu_buffer_rsrc_t rk,
-                                          __amdgpu_buffer_rsrc_t rv, int64_t tile, bool live) {
-  constexpr int PER_WAVE = TK * 16 / (64 * NW);  // 16-byte chunks per lane per operand
-  static_assert(PER_WAVE >= 1 && TK * 16 % (64 * NW) == 0, "tile copy split");
+constexpr int COPY_PER_WAVE = TK * 16 / (64 * NW);  // 16-byte chunks per lane per operand
+
+// This lane's buffer offsets within a tile (fixed for the whole loop): copy z of wave w lands at
+// LDS position p = 64 (w * COPY_PER_WAVE + z) + lane, which holds chunk (p & 15) ^ (row & 15) of
+// row p >> 4.
+template <int NW>
+__device__ __forceinline__ void tile_offsets(unsigned* voff) {
+  static_assert(COPY_PER_WAVE<NW> >= 1 && TK * 16 % (64 * NW) == 0, "tile copy split");
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int z = 0; z < COPY_PER_WAVE<NW>; ++z) {
+    const int p = (wave * COPY_PER_WAVE<NW> + z) * 64 + lane;
+    const int row = p >> 4, chunk = (p & 15) ^ (row & 15);
+    voff[z] = (unsigned)(row * 256 + chunk * 16);
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void tile_copy(uint8_t* ring, int slot, __amdgpu_buffer_rsrc_t rk,
+                                          __amdgpu_buffer_rsrc_t rv, const unsigned* voff, int tile,
+                                          bool live) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // LDS bases in scalar registers
-  const unsigned sbase = live ? (unsigned)(tile * TILE_BYTES) : 0x7ffff000u;  // dead: out of range
+  const unsigned sbase = live ? (unsigned)tile * TILE_BYTES : 0x7ffff000u;  // dead: out of range
   uint8_t* kdst = ring + slot * 2 * TILE_BYTES;
   uint8_t* vdst = kdst + TILE_BYTES;
 #pragma unroll
-  for (int z = 0; z < PER_WAVE; ++z) {
-    const int base = (wave * PER_WAVE + z) * 64;  // first LDS position of this copy
-    const int p = base + lane;
-    const int row = p >> 4, chunk = (p & 15) ^ (row & 15);
-    const unsigned voff = (unsigned)(row * 256 + chunk * 16);
+  for (int z = 0; z < COPY_PER_WAVE<NW>; ++z) {
+    const int base = (wave * COPY_PER_WAVE<NW> + z) * 64;  // first LDS position of this copy
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + base * 16), 16,
-                                             voff, sbase, 0, 0);
+                                             voff[z], sbase, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + base * 16), 16,
-                                             voff, sbase, 0, 0);
+                                             voff[z], sbase, 0, 0);
   }
 }
 
@@ -140,9 +154,11 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
   const int hq = kvh * a.G + min(wave, a.G - 1);
 
   // tile range of this split
-  const int64_t ntiles = (src_ntok + TK - 1) / TK;
-  const int64_t t_begin = ntiles * split / src_splits;
-  const int64_t t_end = ntiles * (split + 1) / src_splits;
+  const int ntiles = (int)((src_ntok + TK - 1) / TK);  // < 2^18: src_ntok * 256 bytes < 2^31
+  const int t_begin = (int)((int64_t)ntiles * split / src_splits);
+  const int t_end = (int)((int64_t)ntiles * (split + 1) / src_splits);
+  unsigned voff[COPY_PER_WAVE<NW>];
+  tile_offsets<NW>(voff);
   const int nbytes = (int)(src_ntok * D * 2);  // this (b, kv head)'s source rows
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(src_k + (int64_t)bh * src_stride * D), (short)0, nbytes, RSRC_WORD3);
@@ -151,7 +167,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
 
   // the first RING - 1 tiles go out before anything else
 #pragma unroll
-  for (int z = 0; z < RING - 1; ++z) tile_copy<NW>(ring, z, rk, rv, t_begin + z, t_begin + z < t_end);
+  for (int z = 0; z < RING - 1; ++z) tile_copy<NW>(ring, z, rk, rv, voff, t_begin + z, t_begin + z < t_end);
 
   // Q^T operand: column tile ct holds rows 16ct + j; lane holds channels 32kb + 8gq + 0..7.
   u32x4 qop[2][4];
@@ -178,10 +194,10 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
   // started early would finish early and leave the CU to the late ones at the end): start at the
   // top level and step down at 1/3, 2/3 and 5/6 of this workgroup's tiles.
   __builtin_amdgcn_s_setprio(3);
-  const int64_t q1 = t_begin + (t_end - t_begin) / 3, q2 = t_begin + 2 * (t_end - t_begin) / 3,
-                q3 = t_begin + 5 * (t_end - t_begin) / 6;
+  const int q1 = t_begin + (t_end - t_begin) / 3, q2 = t_begin + 2 * (t_end - t_begin) / 3,
+            q3 = t_begin + 5 * (t_end - t_begin) / 6;
   int slot = 0;
-  for (int64_t tile = t_begin; tile < t_end; ++tile) {
+  for (int tile = t_begin; tile < t_end; ++tile) {
     if (tile == q1) __builtin_amdgcn_s_setprio(2);
     if (tile == q2) __builtin_amdgcn_s_setprio(1);
     if (tile == q3) __builtin_amdgcn_s_setprio(0);
@@ -189,7 +205,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
     // wave's share of them is visible, and every wave is done with the slot refilled below
     wait_vm<(RING - 2) * COPIES>();
     __syncthreads();
-    tile_copy<NW>(ring, (slot + RING - 1) % RING, rk, rv, tile + RING - 1, tile + RING - 1 < t_end);
+    tile_copy<NW>(ring, (slot + RING - 1) % RING, rk, rv, voff, tile + RING - 1, tile + RING - 1 < t_end);
     if (computes) {
       const int64_t tok0 = tile * TK;
       const int tlen = (int)min<int64_t>(TK, src_ntok - tok0);

@@ -130,6 +130,9 @@ def test_verify_rejects(L):
     assert call(dt=vc.VC_F32, host=1, chunk=1024) == vc.VC_ERR_UNSUPPORTED
     assert call(host=1, chunk=16) == vc.VC_ERR_INVALID
     assert call(ws_bytes=64) == vc.VC_ERR_WORKSPACE
+    # one bf16 source per (b, kv head) is limited to 8388607 tokens (256 B each, 32-bit buffer range)
+    assert call(n=8388608, stride=8388608) == vc.VC_ERR_UNSUPPORTED and "resident" in _err(L)
+    assert call(n=8388608, stride=8388608, host=1, chunk=8388608) == vc.VC_ERR_UNSUPPORTED
 
 
 def test_merge_and_accept_reject(L):
