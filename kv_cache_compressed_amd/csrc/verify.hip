@@ -23,6 +23,8 @@
 // Both paths write unnormalised split partials (o, m, l); the past is split into ranges (or
 // streamed chunk by chunk from pinned host memory through two device stages), the causal block
 // is one more split, and a log-sum-exp merge produces the output.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -70,12 +72,14 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chun
 // buffer -> LDS copy in flight (the compiler cannot tell which LDS bytes those copies target),
 // which would stall every tile on the copies of the tiles behind it. The compiler does not track
 // these reads either: tr16_wait() must run before the registers are used.
+template <int OFF>
 __device__ __forceinline__ u32x4 tr16_issue(unsigned addr) {
+  static_assert(OFF >= 0 && OFF + 4096 <= 65535, "ds offset field");
   u32x2 r0, r1;
   // early clobber: the second read must not find its address register overwritten by the first
-  asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:4096"
+  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
                : "=&v"(r0), "=&v"(r1)
-               : "v"(addr));
+               : "v"(addr), "n"(OFF), "n"(OFF + 4096));
   return u32x4{r0[0], r0[1], r1[0], r1[1]};
 }
 __device__ __forceinline__ void tr16_wait(u32x4& r) { asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r)); }
@@ -196,8 +200,10 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
   __builtin_amdgcn_s_setprio(3);
   const int q1 = t_begin + (t_end - t_begin) / 3, q2 = t_begin + 2 * (t_end - t_begin) / 3,
             q3 = t_begin + 5 * (t_end - t_begin) / 6;
-  int slot = 0;
-  for (int tile = t_begin; tile < t_end; ++tile) {
+  // One tile; the ring slot is a compile-time constant (the loop below is unrolled by RING), so
+  // every LDS address of the tile is a per-lane base plus an immediate offset.
+  auto step = [&](const int tile, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
     if (tile == q1) __builtin_amdgcn_s_setprio(2);
     if (tile == q2) __builtin_amdgcn_s_setprio(1);
     if (tile == q3) __builtin_amdgcn_s_setprio(0);
@@ -210,7 +216,6 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
       const int64_t tok0 = tile * TK;
       const int tlen = (int)min<int64_t>(TK, src_ntok - tok0);
       const uint8_t* sk = ring + slot * 2 * TILE_BYTES;
-      const uint8_t* sv = sk + TILE_BYTES;
       // ---- QK^T: S^T[token][row]: s[tb][ct][r] = token 16 tb + 4 gq + r, row 16 ct + j -------
       f32x4 s[NTB][2];
 #pragma unroll
@@ -289,20 +294,22 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
       // 16 + 4gq + e; source lane s = j of block gq supplies channels 16t + 4(s&3) .. +3 of token
       // 16h + 4gq + (s>>2) for the transpose read h.
       // The reads of step k + 1 are in flight while step k's products run.
-      const unsigned sv_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)sv;
+      // (the ring's LDS base goes into the lane address, the slot's offset into the immediate)
+      const unsigned ring_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)ring;
+      constexpr int VOFF = slot * 2 * TILE_BYTES + TILE_BYTES;
       auto vaddr = [&](int k) {  // step k = (channel tile t, contraction block hf)
         const int t = k / NHF, hf = k % NHF;
         const int row = 32 * hf + 4 * gq + (j >> 2);
         const int byte = (16 * t + 4 * (j & 3)) * 2;  // within the row
-        return sv_lds + (unsigned)(swz(row, byte >> 4) * 16 + (byte & 15));
+        return ring_lds + (unsigned)(swz(row, byte >> 4) * 16 + (byte & 15));
       };
-      u32x4 vop = tr16_issue(vaddr(0));
+      u32x4 vop = tr16_issue<VOFF>(vaddr(0));
 #pragma unroll
       for (int k = 0; k < 8 * NHF; ++k) {
         const int t = k / NHF, hf = k % NHF;
         tr16_wait(vop);
         const u32x4 cur = vop;
-        if (k + 1 < 8 * NHF) vop = tr16_issue(vaddr(k + 1));
+        if (k + 1 < 8 * NHF) vop = tr16_issue<VOFF>(vaddr(k + 1));
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           acc[ct][t] = mfma_bf16(cur, phi[ct][hf], acc[ct][t]);
@@ -310,7 +317,12 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
         }
       }
     }
-    slot = slot + 1 == RING ? 0 : slot + 1;
+  };
+  static_assert(RING == 3, "the tile loop is unrolled by the ring depth");
+  for (int tile = t_begin; tile < t_end; tile += RING) {
+    step(tile, std::integral_constant<int, 0>{});
+    if (tile + 1 < t_end) step(tile + 1, std::integral_constant<int, 1>{});
+    if (tile + 2 < t_end) step(tile + 2, std::integral_constant<int, 2>{});
   }
   wait_vm<0>();  // no copy may still target LDS when the job (and the workgroup) ends
 
