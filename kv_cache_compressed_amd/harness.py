@@ -28,7 +28,7 @@ class RoundState:
     """Device state of one workload: caches, inputs, outputs and workspaces."""
 
     def __init__(self, w: synth.Workload, seed: int = 0, device: str = "cuda", inputs=None,
-                 idx_lists=None, replicas: int = 1):
+                 idx_lists=None, replicas: int = 1, copy_stream=None):
         self.w, self.seed, self.device = w, seed, device
         if inputs is None:
             K, V = synth.kv_past(w, seed)
@@ -114,7 +114,10 @@ class RoundState:
         self.accept_len = torch.zeros((B,), **i32)
         self.next_tok = torch.zeros((B,), **i32)
         self.argmax_v = torch.zeros((B, L), **i32)
-        self.copy_stream = torch.cuda.Stream(device=device) if w.past_on_host else None
+        # host-streamed verify: the stream its chunk copies go on (may be shared between groups)
+        self.copy_stream = None
+        if w.past_on_host:
+            self.copy_stream = copy_stream or torch.cuda.Stream(device=device)
         # projection workspace (draft argmax tickets); zero-filled once, calls leave it zero
         self.ws_proj = torch.zeros((vc.vc_project_workspace(B, 1, w.vocab) + 3) // 4, **i32)
         self._rep = 0
@@ -193,6 +196,12 @@ class RoundState:
         w = self.w
         self.verify_attention()
         self.verify_tokens()
+
+    def draft_phase(self):
+        """The x draft steps of one round (attention with the step's append fused in, then the
+        logits and greedy token), rotating over the compressed-cache replicas."""
+        for j in range(self.w.x):
+            self.draft_step(j)
 
     def run_round(self, timer=None):
         """One round. `timer`, if given, is called as timer(kind, start) with kind in
@@ -281,3 +290,75 @@ class RoundState:
                     a=self.accept_len.cpu().numpy(), next=self.next_tok.cpu().numpy(),
                     out_d=self.out_d.cpu().numpy(), lse_d=self.lse_d.cpu().numpy(),
                     out_v=self.out_v.cpu().numpy(), lse_v=self.lse_v.cpu().numpy())
+
+
+# ---- schedules over several request groups ------------------------------------------------
+# "VeriCache: making lossy KV compression exact", Verifying Without Giving Back the Speedup and
+# Figure 2; "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference", Key Contributions
+# (cross-resource staggering). Drafting reads each group's compressed cache from HBM; verifying
+# streams its full cache from host memory over PCIe. A lock-step schedule runs every group's
+# draft phase and then every group's verify, so PCIe idles while the groups draft and HBM idles
+# while they verify. The staggered schedule runs each group on a stream of its own and starts
+# group g once group g-1 has finished its first draft phase, so one group's verify transfer
+# overlaps the next group's drafting. The groups are independent requests: both schedules
+# produce the same results, bit for bit.
+#
+# Streams and hardware queues: a process on this GPU gets 4 hardware queues, and streams beyond
+# that share them; two streams on one queue run in submission order, which takes the overlap
+# away (a draft phase queued behind another group's verify waits for its whole transfer). So the
+# groups' compute streams must be few and distinct: group 0 on the current stream, one more
+# stream per further group, and one copy stream shared by all groups (pass group 0's
+# `copy_stream` to the other groups' constructors; their verifies take turns on the link anyway).
+def lockstep(groups, rounds: int = 1):
+    """`rounds` lock-step rounds on the current stream: all groups draft, then all verify."""
+    for _ in range(rounds):
+        for st in groups:
+            st.draft_phase()
+        for st in groups:
+            st.verify_step()
+
+
+def staggered(groups, streams, rounds: int = 1):
+    """`rounds` rounds per group, group g on streams[g] (default priority), each round its draft
+    phase then its verify. The verifies take turns on the host link: verify k (group k % G, round
+    k // G) starts once verify k-1 has finished, and each group drafts its next round as soon as
+    its own verify is done, i.e. while the next group's verify streams. Group g > 0 drafts its
+    first round after group g-1's first draft phase. Work is enqueued in timeline order (the
+    next group's draft phase before this group's verify). The current stream waits for every
+    group stream at the end."""
+    ng = len(groups)
+    assert len(streams) == ng and ng >= 1
+    cur = torch.cuda.current_stream()
+    for s in streams:
+        s.wait_stream(cur)
+    first_done = [torch.cuda.Event() for _ in range(ng)]
+    verify_done = None
+
+    def draft(k):  # draft phase of slot k = (group k % ng, round k // ng)
+        g = k % ng
+        if k < ng and g > 0:
+            streams[g].wait_event(first_done[g - 1])
+        with torch.cuda.stream(streams[g]):
+            groups[g].draft_phase()
+            if k < ng:
+                first_done[g].record(streams[g])
+
+    total = rounds * ng
+    draft(0)
+    for k in range(total):
+        # the next slot's draft phase goes in first when it belongs to another group (with one
+        # group it is this group's next round, which follows its verify)
+        early = k + 1 < total and (k + 1) % ng != k % ng
+        if early:
+            draft(k + 1)
+        s = streams[k % ng]
+        if verify_done is not None:
+            s.wait_event(verify_done)
+        with torch.cuda.stream(s):
+            groups[k % ng].verify_step()
+        verify_done = torch.cuda.Event()
+        verify_done.record(s)
+        if k + 1 < total and not early:
+            draft(k + 1)
+    for s in streams:
+        cur.wait_stream(s)
