@@ -237,10 +237,7 @@ def main():
     K, V = synth.kv_past(w, args.seed)
     Kn, Vn = synth.kv_new(w, args.seed)
     inputs = (K, V, Kn, Vn, synth.q_new(w, args.seed), synth.projection(w, args.seed))
-    idx = None
-    if w.drafter == "drop":
-        idx = [[synth.keep_list(w, args.seed, b, h) for h in range(w.Hkv)] for b in range(w.B)]
-    st = harness.RoundState(w, seed=args.seed, inputs=inputs, idx_lists=idx,
+    st = harness.RoundState(w, seed=args.seed, inputs=inputs,
                             replicas=args.replicas if w.drafter == "kivi" else 1)
     if w.past_on_host:
         args.eager = True  # the host-streamed verify's copy-stream events are not captured
@@ -331,6 +328,15 @@ def main():
             "peak_is": "achieved pinned host->device rate of a plain copy of the same bytes in the "
                        "same 64K-token chunks (median of 5)",
             "frac_of_64GBs": round(v_gbs_pcie / 64.0, 4)}
+    if w.drafter == "drop":
+        sel_us = _back_to_back_us(torch, lambda i: st.select_keep(), 20)
+        sel_bytes = w.B * w.Hkv * (w.n * 4 + st.kept * 4)
+        line["keep_selection"] = {
+            "launch_us": round(sel_us, 2), "rows": w.B * w.Hkv, "n": w.n, "kept": st.kept,
+            "GB_s": round(sel_bytes / (sel_us * 1e-6) / 1e9, 1),
+            "note": "vc_select_keep: scores read once (4 B per position) and kept positions written "
+                    "(4 B each) per (b, kv head); one workgroup per row re-reads its row from L2 "
+                    "for each of 4 passes"}
     if w.past_on_host and args.stagger_rounds > 0:
         line["staggering"] = _staggering(torch, harness, synth, st, args.seed, args.stagger_rounds)
     if not args.no_cpu_baseline and args.workload == "c2":

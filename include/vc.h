@@ -15,6 +15,7 @@
  *   vc_verify_attn       L-query causal block attention over the full cache   (verify)
  *   vc_lse_merge         log-sum-exp merge of split partials                  (verify / draft)
  *   vc_accept            per-row argmax, first disagreement, correction token (accept)
+ *   vc_select_keep       kept positions of a token-dropping drafter           (compressor)
  *   vc_project_logits    logits of the attention outputs (+ greedy argmax): the
  *                        single layer's stand-in for a model head              (harness)
  *
@@ -232,6 +233,30 @@ vc_status vc_project_workspace(int32_t B, int32_t L, int32_t V, size_t *bytes);
 vc_status vc_project_logits(const float *W, int32_t V, const float *o, int32_t B, int32_t Hq,
                             int32_t L, float *logits, int32_t *argmax, int64_t argmax_b_stride,
                             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Keep-list selection of a token-dropping drafter ("VeriCache: making lossy KV compression exact",
+ * The Tradeoff VeriCache Is Trying to Escape: token-dropping compressors keep attention sinks and
+ * recent tokens, or score cached entries and evict the least useful; "VeriCache: Turning Lossy KV
+ * Cache into Lossless LLM Inference", Key Contributions: the compressor interface exposes the
+ * dropped positions; Limitations: the same number dropped in every head). The pages give no
+ * scoring rule; scores are an input. For each of `rows` rows (one per (batch row, kv head)):
+ *   lo = min(sinks, n), hi = max(lo, n - recent), fixed = lo + (n - hi),
+ *   take = min(max(0, keep - fixed), hi - lo),
+ *   kept = [0, lo) + the take highest-scoring positions of [lo, hi) + [hi, n), ascending;
+ *   ranking: larger score first, equal scores (-0 == +0) by lower position, NaN below every
+ *   number. The count lo + (n - hi) + take is the same for every row and is returned in *n_keep
+ *   (host memory, written before the launch).
+ *   scores  fp32 device, row r at scores + r * score_row_stride; score_row_stride a multiple of 4
+ *           and >= n rounded up to a multiple of 4 (the buffer holds rows * score_row_stride floats:
+ *           the kernel reads whole 16-byte groups)
+ *   idx     int32 device, row r's kept positions at idx + r * idx_row_stride (idx_row_stride >=
+ *           *n_keep); entries past *n_keep are not written
+ *   1 <= rows <= 65535, 1 <= n <= 2^31 - 1, sinks, recent, keep >= 0.
+ */
+vc_status vc_select_keep(const float *scores, int64_t score_row_stride, int32_t rows, int64_t n,
+                         int64_t sinks, int64_t recent, int64_t keep, int32_t *idx,
+                         int64_t idx_row_stride, int64_t *n_keep, void *stream);
 
 const char *vc_status_string(vc_status s);
 const char *vc_last_error(void);

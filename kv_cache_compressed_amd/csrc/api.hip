@@ -329,4 +329,32 @@ vc_status vc_project_logits(const float* W, int32_t V, const float* o, int32_t B
   return ok();
 }
 
+vc_status vc_select_keep(const float* scores, int64_t score_row_stride, int32_t rows, int64_t n,
+                         int64_t sinks, int64_t recent, int64_t keep, int32_t* idx,
+                         int64_t idx_row_stride, int64_t* n_keep, void* stream) {
+  REQUIRE(n_keep != nullptr, "n_keep is null");
+  REQUIRE_PTR(scores);
+  REQUIRE_PTR(idx);
+  REQUIRE(rows >= 1 && rows <= 65535, "rows must be in [1, 65535] (got %d)", rows);
+  REQUIRE(n >= 1 && n <= 0x7fffffffLL, "n must be in [1, 2^31 - 1]");
+  REQUIRE(sinks >= 0 && recent >= 0 && keep >= 0, "sinks, recent and keep must be >= 0");
+  const int64_t n4 = (n + 3) & ~(int64_t)3;
+  REQUIRE(score_row_stride >= n4 && score_row_stride % 4 == 0,
+          "score_row_stride must be a multiple of 4 and >= n rounded up to a multiple of 4 (%lld)",
+          (long long)n4);
+  const int64_t lo = sinks < n ? sinks : n;
+  const int64_t hi = (n - recent > lo) ? n - recent : lo;
+  const int64_t fixed = lo + (n - hi);
+  int64_t take = keep - fixed;
+  if (take < 0) take = 0;
+  if (take > hi - lo) take = hi - lo;
+  const int64_t count = fixed + take;
+  REQUIRE(idx_row_stride >= count, "idx_row_stride must be >= the kept count %lld", (long long)count);
+  *n_keep = count;
+  hipError_t e = vc::launch_select_keep(scores, score_row_stride, rows, n, lo, hi, take, idx,
+                                        idx_row_stride, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_select_keep launch");
+  return ok();
+}
+
 }  // extern "C"

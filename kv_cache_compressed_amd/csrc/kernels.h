@@ -73,4 +73,9 @@ hipError_t launch_project(const float* W, int V, const float* o, int B, int Hq, 
                           int32_t* idx, int64_t idx_b_stride, void* ws, const ProjectPlan& plan,
                           hipStream_t s);
 
+// Keep-list selection (token-dropping drafter).
+hipError_t launch_select_keep(const float* scores, int64_t s_stride, int rows, int64_t n, int64_t lo,
+                              int64_t hi, int64_t take, int32_t* idx, int64_t idx_stride,
+                              hipStream_t s);
+
 }  // namespace vc

@@ -90,16 +90,25 @@ class RoundState:
                 torch.cuda.synchronize()
                 del kt, vt
         else:
+            # kept positions of every (b, kv head): selected on the GPU from the seeded scores
+            # (vc_select_keep), or taken from `idx_lists` when the caller gives them; the round's
+            # own positions n .. n+x-1 follow, appended as the draft steps reach them
             if idx_lists is None:
-                idx_lists = [[synth.keep_list(w, seed, b, h) for h in range(Hkv)] for b in range(B)]
-            self.idx_lists = idx_lists
-            kept = len(idx_lists[0][0])
-            idx = np.zeros((B, Hkv, kept + x), np.int32)
-            for b in range(B):
-                for h in range(Hkv):
-                    idx[b, h, :kept] = idx_lists[b][h]
-                    idx[b, h, kept:] = np.arange(n, n + x)
-            self.idx = torch.from_numpy(idx).to(device)
+                kept = self.keep_count(w)
+                self.scores = torch.zeros((B, Hkv, (n + 3) // 4 * 4), dtype=torch.float32, device=device)
+                self.scores[:, :, :n] = torch.from_numpy(
+                    np.stack([np.stack([synth.scores(w, seed, b, h) for h in range(Hkv)]) for b in range(B)]))
+                self.idx = torch.empty((B, Hkv, kept + x), dtype=torch.int32, device=device)
+                got = self.select_keep()
+                assert got == kept, (got, kept)
+            else:
+                kept = len(idx_lists[0][0])
+                idx = np.zeros((B, Hkv, kept + x), np.int32)
+                for b in range(B):
+                    for h in range(Hkv):
+                        idx[b, h, :kept] = idx_lists[b][h]
+                self.idx = torch.from_numpy(idx).to(device)
+            self.idx[:, :, kept:] = torch.arange(n, n + x, dtype=torch.int32, device=device)
             self.kept = kept
         # outputs
         f32 = dict(dtype=torch.float32, device=device)
@@ -123,6 +132,20 @@ class RoundState:
         self._rep = 0
         self.verify_ws_bytes = vc.vc_verify_workspace(B, Hq, Hkv, L, n, w.past_on_host,
                                                       w.chunk_tokens, self._vdt())
+
+    @staticmethod
+    def keep_count(w: synth.Workload) -> int:
+        """Kept positions per (b, kv head) of the token-dropping workload: sinks + recent + the
+        selected middle (the count vc_select_keep returns)."""
+        lo = min(w.sinks, w.n)
+        hi = max(lo, w.n - w.recent)
+        fixed = lo + (w.n - hi)
+        return fixed + min(max(0, w.keep - fixed), hi - lo)
+
+    def select_keep(self) -> int:
+        """Select the kept positions from the scores into idx[:, :, :kept] (vc_select_keep)."""
+        w = self.w
+        return vc.vc_select_keep(self.scores, w.n, w.sinks, w.recent, w.keep, self.idx)
 
     def _vdt(self):
         return vc.VC_BF16 if self.w.kv_dtype == "bf16" else vc.VC_F32

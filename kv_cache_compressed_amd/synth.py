@@ -14,8 +14,8 @@ layers, contexts up to ~500K tokens, draft length 30 and 4x compression ("VeriCa
 Lossy KV Cache into Lossless LLM Inference", Methodology and Results). The KIVI parameters
 (group 32, 2/4-bit, residual length and dtype), the outlier-channel recipe (1% of the
 (kv head, channel) slots scaled by 8) and the keep-list recipe (64 sinks + 256 recent +
-top-scoring middle tokens, 25% kept) are the workload recipes of the study, since the pages
-give none of them.
+top-scoring middle tokens, 25% kept; the scores are drawn here, the selection is the method's)
+are the workload recipes of the study, since the pages give none of them.
 """
 from __future__ import annotations
 
@@ -195,19 +195,3 @@ def projection(w: Workload, seed: int = 0) -> np.ndarray:
 def scores(w: Workload, seed: int, b: int, h: int) -> np.ndarray:
     """Seeded per-(b, kv head) importance scores over positions 0..n-1 (float32 N(0,1))."""
     return normal(seed, w.wid, TAG_SCORES, b, h, (w.n,))
-
-
-def keep_list(w: Workload, seed: int, b: int, h: int) -> np.ndarray:
-    """Kept positions of one (b, kv head) for the token-dropping workload, ascending int32.
-
-    Recipe: the first `sinks` tokens, the last `recent` tokens, and the highest-scoring
-    tokens of the middle until `keep` tokens are kept; equal scores prefer the lower position.
-    """
-    n, k = w.n, w.keep
-    lo, hi = min(w.sinks, n), max(min(w.sinks, n), n - w.recent)
-    fixed = np.concatenate([np.arange(0, lo), np.arange(hi, n)])
-    take = max(0, k - fixed.size)
-    s = scores(w, seed, b, h)[lo:hi]
-    order = np.lexsort((np.arange(s.size), -s))  # descending score, then ascending position
-    mid = lo + np.sort(order[:take])
-    return np.sort(np.concatenate([fixed, mid])).astype(np.int32)

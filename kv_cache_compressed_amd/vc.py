@@ -57,6 +57,7 @@ _SIGS = {
     "vc_accept": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
     "vc_project_workspace": [_I32, _I32, _I32, ctypes.POINTER(_SZ)],
     "vc_project_logits": [_P, _I32, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _SZ, _P],
+    "vc_select_keep": [_P, _I64, _I32, _I64, _I64, _I64, _I64, _P, _I64, ctypes.POINTER(_I64), _P],
     "vc_status_string": [_I32],
     "vc_last_error": [],
     "vc_abi_version": [],
@@ -274,4 +275,20 @@ def vc_project_logits(W, o, logits=None, argmax=None, argmax_b_stride: int | Non
     nb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().vc_project_logits(_ptr(W), V, _ptr(o), B, Hq, L, _ptr(logits), _ptr(argmax),
                                    argmax_b_stride, _ptr(ws), nb, _stream(stream)))
+
+
+def vc_select_keep(scores, n: int, sinks: int, recent: int, keep: int, idx, stream=None) -> int:
+    """Kept positions of every row of `scores` (fp32 [..., stride] on the device, rows = all
+    leading dims, row stride = the last dim) into `idx` (int32 [..., idx_stride]); returns the
+    kept count per row."""
+    assert scores.dtype == torch.float32 and idx.dtype == torch.int32
+    assert scores.stride(-1) == 1 and idx.stride(-1) == 1
+    rows = scores.numel() // scores.shape[-1]
+    assert idx.numel() // idx.shape[-1] == rows
+    out = ctypes.c_int64(0)
+    _check(lib().vc_select_keep(_ptr(scores), scores.shape[-1] if scores.dim() == 1 else scores.stride(-2),
+                                rows, n, sinks, recent, keep, _ptr(idx),
+                                idx.shape[-1] if idx.dim() == 1 else idx.stride(-2), ctypes.byref(out),
+                                _stream(stream)))
+    return int(out.value)
 

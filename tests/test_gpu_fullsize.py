@@ -14,6 +14,7 @@ import pytest
 import torch
 
 from kv_cache_compressed_amd import harness, synth
+from oracle import select as osel
 from oracle import accept as oacc
 from oracle.round import Round, logits
 
@@ -42,9 +43,15 @@ def _run(name):
     print(f"[{name}] drawing inputs", flush=True)
     inp = _inputs(w)
     idx = None
-    if w.drafter == "drop":
-        idx = [[synth.keep_list(w, 0, b, h) for h in range(w.Hkv)] for b in range(w.B)]
-    st = harness.RoundState(w, inputs=inp, idx_lists=idx, replicas=4 if w.drafter == "kivi" else 1)
+    st = harness.RoundState(w, inputs=inp, replicas=4 if w.drafter == "kivi" else 1)
+    if w.drafter == "drop":  # kept positions selected on the GPU: every row equals the oracle's
+        idx = [[osel.keep_positions(synth.scores(w, 0, b, h), w.n, w.sinks, w.recent, w.keep)
+                for h in range(w.Hkv)] for b in range(w.B)]
+        got = st.idx.cpu().numpy()
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                assert np.array_equal(got[b, h, :st.kept], idx[b][h]), f"kept positions b={b} h={h}"
+        print(f"[{name}] kept positions of {w.B * w.Hkv} rows equal the oracle's", flush=True)
     if w.past_on_host:
         st.run_round()
         st.run_round()

@@ -16,6 +16,7 @@ from kv_cache_compressed_amd import harness, synth, vc
 from oracle import accept as oacc
 from oracle import attention as oatt
 from oracle import quant as oq
+from oracle import select as osel
 from oracle.round import Round, logits
 
 pytestmark = pytest.mark.gpu
@@ -35,6 +36,20 @@ W_SMALL = {
     "c4s": synth.WORKLOADS["c4"].with_(n=5000, chunk_tokens=1024),
     "c3s": synth.WORKLOADS["c3"].with_(B=2, n=4000),
 }
+
+
+def _oracle_keep(w, seed=0):
+    """The oracle's kept positions of every (b, kv head) of a token-dropping workload."""
+    return [[osel.keep_positions(synth.scores(w, seed, b, h), w.n, w.sinks, w.recent, w.keep)
+             for h in range(w.Hkv)] for b in range(w.B)]
+
+
+def _check_gpu_keep(st, idx):
+    """The harness selected its kept positions on the GPU: they equal the oracle's, bit for bit."""
+    got = st.idx.cpu().numpy()
+    for b in range(len(idx)):
+        for h in range(len(idx[b])):
+            assert np.array_equal(got[b, h, :st.kept], idx[b][h]), f"kept positions b={b} h={h}"
 
 
 def _inputs(w, seed=0):
@@ -399,8 +414,9 @@ def test_round_graph_replays_match_eager(gpu_lib):
 def test_draft_drop_parity(gpu_lib, name):
     w = W_SMALL[name]
     inp = _inputs(w)
-    idx = [[synth.keep_list(w, 0, b, h) for h in range(w.Hkv)] for b in range(w.B)]
-    st = harness.RoundState(w, inputs=inp, idx_lists=idx)
+    idx = _oracle_keep(w)
+    st = harness.RoundState(w, inputs=inp)
+    _check_gpu_keep(st, idx)
     rnd = Round(w, *inp, idx=idx)
     for j in range(w.x):
         st.draft_attention(j)
@@ -444,8 +460,10 @@ def test_draft_drop_keep_all_and_invalid_entries(gpu_lib):
 def test_verify_parity(gpu_lib, name):
     w = W_SMALL[name]
     inp = _inputs(w)
-    idx = [[synth.keep_list(w, 0, b, h) for h in range(w.Hkv)] for b in range(w.B)] if w.drafter == "drop" else None
-    st = harness.RoundState(w, inputs=inp, idx_lists=idx)
+    idx = _oracle_keep(w) if w.drafter == "drop" else None
+    st = harness.RoundState(w, inputs=inp)
+    if idx is not None:
+        _check_gpu_keep(st, idx)
     rnd = Round(w, *inp, idx=idx)
     st.verify_attention()
     res = st.results()
@@ -534,8 +552,10 @@ def _check_tokens(gpu, ref_rounds, w):
 def test_round_tokens(gpu_lib, name):
     w = W_SMALL[name]
     inp = _inputs(w)
-    idx = [[synth.keep_list(w, 0, b, h) for h in range(w.Hkv)] for b in range(w.B)] if w.drafter == "drop" else None
-    st = harness.RoundState(w, inputs=inp, idx_lists=idx)
+    idx = _oracle_keep(w) if w.drafter == "drop" else None
+    st = harness.RoundState(w, inputs=inp)
+    if idx is not None:
+        _check_gpu_keep(st, idx)
     st.run_round()
     gpu = st.results()
     rnd = Round(w, *inp, idx=idx)
@@ -602,3 +622,54 @@ def test_staggered_schedule_matches_lockstep(gpu_lib):
     rnd = Round(w, *inps[1])
     _check_tokens(got[1], [rnd.run(0)], w)
     assert not np.array_equal(got[0]["out_v"], got[1]["out_v"]), "groups must be distinct requests"
+
+
+# ------------------------------------------------------------------------------------------
+# keep-list selection (token-dropping drafter): bit-exact kept positions
+# ------------------------------------------------------------------------------------------
+def _scores(kind, rows, n, seed):
+    g = np.random.default_rng(seed)
+    if kind == "normal":
+        return g.standard_normal((rows, n)).astype(np.float32)
+    if kind == "ties":
+        return g.integers(-3, 4, (rows, n)).astype(np.float32)
+    if kind == "special":
+        vals = np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, np.nan, 1e-45, -1e-45], np.float32)
+        return g.choice(vals, (rows, n))
+    if kind == "equal":
+        return np.full((rows, n), 0.5, np.float32)
+    if kind == "subnormal":
+        return (g.standard_normal((rows, n)) * 1e-39).astype(np.float32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind,rows,n,sinks,recent,keep,pad", [
+    ("normal", 32, 100000, 64, 256, 25000, 0),     # the dropping workload's shape and recipe
+    ("normal", 3, 4113, 64, 256, 1000, 7),         # ragged n, padded rows
+    ("ties", 4, 8191, 64, 256, 3000, 1),
+    ("ties", 2, 20000, 0, 0, 777, 0),
+    ("special", 3, 3001, 5, 7, 1500, 3),
+    ("equal", 2, 5000, 64, 256, 1250, 0),
+    ("subnormal", 2, 6000, 64, 256, 1500, 0),
+    ("normal", 2, 1000, 64, 256, 0, 0),            # keep below sinks + recent: only those
+    ("normal", 2, 1000, 64, 256, 5000, 0),         # keep above n: everything
+    ("normal", 2, 50, 64, 256, 10, 2),             # n below sinks
+    ("normal", 1, 1, 0, 0, 1, 3),
+    ("normal", 2, 3, 0, 0, 2, 1),
+    ("normal", 2, 4099, 1, 0, 2049, 1),            # the middle runs to the row's end
+])
+def test_select_keep_parity(gpu_lib, kind, rows, n, sinks, recent, keep, pad):
+    S = _scores(kind, rows, n, seed=rows * 1000 + n)
+    stride = (n + 3) // 4 * 4 + 4 * pad
+    buf = np.full((rows, stride), np.nan, np.float32)  # padding must never be read as a score
+    buf[:, :n] = S
+    count = osel.keep_count(n, sinks, recent, keep)
+    idx = torch.full((rows, count + 5), -1, dtype=torch.int32, device="cuda")
+    got_count = vc.vc_select_keep(torch.from_numpy(buf).cuda(), n, sinks, recent, keep, idx)
+    torch.cuda.synchronize()
+    assert got_count == count
+    got = idx.cpu().numpy()
+    for r in range(rows):
+        ref = osel.keep_positions(S[r], n, sinks, recent, keep)
+        assert np.array_equal(got[r, :count], ref), f"{kind} row {r}"
+        assert np.all(got[r, count:] == -1), "entries past the kept count are not written"

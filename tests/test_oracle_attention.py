@@ -11,6 +11,7 @@ import pytest
 import torch
 
 from kv_cache_compressed_amd import synth
+from oracle import select as sel
 from oracle import attention as A
 from oracle.quant import KiviLayer
 
@@ -151,16 +152,18 @@ def test_drop_keep_all_is_full_attention():
     assert np.array_equal(o1, o2) and l1 == l2
 
 
-def test_keep_list_invariants():
+def test_keep_list_recipe_of_the_dropping_workload():
+    """The dropping workload's recipe through the oracle's selection: 25% kept, sinks and recent
+    included, every kept middle score >= every dropped one."""
     w = synth.WORKLOADS["c3"].with_(n=5000, B=2, Hkv=2, Hq=4)
     for b in range(2):
         for h in range(2):
-            idx = synth.keep_list(w, 0, b, h)
+            s = synth.scores(w, 0, b, h)
+            idx = sel.keep_positions(s, w.n, w.sinks, w.recent, w.keep)
             assert idx.size == w.keep == 1250
             assert np.all(np.diff(idx) > 0)
             assert set(range(64)) <= set(idx.tolist())
             assert set(range(w.n - 256, w.n)) <= set(idx.tolist())
-            s = synth.scores(w, 0, b, h)
             mid = np.zeros(w.n, bool)
             mid[64:w.n - 256] = True
             kept = np.zeros(w.n, bool)
@@ -168,8 +171,7 @@ def test_keep_list_invariants():
             assert s[mid & kept].min() >= s[mid & ~kept].max()
 
 
-def test_keep_list_ties_prefer_lower_position(monkeypatch):
+def test_keep_list_ties_prefer_lower_position():
     w = synth.WORKLOADS["c3"].with_(n=400, keep_frac=0.9)   # keep 360: 64 + 256 + 40 of 80
-    monkeypatch.setattr(synth, "scores", lambda w_, seed, b, h: np.zeros(w_.n, np.float32))
-    idx = synth.keep_list(w, 0, 0, 0)
+    idx = sel.keep_positions(np.zeros(w.n, np.float32), w.n, w.sinks, w.recent, w.keep)
     assert idx.tolist() == list(range(64)) + list(range(64, 104)) + list(range(144, 400))
