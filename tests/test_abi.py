@@ -193,7 +193,7 @@ def test_kivi_descriptor_follows_replaced_buffers():
 
 def test_select_keep_rejects(L):
     out = ctypes.c_int64(-1)
-    ok = dict(scores=P, stride=1000, rows=4, n=1000, sinks=64, recent=256, keep=250, idx=P, istride=250)
+    ok = dict(scores=P, stride=1000, rows=4, n=1000, sinks=64, recent=256, keep=400, idx=P, istride=400)
 
     def call(**kw):
         a = dict(ok)
@@ -201,11 +201,12 @@ def test_select_keep_rejects(L):
         return L.vc_select_keep(a["scores"], a["stride"], a["rows"], a["n"], a["sinks"], a["recent"],
                                 a["keep"], a["idx"], a["istride"], ctypes.byref(out), None)
 
+    # every case fails validation (a valid call would launch kernels on the fake pointers)
     for kw, msg in [(dict(scores=0), "scores"), (dict(scores=BAD), "aligned"), (dict(idx=0), "idx"),
                     (dict(rows=0), "rows"), (dict(rows=70000), "rows"), (dict(n=0), "n must"),
                     (dict(n=1 << 31), "n must"), (dict(stride=999), "score_row_stride"),
                     (dict(n=1001, stride=1002), "score_row_stride"), (dict(keep=-1), ">= 0"),
-                    (dict(istride=249), "idx_row_stride")]:
+                    (dict(istride=399), "idx_row_stride"), (dict(keep=0, istride=319), "idx_row_stride")]:
         assert call(**kw) == vc.VC_ERR_INVALID, kw
         assert msg in _err(L), (kw, _err(L))
-    assert L.vc_select_keep(P, 1000, 4, 1000, 64, 256, 250, P, 250, None, None) == vc.VC_ERR_INVALID
+    assert L.vc_select_keep(P, 1000, 4, 1000, 64, 256, 400, P, 400, None, None) == vc.VC_ERR_INVALID
