@@ -10,14 +10,16 @@
 //
 // One workgroup of 1024 threads per row. Scores map to order-preserving 32-bit keys (NaN below
 // every number, -0 equal to +0). A radix select over the middle finds the threshold key T and how
-// many keys equal to T are taken (the lowest positions among them): three passes on 11, 11 and 10
-// key bits, each a histogram over the keys that match the digits found so far (8 LDS copies of the
-// 2048 bins, two waves per copy, to spread atomic conflicts) followed by a search from the top bin
-// by wave 0. A last pass walks positions 0..n-1 in order, 16384 per step, and writes every kept
+// many keys equal to T are taken (the lowest positions among them), on 11, 11 and 10 key bits:
+// the first digit from a histogram of the whole middle (8 LDS copies of the 2048 bins, two waves
+// per copy, to spread atomic conflicts; wave 0 searches from the top bin); then the keys of the
+// chosen bin (about 4% of a row of normal scores) are gathered into LDS, when they fit, and the two
+// other digits come from histograms of those candidates alone (otherwise from two more passes
+// over the row). A last pass walks positions 0..n-1 in order, 16384 per step, and writes every kept
 // position at its rank: one block-wide scan per step of packed (ties, other kept) counts gives
-// each thread how many kept positions and ties precede it. Rows are re-read from L2 by every pass;
-// float4 loads, eight in flight per thread in the histogram passes, the next step's four during a
-// step of the last pass.
+// each thread how many kept positions and ties precede it; a thread's 16 positions that all lie in
+// the middle skip the per-position range checks. float4 loads: eight in flight per thread in the
+// row passes, the next step's four during a step of the last pass.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,7 +31,9 @@ constexpr int ST = 1024;        // threads per workgroup
 constexpr int SW = ST / 64;     // waves
 constexpr int NB = 2048;        // bins of an 11-bit digit
 constexpr int NSUB = 8;         // LDS histogram copies
-constexpr int UNROLL = 8;       // float4 loads in flight per thread (histogram passes)
+constexpr int UNROLL = 8;       // float4 loads in flight per thread (row passes)
+constexpr int PT = 16;          // positions per thread per step of the last pass
+constexpr int CAND = 16384;     // candidate keys gathered in LDS
 
 struct SArgs {
   const float* s;       // row r at s + r * s_stride
@@ -83,10 +87,59 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* s_w, u
   return before + incl - x;
 }
 
+struct Shared {
+  uint32_t hist[NSUB * NB];  // 64 KB
+  uint32_t cand[CAND];       // 64 KB
+  uint32_t s_w[SW];
+  uint32_t digit, above, bin, ncand;
+};
+
+// After the histogram copies are filled: sum them into hist[0 .. NB) and let wave 0 find the digit
+// d with (count above d) < remaining <= (count above d) + count(d) (lane l owns bins 32 l .. 32 l
+// + 31). Leaves the digit, the count above it and the count in its bin in shared memory.
+__device__ void find_digit(Shared& sh, int64_t remaining) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __syncthreads();
+  for (int b = tid; b < NB; b += ST) {  // bin b is owned by one thread: sum in place
+    uint32_t c = 0u;
+#pragma unroll
+    for (int w = 0; w < NSUB; ++w) c += sh.hist[w * NB + b];
+    sh.hist[b] = c;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t c[32];
+    uint32_t sum = 0u;
+#pragma unroll
+    for (int b = 0; b < 32; ++b) {
+      c[b] = sh.hist[32 * lane + b];
+      sum += c[b];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const uint32_t total = __shfl(incl, 63, 64);
+    int64_t above = (int64_t)(total - incl);  // candidates in bins of higher lanes
+    if (above < remaining && remaining <= above + (int64_t)sum) {
+      for (int b = 31; b >= 0; --b) {
+        if (above + (int64_t)c[b] >= remaining) {
+          sh.digit = (uint32_t)(32 * lane + b);
+          sh.above = (uint32_t)above;
+          sh.bin = c[b];
+          break;
+        }
+        above += c[b];
+      }
+    }
+  }
+  __syncthreads();
+}
+
 __global__ void __launch_bounds__(ST) select_keep_kernel(SArgs a) {
-  __shared__ uint32_t hist[NSUB * NB];  // 64 KB
-  __shared__ uint32_t s_w[SW];
-  __shared__ uint32_t s_digit, s_above;
+  __shared__ Shared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* row = a.s + (int64_t)blockIdx.x * a.s_stride;
   int32_t* out = a.idx + (int64_t)blockIdx.x * a.idx_stride;
@@ -104,75 +157,86 @@ __global__ void __launch_bounds__(ST) select_keep_kernel(SArgs a) {
   } else {
     uint32_t prefix = 0u, mask = 0u;
     int64_t remaining = a.take;
-    const int64_t a0 = lo & ~(int64_t)3;
-    uint32_t* h = hist + (wave % NSUB) * NB;
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const uint32_t dm = pass == 2 ? 0x3ffu : 0x7ffu;
-      for (int i = tid; i < NSUB * NB; i += ST) hist[i] = 0u;
+    uint32_t* h = sh.hist + (wave % NSUB) * NB;
+    const int m32 = (int)m;
+    auto clear = [&]() {
+      for (int i = tid; i < NSUB * NB; i += ST) sh.hist[i] = 0u;
       __syncthreads();
-      for (int64_t j0 = a0 + 4 * (int64_t)tid; j0 < hi; j0 += (int64_t)4 * ST * UNROLL) {
+    };
+    // f(key) for every middle position of the row, 4 positions per float4 group
+    auto for_row = [&](auto f) {
+      for (int64_t j0 = (lo & ~(int64_t)3) + 4 * (int64_t)tid; j0 < hi; j0 += (int64_t)4 * ST * UNROLL) {
         float4 v[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
           const int64_t j = j0 + (int64_t)4 * ST * u;
           v[u] = j < hi ? load4(row + j) : float4{0.f, 0.f, 0.f, 0.f};
         }
+        // position j + e is in the middle iff (j + e - lo) as unsigned < hi - lo (32-bit: n < 2^31)
+        const int rel0 = (int)(j0 - lo);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-          const int64_t j = j0 + (int64_t)4 * ST * u;
+          const int rel = rel0 + 4 * ST * u;
           const float e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t p = j + e;
-            if (p < lo || p >= hi) continue;
-            const uint32_t k = order_key(e4[e]);
-            if ((k & mask) == prefix) atomicAdd(&h[(k >> shift) & dm], 1u);
-          }
+          for (int e = 0; e < 4; ++e) f(order_key(e4[e]), (unsigned)(rel + e) < (unsigned)m32);
         }
       }
-      __syncthreads();
-      for (int b = tid; b < NB; b += ST) {  // bin b is owned by one thread: sum in place
-        uint32_t c = 0u;
-#pragma unroll
-        for (int w = 0; w < NSUB; ++w) c += hist[w * NB + b];
-        hist[b] = c;
-      }
-      __syncthreads();
-      if (wave == 0) {
-        // lane l owns bins 32 l .. 32 l + 31; find the digit d with
-        // (count above d) < remaining <= (count above d) + count(d)
-        uint32_t c[32];
-        uint32_t sum = 0u;
-#pragma unroll
-        for (int b = 0; b < 32; ++b) {
-          c[b] = hist[32 * lane + b];
-          sum += c[b];
-        }
-        uint32_t incl = sum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t y = __shfl_up(incl, off, 64);
-          if (lane >= off) incl += y;
-        }
-        const uint32_t total = __shfl(incl, 63, 64);
-        int64_t above = (int64_t)(total - incl);  // candidates in bins of higher lanes
-        if (above < remaining && remaining <= above + (int64_t)sum) {
-          for (int b = 31; b >= 0; --b) {
-            if (above + (int64_t)c[b] >= remaining) {
-              s_digit = (uint32_t)(32 * lane + b);
-              s_above = (uint32_t)above;
-              break;
-            }
-            above += c[b];
-          }
-        }
-      }
-      __syncthreads();
-      remaining -= (int64_t)s_above;
-      prefix |= s_digit << shift;
+    };
+    auto take_digit = [&](int shift, uint32_t dm) {
+      find_digit(sh, remaining);
+      remaining -= (int64_t)sh.above;
+      prefix |= sh.digit << shift;
       mask |= dm << shift;
-      __syncthreads();  // s_digit / s_above are rewritten by the next pass
+    };
+    // digit 1: bits 31..21 over the whole middle
+    clear();
+    for_row([&](uint32_t k, bool in) {
+      if (in) atomicAdd(&h[k >> 21], 1u);
+    });
+    take_digit(21, 0x7ffu);
+    const uint32_t nbin = sh.bin;  // keys that share the first digit: the candidates
+    __syncthreads();               // every thread has read the digit before it is rewritten
+    if (nbin <= (uint32_t)CAND) {
+      // gather the candidates' keys into LDS (a slot per candidate from an LDS counter; their
+      // order is irrelevant to the histograms)
+      if (tid == 0) sh.ncand = 0u;
+      __syncthreads();
+      for_row([&](uint32_t k, bool in) {
+        if (in && (k & mask) == prefix) {
+          const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+          if (slot < (uint32_t)CAND) sh.cand[slot] = k;
+        }
+      });
+      __syncthreads();
+      const int nc = (int)min(sh.ncand, (uint32_t)CAND);
+      // digits 2 (bits 20..10) and 3 (bits 9..0) over the candidates
+      clear();
+      for (int i = tid; i < nc; i += ST) {
+        const uint32_t k = sh.cand[i];
+        atomicAdd(&h[(k >> 10) & 0x7ffu], 1u);  // every candidate matches the first digit
+      }
+      take_digit(10, 0x7ffu);
+      __syncthreads();
+      clear();
+      for (int i = tid; i < nc; i += ST) {
+        const uint32_t k = sh.cand[i];
+        if ((k & mask) == prefix) atomicAdd(&h[k & 0x3ffu], 1u);
+      }
+      take_digit(0, 0x3ffu);
+    } else {
+      // too many keys share the first digit: two more passes over the row
+      clear();
+      for_row([&](uint32_t k, bool in) {
+        if (in && (k & mask) == prefix) atomicAdd(&h[(k >> 10) & 0x7ffu], 1u);
+      });
+      take_digit(10, 0x7ffu);
+      __syncthreads();
+      clear();
+      for_row([&](uint32_t k, bool in) {
+        if (in && (k & mask) == prefix) atomicAdd(&h[k & 0x3ffu], 1u);
+      });
+      take_digit(0, 0x3ffu);
     }
     T = prefix;
     r = remaining;
@@ -181,8 +245,8 @@ __global__ void __launch_bounds__(ST) select_keep_kernel(SArgs a) {
   // ---- positions 0..n-1 in order: keep, and write at the rank --------------------------------
   // Each step covers 16 ST positions, 16 consecutive ones per thread; the next step's loads are
   // issued before this step's scan (whose barriers wait for LDS only), so they stay in flight.
-  constexpr int PT = 16;
-  int64_t g_other = 0, g_ties = 0;  // kept non-tie positions and ties before this step
+  int g_other = 0, g_ties = 0;  // kept non-tie positions and ties before this step (< 2^31)
+  const int rr = (int)r, cnt = (int)a.count;
   float4 cur[PT / 4];
   auto load_step = [&](int64_t c0, float4* v) {
 #pragma unroll
@@ -196,6 +260,7 @@ __global__ void __launch_bounds__(ST) select_keep_kernel(SArgs a) {
     float4 nxt[PT / 4];
     if (c0 + (int64_t)PT * ST < a.n) load_step(c0 + (int64_t)PT * ST, nxt);
     const int64_t p0 = c0 + (int64_t)PT * tid;
+    const bool inside = p0 >= lo && p0 + PT <= hi;  // all 16 positions in the middle (hi <= n)
     uint32_t kinds = 0u;  // 2 bits per position: 0 dropped, 1 kept, 2 tie at the threshold
     uint32_t nk = 0u, nt = 0u;
 #pragma unroll
@@ -203,15 +268,14 @@ __global__ void __launch_bounds__(ST) select_keep_kernel(SArgs a) {
       const float e4[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t p = p0 + 4 * u + e;
-        uint32_t kd = 0u;
-        if (p < a.n) {
-          if (p < lo || p >= hi) {
-            kd = 1u;
-          } else {
-            const uint32_t k = order_key(e4[e]);
-            kd = k > T ? 1u : (k == T ? 2u : 0u);
-          }
+        uint32_t kd;
+        const uint32_t k = order_key(e4[e]);
+        const uint32_t by_key = k > T ? 1u : (k == T ? 2u : 0u);
+        if (inside) {
+          kd = by_key;
+        } else {
+          const int64_t p = p0 + 4 * u + e;
+          kd = p >= a.n ? 0u : ((p < lo || p >= hi) ? 1u : by_key);
         }
         kinds |= kd << (2 * (4 * u + e));
         nk += kd == 1u;
@@ -219,26 +283,26 @@ __global__ void __launch_bounds__(ST) select_keep_kernel(SArgs a) {
       }
     }
     uint32_t tot;
-    const uint32_t ex = block_excl_scan((nt << 16) | nk, s_w, tot);  // counts <= 16384 per step
-    int64_t ties_before = g_ties + (ex >> 16);
-    int64_t base = g_other + (ex & 0xffffu) + (ties_before < r ? ties_before : r);
+    const uint32_t ex = block_excl_scan((nt << 16) | nk, sh.s_w, tot);  // counts <= 16384 per step
+    int ties_before = g_ties + (int)(ex >> 16);
+    int base = g_other + (int)(ex & 0xffffu) + (ties_before < rr ? ties_before : rr);
+    const int q0 = (int)p0;  // positions are below n < 2^31
 #pragma unroll
     for (int e = 0; e < PT; ++e) {
       const uint32_t kd = (kinds >> (2 * e)) & 3u;
-      const bool take_it = kd == 1u || (kd == 2u && ties_before < r);
-      if (take_it && base < a.count) out[base] = (int32_t)(p0 + e);
+      const bool take_it = kd == 1u || (kd == 2u && ties_before < rr);
+      if (take_it && base < cnt) out[base] = q0 + e;
       base += take_it;
       ties_before += kd == 2u;
     }
-    g_other += tot & 0xffffu;
-    g_ties += tot >> 16;
+    g_other += (int)(tot & 0xffffu);
+    g_ties += (int)(tot >> 16);
 #pragma unroll
     for (int u = 0; u < PT / 4; ++u) cur[u] = nxt[u];
   }
 }
 
 }  // namespace
-
 hipError_t launch_select_keep(const float* scores, int64_t s_stride, int rows, int64_t n, int64_t lo,
                               int64_t hi, int64_t take, int32_t* idx, int64_t idx_stride,
                               hipStream_t s) {

@@ -650,6 +650,8 @@ def _scores(kind, rows, n, seed):
     ("ties", 2, 20000, 0, 0, 777, 0),
     ("special", 3, 3001, 5, 7, 1500, 3),
     ("equal", 2, 5000, 64, 256, 1250, 0),
+    ("equal", 2, 100000, 64, 256, 25000, 0),       # the threshold bin too large to gather in LDS
+    ("ties", 3, 100000, 64, 256, 25000, 0),        # a large gathered bin (~1/7 of the row)
     ("subnormal", 2, 6000, 64, 256, 1500, 0),
     ("normal", 2, 1000, 64, 256, 0, 0),            # keep below sinks + recent: only those
     ("normal", 2, 1000, 64, 256, 5000, 0),         # keep above n: everything
