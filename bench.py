@@ -335,8 +335,9 @@ def main():
             "launch_us": round(sel_us, 2), "rows": w.B * w.Hkv, "n": w.n, "kept": st.kept,
             "GB_s": round(sel_bytes / (sel_us * 1e-6) / 1e9, 1),
             "note": "vc_select_keep: scores read once (4 B per position) and kept positions written "
-                    "(4 B each) per (b, kv head); one workgroup per row re-reads its row from L2 "
-                    "for each of 4 passes"}
+                    "(4 B each) per (b, kv head); one workgroup per row reads its row three times "
+                    "(first-digit histogram, gathering that digit's candidates, writing the kept "
+                    "positions)"}
     if w.past_on_host and args.stagger_rounds > 0:
         line["staggering"] = _staggering(torch, harness, synth, st, args.seed, args.stagger_rounds)
     if not args.no_cpu_baseline and args.workload == "c2":

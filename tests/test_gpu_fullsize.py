@@ -104,3 +104,34 @@ def test_c3_full_round(gpu_lib):
 def test_c4_full_round(gpu_lib):
     w, rnd, res = _run("c4")
     _check_outputs(w, rnd, res, pairs=[(0, 0), (0, 17), (0, 31)], verify_heads=[(0, 3), (0, 28)])
+
+
+def test_c4_staggered_equals_lockstep(gpu_lib):
+    """Two requests of the host-streamed 500K-token workload (seeds 0 and 1), as bench.py's
+    staggering measurement runs them: the staggered schedule (group 0 on the current stream,
+    group 1 on one more, one shared copy stream) gives every output of the lock-step schedule bit
+    for bit, over two rounds."""
+    w = synth.WORKLOADS["c4"]
+    groups = []
+    for seed in (0, 1):
+        K, V = synth.kv_past(w, seed)
+        Kn, Vn = synth.kv_new(w, seed)
+        inp = (K, V, Kn, Vn, synth.q_new(w, seed), synth.projection(w, seed))
+        cs = groups[0].copy_stream if groups else None
+        groups.append(harness.RoundState(w, seed=seed, inputs=inp, copy_stream=cs))
+        del K, V, inp
+    print("[c4 staggering] groups ready", flush=True)
+    harness.lockstep(groups, rounds=1)
+    ref = [g.results() for g in groups]
+    for g in groups:
+        for t in (g.out_d, g.out_v, g.logits_d, g.logits_v):
+            t.fill_(float("nan"))
+        for t in (g.drafts, g.argmax_v, g.accept_len, g.next_tok):
+            t.fill_(-7)
+    harness.staggered(groups, [torch.cuda.current_stream(), torch.cuda.Stream()], rounds=2)
+    got = [g.results() for g in groups]
+    for gi in range(2):
+        for k in ("out_d", "draft_logits", "drafts", "out_v", "verify_logits", "verified", "a", "next"):
+            assert np.array_equal(got[gi][k], ref[gi][k]), f"group {gi}: {k}"
+    assert not np.array_equal(got[0]["out_v"], got[1]["out_v"])
+    print("[c4 staggering] staggered == lock-step for both groups", flush=True)
