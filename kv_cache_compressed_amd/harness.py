@@ -28,7 +28,7 @@ class RoundState:
     """Device state of one workload: caches, inputs, outputs and workspaces."""
 
     def __init__(self, w: synth.Workload, seed: int = 0, device: str = "cuda", inputs=None,
-                 idx_lists=None, replicas: int = 1, copy_stream=None):
+                 idx_lists=None, replicas: int = 1, copy_stream=None, extra_tokens: int = 0):
         self.w, self.seed, self.device = w, seed, device
         if inputs is None:
             K, V = synth.kv_past(w, seed)
@@ -45,7 +45,11 @@ class RoundState:
         self.q_draft = self.q_verify.permute(2, 0, 1, 3).contiguous()          # [L, B, Hq, 128]
         self.W = _dev(W, torch.float32, device)                                # [V, Hq*128]
         # full cache: device store [B, Hkv, tok_cap, 128] (past + block), or pinned host past
-        cap = w.tok_cap
+        # (extra_tokens: room for a multi-round decode to grow the context past n + L)
+        cap = (w.tok_cap + extra_tokens + 31) // 32 * 32
+        self.cap = cap
+        self.n = n                                   # cached (committed) tokens
+        self.n_q = w.n_q if w.drafter == "kivi" else 0  # of which quantised
         if w.past_on_host:
             self.k_host = torch.empty((B, Hkv, n, 128), dtype=tdt, pin_memory=True)
             self.v_host = torch.empty_like(self.k_host, pin_memory=True)
@@ -75,7 +79,7 @@ class RoundState:
             # steps can read different copies, as the layers of a real model would); they share one
             # residual ring, to which each draft-round entry is appended once.
             for k in range(max(1, replicas)):
-                c = vc.KiviCache(B, Hkv, max(w.n_q, 32), w.bits,
+                c = vc.KiviCache(B, Hkv, (max(w.n_q, 32) + extra_tokens + 31) // 32 * 32, w.bits,
                                  vc.VC_F16 if w.meta_dtype == "f16" else vc.VC_F32,
                                  vc.VC_F16 if w.res_dtype == "f16" else vc.VC_F32, w.res_cap, device)
                 vc.vc_quantize_kv(c, src[0], src[1], 0, w.n_q, src_bh_stride=src[2])
@@ -158,15 +162,15 @@ class RoundState:
         w = self.w
         if w.drafter == "kivi":
             c = cache or self.replicas[0]
-            r = (w.n - w.n_q) + j + 1
-            key = (id(c), w.n_q, r)
+            r = (self.n - self.n_q) + j + 1
+            key = (id(c), self.n_q, r)
             nb = self._ws_sizes.get(key)
             if nb is None:
-                nb = self._ws_sizes[key] = vc.vc_draft_quant_workspace(c, w.n_q, r, w.Hq)
+                nb = self._ws_sizes[key] = vc.vc_draft_quant_workspace(c, self.n_q, r, w.Hq)
             kn = vn = None
             if append:  # the step's own key/value goes into the (shared) residual ring in-kernel
                 kn, vn = self.k_blk[:, :, j], self.v_blk[:, :, j]
-            vc.vc_draft_attn_quant(c, w.n_q, r, self.q_draft[j], self.out_d[j], self.lse_d[j],
+            vc.vc_draft_attn_quant(c, self.n_q, r, self.q_draft[j], self.out_d[j], self.lse_d[j],
                                    self.ws_draft.get(nb), SM_SCALE, k_new=kn, v_new=vn)
         else:
             n_keep = self.kept + j + 1
@@ -178,7 +182,7 @@ class RoundState:
         """Append the key/value of position n+j to the (shared) residual ring."""
         w = self.w
         if w.drafter == "kivi":
-            vc.vc_kivi_append(self.replicas[0], self.k_blk[:, :, j], self.v_blk[:, :, j], w.n + j, 1,
+            vc.vc_kivi_append(self.replicas[0], self.k_blk[:, :, j], self.v_blk[:, :, j], self.n + j, 1,
                               src_bh_stride=w.L * 128)
 
     def draft_step(self, j: int):
@@ -191,6 +195,9 @@ class RoundState:
 
     def verify_attention(self):
         w = self.w
+        if self.n != w.n:  # a multi-round decode has grown the context
+            self.verify_ws_bytes = vc.vc_verify_workspace(w.B, w.Hq, w.Hkv, w.L, self.n, w.past_on_host,
+                                                          w.chunk_tokens, self._vdt())
         ws = self.ws_verify.get(self.verify_ws_bytes)
         if w.past_on_host:
             vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.k_host, self.v_host, w.n,
@@ -198,8 +205,8 @@ class RoundState:
                               past_on_host=True, chunk_tokens=w.chunk_tokens,
                               copy_stream=self.copy_stream)
         else:
-            vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.k_store, self.v_store, w.n,
-                              self.out_v, self.lse_v, ws, SM_SCALE, past_stride=w.tok_cap)
+            vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.k_store, self.v_store, self.n,
+                              self.out_v, self.lse_v, ws, SM_SCALE, past_stride=self.cap)
 
     def draft_tokens(self, j: int):
         """Logits of draft step j and its greedy token, written straight into drafts[:, j]."""
@@ -219,6 +226,45 @@ class RoundState:
         w = self.w
         self.verify_attention()
         self.verify_tokens()
+
+    # ---- multi-round decode of one request ------------------------------------------------
+    def set_round_inputs(self, K_new, V_new, Q):
+        """Load the next round's block keys/values [B, Hkv, L, d] and queries [B, Hq, L, d] (host
+        arrays) into the round's device tensors, in place."""
+        self.k_blk.copy_(torch.from_numpy(np.ascontiguousarray(K_new)).to(self.tdt))
+        self.v_blk.copy_(torch.from_numpy(np.ascontiguousarray(V_new)).to(self.tdt))
+        q = torch.from_numpy(np.ascontiguousarray(Q)).to(self.tdt)
+        self.q_verify.copy_(q)
+        self.q_draft.copy_(q.permute(2, 0, 1, 3))
+
+    def commit(self) -> int:
+        """After a round of a single request (B = 1, HBM-resident KIVI workload): commit the
+        accepted drafts and the verifier's token, i.e. positions n .. n+a, whose keys/values the
+        round's block holds, to the full store (the draft steps already stored positions n .. n+x-1
+        in the residual ring; when all x drafts stand, position n+x is appended here); then flush whole 32-token groups of the oldest residual tokens into the codes of
+        every replica while the residual holds R + 32 or more tokens ("VeriCache: Turning Lossy KV
+        Cache into Lossless LLM Inference", Key Contributions: the compressor interface; the
+        quantised groups are taken from the full-precision store). Returns a. The entry points take
+        one length for the whole batch, so rows that accept different counts would need per-row
+        lengths; this loop runs one request."""
+        w = self.w
+        assert w.B == 1 and w.drafter == "kivi" and not w.past_on_host
+        a = int(self.accept_len[0].item())
+        n0, n1 = self.n, self.n + a + 1
+        assert n1 + w.L <= self.cap, "store capacity exhausted (raise extra_tokens)"
+        self.k_store[:, :, n0:n1] = self.k_blk[:, :, :a + 1]
+        self.v_store[:, :, n0:n1] = self.v_blk[:, :, :a + 1]
+        if a == w.x:  # every draft stood: the bonus position n + x was never drafted, so its
+            # key/value is not in the residual ring yet (the draft steps wrote n .. n+x-1)
+            vc.vc_kivi_append(self.replicas[0], self.k_blk[:, :, w.x], self.v_blk[:, :, w.x], n0 + w.x, 1,
+                              src_bh_stride=w.L * 128)
+        self.n = n1
+        while self.n - self.n_q >= w.R + w.group:
+            for c in self.replicas:
+                vc.vc_quantize_kv(c, self.k_store[:, :, self.n_q:], self.v_store[:, :, self.n_q:],
+                                  self.n_q, w.group, src_bh_stride=self.cap * 128)
+            self.n_q += w.group
+        return a
 
     def draft_phase(self):
         """The x draft steps of one round (attention with the step's append fused in, then the

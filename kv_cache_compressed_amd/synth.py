@@ -110,12 +110,14 @@ WORKLOADS = {
 }
 
 
-def generator(seed: int, wid: int, tag: int, b: int = 0, h: int = 0) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, wid, tag, b, h])))
+def generator(seed: int, wid: int, tag: int, b: int = 0, h: int = 0,
+              extra: int | None = None) -> np.random.Generator:
+    ent = [seed, wid, tag, b, h] + ([] if extra is None else [extra])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(ent)))
 
 
-def normal(seed: int, wid: int, tag: int, b: int, h: int, shape) -> np.ndarray:
-    return generator(seed, wid, tag, b, h).standard_normal(shape, dtype=np.float32)
+def normal(seed: int, wid: int, tag: int, b: int, h: int, shape, extra: int | None = None) -> np.ndarray:
+    return generator(seed, wid, tag, b, h, extra).standard_normal(shape, dtype=np.float32)
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -134,8 +136,9 @@ def outlier_slots(w: Workload, seed: int = 0) -> np.ndarray:
     return np.stack([flat // w.d, flat % w.d], axis=1)
 
 
-def _kv_slice(w: Workload, seed: int, tag: int, b: int, h: int, ntok: int, slots) -> np.ndarray:
-    x = normal(seed, w.wid, tag, b, h, (ntok, w.d))
+def _kv_slice(w: Workload, seed: int, tag: int, b: int, h: int, ntok: int, slots,
+              extra: int | None = None) -> np.ndarray:
+    x = normal(seed, w.wid, tag, b, h, (ntok, w.d), extra)
     if w.kv_dtype == "bf16":
         x = round_bf16(x)
     for hh, c in slots:
@@ -164,24 +167,29 @@ def kv_past(w: Workload, seed: int = 0):
     return K, V
 
 
-def kv_new(w: Workload, seed: int = 0):
-    """Keys/values of the round's positions n..n+x: float32 arrays [B, Hkv, L, d]."""
+def kv_new(w: Workload, seed: int = 0, round_index: int = 0):
+    """Keys/values of the round's positions n..n+x: float32 arrays [B, Hkv, L, d]. Round t > 0 of
+    a multi-round decode draws its own block (positions that a round drafted but did not commit
+    get new values in the next round, as they would once the token there changes)."""
     slots = outlier_slots(w, seed)
+    extra = None if round_index == 0 else round_index
     K = np.empty((w.B, w.Hkv, w.L, w.d), np.float32)
     V = np.empty_like(K)
     for b in range(w.B):
         for h in range(w.Hkv):
-            K[b, h] = _kv_slice(w, seed, TAG_K_NEW, b, h, w.L, slots)
-            V[b, h] = _kv_slice(w, seed, TAG_V_NEW, b, h, w.L, slots)
+            K[b, h] = _kv_slice(w, seed, TAG_K_NEW, b, h, w.L, slots, extra)
+            V[b, h] = _kv_slice(w, seed, TAG_V_NEW, b, h, w.L, slots, extra)
     return K, V
 
 
-def q_new(w: Workload, seed: int = 0) -> np.ndarray:
-    """Queries of positions n..n+x: float32 [B, Hq, L, d] (bf16-valued for bf16 workloads)."""
+def q_new(w: Workload, seed: int = 0, round_index: int = 0) -> np.ndarray:
+    """Queries of positions n..n+x: float32 [B, Hq, L, d] (bf16-valued for bf16 workloads); round
+    t > 0 of a multi-round decode draws its own."""
+    extra = None if round_index == 0 else round_index
     Q = np.empty((w.B, w.Hq, w.L, w.d), np.float32)
     for b in range(w.B):
         for h in range(w.Hq):
-            Q[b, h] = normal(seed, w.wid, TAG_Q_NEW, b, h, (w.L, w.d))
+            Q[b, h] = normal(seed, w.wid, TAG_Q_NEW, b, h, (w.L, w.d), extra)
     if w.kv_dtype == "bf16":
         Q = round_bf16(Q)
     return Q

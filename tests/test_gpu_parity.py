@@ -675,3 +675,58 @@ def test_select_keep_parity(gpu_lib, kind, rows, n, sinks, recent, keep, pad):
         ref = osel.keep_positions(S[r], n, sinks, recent, keep)
         assert np.array_equal(got[r, :count], ref), f"{kind} row {r}"
         assert np.all(got[r, count:] == -1), "entries past the kept count are not written"
+
+
+# ------------------------------------------------------------------------------------------
+# multi-round decode of one request: commit the accepted tokens, flush the residual into codes
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,rounds", [("c1", 40), ("c2", 40)])
+def test_multi_round_decode_with_flush(gpu_lib, name, rounds):
+    """Rounds chained on one request: each round's accepted drafts plus the verifier's token are
+    committed, and whole 32-token groups of the oldest residual tokens are flushed into the codes
+    whenever the residual reaches R + 32. Every round's tokens match the oracle's round at the
+    current context (which quantises every group below n_q = 32 floor((n - R) / 32) at once), and
+    the incrementally flushed codes and metadata equal the oracle's quantisation of the committed
+    keys/values bit for bit."""
+    w = {"c1": synth.WORKLOADS["c1"].with_(n=100), "c2": synth.WORKLOADS["c2"].with_(B=1, n=300, x=6)}[name]
+    inp0 = _inputs(w)
+    W = inp0[5]
+    st = harness.RoundState(w, inputs=inp0, replicas=2, extra_tokens=rounds * w.L + 64)
+    Kc, Vc = inp0[0].copy(), inp0[1].copy()  # committed keys/values (host, exact input values)
+    n, n_q0, accepted = w.n, st.n_q, []
+    for t in range(rounds):
+        if t == 0:
+            Kn, Vn, Q = inp0[2], inp0[3], inp0[4]
+        else:
+            Kn, Vn = synth.kv_new(w, 0, t)
+            Q = synth.q_new(w, 0, t)
+            st.set_round_inputs(Kn, Vn, Q)
+        st.run_round()
+        gpu = st.results()
+        wt = w.with_(n=n)
+        assert st.n == n and st.n_q == wt.n_q, (t, st.n, st.n_q, wt.n_q)
+        ref = Round(wt, Kc, Vc, Kn, Vn, Q, W).run(0)
+        dz = np.abs(gpu["draft_logits"][:, 0] - ref["draft_logits"]).max(axis=1)
+        print(f"[{name}] round {t}: n {n} n_q {st.n_q} a {int(gpu['a'][0])}/{ref['a']} "
+              f"max|dz| per step {np.array2string(dz, precision=2)}", flush=True)
+        _check_tokens(gpu, [ref], wt)
+        a = st.commit()
+        assert a == int(gpu["a"][0])
+        accepted.append(a)
+        Kc = np.concatenate([Kc, Kn[:, :, :a + 1]], axis=2)
+        Vc = np.concatenate([Vc, Vn[:, :, :a + 1]], axis=2)
+        n += a + 1
+    print(f"[{name}] accepted per round {accepted}; n {w.n} -> {st.n}, n_q {n_q0} -> {st.n_q}", flush=True)
+    assert st.n_q > n_q0, "the loop must have flushed at least one group"
+    mdt = np.float16 if w.meta_dtype == "f16" else np.float32
+    nq = st.n_q
+    for c in st.replicas:
+        for h in range(w.Hkv):
+            kc, ks, km = oq.quantize_k(Kc[0, h, :nq], w.bits, w.meta_dtype)
+            vcod, vs, vm = oq.quantize_v(Vc[0, h, :nq], w.bits, w.meta_dtype)
+            assert np.array_equal(c.k_codes[0, h, :nq].cpu().numpy(), oq.pack_codes(kc, w.bits, "k"))
+            assert np.array_equal(c.v_codes[0, h, :nq].cpu().numpy(), oq.pack_codes(vcod, w.bits, "v"))
+            gk = c.k_meta[0, h, :nq // 32].cpu().numpy()
+            gv = c.v_meta[0, h, :nq].cpu().numpy()
+            assert np.array_equal(gk[:, 0], ks.astype(mdt)) and np.array_equal(gk[:, 1], km.astype(mdt))
+            assert np.array_equal(gv[..., 0], vs.astype(mdt)) and np.array_equal(gv[..., 1], vm.astype(mdt))
