@@ -108,7 +108,7 @@ def _h2d_rate(torch, st) -> dict:
     ct = w.chunk_tokens
     dk = torch.empty((w.B, w.Hkv, ct, 128), dtype=st.k_host.dtype, device="cuda")
     dv = torch.empty_like(dk)
-    nbytes = 2 * st.k_host.numel() * st.k_host.element_size()
+    nbytes = 2 * w.B * w.Hkv * w.n * 128 * st.k_host.element_size()
     times = []
     for _ in range(5):
         torch.cuda.synchronize()
@@ -177,6 +177,32 @@ def _staggering(torch, harness, synth, st0, seed: int, rounds: int) -> dict:
                     "never idle afterwards)"}
 
 
+def _decode_loop(torch, harness, synth, w, seed: int, rounds: int) -> dict:
+    """Multi-round decode of one request: each round drafts x tokens, verifies, accepts, commits
+    the accepted positions and flushes whole residual groups into the codes; the next round's
+    queries/keys/values are drawn beforehand and uploaded between rounds."""
+    st = harness.RoundState(w, seed=seed, extra_tokens=rounds * w.L + 64)
+    blocks = [(synth.kv_new(w, seed, t), synth.q_new(w, seed, t)) for t in range(1, rounds + 1)]
+    st.run_round()  # warm-up (sizes every workspace); not committed, so the first timed round repeats it
+    torch.cuda.synchronize()
+    n0, nq0, acc = st.n, st.n_q, []
+    t0 = time.perf_counter()
+    for t in range(rounds):
+        st.run_round()
+        acc.append(st.commit())
+        (Kn, Vn), Q = blocks[t]
+        st.set_round_inputs(Kn, Vn, Q)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    emitted = sum(a + 1 for a in acc)
+    return {"rounds": rounds, "accepted_per_round": acc, "emitted": emitted,
+            "ms_per_round": round(el / rounds * 1e3, 3), "tok_s": round(emitted / el, 2),
+            "context": [n0, st.n], "quantised": [nq0, st.n_q], "flushes": (st.n_q - nq0) // w.group,
+            "note": "one request; per round: x draft steps, verify, accept, commit of the accepted "
+                    "positions (plus the bonus one), flush of whole residual groups; next round's "
+                    "inputs uploaded between rounds (host clock around the rounds)"}
+
+
 def _back_to_back_us(torch, launch, n: int) -> float:
     """Mean duration of n launches enqueued back to back between two events (microseconds)."""
     for i in range(3):
@@ -214,6 +240,9 @@ def main():
     ap.add_argument("--stagger-rounds", type=int, default=3,
                     help="host-streamed workload only: rounds per schedule for the lock-step vs "
                          "staggered comparison over two request groups (0 skips it)")
+    ap.add_argument("--decode-rounds", type=int, default=0,
+                    help="single-request KIVI workloads (c1, c4): also run this many chained decode "
+                         "rounds (commit + residual flush between rounds) and report them")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every launch of a round from Python instead of replaying the "
                          "round captured as a HIP graph")
@@ -340,6 +369,15 @@ def main():
                     "positions)"}
     if w.past_on_host and args.stagger_rounds > 0:
         line["staggering"] = _staggering(torch, harness, synth, st, args.seed, args.stagger_rounds)
+    if args.decode_rounds > 0 and w.B == 1 and w.drafter == "kivi":
+        dl = _decode_loop(torch, harness, synth, w, args.seed, args.decode_rounds)
+        if w.past_on_host:
+            # full-KV greedy decode without a drafter streams the whole past once per token: its
+            # rate is bounded by one host-streamed pass (the verify call measured above)
+            dl["full_kv_decode_tok_s_bound"] = round(1e6 / v_kernel_us, 2)
+            dl["full_kv_bound_is"] = ("1 / (one host-streamed pass over the full KV, the measured "
+                                      "verify call): no run of a drafter-less decode")
+        line["decode_loop"] = dl
     if not args.no_cpu_baseline and args.workload == "c2":
         line["cpu_baseline"] = cpu_baseline(w, inputs, a_plus_1, args.cpu_draft_steps,
                                             args.cpu_verify_heads)

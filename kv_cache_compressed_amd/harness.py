@@ -51,10 +51,11 @@ class RoundState:
         self.n = n                                   # cached (committed) tokens
         self.n_q = w.n_q if w.drafter == "kivi" else 0  # of which quantised
         if w.past_on_host:
-            self.k_host = torch.empty((B, Hkv, n, 128), dtype=tdt, pin_memory=True)
+            self.host_cap = n + extra_tokens
+            self.k_host = torch.empty((B, Hkv, self.host_cap, 128), dtype=tdt, pin_memory=True)
             self.v_host = torch.empty_like(self.k_host, pin_memory=True)
-            self.k_host.copy_(torch.from_numpy(K).to(tdt))
-            self.v_host.copy_(torch.from_numpy(V).to(tdt))
+            self.k_host[:, :, :n].copy_(torch.from_numpy(K).to(tdt))
+            self.v_host[:, :, :n].copy_(torch.from_numpy(V).to(tdt))
             self.k_store = self.v_store = None
         else:
             self.k_store = torch.zeros((B, Hkv, cap, 128), dtype=tdt, device=device)
@@ -200,8 +201,8 @@ class RoundState:
                                                           w.chunk_tokens, self._vdt())
         ws = self.ws_verify.get(self.verify_ws_bytes)
         if w.past_on_host:
-            vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.k_host, self.v_host, w.n,
-                              self.out_v, self.lse_v, ws, SM_SCALE, past_stride=w.n,
+            vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.k_host, self.v_host, self.n,
+                              self.out_v, self.lse_v, ws, SM_SCALE, past_stride=self.host_cap,
                               past_on_host=True, chunk_tokens=w.chunk_tokens,
                               copy_stream=self.copy_stream)
         else:
@@ -238,9 +239,10 @@ class RoundState:
         self.q_draft.copy_(q.permute(2, 0, 1, 3))
 
     def commit(self) -> int:
-        """After a round of a single request (B = 1, HBM-resident KIVI workload): commit the
+        """After a round of a single request (B = 1, KIVI drafter): commit the
         accepted drafts and the verifier's token, i.e. positions n .. n+a, whose keys/values the
-        round's block holds, to the full store (the draft steps already stored positions n .. n+x-1
+        round's block holds, to the full store (in HBM, or in pinned host memory when the verify
+        streams it; the draft steps already stored positions n .. n+x-1
         in the residual ring; when all x drafts stand, position n+x is appended here); then flush whole 32-token groups of the oldest residual tokens into the codes of
         every replica while the residual holds R + 32 or more tokens ("VeriCache: Turning Lossy KV
         Cache into Lossless LLM Inference", Key Contributions: the compressor interface; the
@@ -248,22 +250,33 @@ class RoundState:
         one length for the whole batch, so rows that accept different counts would need per-row
         lengths; this loop runs one request."""
         w = self.w
-        assert w.B == 1 and w.drafter == "kivi" and not w.past_on_host
+        assert w.B == 1 and w.drafter == "kivi"
         a = int(self.accept_len[0].item())
         n0, n1 = self.n, self.n + a + 1
-        assert n1 + w.L <= self.cap, "store capacity exhausted (raise extra_tokens)"
-        self.k_store[:, :, n0:n1] = self.k_blk[:, :, :a + 1]
-        self.v_store[:, :, n0:n1] = self.v_blk[:, :, :a + 1]
+        if w.past_on_host:  # the full cache lives in pinned host memory
+            assert n1 <= self.host_cap, "host store capacity exhausted (raise extra_tokens)"
+            self.k_host[:, :, n0:n1].copy_(self.k_blk[:, :, :a + 1])
+            self.v_host[:, :, n0:n1].copy_(self.v_blk[:, :, :a + 1])
+        else:
+            assert n1 + w.L <= self.cap, "store capacity exhausted (raise extra_tokens)"
+            self.k_store[:, :, n0:n1] = self.k_blk[:, :, :a + 1]
+            self.v_store[:, :, n0:n1] = self.v_blk[:, :, :a + 1]
         if a == w.x:  # every draft stood: the bonus position n + x was never drafted, so its
             # key/value is not in the residual ring yet (the draft steps wrote n .. n+x-1)
             vc.vc_kivi_append(self.replicas[0], self.k_blk[:, :, w.x], self.v_blk[:, :, w.x], n0 + w.x, 1,
                               src_bh_stride=w.L * 128)
         self.n = n1
         while self.n - self.n_q >= w.R + w.group:
+            g0, g1 = self.n_q, self.n_q + w.group
+            if w.past_on_host:  # the group's exact keys/values, staged on the device
+                ks = self.k_host[:, :, g0:g1].to(self.k_blk.device)
+                vs = self.v_host[:, :, g0:g1].to(self.k_blk.device)
+                src = (ks, vs, w.group * 128)
+            else:
+                src = (self.k_store[:, :, g0:], self.v_store[:, :, g0:], self.cap * 128)
             for c in self.replicas:
-                vc.vc_quantize_kv(c, self.k_store[:, :, self.n_q:], self.v_store[:, :, self.n_q:],
-                                  self.n_q, w.group, src_bh_stride=self.cap * 128)
-            self.n_q += w.group
+                vc.vc_quantize_kv(c, src[0], src[1], g0, w.group, src_bh_stride=src[2])
+            self.n_q = g1
         return a
 
     def draft_phase(self):

@@ -680,15 +680,18 @@ def test_select_keep_parity(gpu_lib, kind, rows, n, sinks, recent, keep, pad):
 # ------------------------------------------------------------------------------------------
 # multi-round decode of one request: commit the accepted tokens, flush the residual into codes
 # ------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("name,rounds", [("c1", 40), ("c2", 40)])
+@pytest.mark.parametrize("name,rounds", [("c1", 40), ("c2", 40), ("c4", 12)])
 def test_multi_round_decode_with_flush(gpu_lib, name, rounds):
     """Rounds chained on one request: each round's accepted drafts plus the verifier's token are
-    committed, and whole 32-token groups of the oldest residual tokens are flushed into the codes
+    committed (to the HBM store, or to the pinned host store the verify streams), and whole 32-token groups of the oldest residual tokens are flushed into the codes
     whenever the residual reaches R + 32. Every round's tokens match the oracle's round at the
     current context (which quantises every group below n_q = 32 floor((n - R) / 32) at once), and
     the incrementally flushed codes and metadata equal the oracle's quantisation of the committed
     keys/values bit for bit."""
-    w = {"c1": synth.WORKLOADS["c1"].with_(n=100), "c2": synth.WORKLOADS["c2"].with_(B=1, n=300, x=6)}[name]
+    # (c4: the full cache in pinned host memory, streamed by every verify; n leaves the residual one
+    # token short of a flush)
+    w = {"c1": synth.WORKLOADS["c1"].with_(n=100), "c2": synth.WORKLOADS["c2"].with_(B=1, n=300, x=6),
+         "c4": synth.WORKLOADS["c4"].with_(n=4959, x=8, chunk_tokens=1024)}[name]
     inp0 = _inputs(w)
     W = inp0[5]
     st = harness.RoundState(w, inputs=inp0, replicas=2, extra_tokens=rounds * w.L + 64)
