@@ -203,6 +203,44 @@ def _decode_loop(torch, harness, synth, w, seed: int, rounds: int) -> dict:
                     "inputs uploaded between rounds (host clock around the rounds)"}
 
 
+def _decode_pair(torch, harness, synth, w, seed: int, rounds: int) -> dict:
+    """Two requests of the host-streamed workload (seeds seed, seed + 1) decoded over `rounds`
+    chained rounds each, lock-step against staggered (each from fresh caches on the same inputs)."""
+    seeds = (seed, seed + 1)
+    nxt = {(g, r): (*synth.kv_new(w, seeds[g], r), synth.q_new(w, seeds[g], r))
+           for g in range(2) for r in range(1, rounds)}
+
+    def build():
+        g0 = harness.RoundState(w, seed=seeds[0], extra_tokens=rounds * w.L + 64)
+        g1 = harness.RoundState(w, seed=seeds[1], extra_tokens=rounds * w.L + 64,
+                                copy_stream=g0.copy_stream)
+        for g in (g0, g1):  # warm-up round (sizes workspaces), not committed
+            g.run_round()
+        torch.cuda.synchronize()
+        return [g0, g1]
+
+    out = {}
+    for name in ("lockstep", "staggered"):
+        groups = build()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if name == "lockstep":
+            acc = harness.lockstep_decode(groups, rounds, lambda g, r: nxt[(g, r)])
+        else:
+            acc = harness.staggered_decode(groups, [torch.cuda.current_stream(), torch.cuda.Stream()],
+                                           rounds, lambda g, r: nxt[(g, r)])
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        emitted = sum(a + 1 for ag in acc for a in ag)
+        out[name] = {"ms_per_round": round(el / rounds * 1e3, 3), "tok_s": round(emitted / el, 2),
+                     "accepted": acc}
+        del groups
+    out["speedup"] = round(out["lockstep"]["ms_per_round"] / out["staggered"]["ms_per_round"], 4)
+    out["note"] = ("two requests, each round both draft 30 steps and verify 31 rows over their "
+                   "500K-token pinned-host KV, then commit and flush; same inputs for both schedules")
+    return out
+
+
 def _back_to_back_us(torch, launch, n: int) -> float:
     """Mean duration of n launches enqueued back to back between two events (microseconds)."""
     for i in range(3):
@@ -378,6 +416,9 @@ def main():
             dl["full_kv_bound_is"] = ("1 / (one host-streamed pass over the full KV, the measured "
                                       "verify call): no run of a drafter-less decode")
         line["decode_loop"] = dl
+        if w.past_on_host and args.stagger_rounds > 0:
+            line["decode_two_requests"] = _decode_pair(torch, harness, synth, w, args.seed,
+                                                       args.decode_rounds)
     if not args.no_cpu_baseline and args.workload == "c2":
         line["cpu_baseline"] = cpu_baseline(w, inputs, a_plus_1, args.cpu_draft_steps,
                                             args.cpu_verify_heads)

@@ -444,3 +444,69 @@ def staggered(groups, streams, rounds: int = 1):
             draft(k + 1)
     for s in streams:
         cur.wait_stream(s)
+
+
+def lockstep_decode(groups, rounds: int, next_inputs):
+    """`rounds` chained decode rounds of single-request groups on the current stream, lock-step:
+    all groups draft, all verify, then each commits and loads its next round's inputs
+    (next_inputs(g, r) -> (K_new, V_new, Q) for round r >= 1). Returns the accepted counts per
+    group."""
+    acc = [[] for _ in groups]
+    for r in range(rounds):
+        for st in groups:
+            st.draft_phase()
+        for st in groups:
+            st.verify_step()
+        for g, st in enumerate(groups):
+            acc[g].append(st.commit())
+            if r + 1 < rounds:
+                st.set_round_inputs(*next_inputs(g, r + 1))
+    return acc
+
+
+def staggered_decode(groups, streams, rounds: int, next_inputs):
+    """The staggered schedule of `staggered` over chained decode rounds: after its verify a group
+    commits (the host waits for that group's stream only) and loads its next round's inputs, and
+    its next draft phase is enqueued before the following group's verify, so it runs while that
+    verify streams. Returns the accepted counts per group (the same as `lockstep_decode`)."""
+    ng = len(groups)
+    assert len(streams) == ng and ng >= 1
+    cur = torch.cuda.current_stream()
+    for s in streams:
+        s.wait_stream(cur)
+    first_done = [torch.cuda.Event() for _ in range(ng)]
+    acc = [[] for _ in groups]
+    verify_done = None
+
+    def draft(k):
+        g = k % ng
+        if k < ng and g > 0:
+            streams[g].wait_event(first_done[g - 1])
+        with torch.cuda.stream(streams[g]):
+            groups[g].draft_phase()
+            if k < ng:
+                first_done[g].record(streams[g])
+
+    total = rounds * ng
+    draft(0)
+    for k in range(total):
+        g, r = k % ng, k // ng
+        early = k + 1 < total and (k + 1) % ng != g
+        if early:
+            draft(k + 1)
+        s = streams[g]
+        if verify_done is not None:
+            s.wait_event(verify_done)
+        with torch.cuda.stream(s):
+            groups[g].verify_step()
+            verify_done = torch.cuda.Event()
+            verify_done.record(s)
+            acc[g].append(groups[g].commit())  # waits for this group's stream only
+            if r + 1 < rounds:
+                groups[g].set_round_inputs(*next_inputs(g, r + 1))
+        if k + 1 < total and not early:
+            draft(k + 1)
+    for s in streams:
+        cur.wait_stream(s)
+    return acc
+

@@ -120,3 +120,49 @@ def test_lockstep_order(monkeypatch):
     groups = [_Group(g, log) for g in range(3)]
     harness.lockstep(groups, rounds=2)
     assert log == [("D", 0), ("D", 1), ("D", 2), ("V", 0), ("V", 1), ("V", 2)] * 2
+
+
+def test_staggered_decode_order(monkeypatch):
+    """Chained decode rounds: per group D, V, C(ommit), I(nputs) in order, the next group's draft
+    phase enqueued before the verify it overlaps, commits on the group's own stream."""
+    log = []
+    cur = _Stream("cur", log)
+    fake, current = _fake_torch(log, cur)
+    monkeypatch.setattr(harness, "torch", fake)
+
+    class G:
+        def __init__(self, i):
+            self.i = i
+
+        def draft_phase(self):
+            log.append(("D", self.i, current[0].name))
+
+        def verify_step(self):
+            log.append(("V", self.i, current[0].name))
+
+        def commit(self):
+            log.append(("C", self.i, current[0].name))
+            return 0
+
+        def set_round_inputs(self, *a):
+            log.append(("I", self.i, current[0].name))
+
+    rounds = 3
+    acc = harness.staggered_decode([G(0), G(1)], [_Stream(0, log), _Stream(1, log)], rounds,
+                                   lambda g, r: ())
+    assert acc == [[0] * rounds, [0] * rounds]
+    ph = [e for e in log if e[0] in "DVCI"]
+    for kind, g, s in ph:
+        assert s == g
+    for g in range(2):
+        seq = [k for k, gg, _ in ph if gg == g]
+        assert seq == ["D", "V", "C", "I"] * (rounds - 1) + ["D", "V", "C"]
+    order = [(k, g) for k, g, _ in ph]
+    # group 1's first draft before group 0's first verify; each later draft before the other
+    # group's verify
+    assert order.index(("D", 1)) < order.index(("V", 0))
+    vs = [i for i, e in enumerate(order) if e[0] == "V"]
+    ds = [i for i, e in enumerate(order) if e[0] == "D"]
+    for j in range(1, len(vs)):  # the draft of slot j+1 precedes the verify of slot j
+        if j + 1 < len(ds):
+            assert ds[j + 1] < vs[j]
