@@ -763,3 +763,40 @@ def test_staggered_decode_matches_lockstep(gpu_lib):
         for k in ("out_d", "drafts", "out_v", "verified", "a", "next"):
             assert np.array_equal(ra[k], rb[k]), k
     assert B[0].n_q > w.n_q or B[1].n_q > w.n_q, "at least one flush"
+
+
+# ------------------------------------------------------------------------------------------
+# the pages' guarantee end to end: VeriCache decoding emits the full-KV greedy tokens
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("bits,R", [(4, 32), (2, 32), (4, 320)])
+def test_token_decoder_emits_full_kv_greedy(gpu_lib, bits, R):
+    """A one-layer decoder (head dim 128, 4/2 heads, random fp32 weights) decoded on the GPU with
+    draft rounds over the KIVI cache (R = 320: nothing quantised, an uncompressed drafter) emits
+    exactly the tokens of greedy decoding over the full cache computed by the oracle, up to a
+    first divergence that only a near-tie of the oracle's logits (top-2 gap < 1e-3) may cause."""
+    from kv_cache_compressed_amd.decode_loop import TokenDecoder
+    from oracle import loop as oloop
+
+    m = oloop.TinyModel(seed=5, vocab=384, dm=256, d=128, Hq=4, Hkv=2, max_pos=1024)
+    names = ("E", "P", "Wq", "Wk", "Wv", "Wo", "Wlm")
+    Wt = {k: getattr(m, k).astype(np.float32) for k in names}
+    for k in names:  # the oracle decodes with the same (fp32) weight values
+        setattr(m, k, Wt[k].astype(np.float64))
+    prompt = [int(t) for t in np.random.default_rng(1).integers(0, 384, 200)]
+    steps, x = 96, 8
+    dec = TokenDecoder(Wt, 4, 2, prompt, x=x, bits=bits, R=R, max_new=steps + 32)
+    got = dec.generate(steps)
+    ref = oloop.greedy(m, prompt, steps)
+    print(f"[bits {bits} R {R}] accepted per round {dec.rounds}; n_q {dec.n_q}", flush=True)
+    if got != ref:
+        t = next(i for i in range(steps) if got[i] != ref[i])
+        toks = prompt + ref[:t]
+        K, V = oloop.full_cache(m, toks)
+        z = m.next_logits(toks[-1], len(toks) - 1, K, V)
+        gap = float(oacc.top2_gap(z[None])[0])
+        assert gap < GAP, f"token {t} differs ({got[t]} vs {ref[t]}) with an oracle top-2 gap {gap}"
+        print(f"first divergence at token {t}: near-tie (gap {gap:.2e})", flush=True)
+    if R >= len(prompt) + steps:  # nothing quantised: the drafter reads what the verifier reads
+        assert sum(dec.rounds) >= x * (len(dec.rounds) - 1), dec.rounds
+    else:
+        assert dec.n_q > 32 * ((len(prompt) - 1 - R) // 32), "the loop must have flushed"
