@@ -34,6 +34,23 @@ SM_SCALE = float(np.float32(1.0 / np.sqrt(128.0)))
 D = 128
 
 
+def _dev(a, device) -> torch.Tensor:
+    if isinstance(a, torch.Tensor):
+        return a.to(device=device, dtype=torch.float32).contiguous()
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+
+
+def _head(weights, device) -> torch.Tensor:
+    """[Wlm Wo | Wlm] in fp32 (the product formed in float64 for host arrays, fp32 on the device
+    for device tensors)."""
+    Wo, Wlm = weights["Wo"], weights["Wlm"]
+    if isinstance(Wlm, torch.Tensor):
+        Wlm, Wo = _dev(Wlm, device), _dev(Wo, device)
+        return torch.cat([Wlm @ Wo, Wlm], dim=1).contiguous()
+    Wo, Wlm = np.asarray(Wo, np.float64), np.asarray(Wlm, np.float64)
+    return _dev(np.concatenate([Wlm @ Wo, Wlm], axis=1), device)
+
+
 class TokenDecoder:
     """weights: dict of float32 arrays E [V, dm], P [max_pos, dm], Wq [Hq*128, dm],
     Wk/Wv [Hkv*128, dm], Wo [dm, Hq*128], Wlm [V, dm]; dm a multiple of 128."""
@@ -41,13 +58,11 @@ class TokenDecoder:
     def __init__(self, weights, Hq: int, Hkv: int, prompt, x: int, bits: int = 4, R: int = 32,
                  max_new: int = 256, device: str = "cuda"):
         f32 = dict(dtype=torch.float32, device=device)
-        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
-        self.E, self.P = dev(weights["E"]), dev(weights["P"])
-        self.Wq, self.Wk, self.Wv = dev(weights["Wq"]), dev(weights["Wk"]), dev(weights["Wv"])
-        Wo = np.asarray(weights["Wo"], np.float64)
-        Wlm = np.asarray(weights["Wlm"], np.float64)
-        self.Wp = dev(np.concatenate([Wlm @ Wo, Wlm], axis=1))  # [V, Hq*128 + dm]
-        self.V, self.dm = Wlm.shape
+        self.E, self.P = _dev(weights["E"], device), _dev(weights["P"], device)
+        self.Wq, self.Wk = _dev(weights["Wq"], device), _dev(weights["Wk"], device)
+        self.Wv = _dev(weights["Wv"], device)
+        self.Wp = _head(weights, device)  # [V, Hq*128 + dm]
+        self.V, self.dm = self.E.shape
         assert self.dm % D == 0 and Hq % Hkv == 0
         self.Hq, self.Hkv, self.x, self.L, self.R = Hq, Hkv, x, x + 1, R
         self.Hx = Hq + self.dm // D  # heads of the projected input [o ; x]
@@ -162,3 +177,56 @@ class TokenDecoder:
             self.verify_step()
             out += self.commit()
         return out[:steps]
+
+
+class GreedyDecoder:
+    """The baseline without a drafter: greedy decoding over the full cache, one token per step
+    (the entry's projections, attention of one query row over the full cache, logits with the
+    greedy argmax, the entry's key/value appended to the full cache). Same model and calls as
+    TokenDecoder."""
+
+    def __init__(self, weights, Hq: int, Hkv: int, prompt, max_new: int = 256, device: str = "cuda"):
+        f32 = dict(dtype=torch.float32, device=device)
+        self.E, self.P = _dev(weights["E"], device), _dev(weights["P"], device)
+        self.Wq, self.Wk = _dev(weights["Wq"], device), _dev(weights["Wk"], device)
+        self.Wv = _dev(weights["Wv"], device)
+        self.Wp = _head(weights, device)
+        self.V, self.dm = self.E.shape
+        self.Hq, self.Hkv, self.Hx = Hq, Hkv, Hq + self.dm // D
+        prompt = [int(t) for t in prompt]
+        self.n = len(prompt) - 1
+        self.cap = (self.n + max_new + 63) // 32 * 32
+        n = self.n
+        self.k_store = torch.zeros((1, Hkv, self.cap, D), **f32)
+        self.v_store = torch.zeros_like(self.k_store)
+        X = self.E[torch.tensor(prompt[:n], device=device)] + self.P[:n]
+        self.k_store[0, :, :n] = (X @ self.Wk.T).view(n, Hkv, D).transpose(0, 1)
+        self.v_store[0, :, :n] = (X @ self.Wv.T).view(n, Hkv, D).transpose(0, 1)
+        self.q = torch.zeros((1, Hq, 1, D), **f32)
+        self.k1 = torch.zeros((1, Hkv, 1, D), **f32)
+        self.v1 = torch.zeros_like(self.k1)
+        self.o = torch.zeros((1, self.Hx, 1, D), **f32)
+        self.lse = torch.zeros((1, Hq, 1), **f32)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.toks = torch.zeros((max_new + 1,), **i32)
+        self.toks[0] = prompt[-1]
+        self.ws = vc.Workspace(device)
+        self.ws_proj = torch.zeros((vc.vc_project_workspace(1, 1, self.V) + 3) // 4, **i32)
+
+    def generate(self, steps: int):
+        for i in range(steps):
+            x = self.E[self.toks[i:i + 1].long()][0] + self.P[self.n]
+            self.q[0, :, 0] = (self.Wq @ x).view(self.Hq, D)
+            self.k1[0, :, 0] = (self.Wk @ x).view(self.Hkv, D)
+            self.v1[0, :, 0] = (self.Wv @ x).view(self.Hkv, D)
+            nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, 1, self.n, False, 0, vc.VC_F32)
+            vc.vc_verify_attn(self.q, self.k1, self.v1, self.k_store, self.v_store, self.n, self.o,
+                              self.lse, self.ws.get(nb), SM_SCALE, past_stride=self.cap)
+            self.o[0, self.Hq:, 0] = x.view(-1, D)
+            vc.vc_project_logits(self.Wp, self.o, argmax=self.toks[i + 1:i + 2], argmax_b_stride=1,
+                                 ws=self.ws_proj)
+            self.k_store[:, :, self.n] = self.k1[:, :, 0]
+            self.v_store[:, :, self.n] = self.v1[:, :, 0]
+            self.n += 1
+        return [int(t) for t in self.toks[1:steps + 1].tolist()]
+

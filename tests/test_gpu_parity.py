@@ -773,8 +773,9 @@ def test_token_decoder_emits_full_kv_greedy(gpu_lib, bits, R):
     """A one-layer decoder (head dim 128, 4/2 heads, random fp32 weights) decoded on the GPU with
     draft rounds over the KIVI cache (R = 320: nothing quantised, an uncompressed drafter) emits
     exactly the tokens of greedy decoding over the full cache computed by the oracle, up to a
-    first divergence that only a near-tie of the oracle's logits (top-2 gap < 1e-3) may cause."""
-    from kv_cache_compressed_amd.decode_loop import TokenDecoder
+    first divergence that only a near-tie of the oracle's logits (top-2 gap < 1e-3) may cause; so
+    does the GPU's own drafter-less greedy decode through the same calls."""
+    from kv_cache_compressed_amd.decode_loop import GreedyDecoder, TokenDecoder
     from oracle import loop as oloop
 
     m = oloop.TinyModel(seed=5, vocab=384, dm=256, d=128, Hq=4, Hkv=2, max_pos=1024)
@@ -787,15 +788,18 @@ def test_token_decoder_emits_full_kv_greedy(gpu_lib, bits, R):
     dec = TokenDecoder(Wt, 4, 2, prompt, x=x, bits=bits, R=R, max_new=steps + 32)
     got = dec.generate(steps)
     ref = oloop.greedy(m, prompt, steps)
+    # the GPU's own greedy decode over the full cache (one query row per token) as well
+    greedy_gpu = GreedyDecoder(Wt, 4, 2, prompt, max_new=steps + 8).generate(steps)
     print(f"[bits {bits} R {R}] accepted per round {dec.rounds}; n_q {dec.n_q}", flush=True)
-    if got != ref:
-        t = next(i for i in range(steps) if got[i] != ref[i])
-        toks = prompt + ref[:t]
-        K, V = oloop.full_cache(m, toks)
-        z = m.next_logits(toks[-1], len(toks) - 1, K, V)
-        gap = float(oacc.top2_gap(z[None])[0])
-        assert gap < GAP, f"token {t} differs ({got[t]} vs {ref[t]}) with an oracle top-2 gap {gap}"
-        print(f"first divergence at token {t}: near-tie (gap {gap:.2e})", flush=True)
+    for what, seq in (("VeriCache", got), ("GPU greedy", greedy_gpu)):
+        if seq != ref:
+            t = next(i for i in range(steps) if seq[i] != ref[i])
+            toks = prompt + ref[:t]
+            K, V = oloop.full_cache(m, toks)
+            z = m.next_logits(toks[-1], len(toks) - 1, K, V)
+            gap = float(oacc.top2_gap(z[None])[0])
+            assert gap < GAP, f"{what}: token {t} differs ({seq[t]} vs {ref[t]}), oracle top-2 gap {gap}"
+            print(f"{what}: first divergence at token {t}: near-tie (gap {gap:.2e})", flush=True)
     if R >= len(prompt) + steps:  # nothing quantised: the drafter reads what the verifier reads
         assert sum(dec.rounds) >= x * (len(dec.rounds) - 1), dec.rounds
     else:
