@@ -21,7 +21,9 @@ over the full cache, the accept step compares, and the commit keeps entries 0..a
 and the residual, flushing whole groups into the codes.
 
 Every attention, quantisation, residual append, logits and accept step is a libvc call; the
-embeddings and the q/k/v projections are plain fp32 GEMMs through PyTorch.
+embeddings and the q/k/v projections are plain fp32 GEMMs through PyTorch. The cache holds fp32 or
+bf16 keys/values (q, k, v rounded to bf16 with ties to even), in HBM or, for bf16, in pinned host
+memory that every verify streams in chunks (the pages' long-context setting).
 """
 from __future__ import annotations
 
@@ -51,40 +53,99 @@ def _head(weights, device) -> torch.Tensor:
     return _dev(np.concatenate([Wlm @ Wo, Wlm], axis=1), device)
 
 
-class TokenDecoder:
-    """weights: dict of float32 arrays E [V, dm], P [max_pos, dm], Wq [Hq*128, dm],
-    Wk/Wv [Hkv*128, dm], Wo [dm, Hq*128], Wlm [V, dm]; dm a multiple of 128."""
+class _Model:
+    """Weights on the device and the per-position computations both decoders share."""
 
-    def __init__(self, weights, Hq: int, Hkv: int, prompt, x: int, bits: int = 4, R: int = 32,
-                 max_new: int = 256, device: str = "cuda"):
-        f32 = dict(dtype=torch.float32, device=device)
+    def __init__(self, weights, Hq: int, Hkv: int, kv_dtype: str, device: str):
         self.E, self.P = _dev(weights["E"], device), _dev(weights["P"], device)
         self.Wq, self.Wk = _dev(weights["Wq"], device), _dev(weights["Wk"], device)
         self.Wv = _dev(weights["Wv"], device)
         self.Wp = _head(weights, device)  # [V, Hq*128 + dm]
         self.V, self.dm = self.E.shape
         assert self.dm % D == 0 and Hq % Hkv == 0
+        self.Hq, self.Hkv, self.Hx = Hq, Hkv, Hq + self.dm // D
+        assert kv_dtype in ("f32", "bf16")
+        self.tdt = torch.float32 if kv_dtype == "f32" else torch.bfloat16
+        self.vdt = vc.VC_F32 if kv_dtype == "f32" else vc.VC_BF16
+        self.device = device
+
+    def embed(self, tok1, pos: int):
+        """x of the token in the 1-element device tensor `tok1` at position `pos` (fp32)."""
+        return self.E[tok1.long()][0] + self.P[pos]
+
+    def prefill(self, prompt, n: int, chunk: int, sink):
+        """Keys/values of positions 0..n-1 in chunks: sink(t0, t1, K, V) with K, V [1, Hkv, m, 128]
+        in the cache dtype (device tensors)."""
+        ids = torch.tensor(prompt[:n], device=self.device)
+        for t0 in range(0, n, chunk):
+            t1 = min(n, t0 + chunk)
+            X = self.E[ids[t0:t1]] + self.P[t0:t1]
+            m = t1 - t0
+            K = (X @ self.Wk.T).view(m, self.Hkv, D).transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
+            V = (X @ self.Wv.T).view(m, self.Hkv, D).transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
+            sink(t0, t1, K, V)
+
+
+class _Store:
+    """The full cache [1, Hkv, cap, 128] in the cache dtype, in HBM or in pinned host memory."""
+
+    def __init__(self, Hkv: int, cap: int, dtype, host: bool, device: str):
+        self.host, self.cap, self.device = host, cap, device
+        if host:
+            self.k = torch.empty((1, Hkv, cap, D), dtype=dtype, pin_memory=True)
+            self.v = torch.empty_like(self.k, pin_memory=True)
+        else:
+            self.k = torch.zeros((1, Hkv, cap, D), dtype=dtype, device=device)
+            self.v = torch.zeros_like(self.k)
+
+    def write(self, t0: int, K, V):
+        """Rows t0 .. t0+m-1 from device tensors [1, Hkv, m, 128]."""
+        m = K.shape[2]
+        self.k[:, :, t0:t0 + m].copy_(K)
+        self.v[:, :, t0:t0 + m].copy_(V)
+
+    def device_rows(self, t0: int, t1: int):
+        """(K, V, source stride) of rows t0..t1-1 on the device, for the quantiser (staged when
+        the cache is in host memory)."""
+        if self.host:
+            return (self.k[:, :, t0:t1].to(self.device), self.v[:, :, t0:t1].to(self.device),
+                    (t1 - t0) * D)
+        return self.k[:, :, t0:], self.v[:, :, t0:], self.cap * D
+
+
+class TokenDecoder:
+    """weights: dict of fp32 arrays or device tensors E [V, dm], P [max_pos, dm], Wq [Hq*128, dm],
+    Wk/Wv [Hkv*128, dm], Wo [dm, Hq*128], Wlm [V, dm]; dm a multiple of 128. kv_dtype "f32" or
+    "bf16"; host_past (bf16 only): the full cache in pinned host memory, streamed by every verify in
+    chunks of chunk_tokens on copy_stream."""
+
+    def __init__(self, weights, Hq: int, Hkv: int, prompt, x: int, bits: int = 4, R: int = 32,
+                 max_new: int = 256, kv_dtype: str = "f32", host_past: bool = False,
+                 chunk_tokens: int = 65536, copy_stream=None, device: str = "cuda"):
+        mdl = self.m = _Model(weights, Hq, Hkv, kv_dtype, device)
+        assert not host_past or kv_dtype == "bf16", "a host-streamed cache is bf16"
+        f32 = dict(dtype=torch.float32, device=device)
+        tdt = mdl.tdt
         self.Hq, self.Hkv, self.x, self.L, self.R = Hq, Hkv, x, x + 1, R
-        self.Hx = Hq + self.dm // D  # heads of the projected input [o ; x]
+        self.host, self.chunk = host_past, chunk_tokens
+        self.copy_stream = (copy_stream or torch.cuda.Stream()) if host_past else None
         prompt = [int(t) for t in prompt]
         assert len(prompt) >= 2
         self.n = len(prompt) - 1  # cached positions: every prompt token but the last
-        self.cap = (self.n + max_new + 2 * self.L + 63) // 32 * 32
-        assert self.cap <= self.P.shape[0], "position table too short"
         L = self.L
-        # full cache, round block, outputs
-        self.k_store = torch.zeros((1, Hkv, self.cap, D), **f32)
-        self.v_store = torch.zeros_like(self.k_store)
-        self.k_blk = torch.zeros((1, Hkv, L, D), **f32)
+        self.cap = (self.n + max_new + 2 * L + 63) // 32 * 32
+        assert self.cap <= mdl.P.shape[0], "position table too short"
+        self.store = _Store(Hkv, self.cap, tdt, host_past, device)
+        self.k_blk = torch.zeros((1, Hkv, L, D), dtype=tdt, device=device)
         self.v_blk = torch.zeros_like(self.k_blk)
-        self.q_verify = torch.zeros((1, Hq, L, D), **f32)
-        self.q_draft = torch.zeros((L, 1, Hq, D), **f32)
-        self.xs = torch.zeros((L, self.dm), **f32)
-        self.od = torch.zeros((1, self.Hx, D), **f32)       # draft step [o ; x]
+        self.q_verify = torch.zeros((1, Hq, L, D), dtype=tdt, device=device)
+        self.q_draft = torch.zeros((L, 1, Hq, D), dtype=tdt, device=device)
+        self.xs = torch.zeros((L, mdl.dm), **f32)
+        self.od = torch.zeros((1, mdl.Hx, D), **f32)       # draft step [o ; x]
         self.lse_d = torch.zeros((1, Hq), **f32)
-        self.ov = torch.zeros((1, self.Hx, L, D), **f32)    # verify rows [o ; x]
+        self.ov = torch.zeros((1, mdl.Hx, L, D), **f32)    # verify rows [o ; x]
         self.lse_v = torch.zeros((1, Hq, L), **f32)
-        self.logits_v = torch.zeros((1, L, self.V), **f32)
+        self.logits_v = torch.zeros((1, L, mdl.V), **f32)
         i32 = dict(dtype=torch.int32, device=device)
         self.tok = torch.zeros((L + 1,), **i32)             # block tokens (entry L: spare)
         self.accept_len = torch.zeros((1,), **i32)
@@ -92,34 +153,38 @@ class TokenDecoder:
         self.argmax_v = torch.zeros((1, L), **i32)
         self.ws_draft = vc.Workspace(device)
         self.ws_verify = vc.Workspace(device)
-        self.ws_proj = torch.zeros((vc.vc_project_workspace(1, 1, self.V) + 3) // 4, **i32)
-        # prefill: keys/values of positions 0..n-1, the quantised prefix and the residual
+        self.ws_proj = torch.zeros((vc.vc_project_workspace(1, 1, mdl.V) + 3) // 4, **i32)
+        # prefill: keys/values of positions 0..n-1 into the full cache, the quantised prefix into
+        # the codes (chunk by chunk), the rest into the residual
         n = self.n
-        X = self.E[torch.tensor(prompt[:n], device=device)] + self.P[:n]
-        self.k_store[0, :, :n] = (X @ self.Wk.T).view(n, Hkv, D).transpose(0, 1)
-        self.v_store[0, :, :n] = (X @ self.Wv.T).view(n, Hkv, D).transpose(0, 1)
         self.n_q = 32 * (max(0, n - R) // 32)
         res_cap = (R + 32 + L + 31) // 32 * 32
-        self.cache = vc.KiviCache(1, Hkv, (self.cap + 31) // 32 * 32, bits, vc.VC_F32, vc.VC_F32,
-                                  res_cap, device)
-        if self.n_q:
-            vc.vc_quantize_kv(self.cache, self.k_store, self.v_store, 0, self.n_q,
-                              src_bh_stride=self.cap * D)
+        meta = vc.VC_F32 if kv_dtype == "f32" else vc.VC_F16
+        self.cache = vc.KiviCache(1, Hkv, self.cap, bits, meta, meta, res_cap, device)
+
+        def sink(t0, t1, K, V):
+            self.store.write(t0, K, V)
+            q1 = min(t1, self.n_q)
+            if t0 < q1:
+                vc.vc_quantize_kv(self.cache, K, V, t0, q1 - t0, src_bh_stride=(t1 - t0) * D)
+
+        mdl.prefill(prompt, n, max(32, chunk_tokens // 32 * 32), sink)
         if n > self.n_q:
-            vc.vc_kivi_append(self.cache, self.k_store[:, :, self.n_q:], self.v_store[:, :, self.n_q:],
-                              self.n_q, n - self.n_q, src_bh_stride=self.cap * D)
+            Kr, Vr, stride = self.store.device_rows(self.n_q, n)
+            vc.vc_kivi_append(self.cache, Kr, Vr, self.n_q, n - self.n_q, src_bh_stride=stride)
         self.tok[0] = prompt[-1]
         self.rounds = []  # accepted count per round
 
     # ---- one block entry: embedding and projections -----------------------------------------
     def _entry(self, j: int):
-        x = self.E[self.tok[j:j + 1].long()][0] + self.P[self.n + j]
+        mdl = self.m
+        x = mdl.embed(self.tok[j:j + 1], self.n + j)
         self.xs[j] = x
-        q = self.Wq @ x
-        self.q_verify[0, :, j] = q.view(self.Hq, D)
-        self.q_draft[j, 0] = q.view(self.Hq, D)
-        self.k_blk[0, :, j] = (self.Wk @ x).view(self.Hkv, D)
-        self.v_blk[0, :, j] = (self.Wv @ x).view(self.Hkv, D)
+        q = (mdl.Wq @ x).view(self.Hq, D)
+        self.q_verify[0, :, j] = q
+        self.q_draft[j, 0] = q
+        self.k_blk[0, :, j] = (mdl.Wk @ x).view(self.Hkv, D)
+        self.v_blk[0, :, j] = (mdl.Wv @ x).view(self.Hkv, D)
 
     def draft_step(self, j: int):
         """Draft step j: attention over the compressed cache (storing entry j's key/value into the
@@ -131,18 +196,21 @@ class TokenDecoder:
                                self.ws_draft.get(nb), SM_SCALE, k_new=self.k_blk[:, :, j],
                                v_new=self.v_blk[:, :, j])
         self.od[0, self.Hq:] = self.xs[j].view(-1, D)
-        vc.vc_project_logits(self.Wp, self.od, argmax=self.tok[j + 1:j + 2], argmax_b_stride=1,
+        vc.vc_project_logits(self.m.Wp, self.od, argmax=self.tok[j + 1:j + 2], argmax_b_stride=1,
                              ws=self.ws_proj)
 
     def verify_step(self):
         """Entry x's projections, verify attention over the full cache, logits of every row and
         the greedy accept."""
         self._entry(self.x)
-        nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, self.n, False, 0, vc.VC_F32)
-        vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.k_store, self.v_store, self.n,
-                          self.ov, self.lse_v, self.ws_verify.get(nb), SM_SCALE, past_stride=self.cap)
+        nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, self.n, self.host, self.chunk,
+                                    self.m.vdt)
+        vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.store.k, self.store.v, self.n,
+                          self.ov, self.lse_v, self.ws_verify.get(nb), SM_SCALE,
+                          past_stride=self.cap, past_on_host=self.host, chunk_tokens=self.chunk,
+                          copy_stream=self.copy_stream)
         self.ov[0, self.Hq:] = self.xs.view(self.L, -1, D).transpose(0, 1)
-        vc.vc_project_logits(self.Wp, self.ov, logits=self.logits_v)
+        vc.vc_project_logits(self.m.Wp, self.ov, logits=self.logits_v)
         vc.vc_accept(self.logits_v, self.tok[1:self.L].view(1, self.x), self.accept_len,
                      self.next_tok, self.argmax_v)
 
@@ -154,15 +222,14 @@ class TokenDecoder:
         emitted = [int(t) for t in self.tok[1:a + 1].tolist()] + [int(self.next_tok[0].item())]
         n0, n1 = self.n, self.n + a + 1
         assert n1 + self.L <= self.cap, "cache capacity exhausted (raise max_new)"
-        self.k_store[:, :, n0:n1] = self.k_blk[:, :, :a + 1]
-        self.v_store[:, :, n0:n1] = self.v_blk[:, :, :a + 1]
+        self.store.write(n0, self.k_blk[:, :, :a + 1], self.v_blk[:, :, :a + 1])
         if a == self.x:
             vc.vc_kivi_append(self.cache, self.k_blk[:, :, self.x], self.v_blk[:, :, self.x],
                               n0 + self.x, 1, src_bh_stride=self.L * D)
         self.n = n1
         while self.n - self.n_q >= self.R + 32:
-            vc.vc_quantize_kv(self.cache, self.k_store[:, :, self.n_q:], self.v_store[:, :, self.n_q:],
-                              self.n_q, 32, src_bh_stride=self.cap * D)
+            Kg, Vg, stride = self.store.device_rows(self.n_q, self.n_q + 32)
+            vc.vc_quantize_kv(self.cache, Kg, Vg, self.n_q, 32, src_bh_stride=stride)
             self.n_q += 32
         self.tok[0:1] = self.next_tok
         self.rounds.append(a)
@@ -182,51 +249,51 @@ class TokenDecoder:
 class GreedyDecoder:
     """The baseline without a drafter: greedy decoding over the full cache, one token per step
     (the entry's projections, attention of one query row over the full cache, logits with the
-    greedy argmax, the entry's key/value appended to the full cache). Same model and calls as
-    TokenDecoder."""
+    greedy argmax, the entry's key/value appended to the full cache). Same model, cache placement
+    and calls as TokenDecoder."""
 
-    def __init__(self, weights, Hq: int, Hkv: int, prompt, max_new: int = 256, device: str = "cuda"):
+    def __init__(self, weights, Hq: int, Hkv: int, prompt, max_new: int = 256, kv_dtype: str = "f32",
+                 host_past: bool = False, chunk_tokens: int = 65536, copy_stream=None,
+                 device: str = "cuda"):
+        mdl = self.m = _Model(weights, Hq, Hkv, kv_dtype, device)
+        assert not host_past or kv_dtype == "bf16", "a host-streamed cache is bf16"
         f32 = dict(dtype=torch.float32, device=device)
-        self.E, self.P = _dev(weights["E"], device), _dev(weights["P"], device)
-        self.Wq, self.Wk = _dev(weights["Wq"], device), _dev(weights["Wk"], device)
-        self.Wv = _dev(weights["Wv"], device)
-        self.Wp = _head(weights, device)
-        self.V, self.dm = self.E.shape
-        self.Hq, self.Hkv, self.Hx = Hq, Hkv, Hq + self.dm // D
+        tdt = mdl.tdt
+        self.Hq, self.Hkv = Hq, Hkv
+        self.host, self.chunk = host_past, chunk_tokens
+        self.copy_stream = (copy_stream or torch.cuda.Stream()) if host_past else None
         prompt = [int(t) for t in prompt]
         self.n = len(prompt) - 1
         self.cap = (self.n + max_new + 63) // 32 * 32
-        n = self.n
-        self.k_store = torch.zeros((1, Hkv, self.cap, D), **f32)
-        self.v_store = torch.zeros_like(self.k_store)
-        X = self.E[torch.tensor(prompt[:n], device=device)] + self.P[:n]
-        self.k_store[0, :, :n] = (X @ self.Wk.T).view(n, Hkv, D).transpose(0, 1)
-        self.v_store[0, :, :n] = (X @ self.Wv.T).view(n, Hkv, D).transpose(0, 1)
-        self.q = torch.zeros((1, Hq, 1, D), **f32)
-        self.k1 = torch.zeros((1, Hkv, 1, D), **f32)
+        self.store = _Store(Hkv, self.cap, tdt, host_past, device)
+        mdl.prefill(prompt, self.n, max(32, chunk_tokens // 32 * 32),
+                    lambda t0, t1, K, V: self.store.write(t0, K, V))
+        self.q = torch.zeros((1, Hq, 1, D), dtype=tdt, device=device)
+        self.k1 = torch.zeros((1, Hkv, 1, D), dtype=tdt, device=device)
         self.v1 = torch.zeros_like(self.k1)
-        self.o = torch.zeros((1, self.Hx, 1, D), **f32)
+        self.o = torch.zeros((1, mdl.Hx, 1, D), **f32)
         self.lse = torch.zeros((1, Hq, 1), **f32)
         i32 = dict(dtype=torch.int32, device=device)
         self.toks = torch.zeros((max_new + 1,), **i32)
         self.toks[0] = prompt[-1]
         self.ws = vc.Workspace(device)
-        self.ws_proj = torch.zeros((vc.vc_project_workspace(1, 1, self.V) + 3) // 4, **i32)
+        self.ws_proj = torch.zeros((vc.vc_project_workspace(1, 1, mdl.V) + 3) // 4, **i32)
 
     def generate(self, steps: int):
+        mdl = self.m
         for i in range(steps):
-            x = self.E[self.toks[i:i + 1].long()][0] + self.P[self.n]
-            self.q[0, :, 0] = (self.Wq @ x).view(self.Hq, D)
-            self.k1[0, :, 0] = (self.Wk @ x).view(self.Hkv, D)
-            self.v1[0, :, 0] = (self.Wv @ x).view(self.Hkv, D)
-            nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, 1, self.n, False, 0, vc.VC_F32)
-            vc.vc_verify_attn(self.q, self.k1, self.v1, self.k_store, self.v_store, self.n, self.o,
-                              self.lse, self.ws.get(nb), SM_SCALE, past_stride=self.cap)
+            x = mdl.embed(self.toks[i:i + 1], self.n)
+            self.q[0, :, 0] = (mdl.Wq @ x).view(self.Hq, D)
+            self.k1[0, :, 0] = (mdl.Wk @ x).view(self.Hkv, D)
+            self.v1[0, :, 0] = (mdl.Wv @ x).view(self.Hkv, D)
+            nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, 1, self.n, self.host, self.chunk, mdl.vdt)
+            vc.vc_verify_attn(self.q, self.k1, self.v1, self.store.k, self.store.v, self.n, self.o,
+                              self.lse, self.ws.get(nb), SM_SCALE, past_stride=self.cap,
+                              past_on_host=self.host, chunk_tokens=self.chunk,
+                              copy_stream=self.copy_stream)
             self.o[0, self.Hq:, 0] = x.view(-1, D)
-            vc.vc_project_logits(self.Wp, self.o, argmax=self.toks[i + 1:i + 2], argmax_b_stride=1,
+            vc.vc_project_logits(mdl.Wp, self.o, argmax=self.toks[i + 1:i + 2], argmax_b_stride=1,
                                  ws=self.ws_proj)
-            self.k_store[:, :, self.n] = self.k1[:, :, 0]
-            self.v_store[:, :, self.n] = self.v1[:, :, 0]
+            self.store.write(self.n, self.k1, self.v1)
             self.n += 1
         return [int(t) for t in self.toks[1:steps + 1].tolist()]
-

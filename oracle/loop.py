@@ -22,8 +22,19 @@ from .attention import decode
 from .quant import quantize_groups
 
 
+def bf16(a):
+    """float32 values rounded to the nearest bfloat16 (ties to even), as float64."""
+    u = np.asarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 class TinyModel:
-    def __init__(self, seed=0, vocab=11, dm=16, d=8, Hq=4, Hkv=2, max_pos=128):
+    """kv_bf16: queries, keys and values are stored at bfloat16 precision (rounded from their fp32
+    values), as a cache kept in bf16 holds them."""
+
+    def __init__(self, seed=0, vocab=11, dm=16, d=8, Hq=4, Hkv=2, max_pos=128, kv_bf16=False):
+        self.kv_bf16 = kv_bf16
         g = np.random.default_rng(seed)
         self.V, self.dm, self.d, self.Hq, self.Hkv = vocab, dm, d, Hq, Hkv
         self.E = g.standard_normal((vocab, dm))
@@ -38,14 +49,18 @@ class TinyModel:
     def _x(self, tok, pos):
         return self.E[tok] + self.P[pos]
 
+    def _r(self, a):
+        return bf16(a) if self.kv_bf16 else a
+
     def kv(self, tok, pos):
         x = self._x(tok, pos)
-        return (self.Wk @ x).reshape(self.Hkv, self.d), (self.Wv @ x).reshape(self.Hkv, self.d)
+        return (self._r(self.Wk @ x).reshape(self.Hkv, self.d),
+                self._r(self.Wv @ x).reshape(self.Hkv, self.d))
 
     def next_logits(self, tok, pos, K, V):
         """Logits after token `tok` at `pos`, attending over K/V [Hkv][S, d] (S includes pos)."""
         x = self._x(tok, pos)
-        q = (self.Wq @ x).reshape(self.Hq, self.d)
+        q = self._r(self.Wq @ x).reshape(self.Hq, self.d)
         G = self.Hq // self.Hkv
         o = np.concatenate([decode(q[h], K[h // G], V[h // G], self.scale)[0]
                             for h in range(self.Hq)])

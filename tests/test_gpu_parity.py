@@ -768,29 +768,35 @@ def test_staggered_decode_matches_lockstep(gpu_lib):
 # ------------------------------------------------------------------------------------------
 # the pages' guarantee end to end: VeriCache decoding emits the full-KV greedy tokens
 # ------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("bits,R", [(4, 32), (2, 32), (4, 320)])
-def test_token_decoder_emits_full_kv_greedy(gpu_lib, bits, R):
-    """A one-layer decoder (head dim 128, 4/2 heads, random fp32 weights) decoded on the GPU with
-    draft rounds over the KIVI cache (R = 320: nothing quantised, an uncompressed drafter) emits
+@pytest.mark.parametrize("bits,R,kv,host", [(4, 32, "f32", False), (2, 32, "f32", False),
+                                             (4, 320, "f32", False), (4, 32, "bf16", False),
+                                             (2, 32, "bf16", True)])
+def test_token_decoder_emits_full_kv_greedy(gpu_lib, bits, R, kv, host):
+    """A one-layer decoder (head dim 128, 4/2 heads, random fp32 weights; the cache fp32, or bf16 in
+    HBM or in pinned host memory streamed by every verify) decoded on the GPU with draft rounds
+    over the KIVI cache (R = 320: nothing quantised, an uncompressed drafter) emits
     exactly the tokens of greedy decoding over the full cache computed by the oracle, up to a
     first divergence that only a near-tie of the oracle's logits (top-2 gap < 1e-3) may cause; so
     does the GPU's own drafter-less greedy decode through the same calls."""
     from kv_cache_compressed_amd.decode_loop import GreedyDecoder, TokenDecoder
     from oracle import loop as oloop
 
-    m = oloop.TinyModel(seed=5, vocab=384, dm=256, d=128, Hq=4, Hkv=2, max_pos=1024)
+    m = oloop.TinyModel(seed=5, vocab=384, dm=256, d=128, Hq=4, Hkv=2, max_pos=1024,
+                        kv_bf16=kv == "bf16")
     names = ("E", "P", "Wq", "Wk", "Wv", "Wo", "Wlm")
     Wt = {k: getattr(m, k).astype(np.float32) for k in names}
     for k in names:  # the oracle decodes with the same (fp32) weight values
         setattr(m, k, Wt[k].astype(np.float64))
     prompt = [int(t) for t in np.random.default_rng(1).integers(0, 384, 200)]
     steps, x = 96, 8
-    dec = TokenDecoder(Wt, 4, 2, prompt, x=x, bits=bits, R=R, max_new=steps + 32)
+    opts = dict(kv_dtype=kv, host_past=host, chunk_tokens=64)  # host: several streamed chunks
+    dec = TokenDecoder(Wt, 4, 2, prompt, x=x, bits=bits, R=R, max_new=steps + 32, **opts)
     got = dec.generate(steps)
     ref = oloop.greedy(m, prompt, steps)
     # the GPU's own greedy decode over the full cache (one query row per token) as well
-    greedy_gpu = GreedyDecoder(Wt, 4, 2, prompt, max_new=steps + 8).generate(steps)
-    print(f"[bits {bits} R {R}] accepted per round {dec.rounds}; n_q {dec.n_q}", flush=True)
+    greedy_gpu = GreedyDecoder(Wt, 4, 2, prompt, max_new=steps + 8, **opts).generate(steps)
+    print(f"[bits {bits} R {R} {kv}{' host' if host else ''}] accepted per round {dec.rounds}; "
+          f"n_q {dec.n_q}", flush=True)
     for what, seq in (("VeriCache", got), ("GPU greedy", greedy_gpu)):
         if seq != ref:
             t = next(i for i in range(steps) if seq[i] != ref[i])

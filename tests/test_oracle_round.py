@@ -46,3 +46,25 @@ def test_compressed_round_is_well_formed():
     res = rnd.run(0)
     assert 0 <= res["a"] <= w.x and len(res["emitted"]) == res["a"] + 1
     assert np.all(np.isfinite(res["draft_logits"])) and np.all(res["draft_gap"] >= 0)
+
+
+def test_bf16_rounding_of_the_tiny_model():
+    """The oracle's bf16 rounding (8 significant bits): exact bf16 values are kept, halfway cases go
+    to the neighbour with the even last bit, others to the nearest."""
+    from oracle.loop import bf16
+    cases = [
+        (1.0, 1.0),                          # exact
+        (1.0 + 2 ** -8, 1.0),                # halfway between 1 and 1 + 2^-7: 1 is even
+        (1.0 + 3 * 2 ** -8, 1.0 + 2 ** -6),  # halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even)
+        (1.0 + 2 ** -9, 1.0),                # below halfway
+        (1.0 + 2 ** -8 + 2 ** -12, 1.0 + 2 ** -7),  # above halfway
+        (-2.5, -2.5),
+        (3.0 + 2 ** -7, 3.0),                # spacing 2^-6 in [2, 4): halfway, 3 is even
+        (3.0 + 3 * 2 ** -7, 3.0 + 2 ** -5),  # halfway between 3 + 2^-6 (odd) and 3 + 2^-5 (even)
+    ]
+    x = np.array([c[0] for c in cases], np.float32)
+    assert bf16(x).tolist() == [c[1] for c in cases]
+    g = np.random.default_rng(0).standard_normal(1000).astype(np.float32)
+    r = bf16(g)
+    assert np.all(np.abs(r - g) <= np.abs(g) * 2.0 ** -8)                 # within half a bf16 ulp
+    assert np.all((r.astype(np.float32).view(np.uint32) & 0xFFFF) == 0)   # representable in bf16
