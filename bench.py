@@ -241,6 +241,52 @@ def _decode_pair(torch, harness, synth, w, seed: int, rounds: int) -> dict:
     return out
 
 
+def _e2e_decode(torch, seed: int, context: int, tokens: int) -> dict:
+    """Token-level decoding of one request on a one-layer decoder (Llama-3.1-8B-shaped attention:
+    32 query / 8 kv heads, d 128; d_model 256, vocab 2048, seeded random fp32 weights at the scales
+    of the oracle's model) with a `context`-token prompt whose bf16 cache sits in pinned host
+    memory and is streamed by every verify, in 64K-token chunks: VeriCache (4-bit KIVI drafter in
+    HBM, draft length 30) against greedy decoding over the full cache (one streamed pass per
+    token)."""
+    from kv_cache_compressed_amd.decode_loop import GreedyDecoder, TokenDecoder
+
+    dev, V, dm, Hq, Hkv = "cuda", 2048, 256, 32, 8
+    g = torch.Generator(device=dev).manual_seed(seed)
+    rn = lambda *shape: torch.randn(*shape, generator=g, device=dev)
+    W = {"E": rn(V, dm), "P": 0.5 * rn(context + tokens + 256, dm),
+         "Wq": rn(Hq * 128, dm) / dm ** 0.5, "Wk": rn(Hkv * 128, dm) / dm ** 0.5,
+         "Wv": rn(Hkv * 128, dm) / dm ** 0.5, "Wo": rn(dm, Hq * 128) / (Hq * 128) ** 0.5,
+         "Wlm": 3.0 * rn(V, dm) / dm ** 0.5}
+    prompt = torch.randint(0, V, (context,), generator=g, device=dev).tolist()
+    opts = dict(kv_dtype="bf16", host_past=True, chunk_tokens=65536)
+    out = {"context": context, "tokens": tokens, "model": "one layer, d_model 256, 32/8 heads, d 128, "
+           "vocab 2048, bf16 cache in pinned host memory, 64K-token chunks"}
+    seqs = {}
+    for name in ("vericache", "greedy"):
+        t0 = time.perf_counter()
+        if name == "vericache":
+            dec = TokenDecoder(W, Hq, Hkv, prompt, x=30, bits=4, R=128, max_new=tokens + 64, **opts)
+        else:
+            dec = GreedyDecoder(W, Hq, Hkv, prompt, max_new=tokens + 8, **opts)
+        torch.cuda.synchronize()
+        t_prefill = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        seqs[name] = dec.generate(tokens)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        # every token the rounds produced (the last round may run past `tokens`)
+        emitted = sum(a + 1 for a in dec.rounds) if name == "vericache" else tokens
+        out[name] = {"tok_s": round(emitted / el, 2), "emitted": emitted,
+                     "ms_per_token": round(el / emitted * 1e3, 3), "prefill_s": round(t_prefill, 2)}
+        if name == "vericache":
+            out[name]["accepted_per_round"] = dec.rounds
+        del dec
+    out["speedup"] = round(out["vericache"]["tok_s"] / out["greedy"]["tok_s"], 3)
+    a, b = seqs["vericache"], seqs["greedy"]
+    out["first_divergence"] = next((i for i in range(tokens) if a[i] != b[i]), None)  # of `tokens`
+    return out
+
+
 def _back_to_back_us(torch, launch, n: int) -> float:
     """Mean duration of n launches enqueued back to back between two events (microseconds)."""
     for i in range(3):
@@ -281,6 +327,10 @@ def main():
     ap.add_argument("--decode-rounds", type=int, default=0,
                     help="single-request KIVI workloads (c1, c4): also run this many chained decode "
                          "rounds (commit + residual flush between rounds) and report them")
+    ap.add_argument("--e2e-context", type=int, default=0,
+                    help="also decode one request token by token on a one-layer decoder with a "
+                         "host-streamed bf16 cache of this many tokens: VeriCache vs greedy")
+    ap.add_argument("--e2e-tokens", type=int, default=64)
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every launch of a round from Python instead of replaying the "
                          "round captured as a HIP graph")
@@ -419,6 +469,8 @@ def main():
         if w.past_on_host and args.stagger_rounds > 0:
             line["decode_two_requests"] = _decode_pair(torch, harness, synth, w, args.seed,
                                                        args.decode_rounds)
+    if args.e2e_context > 0:
+        line["e2e_decode"] = _e2e_decode(torch, args.seed, args.e2e_context, args.e2e_tokens)
     if not args.no_cpu_baseline and args.workload == "c2":
         line["cpu_baseline"] = cpu_baseline(w, inputs, a_plus_1, args.cpu_draft_steps,
                                             args.cpu_verify_heads)
