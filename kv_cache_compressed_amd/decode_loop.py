@@ -297,3 +297,193 @@ class GreedyDecoder:
             self.store.write(self.n, self.k1, self.v1)
             self.n += 1
         return [int(t) for t in self.toks[1:steps + 1].tolist()]
+
+
+class LayeredDecoder:
+    """VeriCache decoding of one request on a stack of attention layers on the residual stream
+    (x_{l+1} = x_l + Wo_l attention_l(x_l), logits = Wlm x_L). weights: E, P, Wlm as for
+    TokenDecoder and per-layer lists Wq, Wk, Wv, Wo. Every layer has its own full cache (HBM or
+    pinned host memory) and KIVI cache. Draft steps thread the residual stream through every
+    layer's draft attention over the compressed caches; the verify runs every layer over the full
+    caches for all x + 1 entries. Above the first layer the drafter's keys/values of its own
+    positions differ from the verifier's (their inputs went through compressed attention), so the
+    commit writes the verifier's keys/values of the kept positions into the full caches and over
+    the draft-time entries of the residual rings."""
+
+    def __init__(self, weights, Hq: int, Hkv: int, prompt, x: int, bits: int = 4, R: int = 32,
+                 max_new: int = 256, kv_dtype: str = "f32", host_past: bool = False,
+                 chunk_tokens: int = 65536, device: str = "cuda"):
+        self.E, self.P = _dev(weights["E"], device), _dev(weights["P"], device)
+        self.Wlm = _dev(weights["Wlm"], device)
+        self.Wq = [_dev(w, device) for w in weights["Wq"]]
+        self.Wk = [_dev(w, device) for w in weights["Wk"]]
+        self.Wv = [_dev(w, device) for w in weights["Wv"]]
+        self.Wo = [_dev(w, device) for w in weights["Wo"]]
+        self.nl = len(self.Wq)
+        self.V, self.dm = self.E.shape
+        assert self.dm % D == 0 and Hq % Hkv == 0
+        assert not host_past or kv_dtype == "bf16", "a host-streamed cache is bf16"
+        self.tdt = torch.float32 if kv_dtype == "f32" else torch.bfloat16
+        self.vdt = vc.VC_F32 if kv_dtype == "f32" else vc.VC_BF16
+        self.Hq, self.Hkv, self.x, self.L, self.R = Hq, Hkv, x, x + 1, R
+        self.host, self.chunk, self.device = host_past, chunk_tokens, device
+        self.copy_stream = torch.cuda.Stream() if host_past else None
+        prompt = [int(t) for t in prompt]
+        n = self.n = len(prompt) - 1
+        L = self.L
+        self.cap = (n + max_new + 2 * L + 63) // 32 * 32
+        assert self.cap <= self.P.shape[0], "position table too short"
+        f32 = dict(dtype=torch.float32, device=device)
+        tk = dict(dtype=self.tdt, device=device)
+        nl = self.nl
+        self.stores = [_Store(Hkv, self.cap, self.tdt, host_past, device) for _ in range(nl)]
+        self.kd = [torch.zeros((1, Hkv, L, D), **tk) for _ in range(nl)]   # draft-time k, v
+        self.vd = [torch.zeros((1, Hkv, L, D), **tk) for _ in range(nl)]
+        self.kv_ = [torch.zeros((1, Hkv, L, D), **tk) for _ in range(nl)]  # verifier's k, v
+        self.vv_ = [torch.zeros((1, Hkv, L, D), **tk) for _ in range(nl)]
+        self.qd = torch.zeros((1, Hq, D), **tk)
+        self.qv = torch.zeros((1, Hq, L, D), **tk)
+        self.od = torch.zeros((1, Hq, D), **f32)
+        self.lse_d = torch.zeros((1, Hq), **f32)
+        self.ov = torch.zeros((1, Hq, L, D), **f32)
+        self.lse_v = torch.zeros((1, Hq, L), **f32)
+        self.logits_v = torch.zeros((1, L, self.V), **f32)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.tok = torch.zeros((L + 1,), **i32)
+        self.accept_len = torch.zeros((1,), **i32)
+        self.next_tok = torch.zeros((1,), **i32)
+        self.argmax_v = torch.zeros((1, L), **i32)
+        self.ws_draft = vc.Workspace(device)
+        self.ws_verify = vc.Workspace(device)
+        self.ws_proj = torch.zeros((vc.vc_project_workspace(1, 1, self.V) + 3) // 4, **i32)
+        self.n_q = 32 * (max(0, n - R) // 32)
+        res_cap = (R + 32 + L + 31) // 32 * 32
+        meta = vc.VC_F32 if kv_dtype == "f32" else vc.VC_F16
+        self.caches = [vc.KiviCache(1, Hkv, self.cap, bits, meta, meta, res_cap, device)
+                       for _ in range(nl)]
+        self._prefill(prompt)
+        self.tok[0] = prompt[-1]
+        self.rounds = []
+
+    def _verify(self, l: int, q, k, v, n: int, out, lse):
+        host = self.host and n > 0  # no past yet: nothing to stream (the block alone)
+        nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, q.shape[2], n, host, self.chunk, self.vdt)
+        st = self.stores[l]
+        kp, vp, stride = (st.k, st.v, self.cap) if n > 0 else (k, v, q.shape[2])
+        vc.vc_verify_attn(q, k, v, kp, vp, n, out, lse, self.ws_verify.get(nb), SM_SCALE,
+                          past_stride=stride, past_on_host=host, chunk_tokens=self.chunk,
+                          copy_stream=self.copy_stream)
+
+    def _prefill(self, prompt):
+        """Layer by layer over positions 0..n-1: keys/values into the full cache and the KIVI
+        cache, causal attention in blocks of 32 rows (the verify call over the rows before the
+        block), the residual stream updated."""
+        n, Hq, Hkv = self.n, self.Hq, self.Hkv
+        X = self.E[torch.tensor(prompt[:n], device=self.device)] + self.P[:n]
+        for l in range(self.nl):
+            K = (X @ self.Wk[l].T).view(n, Hkv, D).transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
+            V = (X @ self.Wv[l].T).view(n, Hkv, D).transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
+            self.stores[l].write(0, K, V)
+            c = self.caches[l]
+            if self.n_q:
+                vc.vc_quantize_kv(c, K, V, 0, self.n_q, src_bh_stride=n * D)
+            if n > self.n_q:
+                vc.vc_kivi_append(c, K[:, :, self.n_q:], V[:, :, self.n_q:], self.n_q, n - self.n_q,
+                                  src_bh_stride=n * D)
+            Xn = X.clone()
+            for b0 in range(0, n, 32):
+                b1 = min(n, b0 + 32)
+                m = b1 - b0
+                q = (X[b0:b1] @ self.Wq[l].T).view(m, Hq, D).transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
+                o = torch.zeros((1, Hq, m, D), dtype=torch.float32, device=self.device)
+                lse = torch.zeros((1, Hq, m), dtype=torch.float32, device=self.device)
+                self._verify(l, q, K[:, :, b0:b1].contiguous(), V[:, :, b0:b1].contiguous(), b0, o, lse)
+                Xn[b0:b1] = X[b0:b1] + o[0].transpose(0, 1).reshape(m, -1) @ self.Wo[l].T
+            X = Xn
+
+    def draft_step(self, j: int):
+        x = self.E[self.tok[j:j + 1].long()][0] + self.P[self.n + j]
+        r = (self.n - self.n_q) + j + 1
+        for l in range(self.nl):
+            self.qd[0] = (self.Wq[l] @ x).view(self.Hq, D)
+            self.kd[l][0, :, j] = (self.Wk[l] @ x).view(self.Hkv, D)
+            self.vd[l][0, :, j] = (self.Wv[l] @ x).view(self.Hkv, D)
+            c = self.caches[l]
+            nb = vc.vc_draft_quant_workspace(c, self.n_q, r, self.Hq)
+            vc.vc_draft_attn_quant(c, self.n_q, r, self.qd, self.od, self.lse_d, self.ws_draft.get(nb),
+                                   SM_SCALE, k_new=self.kd[l][:, :, j], v_new=self.vd[l][:, :, j])
+            x = x + self.Wo[l] @ self.od.view(-1)
+        vc.vc_project_logits(self.Wlm, x.view(1, -1, D), argmax=self.tok[j + 1:j + 2], argmax_b_stride=1,
+                             ws=self.ws_proj)
+
+    def verify_step(self):
+        L, n = self.L, self.n
+        X = self.E[self.tok[:L].long()] + self.P[n:n + L]
+        for l in range(self.nl):
+            self.qv.copy_((X @ self.Wq[l].T).view(L, self.Hq, D).transpose(0, 1).unsqueeze(0))
+            self.kv_[l].copy_((X @ self.Wk[l].T).view(L, self.Hkv, D).transpose(0, 1).unsqueeze(0))
+            self.vv_[l].copy_((X @ self.Wv[l].T).view(L, self.Hkv, D).transpose(0, 1).unsqueeze(0))
+            self._verify(l, self.qv, self.kv_[l], self.vv_[l], n, self.ov, self.lse_v)
+            X = X + self.ov[0].transpose(0, 1).reshape(L, -1) @ self.Wo[l].T
+        xl = X.view(L, -1, D).transpose(0, 1).unsqueeze(0).contiguous()
+        vc.vc_project_logits(self.Wlm, xl, logits=self.logits_v)
+        vc.vc_accept(self.logits_v, self.tok[1:L].view(1, self.x), self.accept_len, self.next_tok,
+                     self.argmax_v)
+
+    def commit(self):
+        a = int(self.accept_len[0].item())
+        emitted = [int(t) for t in self.tok[1:a + 1].tolist()] + [int(self.next_tok[0].item())]
+        n0, n1 = self.n, self.n + a + 1
+        assert n1 + self.L <= self.cap, "cache capacity exhausted (raise max_new)"
+        for l in range(self.nl):
+            k, v = self.kv_[l][:, :, :a + 1], self.vv_[l][:, :, :a + 1]
+            self.stores[l].write(n0, k, v)
+            vc.vc_kivi_append(self.caches[l], k, v, n0, a + 1, src_bh_stride=self.L * D)
+        self.n = n1
+        while self.n - self.n_q >= self.R + 32:
+            for l in range(self.nl):
+                Kg, Vg, stride = self.stores[l].device_rows(self.n_q, self.n_q + 32)
+                vc.vc_quantize_kv(self.caches[l], Kg, Vg, self.n_q, 32, src_bh_stride=stride)
+            self.n_q += 32
+        self.tok[0:1] = self.next_tok
+        self.rounds.append(a)
+        return emitted
+
+    def generate(self, steps: int):
+        out = []
+        while len(out) < steps:
+            for j in range(self.x):
+                self.draft_step(j)
+            self.verify_step()
+            out += self.commit()
+        return out[:steps]
+
+
+class LayeredGreedyDecoder(LayeredDecoder):
+    """Greedy decoding over the full caches of the same layer stack, one token per step (no
+    drafter; the KIVI caches are built by the shared prefill and not read)."""
+
+    def __init__(self, weights, Hq: int, Hkv: int, prompt, max_new: int = 256, **kw):
+        super().__init__(weights, Hq, Hkv, prompt, x=1, max_new=max_new, **kw)
+        self.q1 = torch.zeros((1, Hq, 1, D), dtype=self.tdt, device=self.device)
+        self.k1 = torch.zeros((1, Hkv, 1, D), dtype=self.tdt, device=self.device)
+        self.v1 = torch.zeros_like(self.k1)
+        self.o1 = torch.zeros((1, Hq, 1, D), dtype=torch.float32, device=self.device)
+        self.lse1 = torch.zeros((1, Hq, 1), dtype=torch.float32, device=self.device)
+        self.toks = torch.zeros((max_new + 1,), dtype=torch.int32, device=self.device)
+        self.toks[0] = self.tok[0]
+
+    def generate(self, steps: int):
+        for i in range(steps):
+            x = self.E[self.toks[i:i + 1].long()][0] + self.P[self.n]
+            for l in range(self.nl):
+                self.q1[0, :, 0] = (self.Wq[l] @ x).view(self.Hq, D)
+                self.k1[0, :, 0] = (self.Wk[l] @ x).view(self.Hkv, D)
+                self.v1[0, :, 0] = (self.Wv[l] @ x).view(self.Hkv, D)
+                self._verify(l, self.q1, self.k1, self.v1, self.n, self.o1, self.lse1)
+                self.stores[l].write(self.n, self.k1, self.v1)
+                x = x + self.Wo[l] @ self.o1.view(-1)
+            vc.vc_project_logits(self.Wlm, x.view(1, -1, D), argmax=self.toks[i + 1:i + 2],
+                                 argmax_b_stride=1, ws=self.ws_proj)
+            self.n += 1
+        return [int(t) for t in self.toks[1:steps + 1].tolist()]

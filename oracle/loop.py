@@ -173,3 +173,58 @@ def vericache(model, prompt, steps, x, drafter):
         out += emitted
         toks += emitted
     return out, rounds
+
+
+class LayeredModel:
+    """`layers` attention layers stacked on the residual stream: x_0 = E[tok] + P[pos];
+    x_{l+1} = x_l + Wo_l attention_l(Wq_l x_l; keys Wk_l x_l and values Wv_l x_l of positions
+    0..p); logits = Wlm x_L. With one layer it is TinyModel (the drafter and the verifier again
+    share every weight). Layers above the first see keys/values that depend on the attention below,
+    so a drafter's keys/values of its own positions differ from the verifier's there.
+    kv_bf16 as in TinyModel. Weights drawn like TinyModel's, per layer."""
+
+    def __init__(self, seed=0, vocab=11, dm=16, d=8, Hq=4, Hkv=2, layers=2, max_pos=128,
+                 kv_bf16=False):
+        g = np.random.default_rng(seed)
+        self.V, self.dm, self.d, self.Hq, self.Hkv, self.nl = vocab, dm, d, Hq, Hkv, layers
+        self.kv_bf16 = kv_bf16
+        self.E = g.standard_normal((vocab, dm))
+        self.P = 0.5 * g.standard_normal((max_pos, dm))
+        self.Wq, self.Wk, self.Wv, self.Wo = [], [], [], []
+        for _ in range(layers):
+            self.Wq.append(g.standard_normal((Hq * d, dm)) / np.sqrt(dm))
+            self.Wk.append(g.standard_normal((Hkv * d, dm)) / np.sqrt(dm))
+            self.Wv.append(g.standard_normal((Hkv * d, dm)) / np.sqrt(dm))
+            self.Wo.append(g.standard_normal((dm, Hq * d)) / np.sqrt(Hq * d) / np.sqrt(layers))
+        self.Wlm = 3.0 * g.standard_normal((vocab, dm)) / np.sqrt(dm)
+        self.scale = 1.0 / np.sqrt(d)
+
+    def _r(self, a):
+        return bf16(a) if self.kv_bf16 else a
+
+    def logits_all(self, tokens):
+        """Causal forward over every position of `tokens`: logits [len, V] (float64)."""
+        n = len(tokens)
+        X = self.E[np.asarray(tokens)] + self.P[:n]
+        G = self.Hq // self.Hkv
+        for l in range(self.nl):
+            Q = self._r(X @ self.Wq[l].T).reshape(n, self.Hq, self.d)
+            K = self._r(X @ self.Wk[l].T).reshape(n, self.Hkv, self.d)
+            Vv = self._r(X @ self.Wv[l].T).reshape(n, self.Hkv, self.d)
+            O = np.zeros((n, self.Hq, self.d))
+            for p in range(n):
+                for h in range(self.Hq):
+                    O[p, h] = decode(Q[p, h], K[: p + 1, h // G], Vv[: p + 1, h // G], self.scale)[0]
+            X = X + O.reshape(n, -1) @ self.Wo[l].T
+        return X @ self.Wlm.T
+
+
+def greedy_layered(model, prompt, steps):
+    """Plain greedy decoding over the full cache of a LayeredModel."""
+    toks = list(prompt)
+    out = []
+    while len(out) < steps:
+        t = int(np.argmax(model.logits_all(toks)[-1]))
+        out.append(t)
+        toks.append(t)
+    return out

@@ -68,3 +68,22 @@ def test_bf16_rounding_of_the_tiny_model():
     r = bf16(g)
     assert np.all(np.abs(r - g) <= np.abs(g) * 2.0 ** -8)                 # within half a bf16 ulp
     assert np.all((r.astype(np.float32).view(np.uint32) & 0xFFFF) == 0)   # representable in bf16
+
+
+def test_layered_model_one_layer_is_the_tiny_model_and_causal():
+    from oracle.loop import LayeredModel, TinyModel, full_cache
+    lm = LayeredModel(seed=2, vocab=13, dm=16, d=8, Hq=4, Hkv=2, layers=1, max_pos=64)
+    tm = TinyModel(seed=9, vocab=13, dm=16, d=8, Hq=4, Hkv=2, max_pos=64)
+    for k in ("E", "P", "Wlm"):
+        setattr(tm, k, getattr(lm, k))
+    tm.Wq, tm.Wk, tm.Wv, tm.Wo = lm.Wq[0], lm.Wk[0], lm.Wv[0], lm.Wo[0]
+    toks = list(np.random.default_rng(0).integers(0, 13, 20))
+    Z = lm.logits_all(toks)
+    for p in (0, 7, 19):
+        K, V = full_cache(tm, toks[: p + 1])
+        assert np.allclose(Z[p], tm.next_logits(toks[p], p, K, V), rtol=1e-12, atol=1e-12)
+    # causality: later tokens do not change earlier logits (two layers)
+    lm2 = LayeredModel(seed=3, vocab=13, dm=16, d=8, Hq=4, Hkv=2, layers=2, max_pos=64)
+    a = lm2.logits_all(toks)
+    b = lm2.logits_all(toks[:12] + [(t + 1) % 13 for t in toks[12:]])
+    assert np.array_equal(a[:12], b[:12]) and not np.allclose(a[12:], b[12:])
