@@ -175,6 +175,16 @@ class TokenDecoder:
         self.tok[0] = prompt[-1]
         self.rounds = []  # accepted count per round
 
+    def warm(self):
+        """Size every workspace for the largest context this decoder can reach, so that no
+        allocation falls inside a timed decode."""
+        nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, self.cap, self.host, self.chunk,
+                                    self.m.vdt)
+        self.ws_verify.get(nb)
+        r = self.R + 32 + self.L
+        self.ws_draft.get(vc.vc_draft_quant_workspace(self.cache, (self.cap - r) // 32 * 32, r, self.Hq))
+        torch.cuda.synchronize()
+
     # ---- one block entry: embedding and projections -----------------------------------------
     def _entry(self, j: int):
         mdl = self.m
@@ -278,6 +288,12 @@ class GreedyDecoder:
         self.toks[0] = prompt[-1]
         self.ws = vc.Workspace(device)
         self.ws_proj = torch.zeros((vc.vc_project_workspace(1, 1, mdl.V) + 3) // 4, **i32)
+
+    def warm(self):
+        """Size the workspace for the largest context this decoder can reach."""
+        self.ws.get(vc.vc_verify_workspace(1, self.Hq, self.Hkv, 1, self.cap, self.host, self.chunk,
+                                           self.m.vdt))
+        torch.cuda.synchronize()
 
     def generate(self, steps: int):
         mdl = self.m
