@@ -140,7 +140,7 @@ __device__ void find_digit(Shared& sh, int64_t remaining) {
 
 __global__ void __launch_bounds__(ST) select_keep_kernel(SArgs a) {
   __shared__ Shared sh;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6;
   const float* row = a.s + (int64_t)blockIdx.x * a.s_stride;
   int32_t* out = a.idx + (int64_t)blockIdx.x * a.idx_stride;
   const int64_t lo = a.lo, hi = a.hi, m = hi - lo;
