@@ -285,6 +285,40 @@ def _e2e_decode(torch, seed: int, context: int, tokens: int) -> dict:
     out["speedup"] = round(out["vericache"]["tok_s"] / out["greedy"]["tok_s"], 3)
     a, b = seqs["vericache"], seqs["greedy"]
     out["first_divergence"] = next((i for i in range(tokens) if a[i] != b[i]), None)  # of `tokens`
+
+    # two requests (the second prompt drawn after the first), lock-step against staggered
+    # (harness.staggered_decode: one request's verify streams while the other drafts)
+    from kv_cache_compressed_amd import harness
+
+    prompt2 = torch.randint(0, V, (context,), generator=g, device=dev).tolist()
+    rounds = max(1, tokens // 31)
+
+    def pair():
+        d0 = TokenDecoder(W, Hq, Hkv, prompt, x=30, bits=4, R=128, max_new=rounds * 31 + 64, **opts)
+        d1 = TokenDecoder(W, Hq, Hkv, prompt2, x=30, bits=4, R=128, max_new=rounds * 31 + 64,
+                          copy_stream=d0.copy_stream, **opts)
+        d0.warm()
+        d1.warm()
+        return [d0, d1]
+
+    two = {"rounds_per_request": rounds}
+    for name in ("lockstep", "staggered"):
+        ds = pair()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if name == "lockstep":
+            acc = harness.lockstep_decode(ds, rounds, lambda gi, r: ())
+        else:
+            acc = harness.staggered_decode(ds, [torch.cuda.current_stream(), torch.cuda.Stream()],
+                                           rounds, lambda gi, r: ())
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        emitted = sum(len(em) for ga in acc for em in ga)
+        two[name] = {"tok_s": round(emitted / el, 2), "emitted": emitted,
+                     "ms_per_round": round(el / rounds * 1e3, 2)}
+        del ds
+    two["speedup"] = round(two["staggered"]["tok_s"] / two["lockstep"]["tok_s"], 3)
+    out["two_requests"] = two
     return out
 
 

@@ -245,12 +245,19 @@ class TokenDecoder:
         self.rounds.append(a)
         return emitted
 
+    def draft_phase(self):
+        for j in range(self.x):
+            self.draft_step(j)
+
+    def set_round_inputs(self):
+        """Nothing to load: the next round starts from the committed token (for the schedules in
+        harness, which pass each group its next round's inputs)."""
+
     def generate(self, steps: int):
         """Rounds until `steps` tokens are emitted; returns them."""
         out = []
         while len(out) < steps:
-            for j in range(self.x):
-                self.draft_step(j)
+            self.draft_phase()
             self.verify_step()
             out += self.commit()
         return out[:steps]

@@ -465,10 +465,15 @@ def lockstep_decode(groups, rounds: int, next_inputs):
 
 
 def staggered_decode(groups, streams, rounds: int, next_inputs):
-    """The staggered schedule of `staggered` over chained decode rounds: after its verify a group
-    commits (the host waits for that group's stream only) and loads its next round's inputs, and
-    its next draft phase is enqueued before the following group's verify, so it runs while that
-    verify streams. Returns the accepted counts per group (the same as `lockstep_decode`)."""
+    """The staggered schedule of `staggered` over chained decode rounds. Slot k is (group k % G,
+    round k // G). Every group's first draft phase goes in first (group g after group g-1's), then
+    for each slot: the previous slot's commit (the host waits on that group's stream only; the
+    group loads its next round's inputs), this slot's verify (its drafts are already enqueued; it
+    takes its turn on the host link after the previous verify), and the next draft phase of the
+    group that just committed, which runs while this verify streams. Verifies never wait for a
+    draft phase to be enqueued, so the schedule holds whether drafting is bound by the GPU or by
+    the host that enqueues it. Returns what each group's commits returned, per group (the same as
+    `lockstep_decode`)."""
     ng = len(groups)
     assert len(streams) == ng and ng >= 1
     cur = torch.cuda.current_stream()
@@ -476,9 +481,14 @@ def staggered_decode(groups, streams, rounds: int, next_inputs):
         s.wait_stream(cur)
     first_done = [torch.cuda.Event() for _ in range(ng)]
     acc = [[] for _ in groups]
+    total = rounds * ng
+    enq = set()
     verify_done = None
 
     def draft(k):
+        if k >= total or k in enq:
+            return
+        enq.add(k)
         g = k % ng
         if k < ng and g > 0:
             streams[g].wait_event(first_done[g - 1])
@@ -487,26 +497,29 @@ def staggered_decode(groups, streams, rounds: int, next_inputs):
             if k < ng:
                 first_done[g].record(streams[g])
 
-    total = rounds * ng
-    draft(0)
-    for k in range(total):
+    def commit(k):
         g, r = k % ng, k // ng
-        early = k + 1 < total and (k + 1) % ng != g
-        if early:
-            draft(k + 1)
-        s = streams[g]
-        if verify_done is not None:
-            s.wait_event(verify_done)
-        with torch.cuda.stream(s):
-            groups[g].verify_step()
-            verify_done = torch.cuda.Event()
-            verify_done.record(s)
+        with torch.cuda.stream(streams[g]):
             acc[g].append(groups[g].commit())  # waits for this group's stream only
             if r + 1 < rounds:
                 groups[g].set_round_inputs(*next_inputs(g, r + 1))
-        if k + 1 < total and not early:
-            draft(k + 1)
+
+    for k in range(min(ng, total)):
+        draft(k)
+    for k in range(total):
+        if k >= 1:
+            commit(k - 1)
+        draft(k)  # one group: its next round follows its commit
+        s = streams[k % ng]
+        if verify_done is not None:
+            s.wait_event(verify_done)
+        with torch.cuda.stream(s):
+            groups[k % ng].verify_step()
+            verify_done = torch.cuda.Event()
+            verify_done.record(s)
+        if ng > 1:
+            draft(k + ng - 1)  # the group that just committed drafts its next round
+    commit(total - 1)
     for s in streams:
         cur.wait_stream(s)
     return acc
-

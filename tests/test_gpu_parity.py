@@ -847,3 +847,42 @@ def test_layered_decoder_emits_full_kv_greedy(gpu_lib, layers, bits, kv, host):
             assert gap < GAP, f"{what}: token {t} differs ({seq[t]} vs {ref[t]}), oracle top-2 gap {gap}"
             print(f"{what}: first divergence at token {t}: near-tie (gap {gap:.2e})", flush=True)
     assert dec.n_q > 32 * ((len(prompt) - 1 - 32) // 32), "the loop must have flushed"
+
+
+def test_token_decoders_staggered_two_requests(gpu_lib):
+    """Two requests decoded token by token over host-streamed bf16 caches: the staggered schedule
+    (harness.staggered_decode) emits, per request, the same tokens as the lock-step one, and those
+    are the oracle's full-KV greedy tokens of each prompt (up to a near-tie divergence)."""
+    from kv_cache_compressed_amd.decode_loop import TokenDecoder
+    from oracle import loop as oloop
+
+    m = oloop.TinyModel(seed=5, vocab=384, dm=256, d=128, Hq=4, Hkv=2, max_pos=1024, kv_bf16=True)
+    names = ("E", "P", "Wq", "Wk", "Wv", "Wo", "Wlm")
+    Wt = {k: getattr(m, k).astype(np.float32) for k in names}
+    for k in names:
+        setattr(m, k, Wt[k].astype(np.float64))
+    prompts = [[int(t) for t in np.random.default_rng(s).integers(0, 384, 200)] for s in (11, 12)]
+    rounds, x = 5, 8
+    opts = dict(kv_dtype="bf16", host_past=True, chunk_tokens=64)
+
+    def build():
+        d0 = TokenDecoder(Wt, 4, 2, prompts[0], x=x, bits=2, R=32, max_new=rounds * (x + 1) + 16, **opts)
+        d1 = TokenDecoder(Wt, 4, 2, prompts[1], x=x, bits=2, R=32, max_new=rounds * (x + 1) + 16,
+                          copy_stream=d0.copy_stream, **opts)
+        return [d0, d1]
+
+    lock = harness.lockstep_decode(build(), rounds, lambda g, r: ())
+    stag = harness.staggered_decode(build(), [torch.cuda.current_stream(), torch.cuda.Stream()],
+                                    rounds, lambda g, r: ())
+    for g in range(2):
+        a = [t for em in lock[g] for t in em]
+        b = [t for em in stag[g] for t in em]
+        assert a == b, f"request {g}"
+        ref = oloop.greedy(m, prompts[g], len(a))
+        if a != ref:
+            t = next(i for i in range(len(a)) if a[i] != ref[i])
+            toks = prompts[g] + ref[:t]
+            K, V = oloop.full_cache(m, toks)
+            gap = float(oacc.top2_gap(m.next_logits(toks[-1], len(toks) - 1, K, V)[None])[0])
+            assert gap < GAP, f"request {g}: token {t} differs, oracle top-2 gap {gap}"
+        print(f"request {g}: {len(a)} tokens over {rounds} rounds", flush=True)

@@ -122,9 +122,12 @@ def test_lockstep_order(monkeypatch):
     assert log == [("D", 0), ("D", 1), ("D", 2), ("V", 0), ("V", 1), ("V", 2)] * 2
 
 
-def test_staggered_decode_order(monkeypatch):
-    """Chained decode rounds: per group D, V, C(ommit), I(nputs) in order, the next group's draft
-    phase enqueued before the verify it overlaps, commits on the group's own stream."""
+@pytest.mark.parametrize("ng,rounds", [(1, 3), (2, 3), (3, 2)])
+def test_staggered_decode_order(monkeypatch, ng, rounds):
+    """Chained decode rounds: per group D, V, C(ommit), I(nputs) in order on the group's own
+    stream; every verify after the previous slot's commit and before the draft phase of the group
+    that just committed, which is enqueued while that verify is in flight (before the next commit);
+    verifies take turns on the host link."""
     log = []
     cur = _Stream("cur", log)
     fake, current = _fake_torch(log, cur)
@@ -147,22 +150,32 @@ def test_staggered_decode_order(monkeypatch):
         def set_round_inputs(self, *a):
             log.append(("I", self.i, current[0].name))
 
-    rounds = 3
-    acc = harness.staggered_decode([G(0), G(1)], [_Stream(0, log), _Stream(1, log)], rounds,
-                                   lambda g, r: ())
-    assert acc == [[0] * rounds, [0] * rounds]
+    acc = harness.staggered_decode([G(g) for g in range(ng)], [_Stream(g, log) for g in range(ng)],
+                                   rounds, lambda g, r: ())
+    assert acc == [[0] * rounds for _ in range(ng)]
     ph = [e for e in log if e[0] in "DVCI"]
     for kind, g, s in ph:
         assert s == g
-    for g in range(2):
+    for g in range(ng):
         seq = [k for k, gg, _ in ph if gg == g]
         assert seq == ["D", "V", "C", "I"] * (rounds - 1) + ["D", "V", "C"]
     order = [(k, g) for k, g, _ in ph]
-    # group 1's first draft before group 0's first verify; each later draft before the other
-    # group's verify
-    assert order.index(("D", 1)) < order.index(("V", 0))
+    total = ng * rounds
     vs = [i for i, e in enumerate(order) if e[0] == "V"]
+    cs = [i for i, e in enumerate(order) if e[0] == "C"]
     ds = [i for i, e in enumerate(order) if e[0] == "D"]
-    for j in range(1, len(vs)):  # the draft of slot j+1 precedes the verify of slot j
-        if j + 1 < len(ds):
-            assert ds[j + 1] < vs[j]
+    assert [order[i][1] for i in vs] == [k % ng for k in range(total)]  # slot order
+    for k in range(1, total):
+        assert cs[k - 1] < vs[k]          # the previous commit precedes this verify
+    if ng > 1:
+        for k in range(total):
+            if k + ng - 1 < total:        # the committed group's next draft phase under verify k
+                assert vs[k] < ds[k + ng - 1] or k + ng - 1 < ng
+                if k + 1 < total:
+                    assert ds[k + ng - 1] < cs[k]
+        assert all(ds[g] < vs[0] for g in range(ng))  # every group's first draft phase up front
+    # verify k waits for the event recorded after verify k-1 on the previous slot's stream
+    vlog = [i for i, e in enumerate(log) if e[0] == "V"]
+    for k in range(1, total):
+        rec = next(e for e in log[vlog[k - 1] + 1:] if e[0] == "rec")
+        assert ("wait", k % ng, rec[2]) in log[vlog[k - 1]:vlog[k]]
