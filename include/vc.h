@@ -223,9 +223,11 @@ vc_status vc_accept(const float *logits, const int32_t *drafts, int32_t B, int32
  *   W      [V][Hq*128] fp32, device;  o [B][Hq][L][128] fp32, device (the attention outputs:
  *          draft steps have L == 1, the verify block L rows)
  *   logits [B][L][V] fp32 or NULL
- *   argmax row (b, i) written to argmax[b * argmax_b_stride + i] (lowest index on ties), or NULL
+ *   argmax row (b, i) written to argmax[b * argmax_b_stride + i] (lowest index on ties; -0 and +0
+ *          tie; logits are expected finite), or NULL
  *   ws     device, >= vc_project_workspace bytes, 16-byte aligned; zero-filled once before first
- *          use (ticket counters; every call leaves them zero); may be NULL when argmax is NULL.
+ *          use (ticket counters and per-row argmax slots; every call leaves them zero); may be
+ *          NULL when argmax is NULL.
  *          Calls that share a workspace must not overlap.
  *   1 <= B*L <= 2^20, 1 <= V <= 2^24, 1 <= Hq <= 1024, Hq*128*V < 2^31.
  */

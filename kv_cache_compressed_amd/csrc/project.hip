@@ -12,8 +12,10 @@
 // 2048-channel chunk, so every W row is read with coalesced 16-byte loads, all VT rows of a chunk
 // in flight at once and the next chunk's loads issued before this chunk's FMAs. The VT x MT dot
 // products are reduced across the wave by recursive halving (each lane ends with one of the 64
-// sums) and across the 8 waves through LDS. For the argmax each workgroup writes its best (value,
-// index) per row; the last workgroup of a row tile (ticket counter) reduces them.
+// sums) and across the 8 waves through LDS. For the argmax each workgroup folds its best (value,
+// index) per row into one 64-bit slot per row with an atomic max (the value in an order-preserving
+// encoding above the complemented index, so the maximum is the largest value at its lowest index);
+// the last workgroup of a row tile (ticket counter) reads the slots out and clears them.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,7 +28,6 @@ constexpr int PW = PT / 64;     // waves
 constexpr int VT = 8;           // vocabulary rows per workgroup
 constexpr int MT = 8;           // output rows per workgroup
 constexpr int CHUNK = 4 * PT;   // channels per chunk
-constexpr int TG = 8;           // ticket groups per row tile
 static_assert(PW == MT, "one wave per row in the final reduction");
 
 struct PArgs {
@@ -37,12 +38,21 @@ struct PArgs {
   float* z;             // [M][V] or null
   int32_t* idx;         // row (b, i) at idx[b * idx_b_stride + i], or null
   int64_t idx_b_stride;
-  unsigned* counters;   // TG + 1 per row tile (grid.y); zero between calls
-  float* part;          // [M][nvt][2]: (value, index bits) per vocabulary tile
+  unsigned* counters;   // one per row tile (grid.y); zero between calls
+  unsigned long long* slot;  // [M] packed (value, index) maxima; zero between calls
 };
 
 __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
+}
+
+// (value, index) as one unsigned 64-bit key ordered like better() for finite values: the float's
+// bits mapped to an unsigned order (negative: all bits flipped; positive: sign bit set; -0 counts
+// as +0) above 0xffffffff - index. Every key is nonzero, so zero marks an empty slot.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (0xffffffffu - (uint32_t)i);
 }
 
 // Recursive-halving reduction of N values per lane across the 64 lanes of a wave: after the
@@ -140,30 +150,22 @@ __global__ void __launch_bounds__(PT) project_kernel(PArgs a) {
         const int oi = __shfl_xor(bi, off, 64);
         if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
       }
-      // Candidates go out as device-coherent stores and have completed before the ticket is
-      // taken; the last ticket holder reads them back with device-coherent loads. (Release /
-      // acquire fences would write back and invalidate the whole L2 instead, costing
-      // microseconds per call.) Two-level ticket: the tiles of a row tile count in TG group
-      // counters (tile t in group t % TG), the last of each group in a top counter, so no
-      // counter sees more than ~nvt/TG contending atomics.
-      if (lane < MT && m < a.M) {
-        float* p = a.part + ((int64_t)m * a.nvt + blockIdx.x) * 2;
-        store_coherent(p, bv);
-        store_coherent(p + 1, __int_as_float(bi));
+      // The device-scope atomic max has been performed (its old value returned) before the
+      // ticket is taken; the last ticket holder reads the slots with device-coherent loads.
+      // (Release / acquire fences would write back and invalidate the whole L2 instead, costing
+      // microseconds per call.) One counter per row tile: a two-level ticket (group counters,
+      // then a top counter) spreads the contention but adds a round trip, and measured ~0.8 us
+      // slower per call at 256 vocabulary tiles.
+      if (lane < MT && m < a.M && bi != 0x7fffffff) {
+        const unsigned long long old = __hip_atomic_fetch_max(a.slot + m, argmax_key(bv, bi),
+                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::"v"(old));  // use the returned value: wait for the atomic itself
       }
-      wait_vm<0>();
       if (lane == 0) {
-        unsigned* cnt = a.counters + blockIdx.y * (TG + 1);
-        const int grp = blockIdx.x % TG, ngrp = min(TG, a.nvt);
-        const unsigned in_grp = (unsigned)((a.nvt - grp + TG - 1) / TG);
-        int last = 0;
-        if (__hip_atomic_fetch_add(cnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_grp - 1) {
-          __hip_atomic_store(cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (__hip_atomic_fetch_add(cnt + TG, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(ngrp - 1)) {
-            __hip_atomic_store(cnt + TG, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            last = 1;
-          }
-        }
+        unsigned* cnt = a.counters + blockIdx.y;
+        const int last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                         (unsigned)(a.nvt - 1);
+        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = last;
       }
     }
@@ -172,32 +174,13 @@ __global__ void __launch_bounds__(PT) project_kernel(PArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  // Last workgroup of this row tile: wave w reduces the candidates of row m0 + w (4 loads per
-  // lane in flight per batch of 256 tiles).
-  const int row = m0 + wave;
-  if (row >= a.M) return;
-  float cv = -INFINITY;
-  int ci = 0x7fffffff;
-  for (int t0 = 0; t0 < a.nvt; t0 += 256) {
-    float2 pv[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = min(t0 + lane + 64 * k, a.nvt - 1);  // past the end: re-read, no effect
-      pv[k] = load_f32x2<true>(a.part + ((int64_t)row * a.nvt + t) * 2);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int pi = __float_as_int(pv[k].y);
-      if (better(pv[k].x, pi, cv, ci)) { cv = pv[k].x; ci = pi; }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(cv, off, 64);
-    const int oi = __shfl_xor(ci, off, 64);
-    if (better(ov, oi, cv, ci)) { cv = ov; ci = oi; }
-  }
-  if (lane == 0) a.idx[(int64_t)(row / a.L) * a.idx_b_stride + row % a.L] = ci;
+  // Last workgroup of this row tile: thread t < MT reads row m0 + t's slot, clears it and writes
+  // the index.
+  const int row = m0 + tid;
+  if (tid >= MT || row >= a.M) return;
+  const unsigned long long key = __hip_atomic_load(a.slot + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(a.slot + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  a.idx[(int64_t)(row / a.L) * a.idx_b_stride + row % a.L] = (int32_t)(0xffffffffu - (uint32_t)key);
 }
 
 }  // namespace
@@ -206,9 +189,9 @@ ProjectPlan plan_project(int M, int V) {
   ProjectPlan p;
   p.nvt = (V + VT - 1) / VT;
   p.nmt = (M + MT - 1) / MT;
-  const size_t counters = ((size_t)p.nmt * (TG + 1) * sizeof(unsigned) + 255) & ~(size_t)255;
+  const size_t counters = ((size_t)p.nmt * sizeof(unsigned) + 255) & ~(size_t)255;
   p.counter_bytes = counters;
-  p.ws_bytes = counters + (size_t)M * p.nvt * 2 * sizeof(float);
+  p.ws_bytes = counters + (size_t)M * sizeof(unsigned long long);
   return p;
 }
 
@@ -228,7 +211,8 @@ hipError_t launch_project(const float* W, int V, const float* o, int B, int Hq, 
   a.idx = idx;
   a.idx_b_stride = idx_b_stride;
   a.counters = static_cast<unsigned*>(ws);
-  a.part = idx ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan.counter_bytes) : nullptr;
+  a.slot = idx ? reinterpret_cast<unsigned long long*>(static_cast<uint8_t*>(ws) + plan.counter_bytes)
+               : nullptr;
   project_kernel<<<dim3(plan.nvt, plan.nmt), PT, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -148,12 +148,12 @@ def test_merge_and_accept_reject(L):
 
 def test_project_rejects_and_sizes(L):
     """Projection: argument checks (nothing enqueued) and the workspace size (ticket counters,
-    9 per 8-row tile, rounded to 256 B, then an 8-byte candidate per row and 8-row vocabulary tile)."""
+    one per 8-row tile, rounded to 256 B, then one 8-byte argmax slot per row)."""
     n = ctypes.c_size_t()
     assert L.vc_project_workspace(8, 1, 2048, ctypes.byref(n)) == vc.VC_OK
-    assert n.value == 256 + 8 * (2048 // 8) * 8
+    assert n.value == 256 + 8 * 8
     assert L.vc_project_workspace(8, 31, 2048, ctypes.byref(n)) == vc.VC_OK
-    assert n.value == (31 * 9 * 4 + 255) // 256 * 256 + 8 * 31 * 256 * 8
+    assert n.value == 256 + 8 * 31 * 8
     assert L.vc_project_workspace(0, 1, 2048, ctypes.byref(n)) == vc.VC_ERR_INVALID
     call = lambda **a: L.vc_project_logits(a.get("W", P), a.get("V", 2048), a.get("o", P), a.get("B", 8),
                                            a.get("Hq", 32), a.get("L", 1), a.get("z", P), a.get("idx", P),

@@ -149,7 +149,7 @@ def test_project_logits(gpu_lib, B, L, Hq, V):
         # ... and the oracle's, except near-tied rows
         keep = oacc.top2_gap(ref.reshape(B * L, V)).reshape(B, L) >= GAP
         assert np.array_equal(ac[:, :L][keep], oacc.argmax_rows(ref)[keep])
-        assert not ws[: ((B * L + 7) // 8) * 9].any().item()   # ticket counters back at zero
+        assert not ws.any().item()   # ticket counters and argmax slots back at zero
     # logits only, no workspace; argmax only
     z2 = torch.zeros_like(z)
     vc.vc_project_logits(Wt, Ot, logits=z2)
@@ -159,11 +159,16 @@ def test_project_logits(gpu_lib, B, L, Hq, V):
     assert np.array_equal(am2.cpu().numpy(), am.cpu().numpy()[:, :L])
 
 
-def test_project_argmax_ties_lowest_index(gpu_lib):
+@pytest.mark.parametrize("sign", [1, -1])
+def test_project_argmax_ties_lowest_index(gpu_lib, sign):
+    """Exact ties go to the lowest index, also when every logit is negative (sign -1: W <= 0,
+    O >= 0), where the order of the packed (value, index) keys is that of the flipped bits."""
     g = np.random.default_rng(7)
     V, Hq = 300, 4
     W = g.standard_normal((V, Hq * 128)).astype(np.float32)
     O = g.standard_normal((1, Hq, 1, 128)).astype(np.float32)
+    if sign < 0:
+        W, O = -np.abs(W), np.abs(O)
     r = int(np.argmax(logits(W, O[0, :, 0])))
     for k in (3, 150, 299):                    # bitwise copies: exactly tied logits
         W[k] = W[r]
@@ -175,7 +180,9 @@ def test_project_argmax_ties_lowest_index(gpu_lib):
     vc.vc_project_logits(Wt, Ot, logits=z, argmax=am, ws=ws)
     zc = z.cpu().numpy()[0, 0]
     assert zc[3] == zc[r] == zc[150] == zc[299]
+    assert sign > 0 or zc.max() < 0
     assert am.item() == expect
+    assert not ws.any().item()
 
 
 # ------------------------------------------------------------------------------------------
