@@ -60,6 +60,7 @@ class _Model:
         self.E, self.P = _dev(weights["E"], device), _dev(weights["P"], device)
         self.Wq, self.Wk = _dev(weights["Wq"], device), _dev(weights["Wk"], device)
         self.Wv = _dev(weights["Wv"], device)
+        self.Wqkv = torch.cat([self.Wq, self.Wk, self.Wv]).contiguous()  # [(Hq + 2 Hkv) 128, dm]
         self.Wp = _head(weights, device)  # [V, Hq*128 + dm]
         self.V, self.dm = self.E.shape
         assert self.dm % D == 0 and Hq % Hkv == 0
@@ -139,9 +140,13 @@ class TokenDecoder:
         self.k_blk = torch.zeros((1, Hkv, L, D), dtype=tdt, device=device)
         self.v_blk = torch.zeros_like(self.k_blk)
         self.q_verify = torch.zeros((1, Hq, L, D), dtype=tdt, device=device)
-        self.q_draft = torch.zeros((L, 1, Hq, D), dtype=tdt, device=device)
-        self.xs = torch.zeros((L, mdl.dm), **f32)
-        self.od = torch.zeros((1, mdl.Hx, D), **f32)       # draft step [o ; x]
+        # per block entry: [o ; x] of its draft step (x written by the embedding, o by the draft
+        # attention, both read by the projection in place) and q, k, v side by side (fp32 from
+        # one GEMV, then in the cache dtype)
+        self.odx = torch.zeros((L, mdl.Hx, D), **f32)
+        nqkv = (Hq + 2 * Hkv) * D
+        self.y32 = torch.zeros((L, nqkv), **f32)
+        self.yc = self.y32 if tdt == torch.float32 else torch.zeros((L, nqkv), dtype=tdt, device=device)
         self.lse_d = torch.zeros((1, Hq), **f32)
         self.ov = torch.zeros((1, mdl.Hx, L, D), **f32)    # verify rows [o ; x]
         self.lse_v = torch.zeros((1, Hq, L), **f32)
@@ -187,39 +192,49 @@ class TokenDecoder:
 
     # ---- one block entry: embedding and projections -----------------------------------------
     def _entry(self, j: int):
+        """x of entry j (its token read on the device) into odx[j]'s x rows; q, k, v into yc[j]."""
         mdl = self.m
-        x = mdl.embed(self.tok[j:j + 1], self.n + j)
-        self.xs[j] = x
-        q = (mdl.Wq @ x).view(self.Hq, D)
-        self.q_verify[0, :, j] = q
-        self.q_draft[j, 0] = q
-        self.k_blk[0, :, j] = (mdl.Wk @ x).view(self.Hkv, D)
-        self.v_blk[0, :, j] = (mdl.Wv @ x).view(self.Hkv, D)
+        x = self.odx[j, self.Hq:].view(1, mdl.dm)
+        torch.index_select(mdl.E, 0, self.tok[j:j + 1], out=x)
+        x.add_(mdl.P[self.n + j])
+        torch.mv(mdl.Wqkv, x[0], out=self.y32[j])
+        if self.yc is not self.y32:
+            self.yc[j].copy_(self.y32[j])
+
+    def _qkv(self, j: int):
+        """Views of entry j's q [1, Hq, 128], k and v [1, Hkv, 128] in the cache dtype."""
+        Hq, Hkv, y = self.Hq, self.Hkv, self.yc[j]
+        return (y[:Hq * D].view(1, Hq, D), y[Hq * D:(Hq + Hkv) * D].view(1, Hkv, D),
+                y[(Hq + Hkv) * D:].view(1, Hkv, D))
 
     def draft_step(self, j: int):
         """Draft step j: attention over the compressed cache (storing entry j's key/value into the
         residual), logits of [o ; x] and the greedy token into block entry j + 1."""
         self._entry(j)
+        q, k, v = self._qkv(j)
         r = (self.n - self.n_q) + j + 1
         nb = vc.vc_draft_quant_workspace(self.cache, self.n_q, r, self.Hq)
-        vc.vc_draft_attn_quant(self.cache, self.n_q, r, self.q_draft[j], self.od, self.lse_d,
-                               self.ws_draft.get(nb), SM_SCALE, k_new=self.k_blk[:, :, j],
-                               v_new=self.v_blk[:, :, j])
-        self.od[0, self.Hq:] = self.xs[j].view(-1, D)
-        vc.vc_project_logits(self.m.Wp, self.od, argmax=self.tok[j + 1:j + 2], argmax_b_stride=1,
-                             ws=self.ws_proj)
+        vc.vc_draft_attn_quant(self.cache, self.n_q, r, q, self.odx[j, :self.Hq].view(1, self.Hq, D),
+                               self.lse_d, self.ws_draft.get(nb), SM_SCALE, k_new=k, v_new=v)
+        vc.vc_project_logits(self.m.Wp, self.odx[j].view(1, self.m.Hx, D),
+                             argmax=self.tok[j + 1:j + 2], argmax_b_stride=1, ws=self.ws_proj)
 
     def verify_step(self):
         """Entry x's projections, verify attention over the full cache, logits of every row and
         the greedy accept."""
         self._entry(self.x)
+        Hq, Hkv = self.Hq, self.Hkv
+        y = self.yc.view(self.L, Hq + 2 * Hkv, D)
+        self.q_verify[0].copy_(y[:, :Hq].transpose(0, 1))
+        self.k_blk[0].copy_(y[:, Hq:Hq + Hkv].transpose(0, 1))
+        self.v_blk[0].copy_(y[:, Hq + Hkv:].transpose(0, 1))
         nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, self.n, self.host, self.chunk,
                                     self.m.vdt)
         vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.store.k, self.store.v, self.n,
                           self.ov, self.lse_v, self.ws_verify.get(nb), SM_SCALE,
                           past_stride=self.cap, past_on_host=self.host, chunk_tokens=self.chunk,
                           copy_stream=self.copy_stream)
-        self.ov[0, self.Hq:] = self.xs.view(self.L, -1, D).transpose(0, 1)
+        self.ov[0, self.Hq:] = self.odx[:, self.Hq:].transpose(0, 1)
         vc.vc_project_logits(self.m.Wp, self.ov, logits=self.logits_v)
         vc.vc_accept(self.logits_v, self.tok[1:self.L].view(1, self.x), self.accept_len,
                      self.next_tok, self.argmax_v)
@@ -293,6 +308,7 @@ class GreedyDecoder:
         i32 = dict(dtype=torch.int32, device=device)
         self.toks = torch.zeros((max_new + 1,), **i32)
         self.toks[0] = prompt[-1]
+        self.i = 0  # tokens generated so far (generate() continues from there)
         self.ws = vc.Workspace(device)
         self.ws_proj = torch.zeros((vc.vc_project_workspace(1, 1, mdl.V) + 3) // 4, **i32)
 
@@ -303,8 +319,11 @@ class GreedyDecoder:
         torch.cuda.synchronize()
 
     def generate(self, steps: int):
+        """The next `steps` tokens."""
         mdl = self.m
-        for i in range(steps):
+        i0 = self.i
+        assert i0 + steps < self.toks.numel(), "max_new exhausted"
+        for i in range(i0, i0 + steps):
             x = mdl.embed(self.toks[i:i + 1], self.n)
             self.q[0, :, 0] = (mdl.Wq @ x).view(self.Hq, D)
             self.k1[0, :, 0] = (mdl.Wk @ x).view(self.Hkv, D)
@@ -319,7 +338,8 @@ class GreedyDecoder:
                                  ws=self.ws_proj)
             self.store.write(self.n, self.k1, self.v1)
             self.n += 1
-        return [int(t) for t in self.toks[1:steps + 1].tolist()]
+        self.i = i0 + steps
+        return [int(t) for t in self.toks[i0 + 1:i0 + steps + 1].tolist()]
 
 
 class LayeredDecoder:
