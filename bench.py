@@ -262,10 +262,12 @@ def _e2e_decode(torch, seed: int, context: int, tokens: int) -> dict:
     out = {"context": context, "tokens": tokens, "model": "one layer, d_model 256, 32/8 heads, d 128, "
            "vocab 2048, bf16 cache in pinned host memory, 64K-token chunks"}
     seqs = {}
-    for name in ("vericache", "greedy"):
+    # VeriCache with the verify's first two chunks prefetched under the draft phase, and without
+    for name in ("vericache", "vericache_no_prefetch", "greedy"):
         t0 = time.perf_counter()
-        if name == "vericache":
-            dec = TokenDecoder(W, Hq, Hkv, prompt, x=30, bits=4, R=128, max_new=tokens + 96, **opts)
+        if name != "greedy":
+            dec = TokenDecoder(W, Hq, Hkv, prompt, x=30, bits=4, R=128, max_new=tokens + 96,
+                               prefetch_verify=name == "vericache", **opts)
         else:
             dec = GreedyDecoder(W, Hq, Hkv, prompt, max_new=tokens + 8, **opts)
         torch.cuda.synchronize()
@@ -275,23 +277,26 @@ def _e2e_decode(torch, seed: int, context: int, tokens: int) -> dict:
         # costs (code-object loading, the GEMV library's set-up) of ~0.1 s
         warm = dec.generate(1) if name == "greedy" else (dec.draft_phase(), dec.verify_step(), dec.commit())[2]
         torch.cuda.synchronize()
-        rounds0 = len(dec.rounds) if name == "vericache" else 0
+        rounds0 = len(dec.rounds) if name != "greedy" else 0
         t0 = time.perf_counter()
         seqs[name] = warm + dec.generate(tokens)
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         # every token the timed rounds produced (the last round may run past `tokens`)
-        emitted = sum(a + 1 for a in dec.rounds[rounds0:]) if name == "vericache" else tokens
+        emitted = sum(a + 1 for a in dec.rounds[rounds0:]) if name != "greedy" else tokens
         out[name] = {"tok_s": round(emitted / el, 2), "emitted": emitted,
                      "ms_per_token": round(el / emitted * 1e3, 3), "prefill_s": round(t_prefill, 2),
                      "warmup_tokens": len(warm)}
-        if name == "vericache":
+        if name != "greedy":
             out[name]["accepted_per_round"] = dec.rounds[rounds0:]
         del dec
     out["speedup"] = round(out["vericache"]["tok_s"] / out["greedy"]["tok_s"], 3)
-    a, b = seqs["vericache"], seqs["greedy"]
-    m = min(len(a), len(b))  # the greedy run's warm-up token and timed tokens
-    out["first_divergence"] = next((i for i in range(m) if a[i] != b[i]), None)
+    out["prefetch_speedup"] = round(out["vericache"]["tok_s"] / out["vericache_no_prefetch"]["tok_s"], 3)
+    b = seqs["greedy"]
+    for name in ("vericache", "vericache_no_prefetch"):
+        a = seqs[name]
+        m = min(len(a), len(b))  # the greedy run's warm-up token and timed tokens
+        out[name]["first_divergence"] = next((i for i in range(m) if a[i] != b[i]), None)
 
     # two requests (the second prompt drawn after the first), lock-step against staggered
     # (harness.staggered_decode: one request's verify streams while the other drafts)

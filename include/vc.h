@@ -52,6 +52,9 @@ enum {
 
 enum { VC_F32 = 0, VC_F16 = 1, VC_BF16 = 2 };
 
+/* Where the verify's past lives (vc_verify_attn's past_on_host). */
+enum { VC_PAST_DEVICE = 0, VC_PAST_HOST = 1, VC_PAST_HOST_PREFETCHED = 2 };
+
 /*
  * One attention layer's KIVI cache ("VeriCache: Turning Lossy KV Cache into Lossless LLM
  * Inference", Key Contributions: KIVI is one of the quantising drafters; the compressor interface
@@ -170,9 +173,12 @@ vc_status vc_draft_drop_workspace(int32_t B, int32_t Hkv, int32_t Hq, int64_t n_
  *   q            [B][Hq][L][128] in dtype, device
  *   k_blk, v_blk [B][Hkv][L][128] in dtype, device (keys/values of positions n..n+L-1)
  *   k_past, v_past  element (b, h, t, c) at [((b*Hkv + h)*past_stride + t)*128 + c], dtype;
- *                device memory, or pinned host memory when past_on_host != 0 (then streamed in
- *                chunks of chunk_tokens tokens through the workspace, copies on `copy`, compute
- *                on `compute`; pageable host memory is rejected). past_stride >= n.
+ *                device memory (past_on_host = VC_PAST_DEVICE), or pinned host memory
+ *                (VC_PAST_HOST: streamed in chunks of chunk_tokens tokens through the workspace,
+ *                copies on `copy`, compute on `compute`; pageable host memory is rejected; or
+ *                VC_PAST_HOST_PREFETCHED: the same, with the first two chunks' copies already
+ *                issued by vc_verify_prefetch with identical past, sizes and workspace, which this
+ *                call consumes; VC_ERR_INVALID without a matching prefetch). past_stride >= n.
  *   out          [B][Hq][L][128] fp32; lse [B][Hq][L] fp32 or NULL
  *   dtype        VC_BF16 (matrix-core path) or VC_F32 (vector path; device-resident past only)
  *   1 <= L <= 32, n >= 0, Hq % Hkv == 0, Hq/Hkv <= 8; VC_BF16: at most 8388607 tokens per
@@ -186,6 +192,22 @@ vc_status vc_verify_attn(const void *q, const void *k_blk, const void *v_blk, in
                          int32_t past_on_host, int64_t chunk_tokens, int32_t dtype, int32_t B,
                          int32_t Hq, int32_t Hkv, float sm_scale, float *out, float *lse, void *ws,
                          size_t ws_bytes, void *compute_stream, void *copy_stream);
+/*
+ * Prefetch of a host-streamed verify ("VeriCache: making lossy KV compression exact", Verifying
+ * Without Giving Back the Speedup: the full cache is brought in from CPU memory only to verify; the
+ * committed past of a round is known before its drafts are, so its first chunks can cross the link
+ * while the draft steps run). Issues on `copy`, after the work already enqueued on `compute`, the
+ * host-to-device copies of the first two chunks of the past into the workspace's chunk stages,
+ * exactly as vc_verify_attn with VC_PAST_HOST would, and records (host side) that the workspace
+ * holds them. The next vc_verify_attn on this workspace with VC_PAST_HOST_PREFETCHED and the same
+ * k_past, v_past, past_stride, n, chunk_tokens, B, Hq, Hkv and L skips those copies; any other
+ * verify on the workspace discards the record. The caller must not write past rows < n, nor use
+ * the workspace for anything else, between the two calls, and must use the same copy stream.
+ * Arguments as for vc_verify_attn (VC_BF16 past in pinned host memory, n >= 1).
+ */
+vc_status vc_verify_prefetch(const void *k_past, const void *v_past, int64_t past_stride, int64_t n,
+                             int64_t chunk_tokens, int32_t B, int32_t Hq, int32_t Hkv, int32_t L,
+                             void *ws, size_t ws_bytes, void *compute_stream, void *copy_stream);
 vc_status vc_verify_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int64_t n,
                               int32_t past_on_host, int64_t chunk_tokens, int32_t dtype,
                               size_t *bytes);

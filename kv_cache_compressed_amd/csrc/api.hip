@@ -4,7 +4,9 @@
 // reason is kept in a thread-local string for vc_last_error(). No exception crosses the ABI.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -212,6 +214,79 @@ vc_status vc_verify_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int
   return ok();
 }
 
+namespace {
+
+// Prefetches issued by vc_verify_prefetch and not yet consumed, one per workspace.
+struct PendingPrefetch {
+  const void* ws;
+  const void* k;
+  const void* v;
+  int64_t stride, n, chunk;
+  int32_t B, Hq, Hkv, L;
+  bool operator==(const PendingPrefetch& o) const {
+    return ws == o.ws && k == o.k && v == o.v && stride == o.stride && n == o.n && chunk == o.chunk &&
+           B == o.B && Hq == o.Hq && Hkv == o.Hkv && L == o.L;
+  }
+};
+std::mutex g_prefetch_mu;
+std::vector<PendingPrefetch> g_prefetch;
+
+// Removes the record of workspace ws; returns whether it equalled `want` (when given).
+bool take_prefetch(const void* ws, const PendingPrefetch* want) {
+  std::lock_guard<std::mutex> lock(g_prefetch_mu);
+  for (size_t i = 0; i < g_prefetch.size(); ++i) {
+    if (g_prefetch[i].ws != ws) continue;
+    const bool match = want && g_prefetch[i] == *want;
+    g_prefetch.erase(g_prefetch.begin() + i);
+    return match;
+  }
+  return false;
+}
+
+vc_status check_pinned(const void* k_past, const void* v_past) {
+  for (const void* p : {k_past, v_past}) {
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      return fail(VC_ERR_INVALID, "past_on_host needs pinned host memory (hipHostMalloc); got pageable or device memory");
+    }
+  }
+  return VC_OK;
+}
+
+}  // namespace
+
+vc_status vc_verify_prefetch(const void* k_past, const void* v_past, int64_t past_stride, int64_t n,
+                             int64_t chunk_tokens, int32_t B, int32_t Hq, int32_t Hkv, int32_t L,
+                             void* ws, size_t ws_bytes, void* compute_stream, void* copy_stream) {
+  REQUIRE_PTR(k_past);
+  REQUIRE_PTR(v_past);
+  REQUIRE(L >= 1 && L <= 32, "L must be in [1, 32] (got %d)", L);
+  REQUIRE(n >= 1, "a host-streamed past needs n >= 1");
+  REQUIRE(past_stride >= n, "past_stride must be >= n");
+  REQUIRE(B >= 1 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv");
+  REQUIRE((int64_t)B * Hkv <= 65535, "B*Hkv must be <= 65535");
+  REQUIRE(chunk_tokens >= 32, "chunk_tokens must be >= 32 when streaming");
+  if (Hq / Hkv > 8) return fail(VC_ERR_UNSUPPORTED, "Hq/Hkv > 8 is not supported");
+  if (std::min<int64_t>(chunk_tokens, n) > (int64_t)8388607)
+    return fail(VC_ERR_UNSUPPORTED, "more than 8388607 past tokens per (b, kv head) in one chunk (use a smaller chunk_tokens)");
+  const vc_status pin = check_pinned(k_past, v_past);
+  if (pin != VC_OK) return pin;
+  const vc::VerifyPlan plan = vc::plan_verify(B, Hq, Hkv, L, n, 1, chunk_tokens, VC_BF16);
+  if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
+    return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,
+                ws ? ws_bytes : (size_t)0);
+  (void)take_prefetch(ws, nullptr);
+  hipError_t e = vc::launch_verify_prefetch(k_past, v_past, past_stride, n, B, Hkv, ws, plan,
+                                            static_cast<hipStream_t>(compute_stream),
+                                            static_cast<hipStream_t>(copy_stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_verify_prefetch");
+  std::lock_guard<std::mutex> lock(g_prefetch_mu);
+  g_prefetch.push_back({ws, k_past, v_past, past_stride, n, chunk_tokens, B, Hq, Hkv, L});
+  return ok();
+}
+
 vc_status vc_verify_attn(const void* q, const void* k_blk, const void* v_blk, int32_t L,
                          const void* k_past, const void* v_past, int64_t past_stride, int64_t n,
                          int32_t past_on_host, int64_t chunk_tokens, int32_t dtype, int32_t B,
@@ -244,22 +319,23 @@ vc_status vc_verify_attn(const void* q, const void* k_blk, const void* v_blk, in
       return fail(VC_ERR_UNSUPPORTED, "more than 8388607 past tokens per (b, kv head) in one %s",
                   past_on_host ? "chunk (use a smaller chunk_tokens)" : "device-resident past (stream it)");
   }
+  REQUIRE(past_on_host == VC_PAST_DEVICE || past_on_host == VC_PAST_HOST ||
+              past_on_host == VC_PAST_HOST_PREFETCHED,
+          "past_on_host must be VC_PAST_DEVICE, VC_PAST_HOST or VC_PAST_HOST_PREFETCHED");
   if (past_on_host) {
     REQUIRE(chunk_tokens >= 32, "chunk_tokens must be >= 32 when streaming");
     REQUIRE(n >= 1, "a host-streamed past needs n >= 1");
-    for (const void* p : {k_past, v_past}) {
-      hipPointerAttribute_t attr;
-      hipError_t e = hipPointerGetAttributes(&attr, p);
-      if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
-        (void)hipGetLastError();
-        return fail(VC_ERR_INVALID, "past_on_host needs pinned host memory (hipHostMalloc); got pageable or device memory");
-      }
-    }
+    const vc_status pin = check_pinned(k_past, v_past);
+    if (pin != VC_OK) return pin;
   }
   const vc::VerifyPlan plan = vc::plan_verify(B, Hq, Hkv, L, n, past_on_host, chunk_tokens, dtype);
   if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
     return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,
                 ws ? ws_bytes : (size_t)0);
+  // a verify on this workspace consumes (or, without VC_PAST_HOST_PREFETCHED, discards) its prefetch
+  const PendingPrefetch want{ws, k_past, v_past, past_stride, n, chunk_tokens, B, Hq, Hkv, L};
+  if (!take_prefetch(ws, &want) && past_on_host == VC_PAST_HOST_PREFETCHED)
+    return fail(VC_ERR_INVALID, "VC_PAST_HOST_PREFETCHED without a matching vc_verify_prefetch on this workspace");
   hipError_t e = vc::launch_verify(q, k_blk, v_blk, L, k_past, v_past, past_stride, n, past_on_host,
                                    dtype, B, Hq, Hkv, sm_scale, out, lse, ws, plan,
                                    static_cast<hipStream_t>(compute_stream),

@@ -61,6 +61,10 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
                          int past_on_host, int dtype, int B, int Hq, int Hkv, float sm_scale,
                          float* out, float* lse, void* ws, const VerifyPlan& plan,
                          hipStream_t compute, hipStream_t copy);
+// Copies of the first two streamed chunks into the workspace stages (past_on_host == 1 plan).
+hipError_t launch_verify_prefetch(const void* k_past, const void* v_past, int64_t past_stride,
+                                  int64_t n, int B, int Hkv, void* ws, const VerifyPlan& plan,
+                                  hipStream_t compute, hipStream_t copy);
 
 // Logits projection (+ argmax).
 struct ProjectPlan {

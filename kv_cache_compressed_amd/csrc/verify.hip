@@ -472,6 +472,55 @@ VerifyPlan plan_verify(int B, int Hq, int Hkv, int L, int64_t n, int past_on_hos
   return p;
 }
 
+namespace {
+
+// The two chunk stages behind the partials in the workspace: keys then values, [units][ct][128].
+void stage_pointers(void* ws, const VerifyPlan& plan, int64_t units, uint16_t** sk, uint16_t** sv) {
+  char* base = static_cast<char*>(ws) + plan.part_bytes;
+  for (int z = 0; z < 2; ++z) {
+    sk[z] = reinterpret_cast<uint16_t*>(base + z * plan.stage_bytes);
+    sv[z] = sk[z] + (size_t)units * plan.chunk_tokens * D;
+  }
+}
+
+// Host -> device copies of chunk c's keys and values (rows [c ct, min(n, (c + 1) ct)) of every
+// (b, kv head)) into one stage, on `copy`.
+hipError_t copy_chunk(const void* k_past, const void* v_past, int64_t past_stride, int64_t n,
+                      int64_t units, const VerifyPlan& plan, int c, uint16_t* sk, uint16_t* sv,
+                      hipStream_t copy) {
+  const int64_t t0 = (int64_t)c * plan.chunk_tokens;
+  const int64_t len = std::min<int64_t>(plan.chunk_tokens, n - t0);
+  const size_t src_pitch = (size_t)past_stride * D * 2;
+  const size_t width = (size_t)len * D * 2;
+  const size_t dpitch = (size_t)plan.chunk_tokens * D * 2;
+  hipError_t err = hipMemcpy2DAsync(sk, dpitch, static_cast<const char*>(k_past) + t0 * D * 2,
+                                    src_pitch, width, units, hipMemcpyHostToDevice, copy);
+  if (err == hipSuccess)
+    err = hipMemcpy2DAsync(sv, dpitch, static_cast<const char*>(v_past) + t0 * D * 2, src_pitch,
+                           width, units, hipMemcpyHostToDevice, copy);
+  return err;
+}
+
+}  // namespace
+
+hipError_t launch_verify_prefetch(const void* k_past, const void* v_past, int64_t past_stride,
+                                  int64_t n, int B, int Hkv, void* ws, const VerifyPlan& plan,
+                                  hipStream_t compute, hipStream_t copy) {
+  const int64_t units = (int64_t)B * Hkv;
+  uint16_t* stage_k[2];
+  uint16_t* stage_v[2];
+  stage_pointers(ws, plan, units, stage_k, stage_v);
+  hipEvent_t start;
+  if (hipEventCreateWithFlags(&start, hipEventDisableTiming) != hipSuccess) return hipErrorOutOfMemory;
+  // the stages are free once the work already on `compute` (earlier verifies) has run
+  hipError_t err = hipEventRecord(start, compute);
+  if (err == hipSuccess) err = hipStreamWaitEvent(copy, start, 0);
+  for (int c = 0; c < std::min(2, plan.chunks) && err == hipSuccess; ++c)
+    err = copy_chunk(k_past, v_past, past_stride, n, units, plan, c, stage_k[c], stage_v[c], copy);
+  (void)hipEventDestroy(start);
+  return err;
+}
+
 hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, int L,
                          const void* k_past, const void* v_past, int64_t past_stride, int64_t n,
                          int past_on_host, int dtype, int B, int Hq, int Hkv, float sm_scale,
@@ -546,13 +595,11 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
     return launch_merge(part_o, part_ml, (int64_t)rows, plan.total_splits, out, lse, compute);
   } else {
     // Stream the past chunk by chunk: copies on `copy` into stage c % 2, compute on `compute`.
-    char* stage_base = static_cast<char*>(ws) + plan.part_bytes;
+    // With a prefetch (past_on_host == 2) the first two chunks' copies are already on `copy`.
+    const int first = past_on_host == 2 ? std::min(2, plan.chunks) : 0;
     uint16_t* stage_k[2];
     uint16_t* stage_v[2];
-    for (int z = 0; z < 2; ++z) {
-      stage_k[z] = reinterpret_cast<uint16_t*>(stage_base + z * plan.stage_bytes);
-      stage_v[z] = stage_k[z] + (size_t)units * plan.chunk_tokens * D;
-    }
+    stage_pointers(ws, plan, units, stage_k, stage_v);
     hipEvent_t ready[2], done[2], start;
     bool made = true;
     for (int z = 0; z < 2 && made; ++z) {
@@ -564,23 +611,21 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
     // the copy stream must not overwrite stages before earlier work on `compute` is ordered
     err = hipEventRecord(start, compute);
     if (err == hipSuccess) err = hipStreamWaitEvent(copy, start, 0);
-    const size_t src_pitch = (size_t)past_stride * D * 2;
+    // prefetched chunks: `compute` waits for everything on `copy` so far
+    if (first > 0 && err == hipSuccess) err = hipEventRecord(ready[0], copy);
+    if (first > 0 && err == hipSuccess) err = hipStreamWaitEvent(compute, ready[0], 0);
     for (int c = 0; c < plan.chunks && err == hipSuccess; ++c) {
       const int z = c % 2;
       const int64_t t0 = (int64_t)c * plan.chunk_tokens;
       const int64_t len = std::min<int64_t>(plan.chunk_tokens, n - t0);
-      if (c >= 2) err = hipStreamWaitEvent(copy, done[z], 0);
-      const size_t width = (size_t)len * D * 2;
-      const size_t dpitch = (size_t)plan.chunk_tokens * D * 2;
-      if (err == hipSuccess)
-        err = hipMemcpy2DAsync(stage_k[z], dpitch, static_cast<const char*>(k_past) + t0 * D * 2,
-                               src_pitch, width, units, hipMemcpyHostToDevice, copy);
-      if (err == hipSuccess)
-        err = hipMemcpy2DAsync(stage_v[z], dpitch, static_cast<const char*>(v_past) + t0 * D * 2,
-                               src_pitch, width, units, hipMemcpyHostToDevice, copy);
-      if (err == hipSuccess) err = hipEventRecord(ready[z], copy);
-      if (err == hipSuccess) err = hipStreamWaitEvent(compute, ready[z], 0);
-      if (err != hipSuccess) break;
+      if (c >= first) {
+        if (c >= 2) err = hipStreamWaitEvent(copy, done[z], 0);
+        if (err == hipSuccess)
+          err = copy_chunk(k_past, v_past, past_stride, n, units, plan, c, stage_k[z], stage_v[z], copy);
+        if (err == hipSuccess) err = hipEventRecord(ready[z], copy);
+        if (err == hipSuccess) err = hipStreamWaitEvent(compute, ready[z], 0);
+        if (err != hipSuccess) break;
+      }
       a.k = stage_k[z];
       a.v = stage_v[z];
       a.bh_stride = plan.chunk_tokens;

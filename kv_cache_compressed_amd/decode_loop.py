@@ -118,11 +118,13 @@ class TokenDecoder:
     """weights: dict of fp32 arrays or device tensors E [V, dm], P [max_pos, dm], Wq [Hq*128, dm],
     Wk/Wv [Hkv*128, dm], Wo [dm, Hq*128], Wlm [V, dm]; dm a multiple of 128. kv_dtype "f32" or
     "bf16"; host_past (bf16 only): the full cache in pinned host memory, streamed by every verify in
-    chunks of chunk_tokens on copy_stream."""
+    chunks of chunk_tokens on copy_stream; prefetch_verify: each round's draft phase first issues
+    the copies of the verify's first two chunks (vc_verify_prefetch)."""
 
     def __init__(self, weights, Hq: int, Hkv: int, prompt, x: int, bits: int = 4, R: int = 32,
                  max_new: int = 256, kv_dtype: str = "f32", host_past: bool = False,
-                 chunk_tokens: int = 65536, copy_stream=None, device: str = "cuda"):
+                 chunk_tokens: int = 65536, copy_stream=None, prefetch_verify: bool = True,
+                 device: str = "cuda"):
         mdl = self.m = _Model(weights, Hq, Hkv, kv_dtype, device)
         assert not host_past or kv_dtype == "bf16", "a host-streamed cache is bf16"
         f32 = dict(dtype=torch.float32, device=device)
@@ -130,6 +132,7 @@ class TokenDecoder:
         self.Hq, self.Hkv, self.x, self.L, self.R = Hq, Hkv, x, x + 1, R
         self.host, self.chunk = host_past, chunk_tokens
         self.copy_stream = (copy_stream or torch.cuda.Stream()) if host_past else None
+        self.prefetch_verify, self._prefetched = prefetch_verify, None
         prompt = [int(t) for t in prompt]
         assert len(prompt) >= 2
         self.n = len(prompt) - 1  # cached positions: every prompt token but the last
@@ -230,9 +233,13 @@ class TokenDecoder:
         self.v_blk[0].copy_(y[:, Hq + Hkv:].transpose(0, 1))
         nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, self.n, self.host, self.chunk,
                                     self.m.vdt)
+        mode = int(self.host)
+        if self.host and self._prefetched == self.n:
+            mode = vc.VC_PAST_HOST_PREFETCHED
+        self._prefetched = None
         vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.store.k, self.store.v, self.n,
                           self.ov, self.lse_v, self.ws_verify.get(nb), SM_SCALE,
-                          past_stride=self.cap, past_on_host=self.host, chunk_tokens=self.chunk,
+                          past_stride=self.cap, past_on_host=mode, chunk_tokens=self.chunk,
                           copy_stream=self.copy_stream)
         self.ov[0, self.Hq:] = self.odx[:, self.Hq:].transpose(0, 1)
         vc.vc_project_logits(self.m.Wp, self.ov, logits=self.logits_v)
@@ -260,7 +267,21 @@ class TokenDecoder:
         self.rounds.append(a)
         return emitted
 
+    def prefetch(self):
+        """Host-streamed cache: issue the copies of this round's first two verify chunks now (the
+        committed past is fixed for the round), so they cross the link while the draft steps run;
+        the round's verify_step then skips them."""
+        if not self.host:
+            return
+        nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, self.n, True, self.chunk, self.m.vdt)
+        vc.vc_verify_prefetch(self.store.k, self.store.v, self.n, self.ws_verify.get(nb), 1, self.Hq,
+                              self.Hkv, self.L, self.chunk, past_stride=self.cap,
+                              copy_stream=self.copy_stream)
+        self._prefetched = self.n
+
     def draft_phase(self):
+        if self.prefetch_verify:
+            self.prefetch()
         for j in range(self.x):
             self.draft_step(j)
 

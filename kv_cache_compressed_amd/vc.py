@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "vc.h")
 
 VC_OK, VC_ERR_INVALID, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_HIP = 0, 1, 2, 3, 4
 VC_F32, VC_F16, VC_BF16 = 0, 1, 2
+VC_PAST_DEVICE, VC_PAST_HOST, VC_PAST_HOST_PREFETCHED = 0, 1, 2
 _TORCH_DT = {torch.float32: VC_F32, torch.float16: VC_F16, torch.bfloat16: VC_BF16}
 
 _lib = None
@@ -53,6 +54,7 @@ _SIGS = {
     "vc_verify_attn": [_P, _P, _P, _I32, _P, _P, _I64, _I64, _I32, _I64, _I32, _I32, _I32, _I32, _F,
                        _P, _P, _P, _SZ, _P, _P],
     "vc_verify_workspace": [_I32, _I32, _I32, _I32, _I64, _I32, _I64, _I32, ctypes.POINTER(_SZ)],
+    "vc_verify_prefetch": [_P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P],
     "vc_lse_merge": [_P, _P, _I64, _I32, _I32, _P, _P, _P],
     "vc_accept": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
     "vc_project_workspace": [_I32, _I32, _I32, ctypes.POINTER(_SZ)],
@@ -229,10 +231,22 @@ def vc_verify_workspace(B, Hq, Hkv, L, n, past_on_host, chunk_tokens, dtype) -> 
     return nb.value
 
 
+def vc_verify_prefetch(k_past, v_past, n: int, ws: torch.Tensor, B: int, Hq: int, Hkv: int, L: int,
+                       chunk_tokens: int, past_stride: int | None = None, stream=None, copy_stream=None):
+    """Issue the first two streamed chunks' copies of a later vc_verify_attn(...,
+    past_on_host=VC_PAST_HOST_PREFETCHED) with the same past, sizes and workspace."""
+    stride = k_past.shape[2] if past_stride is None else past_stride
+    comp = _stream(stream)
+    cp = _stream(copy_stream) if copy_stream is not None else comp
+    _check(lib().vc_verify_prefetch(_ptr(k_past), _ptr(v_past), stride, n, chunk_tokens, B, Hq, Hkv, L,
+                                    _ptr(ws), ws.numel() * ws.element_size(), comp, cp))
+
+
 def vc_verify_attn(q, k_blk, v_blk, k_past, v_past, n: int, out, lse, ws: torch.Tensor,
-                   sm_scale: float, past_stride: int | None = None, past_on_host: bool = False,
+                   sm_scale: float, past_stride: int | None = None, past_on_host: int = VC_PAST_DEVICE,
                    chunk_tokens: int = 0, stream=None, copy_stream=None):
-    """q [B, Hq, L, 128]; k_blk/v_blk [B, Hkv, L, 128]; k_past/v_past [B, Hkv, >=n, 128]."""
+    """q [B, Hq, L, 128]; k_blk/v_blk [B, Hkv, L, 128]; k_past/v_past [B, Hkv, >=n, 128].
+    past_on_host: VC_PAST_DEVICE (or False), VC_PAST_HOST (or True), VC_PAST_HOST_PREFETCHED."""
     B, Hq, L, _ = q.shape
     Hkv = k_blk.shape[1]
     stride = k_past.shape[2] if past_stride is None else past_stride

@@ -133,6 +133,23 @@ def test_verify_rejects(L):
     # one bf16 source per (b, kv head) is limited to 8388607 tokens (256 B each, 32-bit buffer range)
     assert call(n=8388608, stride=8388608) == vc.VC_ERR_UNSUPPORTED and "resident" in _err(L)
     assert call(n=8388608, stride=8388608, host=1, chunk=8388608) == vc.VC_ERR_UNSUPPORTED
+    assert call(host=3, chunk=1024) == vc.VC_ERR_INVALID and "past_on_host must be" in _err(L)
+
+
+def test_verify_prefetch_rejects(L):
+    """Argument checks of the prefetch (all before any HIP call)."""
+    call = lambda **a: L.vc_verify_prefetch(
+        a.get("kp", P), P, a.get("stride", 4096), a.get("n", 4000), a.get("chunk", 1024), 2,
+        a.get("Hq", 8), 2, a.get("L", 31), P, 1 << 34, None, None)
+    assert call(L=0) == vc.VC_ERR_INVALID
+    assert call(L=33) == vc.VC_ERR_INVALID and "L must be" in _err(L)
+    assert call(n=0) == vc.VC_ERR_INVALID and "n >= 1" in _err(L)
+    assert call(stride=100) == vc.VC_ERR_INVALID
+    assert call(kp=0) == vc.VC_ERR_INVALID
+    assert call(chunk=16) == vc.VC_ERR_INVALID
+    assert call(Hq=5) == vc.VC_ERR_INVALID
+    assert call(Hq=18) == vc.VC_ERR_UNSUPPORTED
+    assert call(n=8388608, stride=8388608, chunk=8388608) == vc.VC_ERR_UNSUPPORTED
 
 
 def test_merge_and_accept_reject(L):

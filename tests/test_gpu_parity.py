@@ -537,6 +537,67 @@ def test_pageable_host_past_is_rejected(gpu_lib):
     assert e.value.status == vc.VC_ERR_INVALID
 
 
+@pytest.mark.parametrize("n,chunk", [(700, 1024), (1500, 1024), (5000, 1024), (4096, 1024)])
+def test_verify_prefetch_equals_streamed(gpu_lib, n, chunk):
+    """A verify whose first two chunks were prefetched (with other work queued on the compute stream
+    in between, as the draft steps are) gives bit-identical outputs to the plain host-streamed
+    verify, which matches the oracle's verify attention (sampled heads). Mismatched or missing
+    prefetches are rejected before anything is enqueued."""
+    g = np.random.default_rng(n + chunk)
+    B, Hq, Hkv, L = 1, 32, 8, 31
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    Kp = bf(g.standard_normal((B, Hkv, n, 128)))
+    Vp = bf(g.standard_normal((B, Hkv, n, 128)))
+    hk, hv = Kp.pin_memory(), Vp.pin_memory()
+    q = bf(g.standard_normal((B, Hq, L, 128))).cuda()
+    kb = bf(g.standard_normal((B, Hkv, L, 128))).cuda()
+    vb = bf(g.standard_normal((B, Hkv, L, 128))).cuda()
+    copy = torch.cuda.Stream()
+    nb = vc.vc_verify_workspace(B, Hq, Hkv, L, n, True, chunk, vc.VC_BF16)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    outs = []
+    for mode in (vc.VC_PAST_HOST, vc.VC_PAST_HOST_PREFETCHED):
+        out = torch.full((B, Hq, L, 128), float("nan"), device="cuda")
+        lse = torch.full((B, Hq, L), float("nan"), device="cuda")
+        if mode == vc.VC_PAST_HOST_PREFETCHED:
+            vc.vc_verify_prefetch(hk, hv, n, ws, B, Hq, Hkv, L, chunk, copy_stream=copy)
+            a = torch.randn(2048, 2048, device="cuda")
+            for _ in range(4):
+                a = a @ a / 64.0            # compute-stream work between prefetch and verify
+        vc.vc_verify_attn(q, kb, vb, hk, hv, n, out, lse, ws, harness.SM_SCALE, past_on_host=mode,
+                          chunk_tokens=chunk, copy_stream=copy)
+        torch.cuda.synchronize()
+        outs.append((out.cpu(), lse.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    # the oracle's verify attention for a few query heads
+    Kf, Vf = Kp.float().numpy(), Vp.float().numpy()
+    qf, kf, vf = q.float().cpu().numpy(), kb.float().cpu().numpy(), vb.float().cpu().numpy()
+    for h in (0, 13, 31):
+        kvh = h // (Hq // Hkv)
+        O, _ = oatt.verify_block(qf[0, h], Kf[0, kvh], Vf[0, kvh], kf[0, kvh], vf[0, kvh])
+        _close(outs[1][0][0, h].numpy(), O, True, TIGHT["verify"], f"prefetched h={h}")
+
+    def expect_invalid(fn):
+        with pytest.raises(vc.VcError) as e:
+            fn()
+        assert e.value.status == vc.VC_ERR_INVALID
+
+    out = torch.zeros((B, Hq, L, 128), device="cuda")
+    verify_pf = lambda m: vc.vc_verify_attn(q, kb, vb, hk, hv, m, out, None, ws, harness.SM_SCALE,
+                                            past_on_host=vc.VC_PAST_HOST_PREFETCHED, chunk_tokens=chunk,
+                                            copy_stream=copy)
+    expect_invalid(lambda: verify_pf(n))                  # nothing prefetched (the last was consumed)
+    vc.vc_verify_prefetch(hk, hv, n, ws, B, Hq, Hkv, L, chunk, copy_stream=copy)
+    expect_invalid(lambda: verify_pf(n - 1))              # a different n: rejected, record dropped
+    expect_invalid(lambda: verify_pf(n))
+    vc.vc_verify_prefetch(hk, hv, n, ws, B, Hq, Hkv, L, chunk, copy_stream=copy)
+    vc.vc_verify_attn(q, kb, vb, hk, hv, n, out, None, ws, harness.SM_SCALE, past_on_host=True,
+                      chunk_tokens=chunk, copy_stream=copy)  # a plain verify discards the record
+    expect_invalid(lambda: verify_pf(n))
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), outs[0][0])
+
+
 # ------------------------------------------------------------------------------------------
 # whole rounds: emitted tokens
 # ------------------------------------------------------------------------------------------
