@@ -148,33 +148,47 @@ def _staggering(torch, harness, synth, st0, seed: int, rounds: int) -> dict:
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
-    timed(lambda: harness.lockstep(groups, 1))          # warm-up (workspaces sized)
-    timed(lambda: harness.staggered(groups, streams, 1))
-    t_draft = np.median([timed(st0.draft_phase) for _ in range(3)])
-    t_verify = np.median([timed(st0.verify_step) for _ in range(3)])
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    st0.verify_attention()  # host time to enqueue one host-streamed verify (copies included?)
-    t_enq = time.perf_counter() - t0
-    torch.cuda.synchronize()
-    t_lock = timed(lambda: harness.lockstep(groups, rounds)) / rounds
-    t_stag = timed(lambda: harness.staggered(groups, streams, rounds)) / rounds
-    res = [g.results() for g in groups]
-    emitted = int(sum((r["a"] + 1).sum() for r in res))
-    return {"groups": 2, "requests_per_group": w.B, "rounds": rounds,
-            "draft_phase_ms": round(t_draft * 1e3, 3), "verify_ms": round(t_verify * 1e3, 3),
-            "lockstep_ms_per_round": round(t_lock * 1e3, 3),
-            "staggered_ms_per_round": round(t_stag * 1e3, 3),
-            "link_bound_ms_per_round": round((t_draft + 2 * rounds * t_verify) / rounds * 1e3, 3),
-            "speedup": round(t_lock / t_stag, 4),
-            "verify_enqueue_host_ms": round(t_enq * 1e3, 3),
-            "draft_time_hidden_frac": round((t_lock - t_stag) / (2 * t_draft), 4),
-            "tok_s_lockstep": round(emitted / t_lock, 3),
-            "tok_s_staggered": round(emitted / t_stag, 3),
-            "note": "per round both groups draft 30 steps and verify 31 rows over their 500K-token "
-                    "pinned-host KV; times from host clocks around synchronised schedules; "
-                    "link_bound = the first draft phase plus back-to-back verifies (the host link "
-                    "never idle afterwards)"}
+    def measure(prefetch: bool) -> dict:
+        for g in groups:
+            g.prefetch_verify = prefetch
+        timed(lambda: harness.lockstep(groups, 1))          # warm-up (workspaces sized)
+        timed(lambda: harness.staggered(groups, streams, 1))
+        out = {}
+        if not prefetch:  # the phases on their own
+            out["draft_phase_ms"] = round(np.median([timed(st0.draft_phase) for _ in range(3)]) * 1e3, 3)
+            out["verify_ms"] = round(np.median([timed(st0.verify_step) for _ in range(3)]) * 1e3, 3)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            st0.verify_attention()  # host time to enqueue one host-streamed verify
+            out["verify_enqueue_host_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
+            torch.cuda.synchronize()
+        t_lock = timed(lambda: harness.lockstep(groups, rounds)) / rounds
+        t_stag = timed(lambda: harness.staggered(groups, streams, rounds)) / rounds
+        res = [g.results() for g in groups]
+        emitted = int(sum((r["a"] + 1).sum() for r in res))
+        out.update({"lockstep_ms_per_round": round(t_lock * 1e3, 3),
+                    "staggered_ms_per_round": round(t_stag * 1e3, 3),
+                    "speedup": round(t_lock / t_stag, 4),
+                    "tok_s_lockstep": round(emitted / t_lock, 3),
+                    "tok_s_staggered": round(emitted / t_stag, 3)})
+        return out
+
+    # staggering on its own (every verify streams all its chunks), then with each round's first
+    # two verify chunks prefetched under its own draft phase
+    out = {"groups": 2, "requests_per_group": w.B, "rounds": rounds}
+    out.update(measure(False))
+    out["link_bound_ms_per_round"] = round(out["draft_phase_ms"] / rounds + 2 * out["verify_ms"], 3)
+    out["draft_time_hidden_frac"] = round((out["lockstep_ms_per_round"] - out["staggered_ms_per_round"])
+                                          / (2 * out["draft_phase_ms"]), 4)
+    out["with_prefetch"] = measure(True)
+    out["note"] = ("per round both groups draft 30 steps and verify 31 rows over their 500K-token "
+                   "pinned-host KV; times from host clocks around synchronised schedules; "
+                   "link_bound = the first draft phase plus back-to-back verifies (the host link "
+                   "never idle afterwards); with_prefetch: every round's draft phase first issues "
+                   "its verify's first two chunk copies")
+    for g in groups:
+        g.prefetch_verify = True
+    return out
 
 
 def _decode_loop(torch, harness, synth, w, seed: int, rounds: int) -> dict:

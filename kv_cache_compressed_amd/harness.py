@@ -132,6 +132,8 @@ class RoundState:
         self.copy_stream = None
         if w.past_on_host:
             self.copy_stream = copy_stream or torch.cuda.Stream(device=device)
+        # host-streamed rounds: issue the verify's first two chunk copies when the round starts
+        self.prefetch_verify, self._prefetched = bool(w.past_on_host), None
         # projection workspace (draft argmax tickets); zero-filled once, calls leave it zero
         self.ws_proj = torch.zeros((vc.vc_project_workspace(B, 1, w.vocab) + 3) // 4, **i32)
         self._rep = 0
@@ -194,16 +196,32 @@ class RoundState:
         self.draft_attention(j, c)
         self.draft_tokens(j)
 
-    def verify_attention(self):
+    def _verify_ws(self):
         w = self.w
         if self.n != w.n:  # a multi-round decode has grown the context
             self.verify_ws_bytes = vc.vc_verify_workspace(w.B, w.Hq, w.Hkv, w.L, self.n, w.past_on_host,
                                                           w.chunk_tokens, self._vdt())
-        ws = self.ws_verify.get(self.verify_ws_bytes)
+        return self.ws_verify.get(self.verify_ws_bytes)
+
+    def prefetch(self):
+        """Host-streamed past: the copies of this round's first two verify chunks, issued now (the
+        committed past is fixed before the drafts exist) so they cross the link under the draft
+        steps; the round's verify skips them."""
+        w = self.w
+        vc.vc_verify_prefetch(self.k_host, self.v_host, self.n, self._verify_ws(), w.B, w.Hq, w.Hkv,
+                              w.L, w.chunk_tokens, past_stride=self.host_cap,
+                              copy_stream=self.copy_stream)
+        self._prefetched = self.n
+
+    def verify_attention(self):
+        w = self.w
+        ws = self._verify_ws()
         if w.past_on_host:
+            mode = vc.VC_PAST_HOST_PREFETCHED if self._prefetched == self.n else vc.VC_PAST_HOST
+            self._prefetched = None
             vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.k_host, self.v_host, self.n,
                               self.out_v, self.lse_v, ws, SM_SCALE, past_stride=self.host_cap,
-                              past_on_host=True, chunk_tokens=w.chunk_tokens,
+                              past_on_host=mode, chunk_tokens=w.chunk_tokens,
                               copy_stream=self.copy_stream)
         else:
             vc.vc_verify_attn(self.q_verify, self.k_blk, self.v_blk, self.k_store, self.v_store, self.n,
@@ -282,6 +300,8 @@ class RoundState:
     def draft_phase(self):
         """The x draft steps of one round (attention with the step's append fused in, then the
         logits and greedy token), rotating over the compressed-cache replicas."""
+        if self.prefetch_verify:
+            self.prefetch()
         for j in range(self.w.x):
             self.draft_step(j)
 
@@ -290,6 +310,8 @@ class RoundState:
         {"draft", "verify"} right before (start=True) and after (start=False) each attention
         launch, on the host thread that enqueues them (for event timing on the current stream)."""
         w = self.w
+        if self.prefetch_verify:
+            self.prefetch()
         for j in range(w.x):
             c = None
             if self.replicas:
