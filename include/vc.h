@@ -13,6 +13,7 @@
  *   vc_draft_attn_quant  one-query decode attention over the quantised cache  (draft)
  *   vc_draft_attn_drop   one-query decode attention over kept positions       (draft)
  *   vc_verify_attn       L-query causal block attention over the full cache   (verify)
+ *   vc_verify_prefetch   first chunk copies of a host-streamed verify, issued early (verify)
  *   vc_lse_merge         log-sum-exp merge of split partials                  (verify / draft)
  *   vc_accept            per-row argmax, first disagreement, correction token (accept)
  *   vc_select_keep       kept positions of a token-dropping drafter           (compressor)
@@ -23,7 +24,8 @@
  *   - Every buffer is owned by the caller. Device pointers are HIP device memory; the library
  *     allocates nothing and keeps no pointer after the stream work ends.
  *   - Calls are asynchronous on the given stream (a hipStream_t passed as void*, NULL = the
- *     default stream) and re-entrant; there is no mutable global state.
+ *     default stream) and re-entrant; the only mutable global state is the host-side record of
+ *     pending vc_verify_prefetch calls (one per workspace, behind a mutex).
  *   - Every argument is checked on the host before anything is enqueued; on any error nothing is
  *     enqueued and a status != VC_OK is returned, with a detail string in vc_last_error()
  *     (thread-local). HIP runtime failures return VC_ERR_HIP. No C++ exception crosses the ABI.
