@@ -228,3 +228,98 @@ def greedy_layered(model, prompt, steps):
         out.append(t)
         toks.append(t)
     return out
+
+
+# ---- a Llama-style layer stack (norms, rotary positions, gated MLP) ---------------------------
+# The pages evaluate Llama-, Mistral- and Qwen-family models ("VeriCache: Turning Lossy KV Cache
+# into Lossless LLM Inference", Results) without describing their layers; the layer below is the
+# published Llama form (pre-norm RMSNorm, rotary position embedding on queries and keys, SwiGLU
+# MLP, a final RMSNorm before the output head). Reading: keys are cached after the rotation, as a
+# KV cache of such a model holds them; the rotation pairs channel i with channel i + d/2.
+
+def rms_norm(X, g, eps=1e-5):
+    """Each row of X divided by its root mean square (eps inside the root), times the gain g."""
+    X = np.asarray(X, np.float64)
+    return X / np.sqrt(np.mean(X * X, axis=-1, keepdims=True) + eps) * g
+
+
+def rope(X, pos, theta=500000.0):
+    """Rotary position embedding of rows X [..., d] at positions pos (broadcast over the leading
+    axes): channel pair (i, i + d/2) is turned by the angle pos * theta^(-2i/d)."""
+    X = np.asarray(X, np.float64)
+    half = X.shape[-1] // 2
+    ang = np.asarray(pos, np.float64)[..., None] * theta ** (-2.0 * np.arange(half) / X.shape[-1])
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = X[..., :half], X[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def silu(X):
+    return X / (1.0 + np.exp(-X))
+
+
+class LlamaModel:
+    """`layers` pre-norm blocks on the residual stream: x_0 = E[tok];
+    h = rms_norm(x_l) g_att_l; q, k = rope(Wq_l h), rope(Wk_l h) at the row's position; v = Wv_l h;
+    x' = x_l + Wo_l attention(q; k, v of positions 0..p);
+    x_{l+1} = x' + W2_l (silu(W1_l h') * (W3_l h')) with h' = rms_norm(x') g_mlp_l;
+    logits = Wlm rms_norm(x_L) g_f. kv_bf16 rounds q, k (after the rotation) and v to bfloat16.
+    Gains are drawn near 1, projections at the scales of LayeredModel, the MLP width F."""
+
+    def __init__(self, seed=0, vocab=11, dm=16, d=8, Hq=4, Hkv=2, layers=2, F=32, kv_bf16=False,
+                 theta=500000.0):
+        g = np.random.default_rng(seed)
+        self.V, self.dm, self.d, self.Hq, self.Hkv, self.nl, self.F = vocab, dm, d, Hq, Hkv, layers, F
+        self.kv_bf16, self.theta = kv_bf16, theta
+        self.E = g.standard_normal((vocab, dm))
+        gain = lambda: 1.0 + 0.1 * g.standard_normal(dm)
+        self.g_att, self.Wq, self.Wk, self.Wv, self.Wo = [], [], [], [], []
+        self.g_mlp, self.W1, self.W3, self.W2 = [], [], [], []
+        for _ in range(layers):
+            self.g_att.append(gain())
+            self.Wq.append(g.standard_normal((Hq * d, dm)) / np.sqrt(dm))
+            self.Wk.append(g.standard_normal((Hkv * d, dm)) / np.sqrt(dm))
+            self.Wv.append(g.standard_normal((Hkv * d, dm)) / np.sqrt(dm))
+            self.Wo.append(g.standard_normal((dm, Hq * d)) / np.sqrt(Hq * d) / np.sqrt(layers))
+            self.g_mlp.append(gain())
+            self.W1.append(g.standard_normal((F, dm)) / np.sqrt(dm))
+            self.W3.append(g.standard_normal((F, dm)) / np.sqrt(dm))
+            self.W2.append(g.standard_normal((dm, F)) / np.sqrt(F) / np.sqrt(layers))
+        self.g_f = gain()
+        self.Wlm = 3.0 * g.standard_normal((vocab, dm)) / np.sqrt(dm)
+        self.scale = 1.0 / np.sqrt(d)
+
+    def _r(self, a):
+        return bf16(a) if self.kv_bf16 else a
+
+    def logits_all(self, tokens, pos0=0):
+        """Causal forward over every position of `tokens` (the first at position pos0): logits
+        [len, V] (float64)."""
+        n = len(tokens)
+        X = self.E[np.asarray(tokens)].copy()
+        pos = pos0 + np.arange(n)
+        G = self.Hq // self.Hkv
+        for l in range(self.nl):
+            H = rms_norm(X, self.g_att[l])
+            Q = self._r(rope((H @ self.Wq[l].T).reshape(n, self.Hq, self.d), pos[:, None], self.theta))
+            K = self._r(rope((H @ self.Wk[l].T).reshape(n, self.Hkv, self.d), pos[:, None], self.theta))
+            Vv = self._r((H @ self.Wv[l].T).reshape(n, self.Hkv, self.d))
+            O = np.zeros((n, self.Hq, self.d))
+            for p in range(n):
+                for h in range(self.Hq):
+                    O[p, h] = decode(Q[p, h], K[: p + 1, h // G], Vv[: p + 1, h // G], self.scale)[0]
+            X = X + O.reshape(n, -1) @ self.Wo[l].T
+            H2 = rms_norm(X, self.g_mlp[l])
+            X = X + (silu(H2 @ self.W1[l].T) * (H2 @ self.W3[l].T)) @ self.W2[l].T
+        return rms_norm(X, self.g_f) @ self.Wlm.T
+
+
+def greedy_llama(model, prompt, steps):
+    """Plain greedy decoding over the full cache of a LlamaModel."""
+    toks = list(prompt)
+    out = []
+    while len(out) < steps:
+        t = int(np.argmax(model.logits_all(toks)[-1]))
+        out.append(t)
+        toks.append(t)
+    return out
