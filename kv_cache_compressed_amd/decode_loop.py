@@ -364,25 +364,37 @@ class GreedyDecoder:
 
 
 class LayeredDecoder:
-    """VeriCache decoding of one request on a stack of attention layers on the residual stream
-    (x_{l+1} = x_l + Wo_l attention_l(x_l), logits = Wlm x_L). weights: E, P, Wlm as for
-    TokenDecoder and per-layer lists Wq, Wk, Wv, Wo. Every layer has its own full cache (HBM or
-    pinned host memory) and KIVI cache. Draft steps thread the residual stream through every
-    layer's draft attention over the compressed caches; the verify runs every layer over the full
-    caches for all x + 1 entries. Above the first layer the drafter's keys/values of its own
-    positions differ from the verifier's (their inputs went through compressed attention), so the
-    commit writes the verifier's keys/values of the kept positions into the full caches and over
-    the draft-time entries of the residual rings."""
+    """VeriCache decoding of one request on a stack of layers on the residual stream. Two layer
+    forms: attention only (x_{l+1} = x_l + Wo_l attention_l(x_l), logits = Wlm x_L; weights E, P,
+    Wlm as for TokenDecoder and per-layer lists Wq, Wk, Wv, Wo), or the Llama form when the
+    weights hold per-layer gains g_att, g_mlp, MLP matrices W1, W3 [F, dm], W2 [dm, F] and a final
+    gain g_f (pre-norm RMSNorm, rotary positions on q and k with theta `rope_theta`, channel i
+    paired with i + 64, SwiGLU MLP, final RMSNorm; no position table). Every layer has its own
+    full cache (HBM or pinned host memory) and KIVI cache; keys are cached after the rotation.
+    Draft steps thread the residual stream through every layer's draft attention over the
+    compressed caches; the verify runs every layer over the full caches for all x + 1 entries.
+    Above the first layer the drafter's keys/values of its own positions differ from the
+    verifier's (their inputs went through compressed attention), so the commit writes the
+    verifier's keys/values of the kept positions into the full caches and over the draft-time
+    entries of the residual rings. Norms, rotations, MLPs and the q/k/v/o GEMMs are fp32 PyTorch
+    ops; attention, quantisation, appends, logits and accept are libvc calls."""
 
     def __init__(self, weights, Hq: int, Hkv: int, prompt, x: int, bits: int = 4, R: int = 32,
                  max_new: int = 256, kv_dtype: str = "f32", host_past: bool = False,
-                 chunk_tokens: int = 65536, device: str = "cuda"):
-        self.E, self.P = _dev(weights["E"], device), _dev(weights["P"], device)
+                 chunk_tokens: int = 65536, rope_theta: float = 500000.0, device: str = "cuda"):
+        self.llama = "g_att" in weights
+        self.E = _dev(weights["E"], device)
+        self.P = None if self.llama else _dev(weights["P"], device)
         self.Wlm = _dev(weights["Wlm"], device)
         self.Wq = [_dev(w, device) for w in weights["Wq"]]
         self.Wk = [_dev(w, device) for w in weights["Wk"]]
         self.Wv = [_dev(w, device) for w in weights["Wv"]]
         self.Wo = [_dev(w, device) for w in weights["Wo"]]
+        if self.llama:
+            lst = lambda k: [_dev(w, device) for w in weights[k]]
+            self.g_att, self.g_mlp = lst("g_att"), lst("g_mlp")
+            self.W1, self.W2, self.W3 = lst("W1"), lst("W2"), lst("W3")
+            self.g_f = _dev(weights["g_f"], device)
         self.nl = len(self.Wq)
         self.V, self.dm = self.E.shape
         assert self.dm % D == 0 and Hq % Hkv == 0
@@ -396,7 +408,13 @@ class LayeredDecoder:
         n = self.n = len(prompt) - 1
         L = self.L
         self.cap = (n + max_new + 2 * L + 63) // 32 * 32
-        assert self.cap <= self.P.shape[0], "position table too short"
+        if self.llama:
+            # rotation angles in float64 on the host, cos/sin rounded once to fp32
+            ang = np.arange(self.cap)[:, None] * rope_theta ** (-2.0 * np.arange(D // 2) / D)
+            self.cos = torch.from_numpy(np.cos(ang).astype(np.float32)).to(device)
+            self.sin = torch.from_numpy(np.sin(ang).astype(np.float32)).to(device)
+        else:
+            assert self.cap <= self.P.shape[0], "position table too short"
         f32 = dict(dtype=torch.float32, device=device)
         tk = dict(dtype=self.tdt, device=device)
         nl = self.nl
@@ -429,6 +447,45 @@ class LayeredDecoder:
         self.tok[0] = prompt[-1]
         self.rounds = []
 
+    # ---- the layer's parts outside attention (fp32) ------------------------------------------
+    def _embed(self, tok, pos0: int):
+        """Residual stream rows [m, dm] of the device int32 tokens `tok` at positions pos0.."""
+        X = self.E[tok.long()]
+        return X if self.llama else X + self.P[pos0:pos0 + X.shape[0]]
+
+    @staticmethod
+    def _rms(X, g):
+        return X * torch.rsqrt((X * X).mean(dim=-1, keepdim=True) + 1e-5) * g
+
+    def _rope(self, Y, pos0: int):
+        """Rows Y [m, heads, 128] at positions pos0.. rotated (pair i, i + 64)."""
+        c = self.cos[pos0:pos0 + Y.shape[0]].unsqueeze(1)
+        s = self.sin[pos0:pos0 + Y.shape[0]].unsqueeze(1)
+        a, b = Y[..., :D // 2], Y[..., D // 2:]
+        return torch.cat([a * c - b * s, b * c + a * s], dim=-1)
+
+    def _qkv(self, l: int, X, pos0: int):
+        """q [m, Hq, 128], k and v [m, Hkv, 128] (fp32) of rows X [m, dm] at positions pos0.."""
+        m = X.shape[0]
+        H = self._rms(X, self.g_att[l]) if self.llama else X
+        q = (H @ self.Wq[l].T).view(m, self.Hq, D)
+        k = (H @ self.Wk[l].T).view(m, self.Hkv, D)
+        v = (H @ self.Wv[l].T).view(m, self.Hkv, D)
+        if self.llama:
+            q, k = self._rope(q, pos0), self._rope(k, pos0)
+        return q, k, v
+
+    def _block_out(self, l: int, X, O):
+        """The residual stream after layer l's attention output O [m, Hq*128] (and MLP)."""
+        X = X + O @ self.Wo[l].T
+        if self.llama:
+            H = self._rms(X, self.g_mlp[l])
+            X = X + (torch.nn.functional.silu(H @ self.W1[l].T) * (H @ self.W3[l].T)) @ self.W2[l].T
+        return X
+
+    def _head_in(self, X):
+        return self._rms(X, self.g_f) if self.llama else X
+
     def _verify(self, l: int, q, k, v, n: int, out, lse):
         host = self.host and n > 0  # no past yet: nothing to stream (the block alone)
         nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, q.shape[2], n, host, self.chunk, self.vdt)
@@ -443,10 +500,11 @@ class LayeredDecoder:
         cache, causal attention in blocks of 32 rows (the verify call over the rows before the
         block), the residual stream updated."""
         n, Hq, Hkv = self.n, self.Hq, self.Hkv
-        X = self.E[torch.tensor(prompt[:n], device=self.device)] + self.P[:n]
+        X = self._embed(torch.tensor(prompt[:n], device=self.device), 0)
+        cache_layout = lambda Y: Y.transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
         for l in range(self.nl):
-            K = (X @ self.Wk[l].T).view(n, Hkv, D).transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
-            V = (X @ self.Wv[l].T).view(n, Hkv, D).transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
+            Q, K, V = self._qkv(l, X, 0)
+            K, V = cache_layout(K), cache_layout(V)
             self.stores[l].write(0, K, V)
             c = self.caches[l]
             if self.n_q:
@@ -454,42 +512,44 @@ class LayeredDecoder:
             if n > self.n_q:
                 vc.vc_kivi_append(c, K[:, :, self.n_q:], V[:, :, self.n_q:], self.n_q, n - self.n_q,
                                   src_bh_stride=n * D)
-            Xn = X.clone()
+            O = torch.zeros((n, Hq * D), dtype=torch.float32, device=self.device)
             for b0 in range(0, n, 32):
                 b1 = min(n, b0 + 32)
                 m = b1 - b0
-                q = (X[b0:b1] @ self.Wq[l].T).view(m, Hq, D).transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
+                q = cache_layout(Q[b0:b1])
                 o = torch.zeros((1, Hq, m, D), dtype=torch.float32, device=self.device)
                 lse = torch.zeros((1, Hq, m), dtype=torch.float32, device=self.device)
                 self._verify(l, q, K[:, :, b0:b1].contiguous(), V[:, :, b0:b1].contiguous(), b0, o, lse)
-                Xn[b0:b1] = X[b0:b1] + o[0].transpose(0, 1).reshape(m, -1) @ self.Wo[l].T
-            X = Xn
+                O[b0:b1] = o[0].transpose(0, 1).reshape(m, -1)
+            X = self._block_out(l, X, O)
 
     def draft_step(self, j: int):
-        x = self.E[self.tok[j:j + 1].long()][0] + self.P[self.n + j]
+        x = self._embed(self.tok[j:j + 1], self.n + j)
         r = (self.n - self.n_q) + j + 1
         for l in range(self.nl):
-            self.qd[0] = (self.Wq[l] @ x).view(self.Hq, D)
-            self.kd[l][0, :, j] = (self.Wk[l] @ x).view(self.Hkv, D)
-            self.vd[l][0, :, j] = (self.Wv[l] @ x).view(self.Hkv, D)
+            q, k, v = self._qkv(l, x, self.n + j)
+            self.qd.copy_(q)
+            self.kd[l][0, :, j] = k[0]
+            self.vd[l][0, :, j] = v[0]
             c = self.caches[l]
             nb = vc.vc_draft_quant_workspace(c, self.n_q, r, self.Hq)
             vc.vc_draft_attn_quant(c, self.n_q, r, self.qd, self.od, self.lse_d, self.ws_draft.get(nb),
                                    SM_SCALE, k_new=self.kd[l][:, :, j], v_new=self.vd[l][:, :, j])
-            x = x + self.Wo[l] @ self.od.view(-1)
-        vc.vc_project_logits(self.Wlm, x.view(1, -1, D), argmax=self.tok[j + 1:j + 2], argmax_b_stride=1,
-                             ws=self.ws_proj)
+            x = self._block_out(l, x, self.od.view(1, -1))
+        vc.vc_project_logits(self.Wlm, self._head_in(x).view(1, -1, D), argmax=self.tok[j + 1:j + 2],
+                             argmax_b_stride=1, ws=self.ws_proj)
 
     def verify_step(self):
         L, n = self.L, self.n
-        X = self.E[self.tok[:L].long()] + self.P[n:n + L]
+        X = self._embed(self.tok[:L], n)
         for l in range(self.nl):
-            self.qv.copy_((X @ self.Wq[l].T).view(L, self.Hq, D).transpose(0, 1).unsqueeze(0))
-            self.kv_[l].copy_((X @ self.Wk[l].T).view(L, self.Hkv, D).transpose(0, 1).unsqueeze(0))
-            self.vv_[l].copy_((X @ self.Wv[l].T).view(L, self.Hkv, D).transpose(0, 1).unsqueeze(0))
+            q, k, v = self._qkv(l, X, n)
+            self.qv.copy_(q.transpose(0, 1).unsqueeze(0))
+            self.kv_[l].copy_(k.transpose(0, 1).unsqueeze(0))
+            self.vv_[l].copy_(v.transpose(0, 1).unsqueeze(0))
             self._verify(l, self.qv, self.kv_[l], self.vv_[l], n, self.ov, self.lse_v)
-            X = X + self.ov[0].transpose(0, 1).reshape(L, -1) @ self.Wo[l].T
-        xl = X.view(L, -1, D).transpose(0, 1).unsqueeze(0).contiguous()
+            X = self._block_out(l, X, self.ov[0].transpose(0, 1).reshape(L, -1))
+        xl = self._head_in(X).view(L, -1, D).transpose(0, 1).unsqueeze(0).contiguous()
         vc.vc_project_logits(self.Wlm, xl, logits=self.logits_v)
         vc.vc_accept(self.logits_v, self.tok[1:L].view(1, self.x), self.accept_len, self.next_tok,
                      self.argmax_v)
@@ -539,15 +599,16 @@ class LayeredGreedyDecoder(LayeredDecoder):
 
     def generate(self, steps: int):
         for i in range(steps):
-            x = self.E[self.toks[i:i + 1].long()][0] + self.P[self.n]
+            x = self._embed(self.toks[i:i + 1], self.n)
             for l in range(self.nl):
-                self.q1[0, :, 0] = (self.Wq[l] @ x).view(self.Hq, D)
-                self.k1[0, :, 0] = (self.Wk[l] @ x).view(self.Hkv, D)
-                self.v1[0, :, 0] = (self.Wv[l] @ x).view(self.Hkv, D)
+                q, k, v = self._qkv(l, x, self.n)
+                self.q1[0, :, 0] = q[0]
+                self.k1[0, :, 0] = k[0]
+                self.v1[0, :, 0] = v[0]
                 self._verify(l, self.q1, self.k1, self.v1, self.n, self.o1, self.lse1)
                 self.stores[l].write(self.n, self.k1, self.v1)
-                x = x + self.Wo[l] @ self.o1.view(-1)
-            vc.vc_project_logits(self.Wlm, x.view(1, -1, D), argmax=self.toks[i + 1:i + 2],
-                                 argmax_b_stride=1, ws=self.ws_proj)
+                x = self._block_out(l, x, self.o1.view(1, -1))
+            vc.vc_project_logits(self.Wlm, self._head_in(x).view(1, -1, D),
+                                 argmax=self.toks[i + 1:i + 2], argmax_b_stride=1, ws=self.ws_proj)
             self.n += 1
         return [int(t) for t in self.toks[1:steps + 1].tolist()]

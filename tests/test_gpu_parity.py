@@ -917,6 +917,44 @@ def test_layered_decoder_emits_full_kv_greedy(gpu_lib, layers, bits, kv, host):
     assert dec.n_q > 32 * ((len(prompt) - 1 - 32) // 32), "the loop must have flushed"
 
 
+@pytest.mark.parametrize("layers,bits,kv,host", [(2, 4, "f32", False), (3, 2, "bf16", True)])
+def test_llama_decoder_emits_full_kv_greedy(gpu_lib, layers, bits, kv, host):
+    """Llama-form layers (RMSNorm, rotary positions on q and k, SwiGLU MLP, final norm): GPU
+    VeriCache decoding and GPU greedy decoding both emit the oracle's full-KV greedy tokens, up to
+    a first divergence that only a near-tie of the oracle's logits may cause."""
+    from kv_cache_compressed_amd.decode_loop import LayeredDecoder, LayeredGreedyDecoder
+    from oracle import loop as oloop
+
+    m = oloop.LlamaModel(seed=11, vocab=384, dm=256, d=128, Hq=4, Hkv=2, layers=layers, F=512,
+                         kv_bf16=kv == "bf16")
+    W = {k: getattr(m, k).astype(np.float32) for k in ("E", "Wlm", "g_f")}
+    per_layer = ("g_att", "Wq", "Wk", "Wv", "Wo", "g_mlp", "W1", "W2", "W3")
+    for k in per_layer:
+        W[k] = [w.astype(np.float32) for w in getattr(m, k)]
+    for k in ("E", "Wlm", "g_f"):                   # the oracle runs on the same fp32 weights
+        setattr(m, k, W[k].astype(np.float64))
+    for k in per_layer:
+        setattr(m, k, [w.astype(np.float64) for w in W[k]])
+    prompt = [int(t) for t in np.random.default_rng(5).integers(0, 384, 150)]
+    steps, x = 40, 8
+    opts = dict(kv_dtype=kv, host_past=host, chunk_tokens=64)
+    dec = LayeredDecoder(W, 4, 2, prompt, x=x, bits=bits, R=32, max_new=steps + 32, **opts)
+    got = dec.generate(steps)
+    greedy_gpu = LayeredGreedyDecoder(W, 4, 2, prompt, max_new=steps + 8, **opts).generate(steps)
+    ref = oloop.greedy_llama(m, prompt, steps)
+    print(f"[llama {layers} layers, {bits}-bit, {kv}{' host' if host else ''}] accepted per round "
+          f"{dec.rounds}; n_q {dec.n_q}", flush=True)
+    for what, seq in (("VeriCache", got), ("GPU greedy", greedy_gpu)):
+        if seq != ref:
+            t = next(i for i in range(steps) if seq[i] != ref[i])
+            z = m.logits_all(prompt + ref[:t])[-1]
+            gap = float(oacc.top2_gap(z[None])[0])
+            assert gap < GAP, f"{what}: token {t} differs ({seq[t]} vs {ref[t]}), oracle top-2 gap {gap}"
+            print(f"{what}: first divergence at token {t}: near-tie (gap {gap:.2e})", flush=True)
+    assert sum(dec.rounds) > 0, "the drafter should get some tokens accepted"
+    assert dec.n_q > 32 * ((len(prompt) - 1 - 32) // 32), "the loop must have flushed"
+
+
 def test_token_decoders_staggered_two_requests(gpu_lib):
     """Two requests decoded token by token over host-streamed bf16 caches: the staggered schedule
     (harness.staggered_decode) emits, per request, the same tokens as the lock-step one, and those
