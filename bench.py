@@ -348,6 +348,70 @@ def _e2e_decode(torch, seed: int, context: int, tokens: int) -> dict:
     return out
 
 
+def _e2e_llama(torch, seed: int, context: int, tokens: int, bits: int = 2, x: int = 30) -> dict:
+    """Token-level decoding of one request on a random-init 4-layer Llama-form decoder (d_model 2048,
+    16 query / 4 kv heads, d 128, SwiGLU width 5632, vocab 32000, weights ~N(0, 0.02) rounded to
+    bf16 values, gains 1; fp32 arithmetic outside the attention calls) with a `context`-token
+    random prompt whose bf16 caches (one per layer) sit in pinned host memory and are streamed by
+    every verify: VeriCache (`bits`-bit KIVI drafter in HBM, fp16 residual of 128, draft length x)
+    against greedy decoding over the full caches."""
+    from kv_cache_compressed_amd.decode_loop import LayeredDecoder, LayeredGreedyDecoder
+
+    dev, V, dm, Hq, Hkv, F, nl = "cuda", 32000, 2048, 16, 4, 5632, 4
+    g = torch.Generator(device=dev).manual_seed(seed)
+    rn = lambda *shape: (0.02 * torch.randn(*shape, generator=g, device=dev)).to(torch.bfloat16).float()
+    one = lambda: torch.ones(dm, device=dev)
+    W = {"E": rn(V, dm), "Wlm": rn(V, dm), "g_f": one(),
+         "g_att": [one() for _ in range(nl)], "g_mlp": [one() for _ in range(nl)],
+         "Wq": [rn(Hq * 128, dm) for _ in range(nl)], "Wk": [rn(Hkv * 128, dm) for _ in range(nl)],
+         "Wv": [rn(Hkv * 128, dm) for _ in range(nl)], "Wo": [rn(dm, Hq * 128) for _ in range(nl)],
+         "W1": [rn(F, dm) for _ in range(nl)], "W3": [rn(F, dm) for _ in range(nl)],
+         "W2": [rn(dm, F) for _ in range(nl)]}
+    prompt = torch.randint(0, V, (context,), generator=g, device=dev).tolist()
+    opts = dict(kv_dtype="bf16", host_past=True, chunk_tokens=65536)
+    out = {"context": context, "tokens": tokens, "drafter": f"KIVI {bits}-bit, x = {x}",
+           "model": "4 Llama-form layers, d_model 2048, 16/4 heads, d 128, SwiGLU 5632, vocab 32000, "
+                    "bf16 caches in pinned host memory"}
+    seqs = {}
+    for name in ("vericache", "greedy"):
+        t0 = time.perf_counter()
+        if name == "vericache":
+            dec = LayeredDecoder(W, Hq, Hkv, prompt, x=x, bits=bits, R=128, max_new=tokens + 96, **opts)
+        else:
+            dec = LayeredGreedyDecoder(W, Hq, Hkv, prompt, max_new=tokens + 8, **opts)
+        torch.cuda.synchronize()
+        t_prefill = time.perf_counter() - t0
+        dec.warm()
+        # one untimed round (greedy: token) pays the first launches' one-time costs
+        if name == "greedy":
+            warm = dec.generate(1)
+        else:
+            for j in range(dec.x):
+                dec.draft_step(j)
+            dec.verify_step()
+            warm = dec.commit()
+        torch.cuda.synchronize()
+        r0 = len(dec.rounds) if name == "vericache" else 0
+        t0 = time.perf_counter()
+        seqs[name] = dec.generate(tokens)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        emitted = sum(a + 1 for a in dec.rounds[r0:]) if name == "vericache" else tokens
+        out[name] = {"tok_s": round(emitted / el, 2), "emitted": emitted,
+                     "ms_per_token": round(el / emitted * 1e3, 3), "prefill_s": round(t_prefill, 2)}
+        if name == "vericache":
+            acc = dec.rounds[r0:]
+            out[name]["rounds"] = len(acc)
+            out[name]["mean_accepted"] = round(float(np.mean(acc)), 2)
+        seqs[name] = warm + seqs[name]
+        del dec
+    out["speedup"] = round(out["vericache"]["tok_s"] / out["greedy"]["tok_s"], 3)
+    a, b = seqs["vericache"], seqs["greedy"]
+    m = min(len(a), len(b))  # the greedy run's warm-up token and timed tokens
+    out["first_divergence"] = next((i for i in range(m) if a[i] != b[i]), None)
+    return out
+
+
 def _back_to_back_us(torch, launch, n: int) -> float:
     """Mean duration of n launches enqueued back to back between two events (microseconds)."""
     for i in range(3):
@@ -388,6 +452,13 @@ def main():
     ap.add_argument("--decode-rounds", type=int, default=0,
                     help="single-request KIVI workloads (c1, c4): also run this many chained decode "
                          "rounds (commit + residual flush between rounds) and report them")
+    ap.add_argument("--llama-context", type=int, default=0,
+                    help="also decode one request on a random 4-layer Llama-form decoder (d_model 2048, "
+                         "16/4 heads, SwiGLU 5632, vocab 32000) with a prompt of this many tokens, "
+                         "caches in pinned host memory: VeriCache (2-bit KIVI, x = 30) vs greedy")
+    ap.add_argument("--llama-tokens", type=int, default=512)
+    ap.add_argument("--llama-bits", type=int, default=2, choices=[2, 4])
+    ap.add_argument("--llama-x", type=int, default=30, help="draft length of the Llama-form run")
     ap.add_argument("--e2e-context", type=int, default=0,
                     help="also decode one request token by token on a one-layer decoder with a "
                          "host-streamed bf16 cache of this many tokens: VeriCache vs greedy")
@@ -532,6 +603,9 @@ def main():
                                                        args.decode_rounds)
     if args.e2e_context > 0:
         line["e2e_decode"] = _e2e_decode(torch, args.seed, args.e2e_context, args.e2e_tokens)
+    if args.llama_context > 0:
+        line["e2e_llama"] = _e2e_llama(torch, args.seed, args.llama_context, args.llama_tokens,
+                                       args.llama_bits, args.llama_x)
     if not args.no_cpu_baseline and args.workload == "c2":
         line["cpu_baseline"] = cpu_baseline(w, inputs, a_plus_1, args.cpu_draft_steps,
                                             args.cpu_verify_heads)

@@ -390,10 +390,14 @@ class LayeredDecoder:
         self.Wk = [_dev(w, device) for w in weights["Wk"]]
         self.Wv = [_dev(w, device) for w in weights["Wv"]]
         self.Wo = [_dev(w, device) for w in weights["Wo"]]
+        # q, k, v from one GEMM per layer
+        self.Wqkv = [torch.cat([q, k, v]).contiguous() for q, k, v in zip(self.Wq, self.Wk, self.Wv)]
         if self.llama:
             lst = lambda k: [_dev(w, device) for w in weights[k]]
             self.g_att, self.g_mlp = lst("g_att"), lst("g_mlp")
-            self.W1, self.W2, self.W3 = lst("W1"), lst("W2"), lst("W3")
+            self.W2 = lst("W2")
+            self.W13 = [torch.cat([_dev(a, device), _dev(b, device)]).contiguous()  # gate and up
+                        for a, b in zip(weights["W1"], weights["W3"])]
             self.g_f = _dev(weights["g_f"], device)
         self.nl = len(self.Wq)
         self.V, self.dm = self.E.shape
@@ -453,9 +457,8 @@ class LayeredDecoder:
         X = self.E[tok.long()]
         return X if self.llama else X + self.P[pos0:pos0 + X.shape[0]]
 
-    @staticmethod
-    def _rms(X, g):
-        return X * torch.rsqrt((X * X).mean(dim=-1, keepdim=True) + 1e-5) * g
+    def _rms(self, X, g):
+        return torch.nn.functional.rms_norm(X, (self.dm,), g, 1e-5)
 
     def _rope(self, Y, pos0: int):
         """Rows Y [m, heads, 128] at positions pos0.. rotated (pair i, i + 64)."""
@@ -466,21 +469,20 @@ class LayeredDecoder:
 
     def _qkv(self, l: int, X, pos0: int):
         """q [m, Hq, 128], k and v [m, Hkv, 128] (fp32) of rows X [m, dm] at positions pos0.."""
-        m = X.shape[0]
+        m, Hq, Hkv = X.shape[0], self.Hq, self.Hkv
         H = self._rms(X, self.g_att[l]) if self.llama else X
-        q = (H @ self.Wq[l].T).view(m, self.Hq, D)
-        k = (H @ self.Wk[l].T).view(m, self.Hkv, D)
-        v = (H @ self.Wv[l].T).view(m, self.Hkv, D)
-        if self.llama:
-            q, k = self._rope(q, pos0), self._rope(k, pos0)
-        return q, k, v
+        Y = (H @ self.Wqkv[l].T).view(m, Hq + 2 * Hkv, D)
+        if self.llama:  # q and k rotated together
+            Y = torch.cat([self._rope(Y[:, :Hq + Hkv], pos0), Y[:, Hq + Hkv:]], dim=1)
+        return Y[:, :Hq], Y[:, Hq:Hq + Hkv], Y[:, Hq + Hkv:]
 
     def _block_out(self, l: int, X, O):
         """The residual stream after layer l's attention output O [m, Hq*128] (and MLP)."""
         X = X + O @ self.Wo[l].T
         if self.llama:
-            H = self._rms(X, self.g_mlp[l])
-            X = X + (torch.nn.functional.silu(H @ self.W1[l].T) * (H @ self.W3[l].T)) @ self.W2[l].T
+            Z = self._rms(X, self.g_mlp[l]) @ self.W13[l].T
+            F = Z.shape[-1] // 2
+            X = X + (torch.nn.functional.silu(Z[..., :F]) * Z[..., F:]) @ self.W2[l].T
         return X
 
     def _head_in(self, X):
@@ -497,8 +499,9 @@ class LayeredDecoder:
 
     def _prefill(self, prompt):
         """Layer by layer over positions 0..n-1: keys/values into the full cache and the KIVI
-        cache, causal attention in blocks of 32 rows (the verify call over the rows before the
-        block), the residual stream updated."""
+        cache, causal attention in blocks of 32 rows (the verify call over the layer's keys and
+        values of the rows before the block, device resident whatever the cache placement), the
+        residual stream updated."""
         n, Hq, Hkv = self.n, self.Hq, self.Hkv
         X = self._embed(torch.tensor(prompt[:n], device=self.device), 0)
         cache_layout = lambda Y: Y.transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
@@ -519,7 +522,9 @@ class LayeredDecoder:
                 q = cache_layout(Q[b0:b1])
                 o = torch.zeros((1, Hq, m, D), dtype=torch.float32, device=self.device)
                 lse = torch.zeros((1, Hq, m), dtype=torch.float32, device=self.device)
-                self._verify(l, q, K[:, :, b0:b1].contiguous(), V[:, :, b0:b1].contiguous(), b0, o, lse)
+                nb = vc.vc_verify_workspace(1, Hq, Hkv, m, b0, False, 0, self.vdt)
+                vc.vc_verify_attn(q, K[:, :, b0:b1].contiguous(), V[:, :, b0:b1].contiguous(), K, V, b0, o,
+                                  lse, self.ws_verify.get(nb), SM_SCALE, past_stride=n)
                 O[b0:b1] = o[0].transpose(0, 1).reshape(m, -1)
             X = self._block_out(l, X, O)
 
@@ -573,7 +578,18 @@ class LayeredDecoder:
         self.rounds.append(a)
         return emitted
 
+    def warm(self):
+        """Size the workspaces for the largest context this decoder can reach, so that no
+        allocation falls inside a timed decode."""
+        self.ws_verify.get(vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, self.cap, self.host,
+                                                  self.chunk, self.vdt))
+        r = self.R + 32 + self.L
+        self.ws_draft.get(vc.vc_draft_quant_workspace(self.caches[0], (self.cap - r) // 32 * 32, r,
+                                                      self.Hq))
+        torch.cuda.synchronize()
+
     def generate(self, steps: int):
+        """Rounds until `steps` tokens are emitted; returns them (later calls continue)."""
         out = []
         while len(out) < steps:
             for j in range(self.x):
@@ -596,9 +612,13 @@ class LayeredGreedyDecoder(LayeredDecoder):
         self.lse1 = torch.zeros((1, Hq, 1), dtype=torch.float32, device=self.device)
         self.toks = torch.zeros((max_new + 1,), dtype=torch.int32, device=self.device)
         self.toks[0] = self.tok[0]
+        self.i = 0  # tokens generated so far (generate() continues from there)
 
     def generate(self, steps: int):
-        for i in range(steps):
+        """The next `steps` tokens."""
+        i0 = self.i
+        assert i0 + steps < self.toks.numel(), "max_new exhausted"
+        for i in range(i0, i0 + steps):
             x = self._embed(self.toks[i:i + 1], self.n)
             for l in range(self.nl):
                 q, k, v = self._qkv(l, x, self.n)
@@ -611,4 +631,5 @@ class LayeredGreedyDecoder(LayeredDecoder):
             vc.vc_project_logits(self.Wlm, self._head_in(x).view(1, -1, D),
                                  argmax=self.toks[i + 1:i + 2], argmax_b_stride=1, ws=self.ws_proj)
             self.n += 1
-        return [int(t) for t in self.toks[1:steps + 1].tolist()]
+        self.i = i0 + steps
+        return [int(t) for t in self.toks[i0 + 1:i0 + steps + 1].tolist()]
