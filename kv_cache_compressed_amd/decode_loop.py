@@ -381,7 +381,8 @@ class LayeredDecoder:
 
     def __init__(self, weights, Hq: int, Hkv: int, prompt, x: int, bits: int = 4, R: int = 32,
                  max_new: int = 256, kv_dtype: str = "f32", host_past: bool = False,
-                 chunk_tokens: int = 65536, rope_theta: float = 500000.0, device: str = "cuda"):
+                 chunk_tokens: int = 65536, rope_theta: float = 500000.0, graphs: bool = True,
+                 device: str = "cuda"):
         self.llama = "g_att" in weights
         self.E = _dev(weights["E"], device)
         self.P = None if self.llama else _dev(weights["P"], device)
@@ -447,9 +448,83 @@ class LayeredDecoder:
         meta = vc.VC_F32 if kv_dtype == "f32" else vc.VC_F16
         self.caches = [vc.KiviCache(1, Hkv, self.cap, bits, meta, meta, res_cap, device)
                        for _ in range(nl)]
+        # one-row steps of the Llama form replay the layer's glue from HIP graphs (captured on
+        # first use): the row's residual stream, position, query and draft-time key/value live in
+        # fixed buffers, the position is read on the device
+        self.use_graphs = graphs and self.llama
+        self.xb = torch.zeros((1, self.dm), **f32)
+        self.hb = torch.zeros((1, self.dm), **f32)
+        self.posb = torch.zeros((1,), dtype=torch.int64, device=device)
+        self.ks = [torch.zeros((1, Hkv, D), **tk) for _ in range(nl)]
+        self.vs = [torch.zeros((1, Hkv, D), **tk) for _ in range(nl)]
+        self.gA = self.gB = self.gH = None
         self._prefill(prompt)
         self.tok[0] = prompt[-1]
         self.rounds = []
+
+    # ---- graph-replayed glue of one-row steps ------------------------------------------------
+    @staticmethod
+    def _gemv(W, x):
+        """W [N, K] fp32 times the row x [1, K] (K a multiple of 128) -> [1, N], through the
+        projection kernel (one row: weight-bound, coalesced 16-byte loads of every W row)."""
+        out = torch.empty((1, 1, W.shape[0]), dtype=torch.float32, device=x.device)
+        vc.vc_project_logits(W, x.contiguous().view(1, -1, D), logits=out)
+        return out.view(1, -1)
+
+    def _glue_a(self, l: int):
+        """Layer l's norm, q/k/v GEMV and rotation of the row in xb at position posb: q into qd,
+        k and v into ks[l], vs[l] (cache dtype)."""
+        Hq, Hkv = self.Hq, self.Hkv
+        Y = self._gemv(self.Wqkv[l], self._rms(self.xb, self.g_att[l])).view(1, Hq + 2 * Hkv, D)
+        c = self.cos.index_select(0, self.posb).unsqueeze(1)
+        s = self.sin.index_select(0, self.posb).unsqueeze(1)
+        a, b = Y[:, :Hq + Hkv, :D // 2], Y[:, :Hq + Hkv, D // 2:]
+        qk = torch.cat([a * c - b * s, b * c + a * s], dim=-1)
+        self.qd.copy_(qk[:, :Hq])
+        self.ks[l].copy_(qk[:, Hq:])
+        self.vs[l].copy_(Y[:, Hq + Hkv:])
+
+    def _glue_b(self, l: int):
+        """Layer l's output projection, residual and MLP on xb, from the attention output od."""
+        X = self.xb + self._gemv(self.Wo[l], self.od.view(1, -1))
+        Z = self._gemv(self.W13[l], self._rms(X, self.g_mlp[l]))
+        F = Z.shape[-1] // 2
+        self.xb.copy_(X + self._gemv(self.W2[l], torch.nn.functional.silu(Z[:, :F]) * Z[:, F:]))
+
+    def _glue_h(self):
+        self.hb.copy_(self._head_in(self.xb))
+
+    def _capture(self):
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        pool = torch.cuda.graph_pool_handle()
+        with torch.cuda.stream(side):
+            for l in range(self.nl):  # one eager pass first (library set-up outside capture)
+                self._glue_a(l)
+                self._glue_b(l)
+            self._glue_h()
+            side.synchronize()
+            gA, gB = [], []
+            for l in range(self.nl):  # captured in the order the steps replay them
+                for lst, fn in ((gA, self._glue_a), (gB, self._glue_b)):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=side, pool=pool):
+                        fn(l)
+                    lst.append(g)
+            gH = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gH, stream=side, pool=pool):
+                self._glue_h()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.gA, self.gB, self.gH = gA, gB, gH
+
+    def _begin_row(self, tok1, pos: int):
+        """xb = embedding of the device token tok1 (1 element), posb = pos."""
+        if self.gH is None:
+            self._capture()
+        torch.index_select(self.E, 0, tok1, out=self.xb)
+        self.posb.fill_(pos)
 
     # ---- the layer's parts outside attention (fp32) ------------------------------------------
     def _embed(self, tok, pos0: int):
@@ -529,8 +604,22 @@ class LayeredDecoder:
             X = self._block_out(l, X, O)
 
     def draft_step(self, j: int):
-        x = self._embed(self.tok[j:j + 1], self.n + j)
         r = (self.n - self.n_q) + j + 1
+        if self.use_graphs:
+            self._begin_row(self.tok[j:j + 1], self.n + j)
+            for l in range(self.nl):
+                self.gA[l].replay()
+                c = self.caches[l]
+                nb = vc.vc_draft_quant_workspace(c, self.n_q, r, self.Hq)
+                vc.vc_draft_attn_quant(c, self.n_q, r, self.qd, self.od, self.lse_d,
+                                       self.ws_draft.get(nb), SM_SCALE, k_new=self.ks[l],
+                                       v_new=self.vs[l])
+                self.gB[l].replay()
+            self.gH.replay()
+            vc.vc_project_logits(self.Wlm, self.hb.view(1, -1, D), argmax=self.tok[j + 1:j + 2],
+                                 argmax_b_stride=1, ws=self.ws_proj)
+            return
+        x = self._embed(self.tok[j:j + 1], self.n + j)
         for l in range(self.nl):
             q, k, v = self._qkv(l, x, self.n + j)
             self.qd.copy_(q)
@@ -619,6 +708,20 @@ class LayeredGreedyDecoder(LayeredDecoder):
         i0 = self.i
         assert i0 + steps < self.toks.numel(), "max_new exhausted"
         for i in range(i0, i0 + steps):
+            if self.use_graphs:
+                self._begin_row(self.toks[i:i + 1], self.n)
+                for l in range(self.nl):
+                    self.gA[l].replay()
+                    q = self.qd.view(1, self.Hq, 1, D)
+                    k, v = self.ks[l].view(1, self.Hkv, 1, D), self.vs[l].view(1, self.Hkv, 1, D)
+                    self._verify(l, q, k, v, self.n, self.od.view(1, self.Hq, 1, D), self.lse1)
+                    self.stores[l].write(self.n, k, v)
+                    self.gB[l].replay()
+                self.gH.replay()
+                vc.vc_project_logits(self.Wlm, self.hb.view(1, -1, D), argmax=self.toks[i + 1:i + 2],
+                                     argmax_b_stride=1, ws=self.ws_proj)
+                self.n += 1
+                continue
             x = self._embed(self.toks[i:i + 1], self.n)
             for l in range(self.nl):
                 q, k, v = self._qkv(l, x, self.n)

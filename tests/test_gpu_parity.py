@@ -917,11 +917,15 @@ def test_layered_decoder_emits_full_kv_greedy(gpu_lib, layers, bits, kv, host):
     assert dec.n_q > 32 * ((len(prompt) - 1 - 32) // 32), "the loop must have flushed"
 
 
-@pytest.mark.parametrize("layers,bits,kv,host", [(2, 4, "f32", False), (3, 2, "bf16", True)])
-def test_llama_decoder_emits_full_kv_greedy(gpu_lib, layers, bits, kv, host):
+@pytest.mark.parametrize("layers,bits,kv,host,graphs", [(2, 4, "f32", False, True),
+                                                        (3, 2, "bf16", True, True),
+                                                        (2, 4, "bf16", False, False)])
+def test_llama_decoder_emits_full_kv_greedy(gpu_lib, layers, bits, kv, host, graphs):
     """Llama-form layers (RMSNorm, rotary positions on q and k, SwiGLU MLP, final norm): GPU
     VeriCache decoding and GPU greedy decoding both emit the oracle's full-KV greedy tokens, up to
-    a first divergence that only a near-tie of the oracle's logits may cause."""
+    a first divergence that only a near-tie of the oracle's logits may cause. graphs: the one-row
+    steps replay the layer's glue from HIP graphs (every replay then feeds the next step, so any
+    stale replay shows up as a token mismatch), else run it eagerly."""
     from kv_cache_compressed_amd.decode_loop import LayeredDecoder, LayeredGreedyDecoder
     from oracle import loop as oloop
 
@@ -937,12 +941,14 @@ def test_llama_decoder_emits_full_kv_greedy(gpu_lib, layers, bits, kv, host):
         setattr(m, k, [w.astype(np.float64) for w in W[k]])
     prompt = [int(t) for t in np.random.default_rng(5).integers(0, 384, 150)]
     steps, x = 40, 8
-    opts = dict(kv_dtype=kv, host_past=host, chunk_tokens=64)
+    opts = dict(kv_dtype=kv, host_past=host, chunk_tokens=64, graphs=graphs)
     dec = LayeredDecoder(W, 4, 2, prompt, x=x, bits=bits, R=32, max_new=steps + 32, **opts)
     got = dec.generate(steps)
+    assert (dec.gH is not None) == graphs
     greedy_gpu = LayeredGreedyDecoder(W, 4, 2, prompt, max_new=steps + 8, **opts).generate(steps)
     ref = oloop.greedy_llama(m, prompt, steps)
-    print(f"[llama {layers} layers, {bits}-bit, {kv}{' host' if host else ''}] accepted per round "
+    print(f"[llama {layers} layers, {bits}-bit, {kv}{' host' if host else ''}"
+          f"{' graphs' if graphs else ''}] accepted per round "
           f"{dec.rounds}; n_q {dec.n_q}", flush=True)
     for what, seq in (("VeriCache", got), ("GPU greedy", greedy_gpu)):
         if seq != ref:
