@@ -244,8 +244,10 @@ vc_status vc_accept(const float *logits, const int32_t *drafts, int32_t B, int32
  * accumulation, optionally fused with the greedy argmax of every row ("VeriCache: making lossy KV
  * compression exact", The Core Idea and Figure 1: the draft's greedy token at every drafted
  * position). Not one of the five calls of the path; it turns their outputs into tokens.
- *   W      [V][Hq*128] fp32, device;  o [B][Hq][L][128] fp32, device (the attention outputs:
- *          draft steps have L == 1, the verify block L rows)
+ *   W      [V][Hq*128], device, w_dtype VC_F32 or VC_BF16 (bf16 weights are widened exactly, so
+ *          bf16-valued weights give the same result in either dtype);  o [B][Hq][L][128] fp32,
+ *          device (the attention outputs: draft steps have L == 1, the verify block L rows; any
+ *          row of Hq*128 values, so one-row calls are plain weight-bound GEMVs)
  *   logits [B][L][V] fp32 or NULL
  *   argmax row (b, i) written to argmax[b * argmax_b_stride + i] (lowest index on ties; -0 and +0
  *          tie; logits are expected finite), or NULL
@@ -256,9 +258,9 @@ vc_status vc_accept(const float *logits, const int32_t *drafts, int32_t B, int32
  *   1 <= B*L <= 2^20, 1 <= V <= 2^24, 1 <= Hq <= 1024, Hq*128*V < 2^31.
  */
 vc_status vc_project_workspace(int32_t B, int32_t L, int32_t V, size_t *bytes);
-vc_status vc_project_logits(const float *W, int32_t V, const float *o, int32_t B, int32_t Hq,
-                            int32_t L, float *logits, int32_t *argmax, int64_t argmax_b_stride,
-                            void *ws, size_t ws_bytes, void *stream);
+vc_status vc_project_logits(const void *W, int32_t w_dtype, int32_t V, const float *o, int32_t B,
+                            int32_t Hq, int32_t L, float *logits, int32_t *argmax,
+                            int64_t argmax_b_stride, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Keep-list selection of a token-dropping drafter ("VeriCache: making lossy KV compression exact",

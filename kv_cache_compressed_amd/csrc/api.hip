@@ -381,11 +381,12 @@ vc_status vc_project_workspace(int32_t B, int32_t L, int32_t V, size_t* bytes) {
   return ok();
 }
 
-vc_status vc_project_logits(const float* W, int32_t V, const float* o, int32_t B, int32_t Hq,
-                            int32_t L, float* logits, int32_t* argmax, int64_t argmax_b_stride,
-                            void* ws, size_t ws_bytes, void* stream) {
+vc_status vc_project_logits(const void* W, int32_t w_dtype, int32_t V, const float* o, int32_t B,
+                            int32_t Hq, int32_t L, float* logits, int32_t* argmax,
+                            int64_t argmax_b_stride, void* ws, size_t ws_bytes, void* stream) {
   REQUIRE_PTR(W);
   REQUIRE_PTR(o);
+  REQUIRE(w_dtype == VC_F32 || w_dtype == VC_BF16, "w_dtype must be VC_F32 or VC_BF16");
   REQUIRE(B >= 1 && L >= 1 && (int64_t)B * L <= (1 << 20), "B*L must be in [1, 2^20]");
   REQUIRE(V >= 1 && V <= (1 << 24), "V must be in [1, 2^24]");
   REQUIRE(Hq >= 1 && Hq <= 1024, "Hq must be in [1, 1024]");
@@ -399,8 +400,8 @@ vc_status vc_project_logits(const float* W, int32_t V, const float* o, int32_t B
                   plan.ws_bytes, ws ? ws_bytes : (size_t)0);
   }
   const vc::ProjectPlan plan = vc::plan_project(B * L, V);
-  hipError_t e = vc::launch_project(W, V, o, B, Hq, L, logits, argmax, argmax_b_stride, ws, plan,
-                                    static_cast<hipStream_t>(stream));
+  hipError_t e = vc::launch_project(W, w_dtype, V, o, B, Hq, L, logits, argmax, argmax_b_stride, ws,
+                                    plan, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "vc_project_logits launch");
   return ok();
 }

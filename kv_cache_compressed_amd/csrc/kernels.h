@@ -73,9 +73,9 @@ struct ProjectPlan {
   size_t ws_bytes;
 };
 ProjectPlan plan_project(int M, int V);
-hipError_t launch_project(const float* W, int V, const float* o, int B, int Hq, int L, float* z,
-                          int32_t* idx, int64_t idx_b_stride, void* ws, const ProjectPlan& plan,
-                          hipStream_t s);
+hipError_t launch_project(const void* W, int w_dtype, int V, const float* o, int B, int Hq, int L,
+                          float* z, int32_t* idx, int64_t idx_b_stride, void* ws,
+                          const ProjectPlan& plan, hipStream_t s);
 
 // Keep-list selection (token-dropping drafter).
 hipError_t launch_select_keep(const float* scores, int64_t s_stride, int rows, int64_t n, int64_t lo,

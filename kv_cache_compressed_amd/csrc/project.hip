@@ -1,4 +1,5 @@
-// Logits projection with a fused greedy argmax: z[b][i][v] = sum_{h,c} W[v][128 h + c] o[b][h][i][c].
+// Logits projection with a fused greedy argmax: z[b][i][v] = sum_{h,c} W[v][128 h + c] o[b][h][i][c]
+// (W fp32, or bf16 widened exactly to fp32; fp32 products and accumulation either way).
 //
 // The round turns each attention output into a token by a greedy decision over logits ("VeriCache:
 // making lossy KV compression exact", The Core Idea and Figure 1: the draft model's greedy token
@@ -31,7 +32,7 @@ constexpr int CHUNK = 4 * PT;   // channels per chunk
 static_assert(PW == MT, "one wave per row in the final reduction");
 
 struct PArgs {
-  const float* W;       // [V][Dm]
+  const void* W;        // [V][Dm], fp32 or bf16 (template parameter of the kernel)
   const float* o;       // [B][Hq][L][128]
   int V, Dm, Hq, L, M;  // M = B * L output rows, row m = (b, i) = (m / L, m % L)
   int nvt;              // vocabulary tiles (grid.x)
@@ -72,16 +73,32 @@ __device__ __forceinline__ void halve(float* r, int lane) {
   }
 }
 
+// Four consecutive weights of a row as fp32: one 16-byte load (fp32 rows) or one 8-byte load
+// widened exactly (bf16 rows).
+template <bool WBF16>
+__device__ __forceinline__ f32x4 load_w4(const void* row, int d) {
+  if constexpr (WBF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(row) + d);
+    return f32x4{bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16),
+                 bf16_bits_to_f32(u.y & 0xffffu), bf16_bits_to_f32(u.y >> 16)};
+  } else {
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + d);
+  }
+}
+
+template <bool WBF16>
 __global__ void __launch_bounds__(PT) project_kernel(PArgs a) {
   static_assert(VT * MT == 64, "one reduced value per lane");
   __shared__ float s_red[PW][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int v0 = blockIdx.x * VT, m0 = blockIdx.y * MT;
+  const int64_t wbytes = WBF16 ? 2 : 4;
 
   // Row pointers (rows past the end read the last row and are never written).
-  const float* wrow[VT];
+  const void* wrow[VT];
 #pragma unroll
-  for (int v = 0; v < VT; ++v) wrow[v] = a.W + (int64_t)min(v0 + v, a.V - 1) * a.Dm;
+  for (int v = 0; v < VT; ++v)
+    wrow[v] = static_cast<const char*>(a.W) + (int64_t)min(v0 + v, a.V - 1) * a.Dm * wbytes;
   int64_t orow[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -94,7 +111,7 @@ __global__ void __launch_bounds__(PT) project_kernel(PArgs a) {
     const int d = min(d0 + 4 * tid, a.Dm - 4);  // past the end: re-read, weighed by 0 below
     const int64_t od = (int64_t)(d >> 7) * a.L * 128 + (d & 127);
 #pragma unroll
-    for (int v = 0; v < VT; ++v) w[v] = *reinterpret_cast<const f32x4*>(wrow[v] + d);
+    for (int v = 0; v < VT; ++v) w[v] = load_w4<WBF16>(wrow[v], d);
 #pragma unroll
     for (int m = 0; m < MT; ++m) x[m] = *reinterpret_cast<const f32x4*>(a.o + orow[m] + od);
   };
@@ -195,9 +212,9 @@ ProjectPlan plan_project(int M, int V) {
   return p;
 }
 
-hipError_t launch_project(const float* W, int V, const float* o, int B, int Hq, int L, float* z,
-                          int32_t* idx, int64_t idx_b_stride, void* ws, const ProjectPlan& plan,
-                          hipStream_t s) {
+hipError_t launch_project(const void* W, int w_dtype, int V, const float* o, int B, int Hq, int L,
+                          float* z, int32_t* idx, int64_t idx_b_stride, void* ws,
+                          const ProjectPlan& plan, hipStream_t s) {
   PArgs a;
   a.W = W;
   a.o = o;
@@ -213,7 +230,10 @@ hipError_t launch_project(const float* W, int V, const float* o, int B, int Hq, 
   a.counters = static_cast<unsigned*>(ws);
   a.slot = idx ? reinterpret_cast<unsigned long long*>(static_cast<uint8_t*>(ws) + plan.counter_bytes)
                : nullptr;
-  project_kernel<<<dim3(plan.nvt, plan.nmt), PT, 0, s>>>(a);
+  if (w_dtype == VC_BF16)
+    project_kernel<true><<<dim3(plan.nvt, plan.nmt), PT, 0, s>>>(a);
+  else
+    project_kernel<false><<<dim3(plan.nvt, plan.nmt), PT, 0, s>>>(a);
   return hipGetLastError();
 }
 

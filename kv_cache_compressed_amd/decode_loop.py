@@ -452,6 +452,17 @@ class LayeredDecoder:
         # first use): the row's residual stream, position, query and draft-time key/value live in
         # fixed buffers, the position is read on the device
         self.use_graphs = graphs and self.llama
+        if self.use_graphs:
+            # the one-row GEMVs read bf16 copies of weights whose values are all bf16 (widened
+            # exactly in the kernel, so the results are the fp32 weights' bit for bit)
+            def gemv_w(w):
+                wb = w.to(torch.bfloat16)
+                return wb if torch.equal(wb.float(), w) else w
+            self.gWqkv = [gemv_w(w) for w in self.Wqkv]
+            self.gWo = [gemv_w(w) for w in self.Wo]
+            self.gW13 = [gemv_w(w) for w in self.W13]
+            self.gW2 = [gemv_w(w) for w in self.W2]
+            self.gWlm = gemv_w(self.Wlm)
         self.xb = torch.zeros((1, self.dm), **f32)
         self.hb = torch.zeros((1, self.dm), **f32)
         self.posb = torch.zeros((1,), dtype=torch.int64, device=device)
@@ -475,7 +486,7 @@ class LayeredDecoder:
         """Layer l's norm, q/k/v GEMV and rotation of the row in xb at position posb: q into qd,
         k and v into ks[l], vs[l] (cache dtype)."""
         Hq, Hkv = self.Hq, self.Hkv
-        Y = self._gemv(self.Wqkv[l], self._rms(self.xb, self.g_att[l])).view(1, Hq + 2 * Hkv, D)
+        Y = self._gemv(self.gWqkv[l], self._rms(self.xb, self.g_att[l])).view(1, Hq + 2 * Hkv, D)
         c = self.cos.index_select(0, self.posb).unsqueeze(1)
         s = self.sin.index_select(0, self.posb).unsqueeze(1)
         a, b = Y[:, :Hq + Hkv, :D // 2], Y[:, :Hq + Hkv, D // 2:]
@@ -486,10 +497,10 @@ class LayeredDecoder:
 
     def _glue_b(self, l: int):
         """Layer l's output projection, residual and MLP on xb, from the attention output od."""
-        X = self.xb + self._gemv(self.Wo[l], self.od.view(1, -1))
-        Z = self._gemv(self.W13[l], self._rms(X, self.g_mlp[l]))
+        X = self.xb + self._gemv(self.gWo[l], self.od.view(1, -1))
+        Z = self._gemv(self.gW13[l], self._rms(X, self.g_mlp[l]))
         F = Z.shape[-1] // 2
-        self.xb.copy_(X + self._gemv(self.W2[l], torch.nn.functional.silu(Z[:, :F]) * Z[:, F:]))
+        self.xb.copy_(X + self._gemv(self.gW2[l], torch.nn.functional.silu(Z[:, :F]) * Z[:, F:]))
 
     def _glue_h(self):
         self.hb.copy_(self._head_in(self.xb))
@@ -616,7 +627,7 @@ class LayeredDecoder:
                                        v_new=self.vs[l])
                 self.gB[l].replay()
             self.gH.replay()
-            vc.vc_project_logits(self.Wlm, self.hb.view(1, -1, D), argmax=self.tok[j + 1:j + 2],
+            vc.vc_project_logits(self.gWlm, self.hb.view(1, -1, D), argmax=self.tok[j + 1:j + 2],
                                  argmax_b_stride=1, ws=self.ws_proj)
             return
         x = self._embed(self.tok[j:j + 1], self.n + j)
@@ -718,7 +729,7 @@ class LayeredGreedyDecoder(LayeredDecoder):
                     self.stores[l].write(self.n, k, v)
                     self.gB[l].replay()
                 self.gH.replay()
-                vc.vc_project_logits(self.Wlm, self.hb.view(1, -1, D), argmax=self.toks[i + 1:i + 2],
+                vc.vc_project_logits(self.gWlm, self.hb.view(1, -1, D), argmax=self.toks[i + 1:i + 2],
                                      argmax_b_stride=1, ws=self.ws_proj)
                 self.n += 1
                 continue

@@ -58,7 +58,7 @@ _SIGS = {
     "vc_lse_merge": [_P, _P, _I64, _I32, _I32, _P, _P, _P],
     "vc_accept": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
     "vc_project_workspace": [_I32, _I32, _I32, ctypes.POINTER(_SZ)],
-    "vc_project_logits": [_P, _I32, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _SZ, _P],
+    "vc_project_logits": [_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _SZ, _P],
     "vc_select_keep": [_P, _I64, _I32, _I64, _I64, _I64, _I64, _P, _I64, ctypes.POINTER(_I64), _P],
     "vc_status_string": [_I32],
     "vc_last_error": [],
@@ -279,15 +279,15 @@ def vc_project_workspace(B: int, L: int, V: int) -> int:
 
 def vc_project_logits(W, o, logits=None, argmax=None, argmax_b_stride: int | None = None,
                       ws: torch.Tensor | None = None, stream=None):
-    """W [V, Hq*128] fp32; o [B, Hq, L, 128] (or [B, Hq, 128] for L == 1) fp32 -> logits [B, L, V]
-    and/or argmax (row (b, i) at argmax.flat[b * argmax_b_stride + i]; default stride L)."""
+    """W [V, Hq*128] fp32 or bf16; o [B, Hq, L, 128] (or [B, Hq, 128] for L == 1) fp32 -> logits
+    [B, L, V] and/or argmax (row (b, i) at argmax.flat[b * argmax_b_stride + i]; default stride L)."""
     V = W.shape[0]
     B, Hq = o.shape[0], o.shape[1]
     L = o.shape[2] if o.dim() == 4 else 1
     if argmax_b_stride is None:
         argmax_b_stride = L
     nb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().vc_project_logits(_ptr(W), V, _ptr(o), B, Hq, L, _ptr(logits), _ptr(argmax),
+    _check(lib().vc_project_logits(_ptr(W), dtype_code(W), V, _ptr(o), B, Hq, L, _ptr(logits), _ptr(argmax),
                                    argmax_b_stride, _ptr(ws), nb, _stream(stream)))
 
 

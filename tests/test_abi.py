@@ -172,10 +172,11 @@ def test_project_rejects_and_sizes(L):
     assert L.vc_project_workspace(8, 31, 2048, ctypes.byref(n)) == vc.VC_OK
     assert n.value == 256 + 8 * 31 * 8
     assert L.vc_project_workspace(0, 1, 2048, ctypes.byref(n)) == vc.VC_ERR_INVALID
-    call = lambda **a: L.vc_project_logits(a.get("W", P), a.get("V", 2048), a.get("o", P), a.get("B", 8),
+    call = lambda **a: L.vc_project_logits(a.get("W", P), a.get("wdt", vc.VC_F32), a.get("V", 2048), a.get("o", P), a.get("B", 8),
                                            a.get("Hq", 32), a.get("L", 1), a.get("z", P), a.get("idx", P),
                                            a.get("stride", 1), a.get("ws", P), a.get("ws_bytes", 1 << 20), None)
     assert call(W=0) == vc.VC_ERR_INVALID
+    assert call(wdt=vc.VC_F16) == vc.VC_ERR_INVALID and "w_dtype" in _err(L)
     assert call(o=BAD) == vc.VC_ERR_INVALID
     assert call(V=0) == vc.VC_ERR_INVALID
     assert call(Hq=0) == vc.VC_ERR_INVALID

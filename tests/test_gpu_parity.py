@@ -159,6 +159,31 @@ def test_project_logits(gpu_lib, B, L, Hq, V):
     assert np.array_equal(am2.cpu().numpy(), am.cpu().numpy()[:, :L])
 
 
+@pytest.mark.parametrize("B,L,Hq,V", [(8, 1, 32, 2048), (2, 31, 32, 2048), (1, 1, 44, 2048),
+                                      (1, 1, 16, 11264), (3, 5, 12, 1003)])
+def test_project_bf16_weights(gpu_lib, B, L, Hq, V):
+    """bf16 weights are widened exactly: with bf16-valued weights the bf16 call gives the fp32 call's
+    logits and argmax bit for bit, both within the oracle's bound (one-row shapes included: the
+    layered decoder's GEMVs)."""
+    g = np.random.default_rng(V + Hq)
+    Wb = torch.from_numpy(g.standard_normal((V, Hq * 128)).astype(np.float32)).to(torch.bfloat16)
+    W = Wb.float().numpy()
+    O = (g.standard_normal((B, Hq, L, 128)) * 0.1).astype(np.float32)
+    ref, bound = _project_ref(W, O)
+    Ot = torch.from_numpy(O).cuda()
+    ws = torch.zeros((vc.vc_project_workspace(B, L, V) + 3) // 4, dtype=torch.int32, device="cuda")
+    res = []
+    for Wt in (torch.from_numpy(W).cuda(), Wb.cuda()):
+        z = torch.full((B, L, V), float("nan"), device="cuda")
+        am = torch.full((B, L), -1, dtype=torch.int32, device="cuda")
+        vc.vc_project_logits(Wt, Ot, logits=z, argmax=am, ws=ws)
+        res.append((z.cpu(), am.cpu()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    assert np.all(np.abs(res[1][0].numpy() - ref) <= bound)
+    assert np.array_equal(res[1][1].numpy(), oacc.argmax_rows(res[1][0].numpy()))
+    assert not ws.any().item()
+
+
 @pytest.mark.parametrize("sign", [1, -1])
 def test_project_argmax_ties_lowest_index(gpu_lib, sign):
     """Exact ties go to the lowest index, also when every logit is negative (sign -1: W <= 0,
