@@ -449,8 +449,8 @@ class LayeredDecoder:
         self.caches = [vc.KiviCache(1, Hkv, self.cap, bits, meta, meta, res_cap, device)
                        for _ in range(nl)]
         # one-row steps of the Llama form replay the layer's glue from HIP graphs (captured on
-        # first use): the row's residual stream, position, query and draft-time key/value live in
-        # fixed buffers, the position is read on the device
+        # first use): the row's residual stream, position and q/k/v live in fixed buffers, the
+        # position is read on the device
         self.use_graphs = graphs and self.llama
         if self.use_graphs:
             # the one-row GEMVs read bf16 copies of weights whose values are all bf16 (widened
@@ -466,8 +466,13 @@ class LayeredDecoder:
         self.xb = torch.zeros((1, self.dm), **f32)
         self.hb = torch.zeros((1, self.dm), **f32)
         self.posb = torch.zeros((1,), dtype=torch.int64, device=device)
-        self.ks = [torch.zeros((1, Hkv, D), **tk) for _ in range(nl)]
-        self.vs = [torch.zeros((1, Hkv, D), **tk) for _ in range(nl)]
+        # the row's q, k, v in the cache dtype, one buffer (each layer's attention reads them
+        # before the next layer's glue rewrites them)
+        self.qkvc = torch.zeros((1, Hq + 2 * Hkv, D), **tk)
+        self.ks1, self.vs1 = self.qkvc[:, Hq:Hq + Hkv], self.qkvc[:, Hq + Hkv:]
+        if self.llama:  # per position: [cos | cos] and [-sin | sin] over the 128 channels
+            self.cs = torch.stack([torch.cat([self.cos, self.cos], 1),
+                                   torch.cat([-self.sin, self.sin], 1)], 1).contiguous()
         self.gA = self.gB = self.gH = None
         self._prefill(prompt)
         self.tok[0] = prompt[-1]
@@ -483,24 +488,24 @@ class LayeredDecoder:
         return out.view(1, -1)
 
     def _glue_a(self, l: int):
-        """Layer l's norm, q/k/v GEMV and rotation of the row in xb at position posb: q into qd,
-        k and v into ks[l], vs[l] (cache dtype)."""
+        """Layer l's norm, q/k/v GEMV and rotation of the row in xb at position posb, then q, k, v
+        into qkvc (cache dtype): the pair (a, b) = (channel i, channel i + 64) becomes
+        (a c - b s, b c + a s), i.e. y c2 + roll(y, 64) s2 with c2 = [c | c], s2 = [-s | s]."""
         Hq, Hkv = self.Hq, self.Hkv
         Y = self._gemv(self.gWqkv[l], self._rms(self.xb, self.g_att[l])).view(1, Hq + 2 * Hkv, D)
-        c = self.cos.index_select(0, self.posb).unsqueeze(1)
-        s = self.sin.index_select(0, self.posb).unsqueeze(1)
-        a, b = Y[:, :Hq + Hkv, :D // 2], Y[:, :Hq + Hkv, D // 2:]
-        qk = torch.cat([a * c - b * s, b * c + a * s], dim=-1)
-        self.qd.copy_(qk[:, :Hq])
-        self.ks[l].copy_(qk[:, Hq:])
-        self.vs[l].copy_(Y[:, Hq + Hkv:])
+        cs = self.cs.index_select(0, self.posb)  # [1, 2, 128]
+        qk = Y[:, :Hq + Hkv]
+        r = torch.roll(qk, D // 2, dims=-1)
+        qk.mul_(cs[:, 0:1])
+        qk.addcmul_(r, cs[:, 1:2])
+        self.qkvc.copy_(Y)
 
     def _glue_b(self, l: int):
         """Layer l's output projection, residual and MLP on xb, from the attention output od."""
         X = self.xb + self._gemv(self.gWo[l], self.od.view(1, -1))
         Z = self._gemv(self.gW13[l], self._rms(X, self.g_mlp[l]))
         F = Z.shape[-1] // 2
-        self.xb.copy_(X + self._gemv(self.gW2[l], torch.nn.functional.silu(Z[:, :F]) * Z[:, F:]))
+        torch.add(X, self._gemv(self.gW2[l], torch.nn.functional.silu(Z[:, :F]) * Z[:, F:]), out=self.xb)
 
     def _glue_h(self):
         self.hb.copy_(self._head_in(self.xb))
@@ -622,9 +627,9 @@ class LayeredDecoder:
                 self.gA[l].replay()
                 c = self.caches[l]
                 nb = vc.vc_draft_quant_workspace(c, self.n_q, r, self.Hq)
-                vc.vc_draft_attn_quant(c, self.n_q, r, self.qd, self.od, self.lse_d,
-                                       self.ws_draft.get(nb), SM_SCALE, k_new=self.ks[l],
-                                       v_new=self.vs[l])
+                vc.vc_draft_attn_quant(c, self.n_q, r, self.qkvc[:, :self.Hq], self.od, self.lse_d,
+                                       self.ws_draft.get(nb), SM_SCALE, k_new=self.ks1,
+                                       v_new=self.vs1)
                 self.gB[l].replay()
             self.gH.replay()
             vc.vc_project_logits(self.gWlm, self.hb.view(1, -1, D), argmax=self.tok[j + 1:j + 2],
@@ -723,8 +728,8 @@ class LayeredGreedyDecoder(LayeredDecoder):
                 self._begin_row(self.toks[i:i + 1], self.n)
                 for l in range(self.nl):
                     self.gA[l].replay()
-                    q = self.qd.view(1, self.Hq, 1, D)
-                    k, v = self.ks[l].view(1, self.Hkv, 1, D), self.vs[l].view(1, self.Hkv, 1, D)
+                    q = self.qkvc[:, :self.Hq].view(1, self.Hq, 1, D)
+                    k, v = self.ks1.view(1, self.Hkv, 1, D), self.vs1.view(1, self.Hkv, 1, D)
                     self._verify(l, q, k, v, self.n, self.od.view(1, self.Hq, 1, D), self.lse1)
                     self.stores[l].write(self.n, k, v)
                     self.gB[l].replay()

@@ -202,7 +202,8 @@ def vc_draft_attn_quant(cache: KiviCache, n_q: int, r: int, q, out, lse, ws: tor
     stride, ndt = 0, 0
     if k_new is not None:
         assert k_new.shape == v_new.shape and k_new.stride() == v_new.stride() and k_new.dim() == 3
-        assert k_new.stride(2) == 1 and k_new.stride(0) == k_new.shape[1] * k_new.stride(1)
+        assert k_new.stride(2) == 1 and (k_new.shape[0] == 1 or
+                                         k_new.stride(0) == k_new.shape[1] * k_new.stride(1))
         stride, ndt = k_new.stride(1), dtype_code(k_new)
     _check(lib().vc_draft_attn_quant(ctypes.byref(d), n_q, r, _ptr(k_new), _ptr(v_new), ndt, stride,
                                      _ptr(q), dtype_code(q), q.shape[1], sm_scale, _ptr(out), _ptr(lse),
