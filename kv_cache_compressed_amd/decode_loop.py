@@ -387,12 +387,10 @@ class LayeredDecoder:
         self.E = _dev(weights["E"], device)
         self.P = None if self.llama else _dev(weights["P"], device)
         self.Wlm = _dev(weights["Wlm"], device)
-        self.Wq = [_dev(w, device) for w in weights["Wq"]]
-        self.Wk = [_dev(w, device) for w in weights["Wk"]]
-        self.Wv = [_dev(w, device) for w in weights["Wv"]]
         self.Wo = [_dev(w, device) for w in weights["Wo"]]
         # q, k, v from one GEMM per layer
-        self.Wqkv = [torch.cat([q, k, v]).contiguous() for q, k, v in zip(self.Wq, self.Wk, self.Wv)]
+        self.Wqkv = [torch.cat([_dev(q, device), _dev(k, device), _dev(v, device)]).contiguous()
+                     for q, k, v in zip(weights["Wq"], weights["Wk"], weights["Wv"])]
         if self.llama:
             lst = lambda k: [_dev(w, device) for w in weights[k]]
             self.g_att, self.g_mlp = lst("g_att"), lst("g_mlp")
@@ -400,7 +398,7 @@ class LayeredDecoder:
             self.W13 = [torch.cat([_dev(a, device), _dev(b, device)]).contiguous()  # gate and up
                         for a, b in zip(weights["W1"], weights["W3"])]
             self.g_f = _dev(weights["g_f"], device)
-        self.nl = len(self.Wq)
+        self.nl = len(self.Wqkv)
         self.V, self.dm = self.E.shape
         assert self.dm % D == 0 and Hq % Hkv == 0
         assert not host_past or kv_dtype == "bf16", "a host-streamed cache is bf16"
