@@ -369,65 +369,121 @@ struct VF32Args {
   float* part_ml;
 };
 
+// fp32 path. Workgroup = 256 threads on one (b, kv head), one chunk of up to RWF of its G*L query
+// rows (row r: head r / L, block row r % L) and one range of the concatenated key sequence
+// [past ; block]. Key tiles of TKF keys and their values are staged in LDS once and serve every row
+// of the chunk. Scores: thread (row group g = tid / 32, key k = tid % 32) takes rows 4g .. 4g+3
+// against key k (the 32 lanes of a row group share its online-softmax state through shuffles);
+// PV: thread (channel tid % 128, row half tid / 128) accumulates 16 rows of one output channel.
+constexpr int TKF = 32;  // keys per tile
+constexpr int RWF = 32;  // query rows per workgroup
+
 __global__ void __launch_bounds__(256) verify_f32_kernel(VF32Args a) {
-  __shared__ float s_q[D];
-  __shared__ float s_p[256];
-  __shared__ float s_red[8];
-  __shared__ float s_o[2][D];
+  __shared__ float s_q[RWF][D + 1];  // padded rows: the 32 key lanes read one column conflict-free
+  __shared__ float s_k[TKF][D + 1];
+  __shared__ float s_v[TKF][D];
+  __shared__ float s_p[RWF][TKF + 1];
+  __shared__ float s_alpha[RWF];
   const int tid = threadIdx.x;
-  const int64_t prow = blockIdx.y;  // (b*Hq + hq)*L + i
   const int split = blockIdx.x;
-  const int i = (int)(prow % a.L);
-  const int64_t bhq = prow / a.L;
-  const int b = (int)(bhq / a.Hq), hq = (int)(bhq % a.Hq);
-  const int bh = b * a.Hkv + hq / a.G;
-  const int64_t nkeys = a.n + i + 1;
+  const int R = a.G * a.L;
+  const int rchunks = (R + RWF - 1) / RWF;
+  const int unit = blockIdx.y / rchunks, r0 = (blockIdx.y % rchunks) * RWF;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int nrows = min(RWF, R - r0);
+  const int64_t nkeys = a.n + a.L;
   const int64_t k_begin = nkeys * split / a.splits, k_end = nkeys * (split + 1) / a.splits;
-  if (tid < D) s_q[tid] = a.q[prow * D + tid] * a.qscale;
-  __syncthreads();
-  float m_run = -INFINITY, l_run = 0.f, o_acc = 0.f;
-  const int c = tid & (D - 1), half = tid >> 7;
-  for (int64_t k0 = k_begin; k0 < k_end; k0 += 256) {
-    const int64_t key = k0 + tid;
-    float s = -INFINITY;
-    if (key < k_end) {
-      const float* kr = key < a.n ? a.k_past + ((int64_t)bh * a.past_stride + key) * D
-                                  : a.k_blk + ((int64_t)bh * a.L + (key - a.n)) * D;
-      float acc = 0.f;
-      for (int cc = 0; cc < D; ++cc) acc += s_q[cc] * kr[cc];
-      s = acc;
-    }
-    const float mx_w = wave_max(s);
-    if ((tid & 63) == 0) s_red[tid >> 6] = mx_w;
-    __syncthreads();
-    const float mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float p = (key < k_end) ? __builtin_amdgcn_exp2f(s - m_new) : 0.f;
-    s_p[tid] = p;
-    const float ps = wave_sum(p);
-    __syncthreads();
-    if ((tid & 63) == 0) s_red[4 + (tid >> 6)] = ps;
-    __syncthreads();
-    l_run = l_run * alpha + (s_red[4] + s_red[5] + s_red[6] + s_red[7]);
-    m_run = m_new;
-    o_acc *= alpha;
-    const int nk = (int)min<int64_t>(256, k_end - k0);
-    for (int t = half; t < nk; t += 2) {
-      const int64_t key2 = k0 + t;
-      const float* vr = key2 < a.n ? a.v_past + ((int64_t)bh * a.past_stride + key2) * D
-                                   : a.v_blk + ((int64_t)bh * a.L + (key2 - a.n)) * D;
-      o_acc += s_p[t] * vr[c];
-    }
-    __syncthreads();
+  auto prow_of = [&](int r) {  // global query row of chunk row r
+    const int rr = r0 + r;
+    return ((int64_t)b * a.Hq + kvh * a.G + rr / a.L) * a.L + rr % a.L;
+  };
+  for (int e = tid; e < RWF * D; e += 256) {
+    const int r = e / D, c = e % D;
+    s_q[r][c] = r < nrows ? a.q[prow_of(r) * D + c] * a.qscale : 0.f;
   }
-  s_o[half][c] = o_acc;
-  __syncthreads();
-  if (tid < D) {
-    a.part_o[(prow * a.splits + split) * D + tid] = s_o[0][tid] + s_o[1][tid];
-    if (tid == 0) {
-      a.part_ml[(prow * a.splits + split) * 2 + 0] = (l_run > 0.f) ? m_run * LN2 : -INFINITY;
-      a.part_ml[(prow * a.splits + split) * 2 + 1] = l_run;
+  const int kk = tid & 31, rg = tid >> 5;    // score mapping
+  const int cc = tid & (D - 1), h2 = tid >> 7;  // PV mapping
+  float m_run[4], l_run[4];
+  int64_t lim[4];  // last visible key of each score row (row i sees keys 0 .. n + i)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+    const int r = rg * 4 + j;
+    lim[j] = r < nrows ? a.n + (r0 + r) % a.L : -1;
+  }
+  float o[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) o[r] = 0.f;
+
+  for (int64_t kt = k_begin; kt < k_end; kt += TKF) {
+    __syncthreads();  // the previous tile's LDS reads are done (and s_q is written)
+    for (int e = tid; e < TKF * D / 4; e += 256) {
+      const int t = e / (D / 4), c4 = (e % (D / 4)) * 4;
+      const int64_t key = kt + t;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (key < k_end) {
+        const int64_t off = key < a.n ? ((int64_t)unit * a.past_stride + key) * D
+                                      : ((int64_t)unit * a.L + (key - a.n)) * D;
+        const float* kb = key < a.n ? a.k_past : a.k_blk;
+        const float* vb = key < a.n ? a.v_past : a.v_blk;
+        kv = *reinterpret_cast<const f32x4*>(kb + off + c4);
+        vv = *reinterpret_cast<const f32x4*>(vb + off + c4);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s_k[t][c4 + u] = kv[u];
+      *reinterpret_cast<f32x4*>(&s_v[t][c4]) = vv;
+    }
+    __syncthreads();
+    const int64_t key = kt + kk;
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int c = 0; c < D; ++c) {
+      const float kc = s_k[kk][c];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[j] = fmaf(s_q[rg * 4 + j][c], kc, sc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = key < k_end && key <= lim[j];
+      float mx = ok ? sc[j] : -INFINITY;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      const float m_new = fmaxf(m_run[j], mx);
+      const float p = ok ? __builtin_amdgcn_exp2f(sc[j] - m_new) : 0.f;
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[j] - m_new);
+      float ps = p;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) ps += __shfl_xor(ps, off, 64);
+      l_run[j] = l_run[j] * alpha + ps;
+      m_run[j] = m_new;
+      s_p[rg * 4 + j][kk] = p;
+      if (kk == 0) s_alpha[rg * 4 + j] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = h2 * 16 + r;
+      float acc = o[r] * s_alpha[row];
+#pragma unroll 8
+      for (int t = 0; t < TKF; ++t) acc = fmaf(s_p[row][t], s_v[t][cc], acc);
+      o[r] = acc;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = h2 * 16 + r;
+    if (row < nrows) a.part_o[(prow_of(row) * a.splits + split) * D + cc] = o[r];
+  }
+  if (kk == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = rg * 4 + j;
+      if (row < nrows) {
+        const int64_t pr = prow_of(row);
+        a.part_ml[(pr * a.splits + split) * 2 + 0] = l_run[j] > 0.f ? m_run[j] * LN2 : -INFINITY;
+        a.part_ml[(pr * a.splits + split) * 2 + 1] = l_run[j];
+      }
     }
   }
 }
@@ -439,7 +495,10 @@ VerifyPlan plan_verify(int B, int Hq, int Hkv, int L, int64_t n, int past_on_hos
   VerifyPlan p{};
   const int64_t units = (int64_t)B * Hkv;
   if (dtype == VC_F32) {
-    p.past_splits = (int)std::max<int64_t>(1, std::min<int64_t>(16, (n + L + 1023) / 1024));
+    // enough (split, unit, row chunk) workgroups to fill the chip, at least one key tile each
+    const int64_t tiles = (n + L + TKF - 1) / TKF;
+    const int64_t wgs = units * ((int64_t)(Hq / Hkv) * L + RWF - 1) / RWF;
+    p.past_splits = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (512 + wgs - 1) / wgs));
     p.chunks = 0;
     p.chunk_tokens = 0;
     p.total_splits = p.past_splits;
@@ -550,8 +609,9 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
     a.qscale = qscale;
     a.part_o = part_o;
     a.part_ml = part_ml;
-    hipLaunchKernelGGL(verify_f32_kernel, dim3(plan.total_splits, (unsigned)rows), dim3(256), 0,
-                       compute, a);
+    const unsigned rchunks = (unsigned)((G * L + RWF - 1) / RWF);
+    hipLaunchKernelGGL(verify_f32_kernel, dim3(plan.total_splits, (unsigned)(B * Hkv) * rchunks),
+                       dim3(256), 0, compute, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     return launch_merge(part_o, part_ml, (int64_t)rows, plan.total_splits, out, lse, compute);
   }
