@@ -348,7 +348,47 @@ def _e2e_decode(torch, seed: int, context: int, tokens: int) -> dict:
     return out
 
 
-def _e2e_llama(torch, seed: int, context: int, tokens: int, bits: int = 2, x: int = 30) -> dict:
+def _e2e_llama_batch(torch, W, prompts, tokens: int, bits: int, x: int, opts: dict) -> dict:
+    """The batched form: every request drafts and verifies in the same rounds (the layer's GEMMs
+    over all rows, attention per request), accepts its own counts and keeps its own context
+    length; greedy decoding of the same batch is the baseline."""
+    from kv_cache_compressed_amd.decode_loop import BatchedLlamaDecoder
+
+    out, seqs = {}, {}
+    for name, xx in (("vericache", x), ("greedy", 0)):
+        t0 = time.perf_counter()
+        dec = BatchedLlamaDecoder(W, 16, 4, prompts, x=xx, bits=bits, R=128, max_new=tokens + 96, **opts)
+        torch.cuda.synchronize()
+        t_prefill = time.perf_counter() - t0
+        dec.warm()
+        for j in range(dec.x):  # one untimed round
+            dec.draft_step(j)
+        dec.verify_step()
+        warm = dec.commit()
+        torch.cuda.synchronize()
+        r0 = len(dec.rounds[0])
+        t0 = time.perf_counter()
+        gen = dec.generate(tokens)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        emitted = sum(sum(a + 1 for a in r[r0:]) for r in dec.rounds)
+        out[name] = {"tok_s": round(emitted / el, 2), "emitted": emitted,
+                     "rounds": len(dec.rounds[0]) - r0, "prefill_s": round(t_prefill, 2)}
+        if xx:
+            out[name]["mean_accepted"] = round(float(np.mean([a for r in dec.rounds for a in r[r0:]])), 2)
+        seqs[name] = [w + g for w, g in zip(warm, gen)]
+        del dec
+    out["speedup"] = round(out["vericache"]["tok_s"] / out["greedy"]["tok_s"], 3)
+    div = []
+    for a, b in zip(seqs["vericache"], seqs["greedy"]):
+        m = min(len(a), len(b))
+        div.append(next((i for i in range(m) if a[i] != b[i]), None))
+    out["first_divergence"] = div if any(d is not None for d in div) else None
+    return out
+
+
+def _e2e_llama(torch, seed: int, context: int, tokens: int, bits: int = 2, x: int = 30,
+               batch: int = 1) -> dict:
     """Token-level decoding of one request on a random-init 4-layer Llama-form decoder (d_model 2048,
     16 query / 4 kv heads, d 128, SwiGLU width 5632, vocab 32000, weights ~N(0, 0.02) rounded to
     bf16 values, gains 1; fp32 arithmetic outside the attention calls) with a `context`-token
@@ -370,8 +410,14 @@ def _e2e_llama(torch, seed: int, context: int, tokens: int, bits: int = 2, x: in
     prompt = torch.randint(0, V, (context,), generator=g, device=dev).tolist()
     opts = dict(kv_dtype="bf16", host_past=True, chunk_tokens=65536)
     out = {"context": context, "tokens": tokens, "drafter": f"KIVI {bits}-bit, x = {x}",
+           "batch": batch,
            "model": "4 Llama-form layers, d_model 2048, 16/4 heads, d 128, SwiGLU 5632, vocab 32000, "
                     "bf16 caches in pinned host memory"}
+    if batch > 1:
+        prompts = [prompt] + [torch.randint(0, V, (context,), generator=g, device=dev).tolist()
+                              for _ in range(batch - 1)]
+        out.update(_e2e_llama_batch(torch, W, prompts, tokens, bits, x, opts))
+        return out
     seqs = {}
     for name in ("vericache", "greedy"):
         t0 = time.perf_counter()
@@ -459,6 +505,8 @@ def main():
     ap.add_argument("--llama-tokens", type=int, default=512)
     ap.add_argument("--llama-bits", type=int, default=2, choices=[2, 4])
     ap.add_argument("--llama-x", type=int, default=30, help="draft length of the Llama-form run")
+    ap.add_argument("--llama-batch", type=int, default=1,
+                    help="requests decoded together in the Llama-form run (config 5: 16)")
     ap.add_argument("--e2e-context", type=int, default=0,
                     help="also decode one request token by token on a one-layer decoder with a "
                          "host-streamed bf16 cache of this many tokens: VeriCache vs greedy")
@@ -605,7 +653,7 @@ def main():
         line["e2e_decode"] = _e2e_decode(torch, args.seed, args.e2e_context, args.e2e_tokens)
     if args.llama_context > 0:
         line["e2e_llama"] = _e2e_llama(torch, args.seed, args.llama_context, args.llama_tokens,
-                                       args.llama_bits, args.llama_x)
+                                       args.llama_bits, args.llama_x, args.llama_batch)
     if not args.no_cpu_baseline and args.workload == "c2":
         line["cpu_baseline"] = cpu_baseline(w, inputs, a_plus_1, args.cpu_draft_steps,
                                             args.cpu_verify_heads)

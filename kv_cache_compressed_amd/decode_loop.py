@@ -750,3 +750,220 @@ class LayeredGreedyDecoder(LayeredDecoder):
             self.n += 1
         self.i = i0 + steps
         return [int(t) for t in self.toks[i0 + 1:i0 + steps + 1].tolist()]
+
+
+class BatchedLlamaDecoder:
+    """VeriCache decoding of B requests at once on Llama-form layers (weights as for
+    LayeredDecoder's Llama form). Every request keeps its own full caches (HBM or pinned host
+    memory), KIVI caches, context length and accepted counts, so requests that accept different
+    numbers of drafts drift apart and each still emits exactly its own full-KV greedy tokens. The
+    layer's norms, GEMMs, rotations and MLP run once over all requests' rows (rotation angles from
+    each row's own position); attention, quantisation, appends, logits and accept are libvc calls,
+    attention one call per request (its own context length). x = 0 gives plain greedy decoding of
+    the batch (a verify of one row per request over the full caches)."""
+
+    def __init__(self, weights, Hq: int, Hkv: int, prompts, x: int, bits: int = 4, R: int = 32,
+                 max_new: int = 256, kv_dtype: str = "f32", host_past: bool = False,
+                 chunk_tokens: int = 65536, rope_theta: float = 500000.0, device: str = "cuda"):
+        assert "g_att" in weights, "Llama-form weights"
+        self.E, self.Wlm = _dev(weights["E"], device), _dev(weights["Wlm"], device)
+        self.g_f = _dev(weights["g_f"], device)
+        lst = lambda k: [_dev(w, device) for w in weights[k]]
+        self.g_att, self.g_mlp, self.Wo, self.W2 = lst("g_att"), lst("g_mlp"), lst("Wo"), lst("W2")
+        self.Wqkv = [torch.cat([_dev(q, device), _dev(k, device), _dev(v, device)]).contiguous()
+                     for q, k, v in zip(weights["Wq"], weights["Wk"], weights["Wv"])]
+        self.W13 = [torch.cat([_dev(a, device), _dev(b, device)]).contiguous()
+                    for a, b in zip(weights["W1"], weights["W3"])]
+        self.nl, (self.V, self.dm) = len(self.Wqkv), self.E.shape
+        assert self.dm % D == 0 and Hq % Hkv == 0
+        assert not host_past or kv_dtype == "bf16", "a host-streamed cache is bf16"
+        self.tdt = torch.float32 if kv_dtype == "f32" else torch.bfloat16
+        self.vdt = vc.VC_F32 if kv_dtype == "f32" else vc.VC_BF16
+        self.Hq, self.Hkv, self.x, self.R = Hq, Hkv, x, R
+        self.L = L = x + 1
+        self.host, self.chunk, self.device = host_past, chunk_tokens, device
+        self.copy_stream = torch.cuda.Stream() if host_past else None
+        prompts = [[int(t) for t in p] for p in prompts]
+        self.B = B = len(prompts)
+        self.n = [len(p) - 1 for p in prompts]
+        self.cap = (max(self.n) + max_new + 2 * L + 63) // 32 * 32
+        ang = np.arange(self.cap)[:, None] * rope_theta ** (-2.0 * np.arange(D // 2) / D)
+        cos = torch.from_numpy(np.cos(ang).astype(np.float32)).to(device)
+        sin = torch.from_numpy(np.sin(ang).astype(np.float32)).to(device)
+        self.cs = torch.stack([torch.cat([cos, cos], 1), torch.cat([-sin, sin], 1)], 1).contiguous()
+        f32 = dict(dtype=torch.float32, device=device)
+        tk = dict(dtype=self.tdt, device=device)
+        i32 = dict(dtype=torch.int32, device=device)
+        nl = self.nl
+        self.stores = [[_Store(Hkv, self.cap, self.tdt, host_past, device) for _ in range(nl)]
+                       for _ in range(B)]
+        meta = vc.VC_F32 if kv_dtype == "f32" else vc.VC_F16
+        res_cap = (R + 32 + L + 31) // 32 * 32
+        self.caches = [[vc.KiviCache(1, Hkv, self.cap, bits, meta, meta, res_cap, device)
+                        for _ in range(nl)] for _ in range(B)]
+        self.n_q = [32 * (max(0, n - R) // 32) for n in self.n]
+        self.qkvc = torch.zeros((B, Hq + 2 * Hkv, D), **tk)       # draft rows' q, k, v
+        self.od = torch.zeros((B, Hq, D), **f32)
+        self.lse_d = torch.zeros((B, Hq), **f32)
+        self.qv = torch.zeros((B, Hq, L, D), **tk)
+        self.kv_ = [torch.zeros((B, Hkv, L, D), **tk) for _ in range(nl)]  # verifier's k, v
+        self.vv_ = [torch.zeros((B, Hkv, L, D), **tk) for _ in range(nl)]
+        self.ov = torch.zeros((B, Hq, L, D), **f32)
+        self.lse_v = torch.zeros((B, Hq, L), **f32)
+        self.logits_v = torch.zeros((B, L, self.V), **f32)
+        self.tok = torch.zeros((B, L + 1), **i32)   # per request: block entries 0..x (+ spare)
+        self.accept_len = torch.zeros((B,), **i32)
+        self.next_tok = torch.zeros((B,), **i32)
+        self.argmax_v = torch.zeros((B, L), **i32)
+        self.ws_draft = vc.Workspace(device)
+        self.ws_verify = vc.Workspace(device)
+        self.ws_proj = torch.zeros((vc.vc_project_workspace(B, 1, self.V) + 3) // 4, **i32)
+        for b, p in enumerate(prompts):
+            self._prefill(b, p)
+        self.tok[:, 0] = torch.tensor([p[-1] for p in prompts], **i32)
+        self.rounds = [[] for _ in range(B)]
+
+    # ---- the layer outside attention, over all rows ------------------------------------------
+    def _rms(self, X, g):
+        return torch.nn.functional.rms_norm(X, (self.dm,), g, 1e-5)
+
+    def _qkv(self, l: int, X, pos):
+        """Rows X [m, dm] at positions pos (device int64 [m]) -> [m, Hq + 2 Hkv, 128] fp32 with q
+        and k rotated."""
+        Y = (self._rms(X, self.g_att[l]) @ self.Wqkv[l].T).view(X.shape[0], -1, D)
+        cs = self.cs.index_select(0, pos)
+        qk = Y[:, :self.Hq + self.Hkv]
+        r = torch.roll(qk, D // 2, dims=-1)
+        qk.mul_(cs[:, 0:1])
+        qk.addcmul_(r, cs[:, 1:2])
+        return Y
+
+    def _block_out(self, l: int, X, O):
+        X = X + O @ self.Wo[l].T
+        Z = self._rms(X, self.g_mlp[l]) @ self.W13[l].T
+        F = Z.shape[-1] // 2
+        return X + (torch.nn.functional.silu(Z[:, :F]) * Z[:, F:]) @ self.W2[l].T
+
+    def _verify(self, b: int, l: int, q, k, v, n: int, out, lse):
+        host = self.host and n > 0
+        nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, q.shape[2], n, host, self.chunk, self.vdt)
+        st = self.stores[b][l]
+        kp, vp, stride = (st.k, st.v, self.cap) if n > 0 else (k, v, q.shape[2])
+        vc.vc_verify_attn(q, k, v, kp, vp, n, out, lse, self.ws_verify.get(nb), SM_SCALE,
+                          past_stride=stride, past_on_host=host, chunk_tokens=self.chunk,
+                          copy_stream=self.copy_stream)
+
+    def _prefill(self, b: int, prompt):
+        """Request b's positions 0..n-1, layer by layer: caches, then causal attention in 32-row
+        blocks over the layer's device-resident keys/values."""
+        n, Hq, Hkv = self.n[b], self.Hq, self.Hkv
+        X = self.E[torch.tensor(prompt[:n], device=self.device)]
+        pos = torch.arange(n, device=self.device)
+        lay = lambda Y: Y.transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
+        for l in range(self.nl):
+            Y = self._qkv(l, X, pos)
+            Q, K, V = Y[:, :Hq], lay(Y[:, Hq:Hq + Hkv]), lay(Y[:, Hq + Hkv:])
+            self.stores[b][l].write(0, K, V)
+            c, nq = self.caches[b][l], self.n_q[b]
+            if nq:
+                vc.vc_quantize_kv(c, K, V, 0, nq, src_bh_stride=n * D)
+            if n > nq:
+                vc.vc_kivi_append(c, K[:, :, nq:], V[:, :, nq:], nq, n - nq, src_bh_stride=n * D)
+            O = torch.zeros((n, Hq * D), dtype=torch.float32, device=self.device)
+            for b0 in range(0, n, 32):
+                b1 = min(n, b0 + 32)
+                m = b1 - b0
+                o = torch.zeros((1, Hq, m, D), dtype=torch.float32, device=self.device)
+                lse = torch.zeros((1, Hq, m), dtype=torch.float32, device=self.device)
+                nb = vc.vc_verify_workspace(1, Hq, Hkv, m, b0, False, 0, self.vdt)
+                vc.vc_verify_attn(lay(Q[b0:b1]), K[:, :, b0:b1].contiguous(), V[:, :, b0:b1].contiguous(),
+                                  K, V, b0, o, lse, self.ws_verify.get(nb), SM_SCALE, past_stride=n)
+                O[b0:b1] = o[0].transpose(0, 1).reshape(m, -1)
+            X = self._block_out(l, X, O)
+
+    # ---- one round ------------------------------------------------------------------------
+    def draft_step(self, j: int):
+        Hq, Hkv, B = self.Hq, self.Hkv, self.B
+        pos = torch.tensor([n + j for n in self.n], device=self.device)
+        X = self.E[self.tok[:, j].long()]
+        for l in range(self.nl):
+            self.qkvc.copy_(self._qkv(l, X, pos))
+            for b in range(B):
+                c, nq = self.caches[b][l], self.n_q[b]
+                r = self.n[b] - nq + j + 1
+                nb = vc.vc_draft_quant_workspace(c, nq, r, Hq)
+                vc.vc_draft_attn_quant(c, nq, r, self.qkvc[b:b + 1, :Hq], self.od[b:b + 1],
+                                       self.lse_d[b:b + 1], self.ws_draft.get(nb), SM_SCALE,
+                                       k_new=self.qkvc[b:b + 1, Hq:Hq + Hkv],
+                                       v_new=self.qkvc[b:b + 1, Hq + Hkv:])
+            X = self._block_out(l, X, self.od.view(B, -1))
+        h = self._rms(X, self.g_f)
+        vc.vc_project_logits(self.Wlm, h.view(B, -1, D), argmax=self.tok.view(-1)[j + 1:],
+                             argmax_b_stride=self.L + 1, ws=self.ws_proj)
+
+    def verify_step(self):
+        Hq, Hkv, B, L = self.Hq, self.Hkv, self.B, self.L
+        pos = (torch.tensor(self.n, device=self.device)[:, None]
+               + torch.arange(L, device=self.device)).view(-1)
+        X = self.E[self.tok[:, :L].reshape(-1).long()]
+        for l in range(self.nl):
+            Y = self._qkv(l, X, pos).view(B, L, -1, D)
+            self.qv.copy_(Y[:, :, :Hq].transpose(1, 2))
+            self.kv_[l].copy_(Y[:, :, Hq:Hq + Hkv].transpose(1, 2))
+            self.vv_[l].copy_(Y[:, :, Hq + Hkv:].transpose(1, 2))
+            for b in range(B):
+                self._verify(b, l, self.qv[b:b + 1], self.kv_[l][b:b + 1], self.vv_[l][b:b + 1],
+                             self.n[b], self.ov[b:b + 1], self.lse_v[b:b + 1])
+            X = self._block_out(l, X, self.ov.transpose(1, 2).reshape(B * L, -1))
+        h = self._rms(X, self.g_f).view(B, L, -1, D).permute(0, 2, 1, 3).contiguous()
+        vc.vc_project_logits(self.Wlm, h, logits=self.logits_v)
+        drafts = self.tok[:, 1:L].contiguous() if L > 1 else None
+        vc.vc_accept(self.logits_v, drafts, self.accept_len, self.next_tok, self.argmax_v)
+
+    def commit(self):
+        """Per request: keep entries 0..a_b (the verifier's keys/values) in the full caches and the
+        residual rings, flush whole groups, start the next round from the emitted token. Returns
+        each request's emitted tokens."""
+        acc = self.accept_len.tolist()
+        nxt = self.next_tok.tolist()
+        toks = self.tok.tolist()
+        L, out = self.L, []
+        for b in range(self.B):
+            a = acc[b]
+            out.append(toks[b][1:a + 1] + [nxt[b]])
+            n0 = self.n[b]
+            assert n0 + a + 1 + L <= self.cap, "cache capacity exhausted (raise max_new)"
+            for l in range(self.nl):
+                k, v = self.kv_[l][b:b + 1, :, :a + 1], self.vv_[l][b:b + 1, :, :a + 1]
+                self.stores[b][l].write(n0, k, v)
+                vc.vc_kivi_append(self.caches[b][l], k, v, n0, a + 1, src_bh_stride=L * D)
+            self.n[b] = n0 + a + 1
+            while self.n[b] - self.n_q[b] >= self.R + 32:
+                g0 = self.n_q[b]
+                for l in range(self.nl):
+                    Kg, Vg, stride = self.stores[b][l].device_rows(g0, g0 + 32)
+                    vc.vc_quantize_kv(self.caches[b][l], Kg, Vg, g0, 32, src_bh_stride=stride)
+                self.n_q[b] = g0 + 32
+            self.rounds[b].append(a)
+        self.tok[:, 0] = self.next_tok
+        return out
+
+    def warm(self):
+        """Size the workspaces for the largest context this decoder can reach."""
+        self.ws_verify.get(vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, self.cap, self.host,
+                                                  self.chunk, self.vdt))
+        r = self.R + 32 + self.L
+        self.ws_draft.get(vc.vc_draft_quant_workspace(self.caches[0][0], (self.cap - r) // 32 * 32, r,
+                                                      self.Hq))
+        torch.cuda.synchronize()
+
+    def generate(self, steps: int):
+        """Rounds until every request has `steps` more tokens; returns each request's tokens."""
+        out = [[] for _ in range(self.B)]
+        while min(len(o) for o in out) < steps:
+            for j in range(self.x):
+                self.draft_step(j)
+            self.verify_step()
+            for o, em in zip(out, self.commit()):
+                o += em
+        return [o[:steps] for o in out]

@@ -986,6 +986,46 @@ def test_llama_decoder_emits_full_kv_greedy(gpu_lib, layers, bits, kv, host, gra
     assert dec.n_q > 32 * ((len(prompt) - 1 - 32) // 32), "the loop must have flushed"
 
 
+@pytest.mark.parametrize("bits,kv,host", [(4, "f32", False), (2, "bf16", True)])
+def test_batched_llama_decoder_per_request_greedy(gpu_lib, bits, kv, host):
+    """Three requests with prompts of different lengths decoded together (the layer's GEMMs over
+    all rows, attention per request): each request accepts its own counts, so the context lengths
+    drift apart, and each still emits its own prompt's full-KV greedy tokens (oracle), as does the
+    batch's greedy decoding (x = 0)."""
+    from kv_cache_compressed_amd.decode_loop import BatchedLlamaDecoder
+    from oracle import loop as oloop
+
+    m = oloop.LlamaModel(seed=13, vocab=384, dm=256, d=128, Hq=4, Hkv=2, layers=2, F=512,
+                         kv_bf16=kv == "bf16")
+    W = {k: getattr(m, k).astype(np.float32) for k in ("E", "Wlm", "g_f")}
+    per_layer = ("g_att", "Wq", "Wk", "Wv", "Wo", "g_mlp", "W1", "W2", "W3")
+    for k in per_layer:
+        W[k] = [w.astype(np.float32) for w in getattr(m, k)]
+    for k in ("E", "Wlm", "g_f"):
+        setattr(m, k, W[k].astype(np.float64))
+    for k in per_layer:
+        setattr(m, k, [w.astype(np.float64) for w in W[k]])
+    g = np.random.default_rng(17)
+    prompts = [[int(t) for t in g.integers(0, 384, n)] for n in (150, 97, 181)]
+    steps = 30
+    opts = dict(kv_dtype=kv, host_past=host, chunk_tokens=64)
+    dec = BatchedLlamaDecoder(W, 4, 2, prompts, x=6, bits=bits, R=32, max_new=steps + 32, **opts)
+    got = dec.generate(steps)
+    greedy = BatchedLlamaDecoder(W, 4, 2, prompts, x=0, max_new=steps + 8, **opts).generate(steps)
+    print(f"[batched llama {bits}-bit {kv}{' host' if host else ''}] accepted per round "
+          f"{dec.rounds}; n {dec.n}", flush=True)
+    assert len(set(len(r) for r in dec.rounds)) == 1 and len(set(dec.n)) > 1
+    for b, prompt in enumerate(prompts):
+        ref = oloop.greedy_llama(m, prompt, steps)
+        for what, seq in (("VeriCache", got[b]), ("greedy", greedy[b])):
+            if seq != ref:
+                t = next(i for i in range(steps) if seq[i] != ref[i])
+                z = m.logits_all(prompt + ref[:t])[-1]
+                gap = float(oacc.top2_gap(z[None])[0])
+                assert gap < GAP, f"request {b} {what}: token {t} differs, oracle top-2 gap {gap}"
+                print(f"request {b} {what}: first divergence at token {t}: near-tie", flush=True)
+
+
 def test_token_decoders_staggered_two_requests(gpu_lib):
     """Two requests decoded token by token over host-streamed bf16 caches: the staggered schedule
     (harness.staggered_decode) emits, per request, the same tokens as the lock-step one, and those
