@@ -379,6 +379,38 @@ def _e2e_llama_batch(torch, W, prompts, tokens: int, bits: int, x: int, opts: di
         seqs[name] = [w + g for w, g in zip(warm, gen)]
         del dec
     out["speedup"] = round(out["vericache"]["tok_s"] / out["greedy"]["tok_s"], 3)
+    # two groups of half the batch each, lock-step against staggered on two streams
+    # (harness.staggered_decode: one group's verify streams while the other drafts)
+    from kv_cache_compressed_amd import harness
+
+    h = len(prompts) // 2
+    rounds = max(1, out["vericache"]["rounds"] // 2)
+    two = {"groups": 2, "requests_per_group": h, "rounds": rounds}
+    for name in ("lockstep", "staggered"):
+        g0 = BatchedLlamaDecoder(W, 16, 4, prompts[:h], x=x, bits=bits, R=128,
+                                 max_new=rounds * (x + 1) + 96, **opts)
+        g1 = BatchedLlamaDecoder(W, 16, 4, prompts[h:2 * h], x=x, bits=bits, R=128,
+                                 max_new=rounds * (x + 1) + 96, copy_stream=g0.copy_stream, **opts)
+        groups = [g0, g1]
+        for g in groups:
+            g.warm()
+        # one untimed round each (first launches), then the timed schedule
+        harness.lockstep_decode(groups, 1, lambda gi, r: ())
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if name == "lockstep":
+            acc = harness.lockstep_decode(groups, rounds, lambda gi, r: ())
+        else:
+            acc = harness.staggered_decode(groups, [torch.cuda.current_stream(), torch.cuda.Stream()],
+                                           rounds, lambda gi, r: ())
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        emitted = sum(len(em) for ga in acc for ems in ga for em in ems)
+        two[name] = {"tok_s": round(emitted / el, 2), "emitted": emitted,
+                     "ms_per_round": round(el / rounds * 1e3, 2)}
+        del groups, g0, g1
+    two["speedup"] = round(two["staggered"]["tok_s"] / two["lockstep"]["tok_s"], 3)
+    out["two_groups"] = two
     div = []
     for a, b in zip(seqs["vericache"], seqs["greedy"]):
         m = min(len(a), len(b))

@@ -764,7 +764,8 @@ class BatchedLlamaDecoder:
 
     def __init__(self, weights, Hq: int, Hkv: int, prompts, x: int, bits: int = 4, R: int = 32,
                  max_new: int = 256, kv_dtype: str = "f32", host_past: bool = False,
-                 chunk_tokens: int = 65536, rope_theta: float = 500000.0, device: str = "cuda"):
+                 chunk_tokens: int = 65536, rope_theta: float = 500000.0, copy_stream=None,
+                 device: str = "cuda"):
         assert "g_att" in weights, "Llama-form weights"
         self.E, self.Wlm = _dev(weights["E"], device), _dev(weights["Wlm"], device)
         self.g_f = _dev(weights["g_f"], device)
@@ -782,7 +783,7 @@ class BatchedLlamaDecoder:
         self.Hq, self.Hkv, self.x, self.R = Hq, Hkv, x, R
         self.L = L = x + 1
         self.host, self.chunk, self.device = host_past, chunk_tokens, device
-        self.copy_stream = torch.cuda.Stream() if host_past else None
+        self.copy_stream = (copy_stream or torch.cuda.Stream()) if host_past else None
         prompts = [[int(t) for t in p] for p in prompts]
         self.B = B = len(prompts)
         self.n = [len(p) - 1 for p in prompts]
@@ -956,6 +957,14 @@ class BatchedLlamaDecoder:
         self.ws_draft.get(vc.vc_draft_quant_workspace(self.caches[0][0], (self.cap - r) // 32 * 32, r,
                                                       self.Hq))
         torch.cuda.synchronize()
+
+    def draft_phase(self):
+        for j in range(self.x):
+            self.draft_step(j)
+
+    def set_round_inputs(self):
+        """Nothing to load: each request's next round starts from its committed token (for the
+        schedules in harness)."""
 
     def generate(self, steps: int):
         """Rounds until every request has `steps` more tokens; returns each request's tokens."""

@@ -1026,6 +1026,34 @@ def test_batched_llama_decoder_per_request_greedy(gpu_lib, bits, kv, host):
                 print(f"request {b} {what}: first divergence at token {t}: near-tie", flush=True)
 
 
+def test_batched_llama_groups_staggered_equal_lockstep(gpu_lib):
+    """Two groups of two requests each (host-streamed bf16 caches, one copy stream): the staggered
+    schedule emits exactly the lock-step schedule's tokens, round by round."""
+    from kv_cache_compressed_amd import harness
+    from kv_cache_compressed_amd.decode_loop import BatchedLlamaDecoder
+    from oracle import loop as oloop
+
+    m = oloop.LlamaModel(seed=19, vocab=384, dm=256, d=128, Hq=4, Hkv=2, layers=2, F=512, kv_bf16=True)
+    W = {k: getattr(m, k).astype(np.float32) for k in ("E", "Wlm", "g_f")}
+    for k in ("g_att", "Wq", "Wk", "Wv", "Wo", "g_mlp", "W1", "W2", "W3"):
+        W[k] = [w.astype(np.float32) for w in getattr(m, k)]
+    g = np.random.default_rng(23)
+    prompts = [[int(t) for t in g.integers(0, 384, n)] for n in (120, 90, 140, 100)]
+    opts = dict(x=6, bits=4, R=32, max_new=64, kv_dtype="bf16", host_past=True, chunk_tokens=64)
+    res = {}
+    for name in ("lockstep", "staggered"):
+        g0 = BatchedLlamaDecoder(W, 4, 2, prompts[:2], **opts)
+        g1 = BatchedLlamaDecoder(W, 4, 2, prompts[2:], copy_stream=g0.copy_stream, **opts)
+        if name == "lockstep":
+            res[name] = harness.lockstep_decode([g0, g1], 4, lambda gi, r: ())
+        else:
+            res[name] = harness.staggered_decode([g0, g1], [torch.cuda.current_stream(),
+                                                            torch.cuda.Stream()], 4, lambda gi, r: ())
+        torch.cuda.synchronize()
+    print(f"[batched groups] lock-step {res['lockstep']}", flush=True)
+    assert res["staggered"] == res["lockstep"]
+
+
 def test_token_decoders_staggered_two_requests(gpu_lib):
     """Two requests decoded token by token over host-streamed bf16 caches: the staggered schedule
     (harness.staggered_decode) emits, per request, the same tokens as the lock-step one, and those
