@@ -379,10 +379,12 @@ constexpr int TKF = 32;  // keys per tile
 constexpr int RWF = 32;  // query rows per workgroup
 
 __global__ void __launch_bounds__(256) verify_f32_kernel(VF32Args a) {
-  __shared__ float s_q[RWF][D + 1];  // padded rows: the 32 key lanes read one column conflict-free
-  __shared__ float s_k[TKF][D + 1];
+  // rows padded by 16 bytes: 16-byte reads stay aligned and the 32 key lanes' reads of one column
+  // block spread over the banks
+  __shared__ float s_q[RWF][D + 4];
+  __shared__ float s_k[TKF][D + 4];
   __shared__ float s_v[TKF][D];
-  __shared__ float s_p[RWF][TKF + 1];
+  __shared__ float s_p[RWF][TKF + 4];
   __shared__ float s_alpha[RWF];
   const int tid = threadIdx.x;
   const int split = blockIdx.x;
@@ -430,18 +432,23 @@ __global__ void __launch_bounds__(256) verify_f32_kernel(VF32Args a) {
         kv = *reinterpret_cast<const f32x4*>(kb + off + c4);
         vv = *reinterpret_cast<const f32x4*>(vb + off + c4);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) s_k[t][c4 + u] = kv[u];
+      *reinterpret_cast<f32x4*>(&s_k[t][c4]) = kv;
       *reinterpret_cast<f32x4*>(&s_v[t][c4]) = vv;
     }
     __syncthreads();
     const int64_t key = kt + kk;
     float sc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int c = 0; c < D; ++c) {
-      const float kc = s_k[kk][c];
+#pragma unroll 4
+    for (int c = 0; c < D; c += 4) {
+      const f32x4 k4 = *reinterpret_cast<const f32x4*>(&s_k[kk][c]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sc[j] = fmaf(s_q[rg * 4 + j][c], kc, sc[j]);
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 q4 = *reinterpret_cast<const f32x4*>(&s_q[rg * 4 + j][c]);
+        sc[j] = fmaf(q4[0], k4[0], sc[j]);
+        sc[j] = fmaf(q4[1], k4[1], sc[j]);
+        sc[j] = fmaf(q4[2], k4[2], sc[j]);
+        sc[j] = fmaf(q4[3], k4[3], sc[j]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -465,8 +472,14 @@ __global__ void __launch_bounds__(256) verify_f32_kernel(VF32Args a) {
     for (int r = 0; r < 16; ++r) {
       const int row = h2 * 16 + r;
       float acc = o[r] * s_alpha[row];
-#pragma unroll 8
-      for (int t = 0; t < TKF; ++t) acc = fmaf(s_p[row][t], s_v[t][cc], acc);
+#pragma unroll 2
+      for (int t = 0; t < TKF; t += 4) {
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[row][t]);
+        acc = fmaf(p4[0], s_v[t][cc], acc);
+        acc = fmaf(p4[1], s_v[t + 1][cc], acc);
+        acc = fmaf(p4[2], s_v[t + 2][cc], acc);
+        acc = fmaf(p4[3], s_v[t + 3][cc], acc);
+      }
       o[r] = acc;
     }
   }
