@@ -7,9 +7,9 @@
 // from one-token decoding); "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference", Key
 // Contributions (verification is bound by the interconnect and FLOPs).
 //
-// bf16 path (matrix cores). Workgroup = 4 waves (8 when G > 4) on one (b, kv head) and one range
-// of 32-token key tiles; wave w < G owns query head kvh*G + w and its L rows (two 16-row column
-// tiles). Tiles reach LDS through direct buffer -> LDS copies into a 3-stage ring (two tiles in
+// bf16 path (matrix cores). Workgroup = 4 waves on one (b, kv head), up to 4 of its query heads
+// (ceil(G / 4) workgroups per tile range when G > 4) and one range of 32-token key tiles; wave w
+// owns one query head and its L rows (two 16-row column tiles). Tiles reach LDS through direct buffer -> LDS copies into a 3-stage ring (two tiles in
 // flight), row-major with swizzled 16-byte chunks, one workgroup barrier per tile. QK^T uses
 // v_mfma_f32_16x16x32_bf16 with the keys as the row operand (S^T), so each lane holds 8 token
 // scores of one query row, which is the layout of the PV product's column operand; the values
@@ -52,6 +52,8 @@ struct VArgs {
   const uint16_t* v_blk;   //   (blockIdx.x == splits), causal, written to partial blk_index
   int blk_index;
   int L, Hq, Hkv, G, total_splits;
+  int Gw;                  // query heads per workgroup: G, or 4 when G > 4 (then ceil(G / 4)
+                           //   workgroups per (b, kv head) and tile range, heads 4 z .. 4 z + 3)
   float qscale;            // sm_scale * log2(e)
   float* part_o;
   float* part_ml;
@@ -125,8 +127,9 @@ __device__ __forceinline__ void tile_copy(uint8_t* ring, int slot, __amdgpu_buff
   }
 }
 
-// Workgroup = NW waves (NW >= G) on one (b, kv head) and one range of 32-token tiles; wave w < G
-// owns query head kvh*G + w and its L rows (two 16-row column tiles); all NW waves copy tiles.
+// Workgroup = NW waves on one (b, kv head), heads Gw z .. Gw z + Gw - 1 of its group (z =
+// blockIdx.z) and one range of 32-token tiles; wave w < Gw owns one of them and its L rows (two
+// 16-row column tiles); all NW waves copy tiles.
 // Tiles stream through a RING-stage LDS ring (RING - 1 in flight) with direct buffer -> LDS
 // copies, one barrier per tile. Keys feed QK^T as the row operand; values are read straight into
 // the PV row operand with the LDS transpose read (ds_read_b64_tr_b16): source lane s of a
@@ -154,8 +157,9 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
   const bool causal = blk || a.causal;
   const int sidx = blk ? a.blk_index : a.split_offset + split;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
-  const bool computes = wave < a.G;
-  const int hq = kvh * a.G + min(wave, a.G - 1);
+  const int hg = (int)blockIdx.z * a.Gw + wave;  // head within the kv group
+  const bool computes = wave < a.Gw && hg < a.G;
+  const int hq = kvh * a.G + min(hg, a.G - 1);
 
   // tile range of this split
   const int ntiles = (int)((src_ntok + TK - 1) / TK);  // < 2^18: src_ntok * 256 bytes < 2^31
@@ -518,7 +522,8 @@ VerifyPlan plan_verify(int B, int Hq, int Hkv, int L, int64_t n, int past_on_hos
     p.stage_bytes = 0;
   } else if (!past_on_host) {
     const int64_t tiles = (n + TK - 1) / TK;
-    int64_t s = (256 * WG_PER_CU + units - 1) / units;
+    const int64_t wunits = units * ((Hq / Hkv + 3) / 4);  // workgroups per tile range
+    int64_t s = (256 * WG_PER_CU + wunits - 1) / wunits;
     s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 4));
     if (n == 0) s = 0;
     p.past_splits = (int)s;
@@ -531,7 +536,8 @@ VerifyPlan plan_verify(int B, int Hq, int Hkv, int L, int64_t n, int past_on_hos
     p.chunk_tokens = ct;
     p.chunks = (int)((n + ct - 1) / ct);
     const int64_t tiles = (ct + TK - 1) / TK;
-    int64_t s = (256 * WG_PER_CU + units - 1) / units;
+    const int64_t wunits = units * ((Hq / Hkv + 3) / 4);  // workgroups per tile range
+    int64_t s = (256 * WG_PER_CU + wunits - 1) / wunits;
     s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 4));
     p.past_splits = (int)s;
     p.total_splits = p.chunks * p.past_splits + 1;
@@ -639,14 +645,16 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
   a.qscale = qscale;
   a.part_o = part_o;
   a.part_ml = part_ml;
-  const int NW = G <= 4 ? 4 : 8;
+  // G > 4 runs as ceil(G / 4) 4-wave workgroups per (b, kv head) and tile range (grid.z), each
+  // on up to 4 of the heads: 3 workgroups per CU instead of one 8-wave workgroup at 2 waves per
+  // SIMD; the other workgroups' reads of the same tiles mostly hit L2
+  constexpr int NW = 4;
+  a.Gw = G <= 4 ? G : 4;
+  const unsigned gz = (unsigned)((G + 3) / 4);
   const dim3 block(64 * NW);
   const unsigned units = (unsigned)(B * Hkv);
   auto launch_bf16 = [&](dim3 grid) {
-    if (NW == 4)
-      hipLaunchKernelGGL(verify_bf16_kernel<4>, grid, block, 0, compute, a);
-    else
-      hipLaunchKernelGGL(verify_bf16_kernel<8>, grid, block, 0, compute, a);
+    hipLaunchKernelGGL(verify_bf16_kernel<NW>, grid, block, 0, compute, a);
   };
 
   a.k_blk = nullptr;
@@ -663,7 +671,7 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
     a.causal = 0;
     a.k_blk = static_cast<const uint16_t*>(k_blk);
     a.v_blk = static_cast<const uint16_t*>(v_blk);
-    launch_bf16(dim3(std::max(plan.past_splits, 1), units));
+    launch_bf16(dim3(std::max(plan.past_splits, 1), units, gz));
     if ((err = hipGetLastError()) != hipSuccess) return err;
     return launch_merge(part_o, part_ml, (int64_t)rows, plan.total_splits, out, lse, compute);
   } else {
@@ -706,7 +714,7 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
       a.splits = plan.past_splits;
       a.split_offset = c * plan.past_splits;
       a.causal = 0;
-      launch_bf16(dim3(plan.past_splits, units));
+      launch_bf16(dim3(plan.past_splits, units, gz));
       if ((err = hipGetLastError()) != hipSuccess) break;
       err = hipEventRecord(done[z], compute);
     }
@@ -728,7 +736,7 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
   a.splits = 1;
   a.split_offset = plan.total_splits - 1;
   a.causal = 1;
-  launch_bf16(dim3(1, units));
+  launch_bf16(dim3(1, units, gz));
   if ((err = hipGetLastError()) != hipSuccess) return err;
   return launch_merge(part_o, part_ml, (int64_t)rows, plan.total_splits, out, lse, compute);
 }
