@@ -39,7 +39,7 @@ struct DDArgs {
   float qscale;
 };
 
-__global__ void __launch_bounds__(THREADS) draft_drop_kernel(DDArgs a) {
+__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) draft_drop_kernel(DDArgs a) {
   // per-wave transposed value tiles; reused for the cross-wave merge after the main loop
   __shared__ uint32_t s_raw[WAVES * D * VT_STRIDE];
   __shared__ float s_m[WAVES][8], s_l[WAVES][8];
@@ -220,7 +220,7 @@ DraftDropPlan plan_draft_drop(int B, int Hkv, int Hq, int64_t n_keep) {
   DraftDropPlan p;
   const int64_t units = (int64_t)B * Hkv;
   const int64_t nblk = (n_keep + BLK - 1) / BLK;
-  int64_t s = std::max<int64_t>(1, 512 / units);  // one resident round at 2 workgroups per CU
+  int64_t s = std::max<int64_t>(1, 768 / units);  // one resident round at 3 workgroups per CU
   s = std::min<int64_t>(s, std::max<int64_t>(1, nblk / 8));
   p.splits = (int)std::max<int64_t>(1, s);
   p.ws_bytes = (size_t)B * Hq * p.splits * (D + 2) * sizeof(float);
