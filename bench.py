@@ -14,7 +14,7 @@ Reported (one JSON line):
                launch / mean launch time measured with HIP events on the launch stream, against
                8 TB/s HBM; `traffic` is the counter-measured HBM traffic per launch when a
                committed counter summary for the current kernel source exists, else null
-  cpu_baseline the CPU oracle timed on a bounded sample of the same round (see `sample`)
+  cpu_baseline the CPU oracle timed on one whole request of the same round (see `sample`)
 """
 from __future__ import annotations
 
@@ -71,58 +71,54 @@ def _traffic_per_launch():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inputs, a_plus_1: int, draft_steps: int, verify_heads: int):
-    """Time the oracle (as written, untuned) on a bounded sample of the round and scale it."""
+def cpu_baseline(w, inputs, row: int = 0):
+    """The oracle (as written, untuned) on one whole request of the same round, timed: its 30 draft
+    steps over every query head, the draft logits and argmax, the 31-row verify of every head, the
+    verify logits and the accept step for batch row `row`. value = the tokens that request's round
+    emits (a + 1, the oracle's own accept result) per second of that wall time. The sample is one
+    of the B requests, measured whole; nothing is scaled."""
     from threadpoolctl import threadpool_info
 
     from oracle.round import Round
 
     rnd = Round(w, *inputs)
-    b = 0
-    for h in range(w.Hkv):  # the compressed cache is built before the timed region, as on the GPU
-        rnd.kivi(b, h)
+    if w.drafter == "kivi":  # the compressed cache is built before the timed region, as on the GPU
+        for h in range(w.Hkv):
+            rnd.kivi(row, h)
     t0 = time.perf_counter()
-    for j in range(draft_steps):
-        rnd.draft_step(b, j)
-    t_draft = (time.perf_counter() - t0) / draft_steps
-    heads = list(range(0, w.Hq, w.Hq // verify_heads))[:verify_heads]
-    t0 = time.perf_counter()
-    for hq in heads:
-        rnd.verify_head(b, hq)
-    t_verify = (time.perf_counter() - t0) * (w.Hq / len(heads))
-    t_round = w.B * (w.x * t_draft + t_verify)
+    res = rnd.run(row)
+    el = time.perf_counter() - t0
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-    cores = max(blas) if blas else 1
-    sample = (f"oracle on batch row 0 of the same round: draft steps 0..{draft_steps - 1} "
-              f"(all {w.Hq} query heads) and the verify rows of {len(heads)} of {w.Hq} query heads; "
-              f"scaled linearly to {w.x} draft steps, {w.Hq} heads and {w.B} batch rows "
-              f"(measured {draft_steps * t_draft + t_verify * len(heads) / w.Hq:.1f} s)")
-    return {"value": a_plus_1 / t_round, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample, "seconds_per_round_est": t_round}
+    affinity = len(os.sched_getaffinity(0))
+    threads = max(blas) if blas else 1
+    return {"value": (res["a"] + 1) / el, "unit": "tok/s", "cores": int(min(threads, affinity)),
+            "kind": "oracle",
+            "sample": (f"oracle on batch row {row} of the same round, whole: {w.x} draft steps of all "
+                       f"{w.Hq} query heads with their logits and argmax, the {w.L}-row verify of all "
+                       f"heads, its logits and the accept step (1 of {w.B} requests; measured, not "
+                       f"scaled); emitted {res['a'] + 1} token(s) in {el:.1f} s"),
+            "seconds": round(el, 2), "emitted": int(res["a"] + 1),
+            "host_cores_available": affinity, "blas_threads": int(threads)}
 
 
-def _h2d_rate(torch, st) -> dict:
-    """Achieved pinned host -> HBM rate of a plain copy of the streamed verify's bytes, in the same
-    chunks (median of 5 passes)."""
+def _h2d_rate(torch, vc, st, passes: int = 10) -> dict:
+    """Achieved pinned host -> HBM rate of the streamed verify's own transfer: vc_verify_stream_copies
+    issues exactly the verify's chunk copies (one 2-D copy per chunk per tensor into the two
+    stages) with nothing else; median of `passes` passes."""
     w = st.w
-    ct = w.chunk_tokens
-    dk = torch.empty((w.B, w.Hkv, ct, 128), dtype=st.k_host.dtype, device="cuda")
-    dv = torch.empty_like(dk)
-    nbytes = 2 * w.B * w.Hkv * w.n * 128 * st.k_host.element_size()
+    ws = st._verify_ws()
+    nbytes = 2 * w.B * w.Hkv * st.n * 128 * st.k_host.element_size()
+    copy = st.copy_stream
     times = []
-    for _ in range(5):
+    for _ in range(passes):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for c0 in range(0, w.n, ct):
-            ln = min(ct, w.n - c0)
-            for b in range(w.B):  # one contiguous pinned -> device copy per (b, kv head) slice
-                for h in range(w.Hkv):
-                    dk[b, h, :ln].copy_(st.k_host[b, h, c0:c0 + ln], non_blocking=True)
-                    dv[b, h, :ln].copy_(st.v_host[b, h, c0:c0 + ln], non_blocking=True)
-        torch.cuda.synchronize()
+        vc.vc_verify_stream_copies(st.k_host, st.v_host, st.n, ws, w.B, w.Hq, w.Hkv, w.L, w.chunk_tokens,
+                                   past_stride=st.host_cap, copy_stream=copy)
+        copy.synchronize()
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
-    return {"bytes": nbytes, "seconds": t, "GB_s": nbytes / t / 1e9}
+    return {"bytes": nbytes, "seconds": t, "GB_s": nbytes / t / 1e9, "passes": passes}
 
 
 def _staggering(torch, harness, synth, st0, seed: int, rounds: int) -> dict:
@@ -514,8 +510,6 @@ def main():
                     help="copies of the compressed cache rotated over the draft steps (keeps the "
                          "205 MB working set from being re-served by the 256 MB last-level cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-draft-steps", type=int, default=12)
-    ap.add_argument("--cpu-verify-heads", type=int, default=16)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the rounds, run a plain device-to-device copy of this many MB three "
                          "times (reference kernel of known traffic for HBM counter runs)")
@@ -555,7 +549,7 @@ def main():
 
     import torch
 
-    from kv_cache_compressed_amd import harness, synth
+    from kv_cache_compressed_amd import harness, synth, vc
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
@@ -605,7 +599,7 @@ def main():
     d_kernel_us = _back_to_back_us(torch, lambda i: st.draft_attention(i % w.x, reps[i % len(reps)]),
                                    3 * w.x)
     v_kernel_us = _back_to_back_us(torch, lambda i: st.verify_attention(), 3 if w.past_on_host else 10)
-    h2d = _h2d_rate(torch, st) if w.past_on_host else None
+    h2d = _h2d_rate(torch, vc, st) if w.past_on_host else None
     a_plus_1 = int((res["a"] + 1).sum())
     tok_s = a_plus_1 / (elapsed / args.steps)
 
@@ -639,7 +633,9 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic if args.workload == "c2" else None,
-                     "bytes_per_launch": int(d_bytes), "launch_us": round(d_kernel_us, 2)},
+                     "bytes_per_launch": int(d_bytes), "launch_us": round(d_kernel_us, 2),
+                     "timing": f"HIP events around {3 * w.x} back-to-back launches of the round's draft "
+                               "calls on the launch stream, after the timed replays (mean per launch)"},
         "draft_attention": {"launch_us": round(d_kernel_us, 2), "GB_s": round(achieved, 1),
                             "TFLOP_s": round(d_flops / d_mean_s / 1e12, 2)},
         "verify_attention": {"launch_us": round(v_kernel_us, 2),
@@ -654,8 +650,9 @@ def main():
         line["verify_attention"]["pcie"] = {
             "bound": "pcie", "achieved": round(v_gbs_pcie, 2), "peak": round(h2d["GB_s"], 2),
             "unit": "GB/s", "frac": round(v_gbs_pcie / h2d["GB_s"], 4),
-            "peak_is": "achieved pinned host->device rate of a plain copy of the same bytes in the "
-                       "same 64K-token chunks (median of 5)",
+            "peak_is": "achieved pinned host->device rate of the verify's own transfer alone "
+                       "(vc_verify_stream_copies: the same 2-D copies of the same 64K-token chunks, "
+                       "no compute; median of 10)",
             "frac_of_64GBs": round(v_gbs_pcie / 64.0, 4)}
     if w.drafter == "drop":
         sel_us = _back_to_back_us(torch, lambda i: st.select_keep(), 20)
@@ -687,8 +684,7 @@ def main():
         line["e2e_llama"] = _e2e_llama(torch, args.seed, args.llama_context, args.llama_tokens,
                                        args.llama_bits, args.llama_x, args.llama_batch)
     if not args.no_cpu_baseline and args.workload == "c2":
-        line["cpu_baseline"] = cpu_baseline(w, inputs, a_plus_1, args.cpu_draft_steps,
-                                            args.cpu_verify_heads)
+        line["cpu_baseline"] = cpu_baseline(w, inputs)
     print(json.dumps(line), flush=True)
 
 

@@ -14,11 +14,13 @@
  *   vc_draft_attn_drop   one-query decode attention over kept positions       (draft)
  *   vc_verify_attn       L-query causal block attention over the full cache   (verify)
  *   vc_verify_prefetch   first chunk copies of a host-streamed verify, issued early (verify)
+ *   vc_verify_stream_copies  a host-streamed verify's copies alone (its link ceiling) (measurement)
  *   vc_lse_merge         log-sum-exp merge of split partials                  (verify / draft)
  *   vc_accept            per-row argmax, first disagreement, correction token (accept)
  *   vc_select_keep       kept positions of a token-dropping drafter           (compressor)
  *   vc_project_logits    logits of the attention outputs (+ greedy argmax): the
  *                        single layer's stand-in for a model head              (harness)
+ *   vc_workspace_bytes   workspace size of any of the calls above               (host only)
  *
  * Conventions (all calls):
  *   - Every buffer is owned by the caller. Device pointers are HIP device memory; the library
@@ -153,9 +155,10 @@ vc_status vc_draft_quant_workspace(const vc_kivi *c, int64_t n_q, int32_t r, int
  * Limitations: identical drop counts for every head).
  * For every (b, query head h, kv head g = h/(Hq/Hkv)): keys/values = rows idx[b][g][0..n_keep-1]
  * of k/v[b][g]; same attention as above.
- *   k, v  [B][Hkv][tok_cap][128] in kv_dtype (VC_BF16 | VC_F16), device
+ *   k, v  [B][Hkv][tok_cap][128] bf16 (kv_dtype must be VC_BF16; other dtypes return
+ *         VC_ERR_UNSUPPORTED), device
  *   idx   [B][Hkv][idx_cap] int32 positions; entries outside [0, tok_cap) contribute nothing
- *   q     [B][Hq][128] in kv_dtype; out [B][Hq][128] fp32; lse [B][Hq] or NULL
+ *   q     [B][Hq][128] bf16; out [B][Hq][128] fp32; lse [B][Hq] or NULL
  *   1 <= n_keep <= idx_cap;  ws as for vc_draft_attn_quant (vc_draft_drop_workspace() bytes).
  */
 vc_status vc_draft_attn_drop(const void *k, const void *v, int32_t kv_dtype, int32_t B,
@@ -213,6 +216,20 @@ vc_status vc_verify_prefetch(const void *k_past, const void *v_past, int64_t pas
 vc_status vc_verify_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int64_t n,
                               int32_t past_on_host, int64_t chunk_tokens, int32_t dtype,
                               size_t *bytes);
+/*
+ * The transfer of a host-streamed verify on its own ("VeriCache: making lossy KV compression exact",
+ * Verifying Without Giving Back the Speedup: the full cache crosses the CPU-GPU link to be
+ * verified; the copy is the bound of that verify). Issues on `copy` exactly the host-to-device copies
+ * vc_verify_attn with VC_PAST_HOST issues for the same arguments (chunk c of every (b, kv head) into
+ * workspace stage c % 2, one 2-D copy per chunk per tensor) and nothing else: no compute, no waits
+ * between chunks. It measures the link's rate for the verify's own transfer pattern (the ceiling
+ * a streamed verify is compared against). The stages' contents are unspecified afterwards; a pending
+ * vc_verify_prefetch on the workspace is discarded. Arguments as for vc_verify_prefetch.
+ */
+vc_status vc_verify_stream_copies(const void *k_past, const void *v_past, int64_t past_stride,
+                                  int64_t n, int64_t chunk_tokens, int32_t B, int32_t Hq,
+                                  int32_t Hkv, int32_t L, void *ws, size_t ws_bytes,
+                                  void *copy_stream);
 
 /*
  * Log-sum-exp merge of S split partials per row (the pages are silent on how split work is
@@ -285,6 +302,21 @@ vc_status vc_project_logits(const void *W, int32_t w_dtype, int32_t V, const flo
 vc_status vc_select_keep(const float *scores, int64_t score_row_stride, int32_t rows, int64_t n,
                          int64_t sinks, int64_t recent, int64_t keep, int32_t *idx,
                          int64_t idx_row_stride, int64_t *n_keep, void *stream);
+
+/*
+ * Workspace size of any call that takes one, by operation code and its size arguments (the same
+ * values as the per-operation queries, which it forwards to; host only, nothing enqueued):
+ *   VC_OP_DRAFT_QUANT  dims {B, Hkv, Hq, n_q}                                (vc_draft_attn_quant)
+ *   VC_OP_DRAFT_DROP   dims {B, Hkv, Hq, n_keep}                             (vc_draft_attn_drop)
+ *   VC_OP_VERIFY       dims {B, Hq, Hkv, L, n, past_on_host, chunk_tokens, dtype}  (vc_verify_attn,
+ *                      vc_verify_prefetch, vc_verify_stream_copies)
+ *   VC_OP_PROJECT      dims {B, L, V}                                        (vc_project_logits)
+ * A wrong count of dims or an unknown op returns VC_ERR_INVALID. The pages give the calls of the
+ * path, not their memory; the caller owns every workspace ("VeriCache: Turning Lossy KV Cache into
+ * Lossless LLM Inference", Key Contributions: one interface for every compressor).
+ */
+enum { VC_OP_DRAFT_QUANT = 1, VC_OP_DRAFT_DROP = 2, VC_OP_VERIFY = 3, VC_OP_PROJECT = 4 };
+vc_status vc_workspace_bytes(int32_t op, const int64_t *dims, int32_t ndims, size_t *bytes);
 
 const char *vc_status_string(vc_status s);
 const char *vc_last_error(void);

@@ -287,6 +287,30 @@ vc_status vc_verify_prefetch(const void* k_past, const void* v_past, int64_t pas
   return ok();
 }
 
+vc_status vc_verify_stream_copies(const void* k_past, const void* v_past, int64_t past_stride,
+                                  int64_t n, int64_t chunk_tokens, int32_t B, int32_t Hq, int32_t Hkv,
+                                  int32_t L, void* ws, size_t ws_bytes, void* copy_stream) {
+  REQUIRE_PTR(k_past);
+  REQUIRE_PTR(v_past);
+  REQUIRE(L >= 1 && L <= 32, "L must be in [1, 32] (got %d)", L);
+  REQUIRE(n >= 1, "a host-streamed past needs n >= 1");
+  REQUIRE(past_stride >= n, "past_stride must be >= n");
+  REQUIRE(B >= 1 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv");
+  REQUIRE((int64_t)B * Hkv <= 65535, "B*Hkv must be <= 65535");
+  REQUIRE(chunk_tokens >= 32, "chunk_tokens must be >= 32 when streaming");
+  const vc_status pin = check_pinned(k_past, v_past);
+  if (pin != VC_OK) return pin;
+  const vc::VerifyPlan plan = vc::plan_verify(B, Hq, Hkv, L, n, 1, chunk_tokens, VC_BF16);
+  if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
+    return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,
+                ws ? ws_bytes : (size_t)0);
+  (void)take_prefetch(ws, nullptr);  // the stages are overwritten: any pending prefetch is gone
+  hipError_t e = vc::launch_verify_copies(k_past, v_past, past_stride, n, B, Hkv, ws, plan,
+                                          static_cast<hipStream_t>(copy_stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_verify_stream_copies");
+  return ok();
+}
+
 vc_status vc_verify_attn(const void* q, const void* k_blk, const void* v_blk, int32_t L,
                          const void* k_past, const void* v_past, int64_t past_stride, int64_t n,
                          int32_t past_on_host, int64_t chunk_tokens, int32_t dtype, int32_t B,
@@ -404,6 +428,50 @@ vc_status vc_project_logits(const void* W, int32_t w_dtype, int32_t V, const flo
                                     plan, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "vc_project_logits launch");
   return ok();
+}
+
+vc_status vc_workspace_bytes(int32_t op, const int64_t* dims, int32_t ndims, size_t* bytes) {
+  REQUIRE(bytes != nullptr, "bytes is null");
+  REQUIRE(dims != nullptr || ndims == 0, "dims is null");
+  auto need = [&](int k) { return ndims == k; };
+  auto fits32 = [&](int k) {
+    for (int i = 0; i < k; ++i)
+      if (dims[i] < INT32_MIN || dims[i] > INT32_MAX) return false;
+    return true;
+  };
+  switch (op) {
+    case VC_OP_DRAFT_QUANT: {  // {B, Hkv, Hq, n_q}
+      REQUIRE(need(4), "VC_OP_DRAFT_QUANT takes 4 dims {B, Hkv, Hq, n_q} (got %d)", ndims);
+      REQUIRE(fits32(3), "B, Hkv and Hq must fit int32");
+      const int64_t B = dims[0], Hkv = dims[1], Hq = dims[2], n_q = dims[3];
+      REQUIRE(B >= 1 && Hkv >= 1 && B * Hkv <= 65535, "B, Hkv >= 1 and B*Hkv <= 65535");
+      REQUIRE(Hq >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv");
+      REQUIRE(n_q >= 0 && n_q % 32 == 0, "n_q must be a non-negative multiple of 32");
+      vc_kivi c{};
+      c.B = (int32_t)B;
+      c.Hkv = (int32_t)Hkv;
+      *bytes = vc::plan_draft_quant(c, n_q, (int)Hq).ws_bytes;
+      return ok();
+    }
+    case VC_OP_DRAFT_DROP:  // {B, Hkv, Hq, n_keep}
+      REQUIRE(need(4), "VC_OP_DRAFT_DROP takes 4 dims {B, Hkv, Hq, n_keep} (got %d)", ndims);
+      REQUIRE(fits32(3), "B, Hkv and Hq must fit int32");
+      return vc_draft_drop_workspace((int32_t)dims[0], (int32_t)dims[1], (int32_t)dims[2], dims[3], bytes);
+    case VC_OP_VERIFY:  // {B, Hq, Hkv, L, n, past_on_host, chunk_tokens, dtype}
+      REQUIRE(need(8), "VC_OP_VERIFY takes 8 dims {B, Hq, Hkv, L, n, past_on_host, chunk_tokens, dtype} (got %d)",
+              ndims);
+      REQUIRE(fits32(4) && dims[5] >= INT32_MIN && dims[5] <= INT32_MAX && dims[7] >= INT32_MIN &&
+                  dims[7] <= INT32_MAX,
+              "B, Hq, Hkv, L, past_on_host and dtype must fit int32");
+      return vc_verify_workspace((int32_t)dims[0], (int32_t)dims[1], (int32_t)dims[2], (int32_t)dims[3],
+                                 dims[4], (int32_t)dims[5], dims[6], (int32_t)dims[7], bytes);
+    case VC_OP_PROJECT:  // {B, L, V}
+      REQUIRE(need(3), "VC_OP_PROJECT takes 3 dims {B, L, V} (got %d)", ndims);
+      REQUIRE(fits32(3), "B, L and V must fit int32");
+      return vc_project_workspace((int32_t)dims[0], (int32_t)dims[1], (int32_t)dims[2], bytes);
+    default:
+      return fail(VC_ERR_INVALID, "unknown op %d", op);
+  }
 }
 
 vc_status vc_select_keep(const float* scores, int64_t score_row_stride, int32_t rows, int64_t n,

@@ -66,6 +66,11 @@ hipError_t launch_verify_prefetch(const void* k_past, const void* v_past, int64_
                                   int64_t n, int B, int Hkv, void* ws, const VerifyPlan& plan,
                                   hipStream_t compute, hipStream_t copy);
 
+// Every chunk copy of a host-streamed verify (chunk c into stage c % 2), with no compute.
+hipError_t launch_verify_copies(const void* k_past, const void* v_past, int64_t past_stride,
+                                int64_t n, int B, int Hkv, void* ws, const VerifyPlan& plan,
+                                hipStream_t copy);
+
 // Logits projection (+ argmax).
 struct ProjectPlan {
   int nvt, nmt;          // vocabulary tiles, row tiles

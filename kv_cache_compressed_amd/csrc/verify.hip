@@ -2,10 +2,10 @@
 //
 // "VeriCache: making lossy KV compression exact", The Core Idea (one pass over the full cache
 // scores every drafted position plus one) and Verifying Without Giving Back the Speedup (the full
-// cache may sit in CPU memory and is brought to the GPU only for verification, loading the
-// interconnect; the verifier checks several positions at once, so it uses compute differently
-// from one-token decoding); "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference", Key
-// Contributions (verification is bound by the interconnect and FLOPs).
+// cache may sit in CPU memory and cross the host link only to be verified; verification is an
+// L-row block per query head, so it is matrix-core work rather than a bandwidth-bound one-row
+// product); "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference", Key Contributions
+// (verification is bound by the interconnect and FLOPs).
 //
 // bf16 path (matrix cores). Workgroup = 4 waves on one (b, kv head), up to 4 of its query heads
 // (ceil(G / 4) workgroups per tile range when G > 4) and one range of 32-token key tiles; wave w
@@ -596,6 +596,19 @@ hipError_t launch_verify_prefetch(const void* k_past, const void* v_past, int64_
   for (int c = 0; c < std::min(2, plan.chunks) && err == hipSuccess; ++c)
     err = copy_chunk(k_past, v_past, past_stride, n, units, plan, c, stage_k[c], stage_v[c], copy);
   (void)hipEventDestroy(start);
+  return err;
+}
+
+hipError_t launch_verify_copies(const void* k_past, const void* v_past, int64_t past_stride,
+                                int64_t n, int B, int Hkv, void* ws, const VerifyPlan& plan,
+                                hipStream_t copy) {
+  const int64_t units = (int64_t)B * Hkv;
+  uint16_t* stage_k[2];
+  uint16_t* stage_v[2];
+  stage_pointers(ws, plan, units, stage_k, stage_v);
+  hipError_t err = hipSuccess;
+  for (int c = 0; c < plan.chunks && err == hipSuccess; ++c)
+    err = copy_chunk(k_past, v_past, past_stride, n, units, plan, c, stage_k[c % 2], stage_v[c % 2], copy);
   return err;
 }
 

@@ -1,10 +1,10 @@
 """One synthetic single-layer draft/verify round on the GPU, driven through libvc.
 
-Device memory and streams come from PyTorch; every attention, quantisation, cache-append, accept
-and draft-step logits/argmax step is a libvc call. The stand-in logits projection (z = W o, an fp32
-product in place of the model's LM head) is libvc's fused projection + argmax kernel for the draft
-steps; for the B*L verify rows, where it is a real GEMM, it is the vendor fp32 GEMM through
-torch.matmul. Inputs come from the seeded generator (kv_cache_compressed_amd.synth).
+Device memory and streams come from PyTorch; every attention, quantisation, cache-append, logits,
+argmax and accept step is a libvc call. The stand-in logits projection (z = W o, an fp32 product in
+place of the model's LM head) is libvc's projection kernel: fused with the greedy argmax for the
+draft steps, followed by the accept kernel for the B*L verify rows. Inputs come from the seeded
+generator (kv_cache_compressed_amd.synth).
 
 Round ("VeriCache: making lossy KV compression exact", The Core Idea): x draft steps over the
 compressed cache (each: draft attention with the step's key/value appended by the same launch,
@@ -18,6 +18,13 @@ import torch
 from . import synth, vc
 
 SM_SCALE = float(np.float32(1.0 / np.sqrt(128.0)))
+
+
+def kivi_split(n: int, R: int, group: int = 32) -> int:
+    """Quantised prefix of a KIVI cache holding n tokens: whole groups, leaving at least R tokens in
+    the full-precision residual (group * floor(max(0, n - R) / group)). Commits keep this true by
+    flushing a group whenever the residual reaches R + group tokens."""
+    return group * (max(0, n - R) // group)
 
 
 def _dev(x: np.ndarray, dtype, device) -> torch.Tensor:
@@ -49,7 +56,7 @@ class RoundState:
         cap = (w.tok_cap + extra_tokens + 31) // 32 * 32
         self.cap = cap
         self.n = n                                   # cached (committed) tokens
-        self.n_q = w.n_q if w.drafter == "kivi" else 0  # of which quantised
+        self.n_q = kivi_split(n, w.R, w.group) if w.drafter == "kivi" else 0  # of which quantised
         if w.past_on_host:
             self.host_cap = n + extra_tokens
             self.k_host = torch.empty((B, Hkv, self.host_cap, 128), dtype=tdt, pin_memory=True)
@@ -80,14 +87,15 @@ class RoundState:
             # steps can read different copies, as the layers of a real model would); they share one
             # residual ring, to which each draft-round entry is appended once.
             for k in range(max(1, replicas)):
-                c = vc.KiviCache(B, Hkv, (max(w.n_q, 32) + extra_tokens + 31) // 32 * 32, w.bits,
+                c = vc.KiviCache(B, Hkv, (max(self.n_q, 32) + extra_tokens + 31) // 32 * 32, w.bits,
                                  vc.VC_F16 if w.meta_dtype == "f16" else vc.VC_F32,
                                  vc.VC_F16 if w.res_dtype == "f16" else vc.VC_F32, w.res_cap, device)
-                vc.vc_quantize_kv(c, src[0], src[1], 0, w.n_q, src_bh_stride=src[2])
+                nq = self.n_q
+                vc.vc_quantize_kv(c, src[0], src[1], 0, nq, src_bh_stride=src[2])
                 if k == 0:
-                    if n > w.n_q:
-                        vc.vc_kivi_append(c, src[0][:, :, w.n_q:], src[1][:, :, w.n_q:], w.n_q,
-                                          n - w.n_q, src_bh_stride=src[2])
+                    if n > nq:
+                        vc.vc_kivi_append(c, src[0][:, :, nq:], src[1][:, :, nq:], nq, n - nq,
+                                          src_bh_stride=src[2])
                 else:
                     c.k_res, c.v_res = self.replicas[0].k_res, self.replicas[0].v_res
                 self.replicas.append(c)
@@ -233,12 +241,9 @@ class RoundState:
                              argmax_b_stride=self.w.x, ws=self.ws_proj)
 
     def verify_tokens(self):
-        """Logits of the verify rows, then greedy accept against the drafts. With B*L rows the
-        stand-in projection is a real GEMM (4 GFLOP fp32 at the 32K workload), so it runs on
-        the vendor fp32 matrix-core GEMM; the fused kernel serves the few-row draft steps."""
-        w = self.w
-        flat = self.out_v.permute(0, 2, 1, 3).reshape(w.B * w.L, w.Hq * 128)
-        torch.matmul(flat, self.W.t(), out=self.logits_v.view(w.B * w.L, w.vocab))
+        """Logits of the B*L verify rows (the projection kernel, reading the outputs in their
+        [B, Hq, L, 128] layout), then the greedy accept against the drafts."""
+        vc.vc_project_logits(self.W, self.out_v, logits=self.logits_v)
         vc.vc_accept(self.logits_v, self.drafts, self.accept_len, self.next_tok, self.argmax_v)
 
     def verify_step(self):
@@ -339,8 +344,9 @@ class RoundState:
             meta_b = 2 if w.meta_dtype == "f16" else 4
             res_b = 2 if w.res_dtype == "f16" else 4
             per_tok = 2 * 128 * w.bits // 8 + (128 * 2 * meta_b) // 32 + 4 * 2 * meta_b
-            r = (w.n - w.n_q) + j + 1
-            kv = w.B * w.Hkv * (w.n_q * per_tok + r * 2 * 128 * res_b)
+            nq = kivi_split(w.n, w.R, w.group)
+            r = (w.n - nq) + j + 1
+            kv = w.B * w.Hkv * (nq * per_tok + r * 2 * 128 * res_b)
         else:
             kv_b = 2 if w.kv_dtype == "bf16" else 4
             kv = w.B * w.Hkv * (self.kept + j + 1) * (2 * 128 * kv_b + 4)

@@ -74,13 +74,6 @@ class Workload:
         return self.Hq // self.Hkv
 
     @property
-    def n_q(self) -> int:
-        """Quantised prefix length after prefill: whole groups leaving >= R tokens in the residual."""
-        if self.drafter != "kivi":
-            return 0
-        return self.group * (max(0, self.n - self.R) // self.group)
-
-    @property
     def keep(self) -> int:
         return int(round(self.keep_frac * self.n))
 

@@ -20,6 +20,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "vc.h")
 VC_OK, VC_ERR_INVALID, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_HIP = 0, 1, 2, 3, 4
 VC_F32, VC_F16, VC_BF16 = 0, 1, 2
 VC_PAST_DEVICE, VC_PAST_HOST, VC_PAST_HOST_PREFETCHED = 0, 1, 2
+VC_OP_DRAFT_QUANT, VC_OP_DRAFT_DROP, VC_OP_VERIFY, VC_OP_PROJECT = 1, 2, 3, 4
 _TORCH_DT = {torch.float32: VC_F32, torch.float16: VC_F16, torch.bfloat16: VC_BF16}
 
 _lib = None
@@ -60,6 +61,8 @@ _SIGS = {
     "vc_project_workspace": [_I32, _I32, _I32, ctypes.POINTER(_SZ)],
     "vc_project_logits": [_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _SZ, _P],
     "vc_select_keep": [_P, _I64, _I32, _I64, _I64, _I64, _I64, _P, _I64, ctypes.POINTER(_I64), _P],
+    "vc_verify_stream_copies": [_P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P],
+    "vc_workspace_bytes": [_I32, ctypes.POINTER(_I64), _I32, ctypes.POINTER(_SZ)],
     "vc_status_string": [_I32],
     "vc_last_error": [],
     "vc_abi_version": [],
@@ -256,6 +259,22 @@ def vc_verify_attn(q, k_blk, v_blk, k_past, v_past, n: int, out, lse, ws: torch.
     _check(lib().vc_verify_attn(_ptr(q), _ptr(k_blk), _ptr(v_blk), L, _ptr(k_past), _ptr(v_past),
                                 stride, n, int(past_on_host), chunk_tokens, dtype_code(q), B, Hq, Hkv,
                                 sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), comp, cp))
+
+
+def vc_verify_stream_copies(k_past, v_past, n: int, ws: torch.Tensor, B: int, Hq: int, Hkv: int,
+                            L: int, chunk_tokens: int, past_stride: int | None = None, copy_stream=None):
+    """Only the chunk copies a host-streamed vc_verify_attn with these arguments issues (no compute)."""
+    stride = k_past.shape[2] if past_stride is None else past_stride
+    _check(lib().vc_verify_stream_copies(_ptr(k_past), _ptr(v_past), stride, n, chunk_tokens, B, Hq, Hkv,
+                                         L, _ptr(ws), ws.numel() * ws.element_size(), _stream(copy_stream)))
+
+
+def vc_workspace_bytes(op: int, dims) -> int:
+    """Workspace bytes of operation `op` (VC_OP_*) for its size arguments `dims`."""
+    arr = (_I64 * max(1, len(dims)))(*dims)
+    n = _SZ(0)
+    _check(lib().vc_workspace_bytes(op, arr, len(dims), ctypes.byref(n)))
+    return n.value
 
 
 def vc_lse_merge(part_o, part_ml, out, lse, stream=None):

@@ -199,6 +199,23 @@ def unpack_codes(packed: np.ndarray, bits: int, kind: str) -> np.ndarray:
     return out.reshape(T, 128)
 
 
+def quantised_prefix(n: int, R: int, group: int = GROUP) -> int:
+    """Tokens held as codes once n tokens are cached with a full-precision residual of R tokens.
+
+    The pages give no residual rule; the workload recipe keeps the most recent tokens in full
+    precision (the last 32 in fp32 for the fp32 layer, a 128-token fp16 residual for the bf16
+    layers). Reading taken: quantise the longest prefix of whole `group`-token groups that leaves
+    at least R tokens unquantised, i.e. group * floor(max(0, n - R) / group); nothing is quantised
+    while n <= R.
+    """
+    if n < 0 or R < 0 or group <= 0:
+        raise ValueError((n, R, group))
+    spare = n - R
+    if spare <= 0:
+        return 0
+    return group * (spare // group)
+
+
 class KiviLayer:
     """Oracle KIVI cache of one (batch, kv-head) slice after prefill.
 

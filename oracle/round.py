@@ -19,7 +19,7 @@ import numpy as np
 
 from . import accept as acc
 from .attention import SM_SCALE_F32, decode, kv_head, verify_block
-from .quant import KiviLayer
+from .quant import KiviLayer, quantised_prefix
 
 
 def logits(W: np.ndarray, O: np.ndarray) -> np.ndarray:
@@ -37,13 +37,15 @@ class Round:
         self.K_new, self.V_new, self.Q, self.W, self.idx = K_new, V_new, Q, W, idx
         self.sm = sm_scale
         self._kivi = {}
+        # quantised prefix after prefill (whole groups before a residual of at least R tokens)
+        self.n_q = quantised_prefix(w.n, w.R, w.group) if w.drafter == "kivi" else 0
 
     # ---- drafter caches -------------------------------------------------------------------
     def kivi(self, b: int, h: int) -> KiviLayer:
         key = (b, h)
         if key not in self._kivi:
             w = self.w
-            lay = KiviLayer(self.K_past[b, h], self.V_past[b, h], w.n_q, w.bits, w.meta_dtype,
+            lay = KiviLayer(self.K_past[b, h], self.V_past[b, h], self.n_q, w.bits, w.meta_dtype,
                             w.res_dtype)
             for j in range(w.x):
                 lay.append(self.K_new[b, h, j], self.V_new[b, h, j])
@@ -57,7 +59,7 @@ class Round:
         q = self.Q[b, hq, j]
         if w.drafter == "kivi":
             lay = self.kivi(b, h)
-            r = (w.n - w.n_q) + j + 1
+            r = (w.n - self.n_q) + j + 1
             return decode(q, lay.keys(r), lay.values(r), self.sm)
         K = np.concatenate([self.K_past[b, h][self.idx[b][h]], self.K_new[b, h, : j + 1]])
         V = np.concatenate([self.V_past[b, h][self.idx[b][h]], self.V_new[b, h, : j + 1]])

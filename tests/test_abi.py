@@ -228,3 +228,43 @@ def test_select_keep_rejects(L):
         assert call(**kw) == vc.VC_ERR_INVALID, kw
         assert msg in _err(L), (kw, _err(L))
     assert L.vc_select_keep(P, 1000, 4, 1000, 64, 256, 400, P, 400, None, None) == vc.VC_ERR_INVALID
+
+
+def test_generic_workspace_query_matches_the_per_op_queries(L):
+    """vc_workspace_bytes forwards to the per-operation sizes for every op, and rejects unknown ops
+    and wrong dim counts."""
+    one = ctypes.c_size_t()
+    k = _kivi(B=8, Hkv=8, tok_cap=32768)
+    assert L.vc_draft_quant_workspace(ctypes.byref(k), 32640, 128, 32, ctypes.byref(one)) == vc.VC_OK
+    assert vc.vc_workspace_bytes(vc.VC_OP_DRAFT_QUANT, [8, 8, 32, 32640]) == one.value
+    assert L.vc_draft_drop_workspace(4, 8, 64, 25000, ctypes.byref(one)) == vc.VC_OK
+    assert vc.vc_workspace_bytes(vc.VC_OP_DRAFT_DROP, [4, 8, 64, 25000]) == one.value
+    for dims in ([8, 32, 8, 31, 32768, 0, 0, vc.VC_BF16], [1, 32, 8, 31, 500000, 1, 65536, vc.VC_BF16],
+                 [1, 32, 8, 9, 2048, 0, 0, vc.VC_F32]):
+        assert L.vc_verify_workspace(*dims, ctypes.byref(one)) == vc.VC_OK
+        assert vc.vc_workspace_bytes(vc.VC_OP_VERIFY, dims) == one.value
+    assert L.vc_project_workspace(8, 31, 2048, ctypes.byref(one)) == vc.VC_OK
+    assert vc.vc_workspace_bytes(vc.VC_OP_PROJECT, [8, 31, 2048]) == one.value
+    arr = (ctypes.c_int64 * 8)(8, 8, 32, 32640, 0, 0, 0, 0)
+    assert L.vc_workspace_bytes(99, arr, 4, ctypes.byref(one)) == vc.VC_ERR_INVALID and "unknown op" in _err(L)
+    assert L.vc_workspace_bytes(vc.VC_OP_DRAFT_QUANT, arr, 3, ctypes.byref(one)) == vc.VC_ERR_INVALID
+    assert L.vc_workspace_bytes(vc.VC_OP_VERIFY, arr, 4, ctypes.byref(one)) == vc.VC_ERR_INVALID
+    assert L.vc_workspace_bytes(vc.VC_OP_DRAFT_QUANT, arr, 4, None) == vc.VC_ERR_INVALID
+    bad = (ctypes.c_int64 * 4)(8, 8, 33, 32640)                    # Hq not a multiple of Hkv
+    assert L.vc_workspace_bytes(vc.VC_OP_DRAFT_QUANT, bad, 4, ctypes.byref(one)) == vc.VC_ERR_INVALID
+    bad = (ctypes.c_int64 * 4)(8, 8, 32, 100)                      # n_q not a multiple of 32
+    assert L.vc_workspace_bytes(vc.VC_OP_DRAFT_QUANT, bad, 4, ctypes.byref(one)) == vc.VC_ERR_INVALID
+
+
+def test_stream_copies_rejects(L):
+    """Argument checks of the copy-only transfer (all before any HIP call)."""
+    call = lambda **a: L.vc_verify_stream_copies(
+        a.get("kp", P), P, a.get("stride", 4096), a.get("n", 4000), a.get("chunk", 1024), 2,
+        a.get("Hq", 8), 2, a.get("L", 31), P, 1 << 34, None)
+    assert call(L=0) == vc.VC_ERR_INVALID
+    assert call(n=0) == vc.VC_ERR_INVALID and "n >= 1" in _err(L)
+    assert call(stride=100) == vc.VC_ERR_INVALID
+    assert call(kp=0) == vc.VC_ERR_INVALID
+    assert call(kp=BAD) == vc.VC_ERR_INVALID
+    assert call(chunk=16) == vc.VC_ERR_INVALID
+    assert call(Hq=5) == vc.VC_ERR_INVALID

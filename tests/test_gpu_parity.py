@@ -38,6 +38,11 @@ W_SMALL = {
 }
 
 
+def nq(w):
+    """The oracle's quantised prefix after prefill (whole groups before a residual of >= R)."""
+    return oq.quantised_prefix(w.n, w.R, w.group)
+
+
 def _oracle_keep(w, seed=0):
     """The oracle's kept positions of every (b, kv head) of a token-dropping workload."""
     return [[osel.keep_positions(synth.scores(w, seed, b, h), w.n, w.sinks, w.recent, w.keep)
@@ -240,7 +245,7 @@ def test_lse_merge(gpu_lib, S):
 # quantisation and residual
 # ------------------------------------------------------------------------------------------
 def _cache_for(w):
-    return vc.KiviCache(w.B, w.Hkv, max(w.n_q, 32), w.bits, vc.VC_F16 if w.meta_dtype == "f16" else vc.VC_F32,
+    return vc.KiviCache(w.B, w.Hkv, max(nq(w), 32), w.bits, vc.VC_F16 if w.meta_dtype == "f16" else vc.VC_F32,
                         vc.VC_F16 if w.res_dtype == "f16" else vc.VC_F32, w.res_cap, "cuda")
 
 
@@ -251,17 +256,17 @@ def test_quantize_bit_exact(gpu_lib, name):
     tdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
     c = _cache_for(w)
     Kd, Vd = torch.from_numpy(K).to("cuda", tdt), torch.from_numpy(V).to("cuda", tdt)
-    vc.vc_quantize_kv(c, Kd, Vd, 0, w.n_q)
+    vc.vc_quantize_kv(c, Kd, Vd, 0, nq(w))
     torch.cuda.synchronize()
     mdt = np.float16 if w.meta_dtype == "f16" else np.float32
     for b in range(w.B):
         for h in range(w.Hkv):
-            kc, ks, km = oq.quantize_k(K[b, h, :w.n_q], w.bits, w.meta_dtype)
-            vcod, vs, vm = oq.quantize_v(V[b, h, :w.n_q], w.bits, w.meta_dtype)
-            assert np.array_equal(c.k_codes[b, h, :w.n_q].cpu().numpy(), oq.pack_codes(kc, w.bits, "k"))
-            assert np.array_equal(c.v_codes[b, h, :w.n_q].cpu().numpy(), oq.pack_codes(vcod, w.bits, "v"))
-            gk = c.k_meta[b, h, :w.n_q // 32].cpu().numpy()
-            gv = c.v_meta[b, h, :w.n_q].cpu().numpy()
+            kc, ks, km = oq.quantize_k(K[b, h, :nq(w)], w.bits, w.meta_dtype)
+            vcod, vs, vm = oq.quantize_v(V[b, h, :nq(w)], w.bits, w.meta_dtype)
+            assert np.array_equal(c.k_codes[b, h, :nq(w)].cpu().numpy(), oq.pack_codes(kc, w.bits, "k"))
+            assert np.array_equal(c.v_codes[b, h, :nq(w)].cpu().numpy(), oq.pack_codes(vcod, w.bits, "v"))
+            gk = c.k_meta[b, h, :nq(w) // 32].cpu().numpy()
+            gv = c.v_meta[b, h, :nq(w)].cpu().numpy()
             assert np.array_equal(gk[:, 0], ks.astype(mdt)) and np.array_equal(gk[:, 1], km.astype(mdt))
             assert np.array_equal(gv[..., 0], vs.astype(mdt)) and np.array_equal(gv[..., 1], vm.astype(mdt))
 
@@ -365,20 +370,20 @@ def test_draft_quant_edges(gpu_lib, n_q_zero):
     K, V, Kn, Vn, Q, W = inp
     c = _cache_for(w)
     Kd, Vd = torch.from_numpy(K).to("cuda", torch.bfloat16), torch.from_numpy(V).to("cuda", torch.bfloat16)
-    vc.vc_quantize_kv(c, Kd, Vd, 0, w.n_q)
-    if w.n > w.n_q:
-        vc.vc_kivi_append(c, Kd[:, :, w.n_q:], Vd[:, :, w.n_q:], w.n_q, w.n - w.n_q, src_bh_stride=w.n * 128)
+    vc.vc_quantize_kv(c, Kd, Vd, 0, nq(w))
+    if w.n > nq(w):
+        vc.vc_kivi_append(c, Kd[:, :, nq(w):], Vd[:, :, nq(w):], nq(w), w.n - nq(w), src_bh_stride=w.n * 128)
     q = torch.from_numpy(Q[:, :, 0]).to("cuda", torch.bfloat16).contiguous()
     out = torch.zeros((w.B, w.Hq, 128), device="cuda")
     lse = torch.zeros((w.B, w.Hq), device="cuda")
-    r = w.n - w.n_q
-    ws = torch.zeros(vc.vc_draft_quant_workspace(c, w.n_q, r, w.Hq), dtype=torch.uint8, device="cuda")
-    vc.vc_draft_attn_quant(c, w.n_q, r, q, out, lse, ws, harness.SM_SCALE)
+    r = w.n - nq(w)
+    ws = torch.zeros(vc.vc_draft_quant_workspace(c, nq(w), r, w.Hq), dtype=torch.uint8, device="cuda")
+    vc.vc_draft_attn_quant(c, nq(w), r, q, out, lse, ws, harness.SM_SCALE)
     torch.cuda.synchronize()
     for h in range(w.Hq):
-        lay = oq.KiviLayer(K[0, h // w.G], V[0, h // w.G], w.n_q, w.bits, w.meta_dtype, w.res_dtype)
+        lay = oq.KiviLayer(K[0, h // w.G], V[0, h // w.G], nq(w), w.bits, w.meta_dtype, w.res_dtype)
         o, l = oatt.decode(Q[0, h, 0], lay.keys(r), lay.values(r))
-        _close(out[0, h].cpu().numpy(), o, True, TIGHT["draft_quant"], f"edge n_q={w.n_q} h={h}")
+        _close(out[0, h].cpu().numpy(), o, True, TIGHT["draft_quant"], f"edge n_q={nq(w)} h={h}")
         assert abs(lse[0, h].item() - l) < 2e-3
 
 
@@ -390,15 +395,15 @@ def test_draft_quant_ticket_merge_repeatable(gpu_lib):
     K, V, Kn, Vn, Q, W = _inputs(w)
     c = _cache_for(w)
     Kd, Vd = torch.from_numpy(K).to("cuda", torch.bfloat16), torch.from_numpy(V).to("cuda", torch.bfloat16)
-    vc.vc_quantize_kv(c, Kd, Vd, 0, w.n_q)
-    r = w.n - w.n_q
-    vc.vc_kivi_append(c, Kd[:, :, w.n_q:], Vd[:, :, w.n_q:], w.n_q, r, src_bh_stride=w.n * 128)
+    vc.vc_quantize_kv(c, Kd, Vd, 0, nq(w))
+    r = w.n - nq(w)
+    vc.vc_kivi_append(c, Kd[:, :, nq(w):], Vd[:, :, nq(w):], nq(w), r, src_bh_stride=w.n * 128)
     q = torch.from_numpy(Q[:, :, 0]).to("cuda", torch.bfloat16).contiguous()
-    big = max(vc.vc_draft_quant_workspace(c, w.n_q, r, w.Hq), vc.vc_draft_quant_workspace(c, 64, r, w.Hq))
+    big = max(vc.vc_draft_quant_workspace(c, nq(w), r, w.Hq), vc.vc_draft_quant_workspace(c, 64, r, w.Hq))
     ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
     outs = {}
     for rep in range(12):
-        for n_q in (w.n_q, 64):  # alternate shapes (different split counts) on one workspace
+        for n_q in (nq(w), 64):  # alternate shapes (different split counts) on one workspace
             out = torch.zeros((w.B, w.Hq, 128), device="cuda")
             lse = torch.zeros((w.B, w.Hq), device="cuda")
             vc.vc_draft_attn_quant(c, n_q, r, q, out, lse, ws, harness.SM_SCALE)
@@ -410,12 +415,12 @@ def test_draft_quant_ticket_merge_repeatable(gpu_lib):
             assert int(ws[:65536].view(torch.int32).abs().sum().item()) == 0, "tickets not returned to zero"
     # the short call is right too: first 64 quantised tokens + the same ring slots, which hold
     # tokens n_q.. because n_q = 64 (mod res_cap) for this workload
-    assert w.n_q % w.res_cap == 64
+    assert nq(w) % w.res_cap == 64
     for h in range(0, w.Hq, 5):
         lay = oq.KiviLayer(K[0, h // w.G], V[0, h // w.G], 64, w.bits, w.meta_dtype, w.res_dtype)
-        ring = oq.KiviLayer(K[0, h // w.G], V[0, h // w.G], w.n_q, w.bits, w.meta_dtype, w.res_dtype)
-        keys = np.concatenate([lay.keys(0), ring.keys(r)[w.n_q:]])
-        vals = np.concatenate([lay.values(0), ring.values(r)[w.n_q:]])
+        ring = oq.KiviLayer(K[0, h // w.G], V[0, h // w.G], nq(w), w.bits, w.meta_dtype, w.res_dtype)
+        keys = np.concatenate([lay.keys(0), ring.keys(r)[nq(w):]])
+        vals = np.concatenate([lay.values(0), ring.values(r)[nq(w):]])
         o, l = oatt.decode(Q[0, h, 0], keys, vals)
         _close(outs[64][0][0, h].cpu().numpy(), o, True, TIGHT["draft_quant"], f"short call h={h}")
 
@@ -525,6 +530,28 @@ def test_verify_shapes(gpu_lib, n, L):
         for hq in range(8):
             O, l = oatt.verify_block(Q[b, hq], K[b, hq // 4], V[b, hq // 4], Kn[b, hq // 4], Vn[b, hq // 4])
             _close(out[b, hq].cpu().numpy(), O, True, TIGHT["verify"], f"verify n={n} L={L} b={b} h={hq}")
+
+
+@pytest.mark.parametrize("G", [3, 5, 6, 7])
+def test_verify_group_sizes(gpu_lib, G):
+    """Query heads per kv head that fill neither one 4-head workgroup exactly nor two (G = 5..7
+    leaves idle waves in the last head slice; G = 3 one idle wave): every head of every row matches
+    the oracle."""
+    Hkv, n, L = 2, 1000, 31
+    w = synth.WORKLOADS["c2"].with_(B=1, Hq=Hkv * G, Hkv=Hkv, n=n, x=L - 1)
+    K, V, Kn, Vn, Q, W = _inputs(w)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", torch.bfloat16)
+    out = torch.full((1, w.Hq, L, 128), float("nan"), device="cuda")
+    lse = torch.full((1, w.Hq, L), float("nan"), device="cuda")
+    ws = torch.zeros(vc.vc_verify_workspace(1, w.Hq, Hkv, L, n, False, 0, vc.VC_BF16), dtype=torch.uint8,
+                     device="cuda")
+    vc.vc_verify_attn(dev(Q), dev(Kn), dev(Vn), dev(K), dev(V), n, out, lse, ws, harness.SM_SCALE)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for hq in range(w.Hq):
+        O, lr = oatt.verify_block(Q[0, hq], K[0, hq // G], V[0, hq // G], Kn[0, hq // G], Vn[0, hq // G])
+        _close(o[0, hq], O, True, TIGHT["verify"], f"verify G={G} h={hq}")
+        assert np.abs(l[0, hq] - lr).max() < 1e-3, f"lse G={G} h={hq}"
 
 
 def test_verify_streamed_equals_resident(gpu_lib):
@@ -855,8 +882,43 @@ def test_staggered_decode_matches_lockstep(gpu_lib):
         ra, rb = a.results(), b.results()
         for k in ("out_d", "drafts", "out_v", "verified", "a", "next"):
             assert np.array_equal(ra[k], rb[k]), k
-    assert B[0].n_q > w.n_q or B[1].n_q > w.n_q, "at least one flush"
+    assert B[0].n_q > nq(w) or B[1].n_q > nq(w), "at least one flush"
 
+
+
+def _tiny_logits(m, prompt, seq):
+    """Oracle logits of a TinyModel at every generated position, teacher-forced on `seq`: row t is
+    the full-KV greedy logits after prompt + seq[:t]."""
+    from oracle import loop as oloop
+    toks = list(prompt) + list(seq)
+    K, V = oloop.full_cache(m, toks)
+    rows = []
+    for t in range(len(seq)):
+        p = len(prompt) - 1 + t
+        rows.append(m.next_logits(toks[p], p, [k[:p + 1] for k in K], [v[:p + 1] for v in V]))
+    return np.stack(rows)
+
+
+def _stack_logits(m, prompt, seq):
+    """The same for a model with a causal logits_all (LayeredModel, LlamaModel): one forward pass
+    over prompt + seq[:-1]."""
+    return m.logits_all(list(prompt) + list(seq[:-1]))[len(prompt) - 1:]
+
+
+def _check_resynced(seq, Z, what):
+    """Every emitted token equals the oracle's full-KV greedy token given the emitted prefix, i.e.
+    the oracle is re-synced onto the decoded sequence at every position, so a near-tie divergence
+    does not end the comparison: each later token is still checked. A differing token is exempt
+    only where the oracle's top-2 gap there is below GAP; exempt positions are counted and
+    printed. Returns their number."""
+    assert Z.shape[0] == len(seq), (Z.shape, len(seq))
+    arg = oacc.argmax_rows(Z)
+    gap = oacc.top2_gap(Z)
+    bad = [t for t in range(len(seq)) if int(seq[t]) != int(arg[t])]
+    hard = [(t, int(seq[t]), int(arg[t]), float(gap[t])) for t in bad if gap[t] >= GAP]
+    assert not hard, f"{what}: tokens differ from the oracle's greedy token (t, got, oracle, gap): {hard}"
+    print(f"{what}: {len(seq)} tokens checked, {len(bad)} exempt near-tie positions {bad}", flush=True)
+    return len(bad)
 
 # ------------------------------------------------------------------------------------------
 # the pages' guarantee end to end: VeriCache decoding emits the full-KV greedy tokens
@@ -885,20 +947,13 @@ def test_token_decoder_emits_full_kv_greedy(gpu_lib, bits, R, kv, host):
     opts = dict(kv_dtype=kv, host_past=host, chunk_tokens=64)  # host: several streamed chunks
     dec = TokenDecoder(Wt, 4, 2, prompt, x=x, bits=bits, R=R, max_new=steps + 32, **opts)
     got = dec.generate(steps)
-    ref = oloop.greedy(m, prompt, steps)
     # the GPU's own greedy decode over the full cache (one query row per token) as well
     greedy_gpu = GreedyDecoder(Wt, 4, 2, prompt, max_new=steps + 8, **opts).generate(steps)
     print(f"[bits {bits} R {R} {kv}{' host' if host else ''}] accepted per round {dec.rounds}; "
           f"n_q {dec.n_q}", flush=True)
     for what, seq in (("VeriCache", got), ("GPU greedy", greedy_gpu)):
-        if seq != ref:
-            t = next(i for i in range(steps) if seq[i] != ref[i])
-            toks = prompt + ref[:t]
-            K, V = oloop.full_cache(m, toks)
-            z = m.next_logits(toks[-1], len(toks) - 1, K, V)
-            gap = float(oacc.top2_gap(z[None])[0])
-            assert gap < GAP, f"{what}: token {t} differs ({seq[t]} vs {ref[t]}), oracle top-2 gap {gap}"
-            print(f"{what}: first divergence at token {t}: near-tie (gap {gap:.2e})", flush=True)
+        assert len(seq) == steps
+        _check_resynced(seq, _tiny_logits(m, prompt, seq), what)
     if R >= len(prompt) + steps:  # nothing quantised: the drafter reads what the verifier reads
         assert sum(dec.rounds) >= x * (len(dec.rounds) - 1), dec.rounds
     else:
@@ -929,16 +984,11 @@ def test_layered_decoder_emits_full_kv_greedy(gpu_lib, layers, bits, kv, host):
     dec = LayeredDecoder(W, 4, 2, prompt, x=x, bits=bits, R=32, max_new=steps + 32, **opts)
     got = dec.generate(steps)
     greedy_gpu = LayeredGreedyDecoder(W, 4, 2, prompt, max_new=steps + 8, **opts).generate(steps)
-    ref = oloop.greedy_layered(m, prompt, steps)
     print(f"[{layers} layers, {bits}-bit, {kv}{' host' if host else ''}] accepted per round "
           f"{dec.rounds}; n_q {dec.n_q}", flush=True)
     for what, seq in (("VeriCache", got), ("GPU greedy", greedy_gpu)):
-        if seq != ref:
-            t = next(i for i in range(steps) if seq[i] != ref[i])
-            z = m.logits_all(prompt + ref[:t])[-1]
-            gap = float(oacc.top2_gap(z[None])[0])
-            assert gap < GAP, f"{what}: token {t} differs ({seq[t]} vs {ref[t]}), oracle top-2 gap {gap}"
-            print(f"{what}: first divergence at token {t}: near-tie (gap {gap:.2e})", flush=True)
+        assert len(seq) == steps
+        _check_resynced(seq, _stack_logits(m, prompt, seq), what)
     assert dec.n_q > 32 * ((len(prompt) - 1 - 32) // 32), "the loop must have flushed"
 
 
@@ -971,17 +1021,12 @@ def test_llama_decoder_emits_full_kv_greedy(gpu_lib, layers, bits, kv, host, gra
     got = dec.generate(steps)
     assert (dec.gH is not None) == graphs
     greedy_gpu = LayeredGreedyDecoder(W, 4, 2, prompt, max_new=steps + 8, **opts).generate(steps)
-    ref = oloop.greedy_llama(m, prompt, steps)
     print(f"[llama {layers} layers, {bits}-bit, {kv}{' host' if host else ''}"
           f"{' graphs' if graphs else ''}] accepted per round "
           f"{dec.rounds}; n_q {dec.n_q}", flush=True)
     for what, seq in (("VeriCache", got), ("GPU greedy", greedy_gpu)):
-        if seq != ref:
-            t = next(i for i in range(steps) if seq[i] != ref[i])
-            z = m.logits_all(prompt + ref[:t])[-1]
-            gap = float(oacc.top2_gap(z[None])[0])
-            assert gap < GAP, f"{what}: token {t} differs ({seq[t]} vs {ref[t]}), oracle top-2 gap {gap}"
-            print(f"{what}: first divergence at token {t}: near-tie (gap {gap:.2e})", flush=True)
+        assert len(seq) == steps
+        _check_resynced(seq, _stack_logits(m, prompt, seq), what)
     assert sum(dec.rounds) > 0, "the drafter should get some tokens accepted"
     assert dec.n_q > 32 * ((len(prompt) - 1 - 32) // 32), "the loop must have flushed"
 
@@ -1016,14 +1061,9 @@ def test_batched_llama_decoder_per_request_greedy(gpu_lib, bits, kv, host):
           f"{dec.rounds}; n {dec.n}", flush=True)
     assert len(set(len(r) for r in dec.rounds)) == 1 and len(set(dec.n)) > 1
     for b, prompt in enumerate(prompts):
-        ref = oloop.greedy_llama(m, prompt, steps)
         for what, seq in (("VeriCache", got[b]), ("greedy", greedy[b])):
-            if seq != ref:
-                t = next(i for i in range(steps) if seq[i] != ref[i])
-                z = m.logits_all(prompt + ref[:t])[-1]
-                gap = float(oacc.top2_gap(z[None])[0])
-                assert gap < GAP, f"request {b} {what}: token {t} differs, oracle top-2 gap {gap}"
-                print(f"request {b} {what}: first divergence at token {t}: near-tie", flush=True)
+            assert len(seq) == steps
+            _check_resynced(seq, _stack_logits(m, prompt, seq), f"request {b} {what}")
 
 
 def test_batched_llama_groups_staggered_equal_lockstep(gpu_lib):
@@ -1083,11 +1123,5 @@ def test_token_decoders_staggered_two_requests(gpu_lib):
         a = [t for em in lock[g] for t in em]
         b = [t for em in stag[g] for t in em]
         assert a == b, f"request {g}"
-        ref = oloop.greedy(m, prompts[g], len(a))
-        if a != ref:
-            t = next(i for i in range(len(a)) if a[i] != ref[i])
-            toks = prompts[g] + ref[:t]
-            K, V = oloop.full_cache(m, toks)
-            gap = float(oacc.top2_gap(m.next_logits(toks[-1], len(toks) - 1, K, V)[None])[0])
-            assert gap < GAP, f"request {g}: token {t} differs, oracle top-2 gap {gap}"
+        _check_resynced(a, _tiny_logits(m, prompts[g], a), f"request {g}")
         print(f"request {g}: {len(a)} tokens over {rounds} rounds", flush=True)

@@ -173,3 +173,30 @@ def test_residual_f16_rounding_of_bf16_is_exact_in_normal_range():
     x = synth.round_bf16(np.random.default_rng(9).standard_normal(10000).astype(np.float32))
     x = x[np.abs(x) >= 2.0 ** -14]
     assert np.array_equal(Q.to_res(x, "f16"), x.astype(np.float64))
+
+
+@pytest.mark.parametrize("R", [0, 1, 31, 32, 33, 128, 129])
+def test_quantised_prefix_brute_force(R):
+    """The quantised prefix after prefill is the largest multiple of 32 that leaves at least R
+    tokens in the residual (brute force over candidates): R <= n - n_q < R + 32 once n >= R, and
+    nothing is quantised while n <= R."""
+    for n in range(0, 400):
+        best = max(c for c in range(0, n + 1, 32) if n - c >= R) if n >= R else 0
+        nq = Q.quantised_prefix(n, R)
+        assert nq == best and nq % 32 == 0, (n, R)
+        if n >= R:
+            assert R <= n - nq < R + 32
+        if n <= R:
+            assert nq == 0
+
+
+def test_quantised_prefix_at_the_workloads():
+    """The three KIVI workloads: 2048 tokens with a 32-token fp32 residual, 32768 and 500000 tokens
+    with a 128-token fp16 residual."""
+    assert Q.quantised_prefix(2048, 32) == 2016
+    assert Q.quantised_prefix(32768, 128) == 32640
+    assert Q.quantised_prefix(500000, 128) == 499872
+    for name in ("c1", "c2", "c4"):
+        w = synth.WORKLOADS[name]
+        nq = Q.quantised_prefix(w.n, w.R, w.group)
+        assert w.n - nq >= w.R and (w.n - nq) - w.R < w.group

@@ -19,8 +19,8 @@ def _inputs(w, seed=0):
 def test_uncompressed_kivi_drafter_accepts_everything():
     # R >= n: nothing is quantised, the residual holds every token at fp32.
     w = synth.WORKLOADS["c1"].with_(n=300, R=400, x=5, B=1, Hq=8, Hkv=2, vocab=64)
-    assert w.n_q == 0
     rnd = Round(w, *_inputs(w))
+    assert rnd.n_q == 0
     res = rnd.run(0)
     assert res["a"] == w.x and res["next"] == res["verified"][-1]
     assert np.array_equal(res["drafts"], res["verified"][:-1])
@@ -87,3 +87,30 @@ def test_layered_model_one_layer_is_the_tiny_model_and_causal():
     a = lm2.logits_all(toks)
     b = lm2.logits_all(toks[:12] + [(t + 1) % 13 for t in toks[12:]])
     assert np.array_equal(a[:12], b[:12]) and not np.allclose(a[12:], b[12:])
+
+
+def test_logits_select_the_concatenated_head_channel():
+    """z = W concat_heads(O) with heads in order and channels contiguous within a head: an output
+    that is zero except at (head h, channel c) picks column h*d + c of W, and a W whose row v is the
+    indicator of slot (h_v, c_v) reads back O[h_v, c_v] (a transposed or head-interleaved concat
+    fails both)."""
+    from oracle.round import logits
+
+    Hq, d, V = 4, 128, 37
+    g = np.random.default_rng(3)
+    W = g.standard_normal((V, Hq * d)).astype(np.float32)
+    for h, c in ((0, 0), (2, 5), (3, 127), (1, 64)):
+        O = np.zeros((Hq, d), np.float32)
+        O[h, c] = 1.0
+        assert np.array_equal(logits(W, O), W[:, h * d + c].astype(np.float64))
+    O = g.standard_normal((Hq, d)).astype(np.float32)
+    slots = [(int(g.integers(0, Hq)), int(g.integers(0, d))) for _ in range(V)]
+    Wi = np.zeros((V, Hq * d), np.float32)
+    for v, (h, c) in enumerate(slots):
+        Wi[v, h * d + c] = 1.0
+    assert np.array_equal(logits(Wi, O), np.array([O[h, c] for h, c in slots], np.float64))
+    # linear in O: two heads' contributions add
+    O2 = np.zeros((Hq, d), np.float32)
+    O2[1, 3], O2[3, 9] = 2.0, -0.5
+    W64 = W.astype(np.float64)
+    assert np.allclose(logits(W, O2), 2.0 * W64[:, d + 3] - 0.5 * W64[:, 3 * d + 9], rtol=0, atol=1e-12)
