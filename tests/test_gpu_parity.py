@@ -827,7 +827,7 @@ def test_multi_round_decode_with_flush(gpu_lib, name, rounds):
         st.run_round()
         gpu = st.results()
         wt = w.with_(n=n)
-        assert st.n == n and st.n_q == wt.n_q, (t, st.n, st.n_q, wt.n_q)
+        assert st.n == n and st.n_q == nq(wt), (t, st.n, st.n_q, nq(wt))
         ref = Round(wt, Kc, Vc, Kn, Vn, Q, W).run(0)
         dz = np.abs(gpu["draft_logits"][:, 0] - ref["draft_logits"]).max(axis=1)
         print(f"[{name}] round {t}: n {n} n_q {st.n_q} a {int(gpu['a'][0])}/{ref['a']} "
@@ -842,15 +842,15 @@ def test_multi_round_decode_with_flush(gpu_lib, name, rounds):
     print(f"[{name}] accepted per round {accepted}; n {w.n} -> {st.n}, n_q {n_q0} -> {st.n_q}", flush=True)
     assert st.n_q > n_q0, "the loop must have flushed at least one group"
     mdt = np.float16 if w.meta_dtype == "f16" else np.float32
-    nq = st.n_q
+    nqf = st.n_q
     for c in st.replicas:
         for h in range(w.Hkv):
-            kc, ks, km = oq.quantize_k(Kc[0, h, :nq], w.bits, w.meta_dtype)
-            vcod, vs, vm = oq.quantize_v(Vc[0, h, :nq], w.bits, w.meta_dtype)
-            assert np.array_equal(c.k_codes[0, h, :nq].cpu().numpy(), oq.pack_codes(kc, w.bits, "k"))
-            assert np.array_equal(c.v_codes[0, h, :nq].cpu().numpy(), oq.pack_codes(vcod, w.bits, "v"))
-            gk = c.k_meta[0, h, :nq // 32].cpu().numpy()
-            gv = c.v_meta[0, h, :nq].cpu().numpy()
+            kc, ks, km = oq.quantize_k(Kc[0, h, :nqf], w.bits, w.meta_dtype)
+            vcod, vs, vm = oq.quantize_v(Vc[0, h, :nqf], w.bits, w.meta_dtype)
+            assert np.array_equal(c.k_codes[0, h, :nqf].cpu().numpy(), oq.pack_codes(kc, w.bits, "k"))
+            assert np.array_equal(c.v_codes[0, h, :nqf].cpu().numpy(), oq.pack_codes(vcod, w.bits, "v"))
+            gk = c.k_meta[0, h, :nqf // 32].cpu().numpy()
+            gv = c.v_meta[0, h, :nqf].cpu().numpy()
             assert np.array_equal(gk[:, 0], ks.astype(mdt)) and np.array_equal(gk[:, 1], km.astype(mdt))
             assert np.array_equal(gv[..., 0], vs.astype(mdt)) and np.array_equal(gv[..., 1], vm.astype(mdt))
 
