@@ -148,6 +148,22 @@ vc_status vc_draft_attn_quant(const vc_kivi *c, int64_t n_q, int32_t r, const vo
                               float *lse, void *ws, size_t ws_bytes, void *stream);
 vc_status vc_draft_quant_workspace(const vc_kivi *c, int64_t n_q, int32_t r, int32_t Hq,
                                    size_t *bytes);
+/*
+ * vc_draft_attn_quant for callers that cannot allocate device memory: code being captured into a
+ * HIP graph, tight serving loops, harnesses that forbid hipMalloc. Same arguments, same kernels and
+ * the same results, without the workspace: the ticket counters and split partials live in a static
+ * scratch array of VC_DRAFT_NOALLOC_SCRATCH_BYTES (4 MiB) that the library holds on every GPU it
+ * runs on until the process ends. Calls whose workspace (vc_draft_quant_workspace) would exceed it
+ * return VC_ERR_WORKSPACE and enqueue nothing (the c2 shape, B 8, 8 kv heads, 32 query heads,
+ * needs ~1.7 MB). Each call first clears the counters it uses with a fill kernel on `stream`. All
+ * calls on one GPU share that GPU's scratch: calls that overlap in time on one GPU (concurrent
+ * streams, threads) race and must be serialised by the caller. Allocates nothing.
+ */
+#define VC_DRAFT_NOALLOC_SCRATCH_BYTES (4u << 20)
+vc_status vc_draft_attn_quant_noalloc(const vc_kivi *c, int64_t n_q, int32_t r, const void *k_new,
+                                      const void *v_new, int32_t new_dtype, int64_t new_bh_stride,
+                                      const void *q, int32_t q_dtype, int32_t Hq, float sm_scale,
+                                      float *out, float *lse, void *stream);
 
 /*
  * Draft attention over kept positions of a token-dropping compressor ("VeriCache: Turning Lossy KV

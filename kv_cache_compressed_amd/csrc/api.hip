@@ -11,6 +11,9 @@
 #include "common.h"
 #include "kernels.h"
 
+static_assert(vc::DRAFT_NOALLOC_SCRATCH_BYTES == VC_DRAFT_NOALLOC_SCRATCH_BYTES,
+              "scratch size in vc.h and kernels.h differ");
+
 namespace {
 
 thread_local std::string g_err;
@@ -163,6 +166,40 @@ vc_status vc_draft_attn_quant(const vc_kivi* c, int64_t n_q, int32_t r, const vo
   hipError_t e = vc::launch_draft_quant(*c, n_q, r, k_new, v_new, new_dtype, new_bh_stride, q, q_dtype,
                                         Hq, sm_scale, out, lse, ws, plan, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "vc_draft_attn_quant launch");
+  return ok();
+}
+
+vc_status vc_draft_attn_quant_noalloc(const vc_kivi* c, int64_t n_q, int32_t r, const void* k_new,
+                                      const void* v_new, int32_t new_dtype, int64_t new_bh_stride,
+                                      const void* q, int32_t q_dtype, int32_t Hq, float sm_scale,
+                                      float* out, float* lse, void* stream) {
+  if (vc_status st = check_kivi(c)) return st;
+  REQUIRE(n_q >= 0 && n_q % 32 == 0 && n_q <= c->tok_cap, "n_q must be a multiple of 32 in [0, tok_cap]");
+  REQUIRE(r >= 0 && r <= c->res_cap, "r must be in [0, res_cap]");
+  REQUIRE(n_q + r >= 1, "no keys: n_q + r must be >= 1");
+  REQUIRE(Hq >= 1 && Hq % c->Hkv == 0, "Hq must be a positive multiple of Hkv");
+  REQUIRE(valid_dtype(q_dtype), "q_dtype must be VC_F32, VC_F16 or VC_BF16");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(out);
+  REQUIRE((k_new == nullptr) == (v_new == nullptr), "k_new and v_new must both be given or both be null");
+  if (k_new) {
+    REQUIRE(r >= 1, "r must be >= 1 when the step's key/value is passed (it is token n_q + r - 1)");
+    REQUIRE(valid_dtype(new_dtype), "new_dtype must be VC_F32, VC_F16 or VC_BF16");
+    REQUIRE(new_bh_stride >= 128, "new_bh_stride must be >= 128");
+  }
+  if (Hq / c->Hkv > 8) return fail(VC_ERR_UNSUPPORTED, "Hq/Hkv > 8 is not supported");
+  if (c->res_cap > 512) return fail(VC_ERR_UNSUPPORTED, "res_cap > 512 is not supported");
+  if ((int64_t)c->B * c->Hkv > (int64_t)(vc::DRAFT_COUNTER_BYTES / 4))
+    return fail(VC_ERR_UNSUPPORTED, "B*Hkv > %d is not supported", (int)(vc::DRAFT_COUNTER_BYTES / 4));
+  const vc::DraftQuantPlan plan = vc::plan_draft_quant(*c, n_q, Hq);
+  if (plan.ws_bytes > vc::DRAFT_NOALLOC_SCRATCH_BYTES)
+    return fail(VC_ERR_WORKSPACE,
+                "this shape needs %zu bytes of scratch; the no-allocation call has %zu (use "
+                "vc_draft_attn_quant with a workspace)", plan.ws_bytes, vc::DRAFT_NOALLOC_SCRATCH_BYTES);
+  hipError_t e = vc::launch_draft_quant_noalloc(*c, n_q, r, k_new, v_new, new_dtype, new_bh_stride, q,
+                                                q_dtype, Hq, sm_scale, out, lse, plan,
+                                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_draft_attn_quant_noalloc");
   return ok();
 }
 

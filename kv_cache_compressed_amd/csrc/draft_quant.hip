@@ -31,10 +31,16 @@
 // the workspace) merges them with log-sum-exp, so one kernel does the whole call and no
 // cache-wide fence is needed.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
+
+// Scratch of the no-allocation draft call (vc_draft_attn_quant_noalloc): the ticket counters and
+// split partials a caller-owned workspace holds otherwise. One copy per GPU, held until the process
+// ends; host code reaches it only through the address hipGetSymbolAddress returns per device.
+static __device__ __align__(256) unsigned char scratch[vc::DRAFT_NOALLOC_SCRATCH_BYTES];
 
 namespace vc {
 
@@ -1150,6 +1156,52 @@ hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* 
   }
 #undef VC_DQ_LAUNCH
   return hipGetLastError();
+}
+
+namespace {
+
+__global__ void clear_counters_kernel(unsigned* counters, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) counters[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device ordinal: the device address of `scratch`
+
+}  // namespace
+
+hipError_t draft_scratch_pointer(void** ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_draft_quant_noalloc(const vc_kivi& c, int64_t n_q, int r, const void* k_new,
+                                      const void* v_new, int new_dtype, int64_t new_bh_stride,
+                                      const void* q, int q_dtype, int Hq, float sm_scale, float* out,
+                                      float* lse, const DraftQuantPlan& plan, hipStream_t s) {
+  void* ws = nullptr;
+  hipError_t err = draft_scratch_pointer(&ws);
+  if (err != hipSuccess) return err;
+  // the tickets start at zero on every call (a fill kernel, not a memset node, so the call can be
+  // captured into a graph); the partials are written before they are read
+  const int units = c.B * c.Hkv;
+  hipLaunchKernelGGL(clear_counters_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s,
+                     static_cast<unsigned*>(ws), units);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  return launch_draft_quant(c, n_q, r, k_new, v_new, new_dtype, new_bh_stride, q, q_dtype, Hq,
+                            sm_scale, out, lse, ws, plan, s);
 }
 
 }  // namespace vc

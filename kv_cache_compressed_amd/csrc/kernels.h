@@ -33,6 +33,15 @@ hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* 
                               int q_dtype, int Hq, float sm_scale, float* out, float* lse, void* ws,
                               const DraftQuantPlan& plan, hipStream_t s);
 
+// The same call with its workspace in a per-device static scratch array (no allocation):
+// counters cleared by a fill kernel on every call, then the same kernel as above.
+constexpr size_t DRAFT_NOALLOC_SCRATCH_BYTES = (size_t)4 << 20;
+hipError_t draft_scratch_pointer(void** ptr);
+hipError_t launch_draft_quant_noalloc(const vc_kivi& c, int64_t n_q, int r, const void* k_new,
+                                      const void* v_new, int new_dtype, int64_t new_bh_stride,
+                                      const void* q, int q_dtype, int Hq, float sm_scale, float* out,
+                                      float* lse, const DraftQuantPlan& plan, hipStream_t s);
+
 // Draft over kept positions.
 struct DraftDropPlan {
   int splits;

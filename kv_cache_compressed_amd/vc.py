@@ -49,6 +49,7 @@ _SIGS = {
     "vc_kivi_append": [_KP, _P, _P, _I32, _I64, _I64, _I64, _P],
     "vc_draft_attn_quant": [_KP, _I64, _I32, _P, _P, _I32, _I64, _P, _I32, _I32, _F, _P, _P, _P, _SZ, _P],
     "vc_draft_quant_workspace": [_KP, _I64, _I32, _I32, ctypes.POINTER(_SZ)],
+    "vc_draft_attn_quant_noalloc": [_KP, _I64, _I32, _P, _P, _I32, _I64, _P, _I32, _I32, _F, _P, _P, _P],
     "vc_draft_attn_drop": [_P, _P, _I32, _I32, _I32, _I64, _P, _I64, _I64, _P, _I32, _F, _P, _P, _P,
                            _SZ, _P],
     "vc_draft_drop_workspace": [_I32, _I32, _I32, _I64, ctypes.POINTER(_SZ)],
@@ -211,6 +212,21 @@ def vc_draft_attn_quant(cache: KiviCache, n_q: int, r: int, q, out, lse, ws: tor
     _check(lib().vc_draft_attn_quant(ctypes.byref(d), n_q, r, _ptr(k_new), _ptr(v_new), ndt, stride,
                                      _ptr(q), dtype_code(q), q.shape[1], sm_scale, _ptr(out), _ptr(lse),
                                      _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def vc_draft_attn_quant_noalloc(cache: KiviCache, n_q: int, r: int, q, out, lse, sm_scale: float,
+                                stream=None, k_new=None, v_new=None):
+    """vc_draft_attn_quant without a workspace (the library's per-device scratch; nothing allocated)."""
+    d = cache.desc()
+    stride, ndt = 0, 0
+    if k_new is not None:
+        assert k_new.shape == v_new.shape and k_new.stride() == v_new.stride() and k_new.dim() == 3
+        assert k_new.stride(2) == 1 and (k_new.shape[0] == 1 or
+                                         k_new.stride(0) == k_new.shape[1] * k_new.stride(1))
+        stride, ndt = k_new.stride(1), dtype_code(k_new)
+    _check(lib().vc_draft_attn_quant_noalloc(ctypes.byref(d), n_q, r, _ptr(k_new), _ptr(v_new), ndt, stride,
+                                             _ptr(q), dtype_code(q), q.shape[1], sm_scale, _ptr(out),
+                                             _ptr(lse), _stream(stream)))
 
 
 def vc_draft_drop_workspace(B: int, Hkv: int, Hq: int, n_keep: int) -> int:
