@@ -81,7 +81,11 @@ hipError_t launch_verify_copies(const void* k_past, const void* v_past, int64_t 
                                 hipStream_t copy);
 
 // Logits projection (+ argmax).
+// Row count from which the projection runs as a tiled fp32 matrix-core product (fewer rows: a
+// weight-streaming kernel with the reduction across lanes).
+constexpr int TILED_MIN_ROWS = 32;
 struct ProjectPlan {
+  bool tiled;            // the tiled matrix-core form (M >= TILED_MIN_ROWS)
   int nvt, nmt;          // vocabulary tiles, row tiles
   size_t counter_bytes;  // ticket counters at the start of the workspace (one per row tile)
   size_t ws_bytes;

@@ -8,7 +8,8 @@
 // concatenated head outputs; this kernel is that projection, and for draft steps it also takes
 // the argmax (lowest index on ties), so no logits round trip and no second launch are needed.
 //
-// Memory bound on W (V x Hq*128 fp32) for few rows. Workgroup = 512 threads on VT = 8 vocabulary
+// Memory bound on W (V x Hq*128 fp32) for few rows (below TILED_MIN_ROWS; more rows take the tiled
+// matrix-core form further down). Workgroup = 512 threads on VT = 8 vocabulary
 // rows and MT = 8 output rows (grid.y covers more rows); thread t owns channels 4t .. 4t+3 of each
 // 2048-channel chunk, so every W row is read with coalesced 16-byte loads, all VT rows of a chunk
 // in flight at once and the next chunk's loads issued before this chunk's FMAs. The VT x MT dot
@@ -200,12 +201,145 @@ __global__ void __launch_bounds__(PT) project_kernel(PArgs a) {
   a.idx[(int64_t)(row / a.L) * a.idx_b_stride + row % a.L] = (int32_t)(0xffffffffu - (uint32_t)key);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Many rows (the verify block's B*L rows): a tiled product on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 accumulation). Workgroup = 4 waves on TMT = 32
+// output rows x TVT = 64 vocabulary rows; wave w owns vocabulary rows 16w .. 16w + 15 against all
+// 32 output rows (two 16 x 16 tiles). K goes through LDS in chunks of KC = 64 (the next chunk's
+// loads in flight in registers while the current one is multiplied). Within a group of four
+// MFMA steps a lane of k-slot s takes the real channels 4s .. 4s + 3 of the group's 16 (the same
+// remap for both operands), so each operand read is one 16-byte LDS load per four steps. The
+// argmax (when asked for) goes through the same per-row slots and row-tile ticket as above.
+// ---------------------------------------------------------------------------------------------
+constexpr int TMT = 32;
+constexpr int TVT = 64;
+constexpr int KC = 64;
+constexpr int KCP = KC + 4;  // padded LDS row (floats)
+
+template <bool WBF16>
+__global__ void __launch_bounds__(256) project_tiled_kernel(PArgs a) {
+  __shared__ __attribute__((aligned(16))) float s_a[TMT * KCP];
+  __shared__ __attribute__((aligned(16))) float s_b[TVT * KCP];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.y * TMT, v0 = blockIdx.x * TVT;
+
+  // staging: A rows (t / 8, two 16-byte pieces), B rows (t / 4, four 16-byte pieces)
+  const int ar = tid >> 3, ap = tid & 7;
+  const int am = min(m0 + ar, a.M - 1);
+  const int64_t abase = ((int64_t)(am / a.L) * a.Hq * a.L + am % a.L) * 128;  // head 0 of row am
+  const int br = tid >> 2, bp = tid & 3;
+  const int64_t brow = (int64_t)min(v0 + br, a.V - 1) * a.Dm;
+  f32x4 ra[2], rb[4];
+  auto load = [&](int k0) {
+    const int64_t ao = abase + (int64_t)(k0 >> 7) * a.L * 128 + (k0 & 127);  // k0 % 64 == 0
+#pragma unroll
+    for (int z = 0; z < 2; ++z) ra[z] = *reinterpret_cast<const f32x4*>(a.o + ao + 4 * ap + 32 * z);
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+      const int64_t d = brow + k0 + 16 * bp + 4 * z;
+      if constexpr (WBF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.W) + d);
+        rb[z] = f32x4{bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16),
+                      bf16_bits_to_f32(u.y & 0xffffu), bf16_bits_to_f32(u.y >> 16)};
+      } else {
+        rb[z] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.W) + d);
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int z = 0; z < 2; ++z) *reinterpret_cast<f32x4*>(s_a + ar * KCP + 4 * ap + 32 * z) = ra[z];
+#pragma unroll
+    for (int z = 0; z < 4; ++z) *reinterpret_cast<f32x4*>(s_b + br * KCP + 16 * bp + 4 * z) = rb[z];
+  };
+
+  const int i16 = lane & 15, ks = lane >> 4;
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  load(0);
+  store();
+  __syncthreads();
+  for (int k0 = 0; k0 < a.Dm; k0 += KC) {
+    const bool more = k0 + KC < a.Dm;
+    if (more) load(k0 + KC);
+#pragma unroll
+    for (int g = 0; g < KC / 16; ++g) {
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(s_b + (16 * wave + i16) * KCP + 16 * g + 4 * ks);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(s_a + (16 * r + i16) * KCP + 16 * g + 4 * ks);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[r], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    if (more) {
+      store();
+      __syncthreads();
+    }
+  }
+
+  // lane holds C[m0 + 16 r + 4 ks + e][v0 + 16 wave + i16]
+  const int v = v0 + 16 * wave + i16;
+  if (a.z && v < a.V) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 16 * r + 4 * ks + e;
+        if (m < a.M) a.z[(int64_t)m * a.V + v] = acc[r][e];
+      }
+  }
+  if (!a.idx) return;
+  // tile-local argmax per row through LDS (the staging space is free after the loop's last barrier)
+  float* s_t = s_a;  // [TMT][TVT + 1]
+  static_assert(TMT * (TVT + 1) <= TMT * KCP + TVT * KCP, "argmax staging");
+  float* s_tt = s_a;
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      s_tt[(16 * r + 4 * ks + e) * (TVT + 1) + 16 * wave + i16] = v < a.V ? acc[r][e] : -INFINITY;
+  __syncthreads();
+  if (tid < TMT) {
+    const int m = m0 + tid;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int c = 0; c < TVT; ++c) {
+      const float x = s_t[tid * (TVT + 1) + c];
+      if (v0 + c < a.V && better(x, v0 + c, bv, bi)) { bv = x; bi = v0 + c; }
+    }
+    if (m < a.M && bi != 0x7fffffff) {
+      const unsigned long long old = __hip_atomic_fetch_max(a.slot + m, argmax_key(bv, bi),
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("" ::"v"(old));  // the atomic has been performed before the ticket below
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    unsigned* cnt = a.counters + blockIdx.y;
+    const int last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (unsigned)(a.nvt - 1);
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const int row = m0 + tid;
+  if (tid >= TMT || row >= a.M) return;
+  const unsigned long long key = __hip_atomic_load(a.slot + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(a.slot + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  a.idx[(int64_t)(row / a.L) * a.idx_b_stride + row % a.L] = (int32_t)(0xffffffffu - (uint32_t)key);
+}
+
 }  // namespace
 
 ProjectPlan plan_project(int M, int V) {
   ProjectPlan p;
-  p.nvt = (V + VT - 1) / VT;
-  p.nmt = (M + MT - 1) / MT;
+  p.tiled = M >= TILED_MIN_ROWS;
+  p.nvt = p.tiled ? (V + TVT - 1) / TVT : (V + VT - 1) / VT;
+  p.nmt = p.tiled ? (M + TMT - 1) / TMT : (M + MT - 1) / MT;
   const size_t counters = ((size_t)p.nmt * sizeof(unsigned) + 255) & ~(size_t)255;
   p.counter_bytes = counters;
   p.ws_bytes = counters + (size_t)M * sizeof(unsigned long long);
@@ -230,10 +364,16 @@ hipError_t launch_project(const void* W, int w_dtype, int V, const float* o, int
   a.counters = static_cast<unsigned*>(ws);
   a.slot = idx ? reinterpret_cast<unsigned long long*>(static_cast<uint8_t*>(ws) + plan.counter_bytes)
                : nullptr;
-  if (w_dtype == VC_BF16)
+  if (plan.tiled) {
+    if (w_dtype == VC_BF16)
+      project_tiled_kernel<true><<<dim3(plan.nvt, plan.nmt), 256, 0, s>>>(a);
+    else
+      project_tiled_kernel<false><<<dim3(plan.nvt, plan.nmt), 256, 0, s>>>(a);
+  } else if (w_dtype == VC_BF16) {
     project_kernel<true><<<dim3(plan.nvt, plan.nmt), PT, 0, s>>>(a);
-  else
+  } else {
     project_kernel<false><<<dim3(plan.nvt, plan.nmt), PT, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -131,7 +131,8 @@ def _project_ref(W, O):
     return z, 32 * 2.0 ** -24 * absum
 
 
-@pytest.mark.parametrize("B,L,Hq,V", [(8, 1, 32, 2048), (3, 5, 12, 1003), (2, 31, 32, 2048), (1, 1, 1, 77)])
+@pytest.mark.parametrize("B,L,Hq,V", [(8, 1, 32, 2048), (3, 5, 12, 1003), (2, 31, 32, 2048), (1, 1, 1, 77),
+                                      (3, 13, 8, 1003), (8, 31, 32, 2048), (33, 1, 2, 130)])
 def test_project_logits(gpu_lib, B, L, Hq, V):
     g = np.random.default_rng(B * 1000 + L * 10 + Hq)
     W = g.standard_normal((V, Hq * 128)).astype(np.float32)
@@ -165,7 +166,7 @@ def test_project_logits(gpu_lib, B, L, Hq, V):
 
 
 @pytest.mark.parametrize("B,L,Hq,V", [(8, 1, 32, 2048), (2, 31, 32, 2048), (1, 1, 44, 2048),
-                                      (1, 1, 16, 11264), (3, 5, 12, 1003)])
+                                      (1, 1, 16, 11264), (3, 5, 12, 1003), (5, 9, 4, 777)])
 def test_project_bf16_weights(gpu_lib, B, L, Hq, V):
     """bf16 weights are widened exactly: with bf16-valued weights the bf16 call gives the fp32 call's
     logits and argmax bit for bit, both within the oracle's bound (one-row shapes included: the
