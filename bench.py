@@ -29,8 +29,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "draft_quant_c2_traffic.json")
-DRAFT_SRC = os.path.join(ROOT, "kv_cache_compressed_amd", "csrc", "draft_quant.hip")
+PROFILES = os.path.join(ROOT, "profiles")
 
 METRIC = "draft/verify attention GB/s (% of 8 TB/s HBM) + verified tokens/s at 32K ctx"
 
@@ -60,13 +59,15 @@ def _src_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def _traffic_per_launch():
-    """HBM bytes per draft launch from the committed counter summary, if it matches the source."""
+def _traffic_per_launch(name: str):
+    """HBM bytes per launch from the committed counter summary profiles/<name>_traffic.json, if it
+    was measured on the kernel source as it is now (else None)."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(os.path.join(PROFILES, f"{name}_traffic.json")))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != _src_hash(DRAFT_SRC):
+    src = os.path.join(ROOT, rec.get("kernel_source", ""))
+    if not os.path.isfile(src) or rec.get("kernel_source_sha256_16") != _src_hash(src):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -357,8 +358,7 @@ def _e2e_llama_batch(torch, W, prompts, tokens: int, bits: int, x: int, opts: di
         torch.cuda.synchronize()
         t_prefill = time.perf_counter() - t0
         dec.warm()
-        for j in range(dec.x):  # one untimed round
-            dec.draft_step(j)
+        dec.draft_phase()  # one untimed round (captures the fused draft phase)
         dec.verify_step()
         warm = dec.commit()
         torch.cuda.synchronize()
@@ -486,6 +486,102 @@ def _e2e_llama(torch, seed: int, context: int, tokens: int, bits: int = 2, x: in
     return out
 
 
+def _remote_prefix(torch, seed: int, context: int, rounds: int, rate: float = 1.2e9) -> dict:
+    """Remote prefix caching, simulated: two requests on the one-layer decoder of `_e2e_decode`
+    (32/8 heads, d 128, d_model 256, vocab 2048), each with a `context`-token prefix whose compressed
+    cache (KIVI 4-bit, fp16 residual 128) crosses a link throttled to `rate` bytes/s
+    (harness.ThrottledLink) while its bf16 full cache stays in pinned host memory and is streamed
+    over the local host link by every verify (x = 30). VeriCache lock-step (both compressed caches
+    land, then both decode) and staggered (the first request decodes while the second's cache is
+    on the link); against greedy full-KV decoding of the same requests with the full cache behind
+    the local link (one streamed pass per token), and with the full cache shipped over the
+    throttled link into HBM first. Times from the requests' arrival to the last token."""
+    from kv_cache_compressed_amd import harness
+    from kv_cache_compressed_amd.decode_loop import GreedyDecoder, TokenDecoder
+
+    dev, V, dm, Hq, Hkv = "cuda", 2048, 256, 32, 8
+    g = torch.Generator(device=dev).manual_seed(seed)
+    rn = lambda *shape: torch.randn(*shape, generator=g, device=dev)
+    W = {"E": rn(V, dm), "P": 0.5 * rn(context + 4096, dm),
+         "Wq": rn(Hq * 128, dm) / dm ** 0.5, "Wk": rn(Hkv * 128, dm) / dm ** 0.5,
+         "Wv": rn(Hkv * 128, dm) / dm ** 0.5, "Wo": rn(dm, Hq * 128) / (Hq * 128) ** 0.5,
+         "Wlm": 3.0 * rn(V, dm) / dm ** 0.5}
+    prompts = [torch.randint(0, V, (context,), generator=g, device=dev).tolist() for _ in range(2)]
+    opts = dict(kv_dtype="bf16", host_past=True, chunk_tokens=65536)
+    kw = dict(x=30, bits=4, R=128, max_new=2 * rounds * 31 + 3000)
+    # warm-up: the first launches of every kernel pay one-time costs
+    w = TokenDecoder(W, Hq, Hkv, prompts[0][:4096], **kw, **opts)
+    w.warm()
+    w.generate(31)
+    del w
+    out = {"context": context, "link_GB_s": rate / 1e9, "rounds": rounds,
+           "model": "one layer, d_model 256, 32/8 heads, d 128, vocab 2048; KIVI 4-bit drafter, x = 30; "
+                    "full bf16 caches in pinned host memory (local host link)"}
+    seqs = {}
+    for sched in ("lockstep", "staggered"):
+        d0 = TokenDecoder(W, Hq, Hkv, prompts[0], **kw, **opts)
+        d1 = TokenDecoder(W, Hq, Hkv, prompts[1], copy_stream=d0.copy_stream, **kw, **opts)
+        for d in (d0, d1):
+            d.warm()
+        nb = [d.stage_remote() for d in (d0, d1)]
+        link = harness.ThrottledLink(rate)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        acc, inf = harness.remote_prefix_decode([d0, d1], link, [torch.cuda.current_stream(),
+                                                                 torch.cuda.Stream()], rounds,
+                                                staggered=sched == "staggered")
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        link.close()
+        emitted = sum(len(em) for ga in acc for em in ga)
+        seqs[sched] = [[t for em in ga for t in em] for ga in acc]
+        out[sched] = {"tok_s": round(emitted / el, 2), "emitted": emitted, "seconds": round(el, 4),
+                      "solo_rounds": inf["solo_rounds"],
+                      "transfer_ms": [round((e - s) * 1e3, 2) for s, e in inf["transfers"]],
+                      "accepted": [list(d0.rounds), list(d1.rounds)]}
+        out["compressed_bytes_per_request"] = nb
+        del d0, d1
+    out["staggered_speedup"] = round(out["staggered"]["tok_s"] / out["lockstep"]["tok_s"], 3)
+    per_req = min(len(s) for s in seqs["lockstep"])
+    # greedy full-KV decoding, the full cache behind the local host link (one streamed pass/token)
+    gd = [GreedyDecoder(W, Hq, Hkv, p, max_new=per_req + 8, **opts) for p in prompts]
+    for d in gd:
+        d.warm()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    greedy = [d.generate(per_req) for d in gd]
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    out["greedy_local"] = {"tok_s": round(2 * per_req / el, 2), "tokens_per_request": per_req,
+                           "seconds": round(el, 3)}
+    del gd
+    # greedy full-KV decoding with the full cache shipped over the throttled link into HBM first
+    gd = [GreedyDecoder(W, Hq, Hkv, p, max_new=per_req + 8, kv_dtype="bf16", host_past=False)
+          for p in prompts]
+    for d in gd:
+        d.warm()
+    nbf = [d.stage_remote() for d in gd]
+    link = harness.ThrottledLink(rate)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    trs = [link.send(d.remote_pieces) for d in gd]
+    remote_greedy = []
+    for d, tr in zip(gd, trs):
+        tr.wait()
+        remote_greedy.append(d.generate(per_req))
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    link.close()
+    out["greedy_remote_full"] = {"tok_s": round(2 * per_req / el, 2), "seconds": round(el, 3),
+                                 "full_bytes_per_request": nbf}
+    out["speedup_vs_greedy_local"] = round(out["staggered"]["tok_s"] / out["greedy_local"]["tok_s"], 3)
+    out["speedup_vs_greedy_remote_full"] = round(out["staggered"]["tok_s"] / out["greedy_remote_full"]["tok_s"], 3)
+    out["first_divergence"] = [
+        next((i for i in range(per_req) if seqs[s][r][i] != ref[r][i]), None)
+        for s in ("lockstep", "staggered") for ref in (greedy, remote_greedy) for r in range(2)]
+    return out
+
+
 def _back_to_back_us(torch, launch, n: int) -> float:
     """Mean duration of n launches enqueued back to back between two events (microseconds)."""
     for i in range(3):
@@ -537,6 +633,11 @@ def main():
                     help="also decode one request token by token on a one-layer decoder with a "
                          "host-streamed bf16 cache of this many tokens: VeriCache vs greedy")
     ap.add_argument("--e2e-tokens", type=int, default=64)
+    ap.add_argument("--remote-prefix", type=int, default=0,
+                    help="also decode two requests whose compressed caches (KIVI 4-bit) of a prefix of "
+                         "this many tokens cross a simulated 1.2 GB/s link, full caches in pinned host "
+                         "memory: VeriCache lock-step vs staggered vs greedy full-KV decoding")
+    ap.add_argument("--remote-rounds", type=int, default=8)
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every launch of a round from Python instead of replaying the "
                          "round captured as a HIP graph")
@@ -607,7 +708,8 @@ def main():
     d_flops = np.mean([st.draft_flops(j) for j in range(w.x)])
     d_mean_s = d_kernel_us * 1e-6
     achieved = d_bytes / d_mean_s / 1e9
-    traffic = _traffic_per_launch()
+    traffic = _traffic_per_launch({"c2": "draft_quant_c2", "c3": "draft_drop_c3"}.get(args.workload, ""))
+    v_traffic = _traffic_per_launch({"c2": "verify_c2", "c3": "verify_c3"}.get(args.workload, ""))
     v_mean_s = v_kernel_us * 1e-6
     v_gbs = st.verify_bytes() / v_mean_s / 1e9
     v_tflops = st.verify_flops() / v_mean_s / 1e12
@@ -632,13 +734,14 @@ def main():
         "roofline": {"bound": "hbm", "kernel": DRAFT_NAME[w.drafter, w.bits],
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic if args.workload == "c2" else None,
+                     "traffic": traffic,
                      "bytes_per_launch": int(d_bytes), "launch_us": round(d_kernel_us, 2),
                      "timing": f"HIP events around {3 * w.x} back-to-back launches of the round's draft "
                                "calls on the launch stream, after the timed replays (mean per launch)"},
         "draft_attention": {"launch_us": round(d_kernel_us, 2), "GB_s": round(achieved, 1),
                             "TFLOP_s": round(d_flops / d_mean_s / 1e12, 2)},
-        "verify_attention": {"launch_us": round(v_kernel_us, 2),
+        "verify_attention": {"launch_us": round(v_kernel_us, 2), "traffic": v_traffic,
+                             "bytes_per_launch": int(st.verify_bytes()),
                              "GB_s": round(v_gbs, 1), "frac_hbm": round(v_gbs / HBM_PEAK_GBS, 4),
                              "TFLOP_s": round(v_tflops, 2),
                              "frac_bf16_mfma": round(v_tflops / 2500.0, 4)},
@@ -680,6 +783,8 @@ def main():
                                                        args.decode_rounds)
     if args.e2e_context > 0:
         line["e2e_decode"] = _e2e_decode(torch, args.seed, args.e2e_context, args.e2e_tokens)
+    if args.remote_prefix > 0:
+        line["remote_prefix"] = _remote_prefix(torch, args.seed, args.remote_prefix, args.remote_rounds)
     if args.llama_context > 0:
         line["e2e_llama"] = _e2e_llama(torch, args.seed, args.llama_context, args.llama_tokens,
                                        args.llama_bits, args.llama_x, args.llama_batch)

@@ -11,6 +11,7 @@
  *   vc_quantize_kv       KIVI-style b-bit quantisation of cached keys/values   (compressor)
  *   vc_kivi_append       append full-precision tokens to the KIVI residual     (compressor)
  *   vc_draft_attn_quant  one-query decode attention over the quantised cache  (draft)
+ *   vc_draft_attn_quant_rows  the same with a context length per batch row     (draft)
  *   vc_draft_attn_drop   one-query decode attention over kept positions       (draft)
  *   vc_verify_attn       L-query causal block attention over the full cache   (verify)
  *   vc_verify_prefetch   first chunk copies of a host-streamed verify, issued early (verify)
@@ -20,6 +21,8 @@
  *   vc_select_keep       kept positions of a token-dropping drafter           (compressor)
  *   vc_project_logits    logits of the attention outputs (+ greedy argmax): the
  *                        single layer's stand-in for a model head              (harness)
+ *   vc_decoder_gemv      fused norm / product / rotation / SwiGLU / residual of
+ *   vc_rmsnorm           a decoder layer's few-row steps (the draft step's model) (harness)
  *   vc_workspace_bytes   workspace size of any of the calls above               (host only)
  *
  * Conventions (all calls):
@@ -148,6 +151,34 @@ vc_status vc_draft_attn_quant(const vc_kivi *c, int64_t n_q, int32_t r, const vo
                               float *lse, void *ws, size_t ws_bytes, void *stream);
 vc_status vc_draft_quant_workspace(const vc_kivi *c, int64_t n_q, int32_t r, int32_t Hq,
                                    size_t *bytes);
+/*
+ * vc_draft_attn_quant with a context length per batch row: batch row b attends over its own
+ * quantised tokens and residual tokens ("VeriCache: making lossy KV compression exact", The Core
+ * Idea: each request of a batch accepts its own number of drafts per round, so the requests' cached
+ * lengths drift apart; one launch then serves the whole batch).
+ *   n_q, r   device arrays of c->B int64 / int32 entries: row b has n_q[b] quantised tokens and
+ *            r[b] + r_add residual tokens (r_add lets one array serve every draft step of a round,
+ *            e.g. r = n - n_q and r_add = j + 1 at step j). Values are read by the kernel, so they
+ *            are not checked: each row's n_q is clamped to [0, tok_cap] and rounded down to a
+ *            multiple of 32, its residual count clamped to [0, res_cap]; a row left with no key gets
+ *            out = 0, lse = -inf.
+ *   n_q_max, r_max  host bounds of every row's values (they size the launch and the workspace,
+ *            vc_draft_quant_workspace(c, n_q_max, r_max, Hq) bytes)
+ *   k_new, v_new  NULL, or (b, kv head)'s row of 128 at b * new_b_stride + h * new_h_stride elements
+ *            (any batch-row stride, e.g. the k part of a fused q/k/v row), stored at each row's own
+ *            residual position before attending (each row's residual count must then be >= 1)
+ *   other arguments as for vc_draft_attn_quant. The lengths live in device memory so a captured
+ *   graph of a draft phase stays valid from round to round while the caller updates them.
+ * Results per row equal the scalar call's on that row alone up to fp32 summation order (the split of
+ * the work follows n_q_max).
+ */
+vc_status vc_draft_attn_quant_rows(const vc_kivi *c, const int64_t *n_q, const int32_t *r,
+                                   int32_t r_add, int64_t n_q_max, int32_t r_max, const void *k_new,
+                                   const void *v_new, int32_t new_dtype, int64_t new_b_stride,
+                                   int64_t new_h_stride, const void *q, int32_t q_dtype, int32_t Hq,
+                                   float sm_scale, float *out, float *lse, void *ws, size_t ws_bytes,
+                                   void *stream);
+
 /*
  * vc_draft_attn_quant for callers that cannot allocate device memory: code being captured into a
  * HIP graph, tight serving loops, harnesses that forbid hipMalloc. Same arguments, same kernels and
@@ -318,6 +349,36 @@ vc_status vc_project_logits(const void *W, int32_t w_dtype, int32_t V, const flo
 vc_status vc_select_keep(const float *scores, int64_t score_row_stride, int32_t rows, int64_t n,
                          int64_t sinks, int64_t recent, int64_t keep, int32_t *idx,
                          int64_t idx_row_stride, int64_t *n_keep, void *stream);
+
+/*
+ * Decoder-layer products for few rows: the layer work of a draft step around its attention, for a
+ * decoder whose drafter and verifier are the same model ("VeriCache: making lossy KV compression
+ * exact", The Core Idea: the drafter decodes each draft token with the full model over the
+ * compressed cache). Llama-form layers (pre-norm RMSNorm, rotary q/k, SwiGLU MLP). Not one of the
+ * path's five calls: they feed it.
+ *   Y[m][n] = s_m * sum_k X[m][k] g[k] W[n][k], m < M, n < N, k < K (K % 4 == 0), fp32 products and
+ *   sums; W [N][K] fp32 or bf16 (widened exactly), X [M][K] fp32 device, g = norm_gain [K] or NULL;
+ *   with a gain s_m = 1 / sqrt(mean_k X[m][k]^2 + eps) (the row's RMS norm), else s_m = 1, g = 1.
+ *   epilogue VC_DEC_STORE   out [M][N] = Y
+ *            VC_DEC_ADD     out [M][N] += Y (a residual stream)
+ *            VC_DEC_ROPE    Y = [q | k | v] heads of 128 (N = (Hq + 2 Hkv) 128); q and k heads are
+ *                           rotated, channel i < 64 with i + 64 at angle index p = pos[m] + pos_add:
+ *                           (y_i c - y_{i+64} s, y_{i+64} c + y_i s), c = cos_t[p][i], s = sin_t[p][i]
+ *                           (tables [n_pos][64] fp32; p is clamped to [0, n_pos)); q_out [M][Hq][128],
+ *                           k_out/v_out [M][Hkv][128] in out_dtype (VC_F32, or VC_BF16 rounded to
+ *                           nearest even)
+ *            VC_DEC_SWIGLU  Y = [gate | up] (N = 2F, N % 8 == 0): out [M][F] = silu(gate) * up
+ *   Unused pointers may be NULL. Weight-streaming: each weight is read once per 8 rows.
+ * vc_rmsnorm: Y[m] = X[m] * g / sqrt(mean(X[m]^2) + eps), X, Y [M][K] fp32 (may alias).
+ */
+enum { VC_DEC_STORE = 0, VC_DEC_ADD = 1, VC_DEC_ROPE = 2, VC_DEC_SWIGLU = 3 };
+vc_status vc_decoder_gemv(int32_t epilogue, const void *W, int32_t w_dtype, int32_t N, int32_t K,
+                          const float *X, int32_t M, const float *norm_gain, float eps, float *out,
+                          void *q_out, void *k_out, void *v_out, int32_t out_dtype, int32_t Hq,
+                          int32_t Hkv, const float *cos_t, const float *sin_t, int32_t n_pos,
+                          const int32_t *pos, int32_t pos_add, void *stream);
+vc_status vc_rmsnorm(const float *X, const float *g, float eps, int32_t M, int32_t K, float *Y,
+                     void *stream);
 
 /*
  * Workspace size of any call that takes one, by operation code and its size arguments (the same

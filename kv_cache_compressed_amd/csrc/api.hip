@@ -2,6 +2,7 @@
 //
 // Every argument is checked before anything is enqueued; on error nothing is enqueued and the
 // reason is kept in a thread-local string for vc_last_error(). No exception crosses the ABI.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -166,6 +167,41 @@ vc_status vc_draft_attn_quant(const vc_kivi* c, int64_t n_q, int32_t r, const vo
   hipError_t e = vc::launch_draft_quant(*c, n_q, r, k_new, v_new, new_dtype, new_bh_stride, q, q_dtype,
                                         Hq, sm_scale, out, lse, ws, plan, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "vc_draft_attn_quant launch");
+  return ok();
+}
+
+vc_status vc_draft_attn_quant_rows(const vc_kivi* c, const int64_t* n_q, const int32_t* r,
+                                   int32_t r_add, int64_t n_q_max, int32_t r_max, const void* k_new,
+                                   const void* v_new, int32_t new_dtype, int64_t new_b_stride,
+                                   int64_t new_h_stride, const void* q, int32_t q_dtype, int32_t Hq,
+                                   float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (vc_status st = check_kivi(c)) return st;
+  REQUIRE(n_q != nullptr && r != nullptr, "n_q and r (device arrays of B entries) are required");
+  REQUIRE(n_q_max >= 0 && n_q_max % 32 == 0 && n_q_max <= c->tok_cap,
+          "n_q_max must be a multiple of 32 in [0, tok_cap]");
+  REQUIRE(r_max >= 1 && r_max <= c->res_cap, "r_max must be in [1, res_cap]");
+  REQUIRE(Hq >= 1 && Hq % c->Hkv == 0, "Hq must be a positive multiple of Hkv");
+  REQUIRE(valid_dtype(q_dtype), "q_dtype must be VC_F32, VC_F16 or VC_BF16");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(out);
+  REQUIRE((k_new == nullptr) == (v_new == nullptr), "k_new and v_new must both be given or both be null");
+  if (k_new) {
+    REQUIRE(valid_dtype(new_dtype), "new_dtype must be VC_F32, VC_F16 or VC_BF16");
+    REQUIRE(new_h_stride >= 128 && new_b_stride >= 0, "new_h_stride must be >= 128, new_b_stride >= 0");
+  }
+  if (Hq / c->Hkv > 8) return fail(VC_ERR_UNSUPPORTED, "Hq/Hkv > 8 is not supported");
+  if (c->res_cap > 512) return fail(VC_ERR_UNSUPPORTED, "res_cap > 512 is not supported");
+  if ((int64_t)c->B * c->Hkv > (int64_t)(vc::DRAFT_COUNTER_BYTES / 4))
+    return fail(VC_ERR_UNSUPPORTED, "B*Hkv > %d is not supported", (int)(vc::DRAFT_COUNTER_BYTES / 4));
+  const vc::DraftQuantPlan plan = vc::plan_draft_quant(*c, n_q_max, Hq);
+  if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
+    return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,
+                ws ? ws_bytes : (size_t)0);
+  hipError_t e = vc::launch_draft_quant_rows(*c, n_q, r, r_add, n_q_max, r_max, k_new, v_new, new_dtype,
+                                             new_b_stride, new_h_stride, q, q_dtype, Hq, sm_scale, out,
+                                             lse, ws, plan, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_draft_attn_quant_rows launch");
   return ok();
 }
 
@@ -464,6 +500,79 @@ vc_status vc_project_logits(const void* W, int32_t w_dtype, int32_t V, const flo
   hipError_t e = vc::launch_project(W, w_dtype, V, o, B, Hq, L, logits, argmax, argmax_b_stride, ws,
                                     plan, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "vc_project_logits launch");
+  return ok();
+}
+
+vc_status vc_decoder_gemv(int32_t epilogue, const void* W, int32_t w_dtype, int32_t N, int32_t K,
+                          const float* X, int32_t M, const float* norm_gain, float eps, float* out,
+                          void* q_out, void* k_out, void* v_out, int32_t out_dtype, int32_t Hq,
+                          int32_t Hkv, const float* cos_t, const float* sin_t, int32_t n_pos,
+                          const int32_t* pos, int32_t pos_add, void* stream) {
+  REQUIRE(epilogue == VC_DEC_STORE || epilogue == VC_DEC_ADD || epilogue == VC_DEC_ROPE ||
+              epilogue == VC_DEC_SWIGLU,
+          "unknown epilogue %d", epilogue);
+  REQUIRE_PTR(W);
+  REQUIRE_PTR(X);
+  REQUIRE(w_dtype == VC_F32 || w_dtype == VC_BF16, "w_dtype must be VC_F32 or VC_BF16");
+  REQUIRE(M >= 1 && M <= 4096, "M must be in [1, 4096]");
+  REQUIRE(K >= 4 && K % 4 == 0, "K must be a positive multiple of 4");
+  REQUIRE(N >= 1, "N must be >= 1");
+  REQUIRE((int64_t)N * K < ((int64_t)1 << 31), "N*K must be < 2^31");
+  if (norm_gain) {
+    REQUIRE_PTR(norm_gain);
+    REQUIRE(eps >= 0.f, "eps must be >= 0");
+  }
+  if (epilogue == VC_DEC_ROPE) {
+    REQUIRE(Hq >= 1 && Hkv >= 1 && N == (Hq + 2 * Hkv) * 128, "ROPE: N must be (Hq + 2 Hkv) * 128");
+    REQUIRE_PTR(q_out);
+    REQUIRE_PTR(k_out);
+    REQUIRE_PTR(v_out);
+    REQUIRE(out_dtype == VC_F32 || out_dtype == VC_BF16, "out_dtype must be VC_F32 or VC_BF16");
+    REQUIRE_PTR(cos_t);
+    REQUIRE_PTR(sin_t);
+    REQUIRE(pos != nullptr, "pos is null");
+    REQUIRE(n_pos >= 1, "n_pos must be >= 1");
+  } else {
+    REQUIRE_PTR(out);
+    if (epilogue == VC_DEC_SWIGLU) REQUIRE(N % 8 == 0, "SWIGLU: N (gate and up columns) must be a multiple of 8");
+  }
+  vc::DecGemv d{};
+  d.epi = epilogue;
+  d.W = W;
+  d.w_bf16 = w_dtype == VC_BF16;
+  d.N = N;
+  d.K = K;
+  d.M = M;
+  d.X = X;
+  d.g = norm_gain;
+  d.eps = eps;
+  d.out = out;
+  d.q_out = q_out;
+  d.k_out = k_out;
+  d.v_out = v_out;
+  d.out_bf16 = out_dtype == VC_BF16;
+  d.Hq = Hq;
+  d.Hkv = Hkv;
+  d.cos_t = cos_t;
+  d.sin_t = sin_t;
+  d.n_pos = n_pos;
+  d.pos = pos;
+  d.pos_add = pos_add;
+  hipError_t e = vc::launch_dec_gemv(d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_decoder_gemv launch");
+  return ok();
+}
+
+vc_status vc_rmsnorm(const float* X, const float* g, float eps, int32_t M, int32_t K, float* Y,
+                     void* stream) {
+  REQUIRE_PTR(X);
+  REQUIRE_PTR(g);
+  REQUIRE_PTR(Y);
+  REQUIRE(M >= 1 && M <= 65535, "M must be in [1, 65535]");
+  REQUIRE(K >= 1, "K must be >= 1");
+  REQUIRE(eps >= 0.f, "eps must be >= 0");
+  hipError_t e = vc::launch_rmsnorm(X, g, eps, M, K, Y, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_rmsnorm launch");
   return ok();
 }
 

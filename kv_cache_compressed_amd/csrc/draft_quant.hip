@@ -85,7 +85,13 @@ struct DQArgs {
   const void* k_new;  // null, or residual token n_q + r - 1 to store before attending
   const void* v_new;
   int new_dtype;
-  int64_t new_bh_stride;  // elements between consecutive (b, kv head) rows of k_new / v_new
+  int64_t new_b_stride;   // elements between batch rows of k_new / v_new
+  int64_t new_h_stride;   // elements between the kv heads of one batch row
+  // Per batch row lengths (vc_draft_attn_quant_rows), in device memory: row b's quantised tokens
+  // row_nq[b] and residual tokens row_r[b] + row_radd, clamped into the cache; null: the scalars.
+  const int64_t* row_nq;
+  const int32_t* row_r;
+  int row_radd;
 };
 
 // Reciprocal of the slot-position power carried by unpacked element e of an operand.
@@ -1044,7 +1050,9 @@ __device__ void append_new_token(const DQArgs& a, int bh) {
   static_assert(THREADS == 2 * D, "one thread per key or value channel");
   const int c = threadIdx.x & (D - 1);
   const bool val = threadIdx.x >= D;
-  const float x = load_as_f32(val ? a.v_new : a.k_new, (int64_t)bh * a.new_bh_stride + c, a.new_dtype);
+  const int64_t src = (int64_t)(bh / a.Hkv) * a.new_b_stride + (int64_t)(bh % a.Hkv) * a.new_h_stride + c;
+  const float x = load_as_f32(val ? a.v_new : a.k_new, src, a.new_dtype);
+  if (a.n_q + a.r < 1) return;  // a row with no residual position (per-row lengths)
   const int64_t slot = (a.n_q + a.r - 1) % a.res_cap;
   const int64_t off = ((int64_t)bh * a.res_cap + slot) * D + c;
   void* dst = const_cast<void*>(val ? a.v_res : a.k_res);
@@ -1055,10 +1063,19 @@ __device__ void append_new_token(const DQArgs& a, int bh) {
 }
 
 template <int BITS, bool META_F16, bool RES_F16, int CPH>
-__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WG_PER_CU, WG_PER_CU))) draft_quant_kernel(DQArgs a) {
+__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WG_PER_CU, WG_PER_CU))) draft_quant_kernel(DQArgs a0) {
   __shared__ float smem[std::max(WAVES * RingPlan<BITS, META_F16>::BYTES / 4, RES_SMEM_FLOATS)];
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
+  DQArgs a = a0;
+  if (a.row_nq) {  // this batch row's lengths (the splits and partial layout stay the launch's)
+    const int b = bh / a.Hkv;
+    const int64_t nq = a.row_nq[b];
+    a.n_q = min(max(nq, (int64_t)0), a.tok_cap) / GROUP * GROUP;
+    a.r = min(max(a.row_r[b] + a.row_radd, 0), a.res_cap);
+    a.ngroups = (int)(a.n_q / GROUP);
+    a.units = a.ngroups + (int64_t)RES_UNITS * ((a.r + GROUP - 1) / GROUP);
+  }
   __builtin_amdgcn_s_setprio(3);  // lowered step by step as the wave's share is worked off
   // Work units: the quantised groups, then RES_UNITS per 32-token residual block; workgroup w
   // takes units [U w / nwg, U (w+1) / nwg). The last workgroup also runs the residual split
@@ -1102,15 +1119,23 @@ DraftQuantPlan plan_draft_quant(const vc_kivi& c, int64_t n_q, int Hq) {
   return p;
 }
 
-hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* k_new,
-                              const void* v_new, int new_dtype, int64_t new_bh_stride, const void* q,
-                              int q_dtype, int Hq, float sm_scale, float* out, float* lse, void* ws,
-                              const DraftQuantPlan& plan, hipStream_t s) {
+namespace {
+
+hipError_t launch_draft_quant_impl(const vc_kivi& c, int64_t n_q, int r, const int64_t* row_nq,
+                                   const int32_t* row_r, int row_radd,
+                                   const void* k_new, const void* v_new, int new_dtype,
+                                   int64_t new_b_stride, int64_t new_h_stride, const void* q, int q_dtype, int Hq,
+                                   float sm_scale, float* out, float* lse, void* ws,
+                                   const DraftQuantPlan& plan, hipStream_t s) {
   DQArgs a;
+  a.row_nq = row_nq;
+  a.row_r = row_r;
+  a.row_radd = row_radd;
   a.k_new = k_new;
   a.v_new = v_new;
   a.new_dtype = new_dtype;
-  a.new_bh_stride = new_bh_stride;
+  a.new_b_stride = new_b_stride;
+  a.new_h_stride = new_h_stride;
   a.k_codes = static_cast<const uint8_t*>(c.k_codes);
   a.v_codes = static_cast<const uint8_t*>(c.v_codes);
   a.k_meta = c.k_meta;
@@ -1156,6 +1181,27 @@ hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* 
   }
 #undef VC_DQ_LAUNCH
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* k_new,
+                              const void* v_new, int new_dtype, int64_t new_bh_stride, const void* q,
+                              int q_dtype, int Hq, float sm_scale, float* out, float* lse, void* ws,
+                              const DraftQuantPlan& plan, hipStream_t s) {
+  return launch_draft_quant_impl(c, n_q, r, nullptr, nullptr, 0, k_new, v_new, new_dtype,
+                                 new_bh_stride * c.Hkv, new_bh_stride, q, q_dtype, Hq, sm_scale, out,
+                                 lse, ws, plan, s);
+}
+
+hipError_t launch_draft_quant_rows(const vc_kivi& c, const int64_t* n_q, const int32_t* r, int r_add,
+                                   int64_t n_q_max, int r_max, const void* k_new, const void* v_new,
+                                   int new_dtype, int64_t new_b_stride, int64_t new_h_stride,
+                                   const void* q, int q_dtype, int Hq, float sm_scale, float* out,
+                                   float* lse, void* ws, const DraftQuantPlan& plan, hipStream_t s) {
+  return launch_draft_quant_impl(c, n_q_max, r_max, n_q, r, r_add, k_new, v_new, new_dtype,
+                                 new_b_stride, new_h_stride, q, q_dtype, Hq, sm_scale, out, lse, ws,
+                                 plan, s);
 }
 
 namespace {

@@ -33,6 +33,14 @@ hipError_t launch_draft_quant(const vc_kivi& c, int64_t n_q, int r, const void* 
                               int q_dtype, int Hq, float sm_scale, float* out, float* lse, void* ws,
                               const DraftQuantPlan& plan, hipStream_t s);
 
+// The same with n_q[b] and r[b] + r_add per batch row (device arrays, clamped into the cache);
+// plan for n_q_max.
+hipError_t launch_draft_quant_rows(const vc_kivi& c, const int64_t* n_q, const int32_t* r, int r_add,
+                                   int64_t n_q_max, int r_max, const void* k_new, const void* v_new,
+                                   int new_dtype, int64_t new_b_stride, int64_t new_h_stride,
+                                   const void* q, int q_dtype, int Hq, float sm_scale, float* out,
+                                   float* lse, void* ws, const DraftQuantPlan& plan, hipStream_t s);
+
 // The same call with its workspace in a per-device static scratch array (no allocation):
 // counters cleared by a fill kernel on every call, then the same kernel as above.
 constexpr size_t DRAFT_NOALLOC_SCRATCH_BYTES = (size_t)4 << 20;
@@ -94,6 +102,32 @@ ProjectPlan plan_project(int M, int V);
 hipError_t launch_project(const void* W, int w_dtype, int V, const float* o, int B, int Hq, int L,
                           float* z, int32_t* idx, int64_t idx_b_stride, void* ws,
                           const ProjectPlan& plan, hipStream_t s);
+
+// Decoder-layer products for few rows (decoder.hip).
+enum { DEC_STORE = 0, DEC_ADD = 1, DEC_ROPE = 2, DEC_SWIGLU = 3 };
+struct DecGemv {
+  int epi;
+  const void* W;
+  int w_bf16;
+  int N, K, M;
+  const float* X;
+  const float* g;  // norm gain or null
+  float eps;
+  float* out;
+  void* q_out;
+  void* k_out;
+  void* v_out;
+  int out_bf16;
+  int Hq, Hkv;
+  const float* cos_t;
+  const float* sin_t;
+  int n_pos;
+  const int32_t* pos;
+  int pos_add;
+};
+hipError_t launch_dec_gemv(const DecGemv& d, hipStream_t s);
+hipError_t launch_rmsnorm(const float* X, const float* g, float eps, int M, int K, float* Y,
+                          hipStream_t s);
 
 // Keep-list selection (token-dropping drafter).
 hipError_t launch_select_keep(const float* scores, int64_t s_stride, int rows, int64_t n, int64_t lo,

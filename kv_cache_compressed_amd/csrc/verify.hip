@@ -49,11 +49,13 @@ struct VArgs {
   int split_offset;        // partial index of this launch's split 0
   int causal;              // source is the round's block: row i sees tokens 0..i
   const uint16_t* k_blk;   // null, or the round's block [B][Hkv][L][D] as one more split
-  const uint16_t* v_blk;   //   (blockIdx.x == splits), causal, written to partial blk_index
+  const uint16_t* v_blk;   //   (the last split's workgroup runs it), causal, to partial blk_index
   int blk_index;
   int L, Hq, Hkv, G, total_splits;
   int Gw;                  // query heads per workgroup: G, or 4 when G > 4 (then ceil(G / 4)
                            //   workgroups per (b, kv head) and tile range, heads 4 z .. 4 z + 3)
+  int gsplits, units, gz;  // logical grid: gsplits tile ranges x units (b, kv head) x gz head slices
+                           //   (the launch is one-dimensional; see logical_block)
   float qscale;            // sm_scale * log2(e)
   float* part_o;
   float* part_ml;
@@ -127,8 +129,33 @@ __device__ __forceinline__ void tile_copy(uint8_t* ring, int slot, __amdgpu_buff
   }
 }
 
-// Workgroup = NW waves on one (b, kv head), heads Gw z .. Gw z + Gw - 1 of its group (z =
-// blockIdx.z) and one range of 32-token tiles; wave w < Gw owns one of them and its L rows (two
+// Logical block (split, unit, z) of linear workgroup W. The hardware deals workgroups to the 8 XCDs
+// in turn by linear id (XCD = W mod 8), and each XCD has its own L2. With two head slices per tile
+// range (G > 4) both slices must stream the same tiles through the same L2 at the same time, or
+// each tile is fetched from HBM twice: slice 0 of pair P runs as W = 16 (P / 8) + P % 8 and slice 1
+// as W + 8 (same XCD, dispatched right after). The grid is padded to whole groups of 16; padding
+// workgroups return at once. With one slice, W is the pair index itself (split fastest).
+struct LogicalBlock {
+  int split, unit, z;
+  bool live;
+};
+__device__ __forceinline__ LogicalBlock logical_block(const VArgs& a) {
+  const int W = (int)blockIdx.x;
+  int P = W, z = 0;
+  if (a.gz == 2) {
+    P = (W >> 4) * 8 + (W & 7);
+    z = (W >> 3) & 1;
+  }
+  LogicalBlock lb;
+  lb.live = P < a.gsplits * a.units;
+  lb.split = P % a.gsplits;
+  lb.unit = P / a.gsplits;
+  lb.z = z;
+  return lb;
+}
+
+// Workgroup = NW waves on one (b, kv head), heads Gw z .. Gw z + Gw - 1 of its group (z: the
+// logical head slice) and one range of 32-token tiles; wave w < Gw owns one of them and its L rows (two
 // 16-row column tiles); all NW waves copy tiles.
 // Tiles stream through a RING-stage LDS ring (RING - 1 in flight) with direct buffer -> LDS
 // copies, one barrier per tile. Keys feed QK^T as the row operand; values are read straight into
@@ -143,21 +170,23 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, gq = lane >> 4;
-  const int bh = blockIdx.y;
-  // Jobs of this workgroup: split blockIdx.x of the launch's source (if blockIdx.x < splits),
+  const LogicalBlock lb = logical_block(a);
+  if (!lb.live) return;  // grid padding
+  const int bh = lb.unit;
+  // Jobs of this workgroup: split lb.split of the launch's source (if lb.split < splits),
   // then, for the last workgroup of the row and when the round's block is given, the block as one
   // more causal split (it is one tile: a workgroup of its own would not fit the resident round).
-  const bool do_past = (int)blockIdx.x < a.splits;
-  const bool do_blk = a.k_blk != nullptr && (int)blockIdx.x == max(a.splits, 1) - 1;
+  const bool do_past = lb.split < a.splits;
+  const bool do_blk = a.k_blk != nullptr && lb.split == max(a.splits, 1) - 1;
   auto run_job = [&](const bool blk) {
   const uint16_t* const src_k = blk ? a.k_blk : a.k;
   const uint16_t* const src_v = blk ? a.v_blk : a.v;
   const int64_t src_stride = blk ? a.L : a.bh_stride, src_ntok = blk ? a.L : a.ntok;
-  const int src_splits = blk ? 1 : a.splits, split = blk ? 0 : blockIdx.x;
+  const int src_splits = blk ? 1 : a.splits, split = blk ? 0 : lb.split;
   const bool causal = blk || a.causal;
   const int sidx = blk ? a.blk_index : a.split_offset + split;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
-  const int hg = (int)blockIdx.z * a.Gw + wave;  // head within the kv group
+  const int hg = lb.z * a.Gw + wave;  // head within the kv group
   const bool computes = wave < a.Gw && hg < a.G;
   const int hq = kvh * a.G + min(hg, a.G - 1);
 
@@ -666,8 +695,13 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
   const unsigned gz = (unsigned)((G + 3) / 4);
   const dim3 block(64 * NW);
   const unsigned units = (unsigned)(B * Hkv);
-  auto launch_bf16 = [&](dim3 grid) {
-    hipLaunchKernelGGL(verify_bf16_kernel<NW>, grid, block, 0, compute, a);
+  a.units = (int)units;
+  a.gz = (int)gz;
+  auto launch_bf16 = [&](dim3 grid) {  // grid.x tile ranges x grid.y units x grid.z head slices
+    a.gsplits = (int)grid.x;
+    unsigned n = grid.x * grid.y * grid.z;
+    if (gz == 2) n = (n + 15) / 16 * 16;  // whole groups of 16 (see logical_block)
+    hipLaunchKernelGGL(verify_bf16_kernel<NW>, dim3(n), block, 0, compute, a);
   };
 
   a.k_blk = nullptr;

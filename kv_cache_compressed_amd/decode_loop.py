@@ -267,6 +267,28 @@ class TokenDecoder:
         self.rounds.append(a)
         return emitted
 
+    def stage_remote(self):
+        """Remote prefix caching (simulated): move the compressed cache's current contents (codes
+        and metadata of the n_q quantised tokens, both residual rings) to pinned host memory, as
+        the far side's copy, and clear the device copy, which must then arrive before the next
+        draft step (harness.remote_prefix_decode sends self.remote_pieces over a ThrottledLink).
+        Returns the compressed bytes."""
+        c, nq = self.cache, self.n_q
+        dev = []
+        for h in range(self.Hkv):
+            dev += [c.k_codes[0, h, :nq], c.v_codes[0, h, :nq], c.k_meta[0, h, :nq // 32],
+                    c.v_meta[0, h, :nq]]
+        dev += [c.k_res, c.v_res]
+        dev = [t for t in dev if t.numel()]
+        host = [torch.empty(t.shape, dtype=t.dtype, pin_memory=True) for t in dev]
+        for d, h in zip(dev, host):
+            h.copy_(d)
+        torch.cuda.synchronize()
+        for d in dev:
+            d.zero_()
+        self.remote_pieces = list(zip(dev, host))
+        return sum(t.numel() * t.element_size() for t in dev)
+
     def prefetch(self):
         """Host-streamed cache: issue the copies of this round's first two verify chunks now (the
         committed past is fixed for the round), so they cross the link while the draft steps run;
@@ -332,6 +354,24 @@ class GreedyDecoder:
         self.i = 0  # tokens generated so far (generate() continues from there)
         self.ws = vc.Workspace(device)
         self.ws_proj = torch.zeros((vc.vc_project_workspace(1, 1, mdl.V) + 3) // 4, **i32)
+
+    def stage_remote(self):
+        """Remote prefix caching (simulated), the full-cache baseline: move the device-resident
+        full cache's rows 0..n-1 to pinned host memory as the far side's copy and clear them; they
+        must arrive (self.remote_pieces over a harness.ThrottledLink) before the next step.
+        Returns the bytes."""
+        assert not self.host, "the baseline ships the full cache into HBM"
+        dev = []
+        for h in range(self.Hkv):
+            dev += [self.store.k[0, h, :self.n], self.store.v[0, h, :self.n]]
+        host = [torch.empty(t.shape, dtype=t.dtype, pin_memory=True) for t in dev]
+        for d, h in zip(dev, host):
+            h.copy_(d)
+        torch.cuda.synchronize()
+        for d in dev:
+            d.zero_()
+        self.remote_pieces = list(zip(dev, host))
+        return sum(t.numel() * t.element_size() for t in dev)
 
     def warm(self):
         """Size the workspace for the largest context this decoder can reach."""
@@ -758,14 +798,22 @@ class BatchedLlamaDecoder:
     memory), KIVI caches, context length and accepted counts, so requests that accept different
     numbers of drafts drift apart and each still emits exactly its own full-KV greedy tokens. The
     layer's norms, GEMMs, rotations and MLP run once over all requests' rows (rotation angles from
-    each row's own position); attention, quantisation, appends, logits and accept are libvc calls,
-    attention one call per request (its own context length). x = 0 gives plain greedy decoding of
-    the batch (a verify of one row per request over the full caches)."""
+    each row's own position). A layer's KIVI caches are one batched cache (a row per request; a
+    request's own appends and flushes go through its row). fused=True (default): a draft step is
+    libvc calls only, per layer the fused norm + q/k/v product + rotation (vc_decoder_gemv ROPE), one
+    draft attention launch for the whole batch with each row's own lengths
+    (vc_draft_attn_quant_rows), the output product into the residual, the fused norm + gate/up
+    product + SwiGLU and the down product into the residual, then the final norm and the head with
+    its greedy argmax: 23 launches for 4 layers (weights read as bf16 when they are bf16 values, the
+    same numbers in half the bytes). fused=False: the same step from PyTorch ops with one attention call per request. The
+    verify step's layer work (B x (x + 1) rows) runs on PyTorch GEMMs either way; its attention is one
+    call per request (each request's full cache is its own store). x = 0 gives plain greedy decoding
+    of the batch (a verify of one row per request over the full caches)."""
 
     def __init__(self, weights, Hq: int, Hkv: int, prompts, x: int, bits: int = 4, R: int = 32,
                  max_new: int = 256, kv_dtype: str = "f32", host_past: bool = False,
                  chunk_tokens: int = 65536, rope_theta: float = 500000.0, copy_stream=None,
-                 device: str = "cuda"):
+                 fused: bool = True, graphs: bool = True, device: str = "cuda"):
         assert "g_att" in weights, "Llama-form weights"
         self.E, self.Wlm = _dev(weights["E"], device), _dev(weights["Wlm"], device)
         self.g_f = _dev(weights["g_f"], device)
@@ -792,6 +840,16 @@ class BatchedLlamaDecoder:
         cos = torch.from_numpy(np.cos(ang).astype(np.float32)).to(device)
         sin = torch.from_numpy(np.sin(ang).astype(np.float32)).to(device)
         self.cs = torch.stack([torch.cat([cos, cos], 1), torch.cat([-sin, sin], 1)], 1).contiguous()
+        self.cos, self.sin = cos.contiguous(), sin.contiguous()
+        self.fused, self.graphs = fused, graphs
+        self.capture_stream = torch.cuda.Stream(device=device) if fused and graphs else None
+        if fused:  # the fused one-row products read bf16 copies of bf16-valued weights (the same
+            # values, half the bytes), else the fp32 weights themselves
+            ws_ = self.Wqkv + self.Wo + self.W13 + self.W2 + [self.Wlm]
+            exact = all(torch.equal(w.to(torch.bfloat16).float(), w) for w in ws_)
+            bf = (lambda w: w.to(torch.bfloat16).contiguous()) if exact else (lambda w: w)
+            self.Wqkv_b, self.Wo_b = [bf(w) for w in self.Wqkv], [bf(w) for w in self.Wo]
+            self.W13_b, self.W2_b, self.Wlm_b = [bf(w) for w in self.W13], [bf(w) for w in self.W2], bf(self.Wlm)
         f32 = dict(dtype=torch.float32, device=device)
         tk = dict(dtype=self.tdt, device=device)
         i32 = dict(dtype=torch.int32, device=device)
@@ -800,10 +858,20 @@ class BatchedLlamaDecoder:
                        for _ in range(B)]
         meta = vc.VC_F32 if kv_dtype == "f32" else vc.VC_F16
         res_cap = (R + 32 + L + 31) // 32 * 32
-        self.caches = [[vc.KiviCache(1, Hkv, self.cap, bits, meta, meta, res_cap, device)
-                        for _ in range(nl)] for _ in range(B)]
+        # per layer one batched KIVI cache; request b's row is self.caches[l].row(b)
+        self.caches = [vc.KiviCache(B, Hkv, self.cap, bits, meta, meta, res_cap, device) for _ in range(nl)]
         self.n_q = [32 * (max(0, n - R) // 32) for n in self.n]
         self.qkvc = torch.zeros((B, Hq + 2 * Hkv, D), **tk)       # draft rows' q, k, v
+        self.qd = torch.zeros((B, Hq, D), **tk)                   # fused step: q, k, v apart
+        self.kd = torch.zeros((B, Hkv, D), **tk)
+        self.vd = torch.zeros((B, Hkv, D), **tk)
+        self.Xd = torch.zeros((B, self.dm), **f32)                 # fused step: residual stream
+        self.Hd = torch.zeros((B, self.W13[0].shape[0] // 2), **f32)
+        self.Xn = torch.zeros((B, self.dm), **f32)
+        self.pos_d = torch.zeros((B,), **i32)                      # n_b (row positions = n_b + j)
+        self.nq_d = torch.zeros((B,), dtype=torch.int64, device=device)  # n_q_b
+        self.r0_d = torch.zeros((B,), **i32)                       # n_b - n_q_b (step j: + j + 1)
+        self.graph, self.graph_key = None, None                    # captured fused draft phase
         self.od = torch.zeros((B, Hq, D), **f32)
         self.lse_d = torch.zeros((B, Hq), **f32)
         self.qv = torch.zeros((B, Hq, L, D), **tk)
@@ -822,6 +890,7 @@ class BatchedLlamaDecoder:
         for b, p in enumerate(prompts):
             self._prefill(b, p)
         self.tok[:, 0] = torch.tensor([p[-1] for p in prompts], **i32)
+        self._upload_lengths()
         self.rounds = [[] for _ in range(B)]
 
     # ---- the layer outside attention, over all rows ------------------------------------------
@@ -865,7 +934,7 @@ class BatchedLlamaDecoder:
             Y = self._qkv(l, X, pos)
             Q, K, V = Y[:, :Hq], lay(Y[:, Hq:Hq + Hkv]), lay(Y[:, Hq + Hkv:])
             self.stores[b][l].write(0, K, V)
-            c, nq = self.caches[b][l], self.n_q[b]
+            c, nq = self.caches[l].row(b), self.n_q[b]
             if nq:
                 vc.vc_quantize_kv(c, K, V, 0, nq, src_bh_stride=n * D)
             if n > nq:
@@ -884,13 +953,15 @@ class BatchedLlamaDecoder:
 
     # ---- one round ------------------------------------------------------------------------
     def draft_step(self, j: int):
+        if self.fused:
+            return self._draft_step_fused(j, *self._phase_bounds())
         Hq, Hkv, B = self.Hq, self.Hkv, self.B
         pos = torch.tensor([n + j for n in self.n], device=self.device)
         X = self.E[self.tok[:, j].long()]
         for l in range(self.nl):
             self.qkvc.copy_(self._qkv(l, X, pos))
             for b in range(B):
-                c, nq = self.caches[b][l], self.n_q[b]
+                c, nq = self.caches[l].row(b), self.n_q[b]
                 r = self.n[b] - nq + j + 1
                 nb = vc.vc_draft_quant_workspace(c, nq, r, Hq)
                 vc.vc_draft_attn_quant(c, nq, r, self.qkvc[b:b + 1, :Hq], self.od[b:b + 1],
@@ -901,6 +972,37 @@ class BatchedLlamaDecoder:
         h = self._rms(X, self.g_f)
         vc.vc_project_logits(self.Wlm, h.view(B, -1, D), argmax=self.tok.view(-1)[j + 1:],
                              argmax_b_stride=self.L + 1, ws=self.ws_proj)
+
+    def _draft_step_fused(self, j: int, nq_max: int, r_max: int):
+        """Draft step j of every request as libvc launches: the embedding gather, then per layer
+        norm + q/k/v + rotation, the batch's draft attention (each row its own lengths from the
+        device arrays, the step's key/value stored into each row's residual), output product into
+        the residual, norm + gate/up + SwiGLU, down product into the residual; final norm and the
+        head's greedy argmax into block entry j + 1. Host work is fixed per step (no lengths read),
+        so the whole draft phase can be captured once and replayed."""
+        Hq, Hkv, B = self.Hq, self.Hkv, self.B
+        X = self.Xd
+        torch.index_select(self.E, 0, self.tok[:, j], out=X)
+        ws = self.ws_draft.get(vc.vc_draft_quant_workspace(self.caches[0], nq_max, r_max, Hq))
+        for l in range(self.nl):
+            vc.vc_decoder_gemv(vc.VC_DEC_ROPE, self.Wqkv_b[l], X, norm_gain=self.g_att[l], q_out=self.qd,
+                               k_out=self.kd, v_out=self.vd, Hq=Hq, Hkv=Hkv, cos_t=self.cos,
+                               sin_t=self.sin, pos=self.pos_d, pos_add=j)
+            vc.vc_draft_attn_quant_rows(self.caches[l], self.nq_d, self.r0_d, j + 1, nq_max, r_max, self.qd,
+                                        self.od, self.lse_d, ws, SM_SCALE, k_new=self.kd, v_new=self.vd)
+            vc.vc_decoder_gemv(vc.VC_DEC_ADD, self.Wo_b[l], self.od.view(B, -1), out=X)
+            vc.vc_decoder_gemv(vc.VC_DEC_SWIGLU, self.W13_b[l], X, norm_gain=self.g_mlp[l], out=self.Hd)
+            vc.vc_decoder_gemv(vc.VC_DEC_ADD, self.W2_b[l], self.Hd, out=X)
+        vc.vc_rmsnorm(X, self.g_f, self.Xn)
+        vc.vc_project_logits(self.Wlm_b, self.Xn.view(B, -1, D), argmax=self.tok.view(-1)[j + 1:],
+                             argmax_b_stride=self.L + 1, ws=self.ws_proj)
+
+    def _phase_bounds(self):
+        """(n_q_max, r_max) the fused draft phase is launched with: the largest quantised prefix
+        rounded up to 128 tokens and the residual ring's capacity, so that the launch shape (and a
+        captured phase) stays the same over many rounds."""
+        nq_max = min(self.caches[0].tok_cap, (max(self.n_q) + 127) // 128 * 128)
+        return nq_max, self.caches[0].res_cap
 
     def verify_step(self):
         Hq, Hkv, B, L = self.Hq, self.Hkv, self.B, self.L
@@ -937,30 +1039,54 @@ class BatchedLlamaDecoder:
             for l in range(self.nl):
                 k, v = self.kv_[l][b:b + 1, :, :a + 1], self.vv_[l][b:b + 1, :, :a + 1]
                 self.stores[b][l].write(n0, k, v)
-                vc.vc_kivi_append(self.caches[b][l], k, v, n0, a + 1, src_bh_stride=L * D)
+                vc.vc_kivi_append(self.caches[l].row(b), k, v, n0, a + 1, src_bh_stride=L * D)
             self.n[b] = n0 + a + 1
             while self.n[b] - self.n_q[b] >= self.R + 32:
                 g0 = self.n_q[b]
                 for l in range(self.nl):
                     Kg, Vg, stride = self.stores[b][l].device_rows(g0, g0 + 32)
-                    vc.vc_quantize_kv(self.caches[b][l], Kg, Vg, g0, 32, src_bh_stride=stride)
+                    vc.vc_quantize_kv(self.caches[l].row(b), Kg, Vg, g0, 32, src_bh_stride=stride)
                 self.n_q[b] = g0 + 32
             self.rounds[b].append(a)
         self.tok[:, 0] = self.next_tok
+        self._upload_lengths()
         return out
+
+    def _upload_lengths(self):
+        """Each request's position and KIVI split (device copies read by the fused draft step)."""
+        self.pos_d.copy_(torch.tensor(self.n, dtype=torch.int32))
+        self.nq_d.copy_(torch.tensor(self.n_q, dtype=torch.int64))
+        self.r0_d.copy_(torch.tensor([n - q for n, q in zip(self.n, self.n_q)], dtype=torch.int32))
 
     def warm(self):
         """Size the workspaces for the largest context this decoder can reach."""
         self.ws_verify.get(vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, self.cap, self.host,
                                                   self.chunk, self.vdt))
         r = self.R + 32 + self.L
-        self.ws_draft.get(vc.vc_draft_quant_workspace(self.caches[0][0], (self.cap - r) // 32 * 32, r,
+        self.ws_draft.get(vc.vc_draft_quant_workspace(self.caches[0], (self.cap - r) // 32 * 32, r,
                                                       self.Hq))
         torch.cuda.synchronize()
 
     def draft_phase(self):
-        for j in range(self.x):
-            self.draft_step(j)
+        """The x draft steps. Fused: replayed from a HIP graph of the whole phase, captured on first
+        use and again whenever the launch bounds change (every kernel of the phase reads the
+        requests' lengths and positions from device memory, so one capture serves many rounds)."""
+        if not (self.fused and self.graphs) or self.x == 0:
+            for j in range(self.x):
+                self.draft_step(j)
+            return
+        key = self._phase_bounds()
+        if self.graph is None or self.graph_key != key:
+            for j in range(self.x):  # eager once (sizes the workspace, loads the kernels)
+                self._draft_step_fused(j, *key)
+            torch.cuda.synchronize()
+            self.graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.graph, stream=self.capture_stream):
+                for j in range(self.x):
+                    self._draft_step_fused(j, *key)
+            self.graph_key = key
+            return
+        self.graph.replay()
 
     def set_round_inputs(self):
         """Nothing to load: each request's next round starts from its committed token (for the
@@ -970,8 +1096,7 @@ class BatchedLlamaDecoder:
         """Rounds until every request has `steps` more tokens; returns each request's tokens."""
         out = [[] for _ in range(self.B)]
         while min(len(o) for o in out) < steps:
-            for j in range(self.x):
-                self.draft_step(j)
+            self.draft_phase()
             self.verify_step()
             for o, em in zip(out, self.commit()):
                 o += em

@@ -12,6 +12,10 @@ logits with the greedy argmax), one verify pass of x+1 rows over the full cache,
 """
 from __future__ import annotations
 
+import queue
+import threading
+import time
+
 import numpy as np
 import torch
 
@@ -551,3 +555,125 @@ def staggered_decode(groups, streams, rounds: int, next_inputs):
     for s in streams:
         cur.wait_stream(s)
     return acc
+
+
+# ------------------------------------------------------------------------------------------
+# remote prefix caching, simulated: the compressed cache crosses a slow network link, the full
+# cache stays behind the local host link ("VeriCache: Turning Lossy KV Cache into Lossless LLM
+# Inference", Key Contributions: the second deployment pipeline; Methodology: 40 GB/s local
+# against 1.2 GB/s remote; "VeriCache: making lossy KV compression exact", The Tradeoff VeriCache
+# Is Trying to Escape: a prefix's cache held remotely is slow to bring in)
+# ------------------------------------------------------------------------------------------
+class Transfer:
+    """One transfer on a ThrottledLink: (device destination, pinned host source) pieces of equal
+    shape. `done` is set once every chunk's copy has been issued (the link time of the last one
+    included); `event` is recorded on the link's stream after the last copy."""
+
+    def __init__(self, pieces):
+        self.pieces = list(pieces)
+        self.nbytes = sum(d.numel() * d.element_size() for d, _ in self.pieces)
+        self.event = torch.cuda.Event()
+        self.done = threading.Event()
+        self.t_start = self.t_end = None
+
+    def wait(self, stream=None):
+        """The host waits until the transfer's copies are all issued; `stream` (default: the
+        current one) then waits for them to land."""
+        self.done.wait()
+        (stream or torch.cuda.current_stream()).wait_event(self.event)
+
+
+class ThrottledLink:
+    """A simulated link of `rate` bytes per second into GPU memory, for data that would come from
+    another machine. Transfers go out in the order they are sent, one at a time, each split into
+    chunks; chunk k of a transfer that starts at t0 is copied (pinned host -> device, on the link's
+    own stream) only once t0 + (bytes up to and including chunk k) / rate has passed, so a transfer
+    of B bytes lands no earlier than B / rate after it starts and the link is busy meanwhile. The
+    real host link is faster than the simulated one, so the pacing sets the arrival time. A host
+    thread does the pacing; nothing on the GPU waits or spins."""
+
+    def __init__(self, rate: float, chunk_bytes: int = 1 << 21, device: str = "cuda"):
+        assert rate > 0 and chunk_bytes > 0
+        self.rate, self.chunk = float(rate), int(chunk_bytes)
+        self.device = device
+        self.stream = torch.cuda.Stream(device=device)
+        self._q = queue.Queue()
+        self._free = 0.0  # host time at which the link finishes its last transfer
+        self._th = threading.Thread(target=self._run, daemon=True)
+        self._th.start()
+
+    def send(self, pieces) -> Transfer:
+        tr = Transfer(pieces)
+        for d, h in tr.pieces:
+            assert d.shape == h.shape and d.dtype == h.dtype and d.is_contiguous() and h.is_contiguous()
+            assert h.device.type == "cpu" and h.is_pinned(), "the far side's copy is pinned host memory"
+        self._q.put(tr)
+        return tr
+
+    def _run(self):
+        with torch.cuda.device(self.stream.device):
+            self._serve()
+
+    def _serve(self):
+        while True:
+            tr = self._q.get()
+            if tr is None:
+                return
+            t0 = max(time.perf_counter(), self._free)
+            sent = 0
+            with torch.cuda.stream(self.stream):
+                for d, h in tr.pieces:
+                    db, hb = d.reshape(-1).view(torch.uint8), h.reshape(-1).view(torch.uint8)
+                    for a in range(0, db.numel(), self.chunk):
+                        b = min(db.numel(), a + self.chunk)
+                        sent += b - a
+                        wait = t0 + sent / self.rate - time.perf_counter()
+                        if wait > 0:
+                            time.sleep(wait)
+                        db[a:b].copy_(hb[a:b], non_blocking=True)
+                tr.event.record(self.stream)
+            self._free = t0 + sent / self.rate
+            tr.t_start, tr.t_end = t0, self._free
+            tr.done.set()
+
+    def close(self):
+        self._q.put(None)
+        self._th.join()
+
+
+def remote_prefix_decode(groups, link: ThrottledLink, streams, rounds: int, staggered: bool = True,
+                         max_solo: int | None = None):
+    """Decode request groups whose compressed caches arrive over `link` (every group's compressed
+    cache is sent at once, as if the requests arrived together; each group's `remote_pieces` are
+    its compressed cache's destination/source pairs) while their full caches stay behind the local
+    host link and are streamed by every verify.
+
+    Lock-step (staggered=False): every compressed cache lands, then `rounds` lock-step rounds.
+    Staggered: group 0 decodes on its own as soon as its compressed cache has landed, round after
+    round (at most `max_solo` rounds, default `rounds`), while the other groups' caches are still
+    crossing the link; once all have landed,
+    `rounds` rounds of every group follow in the staggered schedule (`staggered_decode`). So the
+    slow link's time for the later groups is spent decoding the first one.
+
+    Returns (per group, the tokens each round emitted; {"solo_rounds": rounds group 0 ran alone,
+    "transfers": [(start, end) host times of each group's transfer]})."""
+    ng = len(groups)
+    cur = torch.cuda.current_stream()
+    transfers = [link.send(g.remote_pieces) for g in groups]
+    solo = []
+    if staggered:
+        transfers[0].wait(cur)
+        g0 = groups[0]
+        limit = rounds if max_solo is None else max_solo
+        while len(solo) < limit and not all(tr.done.is_set() for tr in transfers[1:]):
+            g0.draft_phase()
+            g0.verify_step()
+            solo.append(g0.commit())
+    for tr in transfers:
+        tr.wait(cur)
+    if staggered and ng > 1:
+        acc = staggered_decode(groups, streams, rounds, lambda g, r: ())
+    else:
+        acc = lockstep_decode(groups, rounds, lambda g, r: ())
+    acc[0] = solo + acc[0]
+    return acc, {"solo_rounds": len(solo), "transfers": [(tr.t_start, tr.t_end) for tr in transfers]}

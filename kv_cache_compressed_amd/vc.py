@@ -21,6 +21,7 @@ VC_OK, VC_ERR_INVALID, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_HIP = 0, 1, 
 VC_F32, VC_F16, VC_BF16 = 0, 1, 2
 VC_PAST_DEVICE, VC_PAST_HOST, VC_PAST_HOST_PREFETCHED = 0, 1, 2
 VC_OP_DRAFT_QUANT, VC_OP_DRAFT_DROP, VC_OP_VERIFY, VC_OP_PROJECT = 1, 2, 3, 4
+VC_DEC_STORE, VC_DEC_ADD, VC_DEC_ROPE, VC_DEC_SWIGLU = 0, 1, 2, 3
 _TORCH_DT = {torch.float32: VC_F32, torch.float16: VC_F16, torch.bfloat16: VC_BF16}
 
 _lib = None
@@ -49,6 +50,8 @@ _SIGS = {
     "vc_kivi_append": [_KP, _P, _P, _I32, _I64, _I64, _I64, _P],
     "vc_draft_attn_quant": [_KP, _I64, _I32, _P, _P, _I32, _I64, _P, _I32, _I32, _F, _P, _P, _P, _SZ, _P],
     "vc_draft_quant_workspace": [_KP, _I64, _I32, _I32, ctypes.POINTER(_SZ)],
+    "vc_draft_attn_quant_rows": [_KP, _P, _P, _I32, _I64, _I32, _P, _P, _I32, _I64, _I64, _P, _I32, _I32,
+                                 _F, _P, _P, _P, _SZ, _P],
     "vc_draft_attn_quant_noalloc": [_KP, _I64, _I32, _P, _P, _I32, _I64, _P, _I32, _I32, _F, _P, _P, _P],
     "vc_draft_attn_drop": [_P, _P, _I32, _I32, _I32, _I64, _P, _I64, _I64, _P, _I32, _F, _P, _P, _P,
                            _SZ, _P],
@@ -64,6 +67,9 @@ _SIGS = {
     "vc_select_keep": [_P, _I64, _I32, _I64, _I64, _I64, _I64, _P, _I64, ctypes.POINTER(_I64), _P],
     "vc_verify_stream_copies": [_P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P],
     "vc_workspace_bytes": [_I32, ctypes.POINTER(_I64), _I32, ctypes.POINTER(_SZ)],
+    "vc_decoder_gemv": [_I32, _P, _I32, _I32, _I32, _P, _I32, _P, _F, _P, _P, _P, _P, _I32, _I32, _I32,
+                        _P, _P, _I32, _P, _I32, _P],
+    "vc_rmsnorm": [_P, _P, _F, _I32, _I32, _P, _P],
     "vc_status_string": [_I32],
     "vc_last_error": [],
     "vc_abi_version": [],
@@ -147,6 +153,17 @@ class KiviCache:
             object.__setattr__(self, "_desc", None)
         object.__setattr__(self, name, value)
 
+    def row(self, b: int) -> "KiviCache":
+        """Batch row b as a one-row cache over this cache's storage (a request's own appends,
+        flushes and quantisation in a batched cache)."""
+        v = object.__new__(KiviCache)
+        for name in ("Hkv", "tok_cap", "bits", "res_cap", "d", "meta_dtype", "res_dtype"):
+            object.__setattr__(v, name, getattr(self, name))
+        object.__setattr__(v, "B", 1)
+        for name in self._BUFFERS:
+            setattr(v, name, getattr(self, name)[b:b + 1])
+        return v
+
     def desc(self) -> vc_kivi:
         """The C descriptor, built on first use and rebuilt after a buffer is replaced."""
         if getattr(self, "_desc", None) is None:
@@ -212,6 +229,24 @@ def vc_draft_attn_quant(cache: KiviCache, n_q: int, r: int, q, out, lse, ws: tor
     _check(lib().vc_draft_attn_quant(ctypes.byref(d), n_q, r, _ptr(k_new), _ptr(v_new), ndt, stride,
                                      _ptr(q), dtype_code(q), q.shape[1], sm_scale, _ptr(out), _ptr(lse),
                                      _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def vc_draft_attn_quant_rows(cache: KiviCache, n_q, r, r_add: int, n_q_max: int, r_max: int, q, out, lse,
+                             ws: torch.Tensor, sm_scale: float, stream=None, k_new=None, v_new=None):
+    """vc_draft_attn_quant with per-batch-row lengths: n_q (int64) and r (int32) device tensors of B
+    entries, row b's residual count r[b] + r_add; n_q_max, r_max host bounds. k_new/v_new
+    [B, Hkv, 128] views with any batch-row stride (channels contiguous)."""
+    d = cache.desc()
+    assert n_q.dtype == torch.int64 and r.dtype == torch.int32 and n_q.numel() == r.numel() == cache.B
+    bs, hs, ndt = 0, 0, 0
+    if k_new is not None:
+        assert k_new.shape == v_new.shape and k_new.stride() == v_new.stride() and k_new.dim() == 3
+        assert k_new.stride(2) == 1
+        bs, hs, ndt = k_new.stride(0), k_new.stride(1), dtype_code(k_new)
+    _check(lib().vc_draft_attn_quant_rows(ctypes.byref(d), _ptr(n_q), _ptr(r), r_add, n_q_max, r_max,
+                                          _ptr(k_new), _ptr(v_new), ndt, bs, hs, _ptr(q), dtype_code(q),
+                                          q.shape[1], sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                          _stream(stream)))
 
 
 def vc_draft_attn_quant_noalloc(cache: KiviCache, n_q: int, r: int, q, out, lse, sm_scale: float,
@@ -342,3 +377,23 @@ def vc_select_keep(scores, n: int, sinks: int, recent: int, keep: int, idx, stre
                                 _stream(stream)))
     return int(out.value)
 
+
+
+def vc_decoder_gemv(epilogue: int, W, X, out=None, norm_gain=None, eps: float = 1e-5, q_out=None,
+                    k_out=None, v_out=None, Hq: int = 0, Hkv: int = 0, cos_t=None, sin_t=None,
+                    pos=None, pos_add: int = 0, stream=None):
+    """W [N, K] fp32/bf16; X [M, K] fp32 (contiguous rows); see include/vc.h for the epilogues."""
+    N, K = W.shape
+    M = X.shape[0]
+    assert X.is_contiguous() and X.shape[1] == K and W.is_contiguous()
+    odt = dtype_code(q_out) if q_out is not None else VC_F32
+    n_pos = cos_t.shape[0] if cos_t is not None else 0
+    _check(lib().vc_decoder_gemv(epilogue, _ptr(W), dtype_code(W), N, K, _ptr(X), M, _ptr(norm_gain), eps,
+                                 _ptr(out), _ptr(q_out), _ptr(k_out), _ptr(v_out), odt, Hq, Hkv,
+                                 _ptr(cos_t), _ptr(sin_t), n_pos, _ptr(pos), pos_add, _stream(stream)))
+
+
+def vc_rmsnorm(X, g, Y, eps: float = 1e-5, stream=None):
+    """Y[m] = X[m] * g / sqrt(mean(X[m]^2) + eps); X, Y [M, K] fp32."""
+    M, K = X.shape
+    _check(lib().vc_rmsnorm(_ptr(X), _ptr(g), eps, M, K, _ptr(Y), _stream(stream)))

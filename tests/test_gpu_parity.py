@@ -8,6 +8,8 @@ so that a small bug cannot hide under the loose bar.
 
 Sizes span several tiles, splits and ragged tails while the float64 oracle finishes in seconds.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -1032,12 +1034,15 @@ def test_llama_decoder_emits_full_kv_greedy(gpu_lib, layers, bits, kv, host, gra
     assert dec.n_q > 32 * ((len(prompt) - 1 - 32) // 32), "the loop must have flushed"
 
 
-@pytest.mark.parametrize("bits,kv,host", [(4, "f32", False), (2, "bf16", True)])
-def test_batched_llama_decoder_per_request_greedy(gpu_lib, bits, kv, host):
-    """Three requests with prompts of different lengths decoded together (the layer's GEMMs over
-    all rows, attention per request): each request accepts its own counts, so the context lengths
-    drift apart, and each still emits its own prompt's full-KV greedy tokens (oracle), as does the
-    batch's greedy decoding (x = 0)."""
+@pytest.mark.parametrize("bits,kv,host,mode", [(4, "f32", False, "graph"), (2, "bf16", True, "graph"),
+                                               (2, "bf16", False, "eager"), (4, "f32", False, "torch")])
+def test_batched_llama_decoder_per_request_greedy(gpu_lib, bits, kv, host, mode):
+    """Three requests with prompts of different lengths decoded together: each request accepts its
+    own counts, so the context lengths drift apart, and each still emits its own prompt's full-KV
+    greedy tokens (oracle), as does the batch's greedy decoding (x = 0). Draft steps: the fused
+    libvc step (one attention launch per layer for the batch, each row its own lengths) replayed
+    from a captured graph round after round (a stale replay would show as wrong tokens), the same
+    enqueued eagerly, and the PyTorch-glue form with one attention call per request."""
     from kv_cache_compressed_amd.decode_loop import BatchedLlamaDecoder
     from oracle import loop as oloop
 
@@ -1055,7 +1060,9 @@ def test_batched_llama_decoder_per_request_greedy(gpu_lib, bits, kv, host):
     prompts = [[int(t) for t in g.integers(0, 384, n)] for n in (150, 97, 181)]
     steps = 30
     opts = dict(kv_dtype=kv, host_past=host, chunk_tokens=64)
-    dec = BatchedLlamaDecoder(W, 4, 2, prompts, x=6, bits=bits, R=32, max_new=steps + 32, **opts)
+    fused = dict(graph=dict(fused=True, graphs=True), eager=dict(fused=True, graphs=False),
+                 torch=dict(fused=False, graphs=False))[mode]
+    dec = BatchedLlamaDecoder(W, 4, 2, prompts, x=6, bits=bits, R=32, max_new=steps + 32, **opts, **fused)
     got = dec.generate(steps)
     greedy = BatchedLlamaDecoder(W, 4, 2, prompts, x=0, max_new=steps + 8, **opts).generate(steps)
     print(f"[batched llama {bits}-bit {kv}{' host' if host else ''}] accepted per round "
@@ -1126,3 +1133,184 @@ def test_token_decoders_staggered_two_requests(gpu_lib):
         assert a == b, f"request {g}"
         _check_resynced(a, _tiny_logits(m, prompts[g], a), f"request {g}")
         print(f"request {g}: {len(a)} tokens over {rounds} rounds", flush=True)
+
+
+def test_remote_prefix_staggered_matches_lockstep_and_oracle(gpu_lib):
+    """Remote prefix caching, simulated: two requests whose compressed (2-bit KIVI) caches cross a
+    throttled link while their bf16 full caches stay in pinned host memory, streamed by every
+    verify. The device copy of each compressed cache is cleared before it is sent, so decoding
+    before it has landed whole would show as wrong tokens. Lock-step (both caches land, then both
+    decode) and staggered (the first request decodes while the second's cache is on the link)
+    emit the same tokens per request, and those are the oracle's full-KV greedy tokens; the link
+    took at least bytes / rate per transfer, one after the other."""
+    from kv_cache_compressed_amd.decode_loop import TokenDecoder
+    from oracle import loop as oloop
+
+    m = oloop.TinyModel(seed=5, vocab=384, dm=256, d=128, Hq=4, Hkv=2, max_pos=1024, kv_bf16=True)
+    names = ("E", "P", "Wq", "Wk", "Wv", "Wo", "Wlm")
+    Wt = {k: getattr(m, k).astype(np.float32) for k in names}
+    for k in names:
+        setattr(m, k, Wt[k].astype(np.float64))
+    prompts = [[int(t) for t in np.random.default_rng(s).integers(0, 384, 300)] for s in (31, 32)]
+    rounds, x = 4, 8
+    opts = dict(kv_dtype="bf16", host_past=True, chunk_tokens=64)
+    res, info = {}, {}
+    for sched in ("lockstep", "staggered"):
+        d0 = TokenDecoder(Wt, 4, 2, prompts[0], x=x, bits=2, R=32, max_new=400, **opts)
+        d1 = TokenDecoder(Wt, 4, 2, prompts[1], x=x, bits=2, R=32, max_new=400,
+                          copy_stream=d0.copy_stream, **opts)
+        nbytes = [d.stage_remote() for d in (d0, d1)]
+        rate = nbytes[1] / 0.04  # the second cache spends ~40 ms on the link
+        link = harness.ThrottledLink(rate, chunk_bytes=4096)
+        t0 = time.perf_counter()
+        acc, inf = harness.remote_prefix_decode([d0, d1], link, [torch.cuda.current_stream(),
+                                                                 torch.cuda.Stream()], rounds,
+                                                staggered=sched == "staggered")
+        torch.cuda.synchronize()
+        link.close()
+        res[sched] = [[t for em in ga for t in em] for ga in acc]
+        info[sched] = inf
+        for (ts, te), nb in zip(inf["transfers"], nbytes):
+            assert te - ts >= nb / rate * 0.999 and te <= time.perf_counter()
+        (s0, e0), (s1, e1) = inf["transfers"]
+        assert s1 >= e0 - 1e-6, "transfers go one after the other"
+        print(f"[remote prefix {sched}] {nbytes} bytes at {rate / 1e6:.2f} MB/s; solo rounds "
+              f"{inf['solo_rounds']}; tokens {[len(r) for r in res[sched]]}; "
+              f"{time.perf_counter() - t0:.3f} s", flush=True)
+    assert info["staggered"]["solo_rounds"] >= 1, "the first request should decode while the second's cache is in flight"
+    for g in range(2):
+        a, b = res["lockstep"][g], res["staggered"][g]
+        k = min(len(a), len(b))
+        assert k >= rounds and a[:k] == b[:k], f"request {g}"
+        seq = max(a, b, key=len)
+        _check_resynced(seq, _tiny_logits(m, prompts[g], seq), f"remote prefix request {g}")
+
+
+def test_draft_quant_rows_mixed_lengths(gpu_lib):
+    """One launch over batch rows of different cached lengths (vc_draft_attn_quant_rows): each row
+    attends over its own quantised prefix and residual (one row with nothing quantised, one whose
+    residual is one token past a group), stores its step's key/value at its own residual slot, and
+    matches the oracle's decode over that row's keys; the same rows through the scalar call, one at a
+    time, agree within twice the kernel's arithmetic bound (the two launches split the work
+    differently, so their roundings differ)."""
+    base = synth.WORKLOADS["c2"].with_(B=3, n=1500, x=2)
+    K, V, Kn, Vn, Q, W = _inputs(base)
+    ns = [1500, 700, 90]
+    nqs = [oq.quantised_prefix(n, base.R, base.group) for n in ns]
+    c = vc.KiviCache(base.B, base.Hkv, max(nqs), base.bits, vc.VC_F16, vc.VC_F16, base.res_cap, "cuda")
+    for b, (n, nqb) in enumerate(zip(ns, nqs)):
+        Kd = torch.from_numpy(np.ascontiguousarray(K[b:b + 1, :, :n])).to("cuda", torch.bfloat16)
+        Vd = torch.from_numpy(np.ascontiguousarray(V[b:b + 1, :, :n])).to("cuda", torch.bfloat16)
+        cb = c.row(b)
+        if nqb:
+            vc.vc_quantize_kv(cb, Kd, Vd, 0, nqb)
+        vc.vc_kivi_append(cb, Kd[:, :, nqb:], Vd[:, :, nqb:], nqb, n - nqb, src_bh_stride=n * 128)
+    rs = [n - nqb + 1 for n, nqb in zip(ns, nqs)]  # plus the step's own key/value
+    q = torch.from_numpy(Q[:, :, 0]).to("cuda", torch.bfloat16).contiguous()
+    kn = torch.from_numpy(Kn[:, :, 0]).to("cuda", torch.bfloat16).contiguous()
+    vn = torch.from_numpy(Vn[:, :, 0]).to("cuda", torch.bfloat16).contiguous()
+    ws = torch.zeros(vc.vc_draft_quant_workspace(c, max(nqs), max(rs), base.Hq), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((base.B, base.Hq, 128), float("nan"), device="cuda")
+    lse = torch.full((base.B, base.Hq), float("nan"), device="cuda")
+    nq_d = torch.tensor(nqs, dtype=torch.int64, device="cuda")
+    r0_d = torch.tensor([r - 1 for r in rs], dtype=torch.int32, device="cuda")  # + r_add = 1
+    vc.vc_draft_attn_quant_rows(c, nq_d, r0_d, 1, max(nqs), max(rs), q, out, lse, ws, harness.SM_SCALE,
+                                k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(base.B):
+        for h in range(base.Hq):
+            g = h // base.G
+            lay = oq.KiviLayer(K[b, g, :ns[b]], V[b, g, :ns[b]], nqs[b], base.bits, base.meta_dtype,
+                               base.res_dtype)
+            lay.append(Kn[b, g, 0], Vn[b, g, 0])
+            ro, rl = oatt.decode(Q[b, h, 0], lay.keys(rs[b]), lay.values(rs[b]))
+            _close(o[b, h], ro, True, TIGHT["draft_quant"], f"rows b={b} n={ns[b]} h={h}")
+            assert abs(l[b, h] - rl) < 2e-3
+    # the scalar call on each row alone (its residual already holds the step's entry now)
+    for b in range(base.B):
+        cb = c.row(b)
+        wsb = torch.zeros(vc.vc_draft_quant_workspace(cb, nqs[b], rs[b], base.Hq), dtype=torch.uint8,
+                          device="cuda")
+        ob = torch.zeros((1, base.Hq, 128), device="cuda")
+        vc.vc_draft_attn_quant(cb, nqs[b], rs[b], q[b:b + 1], ob, None, wsb, harness.SM_SCALE)
+        torch.cuda.synchronize()
+        scale = max(1.0, float(np.abs(o[b]).max()))
+        assert np.abs(ob[0].cpu().numpy() - o[b]).max() <= 2 * TIGHT["draft_quant"] * scale, f"row {b}"
+
+
+@pytest.mark.parametrize("M,wdt", [(1, "bf16"), (16, "bf16"), (13, "f32"), (33, "bf16")])
+def test_decoder_gemv_epilogues(gpu_lib, M, wdt):
+    """The fused few-row layer products against the oracle's Llama layer pieces (RMS norm, rotary
+    embedding, SiLU, in float64): norm + q/k/v + rotation at per-row positions (bf16 and fp32
+    outputs), the output product added into a residual, norm + gate/up + SwiGLU, and a plain
+    product; ragged row counts and a K that is not a multiple of the 2048-wide chunk."""
+    from oracle import loop as oloop
+
+    g = np.random.default_rng(M * 7 + (wdt == "bf16"))
+    dm, Hq, Hkv, F, cap = 512, 4, 2, 1280, 300
+    tw = torch.bfloat16 if wdt == "bf16" else torch.float32
+    Wr = lambda n, k: torch.from_numpy((0.05 * g.standard_normal((n, k))).astype(np.float32)).to(tw)
+    W64 = lambda t: t.float().double().numpy()
+    X = g.standard_normal((M, dm)).astype(np.float32)
+    gain = (1 + 0.1 * g.standard_normal(dm)).astype(np.float32)
+    pos = g.integers(0, cap - 8, M).astype(np.int32)
+    theta = 500000.0
+    ang = np.arange(cap)[:, None] * theta ** (-2.0 * np.arange(64) / 128)
+    cos_t, sin_t = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    Xd, gd = dev(X), dev(gain)
+    # norm + q/k/v + rotation
+    Wqkv = Wr((Hq + 2 * Hkv) * 128, dm)
+    H = oloop.rms_norm(X, gain.astype(np.float64)) @ W64(Wqkv).T
+    Hh = H.reshape(M, Hq + 2 * Hkv, 128)
+    p = pos.astype(np.float64) + 3
+    ref_q = oloop.rope(Hh[:, :Hq], p[:, None], theta)
+    ref_k = oloop.rope(Hh[:, Hq:Hq + Hkv], p[:, None], theta)
+    ref_v = Hh[:, Hq + Hkv:]
+    for odt in (torch.float32, torch.bfloat16):
+        q = torch.full((M, Hq, 128), float("nan"), dtype=odt, device="cuda")
+        k = torch.full((M, Hkv, 128), float("nan"), dtype=odt, device="cuda")
+        v = torch.full((M, Hkv, 128), float("nan"), dtype=odt, device="cuda")
+        vc.vc_decoder_gemv(vc.VC_DEC_ROPE, Wqkv.cuda(), Xd, norm_gain=gd, q_out=q, k_out=k, v_out=v, Hq=Hq,
+                           Hkv=Hkv, cos_t=dev(cos_t), sin_t=dev(sin_t), pos=dev(pos), pos_add=3)
+        torch.cuda.synchronize()
+        tol = 2e-5 if odt == torch.float32 else 1e-2
+        for got, ref, name in ((q, ref_q, "q"), (k, ref_k, "k"), (v, ref_v, "v")):
+            err = np.abs(got.float().cpu().numpy() - ref).max()
+            print(f"[dec rope M={M} {wdt} {odt}] {name} max|err| {err:.2e}", flush=True)
+            assert err <= tol * max(1.0, np.abs(ref).max()), name
+        if odt == torch.bfloat16:  # rounded to nearest even from the fp32 result
+            q32 = torch.zeros((M, Hq, 128), device="cuda")
+            vc.vc_decoder_gemv(vc.VC_DEC_ROPE, Wqkv.cuda(), Xd, norm_gain=gd, q_out=q32, k_out=torch.zeros_like(k, dtype=torch.float32),
+                               v_out=torch.zeros_like(v, dtype=torch.float32), Hq=Hq, Hkv=Hkv,
+                               cos_t=dev(cos_t), sin_t=dev(sin_t), pos=dev(pos), pos_add=3)
+            assert torch.equal(q32.to(torch.bfloat16), q)
+    # output product added into the residual
+    O = g.standard_normal((M, Hq * 128)).astype(np.float32)
+    Wo = Wr(dm, Hq * 128)
+    R = g.standard_normal((M, dm)).astype(np.float32)
+    Rd = dev(R)
+    vc.vc_decoder_gemv(vc.VC_DEC_ADD, Wo.cuda(), dev(O), out=Rd)
+    ref = R.astype(np.float64) + O.astype(np.float64) @ W64(Wo).T
+    assert np.abs(Rd.cpu().numpy() - ref).max() <= 2e-5 * max(1.0, np.abs(ref).max())
+    # norm + gate/up + SwiGLU
+    W13 = Wr(2 * F, dm)
+    Hn = oloop.rms_norm(X, gain.astype(np.float64))
+    Z = Hn @ W64(W13).T
+    ref = oloop.silu(Z[:, :F]) * Z[:, F:]
+    Hd = torch.full((M, F), float("nan"), device="cuda")
+    vc.vc_decoder_gemv(vc.VC_DEC_SWIGLU, W13.cuda(), Xd, norm_gain=gd, out=Hd)
+    assert np.abs(Hd.cpu().numpy() - ref).max() <= 2e-5 * max(1.0, np.abs(ref).max())
+    # plain product with K = 2560 (a chunk and a ragged one), N not a multiple of 8
+    W2 = Wr(77, 2560)
+    Xk = g.standard_normal((M, 2560)).astype(np.float32)
+    Y = torch.full((M, 77), float("nan"), device="cuda")
+    vc.vc_decoder_gemv(vc.VC_DEC_STORE, W2.cuda(), dev(Xk), out=Y)
+    ref = Xk.astype(np.float64) @ W64(W2).T
+    assert np.abs(Y.cpu().numpy() - ref).max() <= 2e-5 * max(1.0, np.abs(ref).max())
+    # the plain norm
+    Yn = torch.zeros_like(Xd)
+    vc.vc_rmsnorm(Xd, gd, Yn)
+    assert np.abs(Yn.cpu().numpy() - oloop.rms_norm(X, gain.astype(np.float64))).max() < 1e-5
