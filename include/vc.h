@@ -23,6 +23,7 @@
  *                        single layer's stand-in for a model head              (harness)
  *   vc_decoder_gemv      fused norm / product / rotation / SwiGLU / residual of
  *   vc_rmsnorm           a decoder layer's few-row steps (the draft step's model) (harness)
+ *   vc_embed_rows        embedding rows of a block entry's tokens               (harness)
  *   vc_workspace_bytes   workspace size of any of the calls above               (host only)
  *
  * Conventions (all calls):
@@ -370,6 +371,8 @@ vc_status vc_select_keep(const float *scores, int64_t score_row_stride, int32_t 
  *            VC_DEC_SWIGLU  Y = [gate | up] (N = 2F, N % 8 == 0): out [M][F] = silu(gate) * up
  *   Unused pointers may be NULL. Weight-streaming: each weight is read once per 8 rows.
  * vc_rmsnorm: Y[m] = X[m] * g / sqrt(mean(X[m]^2) + eps), X, Y [M][K] fp32 (may alias).
+ * vc_embed_rows: out[m] = E[tok[m * tok_stride]] for m < M, E [V][K] fp32, tok int32 (device, any
+ *   stride, e.g. one block entry of every request); an id outside [0, V) gives a zero row.
  */
 enum { VC_DEC_STORE = 0, VC_DEC_ADD = 1, VC_DEC_ROPE = 2, VC_DEC_SWIGLU = 3 };
 vc_status vc_decoder_gemv(int32_t epilogue, const void *W, int32_t w_dtype, int32_t N, int32_t K,
@@ -379,6 +382,8 @@ vc_status vc_decoder_gemv(int32_t epilogue, const void *W, int32_t w_dtype, int3
                           const int32_t *pos, int32_t pos_add, void *stream);
 vc_status vc_rmsnorm(const float *X, const float *g, float eps, int32_t M, int32_t K, float *Y,
                      void *stream);
+vc_status vc_embed_rows(const float *E, int32_t V, int32_t K, const int32_t *tok, int64_t tok_stride,
+                        int32_t M, float *out, void *stream);
 
 /*
  * Workspace size of any call that takes one, by operation code and its size arguments (the same

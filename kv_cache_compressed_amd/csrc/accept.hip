@@ -5,9 +5,10 @@
 // the full-cache prediction; the full-cache token is emitted there, or the extra prediction when
 // every draft matches. Ties in the argmax go to the lowest token id.
 //
-// One workgroup of 1024 threads (16 waves) per batch row: wave w scans rows w, w+16, ... with
-// 16-byte loads and a shuffle reduction of (value, index) pairs, then one thread walks the L
-// argmax values to find the first disagreement. No atomics, no inter-workgroup traffic.
+// One workgroup of 1024 threads (16 waves) per batch row: the L rows one after the other, each
+// scanned by all 16 waves (a slice each) with 16-byte loads, a shuffle reduction of (value, index)
+// pairs per wave and an LDS reduction over the waves; then one thread walks the L argmax values to
+// find the first disagreement. No atomics, no inter-workgroup traffic.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,26 +30,32 @@ __global__ void __launch_bounds__(1024) accept_kernel(const float* __restrict__ 
                                                       int32_t* __restrict__ next_token,
                                                       int32_t* __restrict__ argmax_out) {
   __shared__ int s_arg[MAX_L];
+  __shared__ float s_bv[WAVES];
+  __shared__ int s_bi[WAVES];
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool vec = (V % 4) == 0;
-  for (int row = wave; row < L; row += WAVES) {
+  // Rows one after the other, each spread over all 16 waves (wave w scans a 1/16 slice of the
+  // row), so a single row (a greedy step) still has 1024 threads' loads in flight.
+  for (int row = 0; row < L; ++row) {
     const float* z = logits + ((int64_t)b * L + row) * V;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     if (vec) {
-      // UNROLL 16-byte loads per lane in flight at a time (lanes past the row re-read its last
+      // UNROLL 16-byte loads per lane in flight at a time (lanes past the slice re-read its last
       // float4 and lose every comparison: an equal value at a higher index never wins)
-      constexpr int UNROLL = 8;
+      constexpr int UNROLL = 4;
       const float4* z4 = reinterpret_cast<const float4*>(z);
       const int n4 = V / 4;
-      for (int i0 = 0; i0 < n4; i0 += 64 * UNROLL) {
+      const int per = (n4 + WAVES - 1) / WAVES;
+      const int s0 = min(wave * per, n4), s1 = min(s0 + per, n4);
+      for (int i0 = s0; i0 < s1; i0 += 64 * UNROLL) {
         float4 t[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) t[u] = z4[min(i0 + 64 * u + lane, n4 - 1)];
+        for (int u = 0; u < UNROLL; ++u) t[u] = z4[min(i0 + 64 * u + lane, s1 - 1)];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-          const int base = 4 * min(i0 + 64 * u + lane, n4 - 1);
+          const int base = 4 * min(i0 + 64 * u + lane, s1 - 1);
           if (better(t[u].x, base + 0, bv, bi)) { bv = t[u].x; bi = base + 0; }
           if (better(t[u].y, base + 1, bv, bi)) { bv = t[u].y; bi = base + 1; }
           if (better(t[u].z, base + 2, bv, bi)) { bv = t[u].z; bi = base + 2; }
@@ -56,7 +63,7 @@ __global__ void __launch_bounds__(1024) accept_kernel(const float* __restrict__ 
         }
       }
     } else {
-      for (int i = lane; i < V; i += 64) {
+      for (int i = threadIdx.x; i < V; i += 64 * WAVES) {
         const float t = z[i];
         if (better(t, i, bv, bi)) { bv = t; bi = i; }
       }
@@ -67,11 +74,20 @@ __global__ void __launch_bounds__(1024) accept_kernel(const float* __restrict__ 
       if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
     }
     if (lane == 0) {
-      s_arg[row] = bi;
-      if (argmax_out) argmax_out[(int64_t)b * L + row] = bi;
+      s_bv[wave] = bv;
+      s_bi[wave] = bi;
     }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float v = s_bv[0];
+      int ix = s_bi[0];
+      for (int w = 1; w < WAVES; ++w)
+        if (better(s_bv[w], s_bi[w], v, ix)) { v = s_bv[w]; ix = s_bi[w]; }
+      s_arg[row] = ix;
+      if (argmax_out) argmax_out[(int64_t)b * L + row] = ix;
+    }
+    __syncthreads();  // s_bv / s_bi are reused by the next row
   }
-  __syncthreads();
   if (threadIdx.x == 0) {
     int a = L - 1;
     for (int i = 0; i < L - 1; ++i) {

@@ -576,6 +576,18 @@ vc_status vc_rmsnorm(const float* X, const float* g, float eps, int32_t M, int32
   return ok();
 }
 
+vc_status vc_embed_rows(const float* E, int32_t V, int32_t K, const int32_t* tok, int64_t tok_stride,
+                        int32_t M, float* out, void* stream) {
+  REQUIRE_PTR(E);
+  REQUIRE_PTR(out);
+  REQUIRE(tok != nullptr, "tok is null");
+  REQUIRE(V >= 1 && K >= 1 && M >= 1 && M <= 65535, "V, K >= 1 and M in [1, 65535]");
+  REQUIRE(tok_stride >= 1, "tok_stride must be >= 1");
+  hipError_t e = vc::launch_embed(E, V, K, tok, tok_stride, M, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_embed_rows launch");
+  return ok();
+}
+
 vc_status vc_workspace_bytes(int32_t op, const int64_t* dims, int32_t ndims, size_t* bytes) {
   REQUIRE(bytes != nullptr, "bytes is null");
   REQUIRE(dims != nullptr || ndims == 0, "dims is null");

@@ -11,11 +11,11 @@
 // One kernel, four epilogues. Y[m][n] = s_m * sum_k X[m][k] g[k] W[n][k] with W [N][K] fp32 or bf16
 // (bf16 widened exactly), fp32 products and accumulation, s_m = 1 / sqrt(mean_k X[m][k]^2 + eps)
 // and g the norm gain when the norm is fused (else s_m = 1, g = 1). The sum of squares is gathered
-// from the same loads as the product, so the norm costs no extra pass. Workgroup = 512 threads on
-// 8 output columns and 8 rows; thread t owns k = 4t .. 4t+3 of every 2048-wide chunk; the 64 dot
-// products are reduced across each wave by recursive halving and across the 8 waves through LDS.
-// The 8 columns are two groups of 4 taken P columns apart (c .. c+3 and c+P .. c+P+3), so the
-// epilogues that combine column c with column c+P find both in one workgroup:
+// from the same loads as the product, so the norm costs no extra pass. Workgroup = 256 threads on
+// 4 output columns and 16 rows; thread t owns k = 4t .. 4t+3 of every 1024-wide chunk; the 64 dot
+// products are reduced across each wave by recursive halving and across the 4 waves through LDS.
+// The 4 columns are two pairs taken P columns apart (c, c+1 and c+P, c+P+1), so the epilogues that
+// combine column c with column c+P find both in one workgroup:
 //   STORE   Y -> out (fp32)
 //   ADD     out += Y (the residual stream)
 //   ROPE    Y holds [q | k | v] heads of 128: q and k are rotated (channel i with i + 64, angle
@@ -29,10 +29,11 @@ namespace vc {
 
 namespace {
 
-constexpr int GT = 512;        // threads
+constexpr int GT = 256;        // threads (1 wave per SIMD: 3 workgroups fit a CU)
 constexpr int GW = GT / 64;    // waves
-constexpr int GV = 8;          // output columns per workgroup (two groups of 4, P apart)
-constexpr int GM = 8;          // rows per workgroup
+constexpr int GV = 4;          // output columns per workgroup (two groups of 2, P apart)
+constexpr int GM = 16;         // rows per workgroup (a draft step's batch in one tile: each weight
+                               // is read once per 16 rows)
 constexpr int GCHUNK = 4 * GT; // k per chunk
 
 struct GArgs {
@@ -90,8 +91,8 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
 
 // First column of this workgroup's first group.
 __device__ __forceinline__ int first_col(const GArgs& a, int w) {
-  const int per = a.P / 4;  // workgroups per pairing period
-  return (w / per) * a.period + (w % per) * 4;
+  const int per = a.P / 2;  // workgroups per pairing period
+  return (w / per) * a.period + (w % per) * 2;
 }
 
 template <bool WBF16>
@@ -105,7 +106,7 @@ __global__ void __launch_bounds__(GT) dec_gemv_kernel(GArgs a) {
   const void* wrow[GV];
 #pragma unroll
   for (int v = 0; v < GV; ++v) {
-    const int col = c0 + (v & 3) + (v >> 2) * a.P;
+    const int col = c0 + (v & 1) + (v >> 1) * a.P;
     wrow[v] = static_cast<const char*>(a.W) + (int64_t)min(col, a.N - 1) * a.K * wb;
   }
   const float* xrow[GM];
@@ -159,7 +160,7 @@ __global__ void __launch_bounds__(GT) dec_gemv_kernel(GArgs a) {
   }
   __syncthreads();
   if (wave != 0) return;
-  // lane = v * GM + m: column group v >> 2, column offset v & 3, row m
+  // lane = v * GM + m: column pair v >> 1, column offset v & 1, row m
   const int v = lane / GM, m = lane % GM;
   float y = 0.f;
 #pragma unroll
@@ -170,10 +171,10 @@ __global__ void __launch_bounds__(GT) dec_gemv_kernel(GArgs a) {
     for (int w2 = 0; w2 < GW; ++w2) t += s_ss[w2][m];
     y *= 1.0f / sqrtf(t / (float)a.K + a.eps);
   }
-  const float partner = __shfl_xor(y, 4 * GM, 64);  // same row, the other column group
+  const float partner = __shfl_xor(y, 2 * GM, 64);  // same row, the other column pair
   const int row = m0 + m;
-  const int col = c0 + (v & 3) + (v >> 2) * a.P;
-  const bool first = v < 4;
+  const int col = c0 + (v & 1) + (v >> 1) * a.P;
+  const bool first = v < 2;
   if (row >= a.M || col >= a.N) return;
   switch (a.epi) {
     case DEC_STORE:
@@ -231,6 +232,18 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* X, const floa
   for (int k = threadIdx.x; k < K; k += 256) y[k] = x[k] * inv * g[k];
 }
 
+// Embedding rows: out[m] = E[tok[m * tok_stride]] (fp32 rows of K), one workgroup per row; ids
+// outside [0, V) give a zero row.
+__global__ void __launch_bounds__(256) embed_kernel(const float* E, int V, int K, const int32_t* tok,
+                                                    int64_t tok_stride, float* out) {
+  const int m = blockIdx.x;
+  const int t = tok[(int64_t)m * tok_stride];
+  float* o = out + (int64_t)m * K;
+  const bool ok = t >= 0 && t < V;
+  const float* e = E + (int64_t)(ok ? t : 0) * K;
+  for (int k = threadIdx.x; k < K; k += 256) o[k] = ok ? e[k] : 0.f;
+}
+
 }  // namespace
 
 hipError_t launch_dec_gemv(const DecGemv& d, hipStream_t s) {
@@ -259,21 +272,27 @@ hipError_t launch_dec_gemv(const DecGemv& d, hipStream_t s) {
   if (d.epi == DEC_ROPE) {  // heads of 128: columns c and c + 64
     a.P = 64;
     a.period = 128;
-    groups = (unsigned)(d.N / 8);
+    groups = (unsigned)(d.N / GV);
   } else if (d.epi == DEC_SWIGLU) {  // gate column c with up column c + N/2
     a.P = d.N / 2;
     a.period = d.N;
-    groups = (unsigned)(d.N / 8);
-  } else {  // plain: consecutive groups of 4, partner group right after
-    a.P = 4;
-    a.period = 8;
-    groups = (unsigned)((d.N + 7) / 8);
+    groups = (unsigned)(d.N / GV);
+  } else {  // plain: consecutive pairs, the partner pair right after
+    a.P = 2;
+    a.period = 4;
+    groups = (unsigned)((d.N + GV - 1) / GV);
   }
   const dim3 grid(groups, (unsigned)((d.M + GM - 1) / GM));
   if (d.w_bf16)
     hipLaunchKernelGGL(dec_gemv_kernel<true>, grid, dim3(GT), 0, s, a);
   else
     hipLaunchKernelGGL(dec_gemv_kernel<false>, grid, dim3(GT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const float* E, int V, int K, const int32_t* tok, int64_t tok_stride, int M,
+                        float* out, hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel, dim3((unsigned)M), dim3(256), 0, s, E, V, K, tok, tok_stride, out);
   return hipGetLastError();
 }
 

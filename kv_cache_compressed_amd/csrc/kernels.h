@@ -128,6 +128,8 @@ struct DecGemv {
 hipError_t launch_dec_gemv(const DecGemv& d, hipStream_t s);
 hipError_t launch_rmsnorm(const float* X, const float* g, float eps, int M, int K, float* Y,
                           hipStream_t s);
+hipError_t launch_embed(const float* E, int V, int K, const int32_t* tok, int64_t tok_stride, int M,
+                        float* out, hipStream_t s);
 
 // Keep-list selection (token-dropping drafter).
 hipError_t launch_select_keep(const float* scores, int64_t s_stride, int rows, int64_t n, int64_t lo,

@@ -803,9 +803,10 @@ class BatchedLlamaDecoder:
     libvc calls only, per layer the fused norm + q/k/v product + rotation (vc_decoder_gemv ROPE), one
     draft attention launch for the whole batch with each row's own lengths
     (vc_draft_attn_quant_rows), the output product into the residual, the fused norm + gate/up
-    product + SwiGLU and the down product into the residual, then the final norm and the head with
-    its greedy argmax: 23 launches for 4 layers (weights read as bf16 when they are bf16 values, the
-    same numbers in half the bytes). fused=False: the same step from PyTorch ops with one attention call per request. The
+    product + SwiGLU and the down product into the residual, then the head (final norm fused into
+    its product) and the greedy argmax: 24 launches for 4 layers (weights read as bf16 when they are
+    bf16 values, the same numbers in half the bytes); graphs=True replays the whole draft phase from
+    one captured graph (its kernels read lengths and positions from device memory). fused=False: the same step from PyTorch ops with one attention call per request. The
     verify step's layer work (B x (x + 1) rows) runs on PyTorch GEMMs either way; its attention is one
     call per request (each request's full cache is its own store). x = 0 gives plain greedy decoding
     of the batch (a verify of one row per request over the full caches)."""
@@ -813,7 +814,7 @@ class BatchedLlamaDecoder:
     def __init__(self, weights, Hq: int, Hkv: int, prompts, x: int, bits: int = 4, R: int = 32,
                  max_new: int = 256, kv_dtype: str = "f32", host_past: bool = False,
                  chunk_tokens: int = 65536, rope_theta: float = 500000.0, copy_stream=None,
-                 fused: bool = True, graphs: bool = True, device: str = "cuda"):
+                 fused: bool = True, graphs: bool = False, device: str = "cuda"):
         assert "g_att" in weights, "Llama-form weights"
         self.E, self.Wlm = _dev(weights["E"], device), _dev(weights["Wlm"], device)
         self.g_f = _dev(weights["g_f"], device)
@@ -867,7 +868,9 @@ class BatchedLlamaDecoder:
         self.vd = torch.zeros((B, Hkv, D), **tk)
         self.Xd = torch.zeros((B, self.dm), **f32)                 # fused step: residual stream
         self.Hd = torch.zeros((B, self.W13[0].shape[0] // 2), **f32)
-        self.Xn = torch.zeros((B, self.dm), **f32)
+        self.logits_d = torch.zeros((B, self.V), **f32)            # fused step: head logits
+        self.acc_d = torch.zeros((B,), **i32)
+        self.next_d = torch.zeros((B,), **i32)
         self.pos_d = torch.zeros((B,), **i32)                      # n_b (row positions = n_b + j)
         self.nq_d = torch.zeros((B,), dtype=torch.int64, device=device)  # n_q_b
         self.r0_d = torch.zeros((B,), **i32)                       # n_b - n_q_b (step j: + j + 1)
@@ -982,7 +985,7 @@ class BatchedLlamaDecoder:
         so the whole draft phase can be captured once and replayed."""
         Hq, Hkv, B = self.Hq, self.Hkv, self.B
         X = self.Xd
-        torch.index_select(self.E, 0, self.tok[:, j], out=X)
+        vc.vc_embed_rows(self.E, self.tok[:, j], X)
         ws = self.ws_draft.get(vc.vc_draft_quant_workspace(self.caches[0], nq_max, r_max, Hq))
         for l in range(self.nl):
             vc.vc_decoder_gemv(vc.VC_DEC_ROPE, self.Wqkv_b[l], X, norm_gain=self.g_att[l], q_out=self.qd,
@@ -993,9 +996,10 @@ class BatchedLlamaDecoder:
             vc.vc_decoder_gemv(vc.VC_DEC_ADD, self.Wo_b[l], self.od.view(B, -1), out=X)
             vc.vc_decoder_gemv(vc.VC_DEC_SWIGLU, self.W13_b[l], X, norm_gain=self.g_mlp[l], out=self.Hd)
             vc.vc_decoder_gemv(vc.VC_DEC_ADD, self.W2_b[l], self.Hd, out=X)
-        vc.vc_rmsnorm(X, self.g_f, self.Xn)
-        vc.vc_project_logits(self.Wlm_b, self.Xn.view(B, -1, D), argmax=self.tok.view(-1)[j + 1:],
-                             argmax_b_stride=self.L + 1, ws=self.ws_proj)
+        # head: final norm fused into the logits product, then each row's greedy argmax
+        vc.vc_decoder_gemv(vc.VC_DEC_STORE, self.Wlm_b, X, norm_gain=self.g_f, out=self.logits_d)
+        vc.vc_accept(self.logits_d.view(B, 1, -1), None, self.acc_d, self.next_d)
+        self.tok[:, j + 1].copy_(self.next_d)
 
     def _phase_bounds(self):
         """(n_q_max, r_max) the fused draft phase is launched with: the largest quantised prefix

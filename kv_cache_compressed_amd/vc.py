@@ -70,6 +70,7 @@ _SIGS = {
     "vc_decoder_gemv": [_I32, _P, _I32, _I32, _I32, _P, _I32, _P, _F, _P, _P, _P, _P, _I32, _I32, _I32,
                         _P, _P, _I32, _P, _I32, _P],
     "vc_rmsnorm": [_P, _P, _F, _I32, _I32, _P, _P],
+    "vc_embed_rows": [_P, _I32, _I32, _P, _I64, _I32, _P, _P],
     "vc_status_string": [_I32],
     "vc_last_error": [],
     "vc_abi_version": [],
@@ -397,3 +398,11 @@ def vc_rmsnorm(X, g, Y, eps: float = 1e-5, stream=None):
     """Y[m] = X[m] * g / sqrt(mean(X[m]^2) + eps); X, Y [M, K] fp32."""
     M, K = X.shape
     _check(lib().vc_rmsnorm(_ptr(X), _ptr(g), eps, M, K, _ptr(Y), _stream(stream)))
+
+
+def vc_embed_rows(E, tok, out, stream=None):
+    """out[m] = E[tok[m]] for a 1-D int32 device view `tok` (any stride); E [V, K] fp32."""
+    V, K = E.shape
+    assert tok.dim() == 1 and tok.dtype == torch.int32 and out.shape == (tok.shape[0], K)
+    _check(lib().vc_embed_rows(_ptr(E), V, K, _ptr(tok), tok.stride(0), tok.shape[0], _ptr(out),
+                               _stream(stream)))

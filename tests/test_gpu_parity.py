@@ -1314,3 +1314,16 @@ def test_decoder_gemv_epilogues(gpu_lib, M, wdt):
     Yn = torch.zeros_like(Xd)
     vc.vc_rmsnorm(Xd, gd, Yn)
     assert np.abs(Yn.cpu().numpy() - oloop.rms_norm(X, gain.astype(np.float64))).max() < 1e-5
+
+
+def test_embed_rows(gpu_lib):
+    """Embedding rows of one block entry of every request (a strided id view): rows of E, and an id
+    outside the vocabulary gives a zero row."""
+    g = np.random.default_rng(9)
+    E = g.standard_normal((50, 256)).astype(np.float32)
+    tok = torch.tensor([[3, 0, 1], [49, 7, 2], [-1, 5, 5], [50, 9, 9]], dtype=torch.int32, device="cuda")
+    out = torch.full((4, 256), float("nan"), device="cuda")
+    vc.vc_embed_rows(torch.from_numpy(E).cuda(), tok[:, 0], out)
+    torch.cuda.synchronize()
+    ref = np.stack([E[3], E[49], np.zeros(256, np.float32), np.zeros(256, np.float32)])
+    assert np.array_equal(out.cpu().numpy(), ref)
