@@ -370,6 +370,7 @@ def _e2e_llama_batch(torch, W, prompts, tokens: int, bits: int, x: int, opts: di
         emitted = sum(sum(a + 1 for a in r[r0:]) for r in dec.rounds)
         out[name] = {"tok_s": round(emitted / el, 2), "emitted": emitted,
                      "rounds": len(dec.rounds[0]) - r0, "prefill_s": round(t_prefill, 2)}
+        print(f"# e2e_llama batch {name}: {out[name]}", file=sys.stderr, flush=True)
         if xx:
             out[name]["mean_accepted"] = round(float(np.mean([a for r in dec.rounds for a in r[r0:]])), 2)
         seqs[name] = [w + g for w, g in zip(warm, gen)]
@@ -404,6 +405,7 @@ def _e2e_llama_batch(torch, W, prompts, tokens: int, bits: int, x: int, opts: di
         emitted = sum(len(em) for ga in acc for ems in ga for em in ems)
         two[name] = {"tok_s": round(emitted / el, 2), "emitted": emitted,
                      "ms_per_round": round(el / rounds * 1e3, 2)}
+        print(f"# e2e_llama two groups {name}: {two[name]}", file=sys.stderr, flush=True)
         del groups, g0, g1
     two["speedup"] = round(two["staggered"]["tok_s"] / two["lockstep"]["tok_s"], 3)
     out["two_groups"] = two
