@@ -369,7 +369,16 @@ vc_status vc_select_keep(const float *scores, int64_t score_row_stride, int32_t 
  *                           k_out/v_out [M][Hkv][128] in out_dtype (VC_F32, or VC_BF16 rounded to
  *                           nearest even)
  *            VC_DEC_SWIGLU  Y = [gate | up] (N = 2F, N % 8 == 0): out [M][F] = silu(gate) * up
- *   Unused pointers may be NULL. Weight-streaming: each weight is read once per 8 rows.
+ *   Unused pointers may be NULL.
+ *   ws: NULL selects the vector form (each weight read once per 16 rows; X re-read per 4 columns).
+ *   Otherwise, for bf16 weights with K % 32 == 0 (and for VC_DEC_SWIGLU N % 128 == 0), the
+ *   matrix-core form runs: X (times the gain) split exactly into three bf16 pieces, bf16 products
+ *   (exact) summed in fp32, K cut into slices whose partial tiles are added in slice order by the
+ *   last slice to finish (deterministic). ws then holds >= vc_decoder_gemv_workspace() bytes of
+ *   device memory, zero-filled before its first use; every completed call leaves its tickets at
+ *   zero again. Calls that share a workspace must not overlap (same stream, or ordered). Where the
+ *   matrix-core form does not apply, ws is ignored. VC_ERR_INVALID if ws_bytes is too small.
+ * vc_decoder_gemv_workspace: that size (0 where the matrix-core form does not apply), host only.
  * vc_rmsnorm: Y[m] = X[m] * g / sqrt(mean(X[m]^2) + eps), X, Y [M][K] fp32 (may alias).
  * vc_embed_rows: out[m] = E[tok[m * tok_stride]] for m < M, E [V][K] fp32, tok int32 (device, any
  *   stride, e.g. one block entry of every request); an id outside [0, V) gives a zero row.
@@ -379,7 +388,10 @@ vc_status vc_decoder_gemv(int32_t epilogue, const void *W, int32_t w_dtype, int3
                           const float *X, int32_t M, const float *norm_gain, float eps, float *out,
                           void *q_out, void *k_out, void *v_out, int32_t out_dtype, int32_t Hq,
                           int32_t Hkv, const float *cos_t, const float *sin_t, int32_t n_pos,
-                          const int32_t *pos, int32_t pos_add, void *stream);
+                          const int32_t *pos, int32_t pos_add, void *ws, size_t ws_bytes,
+                          void *stream);
+vc_status vc_decoder_gemv_workspace(int32_t epilogue, int32_t w_dtype, int32_t N, int32_t K, int32_t M,
+                                    size_t *bytes);
 vc_status vc_rmsnorm(const float *X, const float *g, float eps, int32_t M, int32_t K, float *Y,
                      void *stream);
 vc_status vc_embed_rows(const float *E, int32_t V, int32_t K, const int32_t *tok, int64_t tok_stride,
@@ -393,11 +405,12 @@ vc_status vc_embed_rows(const float *E, int32_t V, int32_t K, const int32_t *tok
  *   VC_OP_VERIFY       dims {B, Hq, Hkv, L, n, past_on_host, chunk_tokens, dtype}  (vc_verify_attn,
  *                      vc_verify_prefetch, vc_verify_stream_copies)
  *   VC_OP_PROJECT      dims {B, L, V}                                        (vc_project_logits)
+ *   VC_OP_DECODER      dims {epilogue, w_dtype, N, K, M}                     (vc_decoder_gemv)
  * A wrong count of dims or an unknown op returns VC_ERR_INVALID. The pages give the calls of the
  * path, not their memory; the caller owns every workspace ("VeriCache: Turning Lossy KV Cache into
  * Lossless LLM Inference", Key Contributions: one interface for every compressor).
  */
-enum { VC_OP_DRAFT_QUANT = 1, VC_OP_DRAFT_DROP = 2, VC_OP_VERIFY = 3, VC_OP_PROJECT = 4 };
+enum { VC_OP_DRAFT_QUANT = 1, VC_OP_DRAFT_DROP = 2, VC_OP_VERIFY = 3, VC_OP_PROJECT = 4, VC_OP_DECODER = 5 };
 vc_status vc_workspace_bytes(int32_t op, const int64_t *dims, int32_t ndims, size_t *bytes);
 
 const char *vc_status_string(vc_status s);

@@ -507,7 +507,8 @@ vc_status vc_decoder_gemv(int32_t epilogue, const void* W, int32_t w_dtype, int3
                           const float* X, int32_t M, const float* norm_gain, float eps, float* out,
                           void* q_out, void* k_out, void* v_out, int32_t out_dtype, int32_t Hq,
                           int32_t Hkv, const float* cos_t, const float* sin_t, int32_t n_pos,
-                          const int32_t* pos, int32_t pos_add, void* stream) {
+                          const int32_t* pos, int32_t pos_add, void* ws, size_t ws_bytes,
+                          void* stream) {
   REQUIRE(epilogue == VC_DEC_STORE || epilogue == VC_DEC_ADD || epilogue == VC_DEC_ROPE ||
               epilogue == VC_DEC_SWIGLU,
           "unknown epilogue %d", epilogue);
@@ -558,8 +559,28 @@ vc_status vc_decoder_gemv(int32_t epilogue, const void* W, int32_t w_dtype, int3
   d.n_pos = n_pos;
   d.pos = pos;
   d.pos_add = pos_add;
+  if (ws) {
+    const vc::DecPlan p = vc::plan_dec_gemv(epilogue, d.w_bf16, N, K, M);
+    REQUIRE_PTR(ws);
+    REQUIRE(!p.mfma || ws_bytes >= p.ws_bytes, "ws_bytes %zu < vc_decoder_gemv_workspace() = %zu",
+            ws_bytes, p.ws_bytes);
+    d.ws = p.mfma ? ws : nullptr;
+  }
   hipError_t e = vc::launch_dec_gemv(d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "vc_decoder_gemv launch");
+  return ok();
+}
+
+vc_status vc_decoder_gemv_workspace(int32_t epilogue, int32_t w_dtype, int32_t N, int32_t K, int32_t M,
+                                    size_t* bytes) {
+  REQUIRE(bytes != nullptr, "bytes is null");
+  REQUIRE(epilogue == VC_DEC_STORE || epilogue == VC_DEC_ADD || epilogue == VC_DEC_ROPE ||
+              epilogue == VC_DEC_SWIGLU,
+          "unknown epilogue %d", epilogue);
+  REQUIRE(w_dtype == VC_F32 || w_dtype == VC_BF16, "w_dtype must be VC_F32 or VC_BF16");
+  REQUIRE(M >= 1 && M <= 4096 && K >= 4 && K % 4 == 0 && N >= 1, "M in [1, 4096], K a positive multiple of 4, N >= 1");
+  const vc::DecPlan p = vc::plan_dec_gemv(epilogue, w_dtype == VC_BF16, N, K, M);
+  *bytes = p.mfma ? p.ws_bytes : 0;
   return ok();
 }
 
@@ -627,6 +648,11 @@ vc_status vc_workspace_bytes(int32_t op, const int64_t* dims, int32_t ndims, siz
       REQUIRE(need(3), "VC_OP_PROJECT takes 3 dims {B, L, V} (got %d)", ndims);
       REQUIRE(fits32(3), "B, L and V must fit int32");
       return vc_project_workspace((int32_t)dims[0], (int32_t)dims[1], (int32_t)dims[2], bytes);
+    case VC_OP_DECODER:  // {epilogue, w_dtype, N, K, M}
+      REQUIRE(need(5), "VC_OP_DECODER takes 5 dims {epilogue, w_dtype, N, K, M} (got %d)", ndims);
+      REQUIRE(fits32(5), "epilogue, w_dtype, N, K and M must fit int32");
+      return vc_decoder_gemv_workspace((int32_t)dims[0], (int32_t)dims[1], (int32_t)dims[2],
+                                       (int32_t)dims[3], (int32_t)dims[4], bytes);
     default:
       return fail(VC_ERR_INVALID, "unknown op %d", op);
   }

@@ -124,7 +124,16 @@ struct DecGemv {
   int n_pos;
   const int32_t* pos;
   int pos_add;
+  void* ws;  // null: the vector form; else the matrix-core form's workspace (when it applies)
 };
+// The matrix-core form of a product: whether it applies (bf16 weights, K % 32 == 0, paired blocks
+// of 64 columns), its split of K and the workspace it needs (tickets + slice partials).
+struct DecPlan {
+  bool mfma;
+  int groups, row_tiles, S;
+  size_t ws_bytes;
+};
+DecPlan plan_dec_gemv(int epi, int w_bf16, int N, int K, int M);
 hipError_t launch_dec_gemv(const DecGemv& d, hipStream_t s);
 hipError_t launch_rmsnorm(const float* X, const float* g, float eps, int M, int K, float* Y,
                           hipStream_t s);

@@ -808,8 +808,14 @@ class BatchedLlamaDecoder:
     bf16 values, the same numbers in half the bytes); graphs=True replays the whole draft phase from
     one captured graph (its kernels read lengths and positions from device memory). fused=False: the same step from PyTorch ops with one attention call per request. The
     verify step's layer work (B x (x + 1) rows) runs on PyTorch GEMMs either way; its attention is one
-    call per request (each request's full cache is its own store). x = 0 gives plain greedy decoding
-    of the batch (a verify of one row per request over the full caches)."""
+    call per request (each request's full cache is its own store). With the full caches in host
+    memory the verify's calls stream through a ring of VRING workspaces: each call's copies are
+    issued VRING - 1 calls ahead (vc_verify_prefetch), and the first VRING calls' copies at the start
+    of the round, under the draft steps (a round's committed past is known before its drafts), so
+    the host link does not wait for any call's compute. x = 0 gives plain greedy decoding of the
+    batch (a verify of one row per request over the full caches)."""
+
+    VRING = 4
 
     def __init__(self, weights, Hq: int, Hkv: int, prompts, x: int, bits: int = 4, R: int = 32,
                  max_new: int = 256, kv_dtype: str = "f32", host_past: bool = False,
@@ -851,6 +857,13 @@ class BatchedLlamaDecoder:
             bf = (lambda w: w.to(torch.bfloat16).contiguous()) if exact else (lambda w: w)
             self.Wqkv_b, self.Wo_b = [bf(w) for w in self.Wqkv], [bf(w) for w in self.Wo]
             self.W13_b, self.W2_b, self.Wlm_b = [bf(w) for w in self.W13], [bf(w) for w in self.W2], bf(self.Wlm)
+            # one workspace for the step's products (they run in order on one stream): the
+            # matrix-core form where the weights are bf16, zero-filled once
+            need = [vc.vc_decoder_gemv_workspace(e, vc.dtype_code(w), w.shape[0], w.shape[1], B)
+                    for e, w in ((vc.VC_DEC_ROPE, self.Wqkv_b[0]), (vc.VC_DEC_ADD, self.Wo_b[0]),
+                                 (vc.VC_DEC_SWIGLU, self.W13_b[0]), (vc.VC_DEC_ADD, self.W2_b[0]),
+                                 (vc.VC_DEC_STORE, self.Wlm_b))]
+            self.ws_dec = torch.zeros(max(need), dtype=torch.uint8, device=device) if max(need) else None
         f32 = dict(dtype=torch.float32, device=device)
         tk = dict(dtype=self.tdt, device=device)
         i32 = dict(dtype=torch.int32, device=device)
@@ -889,6 +902,8 @@ class BatchedLlamaDecoder:
         self.argmax_v = torch.zeros((B, L), **i32)
         self.ws_draft = vc.Workspace(device)
         self.ws_verify = vc.Workspace(device)
+        self.vring = [vc.Workspace(device) for _ in range(self.VRING)] if host_past else []
+        self._pf, self._pf_open = 0, False  # verify calls whose copies are issued this round
         self.ws_proj = torch.zeros((vc.vc_project_workspace(B, 1, self.V) + 3) // 4, **i32)
         for b, p in enumerate(prompts):
             self._prefill(b, p)
@@ -917,11 +932,31 @@ class BatchedLlamaDecoder:
         F = Z.shape[-1] // 2
         return X + (torch.nn.functional.silu(Z[:, :F]) * Z[:, F:]) @ self.W2[l].T
 
+    def _prefetch(self, upto: int):
+        """Issue the copies of this round's verify calls self._pf .. upto - 1 (call l B + b: layer
+        l, request b), each into its ring workspace, after the compute work enqueued so far (which
+        holds the last call that used that workspace)."""
+        while self._pf < min(upto, self.nl * self.B):
+            i = self._pf
+            l, b = divmod(i, self.B)
+            n, st = self.n[b], self.stores[b][l]
+            nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, n, True, self.chunk, self.vdt)
+            vc.vc_verify_prefetch(st.k, st.v, n, self.vring[i % self.VRING].get(nb), 1, self.Hq, self.Hkv,
+                                  self.L, self.chunk, past_stride=self.cap, copy_stream=self.copy_stream)
+            self._pf += 1
+
     def _verify(self, b: int, l: int, q, k, v, n: int, out, lse):
         host = self.host and n > 0
         nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, q.shape[2], n, host, self.chunk, self.vdt)
         st = self.stores[b][l]
         kp, vp, stride = (st.k, st.v, self.cap) if n > 0 else (k, v, q.shape[2])
+        if host and q.shape[2] == self.L:  # a round's verify: through the prefetch ring
+            i = l * self.B + b
+            self._prefetch(i + self.VRING)
+            vc.vc_verify_attn(q, k, v, kp, vp, n, out, lse, self.vring[i % self.VRING].get(nb), SM_SCALE,
+                              past_stride=stride, past_on_host=vc.VC_PAST_HOST_PREFETCHED,
+                              chunk_tokens=self.chunk, copy_stream=self.copy_stream)
+            return
         vc.vc_verify_attn(q, k, v, kp, vp, n, out, lse, self.ws_verify.get(nb), SM_SCALE,
                           past_stride=stride, past_on_host=host, chunk_tokens=self.chunk,
                           copy_stream=self.copy_stream)
@@ -990,14 +1025,16 @@ class BatchedLlamaDecoder:
         for l in range(self.nl):
             vc.vc_decoder_gemv(vc.VC_DEC_ROPE, self.Wqkv_b[l], X, norm_gain=self.g_att[l], q_out=self.qd,
                                k_out=self.kd, v_out=self.vd, Hq=Hq, Hkv=Hkv, cos_t=self.cos,
-                               sin_t=self.sin, pos=self.pos_d, pos_add=j)
+                               sin_t=self.sin, pos=self.pos_d, pos_add=j, ws=self.ws_dec)
             vc.vc_draft_attn_quant_rows(self.caches[l], self.nq_d, self.r0_d, j + 1, nq_max, r_max, self.qd,
                                         self.od, self.lse_d, ws, SM_SCALE, k_new=self.kd, v_new=self.vd)
-            vc.vc_decoder_gemv(vc.VC_DEC_ADD, self.Wo_b[l], self.od.view(B, -1), out=X)
-            vc.vc_decoder_gemv(vc.VC_DEC_SWIGLU, self.W13_b[l], X, norm_gain=self.g_mlp[l], out=self.Hd)
-            vc.vc_decoder_gemv(vc.VC_DEC_ADD, self.W2_b[l], self.Hd, out=X)
+            vc.vc_decoder_gemv(vc.VC_DEC_ADD, self.Wo_b[l], self.od.view(B, -1), out=X, ws=self.ws_dec)
+            vc.vc_decoder_gemv(vc.VC_DEC_SWIGLU, self.W13_b[l], X, norm_gain=self.g_mlp[l], out=self.Hd,
+                               ws=self.ws_dec)
+            vc.vc_decoder_gemv(vc.VC_DEC_ADD, self.W2_b[l], self.Hd, out=X, ws=self.ws_dec)
         # head: final norm fused into the logits product, then each row's greedy argmax
-        vc.vc_decoder_gemv(vc.VC_DEC_STORE, self.Wlm_b, X, norm_gain=self.g_f, out=self.logits_d)
+        vc.vc_decoder_gemv(vc.VC_DEC_STORE, self.Wlm_b, X, norm_gain=self.g_f, out=self.logits_d,
+                           ws=self.ws_dec)
         vc.vc_accept(self.logits_d.view(B, 1, -1), None, self.acc_d, self.next_d)
         self.tok[:, j + 1].copy_(self.next_d)
 
@@ -1010,6 +1047,9 @@ class BatchedLlamaDecoder:
 
     def verify_step(self):
         Hq, Hkv, B, L = self.Hq, self.Hkv, self.B, self.L
+        if not self._pf_open:  # no draft phase issued this round's first copies
+            self._pf = 0
+        self._pf_open = False
         pos = (torch.tensor(self.n, device=self.device)[:, None]
                + torch.arange(L, device=self.device)).view(-1)
         X = self.E[self.tok[:, :L].reshape(-1).long()]
@@ -1064,8 +1104,10 @@ class BatchedLlamaDecoder:
 
     def warm(self):
         """Size the workspaces for the largest context this decoder can reach."""
-        self.ws_verify.get(vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, self.cap, self.host,
-                                                  self.chunk, self.vdt))
+        nb = vc.vc_verify_workspace(1, self.Hq, self.Hkv, self.L, self.cap, self.host, self.chunk, self.vdt)
+        self.ws_verify.get(nb)
+        for w in self.vring:
+            w.get(nb)
         r = self.R + 32 + self.L
         self.ws_draft.get(vc.vc_draft_quant_workspace(self.caches[0], (self.cap - r) // 32 * 32, r,
                                                       self.Hq))
@@ -1074,7 +1116,11 @@ class BatchedLlamaDecoder:
     def draft_phase(self):
         """The x draft steps. Fused: replayed from a HIP graph of the whole phase, captured on first
         use and again whenever the launch bounds change (every kernel of the phase reads the
-        requests' lengths and positions from device memory, so one capture serves many rounds)."""
+        requests' lengths and positions from device memory, so one capture serves many rounds).
+        With host-resident full caches the round's first verify copies are issued first."""
+        if self.host:
+            self._pf, self._pf_open = 0, True
+            self._prefetch(self.VRING)
         if not (self.fused and self.graphs) or self.x == 0:
             for j in range(self.x):
                 self.draft_step(j)

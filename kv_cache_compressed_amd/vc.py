@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "vc.h")
 VC_OK, VC_ERR_INVALID, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_HIP = 0, 1, 2, 3, 4
 VC_F32, VC_F16, VC_BF16 = 0, 1, 2
 VC_PAST_DEVICE, VC_PAST_HOST, VC_PAST_HOST_PREFETCHED = 0, 1, 2
-VC_OP_DRAFT_QUANT, VC_OP_DRAFT_DROP, VC_OP_VERIFY, VC_OP_PROJECT = 1, 2, 3, 4
+VC_OP_DRAFT_QUANT, VC_OP_DRAFT_DROP, VC_OP_VERIFY, VC_OP_PROJECT, VC_OP_DECODER = 1, 2, 3, 4, 5
 VC_DEC_STORE, VC_DEC_ADD, VC_DEC_ROPE, VC_DEC_SWIGLU = 0, 1, 2, 3
 _TORCH_DT = {torch.float32: VC_F32, torch.float16: VC_F16, torch.bfloat16: VC_BF16}
 
@@ -68,7 +68,8 @@ _SIGS = {
     "vc_verify_stream_copies": [_P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P],
     "vc_workspace_bytes": [_I32, ctypes.POINTER(_I64), _I32, ctypes.POINTER(_SZ)],
     "vc_decoder_gemv": [_I32, _P, _I32, _I32, _I32, _P, _I32, _P, _F, _P, _P, _P, _P, _I32, _I32, _I32,
-                        _P, _P, _I32, _P, _I32, _P],
+                        _P, _P, _I32, _P, _I32, _P, _SZ, _P],
+    "vc_decoder_gemv_workspace": [_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
     "vc_rmsnorm": [_P, _P, _F, _I32, _I32, _P, _P],
     "vc_embed_rows": [_P, _I32, _I32, _P, _I64, _I32, _P, _P],
     "vc_status_string": [_I32],
@@ -382,8 +383,10 @@ def vc_select_keep(scores, n: int, sinks: int, recent: int, keep: int, idx, stre
 
 def vc_decoder_gemv(epilogue: int, W, X, out=None, norm_gain=None, eps: float = 1e-5, q_out=None,
                     k_out=None, v_out=None, Hq: int = 0, Hkv: int = 0, cos_t=None, sin_t=None,
-                    pos=None, pos_add: int = 0, stream=None):
-    """W [N, K] fp32/bf16; X [M, K] fp32 (contiguous rows); see include/vc.h for the epilogues."""
+                    pos=None, pos_add: int = 0, ws=None, stream=None):
+    """W [N, K] fp32/bf16; X [M, K] fp32 (contiguous rows); see include/vc.h for the epilogues.
+    ws: None (vector form) or a zero-filled uint8 device buffer of vc_decoder_gemv_workspace()
+    bytes (matrix-core form where it applies)."""
     N, K = W.shape
     M = X.shape[0]
     assert X.is_contiguous() and X.shape[1] == K and W.is_contiguous()
@@ -391,7 +394,15 @@ def vc_decoder_gemv(epilogue: int, W, X, out=None, norm_gain=None, eps: float = 
     n_pos = cos_t.shape[0] if cos_t is not None else 0
     _check(lib().vc_decoder_gemv(epilogue, _ptr(W), dtype_code(W), N, K, _ptr(X), M, _ptr(norm_gain), eps,
                                  _ptr(out), _ptr(q_out), _ptr(k_out), _ptr(v_out), odt, Hq, Hkv,
-                                 _ptr(cos_t), _ptr(sin_t), n_pos, _ptr(pos), pos_add, _stream(stream)))
+                                 _ptr(cos_t), _ptr(sin_t), n_pos, _ptr(pos), pos_add, _ptr(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def vc_decoder_gemv_workspace(epilogue: int, w_dtype: int, N: int, K: int, M: int) -> int:
+    """Bytes of the matrix-core form's workspace (0 where it does not apply)."""
+    n = _SZ(0)
+    _check(lib().vc_decoder_gemv_workspace(epilogue, w_dtype, N, K, M, ctypes.byref(n)))
+    return n.value
 
 
 def vc_rmsnorm(X, g, Y, eps: float = 1e-5, stream=None):

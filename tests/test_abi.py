@@ -256,6 +256,28 @@ def test_generic_workspace_query_matches_the_per_op_queries(L):
     assert L.vc_workspace_bytes(vc.VC_OP_DRAFT_QUANT, bad, 4, ctypes.byref(one)) == vc.VC_ERR_INVALID
 
 
+def test_decoder_workspace_query(L):
+    """The matrix-core form's workspace: none where it does not apply (fp32 weights, K not a multiple
+    of 32, gate/up halves not in blocks of 64), tickets only when K is not cut (K < 256), tickets
+    plus one 128 x 16 tile (+ 16 sums of squares) per slice otherwise; the generic query agrees."""
+    q = lambda *d: vc.vc_decoder_gemv_workspace(*d)
+    assert q(vc.VC_DEC_STORE, vc.VC_F32, 32000, 2048, 16) == 0
+    assert q(vc.VC_DEC_STORE, vc.VC_BF16, 32000, 2044, 16) == 0
+    assert q(vc.VC_DEC_SWIGLU, vc.VC_BF16, 2 * 1000, 2048, 16) == 0
+    assert q(vc.VC_DEC_STORE, vc.VC_BF16, 200, 160, 16) == 256
+    # q/k/v of 16 + 2 x 4 heads, K 2048, 16 rows: 24 column groups, 8 slices of 256
+    assert q(vc.VC_DEC_ROPE, vc.VC_BF16, 3072, 2048, 16) == 256 + 24 * 8 * (128 * 16 + 16) * 4
+    # three row tiles: tickets and tiles per row tile
+    assert q(vc.VC_DEC_ADD, vc.VC_BF16, 512, 512, 33) == 256 + 3 * 4 * 2 * (128 * 16 + 16) * 4
+    for d in ([vc.VC_DEC_ROPE, vc.VC_BF16, 3072, 2048, 16], [vc.VC_DEC_SWIGLU, vc.VC_BF16, 11264, 2048, 16],
+              [vc.VC_DEC_STORE, vc.VC_F32, 77, 2560, 5]):
+        assert vc.vc_workspace_bytes(vc.VC_OP_DECODER, d) == q(*d)
+    one = ctypes.c_size_t()
+    assert L.vc_decoder_gemv_workspace(9, vc.VC_BF16, 64, 64, 1, ctypes.byref(one)) == vc.VC_ERR_INVALID
+    assert L.vc_decoder_gemv_workspace(0, vc.VC_BF16, 64, 66, 1, ctypes.byref(one)) == vc.VC_ERR_INVALID
+    assert L.vc_decoder_gemv_workspace(0, vc.VC_BF16, 64, 64, 0, ctypes.byref(one)) == vc.VC_ERR_INVALID
+
+
 def test_stream_copies_rejects(L):
     """Argument checks of the copy-only transfer (all before any HIP call)."""
     call = lambda **a: L.vc_verify_stream_copies(

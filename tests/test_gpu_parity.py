@@ -1240,15 +1240,26 @@ def test_draft_quant_rows_mixed_lengths(gpu_lib):
         assert np.abs(ob[0].cpu().numpy() - o[b]).max() <= 2 * TIGHT["draft_quant"] * scale, f"row {b}"
 
 
-@pytest.mark.parametrize("M,wdt", [(1, "bf16"), (16, "bf16"), (13, "f32"), (33, "bf16")])
-def test_decoder_gemv_epilogues(gpu_lib, M, wdt):
+@pytest.mark.parametrize("M,wdt,form", [(1, "bf16", "vector"), (16, "bf16", "vector"), (13, "f32", "vector"),
+                                         (33, "bf16", "vector"), (1, "bf16", "matrix"), (16, "bf16", "matrix"),
+                                         (7, "bf16", "matrix"), (33, "bf16", "matrix")])
+def test_decoder_gemv_epilogues(gpu_lib, M, wdt, form):
     """The fused few-row layer products against the oracle's Llama layer pieces (RMS norm, rotary
     embedding, SiLU, in float64): norm + q/k/v + rotation at per-row positions (bf16 and fp32
     outputs), the output product added into a residual, norm + gate/up + SwiGLU, and a plain
-    product; ragged row counts and a K that is not a multiple of the 2048-wide chunk."""
+    product; ragged row counts and a K that is not a multiple of the 2048-wide chunk. Both forms:
+    the vector one (no workspace) and the matrix-core one (K cut into slices, a ragged last column
+    group, several row tiles at M = 33)."""
     from oracle import loop as oloop
 
-    g = np.random.default_rng(M * 7 + (wdt == "bf16"))
+    def ws_for(epi, W, M_):
+        if form == "vector":
+            return None
+        nb = vc.vc_decoder_gemv_workspace(epi, vc.dtype_code(W), W.shape[0], W.shape[1], M_)
+        assert nb > 0
+        return torch.zeros(nb, dtype=torch.uint8, device="cuda")
+
+    g = np.random.default_rng(M * 7 + (wdt == "bf16") + 100 * (form == "matrix"))
     dm, Hq, Hkv, F, cap = 512, 4, 2, 1280, 300
     tw = torch.bfloat16 if wdt == "bf16" else torch.float32
     Wr = lambda n, k: torch.from_numpy((0.05 * g.standard_normal((n, k))).astype(np.float32)).to(tw)
@@ -1274,7 +1285,8 @@ def test_decoder_gemv_epilogues(gpu_lib, M, wdt):
         k = torch.full((M, Hkv, 128), float("nan"), dtype=odt, device="cuda")
         v = torch.full((M, Hkv, 128), float("nan"), dtype=odt, device="cuda")
         vc.vc_decoder_gemv(vc.VC_DEC_ROPE, Wqkv.cuda(), Xd, norm_gain=gd, q_out=q, k_out=k, v_out=v, Hq=Hq,
-                           Hkv=Hkv, cos_t=dev(cos_t), sin_t=dev(sin_t), pos=dev(pos), pos_add=3)
+                           Hkv=Hkv, cos_t=dev(cos_t), sin_t=dev(sin_t), pos=dev(pos), pos_add=3,
+                           ws=ws_for(vc.VC_DEC_ROPE, Wqkv, M))
         torch.cuda.synchronize()
         tol = 2e-5 if odt == torch.float32 else 1e-2
         for got, ref, name in ((q, ref_q, "q"), (k, ref_k, "k"), (v, ref_v, "v")):
@@ -1285,14 +1297,15 @@ def test_decoder_gemv_epilogues(gpu_lib, M, wdt):
             q32 = torch.zeros((M, Hq, 128), device="cuda")
             vc.vc_decoder_gemv(vc.VC_DEC_ROPE, Wqkv.cuda(), Xd, norm_gain=gd, q_out=q32, k_out=torch.zeros_like(k, dtype=torch.float32),
                                v_out=torch.zeros_like(v, dtype=torch.float32), Hq=Hq, Hkv=Hkv,
-                               cos_t=dev(cos_t), sin_t=dev(sin_t), pos=dev(pos), pos_add=3)
+                               cos_t=dev(cos_t), sin_t=dev(sin_t), pos=dev(pos), pos_add=3,
+                               ws=ws_for(vc.VC_DEC_ROPE, Wqkv, M))
             assert torch.equal(q32.to(torch.bfloat16), q)
     # output product added into the residual
     O = g.standard_normal((M, Hq * 128)).astype(np.float32)
     Wo = Wr(dm, Hq * 128)
     R = g.standard_normal((M, dm)).astype(np.float32)
     Rd = dev(R)
-    vc.vc_decoder_gemv(vc.VC_DEC_ADD, Wo.cuda(), dev(O), out=Rd)
+    vc.vc_decoder_gemv(vc.VC_DEC_ADD, Wo.cuda(), dev(O), out=Rd, ws=ws_for(vc.VC_DEC_ADD, Wo, M))
     ref = R.astype(np.float64) + O.astype(np.float64) @ W64(Wo).T
     assert np.abs(Rd.cpu().numpy() - ref).max() <= 2e-5 * max(1.0, np.abs(ref).max())
     # norm + gate/up + SwiGLU
@@ -1301,15 +1314,34 @@ def test_decoder_gemv_epilogues(gpu_lib, M, wdt):
     Z = Hn @ W64(W13).T
     ref = oloop.silu(Z[:, :F]) * Z[:, F:]
     Hd = torch.full((M, F), float("nan"), device="cuda")
-    vc.vc_decoder_gemv(vc.VC_DEC_SWIGLU, W13.cuda(), Xd, norm_gain=gd, out=Hd)
+    vc.vc_decoder_gemv(vc.VC_DEC_SWIGLU, W13.cuda(), Xd, norm_gain=gd, out=Hd,
+                       ws=ws_for(vc.VC_DEC_SWIGLU, W13, M))
     assert np.abs(Hd.cpu().numpy() - ref).max() <= 2e-5 * max(1.0, np.abs(ref).max())
     # plain product with K = 2560 (a chunk and a ragged one), N not a multiple of 8
     W2 = Wr(77, 2560)
     Xk = g.standard_normal((M, 2560)).astype(np.float32)
     Y = torch.full((M, 77), float("nan"), device="cuda")
-    vc.vc_decoder_gemv(vc.VC_DEC_STORE, W2.cuda(), dev(Xk), out=Y)
+    ws2 = ws_for(vc.VC_DEC_STORE, W2, M)
+    vc.vc_decoder_gemv(vc.VC_DEC_STORE, W2.cuda(), dev(Xk), out=Y, ws=ws2)
     ref = Xk.astype(np.float64) @ W64(W2).T
     assert np.abs(Y.cpu().numpy() - ref).max() <= 2e-5 * max(1.0, np.abs(ref).max())
+    if ws2 is not None:  # the tickets are back at zero: a second call with the same workspace agrees
+        Y2 = torch.full((M, 77), float("nan"), device="cuda")
+        vc.vc_decoder_gemv(vc.VC_DEC_STORE, W2.cuda(), dev(Xk), out=Y2, ws=ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y2)
+        assert not ws2[:256].any()
+        with pytest.raises(vc.VcError, match="ws_bytes"):  # a workspace too small is refused
+            vc.vc_decoder_gemv(vc.VC_DEC_STORE, W2.cuda(), dev(Xk), out=Y2, ws=ws2[:64])
+        # K below one slice's minimum (one slice, no partials), with the norm
+        W3 = Wr(200, 160)
+        Xs = g.standard_normal((M, 160)).astype(np.float32)
+        g3 = (1 + 0.1 * g.standard_normal(160)).astype(np.float32)
+        Y3 = torch.full((M, 200), float("nan"), device="cuda")
+        vc.vc_decoder_gemv(vc.VC_DEC_STORE, W3.cuda(), dev(Xs), norm_gain=dev(g3), out=Y3,
+                           ws=ws_for(vc.VC_DEC_STORE, W3, M))
+        ref = oloop.rms_norm(Xs, g3.astype(np.float64)) @ W64(W3).T
+        assert np.abs(Y3.cpu().numpy() - ref).max() <= 2e-5 * max(1.0, np.abs(ref).max())
     # the plain norm
     Yn = torch.zeros_like(Xd)
     vc.vc_rmsnorm(Xd, gd, Yn)
