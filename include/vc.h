@@ -375,9 +375,11 @@ vc_status vc_select_keep(const float *scores, int64_t score_row_stride, int32_t 
  *   matrix-core form runs: X (times the gain) split exactly into three bf16 pieces, bf16 products
  *   (exact) summed in fp32, K cut into slices whose partial tiles are added in slice order by the
  *   last slice to finish (deterministic). ws then holds >= vc_decoder_gemv_workspace() bytes of
- *   device memory, zero-filled before its first use; every completed call leaves its tickets at
- *   zero again. Calls that share a workspace must not overlap (same stream, or ordered). Where the
- *   matrix-core form does not apply, ws is ignored. VC_ERR_INVALID if ws_bytes is too small.
+ *   device memory, zero-filled before its first use; its layout (16 KB of tickets, then the slice
+ *   partials) is the same for every shape, and every completed call leaves its tickets at zero
+ *   again, so one workspace sized for the largest of several products serves them all. Calls that
+ *   share a workspace must not overlap (same stream, or ordered). Where the matrix-core form does
+ *   not apply, ws is ignored. VC_ERR_INVALID if ws_bytes is too small.
  * vc_decoder_gemv_workspace: that size (0 where the matrix-core form does not apply), host only.
  * vc_rmsnorm: Y[m] = X[m] * g / sqrt(mean(X[m]^2) + eps), X, Y [M][K] fp32 (may alias).
  * vc_embed_rows: out[m] = E[tok[m * tok_stride]] for m < M, E [V][K] fp32, tok int32 (device, any

@@ -259,6 +259,10 @@ constexpr int MTILE = MC * 16;     // one slice's partial tile (floats)
 constexpr int MSLOT = MTILE + 16;  // + the rows' sums of squares
 constexpr int MTARGET = 512;       // workgroups a launch aims for (2 resident per CU)
 constexpr int MSMAX = 32;          // most slices
+// Workspace layout, the same for every shape so that products of different shapes can share one
+// workspace: MUNITS ticket counters (zero between calls), then the slice partials.
+constexpr int MUNITS = 4096;       // most column groups x row tiles
+constexpr size_t MPART_OFF = (size_t)MUNITS * 4;
 
 // First column of column group w (two blocks of 64 columns, P apart).
 __device__ __forceinline__ int first_col_m(const GArgs& a, int w) {
@@ -461,8 +465,11 @@ DecPlan plan_dec_gemv(int epi, int w_bf16, int N, int K, int M) {
     p.mfma = false;
     return p;
   }
-  const size_t cnt = ((size_t)units * 4 + 255) / 256 * 256;
-  p.ws_bytes = cnt + (p.S > 1 ? (size_t)units * p.S * MSLOT * 4 : 0);
+  if (units > MUNITS) {
+    p.mfma = false;
+    return p;
+  }
+  p.ws_bytes = MPART_OFF + (p.S > 1 ? (size_t)units * p.S * MSLOT * 4 : 0);
   return p;
 }
 
@@ -495,8 +502,7 @@ hipError_t launch_dec_gemv(const DecGemv& d, hipStream_t s) {
     a.S = p.S;
     a.groups = p.groups;
     a.counters = static_cast<unsigned*>(d.ws);
-    a.part = reinterpret_cast<float*>(static_cast<char*>(d.ws) +
-                                      ((size_t)p.groups * p.row_tiles * 4 + 255) / 256 * 256);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(d.ws) + MPART_OFF);
     hipLaunchKernelGGL(dec_gemv_mfma_kernel, dim3((unsigned)(p.groups * p.S), (unsigned)p.row_tiles),
                        dim3(MTH), 0, s, a);
     return hipGetLastError();

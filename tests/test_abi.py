@@ -264,11 +264,14 @@ def test_decoder_workspace_query(L):
     assert q(vc.VC_DEC_STORE, vc.VC_F32, 32000, 2048, 16) == 0
     assert q(vc.VC_DEC_STORE, vc.VC_BF16, 32000, 2044, 16) == 0
     assert q(vc.VC_DEC_SWIGLU, vc.VC_BF16, 2 * 1000, 2048, 16) == 0
-    assert q(vc.VC_DEC_STORE, vc.VC_BF16, 200, 160, 16) == 256
+    T = 4096 * 4  # the tickets: a fixed region, so that differently shaped products can share
+    assert q(vc.VC_DEC_STORE, vc.VC_BF16, 200, 160, 16) == T
     # q/k/v of 16 + 2 x 4 heads, K 2048, 16 rows: 24 column groups, 8 slices of 256
-    assert q(vc.VC_DEC_ROPE, vc.VC_BF16, 3072, 2048, 16) == 256 + 24 * 8 * (128 * 16 + 16) * 4
+    assert q(vc.VC_DEC_ROPE, vc.VC_BF16, 3072, 2048, 16) == T + 24 * 8 * (128 * 16 + 16) * 4
     # three row tiles: tickets and tiles per row tile
-    assert q(vc.VC_DEC_ADD, vc.VC_BF16, 512, 512, 33) == 256 + 3 * 4 * 2 * (128 * 16 + 16) * 4
+    assert q(vc.VC_DEC_ADD, vc.VC_BF16, 512, 512, 33) == T + 3 * 4 * 2 * (128 * 16 + 16) * 4
+    # more than 4096 column groups x row tiles: the vector form only
+    assert q(vc.VC_DEC_STORE, vc.VC_BF16, 128 * 4097, 256, 16) == 0
     for d in ([vc.VC_DEC_ROPE, vc.VC_BF16, 3072, 2048, 16], [vc.VC_DEC_SWIGLU, vc.VC_BF16, 11264, 2048, 16],
               [vc.VC_DEC_STORE, vc.VC_F32, 77, 2560, 5]):
         assert vc.vc_workspace_bytes(vc.VC_OP_DECODER, d) == q(*d)

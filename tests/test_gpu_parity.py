@@ -1074,6 +1074,37 @@ def test_batched_llama_decoder_per_request_greedy(gpu_lib, bits, kv, host, mode)
             _check_resynced(seq, _stack_logits(m, prompt, seq), f"request {b} {what}")
 
 
+def test_batched_llama_fused_drafts_equal_torch_drafts(gpu_lib):
+    """With bf16-valued weights the fused draft step runs its products on the matrix cores; its
+    drafts (the drafter's own greedy tokens, which decide acceptance but never the emitted tokens)
+    equal those of the PyTorch-glue draft step from the same state, round after round, and so do
+    the accepted counts."""
+    from kv_cache_compressed_amd.decode_loop import BatchedLlamaDecoder
+    from oracle import loop as oloop
+
+    m = oloop.LlamaModel(seed=31, vocab=2048, dm=512, d=128, Hq=4, Hkv=2, layers=2, F=1280)
+    r = lambda w: torch.from_numpy(np.asarray(w, np.float32)).to(torch.bfloat16).float().numpy()
+    W = {k: r(getattr(m, k)) for k in ("E", "Wlm", "g_f")}
+    for k in ("g_att", "Wq", "Wk", "Wv", "Wo", "g_mlp", "W1", "W2", "W3"):
+        W[k] = [r(w) for w in getattr(m, k)]
+    g = np.random.default_rng(37)
+    prompts = [[int(t) for t in g.integers(0, 2048, n)] for n in (200, 150, 260, 90)]
+    decs = {mode: BatchedLlamaDecoder(W, 4, 2, prompts, x=8, bits=4, R=32, max_new=80, fused=mode == "fused")
+            for mode in ("fused", "torch")}
+    assert decs["fused"].ws_dec is not None  # the matrix-core form is in use
+    for rnd in range(6):
+        for d in decs.values():
+            d.draft_phase()
+        a, b = decs["fused"].tok.cpu(), decs["torch"].tok.cpu()
+        assert torch.equal(a, b), f"round {rnd}: drafts differ\n{a}\n{b}"
+        for d in decs.values():
+            d.verify_step()
+            d.commit()
+        assert decs["fused"].rounds == decs["torch"].rounds
+    print(f"[fused vs torch drafts] accepted per round {decs['fused'].rounds}", flush=True)
+    assert sum(sum(r) for r in decs["fused"].rounds) > 0
+
+
 def test_batched_llama_groups_staggered_equal_lockstep(gpu_lib):
     """Two groups of two requests each (host-streamed bf16 caches, one copy stream): the staggered
     schedule emits exactly the lock-step schedule's tokens, round by round."""
@@ -1330,7 +1361,7 @@ def test_decoder_gemv_epilogues(gpu_lib, M, wdt, form):
         vc.vc_decoder_gemv(vc.VC_DEC_STORE, W2.cuda(), dev(Xk), out=Y2, ws=ws2)
         torch.cuda.synchronize()
         assert torch.equal(Y, Y2)
-        assert not ws2[:256].any()
+        assert not ws2[:16384].any()
         with pytest.raises(vc.VcError, match="ws_bytes"):  # a workspace too small is refused
             vc.vc_decoder_gemv(vc.VC_DEC_STORE, W2.cuda(), dev(Xk), out=Y2, ws=ws2[:64])
         # K below one slice's minimum (one slice, no partials), with the norm
@@ -1346,6 +1377,51 @@ def test_decoder_gemv_epilogues(gpu_lib, M, wdt, form):
     Yn = torch.zeros_like(Xd)
     vc.vc_rmsnorm(Xd, gd, Yn)
     assert np.abs(Yn.cpu().numpy() - oloop.rms_norm(X, gain.astype(np.float64))).max() < 1e-5
+
+
+def test_decoder_gemv_shared_workspace(gpu_lib):
+    """A draft step's five products (norm + q/k/v + rotation, output product into the residual,
+    norm + gate/up + SwiGLU, down product into the residual, norm + head) through ONE workspace
+    sized for the largest, twice over: every result equals the same product run with a fresh
+    workspace of its own, bit for bit (each product's partials stay clear of every other shape's
+    tickets, and every call leaves its tickets at zero)."""
+    g = np.random.default_rng(29)
+    M, dm, Hq, Hkv, F, V, cap = 16, 512, 4, 2, 1280, 4096, 64
+    bf = lambda n, k: torch.from_numpy((0.05 * g.standard_normal((n, k))).astype(np.float32)).to(
+        torch.bfloat16).cuda()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    Wqkv, Wo, W13, W2, Wlm = bf((Hq + 2 * Hkv) * 128, dm), bf(dm, Hq * 128), bf(2 * F, dm), bf(dm, F), bf(V, dm)
+    gain = dev((1 + 0.1 * g.standard_normal(dm)).astype(np.float32))
+    ang = np.arange(cap)[:, None] * 500000.0 ** (-2.0 * np.arange(64) / 128)
+    cos_t, sin_t = dev(np.cos(ang).astype(np.float32)), dev(np.sin(ang).astype(np.float32))
+    pos = dev(g.integers(0, cap, M).astype(np.int32))
+    X0 = dev(g.standard_normal((M, dm)).astype(np.float32))
+
+    def step(ws_of):
+        X = X0.clone()
+        q, k, v = (torch.zeros((M, h, 128), device="cuda") for h in (Hq, Hkv, Hkv))
+        vc.vc_decoder_gemv(vc.VC_DEC_ROPE, Wqkv, X, norm_gain=gain, q_out=q, k_out=k, v_out=v, Hq=Hq, Hkv=Hkv,
+                           cos_t=cos_t, sin_t=sin_t, pos=pos, ws=ws_of(vc.VC_DEC_ROPE, Wqkv))
+        vc.vc_decoder_gemv(vc.VC_DEC_ADD, Wo, q.view(M, -1).contiguous(), out=X, ws=ws_of(vc.VC_DEC_ADD, Wo))
+        H = torch.zeros((M, F), device="cuda")
+        vc.vc_decoder_gemv(vc.VC_DEC_SWIGLU, W13, X, norm_gain=gain, out=H, ws=ws_of(vc.VC_DEC_SWIGLU, W13))
+        vc.vc_decoder_gemv(vc.VC_DEC_ADD, W2, H, out=X, ws=ws_of(vc.VC_DEC_ADD, W2))
+        Y = torch.zeros((M, V), device="cuda")
+        vc.vc_decoder_gemv(vc.VC_DEC_STORE, Wlm, X, norm_gain=gain, out=Y, ws=ws_of(vc.VC_DEC_STORE, Wlm))
+        torch.cuda.synchronize()
+        return [t.clone() for t in (q, k, v, H, X, Y)]
+
+    need = lambda e, W: vc.vc_decoder_gemv_workspace(e, vc.VC_BF16, W.shape[0], W.shape[1], M)
+    sizes = [need(vc.VC_DEC_ROPE, Wqkv), need(vc.VC_DEC_ADD, Wo), need(vc.VC_DEC_SWIGLU, W13),
+             need(vc.VC_DEC_ADD, W2), need(vc.VC_DEC_STORE, Wlm)]
+    assert min(sizes) > 16384 and len(set(sizes)) > 1  # every product cuts K; shapes differ
+    fresh = step(lambda e, W: torch.zeros(need(e, W), dtype=torch.uint8, device="cuda"))
+    shared = torch.zeros(max(sizes), dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        got = step(lambda e, W: shared)
+        for a, b, name in zip(got, fresh, ("q", "k", "v", "H", "X", "logits")):
+            assert torch.equal(a, b), f"pass {rep}: {name}"
+    assert not shared[:16384].any()
 
 
 def test_embed_rows(gpu_lib):
