@@ -5,10 +5,12 @@
 // the full-cache prediction; the full-cache token is emitted there, or the extra prediction when
 // every draft matches. Ties in the argmax go to the lowest token id.
 //
-// One workgroup of 1024 threads (16 waves) per batch row: the L rows one after the other, each
-// scanned by all 16 waves (a slice each) with 16-byte loads, a shuffle reduction of (value, index)
-// pairs per wave and an LDS reduction over the waves; then one thread walks the L argmax values to
-// find the first disagreement. No atomics, no inter-workgroup traffic.
+// One workgroup of 1024 threads (16 waves) per batch row. The waves are dealt over the L rows so
+// that all 16 keep loads in flight whatever L is: WPR = 16 / L waves per row (a power of two, at
+// least 1), each scanning a slice of its row with 16-byte loads, rows taken 16 / WPR at a time; a
+// shuffle reduction of (value, index) pairs per wave and an LDS reduction over a row's waves give
+// its argmax; then one thread walks the L argmax values to find the first disagreement. No
+// atomics, no inter-workgroup traffic.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,37 +37,42 @@ __global__ void __launch_bounds__(1024) accept_kernel(const float* __restrict__ 
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool vec = (V % 4) == 0;
-  // Rows one after the other, each spread over all 16 waves (wave w scans a 1/16 slice of the
-  // row), so a single row (a greedy step) still has 1024 threads' loads in flight.
-  for (int row = 0; row < L; ++row) {
-    const float* z = logits + ((int64_t)b * L + row) * V;
+  int wpr = WAVES;  // waves per row: the largest power of two with wpr * L <= WAVES, at least 1
+  while (wpr > 1 && wpr * L > WAVES) wpr >>= 1;
+  const int conc = WAVES / wpr;  // rows in flight at a time
+  const int sub = wave % wpr;
+  for (int r0 = 0; r0 < L; r0 += conc) {
+    const int row = r0 + wave / wpr;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    if (vec) {
-      // UNROLL 16-byte loads per lane in flight at a time (lanes past the slice re-read its last
-      // float4 and lose every comparison: an equal value at a higher index never wins)
-      constexpr int UNROLL = 4;
-      const float4* z4 = reinterpret_cast<const float4*>(z);
-      const int n4 = V / 4;
-      const int per = (n4 + WAVES - 1) / WAVES;
-      const int s0 = min(wave * per, n4), s1 = min(s0 + per, n4);
-      for (int i0 = s0; i0 < s1; i0 += 64 * UNROLL) {
-        float4 t[UNROLL];
+    if (row < L) {
+      const float* z = logits + ((int64_t)b * L + row) * V;
+      if (vec) {
+        // UNROLL 16-byte loads per lane in flight at a time (lanes past the slice re-read its
+        // last float4 and lose every comparison: an equal value at a higher index never wins)
+        constexpr int UNROLL = 8;
+        const float4* z4 = reinterpret_cast<const float4*>(z);
+        const int n4 = V / 4;
+        const int per = (n4 + wpr - 1) / wpr;
+        const int s0 = min(sub * per, n4), s1 = min(s0 + per, n4);
+        for (int i0 = s0; i0 < s1; i0 += 64 * UNROLL) {
+          float4 t[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) t[u] = z4[min(i0 + 64 * u + lane, s1 - 1)];
+          for (int u = 0; u < UNROLL; ++u) t[u] = z4[min(i0 + 64 * u + lane, s1 - 1)];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          const int base = 4 * min(i0 + 64 * u + lane, s1 - 1);
-          if (better(t[u].x, base + 0, bv, bi)) { bv = t[u].x; bi = base + 0; }
-          if (better(t[u].y, base + 1, bv, bi)) { bv = t[u].y; bi = base + 1; }
-          if (better(t[u].z, base + 2, bv, bi)) { bv = t[u].z; bi = base + 2; }
-          if (better(t[u].w, base + 3, bv, bi)) { bv = t[u].w; bi = base + 3; }
+          for (int u = 0; u < UNROLL; ++u) {
+            const int base = 4 * min(i0 + 64 * u + lane, s1 - 1);
+            if (better(t[u].x, base + 0, bv, bi)) { bv = t[u].x; bi = base + 0; }
+            if (better(t[u].y, base + 1, bv, bi)) { bv = t[u].y; bi = base + 1; }
+            if (better(t[u].z, base + 2, bv, bi)) { bv = t[u].z; bi = base + 2; }
+            if (better(t[u].w, base + 3, bv, bi)) { bv = t[u].w; bi = base + 3; }
+          }
         }
-      }
-    } else {
-      for (int i = threadIdx.x; i < V; i += 64 * WAVES) {
-        const float t = z[i];
-        if (better(t, i, bv, bi)) { bv = t; bi = i; }
+      } else {
+        for (int i = sub * 64 + lane; i < V; i += 64 * wpr) {
+          const float t = z[i];
+          if (better(t, i, bv, bi)) { bv = t; bi = i; }
+        }
       }
     }
     for (int m = 32; m >= 1; m >>= 1) {
@@ -78,15 +85,15 @@ __global__ void __launch_bounds__(1024) accept_kernel(const float* __restrict__ 
       s_bi[wave] = bi;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      float v = s_bv[0];
-      int ix = s_bi[0];
-      for (int w = 1; w < WAVES; ++w)
+    if (lane == 0 && sub == 0 && row < L) {  // the row's first wave combines its wpr waves
+      float v = s_bv[wave];
+      int ix = s_bi[wave];
+      for (int w = wave + 1; w < wave + wpr; ++w)
         if (better(s_bv[w], s_bi[w], v, ix)) { v = s_bv[w]; ix = s_bi[w]; }
       s_arg[row] = ix;
       if (argmax_out) argmax_out[(int64_t)b * L + row] = ix;
     }
-    __syncthreads();  // s_bv / s_bi are reused by the next row
+    __syncthreads();  // s_bv / s_bi are reused by the next rows; s_arg complete after the last
   }
   if (threadIdx.x == 0) {
     int a = L - 1;

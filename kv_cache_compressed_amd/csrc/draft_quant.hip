@@ -605,8 +605,18 @@ __device__ void quant_split_t(const DQArgs& a, int bh, int g_begin, int g_end, i
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float* s_p = reinterpret_cast<float*>(gr.scratch());  // [4 heads][32 tokens] weights
-  float* s_alpha = s_p + 128;                            // [4] rescale factors
+  // [4 heads][SP_PITCH] weights (32 tokens, padded so the four heads' rows start in different
+  // banks), then [4] rescale factors
+  constexpr int SP_PITCH = 36;
+  float* s_p = reinterpret_cast<float*>(gr.scratch());
+  float* s_alpha = s_p + 4 * SP_PITCH;
+  // q*s table cells (16 bytes): head h, part (0 hi, 1 lo), 8-channel chunk c at
+  // 16 (4 part + h) + (c ^ (4 part + h)): the eight (head, part) rows a QK operand read touches
+  // for one chunk land in eight different bank groups
+  const int trow_s = 4 * (j & 1) + (j >> 2);
+  int tcell[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) tcell[kb] = 16 * trow_s + ((4 * kb + gq) ^ trow_s);
   const ProgressPriority prio(gr.n);
   for (int i = 0; i < gr.n; ++i) {
     prio.step(i);
@@ -623,7 +633,7 @@ __device__ void quant_split_t(const DQArgs& a, int bh, int g_begin, int g_end, i
     }
     const float bias = sb[0] * a.qscale;  // head gq
     // ---- q*s table over this slot's code words (already in registers; the slot is refilled
-    // only after this group): hi parts at [h][chunk], lo parts at [4 + h][chunk], 16 bytes each
+    // only after this group), cells as above (hi parts in rows 0-3, lo parts in rows 4-7)
     u32x4* tbl = reinterpret_cast<u32x4*>(sl);
     {
       const u32x4 sc = *reinterpret_cast<const u32x4*>(mb + (lane & 15) * 16);
@@ -633,16 +643,16 @@ __device__ void quant_split_t(const DQArgs& a, int bh, int g_begin, int g_end, i
         thi[e2] = mix_mul2(qs[2 * e2], qs[2 * e2 + 1], sc[e2]);
         tlo[e2] = mix_rem2(qs[2 * e2], qs[2 * e2 + 1], sc[e2], thi[e2]);
       }
-      tbl[lane] = thi;
-      tbl[64 + lane] = tlo;
+      tbl[16 * th + (tc ^ th)] = thi;
+      tbl[64 + 16 * th + (tc ^ (4 + th))] = tlo;
       wave_lds_order();
     }
     // ---- QK^T transposed: s[tb][r] = head gq, part r, token 16 tb + j -------------------------
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    const u32x4* trow = tbl + (j & 1) * 64 + 16 * (j >> 2) + gq;
+
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const u32x4 aq = trow[4 * kb];
+      const u32x4 aq = tbl[tcell[kb]];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const u32x4 bk = BITS == 2 ? unpack2(kwd[2 * tb + kb / 2], kb & 1) : unpack4(kwd[4 * tb + kb]);
@@ -670,12 +680,12 @@ __device__ void quant_split_t(const DQArgs& a, int bh, int g_begin, int g_end, i
     const float p0 = __builtin_amdgcn_exp2f(fmaf(z0, KS, off));
     const float p1 = __builtin_amdgcn_exp2f(fmaf(z1, KS, off));
     l_lane += p0 + p1;
-    s_p[gq * 32 + j] = p0;
-    s_p[gq * 32 + 16 + j] = p1;
+    s_p[gq * SP_PITCH + j] = p0;
+    s_p[gq * SP_PITCH + 16 + j] = p1;
     wave_lds_order();
     // ---- PV operand: element e = token 16 (e/4) + 4 gq + e%4 of head hp ----------------------
-    const float4 pa = *reinterpret_cast<const float4*>(s_p + hp * 32 + 4 * gq);
-    const float4 pb = *reinterpret_cast<const float4*>(s_p + hp * 32 + 16 + 4 * gq);
+    const float4 pa = *reinterpret_cast<const float4*>(s_p + hp * SP_PITCH + 4 * gq);
+    const float4 pb = *reinterpret_cast<const float4*>(s_p + hp * SP_PITCH + 16 + 4 * gq);
     const float pe[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
     uint32_t wv[8];
 #pragma unroll

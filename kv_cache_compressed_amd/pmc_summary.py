@@ -18,6 +18,19 @@ per dispatch (median) are multiplied by that scale. Writes profiles/<name>_traff
 hash of the kernel's source it was measured on, which bench.py checks before reporting it) and
 profiles/<name>_traffic.md.
 
+A counter_collection.csv summed over counter instances (one row per dispatch and counter, the
+columns the other subcommands read), to keep the files of long runs small:
+
+    python -m kv_cache_compressed_amd.pmc_summary reduce RAW.csv OUT.csv
+
+Kernel time summary of a `rocprofv3 --kernel-trace --stats --output-format csv` run:
+
+    python -m kv_cache_compressed_amd.pmc_summary stats X_kernel_stats.csv --name c2_round \
+        --title "..." --command "..." [--note "..."]
+
+writes profiles/<name>_kernel_stats.md (kernels by total time: calls, average / min / max
+microseconds, share of GPU time).
+
 Per-kernel medians of any counters (e.g. the matrix-core pass):
 
     python -m kv_cache_compressed_amd.pmc_summary counters M.csv --name verify_c2_mfma \\
@@ -118,8 +131,11 @@ def traffic(args):
 
 
 def counters(args):
-    names = counter_names(args.csv)
-    data = {c: per_dispatch(args.csv, c) for c in names}
+    data = {}
+    for path in args.csv:  # one file per counter pass; a counter read in several passes: the first
+        for c in counter_names(path):
+            data.setdefault(c, per_dispatch(path, c))
+    names = sorted(data)
     rows = []
     for k in args.kernels:
         med, nd = {}, 0
@@ -137,20 +153,69 @@ def counters(args):
     md = [f"# {args.title}\n",
           "Command (repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first):\n",
           "```", args.command,
-          f"python -m kv_cache_compressed_amd.pmc_summary counters <out>/m_counter_collection.csv "
+          f"python -m kv_cache_compressed_amd.pmc_summary counters <pass csv> ... "
           f"--name {args.name} --kernels {' '.join(args.kernels)}", "```\n",
-          "Medians per dispatch. `GRBM_GUI_ACTIVE` is summed over the 8 XCDs; matrix-core "
-          "utilisation = `SQ_VALU_MFMA_BUSY_CYCLES` / (`GRBM_GUI_ACTIVE` / 8 x 1024 SIMDs).\n",
-          "| kernel | dispatches | " + " | ".join(f"`{c}`" for c in names) + " | MFMA busy |",
-          "|---|---:|" + "---:|" * len(names) + "---:|"]
-    for k, nd, med, util in rows:
-        cells = " | ".join(f"{med[c]:,.0f}" if c in med else "" for c in names)
-        md.append(f"| `{k}` | {nd} | {cells} | {'' if util is None else f'{100 * util:.1f}%'} |")
+          "Medians per dispatch, one row per counter (a rocprofv3 run collects one pass of counters; "
+          "the passes are separate runs of the same command). `GRBM_GUI_ACTIVE` is summed over the "
+          "8 XCDs; matrix-core utilisation = `SQ_VALU_MFMA_BUSY_CYCLES` / (`GRBM_GUI_ACTIVE` / 8 x "
+          "1024 SIMDs); the `SQ_WAIT_*` / `SQ_ACTIVE_*` shares are of `SQ_WAVE_CYCLES`.\n",
+          "| counter | " + " | ".join(f"`{k}` ({nd} dispatches)" for k, nd, _, _ in rows) + " |",
+          "|---|" + "---:|" * len(rows)]
+    for c in names:
+        cells = []
+        for _, _, med, _ in rows:
+            v = med.get(c)
+            cell = "" if v is None else f"{v:,.0f}"
+            if v is not None and c.startswith(("SQ_WAIT", "SQ_ACTIVE")) and med.get("SQ_WAVE_CYCLES"):
+                cell += f" ({100 * v / med['SQ_WAVE_CYCLES']:.1f}%)"
+            cells.append(cell)
+        md.append(f"| `{c}` | " + " | ".join(cells) + " |")
+    md.append("| MFMA busy | " + " | ".join("" if u is None else f"{100 * u:.1f}%" for _, _, _, u in rows) + " |")
     md.append("")
     if args.note:
         md.append(args.note + "\n")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     open(os.path.join(ROOT, "profiles", f"{args.name}_counters.md"), "w").write("\n".join(md))
+    print("\n".join(md))
+
+
+def reduce(args):
+    acc, names = {}, {}
+    for r in csv.DictReader(open(args.raw)):
+        key = (int(r["Dispatch_Id"]), r["Counter_Name"])
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        names[int(r["Dispatch_Id"])] = r["Kernel_Name"]
+    with open(args.out, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for (d, c), v in sorted(acc.items()):
+            w.writerow([d, names[d], c, v])
+
+
+def short_name(name: str, width: int = 90) -> str:
+    n = name.replace("(anonymous namespace)::", "").replace("vc::", "").replace("void ", "")
+    return n if len(n) <= width else n[:width - 3] + "..."
+
+
+def stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    md = [f"# {args.title}\n",
+          "Command (repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first):\n",
+          "```", args.command,
+          f"python -m kv_cache_compressed_amd.pmc_summary stats <out>/<x>_kernel_stats.csv --name {args.name}",
+          "```\n"]
+    if args.note:
+        md.append(args.note + "\n")
+    md += ["| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows[:args.top]:
+        md.append(f"| `{short_name(r['Name'])}` | {int(r['Calls'])} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                  f"{100 * float(r['TotalDurationNs']) / total:.2f} |")
+    md.append("")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    open(os.path.join(ROOT, "profiles", f"{args.name}_kernel_stats.md"), "w").write("\n".join(md))
     print("\n".join(md))
 
 
@@ -168,14 +233,24 @@ def main():
     t.add_argument("--workload", required=True)
     t.add_argument("--command", required=True, help="the profiled command, <COUNTER> for the counter")
     c = sub.add_parser("counters")
-    c.add_argument("csv")
+    c.add_argument("csv", nargs="+")
     c.add_argument("--name", required=True)
     c.add_argument("--kernels", nargs="+", required=True)
     c.add_argument("--title", required=True)
     c.add_argument("--command", required=True)
     c.add_argument("--note", default="")
+    r = sub.add_parser("reduce")
+    r.add_argument("raw")
+    r.add_argument("out")
+    st = sub.add_parser("stats")
+    st.add_argument("csv")
+    st.add_argument("--name", required=True)
+    st.add_argument("--title", required=True)
+    st.add_argument("--command", required=True)
+    st.add_argument("--note", default="")
+    st.add_argument("--top", type=int, default=16)
     args = ap.parse_args()
-    traffic(args) if args.cmd == "traffic" else counters(args)
+    {"traffic": traffic, "counters": counters, "reduce": reduce, "stats": stats}[args.cmd](args)
 
 
 if __name__ == "__main__":

@@ -95,7 +95,8 @@ def test_accept_worked_example(gpu_lib):
     assert am.cpu().numpy()[0].tolist() == verified
 
 
-@pytest.mark.parametrize("B,L,V", [(1, 9, 2048), (8, 31, 2048), (16, 31, 32000), (3, 5, 2047), (8, 1, 2048)])
+@pytest.mark.parametrize("B,L,V", [(1, 9, 2048), (8, 31, 2048), (16, 31, 32000), (3, 5, 2047), (8, 1, 2048),
+                                   (2, 3, 1000), (4, 16, 4096), (2, 17, 333), (1, 64, 512)])
 def test_accept_random(gpu_lib, B, L, V):
     g = np.random.default_rng(B * 100 + L)
     Z = g.standard_normal((B, L, V)).astype(np.float32)
