@@ -15,6 +15,7 @@
  *   vc_draft_attn_drop   one-query decode attention over kept positions       (draft)
  *   vc_verify_attn       L-query causal block attention over the full cache   (verify)
  *   vc_verify_prefetch   first chunk copies of a host-streamed verify, issued early (verify)
+ *   vc_prefill_attn      causal self-attention of a prompt's rows, one launch   (prefill)
  *   vc_verify_stream_copies  a host-streamed verify's copies alone (its link ceiling) (measurement)
  *   vc_lse_merge         log-sum-exp merge of split partials                  (verify / draft)
  *   vc_accept            per-row argmax, first disagreement, correction token (accept)
@@ -246,6 +247,27 @@ vc_status vc_verify_attn(const void *q, const void *k_blk, const void *v_blk, in
                          int32_t Hq, int32_t Hkv, float sm_scale, float *out, float *lse, void *ws,
                          size_t ws_bytes, void *compute_stream, void *copy_stream);
 /*
+ * Prefill attention: causal self-attention of a prompt's n rows, the pass that fills the caches
+ * before the first round ("VeriCache: making lossy KV compression exact", The Core Idea: both the
+ * full and the compressed cache hold the prompt's keys and values before drafting starts). Row i
+ * (position i) of query head h attends over tokens 0..i of kv head h / (Hq/Hkv); the same
+ * arithmetic as the bf16 verify (bf16 products on the matrix cores, fp32 scores, the softmax
+ * weights as a bf16 hi + lo pair, split partials merged with log-sum-exp): 32-row blocks, each
+ * over the key tiles up to its own (the diagonal tile masked), the longest blocks first, all in
+ * one launch plus the merge.
+ *   q      [B][Hq][n][128] bf16, device
+ *   k, v   element (b, h, t, c) at [((b*Hkv + h)*kv_stride + t)*128 + c], bf16, device;
+ *          kv_stride >= n
+ *   out    [B][Hq][n][128] fp32; lse [B][Hq][n] fp32 (natural log) or NULL
+ *   n >= 1 (at most 8388607), Hq % Hkv == 0, Hq/Hkv <= 8 (else VC_ERR_UNSUPPORTED),
+ *   B*Hkv*ceil(n/32) <= 2^24; ws: vc_prefill_workspace() bytes (split partials).
+ */
+vc_status vc_prefill_attn(const void *q, const void *k, const void *v, int64_t kv_stride, int64_t n,
+                          int32_t B, int32_t Hq, int32_t Hkv, float sm_scale, float *out, float *lse,
+                          void *ws, size_t ws_bytes, void *stream);
+vc_status vc_prefill_workspace(int32_t B, int32_t Hq, int32_t Hkv, int64_t n, size_t *bytes);
+
+/*
  * Prefetch of a host-streamed verify ("VeriCache: making lossy KV compression exact", Verifying
  * Without Giving Back the Speedup: the full cache is brought in from CPU memory only to verify; the
  * committed past of a round is known before its drafts are, so its first chunks can cross the link
@@ -408,11 +430,13 @@ vc_status vc_embed_rows(const float *E, int32_t V, int32_t K, const int32_t *tok
  *                      vc_verify_prefetch, vc_verify_stream_copies)
  *   VC_OP_PROJECT      dims {B, L, V}                                        (vc_project_logits)
  *   VC_OP_DECODER      dims {epilogue, w_dtype, N, K, M}                     (vc_decoder_gemv)
+ *   VC_OP_PREFILL      dims {B, Hq, Hkv, n}                                  (vc_prefill_attn)
  * A wrong count of dims or an unknown op returns VC_ERR_INVALID. The pages give the calls of the
  * path, not their memory; the caller owns every workspace ("VeriCache: Turning Lossy KV Cache into
  * Lossless LLM Inference", Key Contributions: one interface for every compressor).
  */
-enum { VC_OP_DRAFT_QUANT = 1, VC_OP_DRAFT_DROP = 2, VC_OP_VERIFY = 3, VC_OP_PROJECT = 4, VC_OP_DECODER = 5 };
+enum { VC_OP_DRAFT_QUANT = 1, VC_OP_DRAFT_DROP = 2, VC_OP_VERIFY = 3, VC_OP_PROJECT = 4, VC_OP_DECODER = 5,
+       VC_OP_PREFILL = 6 };
 vc_status vc_workspace_bytes(int32_t op, const int64_t *dims, int32_t ndims, size_t *bytes);
 
 const char *vc_status_string(vc_status s);

@@ -287,6 +287,38 @@ vc_status vc_verify_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int
   return ok();
 }
 
+vc_status vc_prefill_workspace(int32_t B, int32_t Hq, int32_t Hkv, int64_t n, size_t* bytes) {
+  REQUIRE(bytes != nullptr, "bytes is null");
+  REQUIRE(B >= 1 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, "bad head/batch sizes");
+  REQUIRE(n >= 1, "n must be >= 1");
+  *bytes = vc::plan_prefill(B, Hq, Hkv, n).ws_bytes;
+  return ok();
+}
+
+vc_status vc_prefill_attn(const void* q, const void* k, const void* v, int64_t kv_stride, int64_t n,
+                          int32_t B, int32_t Hq, int32_t Hkv, float sm_scale, float* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  REQUIRE(n >= 1, "n must be >= 1");
+  REQUIRE(kv_stride >= n, "kv_stride must be >= n");
+  REQUIRE(B >= 1 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv");
+  if (Hq / Hkv > 8) return fail(VC_ERR_UNSUPPORTED, "Hq/Hkv > 8 is not supported");
+  // keys of one (b, kv head) are addressed through a buffer resource of < 2^31 bytes
+  if (n > (int64_t)8388607) return fail(VC_ERR_UNSUPPORTED, "more than 8388607 tokens per (b, kv head)");
+  REQUIRE((int64_t)B * Hkv * ((n + 31) / 32) <= (int64_t)1 << 24, "B*Hkv*ceil(n/32) must be <= 2^24");
+  const vc::PrefillPlan plan = vc::plan_prefill(B, Hq, Hkv, n);
+  if (ws == nullptr || ws_bytes < plan.ws_bytes || !aligned16(ws))
+    return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,
+                ws ? ws_bytes : (size_t)0);
+  hipError_t e = vc::launch_prefill(q, k, v, kv_stride, n, B, Hq, Hkv, sm_scale, out, lse, ws, plan,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_prefill_attn launch");
+  return ok();
+}
+
 namespace {
 
 // Prefetches issued by vc_verify_prefetch and not yet consumed, one per workspace.
@@ -648,6 +680,10 @@ vc_status vc_workspace_bytes(int32_t op, const int64_t* dims, int32_t ndims, siz
       REQUIRE(need(3), "VC_OP_PROJECT takes 3 dims {B, L, V} (got %d)", ndims);
       REQUIRE(fits32(3), "B, L and V must fit int32");
       return vc_project_workspace((int32_t)dims[0], (int32_t)dims[1], (int32_t)dims[2], bytes);
+    case VC_OP_PREFILL:  // {B, Hq, Hkv, n}
+      REQUIRE(need(4), "VC_OP_PREFILL takes 4 dims {B, Hq, Hkv, n} (got %d)", ndims);
+      REQUIRE(fits32(3), "B, Hq and Hkv must fit int32");
+      return vc_prefill_workspace((int32_t)dims[0], (int32_t)dims[1], (int32_t)dims[2], dims[3], bytes);
     case VC_OP_DECODER:  // {epilogue, w_dtype, N, K, M}
       REQUIRE(need(5), "VC_OP_DECODER takes 5 dims {epilogue, w_dtype, N, K, M} (got %d)", ndims);
       REQUIRE(fits32(5), "epilogue, w_dtype, N, K and M must fit int32");

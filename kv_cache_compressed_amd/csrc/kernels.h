@@ -73,6 +73,15 @@ struct VerifyPlan {
 };
 VerifyPlan plan_verify(int B, int Hq, int Hkv, int L, int64_t n, int past_on_host,
                        int64_t chunk_tokens, int dtype);
+// Prefill: causal self-attention of n rows (bf16), one launch plus the merge.
+struct PrefillPlan {
+  int splits;       // tile ranges per row block (partials per row)
+  size_t ws_bytes;
+};
+PrefillPlan plan_prefill(int B, int Hq, int Hkv, int64_t n);
+hipError_t launch_prefill(const void* q, const void* k, const void* v, int64_t kv_stride, int64_t n,
+                          int B, int Hq, int Hkv, float sm_scale, float* out, float* lse, void* ws,
+                          const PrefillPlan& plan, hipStream_t s);
 hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, int L,
                          const void* k_past, const void* v_past, int64_t past_stride, int64_t n,
                          int past_on_host, int dtype, int B, int Hq, int Hkv, float sm_scale,

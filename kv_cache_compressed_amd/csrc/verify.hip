@@ -59,6 +59,11 @@ struct VArgs {
   float qscale;            // sm_scale * log2(e)
   float* part_o;
   float* part_ml;
+  // prefill form only: causal self-attention of n rows; unit = (row block, b, kv head), row
+  // block rb = rows 32 rb .. over key tiles 0 .. rb (the diagonal tile masked), heaviest first
+  int n_rows;              // n
+  int bh_units;            // B * Hkv
+  int rblocks;             // ceil(n / 32)
 };
 
 constexpr float LAZY = 2.0f;  // log2 slack before a row's reference max is moved
@@ -162,7 +167,7 @@ __device__ __forceinline__ LogicalBlock logical_block(const VArgs& a) {
 // the PV row operand with the LDS transpose read (ds_read_b64_tr_b16): source lane s of a
 // 16-lane block supplies 4 consecutive channels of one token row and result lane i receives
 // element e from source lane 4e + i/4, so no transposed copy of the values is ever written.
-template <int NW>
+template <int NW, bool PREFILL>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4 ? WG_PER_CU : 2))) verify_bf16_kernel(VArgs a) {
   constexpr int NT = 64 * NW;
   constexpr int COPIES = 2 * TK * 16 / NT;  // buffer -> LDS copies per lane per tile
@@ -172,7 +177,12 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
   const int j = lane & 15, gq = lane >> 4;
   const LogicalBlock lb = logical_block(a);
   if (!lb.live) return;  // grid padding
-  const int bh = lb.unit;
+  // prefill: this unit's row block (the longest first) and its rows' positions
+  const int rb = PREFILL ? a.rblocks - 1 - lb.unit / a.bh_units : 0;
+  const int pos0 = PREFILL ? 32 * rb : 0;                          // position of row 0
+  const int Lu = PREFILL ? min(32, a.n_rows - pos0) : a.L;         // this unit's rows
+  const int qrows = PREFILL ? a.n_rows : a.L;                      // rows per (b, head) in q / out
+  const int bh = PREFILL ? lb.unit % a.bh_units : lb.unit;
   // Jobs of this workgroup: split lb.split of the launch's source (if lb.split < splits),
   // then, for the last workgroup of the row and when the round's block is given, the block as one
   // more causal split (it is one tile: a workgroup of its own would not fit the resident round).
@@ -181,9 +191,9 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
   auto run_job = [&](const bool blk) {
   const uint16_t* const src_k = blk ? a.k_blk : a.k;
   const uint16_t* const src_v = blk ? a.v_blk : a.v;
-  const int64_t src_stride = blk ? a.L : a.bh_stride, src_ntok = blk ? a.L : a.ntok;
+  const int64_t src_stride = blk ? a.L : a.bh_stride, src_ntok = blk ? a.L : PREFILL ? pos0 + Lu : a.ntok;
   const int src_splits = blk ? 1 : a.splits, split = blk ? 0 : lb.split;
-  const bool causal = blk || a.causal;
+  const bool causal = blk || a.causal || PREFILL;
   const int sidx = blk ? a.blk_index : a.split_offset + split;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int hg = lb.z * a.Gw + wave;  // head within the kv group
@@ -210,10 +220,10 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
   u32x4 qop[2][4];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
-    const int row = min(16 * ct + j, a.L - 1);  // rows past L read row L-1 and are never written
+    const int row = pos0 + min(16 * ct + j, Lu - 1);  // rows past L read row L-1, never written
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const int64_t off = (((int64_t)b * a.Hq + hq) * a.L + row) * D + 32 * kb + 8 * gq;
+      const int64_t off = (((int64_t)b * a.Hq + hq) * qrows + row) * D + 32 * kb + 8 * gq;
       qop[ct][kb] = *reinterpret_cast<const u32x4*>(a.q + off);
     }
   }
@@ -267,7 +277,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
       }
       // ---- masked online softmax per query row, lazily moved reference max ------------------
       // (scores are scaled inside the exponent: the max is taken on the raw products)
-      const bool masked = causal || tlen < TK;
+      // (prefill: only the diagonal tile masks; the tiles before it are whole)
+      const bool masked = (causal && (!PREFILL || tok0 + TK > pos0)) || tlen < TK;
       u32x4 phi[2][NHF], plo[2][NHF];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -277,8 +288,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
         for (int e = 0; e < 4 * NTB; ++e) raw[e] = s[e >> 2][ct][e & 3];
         if (masked) {
           asm volatile("");  // keep this rarely taken path a branch (no if-conversion)
-          // tokens of this tile that row sees: tok < lim
-          const int lim = causal ? (int)min<int64_t>(tlen, row + 1 - tok0) : tlen;
+          // tokens of this tile that row sees: tok < lim (row at position pos0 + row)
+          const int lim = causal ? (int)min<int64_t>(tlen, pos0 + row + 1 - tok0) : tlen;
 #pragma unroll
           for (int e = 0; e < 4 * NTB; ++e) {
             const int tok = 16 * (e >> 2) + 4 * gq + (e & 3);
@@ -365,8 +376,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
     for (int ct = 0; ct < 2; ++ct) {
       const int row = 16 * ct + j;
       const float l = sum_over_rows(l_lane[ct]);
-      if (row < a.L) {
-        const int64_t prow = ((int64_t)b * a.Hq + hq) * a.L + row;
+      if (row < Lu) {
+        const int64_t prow = ((int64_t)b * a.Hq + hq) * qrows + pos0 + row;
         float* po = a.part_o + (prow * a.total_splits + sidx) * D;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
@@ -641,6 +652,62 @@ hipError_t launch_verify_copies(const void* k_past, const void* v_past, int64_t 
   return err;
 }
 
+PrefillPlan plan_prefill(int B, int Hq, int Hkv, int64_t n) {
+  PrefillPlan p{};
+  const int64_t rblocks = (n + TK - 1) / TK;
+  const int64_t wunits = (int64_t)B * Hkv * rblocks * ((Hq / Hkv + 3) / 4);
+  // one tile range per row block unless that leaves the chip short of workgroups
+  p.splits = (int)std::max<int64_t>(1, std::min<int64_t>((256 * WG_PER_CU + wunits - 1) / wunits,
+                                                         std::max<int64_t>(1, rblocks / 8)));
+  const size_t rows = (size_t)B * Hq * n;
+  p.ws_bytes = (rows * p.splits * (D + 2) * sizeof(float) + 255) & ~(size_t)255;
+  return p;
+}
+
+hipError_t launch_prefill(const void* q, const void* k, const void* v, int64_t kv_stride, int64_t n,
+                          int B, int Hq, int Hkv, float sm_scale, float* out, float* lse, void* ws,
+                          const PrefillPlan& plan, hipStream_t s) {
+  const size_t rows = (size_t)B * Hq * n;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o + rows * plan.splits * D;
+  const int G = Hq / Hkv;
+  VArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.bh_stride = kv_stride;
+  a.ntok = n;
+  a.splits = plan.splits;
+  a.split_offset = 0;
+  a.causal = 1;
+  a.k_blk = nullptr;
+  a.v_blk = nullptr;
+  a.blk_index = 0;
+  a.L = 32;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.total_splits = plan.splits;
+  a.Gw = G <= 4 ? G : 4;
+  a.qscale = sm_scale * LOG2E;
+  a.part_o = part_o;
+  a.part_ml = part_ml;
+  a.n_rows = (int)n;
+  a.bh_units = B * Hkv;
+  a.rblocks = (int)((n + TK - 1) / TK);
+  constexpr int NW = 4;
+  const int gz = (G + 3) / 4;
+  a.units = a.bh_units * a.rblocks;
+  a.gz = gz;
+  a.gsplits = plan.splits;
+  unsigned wgs = (unsigned)(a.gsplits * a.units * gz);
+  if (gz == 2) wgs = (wgs + 15) / 16 * 16;  // whole groups of 16 (see logical_block)
+  hipLaunchKernelGGL((verify_bf16_kernel<NW, true>), dim3(wgs), dim3(64 * NW), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_merge(part_o, part_ml, (int64_t)rows, plan.splits, out, lse, s);
+}
+
 hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, int L,
                          const void* k_past, const void* v_past, int64_t past_stride, int64_t n,
                          int past_on_host, int dtype, int B, int Hq, int Hkv, float sm_scale,
@@ -701,7 +768,7 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
     a.gsplits = (int)grid.x;
     unsigned n = grid.x * grid.y * grid.z;
     if (gz == 2) n = (n + 15) / 16 * 16;  // whole groups of 16 (see logical_block)
-    hipLaunchKernelGGL(verify_bf16_kernel<NW>, dim3(n), block, 0, compute, a);
+    hipLaunchKernelGGL((verify_bf16_kernel<NW, false>), dim3(n), block, 0, compute, a);
   };
 
   a.k_blk = nullptr;

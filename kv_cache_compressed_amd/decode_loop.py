@@ -87,6 +87,26 @@ class _Model:
             sink(t0, t1, K, V)
 
 
+def _causal_attention(Q, K, V, n: int, Hq: int, Hkv: int, vdt: int, ws: "vc.Workspace", device) -> torch.Tensor:
+    """Causal self-attention of a prompt's n rows for the prefill: Q [1, Hq, n, 128], K, V
+    [1, Hkv, n, 128] in the cache dtype -> O [n, Hq * 128] fp32. bf16: one vc_prefill_attn launch;
+    fp32 caches: the verify call block by block (32 rows over the keys before the block)."""
+    if vdt == vc.VC_BF16:
+        o = torch.empty((1, Hq, n, D), dtype=torch.float32, device=device)
+        vc.vc_prefill_attn(Q, K, V, n, o, None, ws.get(vc.vc_prefill_workspace(1, Hq, Hkv, n)), SM_SCALE)
+        return o[0].transpose(0, 1).reshape(n, -1)
+    O = torch.zeros((n, Hq * D), dtype=torch.float32, device=device)
+    for b0 in range(0, n, 32):
+        b1 = min(n, b0 + 32)
+        m = b1 - b0
+        o = torch.zeros((1, Hq, m, D), dtype=torch.float32, device=device)
+        nb = vc.vc_verify_workspace(1, Hq, Hkv, m, b0, False, 0, vdt)
+        vc.vc_verify_attn(Q[:, :, b0:b1].contiguous(), K[:, :, b0:b1].contiguous(), V[:, :, b0:b1].contiguous(),
+                          K, V, b0, o, None, ws.get(nb), SM_SCALE, past_stride=n)
+        O[b0:b1] = o[0].transpose(0, 1).reshape(m, -1)
+    return O
+
+
 class _Store:
     """The full cache [1, Hkv, cap, 128] in the cache dtype, in HBM or in pinned host memory."""
 
@@ -628,9 +648,8 @@ class LayeredDecoder:
 
     def _prefill(self, prompt):
         """Layer by layer over positions 0..n-1: keys/values into the full cache and the KIVI
-        cache, causal attention in blocks of 32 rows (the verify call over the layer's keys and
-        values of the rows before the block, device resident whatever the cache placement), the
-        residual stream updated."""
+        cache, causal attention over the layer's device-resident keys/values (whatever the cache
+        placement; see _causal_attention), the residual stream updated."""
         n, Hq, Hkv = self.n, self.Hq, self.Hkv
         X = self._embed(torch.tensor(prompt[:n], device=self.device), 0)
         cache_layout = lambda Y: Y.transpose(0, 1).unsqueeze(0).to(self.tdt).contiguous()
@@ -644,17 +663,7 @@ class LayeredDecoder:
             if n > self.n_q:
                 vc.vc_kivi_append(c, K[:, :, self.n_q:], V[:, :, self.n_q:], self.n_q, n - self.n_q,
                                   src_bh_stride=n * D)
-            O = torch.zeros((n, Hq * D), dtype=torch.float32, device=self.device)
-            for b0 in range(0, n, 32):
-                b1 = min(n, b0 + 32)
-                m = b1 - b0
-                q = cache_layout(Q[b0:b1])
-                o = torch.zeros((1, Hq, m, D), dtype=torch.float32, device=self.device)
-                lse = torch.zeros((1, Hq, m), dtype=torch.float32, device=self.device)
-                nb = vc.vc_verify_workspace(1, Hq, Hkv, m, b0, False, 0, self.vdt)
-                vc.vc_verify_attn(q, K[:, :, b0:b1].contiguous(), V[:, :, b0:b1].contiguous(), K, V, b0, o,
-                                  lse, self.ws_verify.get(nb), SM_SCALE, past_stride=n)
-                O[b0:b1] = o[0].transpose(0, 1).reshape(m, -1)
+            O = _causal_attention(cache_layout(Q), K, V, n, Hq, Hkv, self.vdt, self.ws_verify, self.device)
             X = self._block_out(l, X, O)
 
     def draft_step(self, j: int):
@@ -962,8 +971,8 @@ class BatchedLlamaDecoder:
                           copy_stream=self.copy_stream)
 
     def _prefill(self, b: int, prompt):
-        """Request b's positions 0..n-1, layer by layer: caches, then causal attention in 32-row
-        blocks over the layer's device-resident keys/values."""
+        """Request b's positions 0..n-1, layer by layer: caches, then causal attention over the
+        layer's device-resident keys/values (_causal_attention)."""
         n, Hq, Hkv = self.n[b], self.Hq, self.Hkv
         X = self.E[torch.tensor(prompt[:n], device=self.device)]
         pos = torch.arange(n, device=self.device)
@@ -977,16 +986,7 @@ class BatchedLlamaDecoder:
                 vc.vc_quantize_kv(c, K, V, 0, nq, src_bh_stride=n * D)
             if n > nq:
                 vc.vc_kivi_append(c, K[:, :, nq:], V[:, :, nq:], nq, n - nq, src_bh_stride=n * D)
-            O = torch.zeros((n, Hq * D), dtype=torch.float32, device=self.device)
-            for b0 in range(0, n, 32):
-                b1 = min(n, b0 + 32)
-                m = b1 - b0
-                o = torch.zeros((1, Hq, m, D), dtype=torch.float32, device=self.device)
-                lse = torch.zeros((1, Hq, m), dtype=torch.float32, device=self.device)
-                nb = vc.vc_verify_workspace(1, Hq, Hkv, m, b0, False, 0, self.vdt)
-                vc.vc_verify_attn(lay(Q[b0:b1]), K[:, :, b0:b1].contiguous(), V[:, :, b0:b1].contiguous(),
-                                  K, V, b0, o, lse, self.ws_verify.get(nb), SM_SCALE, past_stride=n)
-                O[b0:b1] = o[0].transpose(0, 1).reshape(m, -1)
+            O = _causal_attention(lay(Q), K, V, n, Hq, Hkv, self.vdt, self.ws_verify, self.device)
             X = self._block_out(l, X, O)
 
     # ---- one round ------------------------------------------------------------------------

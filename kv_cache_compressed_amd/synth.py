@@ -27,7 +27,7 @@ import torch
 
 # Fixed tensor tags of the seed sequence.
 TAG_K_PAST, TAG_V_PAST, TAG_Q_NEW, TAG_K_NEW, TAG_V_NEW = 0, 1, 3, 4, 5
-TAG_W, TAG_SCORES, TAG_OUTLIERS = 6, 7, 8
+TAG_W, TAG_SCORES, TAG_OUTLIERS, TAG_Q_PROMPT = 6, 7, 8, 9
 
 _POOL_WORKERS = 8
 
@@ -183,6 +183,18 @@ def q_new(w: Workload, seed: int = 0, round_index: int = 0) -> np.ndarray:
     for b in range(w.B):
         for h in range(w.Hq):
             Q[b, h] = normal(seed, w.wid, TAG_Q_NEW, b, h, (w.L, w.d), extra)
+    if w.kv_dtype == "bf16":
+        Q = round_bf16(Q)
+    return Q
+
+
+def q_prompt(w: Workload, seed: int = 0) -> np.ndarray:
+    """Queries of a prompt's positions 0..n-1: float32 [B, Hq, n, d] (bf16-valued for bf16
+    workloads), for the prefill pass."""
+    Q = np.empty((w.B, w.Hq, w.n, w.d), np.float32)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            Q[b, h] = normal(seed, w.wid, TAG_Q_PROMPT, b, h, (w.n, w.d))
     if w.kv_dtype == "bf16":
         Q = round_bf16(Q)
     return Q

@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "vc.h")
 VC_OK, VC_ERR_INVALID, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_HIP = 0, 1, 2, 3, 4
 VC_F32, VC_F16, VC_BF16 = 0, 1, 2
 VC_PAST_DEVICE, VC_PAST_HOST, VC_PAST_HOST_PREFETCHED = 0, 1, 2
-VC_OP_DRAFT_QUANT, VC_OP_DRAFT_DROP, VC_OP_VERIFY, VC_OP_PROJECT, VC_OP_DECODER = 1, 2, 3, 4, 5
+VC_OP_DRAFT_QUANT, VC_OP_DRAFT_DROP, VC_OP_VERIFY, VC_OP_PROJECT, VC_OP_DECODER, VC_OP_PREFILL = 1, 2, 3, 4, 5, 6
 VC_DEC_STORE, VC_DEC_ADD, VC_DEC_ROPE, VC_DEC_SWIGLU = 0, 1, 2, 3
 _TORCH_DT = {torch.float32: VC_F32, torch.float16: VC_F16, torch.bfloat16: VC_BF16}
 
@@ -70,6 +70,8 @@ _SIGS = {
     "vc_decoder_gemv": [_I32, _P, _I32, _I32, _I32, _P, _I32, _P, _F, _P, _P, _P, _P, _I32, _I32, _I32,
                         _P, _P, _I32, _P, _I32, _P, _SZ, _P],
     "vc_decoder_gemv_workspace": [_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
+    "vc_prefill_attn": [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P],
+    "vc_prefill_workspace": [_I32, _I32, _I32, _I64, ctypes.POINTER(_SZ)],
     "vc_rmsnorm": [_P, _P, _F, _I32, _I32, _P, _P],
     "vc_embed_rows": [_P, _I32, _I32, _P, _I64, _I32, _P, _P],
     "vc_status_string": [_I32],
@@ -286,6 +288,23 @@ def vc_verify_workspace(B, Hq, Hkv, L, n, past_on_host, chunk_tokens, dtype) -> 
     _check(lib().vc_verify_workspace(B, Hq, Hkv, L, n, int(past_on_host), chunk_tokens, dtype,
                                      ctypes.byref(nb)))
     return nb.value
+
+
+def vc_prefill_workspace(B: int, Hq: int, Hkv: int, n: int) -> int:
+    b = _SZ(0)
+    _check(lib().vc_prefill_workspace(B, Hq, Hkv, n, ctypes.byref(b)))
+    return b.value
+
+
+def vc_prefill_attn(q, k, v, n: int, out, lse, ws: torch.Tensor, sm_scale: float, kv_stride: int | None = None,
+                    stream=None):
+    """q [B, Hq, n, 128] bf16; k, v [B, Hkv, >= n, 128] bf16 (kv_stride = their token dimension);
+    out [B, Hq, n, 128] fp32; lse [B, Hq, n] or None. Causal self-attention of the n rows."""
+    B, Hq = q.shape[0], q.shape[1]
+    Hkv = k.shape[1]
+    stride = k.shape[2] if kv_stride is None else kv_stride
+    _check(lib().vc_prefill_attn(_ptr(q), _ptr(k), _ptr(v), stride, n, B, Hq, Hkv, sm_scale, _ptr(out),
+                                 _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def vc_verify_prefetch(k_past, v_past, n: int, ws: torch.Tensor, B: int, Hq: int, Hkv: int, L: int,

@@ -281,6 +281,31 @@ def test_decoder_workspace_query(L):
     assert L.vc_decoder_gemv_workspace(0, vc.VC_BF16, 64, 64, 0, ctypes.byref(one)) == vc.VC_ERR_INVALID
 
 
+def test_prefill_rejects_and_sizes(L):
+    """Argument checks of the prefill call (all before any HIP call) and its workspace: one split
+    partial (128 + 2 floats) per row and tile range; the generic query agrees."""
+    one = ctypes.c_size_t()
+    call = lambda **a: L.vc_prefill_attn(a.get("q", P), P, P, a.get("stride", 4096), a.get("n", 4000),
+                                         a.get("B", 1), a.get("Hq", 32), a.get("Hkv", 8), ctypes.c_float(0.1),
+                                         a.get("out", P), None, a.get("ws", P), a.get("wsb", 1 << 34), None)
+    assert call(n=0) == vc.VC_ERR_INVALID and "n must" in _err(L)
+    assert call(stride=3999) == vc.VC_ERR_INVALID and "kv_stride" in _err(L)
+    assert call(Hq=30) == vc.VC_ERR_INVALID
+    assert call(q=0) == vc.VC_ERR_INVALID
+    assert call(out=BAD) == vc.VC_ERR_INVALID
+    assert call(Hq=72) == vc.VC_ERR_UNSUPPORTED
+    assert call(n=8388608, stride=8388608) == vc.VC_ERR_UNSUPPORTED
+    assert call(wsb=16) == vc.VC_ERR_WORKSPACE
+    assert call(ws=0) == vc.VC_ERR_WORKSPACE
+    for d in ([1, 16, 4, 16384], [2, 8, 2, 33], [1, 64, 8, 1]):
+        assert L.vc_prefill_workspace(*d, ctypes.byref(one)) == vc.VC_OK
+        assert vc.vc_workspace_bytes(vc.VC_OP_PREFILL, d) == one.value
+        B, Hq, Hkv, n = d
+        splits = one.value // (B * Hq * n * 130 * 4)
+        assert splits >= 1 and one.value >= B * Hq * n * splits * 130 * 4
+    assert L.vc_prefill_workspace(1, 16, 4, 0, ctypes.byref(one)) == vc.VC_ERR_INVALID
+
+
 def test_stream_copies_rejects(L):
     """Argument checks of the copy-only transfer (all before any HIP call)."""
     call = lambda **a: L.vc_verify_stream_copies(

@@ -536,6 +536,69 @@ def test_verify_shapes(gpu_lib, n, L):
             _close(out[b, hq].cpu().numpy(), O, True, TIGHT["verify"], f"verify n={n} L={L} b={b} h={hq}")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,n,stride", [(2, 8, 2, 1, 1), (2, 8, 2, 31, 40), (2, 8, 2, 33, 33),
+                                                (1, 8, 2, 100, 128), (2, 8, 2, 257, 257), (1, 16, 2, 300, 300),
+                                                (1, 6, 2, 97, 97)])
+def test_prefill_vs_oracle(gpu_lib, B, Hq, Hkv, n, stride):
+    """Prefill (causal self-attention of the prompt's rows, one launch): every row of every head
+    against the oracle's causal block attention over an empty past (row i over tokens 0..i). One
+    row, a ragged last block, exactly one block plus one row, keys/values with a token stride
+    larger than n, 8 query heads per kv head (two head slices) and G = 3."""
+    w = synth.WORKLOADS["c2"].with_(B=B, Hq=Hq, Hkv=Hkv, n=n)
+    K, V = synth.kv_past(w)
+    Q = synth.q_prompt(w)
+    G = Hq // Hkv
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", torch.bfloat16)
+    Kp = np.zeros((B, Hkv, stride, 128), np.float32)
+    Vp = np.zeros_like(Kp)
+    Kp[:, :, :n], Vp[:, :, :n] = K, V
+    out = torch.full((B, Hq, n, 128), float("nan"), device="cuda")
+    lse = torch.full((B, Hq, n), float("nan"), device="cuda")
+    ws = torch.zeros(vc.vc_prefill_workspace(B, Hq, Hkv, n), dtype=torch.uint8, device="cuda")
+    vc.vc_prefill_attn(dev(Q), dev(Kp), dev(Vp), n, out, lse, ws, harness.SM_SCALE)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    empty = np.zeros((0, 128))
+    for b in range(B):
+        for hq in range(Hq):
+            O, lr = oatt.verify_block(Q[b, hq], empty, empty, K[b, hq // G], V[b, hq // G])
+            _close(o[b, hq], O, True, TIGHT["verify"], f"prefill n={n} b={b} h={hq}")
+            assert np.abs(l[b, hq] - lr).max() < 1e-3, f"lse b={b} h={hq}"
+
+
+def test_prefill_long_prompt_sampled_rows(gpu_lib):
+    """A 4000-token prompt (125 row blocks, the longest over 125 key tiles) at 32/8 heads: sampled
+    rows of every head against the oracle's decode at their positions, and the same launch agrees
+    with the verify call run block by block (past = the rows before the block) on those rows."""
+    n, Hq, Hkv = 4000, 32, 8
+    w = synth.WORKLOADS["c2"].with_(B=1, Hq=Hq, Hkv=Hkv, n=n)
+    K, V = synth.kv_past(w)
+    Q = synth.q_prompt(w)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", torch.bfloat16)
+    Kd, Vd, Qd = dev(K), dev(V), dev(Q)
+    out = torch.zeros((1, Hq, n, 128), device="cuda")
+    ws = torch.zeros(vc.vc_prefill_workspace(1, Hq, Hkv, n), dtype=torch.uint8, device="cuda")
+    vc.vc_prefill_attn(Qd, Kd, Vd, n, out, None, ws, harness.SM_SCALE)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    rows = [0, 31, 32, 1999, 2016, 3968, 3999]
+    for hq in range(0, Hq, 5):
+        for i in rows:
+            O, _ = oatt.decode(Q[0, hq, i], K[0, hq // 4, :i + 1], V[0, hq // 4, :i + 1])
+            _close(o[0, hq, i], O, True, TIGHT["verify"], f"prefill row {i} h={hq}")
+    for i0 in (0, 1984, 3968):  # the blocks of rows 0, 2016 and 3968 through the verify call
+        L = min(32, n - i0)
+        ov = torch.zeros((1, Hq, L, 128), device="cuda")
+        wv = torch.zeros(vc.vc_verify_workspace(1, Hq, Hkv, L, i0, False, 0, vc.VC_BF16), dtype=torch.uint8,
+                         device="cuda")
+        kp = Kd if i0 else Kd[:, :, :1]
+        vc.vc_verify_attn(Qd[:, :, i0:i0 + L].contiguous(), Kd[:, :, i0:i0 + L].contiguous(),
+                          Vd[:, :, i0:i0 + L].contiguous(), kp, Vd if i0 else Vd[:, :, :1], i0, ov, None, wv,
+                          harness.SM_SCALE, past_stride=n if i0 else 1)
+        torch.cuda.synchronize()
+        assert np.abs(ov.cpu().numpy()[0] - o[0, :, i0:i0 + L]).max() < 2 * TIGHT["verify"], f"block {i0}"
+
+
 @pytest.mark.parametrize("G", [3, 5, 6, 7])
 def test_verify_group_sizes(gpu_lib, G):
     """Query heads per kv head that fill neither one 4-head workgroup exactly nor two (G = 5..7
