@@ -351,10 +351,11 @@ def _e2e_llama_batch(torch, W, prompts, tokens: int, bits: int, x: int, opts: di
     length; greedy decoding of the same batch is the baseline."""
     from kv_cache_compressed_amd.decode_loop import BatchedLlamaDecoder
 
-    out, seqs = {}, {}
+    out, seqs, margins = {}, {}, {}
     for name, xx in (("vericache", x), ("greedy", 0)):
         t0 = time.perf_counter()
-        dec = BatchedLlamaDecoder(W, 16, 4, prompts, x=xx, bits=bits, R=128, max_new=tokens + 96, **opts)
+        dec = BatchedLlamaDecoder(W, 16, 4, prompts, x=xx, bits=bits, R=128, max_new=tokens + 96,
+                                  margins=True, **opts)
         torch.cuda.synchronize()
         t_prefill = time.perf_counter() - t0
         dec.warm()
@@ -374,6 +375,7 @@ def _e2e_llama_batch(torch, W, prompts, tokens: int, bits: int, x: int, opts: di
         if xx:
             out[name]["mean_accepted"] = round(float(np.mean([a for r in dec.rounds for a in r[r0:]])), 2)
         seqs[name] = [w + g for w, g in zip(warm, gen)]
+        margins[name] = dec.margin_log
         del dec
     out["speedup"] = round(out["vericache"]["tok_s"] / out["greedy"]["tok_s"], 3)
     # two groups of half the batch each, lock-step against staggered on two streams
@@ -409,11 +411,19 @@ def _e2e_llama_batch(torch, W, prompts, tokens: int, bits: int, x: int, opts: di
         del groups, g0, g1
     two["speedup"] = round(two["staggered"]["tok_s"] / two["lockstep"]["tok_s"], 3)
     out["two_groups"] = two
+    # Token comparison with the greedy decoding of the batch: the first position where a request's
+    # tokens differ (after it the two continue from different contexts), with the top-2 logit gap
+    # of the rows both decoders chose that token from; a gap below 1e-3 is a near-tie, where two
+    # correct computations in different orders may pick different tokens.
     div = []
-    for a, b in zip(seqs["vericache"], seqs["greedy"]):
+    for r, (a, b) in enumerate(zip(seqs["vericache"], seqs["greedy"])):
         m = min(len(a), len(b))
-        div.append(next((i for i in range(m) if a[i] != b[i]), None))
-    out["first_divergence"] = div if any(d is not None for d in div) else None
+        i = next((i for i in range(m) if a[i] != b[i]), None)
+        if i is not None:
+            gap = min(margins["vericache"][r][i], margins["greedy"][r][i])
+            div.append({"request": r, "position": i, "margin": gap, "near_tie": gap < 1e-3})
+    out["first_divergence"] = [d for d in div if not d["near_tie"]] or None
+    out["near_tie_divergences"] = [d for d in div if d["near_tie"]]
     return out
 
 

@@ -19,6 +19,7 @@
  *   vc_verify_stream_copies  a host-streamed verify's copies alone (its link ceiling) (measurement)
  *   vc_lse_merge         log-sum-exp merge of split partials                  (verify / draft)
  *   vc_accept            per-row argmax, first disagreement, correction token (accept)
+ *   vc_logit_margins     top-2 logit gap per row (near-ties, for token comparisons) (harness)
  *   vc_select_keep       kept positions of a token-dropping drafter           (compressor)
  *   vc_project_logits    logits of the attention outputs (+ greedy argmax): the
  *                        single layer's stand-in for a model head              (harness)
@@ -324,6 +325,15 @@ vc_status vc_lse_merge(const float *part_o, const float *part_ml, int64_t rows, 
  */
 vc_status vc_accept(const float *logits, const int32_t *drafts, int32_t B, int32_t L, int32_t V,
                     int32_t *accept_len, int32_t *next_token, int32_t *argmax, void *stream);
+
+/*
+ * Top-2 margins of logits rows, for comparing two decodings token by token: a row whose two best
+ * logits lie within a tolerance is a near-tie, where two correct computations may pick different
+ * tokens. Not part of the round.
+ *   gap[r] = z_best - z_second over distinct indices of logits[r][0..V-1] (0 when the best value
+ *   occurs twice; +inf when V == 1); logits [rows][V] fp32 finite, gap [rows] fp32, device.
+ */
+vc_status vc_logit_margins(const float *logits, int64_t rows, int32_t V, float *gap, void *stream);
 
 /*
  * Logits projection, the round's stand-in for a model's output head (a single attention layer has

@@ -108,6 +108,43 @@ __global__ void __launch_bounds__(1024) accept_kernel(const float* __restrict__ 
   }
 }
 
+// Top-2 margin of each logits row: gap[r] = z_best - z_second over distinct indices (0 when the
+// best value occurs twice). One 256-thread workgroup per row.
+__global__ void __launch_bounds__(256) margin_kernel(const float* __restrict__ logits, int V,
+                                                     float* __restrict__ gap) {
+  __shared__ float s1[4], s2[4];
+  const float* z = logits + (int64_t)blockIdx.x * V;
+  float b1 = -INFINITY, b2 = -INFINITY;  // best and second best of this thread's elements
+  for (int i = threadIdx.x; i < V; i += 256) {
+    const float t = z[i];
+    if (t > b1) {
+      b2 = b1;
+      b1 = t;
+    } else if (t > b2) {
+      b2 = t;
+    }
+  }
+  auto merge = [](float& a1, float& a2, float c1, float c2) {
+    const float hi = fmaxf(a1, c1), lo = fminf(a1, c1);
+    a1 = hi;
+    a2 = fmaxf(lo, fmaxf(a2, c2));
+  };
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float c1 = __shfl_xor(b1, m, 64), c2 = __shfl_xor(b2, m, 64);
+    merge(b1, b2, c1, c2);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    s1[threadIdx.x >> 6] = b1;
+    s2[threadIdx.x >> 6] = b2;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a1 = s1[0], a2 = s2[0];
+    for (int w = 1; w < 4; ++w) merge(a1, a2, s1[w], s2[w]);
+    gap[blockIdx.x] = V > 1 ? a1 - a2 : INFINITY;
+  }
+}
+
 __global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     int64_t rows, int S, float* __restrict__ out,
@@ -124,6 +161,11 @@ hipError_t launch_accept(const float* logits, const int32_t* drafts, int B, int 
                          int32_t* accept_len, int32_t* next_token, int32_t* argmax, hipStream_t s) {
   hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(1024), 0, s, logits, drafts, L, V, accept_len,
                      next_token, argmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_margins(const float* logits, int64_t rows, int V, float* gap, hipStream_t s) {
+  hipLaunchKernelGGL(margin_kernel, dim3((unsigned)rows), dim3(256), 0, s, logits, V, gap);
   return hipGetLastError();
 }
 

@@ -502,6 +502,16 @@ vc_status vc_accept(const float* logits, const int32_t* drafts, int32_t B, int32
   return ok();
 }
 
+vc_status vc_logit_margins(const float* logits, int64_t rows, int32_t V, float* gap, void* stream) {
+  REQUIRE_PTR(logits);
+  REQUIRE(gap != nullptr, "gap is null");
+  REQUIRE(rows >= 1 && rows <= ((int64_t)1 << 31) - 1, "rows must be in [1, 2^31 - 1]");
+  REQUIRE(V >= 1 && V <= (1 << 30), "V must be in [1, 2^30]");
+  hipError_t e = vc::launch_margins(logits, rows, V, gap, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_logit_margins launch");
+  return ok();
+}
+
 vc_status vc_project_workspace(int32_t B, int32_t L, int32_t V, size_t* bytes) {
   REQUIRE(bytes != nullptr, "bytes is null");
   REQUIRE(B >= 1 && L >= 1 && (int64_t)B * L <= (1 << 20), "B*L must be in [1, 2^20]");

@@ -829,7 +829,7 @@ class BatchedLlamaDecoder:
     def __init__(self, weights, Hq: int, Hkv: int, prompts, x: int, bits: int = 4, R: int = 32,
                  max_new: int = 256, kv_dtype: str = "f32", host_past: bool = False,
                  chunk_tokens: int = 65536, rope_theta: float = 500000.0, copy_stream=None,
-                 fused: bool = True, graphs: bool = False, device: str = "cuda"):
+                 fused: bool = True, graphs: bool = False, margins: bool = False, device: str = "cuda"):
         assert "g_att" in weights, "Llama-form weights"
         self.E, self.Wlm = _dev(weights["E"], device), _dev(weights["Wlm"], device)
         self.g_f = _dev(weights["g_f"], device)
@@ -909,6 +909,11 @@ class BatchedLlamaDecoder:
         self.accept_len = torch.zeros((B,), **i32)
         self.next_tok = torch.zeros((B,), **i32)
         self.argmax_v = torch.zeros((B, L), **i32)
+        # margins=True: the top-2 logit gap of the row each emitted token was chosen from, per
+        # request (self.margin_log), for token-by-token comparisons with near-ties set apart
+        self.margins = margins
+        self.gap_v = torch.zeros((B, L), **f32)
+        self.margin_log = [[] for _ in range(B)]
         self.ws_draft = vc.Workspace(device)
         self.ws_verify = vc.Workspace(device)
         self.vring = [vc.Workspace(device) for _ in range(self.VRING)] if host_past else []
@@ -1066,6 +1071,8 @@ class BatchedLlamaDecoder:
         vc.vc_project_logits(self.Wlm, h, logits=self.logits_v)
         drafts = self.tok[:, 1:L].contiguous() if L > 1 else None
         vc.vc_accept(self.logits_v, drafts, self.accept_len, self.next_tok, self.argmax_v)
+        if self.margins:
+            vc.vc_logit_margins(self.logits_v, self.gap_v)
 
     def commit(self):
         """Per request: keep entries 0..a_b (the verifier's keys/values) in the full caches and the
@@ -1074,10 +1081,13 @@ class BatchedLlamaDecoder:
         acc = self.accept_len.tolist()
         nxt = self.next_tok.tolist()
         toks = self.tok.tolist()
+        gaps = self.gap_v.tolist() if self.margins else None
         L, out = self.L, []
         for b in range(self.B):
             a = acc[b]
             out.append(toks[b][1:a + 1] + [nxt[b]])
+            if gaps is not None:
+                self.margin_log[b] += gaps[b][:a + 1]
             n0 = self.n[b]
             assert n0 + a + 1 + L <= self.cap, "cache capacity exhausted (raise max_new)"
             for l in range(self.nl):

@@ -62,6 +62,7 @@ _SIGS = {
     "vc_verify_prefetch": [_P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P],
     "vc_lse_merge": [_P, _P, _I64, _I32, _I32, _P, _P, _P],
     "vc_accept": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
+    "vc_logit_margins": [_P, _I64, _I32, _P, _P],
     "vc_project_workspace": [_I32, _I32, _I32, ctypes.POINTER(_SZ)],
     "vc_project_logits": [_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _SZ, _P],
     "vc_select_keep": [_P, _I64, _I32, _I64, _I64, _I64, _I64, _P, _I64, ctypes.POINTER(_I64), _P],
@@ -361,6 +362,15 @@ def vc_accept(logits, drafts, accept_len, next_token, argmax=None, stream=None):
     B, L, V = logits.shape
     _check(lib().vc_accept(_ptr(logits), _ptr(drafts), B, L, V, _ptr(accept_len), _ptr(next_token),
                            _ptr(argmax), _stream(stream)))
+
+
+def vc_logit_margins(logits, gap, stream=None):
+    """gap[r] = best - second best of logits row r (logits [..., V] fp32 contiguous; gap has one
+    entry per row)."""
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    assert logits.is_contiguous() and gap.numel() == rows and gap.dtype == torch.float32
+    _check(lib().vc_logit_margins(_ptr(logits), rows, V, _ptr(gap), _stream(stream)))
 
 
 def vc_project_workspace(B: int, L: int, V: int) -> int:

@@ -306,6 +306,13 @@ def test_prefill_rejects_and_sizes(L):
     assert L.vc_prefill_workspace(1, 16, 4, 0, ctypes.byref(one)) == vc.VC_ERR_INVALID
 
 
+def test_logit_margins_rejects(L):
+    assert L.vc_logit_margins(P, 0, 10, P, None) == vc.VC_ERR_INVALID
+    assert L.vc_logit_margins(P, 4, 0, P, None) == vc.VC_ERR_INVALID
+    assert L.vc_logit_margins(None, 4, 10, P, None) == vc.VC_ERR_INVALID
+    assert L.vc_logit_margins(P, 4, 10, None, None) == vc.VC_ERR_INVALID
+
+
 def test_stream_copies_rejects(L):
     """Argument checks of the copy-only transfer (all before any HIP call)."""
     call = lambda **a: L.vc_verify_stream_copies(

@@ -95,6 +95,26 @@ def test_accept_worked_example(gpu_lib):
     assert am.cpu().numpy()[0].tolist() == verified
 
 
+@pytest.mark.parametrize("rows,V", [(7, 32000), (3, 1), (5, 2), (40, 1000)])
+def test_logit_margins(gpu_lib, rows, V):
+    """Top-2 gap per row against numpy: random rows, a row whose best value occurs twice (gap 0)
+    and a row with a planted gap."""
+    g = np.random.default_rng(rows * 7 + V)
+    z = g.standard_normal((rows, V)).astype(np.float32)
+    if V > 1:
+        z[0, V // 3] = z[0, V - 1] = z[0].max() + 1.0          # tie for the best value
+        if rows > 1:
+            z[1, 0] = z[1].max() + np.float32(0.25)             # planted gap
+    gap = torch.full((rows,), float("nan"), device="cuda")
+    vc.vc_logit_margins(torch.from_numpy(z).cuda(), gap)
+    torch.cuda.synchronize()
+    srt = np.sort(z, axis=1)
+    ref = srt[:, -1] - srt[:, -2] if V > 1 else np.full(rows, np.inf, np.float32)
+    assert np.array_equal(gap.cpu().numpy(), ref.astype(np.float32))
+    if V > 1:
+        assert gap[0].item() == 0.0
+
+
 @pytest.mark.parametrize("B,L,V", [(1, 9, 2048), (8, 31, 2048), (16, 31, 32000), (3, 5, 2047), (8, 1, 2048),
                                    (2, 3, 1000), (4, 16, 4096), (2, 17, 333), (1, 64, 512)])
 def test_accept_random(gpu_lib, B, L, V):
