@@ -115,6 +115,9 @@ class _Store:
         if host:
             self.k = torch.empty((1, Hkv, cap, D), dtype=dtype, pin_memory=True)
             self.v = torch.empty_like(self.k, pin_memory=True)
+            # CPU views of the same memory (16-bit rows as int16), for host-side row copies
+            raw = (lambda t: t.view(torch.int16)) if dtype.itemsize == 2 else (lambda t: t)
+            self.k_np, self.v_np = raw(self.k).numpy(), raw(self.v).numpy()
         else:
             self.k = torch.zeros((1, Hkv, cap, D), dtype=dtype, device=device)
             self.v = torch.zeros_like(self.k)
@@ -902,6 +905,14 @@ class BatchedLlamaDecoder:
         self.qv = torch.zeros((B, Hq, L, D), **tk)
         self.kv_ = [torch.zeros((B, Hkv, L, D), **tk) for _ in range(nl)]  # verifier's k, v
         self.vv_ = [torch.zeros((B, Hkv, L, D), **tk) for _ in range(nl)]
+        # host stores: the round's block rows reach pinned staging in one copy per layer and
+        # tensor, then the kept rows go to each request's store by CPU slice copies (int16 views of
+        # the bf16 rows), instead of two synchronous device-to-host copies per (request, layer)
+        if host_past:
+            pin = lambda: torch.empty((B, Hkv, L, D), dtype=self.tdt, pin_memory=True)
+            self.stage_k, self.stage_v = [pin() for _ in range(nl)], [pin() for _ in range(nl)]
+            i16 = lambda t: t.view(torch.int16).numpy()
+            self.stage_np = [(i16(k), i16(v)) for k, v in zip(self.stage_k, self.stage_v)]
         self.ov = torch.zeros((B, Hq, L, D), **f32)
         self.lse_v = torch.zeros((B, Hq, L), **f32)
         self.logits_v = torch.zeros((B, L, self.V), **f32)
@@ -1078,6 +1089,10 @@ class BatchedLlamaDecoder:
         """Per request: keep entries 0..a_b (the verifier's keys/values) in the full caches and the
         residual rings, flush whole groups, start the next round from the emitted token. Returns
         each request's emitted tokens."""
+        if self.host:  # every layer's block rows to pinned staging (complete at the sync below)
+            for l in range(self.nl):
+                self.stage_k[l].copy_(self.kv_[l], non_blocking=True)
+                self.stage_v[l].copy_(self.vv_[l], non_blocking=True)
         acc = self.accept_len.tolist()
         nxt = self.next_tok.tolist()
         toks = self.tok.tolist()
@@ -1092,7 +1107,12 @@ class BatchedLlamaDecoder:
             assert n0 + a + 1 + L <= self.cap, "cache capacity exhausted (raise max_new)"
             for l in range(self.nl):
                 k, v = self.kv_[l][b:b + 1, :, :a + 1], self.vv_[l][b:b + 1, :, :a + 1]
-                self.stores[b][l].write(n0, k, v)
+                if self.host:
+                    st, (sk, sv) = self.stores[b][l], self.stage_np[l]
+                    st.k_np[0, :, n0:n0 + a + 1] = sk[b, :, :a + 1]
+                    st.v_np[0, :, n0:n0 + a + 1] = sv[b, :, :a + 1]
+                else:
+                    self.stores[b][l].write(n0, k, v)
                 vc.vc_kivi_append(self.caches[l].row(b), k, v, n0, a + 1, src_bh_stride=L * D)
             self.n[b] = n0 + a + 1
             while self.n[b] - self.n_q[b] >= self.R + 32:
