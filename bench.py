@@ -122,6 +122,35 @@ def _h2d_rate(torch, vc, st, passes: int = 10) -> dict:
     return {"bytes": nbytes, "seconds": t, "GB_s": nbytes / t / 1e9, "passes": passes}
 
 
+def _read_stream(torch, vc, nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """HBM read ceiling: vc_hbm_read_stream over a 1 GiB buffer (4x the 256 MB last-level cache),
+    timed with HIP events on the launch stream, median of `reps` launches, at 384, 512 and 768
+    workgroups (the plain read is fastest at about two workgroups per CU and falls to ~5.1 TB/s
+    from 1024 up); the best of the three."""
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    sink = torch.empty(768 * 256, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    best = None
+    for blocks in (384, 512, 768):
+        for _ in range(2):
+            vc.vc_hbm_read_stream(buf, sink, blocks)
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            vc.vc_hbm_read_stream(buf, sink, blocks)
+            e1.record(s)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        t = float(np.median(times))
+        if best is None or t < best[0]:
+            best = (t, blocks)
+    del buf
+    t, blocks = best
+    return {"GB_s": round(nbytes / t / 1e9, 1), "bytes": nbytes, "us": round(t * 1e6, 1), "reps": reps,
+            "workgroups": blocks, "kernel": "vc_hbm_read_stream (16-byte loads, XOR-folded)"}
+
+
 def _staggering(torch, harness, synth, st0, seed: int, rounds: int) -> dict:
     """Two request groups of the host-streamed workload (the second drawn with seed + 1): round
     time of the lock-step schedule (all groups draft, then all verify) against the staggered one
@@ -760,6 +789,8 @@ def main():
         "round": {"accepted": [int(a) for a in res["a"]], "emitted_per_round": a_plus_1,
                   "positions_verified_per_s": round(w.B * w.L / (elapsed / args.steps), 1)},
     }
+    rs = _read_stream(torch, vc)
+    line["roofline"]["read_stream"] = dict(rs, frac=round(achieved / rs["GB_s"], 4))
     if h2d is not None:
         v_gbs_pcie = st.verify_bytes() / v_mean_s / 1e9
         line["verify_attention"]["pcie"] = {

@@ -20,6 +20,7 @@
  *   vc_lse_merge         log-sum-exp merge of split partials                  (verify / draft)
  *   vc_accept            per-row argmax, first disagreement, correction token (accept)
  *   vc_logit_margins     top-2 logit gap per row (near-ties, for token comparisons) (harness)
+ *   vc_hbm_read_stream   a plain streaming read (the HBM read ceiling)           (measurement)
  *   vc_select_keep       kept positions of a token-dropping drafter           (compressor)
  *   vc_project_logits    logits of the attention outputs (+ greedy argmax): the
  *                        single layer's stand-in for a model head              (harness)
@@ -334,6 +335,15 @@ vc_status vc_accept(const float *logits, const int32_t *drafts, int32_t B, int32
  *   occurs twice; +inf when V == 1); logits [rows][V] fp32 finite, gap [rows] fp32, device.
  */
 vc_status vc_logit_margins(const float *logits, int64_t rows, int32_t V, float *gap, void *stream);
+
+/*
+ * Plain streaming read of `bytes` of device memory (measurement: the HBM read rate a
+ * bandwidth-bound kernel is set against, beside the 8 TB/s peak; not part of the round).
+ * `blocks` workgroups of 256 threads stride over src with 16-byte loads and each thread writes
+ * the XOR of what it read to sink[blocks * 256] (uint32, device), so every load is kept.
+ * bytes a positive multiple of 16, src 16-byte aligned, 1 <= blocks <= 65536.
+ */
+vc_status vc_hbm_read_stream(const void *src, size_t bytes, uint32_t *sink, int32_t blocks, void *stream);
 
 /*
  * Logits projection, the round's stand-in for a model's output head (a single attention layer has

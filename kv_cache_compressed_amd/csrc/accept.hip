@@ -145,6 +145,25 @@ __global__ void __launch_bounds__(256) margin_kernel(const float* __restrict__ l
   }
 }
 
+// Plain streaming read of n16 16-byte words (the HBM read ceiling a bandwidth-bound kernel is
+// compared with): workgroups stride over the buffer with four 16-byte loads per thread in flight,
+// fold what they read with XOR and write one word per thread, so no load can be dropped.
+__global__ void __launch_bounds__(256) read_stream_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 __global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     int64_t rows, int S, float* __restrict__ out,
@@ -166,6 +185,12 @@ hipError_t launch_accept(const float* logits, const int32_t* drafts, int B, int 
 
 hipError_t launch_margins(const float* logits, int64_t rows, int V, float* gap, hipStream_t s) {
   hipLaunchKernelGGL(margin_kernel, dim3((unsigned)rows), dim3(256), 0, s, logits, V, gap);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_stream(const void* src, int64_t n16, uint32_t* sink, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL(read_stream_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const uint4*>(src), n16, sink);
   return hipGetLastError();
 }
 

@@ -512,6 +512,17 @@ vc_status vc_logit_margins(const float* logits, int64_t rows, int32_t V, float* 
   return ok();
 }
 
+vc_status vc_hbm_read_stream(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream) {
+  REQUIRE_PTR(src);
+  REQUIRE(sink != nullptr, "sink is null");
+  REQUIRE(bytes >= 16 && bytes % 16 == 0, "bytes must be a positive multiple of 16");
+  REQUIRE(blocks >= 1 && blocks <= 65536, "blocks must be in [1, 65536]");
+  hipError_t e = vc::launch_read_stream(src, (int64_t)(bytes / 16), sink, blocks,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "vc_hbm_read_stream launch");
+  return ok();
+}
+
 vc_status vc_project_workspace(int32_t B, int32_t L, int32_t V, size_t* bytes) {
   REQUIRE(bytes != nullptr, "bytes is null");
   REQUIRE(B >= 1 && L >= 1 && (int64_t)B * L <= (1 << 20), "B*L must be in [1, 2^20]");

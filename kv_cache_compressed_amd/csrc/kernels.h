@@ -14,6 +14,7 @@ hipError_t launch_append(const vc_kivi& c, const void* k, const void* v, int src
                          int64_t src_bh_stride, int64_t t0, int64_t ntok, hipStream_t s);
 
 hipError_t launch_margins(const float* logits, int64_t rows, int V, float* gap, hipStream_t s);
+hipError_t launch_read_stream(const void* src, int64_t n16, uint32_t* sink, int blocks, hipStream_t s);
 hipError_t launch_accept(const float* logits, const int32_t* drafts, int B, int L, int V,
                          int32_t* accept_len, int32_t* next_token, int32_t* argmax, hipStream_t s);
 

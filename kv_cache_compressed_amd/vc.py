@@ -63,6 +63,7 @@ _SIGS = {
     "vc_lse_merge": [_P, _P, _I64, _I32, _I32, _P, _P, _P],
     "vc_accept": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
     "vc_logit_margins": [_P, _I64, _I32, _P, _P],
+    "vc_hbm_read_stream": [_P, _SZ, _P, _I32, _P],
     "vc_project_workspace": [_I32, _I32, _I32, ctypes.POINTER(_SZ)],
     "vc_project_logits": [_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _SZ, _P],
     "vc_select_keep": [_P, _I64, _I32, _I64, _I64, _I64, _I64, _P, _I64, ctypes.POINTER(_I64), _P],
@@ -371,6 +372,14 @@ def vc_logit_margins(logits, gap, stream=None):
     rows = logits.numel() // V
     assert logits.is_contiguous() and gap.numel() == rows and gap.dtype == torch.float32
     _check(lib().vc_logit_margins(_ptr(logits), rows, V, _ptr(gap), _stream(stream)))
+
+
+def vc_hbm_read_stream(src, sink, blocks: int, stream=None):
+    """Read all of `src` (device tensor, bytes a multiple of 16) once; sink: int32 device tensor of
+    blocks * 256 entries."""
+    nbytes = src.numel() * src.element_size()
+    assert sink.numel() >= blocks * 256
+    _check(lib().vc_hbm_read_stream(_ptr(src), nbytes, _ptr(sink), blocks, _stream(stream)))
 
 
 def vc_project_workspace(B: int, L: int, V: int) -> int:

@@ -306,6 +306,14 @@ def test_prefill_rejects_and_sizes(L):
     assert L.vc_prefill_workspace(1, 16, 4, 0, ctypes.byref(one)) == vc.VC_ERR_INVALID
 
 
+def test_read_stream_rejects(L):
+    assert L.vc_hbm_read_stream(P, 0, P, 4, None) == vc.VC_ERR_INVALID
+    assert L.vc_hbm_read_stream(P, 24, P, 4, None) == vc.VC_ERR_INVALID
+    assert L.vc_hbm_read_stream(P, 32, P, 0, None) == vc.VC_ERR_INVALID
+    assert L.vc_hbm_read_stream(BAD, 32, P, 4, None) == vc.VC_ERR_INVALID
+    assert L.vc_hbm_read_stream(P, 32, None, 4, None) == vc.VC_ERR_INVALID
+
+
 def test_logit_margins_rejects(L):
     assert L.vc_logit_margins(P, 0, 10, P, None) == vc.VC_ERR_INVALID
     assert L.vc_logit_margins(P, 4, 0, P, None) == vc.VC_ERR_INVALID

@@ -1508,6 +1508,18 @@ def test_decoder_gemv_shared_workspace(gpu_lib):
     assert not shared[:16384].any()
 
 
+def test_hbm_read_stream_reads_every_word(gpu_lib):
+    """The read-ceiling kernel reads every 16-byte word exactly once: the XOR of its sink equals
+    the XOR of the buffer (odd sizes leave a ragged tail per stride)."""
+    g = np.random.default_rng(5)
+    for n16, blocks in ((1, 1), (1000, 3), (123457, 64)):
+        x = g.integers(0, 2 ** 31, n16 * 4).astype(np.int32)
+        sink = torch.zeros(blocks * 256, dtype=torch.int32, device="cuda")
+        vc.vc_hbm_read_stream(torch.from_numpy(x).cuda(), sink, blocks)
+        torch.cuda.synchronize()
+        assert np.bitwise_xor.reduce(sink.cpu().numpy()) == np.bitwise_xor.reduce(x), (n16, blocks)
+
+
 def test_embed_rows(gpu_lib):
     """Embedding rows of one block entry of every request (a strided id view): rows of E, and an id
     outside the vocabulary gives a zero row."""
