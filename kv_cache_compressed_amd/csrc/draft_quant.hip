@@ -529,11 +529,23 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+// Max over the row for values that are never NaN (scores: finite, or -inf for no token): four
+// DPP-operand maxima. Written out because the fmaxf form compiles to a DPP move, a quieting max
+// and the max per step (12 instructions); each DPP read of a register a vector instruction just
+// wrote needs two wait states (the s_nop 1).
 __device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_mov<0x124>(x));  // row_ror:4
-  return fmaxf(x, dpp_mov<0x128>(x));  // row_ror:8
+  float y;
+  asm("s_nop 1\n\t"
+      "v_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf"
+      : "=&v"(y)
+      : "v"(x));
+  return y;
 }
 __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_mov<0xB1>(x);
