@@ -328,6 +328,7 @@ struct PendingPrefetch {
   const void* v;
   int64_t stride, n, chunk;
   int32_t B, Hq, Hkv, L;
+  hipEvent_t done;  // recorded on the copy stream right after the prefetch's copies
   bool operator==(const PendingPrefetch& o) const {
     return ws == o.ws && k == o.k && v == o.v && stride == o.stride && n == o.n && chunk == o.chunk &&
            B == o.B && Hq == o.Hq && Hkv == o.Hkv && L == o.L;
@@ -336,12 +337,17 @@ struct PendingPrefetch {
 std::mutex g_prefetch_mu;
 std::vector<PendingPrefetch> g_prefetch;
 
-// Removes the record of workspace ws; returns whether it equalled `want` (when given).
-bool take_prefetch(const void* ws, const PendingPrefetch* want) {
+// Removes the record of workspace ws; returns whether it equalled `want` (when given). On a match
+// the record's event passes to *done (the caller destroys it); otherwise it is destroyed here.
+bool take_prefetch(const void* ws, const PendingPrefetch* want, hipEvent_t* done = nullptr) {
   std::lock_guard<std::mutex> lock(g_prefetch_mu);
   for (size_t i = 0; i < g_prefetch.size(); ++i) {
     if (g_prefetch[i].ws != ws) continue;
     const bool match = want && g_prefetch[i] == *want;
+    if (match && done)
+      *done = g_prefetch[i].done;
+    else if (g_prefetch[i].done)
+      (void)hipEventDestroy(g_prefetch[i].done);
     g_prefetch.erase(g_prefetch.begin() + i);
     return match;
   }
@@ -383,12 +389,13 @@ vc_status vc_verify_prefetch(const void* k_past, const void* v_past, int64_t pas
     return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,
                 ws ? ws_bytes : (size_t)0);
   (void)take_prefetch(ws, nullptr);
+  hipEvent_t done = nullptr;
   hipError_t e = vc::launch_verify_prefetch(k_past, v_past, past_stride, n, B, Hkv, ws, plan,
                                             static_cast<hipStream_t>(compute_stream),
-                                            static_cast<hipStream_t>(copy_stream));
+                                            static_cast<hipStream_t>(copy_stream), &done);
   if (e != hipSuccess) return hip_fail(e, "vc_verify_prefetch");
   std::lock_guard<std::mutex> lock(g_prefetch_mu);
-  g_prefetch.push_back({ws, k_past, v_past, past_stride, n, chunk_tokens, B, Hq, Hkv, L});
+  g_prefetch.push_back({ws, k_past, v_past, past_stride, n, chunk_tokens, B, Hq, Hkv, L, done});
   return ok();
 }
 
@@ -462,13 +469,19 @@ vc_status vc_verify_attn(const void* q, const void* k_blk, const void* v_blk, in
     return fail(VC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", plan.ws_bytes,
                 ws ? ws_bytes : (size_t)0);
   // a verify on this workspace consumes (or, without VC_PAST_HOST_PREFETCHED, discards) its prefetch
-  const PendingPrefetch want{ws, k_past, v_past, past_stride, n, chunk_tokens, B, Hq, Hkv, L};
-  if (!take_prefetch(ws, &want) && past_on_host == VC_PAST_HOST_PREFETCHED)
+  const PendingPrefetch want{ws, k_past, v_past, past_stride, n, chunk_tokens, B, Hq, Hkv, L, nullptr};
+  hipEvent_t prefetched = nullptr;
+  if (!take_prefetch(ws, &want, &prefetched) && past_on_host == VC_PAST_HOST_PREFETCHED)
     return fail(VC_ERR_INVALID, "VC_PAST_HOST_PREFETCHED without a matching vc_verify_prefetch on this workspace");
+  if (past_on_host != VC_PAST_HOST_PREFETCHED && prefetched) {  // a prefetch this call does not use
+    (void)hipEventDestroy(prefetched);
+    prefetched = nullptr;
+  }
   hipError_t e = vc::launch_verify(q, k_blk, v_blk, L, k_past, v_past, past_stride, n, past_on_host,
                                    dtype, B, Hq, Hkv, sm_scale, out, lse, ws, plan,
                                    static_cast<hipStream_t>(compute_stream),
-                                   static_cast<hipStream_t>(copy_stream));
+                                   static_cast<hipStream_t>(copy_stream), prefetched);
+  if (prefetched) (void)hipEventDestroy(prefetched);  // the wait on it is enqueued
   if (e != hipSuccess) return hip_fail(e, "vc_verify_attn");
   return ok();
 }

@@ -88,11 +88,13 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
                          const void* k_past, const void* v_past, int64_t past_stride, int64_t n,
                          int past_on_host, int dtype, int B, int Hq, int Hkv, float sm_scale,
                          float* out, float* lse, void* ws, const VerifyPlan& plan,
-                         hipStream_t compute, hipStream_t copy);
-// Copies of the first two streamed chunks into the workspace stages (past_on_host == 1 plan).
+                         hipStream_t compute, hipStream_t copy, hipEvent_t prefetched);
+// Copies of the first two streamed chunks into the workspace stages (past_on_host == 1 plan);
+// *done is recorded on `copy` right after them (the caller owns it: the verify that consumes the
+// prefetch waits on it, so it never waits for copies enqueued later for other calls).
 hipError_t launch_verify_prefetch(const void* k_past, const void* v_past, int64_t past_stride,
                                   int64_t n, int B, int Hkv, void* ws, const VerifyPlan& plan,
-                                  hipStream_t compute, hipStream_t copy);
+                                  hipStream_t compute, hipStream_t copy, hipEvent_t* done);
 
 // Every chunk copy of a host-streamed verify (chunk c into stage c % 2), with no compute.
 hipError_t launch_verify_copies(const void* k_past, const void* v_past, int64_t past_stride,

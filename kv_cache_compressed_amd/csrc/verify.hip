@@ -623,7 +623,8 @@ hipError_t copy_chunk(const void* k_past, const void* v_past, int64_t past_strid
 
 hipError_t launch_verify_prefetch(const void* k_past, const void* v_past, int64_t past_stride,
                                   int64_t n, int B, int Hkv, void* ws, const VerifyPlan& plan,
-                                  hipStream_t compute, hipStream_t copy) {
+                                  hipStream_t compute, hipStream_t copy, hipEvent_t* done) {
+  *done = nullptr;
   const int64_t units = (int64_t)B * Hkv;
   uint16_t* stage_k[2];
   uint16_t* stage_v[2];
@@ -636,6 +637,12 @@ hipError_t launch_verify_prefetch(const void* k_past, const void* v_past, int64_
   for (int c = 0; c < std::min(2, plan.chunks) && err == hipSuccess; ++c)
     err = copy_chunk(k_past, v_past, past_stride, n, units, plan, c, stage_k[c], stage_v[c], copy);
   (void)hipEventDestroy(start);
+  if (err == hipSuccess) err = hipEventCreateWithFlags(done, hipEventDisableTiming);
+  if (err == hipSuccess) err = hipEventRecord(*done, copy);
+  if (err != hipSuccess && *done) {
+    (void)hipEventDestroy(*done);
+    *done = nullptr;
+  }
   return err;
 }
 
@@ -712,7 +719,7 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
                          const void* k_past, const void* v_past, int64_t past_stride, int64_t n,
                          int past_on_host, int dtype, int B, int Hq, int Hkv, float sm_scale,
                          float* out, float* lse, void* ws, const VerifyPlan& plan,
-                         hipStream_t compute, hipStream_t copy) {
+                         hipStream_t compute, hipStream_t copy, hipEvent_t prefetched) {
   const size_t rows = (size_t)B * Hq * L;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + rows * plan.total_splits * D;
@@ -806,9 +813,9 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
     // the copy stream must not overwrite stages before earlier work on `compute` is ordered
     err = hipEventRecord(start, compute);
     if (err == hipSuccess) err = hipStreamWaitEvent(copy, start, 0);
-    // prefetched chunks: `compute` waits for everything on `copy` so far
-    if (first > 0 && err == hipSuccess) err = hipEventRecord(ready[0], copy);
-    if (first > 0 && err == hipSuccess) err = hipStreamWaitEvent(compute, ready[0], 0);
+    // prefetched chunks: `compute` waits for the prefetch's own copies (recorded right after
+    // them), not for whatever later calls have queued on `copy` since
+    if (first > 0 && err == hipSuccess) err = hipStreamWaitEvent(compute, prefetched, 0);
     for (int c = 0; c < plan.chunks && err == hipSuccess; ++c) {
       const int z = c % 2;
       const int64_t t0 = (int64_t)c * plan.chunk_tokens;
@@ -832,9 +839,8 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
       if ((err = hipGetLastError()) != hipSuccess) break;
       err = hipEventRecord(done[z], compute);
     }
-    // make `compute` wait for the copy stream's last command (covers every copy)
-    if (err == hipSuccess) err = hipEventRecord(ready[0], copy);
-    if (err == hipSuccess) err = hipStreamWaitEvent(compute, ready[0], 0);
+    // every copy of this call is now behind a wait on `compute`: the prefetched chunks behind
+    // `prefetched`, each later chunk behind its ready event before its kernel
     for (int z = 0; z < 2; ++z) {
       (void)hipEventDestroy(ready[z]);
       (void)hipEventDestroy(done[z]);
