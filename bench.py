@@ -343,7 +343,9 @@ def _e2e_decode(torch, seed: int, context: int, tokens: int) -> dict:
     from kv_cache_compressed_amd import harness
 
     prompt2 = torch.randint(0, V, (context,), generator=g, device=dev).tolist()
-    rounds = max(1, tokens // 31)
+    # at least 12 rounds: with fewer, the start (both requests' first draft phases before any
+    # verify) weighs on the per-round time as much as the schedule does
+    rounds = max(12, tokens // 31)
 
     def pair():
         d0 = TokenDecoder(W, Hq, Hkv, prompt, x=30, bits=4, R=128, max_new=rounds * 31 + 64, **opts)
