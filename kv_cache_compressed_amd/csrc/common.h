@@ -309,16 +309,19 @@ __device__ __forceinline__ void merge_row_wave(const float* __restrict__ part_o,
           l += w * ml.y;
         }
       }
-      // four splits per step, loads in flight together; steps past the last split read split
-      // S - 1 again with the weight 0 that lanes past S hold
+      // sixteen splits per step, their loads in flight together; steps past the last split read
+      // split S - 1 again with the weight 0 that lanes past S hold
       const int n = min(64, S - s0);
-      for (int i = 0; i < n; i += 4) {
+      for (int i = 0; i < n; i += 16) {
+        float2 po[16];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 16; ++u)
+          po[u] = load_f32x2<COHERENT>(part_o + (int64_t)min(s0 + i + u, S - 1) * D + 2 * lane);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
           const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i + u));
-          const float2 po = load_f32x2<COHERENT>(part_o + (int64_t)min(s0 + i + u, S - 1) * D + 2 * lane);
-          o0 += wi * po.x;
-          o1 += wi * po.y;
+          o0 += wi * po[u].x;
+          o1 += wi * po[u].y;
         }
       }
     }
