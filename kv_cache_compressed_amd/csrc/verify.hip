@@ -38,6 +38,9 @@ constexpr int NHF = TK / 32;       // 32-token PV contraction blocks per tile
 constexpr int WG_PER_CU = 3;       // resident workgroups per CU (waves per SIMD for G <= 4)
 constexpr int RING = 3;            // tile stages per workgroup (RING - 1 in flight)
 constexpr int TILE_BYTES = TK * D * 2;  // one tile of keys (or values), bf16
+constexpr int NUM_CUS = 256;
+// Relative tile share of a workgroup by dispatch tier (see tile_start), in hundredths.
+constexpr int TIER_W0 = 105, TIER_W1 = 100, TIER_W2 = 95;
 
 struct VArgs {
   const uint16_t* q;       // [B][Hq][L][D] bf16
@@ -56,6 +59,7 @@ struct VArgs {
                            //   workgroups per (b, kv head) and tile range, heads 4 z .. 4 z + 3)
   int gsplits, units, gz;  // logical grid: gsplits tile ranges x units (b, kv head) x gz head slices
                            //   (the launch is one-dimensional; see logical_block)
+  int tiered;              // one resident round (not prefill): unit fastest, shares by tier
   float qscale;            // sm_scale * log2(e)
   float* part_o;
   float* part_ml;
@@ -153,10 +157,38 @@ __device__ __forceinline__ LogicalBlock logical_block(const VArgs& a) {
   }
   LogicalBlock lb;
   lb.live = P < a.gsplits * a.units;
-  lb.split = P % a.gsplits;
-  lb.unit = P / a.gsplits;
+  if (a.tiered) {  // consecutive pairs take the same split of consecutive units
+    lb.split = P / a.units;
+    lb.unit = P % a.units;
+  } else {
+    lb.split = P % a.gsplits;
+    lb.unit = P / a.gsplits;
+  }
   lb.z = z;
   return lb;
+}
+
+// First tile of split s (of nsplit) of a unit's ntiles. Untiered: equal shares. Tiered (the grid
+// fits one resident round): the hardware deals workgroups W < 256 to the CUs' first slots, then
+// the second, then the third, and a later tier starts its copies behind the earlier tiers' and
+// its waves issue behind older ones (its loop ran ~11% longer on equal work); pair P = s * units
+// + unit is in tier W / 256 = P / (256 / gz), so every unit's splits cover all tiers and a split's
+// share follows its tier's weight. The ranges depend on the launch shape only (deterministic).
+__device__ int tile_start(const VArgs& a, int unit, int s, int nsplit, int ntiles) {
+  if (!a.tiered) return (int)((int64_t)ntiles * s / nsplit);
+  const int w[3] = {TIER_W0, TIER_W1, TIER_W2};
+  const int per = NUM_CUS / a.gz;  // pairs per tier
+  int64_t cum = 0, tot = 0;
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int lo = per * t - unit, hi = per * (t + 1) - unit;
+    const int f0 = t == 0 ? 0 : min(nsplit, max(0, (lo + a.units - 1) / a.units));
+    const int f1 = t == 2 ? nsplit : min(nsplit, max(0, (hi + a.units - 1) / a.units));
+    const int n = max(0, f1 - f0);
+    tot += (int64_t)w[t] * n;
+    cum += (int64_t)w[t] * min(n, max(0, s - f0));
+  }
+  return tot > 0 ? (int)((int64_t)ntiles * cum / tot) : 0;
 }
 
 // Workgroup = NW waves on one (b, kv head), heads Gw z .. Gw z + Gw - 1 of its group (z: the
@@ -202,8 +234,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW
 
   // tile range of this split
   const int ntiles = (int)((src_ntok + TK - 1) / TK);  // < 2^18: src_ntok * 256 bytes < 2^31
-  const int t_begin = (int)((int64_t)ntiles * split / src_splits);
-  const int t_end = (int)((int64_t)ntiles * (split + 1) / src_splits);
+  const int t_begin = blk ? 0 : tile_start(a, lb.unit, split, src_splits, ntiles);
+  const int t_end = blk ? ntiles : tile_start(a, lb.unit, split + 1, src_splits, ntiles);
   unsigned voff[COPY_PER_WAVE<NW>];
   tile_offsets<NW>(voff);
   const int nbytes = (int)(src_ntok * D * 2);  // this (b, kv head)'s source rows
@@ -707,6 +739,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, int64_t k
   a.units = a.bh_units * a.rblocks;
   a.gz = gz;
   a.gsplits = plan.splits;
+  a.tiered = 0;  // row blocks go out heaviest first (split fastest)
   unsigned wgs = (unsigned)(a.gsplits * a.units * gz);
   if (gz == 2) wgs = (wgs + 15) / 16 * 16;  // whole groups of 16 (see logical_block)
   hipLaunchKernelGGL((verify_bf16_kernel<NW, true>), dim3(wgs), dim3(64 * NW), 0, s, a);
@@ -775,6 +808,7 @@ hipError_t launch_verify(const void* q, const void* k_blk, const void* v_blk, in
     a.gsplits = (int)grid.x;
     unsigned n = grid.x * grid.y * grid.z;
     if (gz == 2) n = (n + 15) / 16 * 16;  // whole groups of 16 (see logical_block)
+    a.tiered = n <= (unsigned)(NUM_CUS * WG_PER_CU);
     hipLaunchKernelGGL((verify_bf16_kernel<NW, false>), dim3(n), block, 0, compute, a);
   };
 
