@@ -178,6 +178,37 @@ __device__ __forceinline__ float sum_over_rows(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// Recursive-halving reduction of S * 2 values per lane across the 64 lanes of a wave (S = 32: 64
+// values): after the step of lane bit b (S = 2^b), a lane keeps the half of its values selected by
+// that bit, summed with its partner's copy of the same half; lane l ends with the wave total of
+// value l. No LDS: the bit-5 and bit-4 steps exchange whole registers between wave halves / odd
+// and even rows (permlane32_swap / permlane16_swap: after swapping (r[i], r[i + S]) a lane holds
+// its own and its partner's copy of the half it keeps, so one add finishes the step); the bit-3 ..
+// bit-0 steps read the partner through DPP (row_mirror pairs lanes l and 15 - l, row_half_mirror
+// l and 7 - l, quad permutes l ^ 2 and l ^ 1: each pair differs in the step's bit and agrees in
+// the bits above it, which is all a halving step needs).
+template <int S>
+__device__ __forceinline__ void wave_halve(float* r, int lane) {
+  if constexpr (S >= 16) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const auto p = S == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(r[i]), __float_as_uint(r[i + S]), false, false)
+                             : __builtin_amdgcn_permlane16_swap(__float_as_uint(r[i]), __float_as_uint(r[i + S]), false, false);
+      r[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    wave_halve<S / 2>(r, lane);
+  } else if constexpr (S >= 1) {
+    constexpr int CTRL = S == 8 ? 0x140 : S == 4 ? 0x141 : S == 2 ? 0x4E : 0xB1;
+    const bool up = lane & S;
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const float send = up ? r[i] : r[i + S];
+      const float keep = up ? r[i + S] : r[i];
+      r[i] = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xF, 0xF, false));
+    }
+    wave_halve<S / 2>(r, lane);
+  }
+}
 __device__ __forceinline__ float wave_max(float x) {
   for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, shfl_xor(x, m));
   return x;

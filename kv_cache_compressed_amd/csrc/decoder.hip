@@ -77,20 +77,6 @@ __device__ __forceinline__ f32x4 w4(const void* row, int k) {
   }
 }
 
-template <int S>
-__device__ __forceinline__ void halve(float* r, int lane) {
-  if constexpr (S >= 1) {
-    const bool up = lane & S;
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-      const float send = up ? r[i] : r[i + S];
-      const float keep = up ? r[i + S] : r[i];
-      r[i] = keep + __shfl_xor(send, S, 64);
-    }
-    halve<S / 2>(r, lane);
-  }
-}
-
 __device__ __forceinline__ uint16_t bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);  // finite inputs
@@ -199,7 +185,7 @@ __global__ void __launch_bounds__(GT) dec_gemv_kernel(GArgs a) {
         }
     }
   }
-  halve<32>(acc, lane);
+  wave_halve<32>(acc, lane);
   s_red[wave][lane] = acc[0];
   if (a.g) {
 #pragma unroll

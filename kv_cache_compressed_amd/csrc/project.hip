@@ -57,23 +57,6 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
   return ((unsigned long long)u << 32) | (0xffffffffu - (uint32_t)i);
 }
 
-// Recursive-halving reduction of N values per lane across the 64 lanes of a wave: after the
-// step of lane bit k, a lane keeps the half of its values selected by that bit, summed with the
-// partner lane's copy of the same half; lane l ends with the wave total of value l (N == 64).
-template <int S>
-__device__ __forceinline__ void halve(float* r, int lane) {
-  if constexpr (S >= 1) {
-    const bool up = lane & S;
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-      const float send = up ? r[i] : r[i + S];
-      const float keep = up ? r[i + S] : r[i];
-      r[i] = keep + __shfl_xor(send, S, 64);
-    }
-    halve<S / 2>(r, lane);
-  }
-}
-
 // Four consecutive weights of a row as fp32: one 16-byte load (fp32 rows) or one 8-byte load
 // widened exactly (bf16 rows).
 template <bool WBF16>
@@ -147,7 +130,7 @@ __global__ void __launch_bounds__(PT) project_kernel(PArgs a) {
     }
   }
 
-  halve<32>(acc, lane);
+  wave_halve<32>(acc, lane);
   s_red[wave][lane] = acc[0];
   __syncthreads();
   __shared__ int s_last;
