@@ -143,7 +143,9 @@ __device__ __forceinline__ void tile_copy(uint8_t* ring, int slot, __amdgpu_buff
 // range (G > 4) both slices must stream the same tiles through the same L2 at the same time, or
 // each tile is fetched from HBM twice: slice 0 of pair P runs as W = 16 (P / 8) + P % 8 and slice 1
 // as W + 8 (same XCD, dispatched right after). The grid is padded to whole groups of 16; padding
-// workgroups return at once. With one slice, W is the pair index itself (split fastest).
+// workgroups return at once. With one slice, W is the pair index itself. Pair P is split
+// P / units of unit P % units when the launch is tiered (see tile_start), else split P % gsplits
+// of unit P / gsplits (the prefill's heaviest-first unit order).
 struct LogicalBlock {
   int split, unit, z;
   bool live;
