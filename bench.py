@@ -27,14 +27,6 @@ import time
 
 import numpy as np
 
-# The schedules below run up to four streams at once (the launch stream, a second compute stream
-# and a copy stream, beside torch's own). HIP maps streams onto a fixed set of hardware queues
-# (4 by default) in creation order, and streams that share a queue run one after the other: in a
-# process that has created a few streams before, the staggered two-request decode measured 78.8
-# ms per round with 4 queues against 73.4 ms with 8 (its lock-step schedule 74.0 / 73.9 ms).
-if int(os.environ.get("GPU_MAX_HW_QUEUES") or 4) < 8:
-    os.environ["GPU_MAX_HW_QUEUES"] = "8"
-
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
@@ -307,7 +299,12 @@ def _e2e_decode(torch, seed: int, context: int, tokens: int) -> dict:
          "Wv": rn(Hkv * 128, dm) / dm ** 0.5, "Wo": rn(dm, Hq * 128) / (Hq * 128) ** 0.5,
          "Wlm": 3.0 * rn(V, dm) / dm ** 0.5}
     prompt = torch.randint(0, V, (context,), generator=g, device=dev).tolist()
-    opts = dict(kv_dtype="bf16", host_past=True, chunk_tokens=65536)
+    # One copy stream and one second compute stream for every decoder of this run: HIP maps streams
+    # onto a few hardware queues (4 per process by default) and streams that share a queue run one
+    # after the other; with a fresh copy stream per decoder the two-request pair's copy stream came
+    # to share a queue with a group stream (staggered 78.8 ms per round against 73.4).
+    copy, second = torch.cuda.Stream(), torch.cuda.Stream()
+    opts = dict(kv_dtype="bf16", host_past=True, chunk_tokens=65536, copy_stream=copy)
     out = {"context": context, "tokens": tokens, "model": "one layer, d_model 256, 32/8 heads, d 128, "
            "vocab 2048, bf16 cache in pinned host memory, 64K-token chunks"}
     seqs = {}
@@ -358,8 +355,7 @@ def _e2e_decode(torch, seed: int, context: int, tokens: int) -> dict:
 
     def pair():
         d0 = TokenDecoder(W, Hq, Hkv, prompt, x=30, bits=4, R=128, max_new=rounds * 31 + 64, **opts)
-        d1 = TokenDecoder(W, Hq, Hkv, prompt2, x=30, bits=4, R=128, max_new=rounds * 31 + 64,
-                          copy_stream=d0.copy_stream, **opts)
+        d1 = TokenDecoder(W, Hq, Hkv, prompt2, x=30, bits=4, R=128, max_new=rounds * 31 + 64, **opts)
         d0.warm()
         d1.warm()
         return [d0, d1]
@@ -372,8 +368,8 @@ def _e2e_decode(torch, seed: int, context: int, tokens: int) -> dict:
         if name == "lockstep":
             acc = harness.lockstep_decode(ds, rounds, lambda gi, r: ())
         else:
-            acc = harness.staggered_decode(ds, [torch.cuda.current_stream(), torch.cuda.Stream()],
-                                           rounds, lambda gi, r: ())
+            acc = harness.staggered_decode(ds, [torch.cuda.current_stream(), second], rounds,
+                                           lambda gi, r: ())
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         emitted = sum(len(em) for ga in acc for em in ga)

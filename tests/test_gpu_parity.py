@@ -556,6 +556,30 @@ def test_verify_shapes(gpu_lib, n, L):
             _close(out[b, hq].cpu().numpy(), O, True, TIGHT["verify"], f"verify n={n} L={L} b={b} h={hq}")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,n,L", [(100, 8, 8, 100, 4), (52, 48, 8, 300, 31)])
+def test_verify_grid_beyond_one_round(gpu_lib, B, Hq, Hkv, n, L):
+    """More (b, kv head) rows than one resident round of workgroups holds (800 and 832 workgroups,
+    the second with two head slices): the launch deals tile ranges split-fastest with equal
+    shares instead of by dispatch tier; sampled rows against the oracle."""
+    w = synth.WORKLOADS["c2"].with_(B=B, Hq=Hq, Hkv=Hkv, n=n, x=L - 1)
+    K, V, Kn, Vn, Q, W = _inputs(w)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", torch.bfloat16)
+    out = torch.full((B, Hq, L, 128), float("nan"), device="cuda")
+    lse = torch.full((B, Hq, L), float("nan"), device="cuda")
+    nb = vc.vc_verify_workspace(B, Hq, Hkv, L, n, False, 0, vc.VC_BF16)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    vc.vc_verify_attn(dev(Q), dev(Kn), dev(Vn), dev(K), dev(V), n, out, lse, ws, harness.SM_SCALE,
+                      past_stride=n)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+    for b in (0, 1, B // 2, B - 1):
+        for hq in (0, Hq // 2 + 1, Hq - 1):
+            O, l = oatt.verify_block(Q[b, hq], K[b, hq // G], V[b, hq // G], Kn[b, hq // G], Vn[b, hq // G])
+            _close(out[b, hq].cpu().numpy(), O, True, TIGHT["verify"], f"verify B={B} b={b} h={hq}")
+            _close(lse[b, hq].cpu().numpy(), l, True, TIGHT["verify"], f"verify lse B={B} b={b} h={hq}")
+
+
 @pytest.mark.parametrize("Hq,Hkv,n", [(6, 2, 997), (10, 2, 1000), (12, 2, 1003), (14, 2, 2050), (16, 2, 1500)])
 def test_verify_head_groups(gpu_lib, Hq, Hkv, n):
     """3, 5, 6, 7 and 8 query heads per kv head (more than 4 run as two head slices per tile range,
