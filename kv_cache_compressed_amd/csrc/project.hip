@@ -188,11 +188,13 @@ __global__ void __launch_bounds__(PT) project_kernel(PArgs a) {
 // Many rows (the verify block's B*L rows): a tiled product on the fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 accumulation). Workgroup = 4 waves on TMT = 32
 // output rows x TVT = 64 vocabulary rows; wave w owns vocabulary rows 16w .. 16w + 15 against all
-// 32 output rows (two 16 x 16 tiles). K goes through LDS in chunks of KC = 64 (the next chunk's
-// loads in flight in registers while the current one is multiplied). Within a group of four
+// 32 output rows (two 16 x 16 tiles). K goes through two LDS slots in chunks of KC = 64 (the next
+// chunk stored to one slot while the current one is multiplied from the other, the two after it in
+// flight in registers). Within a group of four
 // MFMA steps a lane of k-slot s takes the real channels 4s .. 4s + 3 of the group's 16 (the same
 // remap for both operands), so each operand read is one 16-byte LDS load per four steps. The
-// argmax (when asked for) goes through the same per-row slots and row-tile ticket as above.
+// argmax (when asked for) goes through per-row slots (atomic max of the same 64-bit keys) and a
+// row-tile ticket.
 // ---------------------------------------------------------------------------------------------
 constexpr int TMT = 32;
 constexpr int TVT = 64;
@@ -201,8 +203,8 @@ constexpr int KCP = KC + 4;  // padded LDS row (floats)
 
 template <bool WBF16>
 __global__ void __launch_bounds__(256) project_tiled_kernel(PArgs a) {
-  __shared__ __attribute__((aligned(16))) float s_a[TMT * KCP];
-  __shared__ __attribute__((aligned(16))) float s_b[TVT * KCP];
+  __shared__ __attribute__((aligned(16))) float s_a[2][TMT * KCP];  // two chunk slots
+  __shared__ __attribute__((aligned(16))) float s_b[2][TVT * KCP];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.y * TMT, v0 = blockIdx.x * TVT;
@@ -213,55 +215,70 @@ __global__ void __launch_bounds__(256) project_tiled_kernel(PArgs a) {
   const int64_t abase = ((int64_t)(am / a.L) * a.Hq * a.L + am % a.L) * 128;  // head 0 of row am
   const int br = tid >> 2, bp = tid & 3;
   const int64_t brow = (int64_t)min(v0 + br, a.V - 1) * a.Dm;
-  f32x4 ra[2], rb[4];
-  auto load = [&](int k0) {
+  // Staging ring: chunk k is multiplied from LDS slot k % 2 while chunk k + 1 is stored to the other
+  // slot and the loads of chunks k + 2 .. k + NB - 1 are in flight in registers (a load past the
+  // last chunk re-reads the last one, so every step issues the same loads and waits for exactly the
+  // chunk it stores); one barrier per chunk.
+  constexpr int NB = 4;
+  const int nch = a.Dm / KC;
+  f32x4 ra[NB][2], rb[NB][4];
+  auto load = [&](int c, f32x4* qa, f32x4* qb) {
+    const int k0 = min(c, nch - 1) * KC;
     const int64_t ao = abase + (int64_t)(k0 >> 7) * a.L * 128 + (k0 & 127);  // k0 % 64 == 0
 #pragma unroll
-    for (int z = 0; z < 2; ++z) ra[z] = *reinterpret_cast<const f32x4*>(a.o + ao + 4 * ap + 32 * z);
+    for (int z = 0; z < 2; ++z) qa[z] = *reinterpret_cast<const f32x4*>(a.o + ao + 4 * ap + 32 * z);
 #pragma unroll
     for (int z = 0; z < 4; ++z) {
       const int64_t d = brow + k0 + 16 * bp + 4 * z;
       if constexpr (WBF16) {
         const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.W) + d);
-        rb[z] = f32x4{bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16),
+        qb[z] = f32x4{bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16),
                       bf16_bits_to_f32(u.y & 0xffffu), bf16_bits_to_f32(u.y >> 16)};
       } else {
-        rb[z] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.W) + d);
+        qb[z] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.W) + d);
       }
     }
   };
-  auto store = [&]() {
+  auto store = [&](int slot, const f32x4* qa, const f32x4* qb) {
 #pragma unroll
-    for (int z = 0; z < 2; ++z) *reinterpret_cast<f32x4*>(s_a + ar * KCP + 4 * ap + 32 * z) = ra[z];
+    for (int z = 0; z < 2; ++z) *reinterpret_cast<f32x4*>(s_a[slot] + ar * KCP + 4 * ap + 32 * z) = qa[z];
 #pragma unroll
-    for (int z = 0; z < 4; ++z) *reinterpret_cast<f32x4*>(s_b + br * KCP + 16 * bp + 4 * z) = rb[z];
+    for (int z = 0; z < 4; ++z) *reinterpret_cast<f32x4*>(s_b[slot] + br * KCP + 16 * bp + 4 * z) = qb[z];
   };
 
   const int i16 = lane & 15, ks = lane >> 4;
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  load(0);
-  store();
+#pragma unroll
+  for (int c = 0; c < NB - 1; ++c) load(c, ra[c], rb[c]);
+  store(0, ra[0], rb[0]);
   __syncthreads();
-  for (int k0 = 0; k0 < a.Dm; k0 += KC) {
-    const bool more = k0 + KC < a.Dm;
-    if (more) load(k0 + KC);
+  for (int c0 = 0; c0 < nch; c0 += NB) {
 #pragma unroll
-    for (int g = 0; g < KC / 16; ++g) {
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(s_b + (16 * wave + i16) * KCP + 16 * g + 4 * ks);
+    for (int u = 0; u < NB; ++u) {
+      const int k = c0 + u;
+      load(k + NB - 1, ra[(u + NB - 1) % NB], rb[(u + NB - 1) % NB]);
+      // chunk k + 1 into the other slot (last read by chunk k - 1, before the previous barrier;
+      // past the end: unused)
+      store((u + 1) % 2, ra[(u + 1) % NB], rb[(u + 1) % NB]);
+      if (k < nch) {
+        const float* sa = s_a[u % 2];
+        const float* sb = s_b[u % 2];
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(s_a + (16 * r + i16) * KCP + 16 * g + 4 * ks);
+        for (int g = 0; g < KC / 16; ++g) {
+          const f32x4 bv = *reinterpret_cast<const f32x4*>(sb + (16 * wave + i16) * KCP + 16 * g + 4 * ks);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[r], 0, 0, 0);
+          for (int r = 0; r < 2; ++r) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(sa + (16 * r + i16) * KCP + 16 * g + 4 * ks);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[r], 0, 0, 0);
+          }
+        }
       }
-    }
-    __syncthreads();
-    if (more) {
-      store();
       __syncthreads();
     }
   }
+  wait_vm<0>();  // the ring's last loads (past the end) have landed
 
   // lane holds C[m0 + 16 r + 4 ks + e][v0 + 16 wave + i16]
   const int v = v0 + 16 * wave + i16;
@@ -276,9 +293,9 @@ __global__ void __launch_bounds__(256) project_tiled_kernel(PArgs a) {
   }
   if (!a.idx) return;
   // tile-local argmax per row through LDS (the staging space is free after the loop's last barrier)
-  float* s_t = s_a;  // [TMT][TVT + 1]
-  static_assert(TMT * (TVT + 1) <= TMT * KCP + TVT * KCP, "argmax staging");
-  float* s_tt = s_a;
+  float* s_t = s_a[0];  // [TMT][TVT + 1]
+  static_assert(TMT * (TVT + 1) <= TMT * KCP, "argmax staging");
+  float* s_tt = s_a[0];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
