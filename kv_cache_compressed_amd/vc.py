@@ -14,7 +14,7 @@ import re
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libvc.so")
+LIB_PATH = os.environ.get("VC_LIB") or os.path.join(PKG, "libvc.so")  # VC_LIB: another build
 HEADER = os.path.join(os.path.dirname(PKG), "include", "vc.h")
 
 VC_OK, VC_ERR_INVALID, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_HIP = 0, 1, 2, 3, 4
