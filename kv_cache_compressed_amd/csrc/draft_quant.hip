@@ -55,9 +55,11 @@ constexpr float SCALE_PV = 256.0f;     // 2^8: same for the PV operand
 constexpr float SUBNORMAL = 16777216.0f;  // 2^24: one fp16 subnormal step is 2^-24
 constexpr float LAZY = 2.0f;           // log2 slack before the running max is moved
 // Workgroups resident per CU (= waves per SIMD); the LDS of a CU (160 KB) is shared among them.
-constexpr int WG_PER_CU = 3;
+// 2-bit groups (3 KB) carry more compute per byte and need a third wave per SIMD to cover it;
+// 4-bit groups (5 KB) stream faster with two waves and the deeper ring that leaves room for.
+constexpr int wg_per_cu(int bits) { return bits == 2 ? 3 : 2; }
 constexpr int NUM_CUS = 256;
-constexpr int RING_WAVE_BYTES = (160 * 1024 / WG_PER_CU / WAVES) / 1024 * 1024;
+constexpr int ring_wave_bytes(int bits) { return (160 * 1024 / wg_per_cu(bits) / WAVES) / 1024 * 1024; }
 // LDS: residual split [q 8xD | p 8xRES_MAX | ml 16 | reduction WAVESx8xD] floats; the quantised
 // split uses it for one 12 KB ring per wave and, after its loop, the wave merge.
 constexpr int RES_SMEM_FLOATS = 8 * D + 8 * RES_MAX + 16 + WAVES * 8 * D;
@@ -122,7 +124,7 @@ struct RingPlan {
   static constexpr int MB = META_F16 ? 512 : 1024;     // one group's key (or value) metadata
   static constexpr int SLOT = 2 * CB + 2 * MB;
   static constexpr int LOADS = SLOT / 1024;
-  static constexpr int DEPTH = std::max(2, (RING_WAVE_BYTES - WAVE_SCRATCH) / SLOT);
+  static constexpr int DEPTH = std::max(2, (ring_wave_bytes(BITS) - WAVE_SCRATCH) / SLOT);
   static constexpr int BYTES = DEPTH * SLOT + WAVE_SCRATCH;  // per wave
   static_assert(SLOT % 1024 == 0, "ring plan");
 };
@@ -1085,7 +1087,7 @@ __device__ void append_new_token(const DQArgs& a, int bh) {
 }
 
 template <int BITS, bool META_F16, bool RES_F16, int CPH>
-__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WG_PER_CU, WG_PER_CU))) draft_quant_kernel(DQArgs a0) {
+__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wg_per_cu(BITS), wg_per_cu(BITS)))) draft_quant_kernel(DQArgs a0) {
   __shared__ float smem[std::max(WAVES * RingPlan<BITS, META_F16>::BYTES / 4, RES_SMEM_FLOATS)];
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
@@ -1129,9 +1131,9 @@ DraftQuantPlan plan_draft_quant(const vc_kivi& c, int64_t n_q, int Hq) {
   DraftQuantPlan p;
   const int64_t ngroups = n_q / GROUP;
   const int64_t units = (int64_t)c.B * c.Hkv;
-  // One resident round of workgroups: 256 CUs x 3 workgroups (the kernel is built for 3 waves
-  // per SIMD), splits + 1 per (b, kv head); at least 2 groups per wave.
-  int64_t s = std::max<int64_t>(1, NUM_CUS * WG_PER_CU / units - 1);
+  // One resident round of workgroups: 256 CUs x the workgroups per CU the kernel is built for
+  // (its waves per SIMD), splits + 1 per (b, kv head); at least 2 groups per wave.
+  int64_t s = std::max<int64_t>(1, NUM_CUS * wg_per_cu(c.bits) / units - 1);
   s = std::min<int64_t>(s, std::max<int64_t>(1, ngroups / 8));
   if (ngroups == 0) s = 0;
   p.splits = (int)s;
