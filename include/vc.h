@@ -444,7 +444,8 @@ vc_status vc_embed_rows(const float *E, int32_t V, int32_t K, const int32_t *tok
 /*
  * Workspace size of any call that takes one, by operation code and its size arguments (the same
  * values as the per-operation queries, which it forwards to; host only, nothing enqueued):
- *   VC_OP_DRAFT_QUANT  dims {B, Hkv, Hq, n_q}                                (vc_draft_attn_quant)
+ *   VC_OP_DRAFT_QUANT  dims {B, Hkv, Hq, n_q}                                (vc_draft_attn_quant;
+ *                      the size for 2-bit codes, which is also enough for 4-bit ones)
  *   VC_OP_DRAFT_DROP   dims {B, Hkv, Hq, n_keep}                             (vc_draft_attn_drop)
  *   VC_OP_VERIFY       dims {B, Hq, Hkv, L, n, past_on_host, chunk_tokens, dtype}  (vc_verify_attn,
  *                      vc_verify_prefetch, vc_verify_stream_copies)

@@ -695,6 +695,7 @@ vc_status vc_workspace_bytes(int32_t op, const int64_t* dims, int32_t ndims, siz
       vc_kivi c{};
       c.B = (int32_t)B;
       c.Hkv = (int32_t)Hkv;
+      c.bits = 2;  // 2-bit caches split the context most finely: the size covers either width
       *bytes = vc::plan_draft_quant(c, n_q, (int)Hq).ws_bytes;
       return ok();
     }
