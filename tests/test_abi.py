@@ -237,6 +237,11 @@ def test_generic_workspace_query_matches_the_per_op_queries(L):
     k = _kivi(B=8, Hkv=8, tok_cap=32768)
     assert L.vc_draft_quant_workspace(ctypes.byref(k), 32640, 128, 32, ctypes.byref(one)) == vc.VC_OK
     assert vc.vc_workspace_bytes(vc.VC_OP_DRAFT_QUANT, [8, 8, 32, 32640]) == one.value
+    # 4-bit caches split the context more coarsely: the generic size (2-bit) still covers them
+    for B, Hkv, Hq, n_q in ((8, 8, 32, 32640), (1, 8, 32, 499872), (1, 8, 32, 2016)):
+        k4 = _kivi(bits=4, B=B, Hkv=Hkv, tok_cap=n_q + 128)
+        assert L.vc_draft_quant_workspace(ctypes.byref(k4), n_q, 128, Hq, ctypes.byref(one)) == vc.VC_OK
+        assert vc.vc_workspace_bytes(vc.VC_OP_DRAFT_QUANT, [B, Hkv, Hq, n_q]) >= one.value
     assert L.vc_draft_drop_workspace(4, 8, 64, 25000, ctypes.byref(one)) == vc.VC_OK
     assert vc.vc_workspace_bytes(vc.VC_OP_DRAFT_DROP, [4, 8, 64, 25000]) == one.value
     for dims in ([8, 32, 8, 31, 32768, 0, 0, vc.VC_BF16], [1, 32, 8, 31, 500000, 1, 65536, vc.VC_BF16],
