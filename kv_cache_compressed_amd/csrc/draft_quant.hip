@@ -632,9 +632,8 @@ __device__ void quant_split_t(const DQArgs& a, int bh, int g_begin, int g_end, i
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) tcell[kb] = 16 * trow_s + ((4 * kb + gq) ^ trow_s);
   const ProgressPriority prio(gr.n);
-  for (int i = 0; i < gr.n; ++i) {
-    prio.step(i);
-    uint8_t* sl = gr.acquire(i);
+  // One group in the slot sl.
+  auto group = [&](uint8_t* sl) {
     const uint8_t* mb = sl + 2 * RingPlan<BITS, true>::CB;
     uint32_t kwd[WPL], vwd[WPL];
     gr.codes(sl, lane, kwd, vwd);
@@ -719,6 +718,23 @@ __device__ void quant_split_t(const DQArgs& a, int bh, int g_begin, int g_end, i
       const u32x4 av = BITS == 2 ? unpack2(vwd[t / 2], t & 1) : unpack4(vwd[t]);
       acc[t] = mfma_f16(av, bp, acc[t]);
     }
+  };
+  // Whole turns of the ring with the slot fixed at compile time (LDS addresses as immediate
+  // offsets: i is a multiple of DEPTH there, so group i + u sits in slot u), then the remaining
+  // groups.
+  constexpr int DEPTH = RingPlan<BITS, true>::DEPTH;
+  int i = 0;
+  for (; i + DEPTH <= gr.n; i += DEPTH) {
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+      prio.step(i + u);
+      gr.acquire(i + u);
+      group(gr.ring + u * RingPlan<BITS, true>::SLOT);
+    }
+  }
+  for (; i < gr.n; ++i) {
+    prio.step(i);
+    group(gr.acquire(i));
   }
 
   // ---- wave result -> LDS: m [WAVES][8], l [WAVES][8], o [WAVES][8][D] --------------------
