@@ -385,6 +385,26 @@ def test_draft_quant_parity(gpu_lib, name):
             _close(res["lse_d"][j, b], lse, bf16, TIGHT["draft_quant"], f"{name} draft lse j={j} b={b}")
 
 
+@pytest.mark.parametrize("name,B,n", [("c2", 8, 6300), ("c2", 8, 9999), ("c4", 1, 40000)])
+def test_draft_quant_whole_ring_turns(gpu_lib, name, B, n):
+    """Contexts long enough that each wave takes several whole turns of its LDS ring (the unrolled
+    loop: four groups per turn at 2-bit, three at 4-bit) plus a remainder: every head of the first
+    and last draft step against the oracle."""
+    w = synth.WORKLOADS[name].with_(B=B, n=n, x=2, chunk_tokens=4096)
+    inp = _inputs(w)
+    st = harness.RoundState(w, inputs=inp)
+    rnd = Round(w, *inp)
+    bf16 = w.kv_dtype == "bf16"
+    for j in range(w.x):
+        st.draft_attention(j)
+    res = st.results()
+    for j in (0, w.x - 1):
+        for b in range(w.B):
+            O, lse = rnd.draft_step(b, j)
+            _close(res["out_d"][j, b], O, bf16, TIGHT["draft_quant"], f"{name} n={n} draft j={j} b={b}")
+            _close(res["lse_d"][j, b], lse, bf16, TIGHT["draft_quant"], f"{name} n={n} lse j={j} b={b}")
+
+
 @pytest.mark.parametrize("n_q_zero", [True, False])
 def test_draft_quant_edges(gpu_lib, n_q_zero):
     """Residual only (nothing quantised) and quantised only (empty residual)."""
