@@ -72,7 +72,18 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3,
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t blk = blk_begin + wave; blk < blk_end; blk += WAVES) {
+  // Progress-based wave priority: every wave starts at the top level and steps down at 1/3, 2/3
+  // and 5/6 of its share, so waves that started early yield to later ones and the waves of a CU
+  // finish closer together.
+  const int nmine = __builtin_amdgcn_readfirstlane(
+      (int)(blk_begin + wave < blk_end ? (blk_end - blk_begin - wave + WAVES - 1) / WAVES : 0));
+  const int q1 = nmine / 3, q2 = 2 * nmine / 3, q3 = 5 * nmine / 6;
+  __builtin_amdgcn_s_setprio(3);
+  int it = 0;
+  for (int64_t blk = blk_begin + wave; blk < blk_end; blk += WAVES, ++it) {
+    if (it == q1) __builtin_amdgcn_s_setprio(2);
+    if (it == q2) __builtin_amdgcn_s_setprio(1);
+    if (it == q3) __builtin_amdgcn_s_setprio(0);
     const int64_t e0 = blk * BLK;
     // ---- gather keys into the row operand: lane (token 16tb + j, quarter gq) ----------------
     u32x4 kop[2][4];
@@ -168,6 +179,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3,
     wave_lds_sync();  // operand reads finish before the next block overwrites the tile
   }
 
+  __builtin_amdgcn_s_setprio(3);  // the partial stores end the workgroup's share
   // ---- wave result -> LDS (column 2h holds the hi sum, 2h+1 the lo sum) ---------------------
   const float l_tot = sum_over_rows(l_lane);
   __syncthreads();  // every wave is done with its value tile before s_o reuses the storage
