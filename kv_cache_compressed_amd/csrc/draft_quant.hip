@@ -1105,6 +1105,7 @@ __device__ void append_new_token(const DQArgs& a, int bh) {
 template <int BITS, bool META_F16, bool RES_F16, int CPH>
 __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wg_per_cu(BITS), wg_per_cu(BITS)))) draft_quant_kernel(DQArgs a0) {
   __shared__ float smem[std::max(WAVES * RingPlan<BITS, META_F16>::BYTES / 4, RES_SMEM_FLOATS)];
+  static_assert(wg_per_cu(BITS) * sizeof(smem) <= 160 * 1024, "the workgroups per CU must fit its LDS");
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
   DQArgs a = a0;
